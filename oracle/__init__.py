@@ -1,0 +1,314 @@
+"""CPU oracle for the Medusa tree-decode step -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the bench's ``cpu_baseline``
+leg import this package. The GPU library (``medusa_draft_heads_amd``) never
+imports it and shares no code with it; the two meet only through the seeded
+inputs of ``synth``.
+
+The arithmetic lives in ``oracle.c`` (plain loops, double precision). This
+module marshals numpy arrays and orchestrates the steps in the order the
+pages give them:
+
+* heads -- Medusa heads versus separate draft model, "What each one is":
+  every head is a residual block on the target's last hidden state followed
+  by its own vocabulary projection;
+* per-head top-k and the tree of combinations -- same page, "Trees";
+* tree-masked attention over the KV cache -- same page, "Trees";
+* greedy acceptance and the cache entries of the accepted branch -- same
+  page, "Trees" and "Acceptance";
+* Hydra heads -- the Hydra summary and abstract: each head also sees the
+  token speculated before it.
+
+bf16 arrays are numpy uint16 bit patterns; float32 arrays are float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Dict, Optional, Sequence
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    if force or not os.path.exists(_LIB):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared",
+                               "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=False)
+        L = ctypes.CDLL(_LIB)
+        i, i64, d, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
+        sig = {
+            "orc_set_threads": ([i], None),
+            "orc_get_threads": ([], i),
+            "orc_to_double": ([i, i64, vp, vp], None),
+            "orc_head_weight_elems": ([i, i, i], i64),
+            "orc_residual": ([i, i, i, i, vp, vp, vp, vp, vp], None),
+            "orc_vocab_topk": ([i, i, i, i, vp, vp, i, vp, vp, vp, vp], None),
+            "orc_tree_tokens_medusa": ([i, vp, vp, i, i, i, vp, vp, vp, vp, vp, vp], None),
+            "orc_tree_attention": ([i, i, i, vp, i, i, i, i, vp, vp, vp, vp, d, vp], None),
+            "orc_argmax": ([i64, i, vp, vp], None),
+            "orc_accept": ([i, vp, i, i, vp, vp, vp, vp, vp, vp, vp], None),
+            "orc_compact": ([i, i, i, i, i, vp, vp, vp, vp, vp, i], None),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _p(a: Optional[np.ndarray]):
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"], "oracle inputs must be C-contiguous"
+    return a.ctypes.data
+
+
+def _dt(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    raise TypeError("storage dtype must be float32 or uint16 (bf16 bits), got %s" % a.dtype)
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(int(n))
+
+
+def threads() -> int:
+    return int(lib().orc_get_threads())
+
+
+def to_double(a: np.ndarray) -> np.ndarray:
+    a = np.ascontiguousarray(a)
+    out = np.empty(a.shape, dtype=np.float64)
+    lib().orc_to_double(_dt(a), a.size, _p(a), _p(out))
+    return out
+
+
+def head_weight_elems(din: int, d: int, V: int) -> int:
+    return int(lib().orc_head_weight_elems(din, d, V))
+
+
+# ------------------------------------------------------------------ heads
+
+def residual(W_k: np.ndarray, b_k: Optional[np.ndarray], x: np.ndarray, base: np.ndarray) -> np.ndarray:
+    """hres = base + SiLU(W_k x + b_k) for every row of x (double in, double out)."""
+    d, din = W_k.shape
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    base = np.ascontiguousarray(base, dtype=np.float64)
+    M = x.shape[0]
+    assert x.shape == (M, din) and base.shape == (M, d)
+    out = np.empty((M, d), dtype=np.float64)
+    if b_k is not None:
+        assert b_k.dtype == W_k.dtype
+    lib().orc_residual(_dt(W_k), M, din, d, _p(x), _p(base), _p(np.ascontiguousarray(W_k)),
+                       _p(None if b_k is None else np.ascontiguousarray(b_k)), _p(out))
+    return out
+
+
+def vocab_topk(U_k: np.ndarray, hres: np.ndarray, k: int, want_logits: bool = False):
+    """Top-k of U_k hres per row, sorted by (value desc, index asc), and its margin."""
+    V, d = U_k.shape
+    hres = np.ascontiguousarray(hres, dtype=np.float64)
+    M = hres.shape[0]
+    idx = np.empty((M, k), dtype=np.int32)
+    val = np.empty((M, k), dtype=np.float64)
+    margin = np.empty(M, dtype=np.float64)
+    logits = np.empty((M, V), dtype=np.float64) if want_logits else None
+    lib().orc_vocab_topk(_dt(U_k), M, d, V, _p(hres), _p(np.ascontiguousarray(U_k)), k,
+                         _p(idx), _p(val), _p(margin), _p(logits))
+    return idx, val, margin, logits
+
+
+def heads_medusa(W, b, U, h, topk: Sequence[int], rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+    """All K Medusa heads on hidden-state rows h [M, d].
+
+    Returns hres [K, R, d], idx [R, K, kmax] (-1 padded), val [R, K, kmax]
+    (-inf padded), margin [R, K], for the R selected rows (all by default).
+    """
+    K = W.shape[0]
+    hd = to_double(h)
+    if rows is not None:
+        hd = hd[np.asarray(rows)]
+    R, d = hd.shape
+    kmax = max(topk)
+    hres = np.empty((K, R, d), dtype=np.float64)
+    idx = np.full((R, K, kmax), -1, dtype=np.int32)
+    val = np.full((R, K, kmax), -np.inf, dtype=np.float64)
+    margin = np.empty((R, K), dtype=np.float64)
+    for k in range(K):
+        hres[k] = residual(W[k], b[k], hd, hd)
+        i_, v_, m_, _ = vocab_topk(U[k], hres[k], topk[k])
+        idx[:, k, : topk[k]] = i_
+        val[:, k, : topk[k]] = v_
+        margin[:, k] = m_
+    return {"hres": hres, "idx": idx, "val": val, "margin": margin}
+
+
+def _depths(parent: Sequence[int]):
+    dep = []
+    for n in range(len(parent)):
+        d, c = 0, n
+        while parent[c] >= 0:
+            c = parent[c]
+            d += 1
+        dep.append(d)
+    return dep
+
+
+def hydra_rows(parent: Sequence[int], level: int):
+    """Parents whose children sit at depth `level`, in node order."""
+    dep = _depths(parent)
+    return [p for p in range(len(parent)) if dep[p] == level - 1 and any(parent[c] == p for c in range(len(parent)))]
+
+
+def hydra_expand(W, b, U, E, h, topo_parent, topo_rank, topk: Sequence[int], root_tok, lens,
+                 requests: Optional[Sequence[int]] = None) -> Dict[str, object]:
+    """Hydra heads, level by level (the Hydra summary and abstract).
+
+    Level i runs head i on one row per (request, parent at depth i - 1 with
+    children): x = [h_b ; E[token of the parent]], hres = h_b + SiLU(W_i x +
+    b_i), then head i's projection and top-k_i. A node at depth i takes entry
+    rank(n) of its own parent's list. Returns the tree tokens, positions and
+    every level's (rows, hres, idx, val, margin).
+    """
+    K = W.shape[0]
+    N = len(topo_parent)
+    dep = _depths(topo_parent)
+    B = h.shape[0]
+    reqs = list(range(B)) if requests is None else list(requests)
+    hd = to_double(h)
+    Ed_cache: Dict[int, np.ndarray] = {}
+
+    def emb(tok: int) -> np.ndarray:
+        if tok not in Ed_cache:
+            Ed_cache[tok] = to_double(np.ascontiguousarray(E[tok]))
+        return Ed_cache[tok]
+
+    tok = np.full((B, N), -1, dtype=np.int32)
+    pos = np.zeros((B, N), dtype=np.int32)
+    for b_ in reqs:
+        tok[b_, 0] = root_tok[b_]
+        for n in range(N):
+            pos[b_, n] = lens[b_] + dep[n]
+    levels = []
+    for i in range(1, K + 1):
+        parents = hydra_rows(topo_parent, i)
+        if not parents:
+            break
+        rows = [(b_, p) for b_ in reqs for p in parents]
+        x = np.stack([np.concatenate([hd[b_], emb(int(tok[b_, p]))]) for (b_, p) in rows])
+        base = np.stack([hd[b_] for (b_, _) in rows])
+        hres = residual(W[i - 1], b[i - 1], x, base)
+        idx, val, margin, _ = vocab_topk(U[i - 1], hres, topk[i - 1])
+        row_of = {rp: r for r, rp in enumerate(rows)}
+        for b_ in reqs:
+            for n in range(N):
+                if dep[n] == i:
+                    tok[b_, n] = idx[row_of[(b_, topo_parent[n])], topo_rank[n]]
+        levels.append({"rows": rows, "hres": hres, "idx": idx, "val": val, "margin": margin})
+    return {"tree_tok": tok, "tree_pos": pos, "levels": levels}
+
+
+# ------------------------------------------------------------------ tree
+
+def tree_tokens_medusa(parent, rank, topk_idx: np.ndarray, src_row, root_tok, lens):
+    M, K, kmax = topk_idx.shape
+    N = len(parent)
+    B = len(root_tok)
+    par = np.asarray(parent, dtype=np.int8)
+    rk = np.asarray(rank, dtype=np.int8)
+    tok = np.empty((B, N), dtype=np.int32)
+    pos = np.empty((B, N), dtype=np.int32)
+    lib().orc_tree_tokens_medusa(N, _p(par), _p(rk), B, K, kmax, _p(np.ascontiguousarray(topk_idx, dtype=np.int32)),
+                                 _p(np.ascontiguousarray(src_row, dtype=np.int32)),
+                                 _p(np.ascontiguousarray(root_tok, dtype=np.int32)),
+                                 _p(np.ascontiguousarray(lens, dtype=np.int32)), _p(tok), _p(pos))
+    return tok, pos
+
+
+def tree_attention(parent, q: np.ndarray, Kc: np.ndarray, Vc: np.ndarray, lens, scale: Optional[float] = None):
+    B, N, Hq, hd = q.shape
+    _, Hkv, Lcap, _ = Kc.shape
+    assert len(parent) == N and Kc.shape == Vc.shape and Hq % Hkv == 0
+    if scale is None:
+        scale = 1.0 / np.sqrt(hd)
+    out = np.empty((B, N, Hq, hd), dtype=np.float64)
+    par = np.asarray(parent, dtype=np.int8)
+    lib().orc_tree_attention(_dt(q), B, N, _p(par), Hq, Hkv, hd, Lcap, _p(np.ascontiguousarray(q)),
+                             _p(np.ascontiguousarray(Kc)), _p(np.ascontiguousarray(Vc)),
+                             _p(np.ascontiguousarray(lens, dtype=np.int32)), float(scale), _p(out))
+    return out
+
+
+# --------------------------------------------------------- verify / accept
+
+def argmax(logits: np.ndarray) -> np.ndarray:
+    x = np.ascontiguousarray(logits, dtype=np.float32)
+    V = x.shape[-1]
+    R = x.size // V
+    out = np.empty(R, dtype=np.int32)
+    lib().orc_argmax(R, V, _p(x), _p(out))
+    return out.reshape(x.shape[:-1])
+
+
+def accept(parent, K: int, tree_tok: np.ndarray, tstar: np.ndarray, lens):
+    B, N = tree_tok.shape
+    par = np.asarray(parent, dtype=np.int8)
+    acc = np.empty(B, dtype=np.int32)
+    path = np.empty((B, K + 1), dtype=np.int32)
+    nxt = np.empty(B, dtype=np.int32)
+    src = np.empty((B, K + 1), dtype=np.int32)
+    lib().orc_accept(N, _p(par), B, K, _p(np.ascontiguousarray(tree_tok, dtype=np.int32)),
+                     _p(np.ascontiguousarray(tstar, dtype=np.int32)),
+                     _p(np.ascontiguousarray(lens, dtype=np.int32)), _p(acc), _p(path), _p(nxt), _p(src))
+    return {"accept_len": acc, "path": path, "next_tok": nxt, "compact_src": src}
+
+
+def compact(Kc: np.ndarray, Vc: np.ndarray, lens, accept_len, path, K: int):
+    """In place on copies: returns (Kc', Vc', lens')."""
+    Kc = np.ascontiguousarray(Kc).copy()
+    Vc = np.ascontiguousarray(Vc).copy()
+    B, Hkv, Lcap, hd = Kc.shape
+    ln = np.ascontiguousarray(lens, dtype=np.int32).copy()
+    lib().orc_compact(_dt(Kc), B, Hkv, hd, Lcap, _p(Kc), _p(Vc), _p(ln),
+                      _p(np.ascontiguousarray(accept_len, dtype=np.int32)),
+                      _p(np.ascontiguousarray(path, dtype=np.int32)), K)
+    return Kc, Vc, ln
+
+
+def step_medusa(wl, wts: Dict[str, np.ndarray], inp: Dict[str, np.ndarray], topo, logits: np.ndarray):
+    """One whole decode step on the CPU: heads, tree, attention, verification, accept, compaction."""
+    K = wl.K
+    heads = heads_medusa(wts["W"], wts["b"], wts["U"], inp["h"], wl.topk,
+                         rows=sorted(set(int(r) for r in inp["src_row"])))
+    # heads ran on the distinct source rows only; map them back to row ids
+    rows = sorted(set(int(r) for r in inp["src_row"]))
+    full_idx = np.full((wl.M, K, wl.kmax), -1, dtype=np.int32)
+    for j, r in enumerate(rows):
+        full_idx[r] = heads["idx"][j]
+    tok, pos = tree_tokens_medusa(topo.parent, topo.rank, full_idx, inp["src_row"], inp["root_tok"], inp["lens"])
+    out = tree_attention(topo.parent, inp["q"], inp["Kc"], inp["Vc"], inp["lens"])
+    tstar = argmax(logits)
+    acc = accept(topo.parent, K, tok, tstar, inp["lens"])
+    Kc2, Vc2, lens2 = compact(inp["Kc"], inp["Vc"], inp["lens"], acc["accept_len"], acc["path"], K)
+    return {"heads": heads, "tree_tok": tok, "tree_pos": pos, "attn": out, "tstar": tstar, **acc,
+            "Kc": Kc2, "Vc": Vc2, "lens": lens2}
