@@ -1,0 +1,215 @@
+"""Medusa tree-decode step throughput on one MI355X.
+
+One step = the whole hot path on one batch of seeded synthetic input, inputs
+resident in HBM: heads (residual block + vocabulary projection + per-head
+top-k) -> candidate tree -> tree attention over the KV cache -> target argmax,
+greedy acceptance and KV compaction. Default workload: 70B-shaped heads at
+batch 1 (d = 8,192, V = 128,256, 4 heads in bf16 = 8.94 GB of weights, top-k
+(10, 4, 2, 1), 64-node tree, GQA 64/8 heads of 128, 4,096 cached positions).
+
+Prints one JSON line: steps/s, the roofline of the dominant kernel (the
+vocabulary projection + top-k, timed live with HIP events on the stream it
+runs on) and the CPU oracle's own throughput on the same inputs.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+PMC_FILE = os.path.join(ROOT, "profiles", "vocab_topk_70b_pmc.json")
+
+
+def log(msg: str) -> None:
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def file_sha(path: str) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="70b", choices=["70b", "70b_chain", "8b", "tiny", "70b_b8", "hydra_b4"])
+    ap.add_argument("--sets", type=int, default=8, help="input sets rotated to keep them out of the 256 MB MALL")
+    ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps timed for the CPU baseline (0: skip)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy (scale factor for HBM counters)")
+    ap.add_argument("--seed", type=int, default=70)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
+        return 2
+
+    import torch
+
+    import medusa_draft_heads_amd as md
+    import oracle
+    from synth.workloads import ALL, plant, step_inputs, weights
+
+    wl = ALL[args.workload]
+    if wl.kind != "medusa" or wl.rows_per_request != 1:
+        print("bench.py: the timed step covers the batch-1 Medusa workloads", file=sys.stderr)
+        return 2
+    topo = wl.topology()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    t0 = time.time()
+    w = weights(wl, args.seed)
+    log("weights generated (%.1f s)" % (time.time() - t0))
+    wd = {k: to_dev(v) for k, v in w.items()}
+    torch.cuda.synchronize()
+    log("weights on the GPU (%.1f GB)" % (sum(v.numel() * v.element_size() for v in wd.values()) / 1e9))
+
+    # input sets; each set's logits are planted from the oracle's own tree tokens,
+    # and the oracle's whole step on the first --cpu-steps sets is the CPU baseline
+    sets, cpu_times, acc_oracle = [], [], []
+    threads = oracle.threads()
+    for s in range(args.sets):
+        x = step_inputs(wl, args.seed, step=s)
+        ta = time.perf_counter()
+        heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], wl.topk)
+        tok, pos = oracle.tree_tokens_medusa(topo.parent, topo.rank, heads["idx"], x["src_row"], x["root_tok"],
+                                             x["lens"])
+        tb = time.perf_counter()
+        logits = plant(x["logits"], topo, tok, wl.a, seed=args.seed, step=s)
+        if s < args.cpu_steps:
+            tc = time.perf_counter()
+            oracle.tree_attention(topo.parent, x["q"], x["Kc"], x["Vc"], x["lens"])
+            tstar = oracle.argmax(logits)
+            r = oracle.accept(topo.parent, wl.K, tok, tstar, x["lens"])
+            oracle.compact(x["Kc"], x["Vc"], x["lens"], r["accept_len"], r["path"], wl.K)
+            td = time.perf_counter()
+            cpu_times.append((tb - ta) + (td - tc))
+            acc_oracle.append(int(r["accept_len"][0]))
+            log("oracle step %d: %.2f s (accept_len %d)" % (s, cpu_times[-1], acc_oracle[-1]))
+        xd = {k: to_dev(v) for k, v in x.items() if k != "logits"}
+        xd["logits"] = to_dev(logits)
+        xd["lens0"] = xd["lens"].clone()
+        sets.append(xd)
+    torch.cuda.synchronize()
+    log("%d input sets on the GPU" % len(sets))
+
+    cfg = md.StepConfig(kind=md.MD_HEADS_MEDUSA, dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32,
+                        B=wl.B, M=wl.M, d=wl.d, V=wl.V, K=wl.K, k_per_head=wl.topk, parent=topo.parent,
+                        rank=topo.rank, Hq=wl.Hq, Hkv=wl.Hkv, hd=wl.hd, Lcap=wl.Lcap, max_len=wl.L_max)
+    step = md.MedusaStep(cfg)
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for a, b in ev:  # materialise the underlying hipEvent_t handles
+        a.record(stream)
+        b.record(stream)
+    torch.cuda.synchronize()
+
+    accepted = []
+
+    def one_step(i: int, timed_pair=None):
+        xd = sets[i % len(sets)]
+        xd["lens"].copy_(xd["lens0"])  # every step starts from the same cached length
+        if timed_pair is not None:
+            md.md_set_vocab_timing_events(timed_pair[0].cuda_event, timed_pair[1].cuda_event)
+        step.run(wd, xd)
+        if timed_pair is not None:
+            md.md_set_vocab_timing_events(None, None)
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        one_step(args.warmup + i, ev[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = t_start.elapsed_time(t_end)
+    ms_per_step = ms_total / args.steps
+    vocab_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    for xd in sets:  # one more pass to report the accepted lengths per set
+        pass
+    acc_len = step.accept_len.cpu().numpy().tolist()
+
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies done")
+
+    # algorithmic bytes: the vocabulary projections once plus h' once (float32)
+    vocab_bytes = wl.K * wl.V * wl.d * (2 if wl.dtype == "bf16" else 4) + wl.K * wl.M * wl.d * 4
+    achieved = vocab_bytes / (vocab_ms * 1e-3) / 1e9
+    esz = 2 if wl.dtype == "bf16" else 4
+    step_bytes = (md.md_heads_weight_bytes(0, 1 if esz == 2 else 0, wl.d, wl.V, wl.K)
+                  + 2 * wl.B * wl.Hkv * (wl.L_max + wl.N) * wl.hd * esz  # K and V of prefix + tree
+                  + 2 * wl.B * wl.N * wl.Hq * wl.hd * esz  # q in, attention out
+                  + wl.B * wl.N * wl.V * 4)  # verification logits
+    traffic = None
+    if os.path.exists(PMC_FILE):
+        with open(PMC_FILE) as f:
+            pmc = json.load(f)
+        if pmc.get("heads_hip_sha256") == file_sha(os.path.join(ROOT, "medusa_draft_heads_amd", "csrc", "heads.hip")) \
+                and pmc.get("workload") == args.workload:
+            traffic = pmc.get("hbm_bytes_per_launch")
+    cpu = None
+    if cpu_times:
+        cpu = {"value": round(1.0 / float(np.median(cpu_times)), 4), "unit": "steps/s", "cores": threads,
+               "kind": "oracle",
+               "sample": "%d whole oracle steps (heads, tree, attention, argmax, accept, compaction) on the same "
+                         "seeded inputs, median" % len(cpu_times)}
+    E = 1.0
+    run = 1.0
+    for ai in wl.a:
+        run *= ai
+        E += run
+    out = {
+        "metric": "Medusa tree-decode steps/s at 70B-shaped heads, batch 1; achieved HBM GB/s % peak",
+        "value": round(1000.0 / ms_per_step, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic (seeded Philox inputs, random-init heads of the workload's shape)",
+        "config": {"workload": wl.name, "batch": wl.B, "d": wl.d, "V": wl.V, "heads": wl.K, "topk": list(wl.topk),
+                   "tree_nodes": wl.N, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.hd, "L": wl.L_max,
+                   "input_sets": len(sets)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                     "kernel": "k_vocab_topk (vocabulary projection + per-head top-k)",
+                     "kernel_ms": round(vocab_ms, 4), "bytes_per_launch": vocab_bytes},
+        "step_hbm": {"bytes_per_step": step_bytes, "GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+                     "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "acceptance": {"last_step_accept_len": acc_len, "oracle_accept_len": acc_oracle, "E_closed_form": round(E, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,191 @@
+/*
+ * libmedusa -- the Medusa tree-decode step on AMD Instinct MI355X (gfx950).
+ *
+ * One decode step, as the pages describe it:
+ *   1. md_medusa_heads  K draft heads on the target's last hidden state, each a
+ *                       residual block h + SiLU(W h + b) followed by its own
+ *                       d x V vocabulary projection, reduced straight to each
+ *                       head's top-k (the logits never reach memory).
+ *                       ("Medusa heads versus separate draft model", sections
+ *                       "What each one is" and "Cost per step".) Hydra's
+ *                       sequentially dependent heads run one level per call
+ *                       (Hydra abstract and summary).
+ *   2. md_tree_build    the candidate tree: every node takes one entry of its
+ *                       head's top-k list at a fixed topology ("Trees").
+ *   3. md_tree_attention every tree node attends to the KV cache and to its
+ *                       own root path, all in one pass ("Trees": one pass with
+ *                       a tree attention mask).
+ *   4. md_tree_accept   the target's greedy choice per node, the deepest branch
+ *                       whose drafts all match it, and the move of that
+ *                       branch's cache entries next to the prefix ("Trees":
+ *                       the step advances along the branch that matches;
+ *                       "Acceptance": E counts the target's token plus the
+ *                       accepted drafts).
+ *
+ * Conventions for every call
+ *  - Pointers marked (device) are HIP device pointers; (host) are host memory.
+ *    The caller owns every buffer. The library allocates and frees nothing and
+ *    keeps no pointer past the call.
+ *  - `stream` is a hipStream_t (NULL: the null stream). Calls only enqueue
+ *    work and return; outputs are valid once the stream reaches that point.
+ *    No call synchronises the host.
+ *  - All argument checks run on the host before any HIP call. A non-zero
+ *    return means nothing was enqueued (except MD_EHIP, which reports a
+ *    failed launch). md_last_error() gives a thread-local description.
+ *  - Tensors are dense row-major (C order). dt selects the storage type of
+ *    activations, weights and the KV cache: MD_F32 or MD_BF16. Arithmetic is
+ *    float32 throughout.
+ *  - Inputs must be finite; NaN or Inf inputs give unspecified results.
+ *  - Calls that overlap on one workspace race; one workspace per stream.
+ */
+#ifndef MEDUSA_H
+#define MEDUSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MD_OK = 0,
+    MD_EINVAL = -1,       /* null pointer, non-positive size, malformed tree */
+    MD_EUNSUPPORTED = -2, /* a size outside what the kernels implement */
+    MD_ERANGE = -3,       /* lengths that do not fit the cache capacity */
+    MD_EWORKSPACE = -4,   /* workspace smaller than the *_workspace_bytes query */
+    MD_EHIP = -5          /* a HIP launch or runtime call failed */
+} md_status;
+
+typedef enum { MD_F32 = 0, MD_BF16 = 1 } md_dtype;
+typedef enum { MD_HEADS_MEDUSA = 0, MD_HEADS_HYDRA = 1 } md_heads_kind;
+
+#define MD_MAX_NODES 64 /* a tree fits one 64-lane wavefront and one 64-bit mask */
+#define MD_MAX_HEADS 8
+#define MD_MAX_TOPK 16
+
+/* A fixed tree topology (host memory, passed by pointer, copied per call).
+ * Node 0 is the root (the target's own next token). For n >= 1, parent[n] is
+ * an earlier node (0 <= parent[n] < n), depths never decrease with the node
+ * index (breadth-first numbering), and rank[n] is the entry of the depth-j
+ * head's top-k list that node n carries (j = depth of n). Siblings carry
+ * distinct ranks. parent[0] = -1, rank[0] = 0. Entries at n >= `n` are
+ * ignored. */
+typedef struct {
+    int32_t n;
+    int8_t parent[MD_MAX_NODES];
+    int8_t rank[MD_MAX_NODES];
+} md_tree;
+
+/* Checks a topology against K heads with top-k widths k_per_head[K] (host):
+ * 1 <= n <= 64, parent order, breadth-first numbering, depth <= K, distinct
+ * sibling ranks, rank < k_per_head[depth - 1]. Host only; returns MD_OK or
+ * MD_EINVAL. */
+int md_tree_validate(const md_tree* t, int K, const int32_t* k_per_head);
+
+/* Bytes of weights one call of the heads reads: K heads of (d x din residual
+ * matrix + d bias + V x d projection), din = d (Medusa) or 2d (Hydra), at the
+ * storage size of dt ("Cost per step": 1,117.8M parameters per head at
+ * d = 8,192, V = 128,256). Returns -1 on invalid arguments. */
+int64_t md_heads_weight_bytes(int kind, int dt, int d, int V, int K);
+
+/* Workspace the heads need for M rows (Medusa) or the largest level's rows
+ * (Hydra: B requests times the most parents on one level, at most 64 * B). */
+size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, int kmax);
+
+/* The draft heads and their top-k lists.
+ *
+ * Medusa (kind = MD_HEADS_MEDUSA, level = 0): for every row m < M of
+ * h [M][d] (device, dt) and every head k < K:
+ *     h'_k[m] = h[m] + SiLU(W[k] h[m] + b[k])      W [K][d][d], b [K][d]
+ *     logit   = U[k] h'_k[m]                       U [K][V][d]   (device, dt)
+ * topk_idx[m][k][j], topk_val[m][k][j] (device int32 / float32, [M][K][kmax])
+ * receive the k_per_head[k] best logits ordered by value descending, equal
+ * values by index ascending; entries j >= k_per_head[k] are -1 / -inf.
+ * h' enters the projection in float32.
+ *
+ * Hydra (kind = MD_HEADS_HYDRA, level = i in 1..K): head i-1 only, one row per
+ * (request b < M, parent p at depth i-1 that has children in `tree`, in node
+ * order): x = [h[b] ; E[tok(p)]] with tok(root) = root_tok[b] and
+ * tok(p) = tree_tok[b][p] otherwise; h' = h[b] + SiLU(W[i-1] x + b[i-1]) with
+ * W [K][d][2d]; logits = U[i-1] h'. Row r = b * P_i + (index of p among the
+ * level's parents). Outputs are [rows][1][kmax]. E [V][d] (device, dt),
+ * root_tok [M], tree_tok [M][tree->n] (device int32); tree (host).
+ *
+ * b may be NULL (zero bias). h_res (device float32, optional) receives h'
+ * as [K][M][d] (Medusa) or [rows][d] (Hydra). ws (device) must hold
+ * md_heads_workspace_bytes(...). k_per_head (host) has K entries in [1, 16],
+ * kmax = their maximum. Requires d % 8 == 0, K <= 8. */
+int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t* k_per_head, int level,
+                    const md_tree* tree, const void* h, const void* W, const void* b, const void* U,
+                    const void* E, const int32_t* root_tok, const int32_t* tree_tok, int32_t* topk_idx,
+                    float* topk_val, float* h_res, void* ws, size_t ws_bytes, void* stream);
+
+/* The candidate tree's tokens and positions ("Trees").
+ *
+ * Medusa (kind = MD_HEADS_MEDUSA, level = 0): tree_tok[b][n] = root_tok[b] for
+ * the root, else topk_idx[src_row[b]][depth(n) - 1][rank(n)] with topk_idx
+ * [M][K][kmax]; tree_pos[b][n] = lens[b] + depth(n). A src_row entry outside
+ * [0, M) yields -1 tokens for that request's non-root nodes.
+ * Hydra (kind = MD_HEADS_HYDRA, level = i in 1..K): fills the depth-i nodes
+ * from the level's lists [rows][1][kmax] (each node reads its own parent's
+ * row, as md_medusa_heads numbers them); level 1 also writes the root token
+ * and every position. M and src_row are ignored for Hydra (src_row may be
+ * NULL). All arrays are device int32; tree_tok, tree_pos are [B][tree->n]. */
+int md_tree_build(const md_tree* tree, int kind, int B, int M, int K, int kmax, int level, const int32_t* topk_idx,
+                  const int32_t* src_row, const int32_t* root_tok, const int32_t* lens, int32_t* tree_tok,
+                  int32_t* tree_pos, void* stream);
+
+/* Workspace for md_tree_attention at these sizes (max_len bounds lens). */
+size_t md_attention_workspace_bytes(int dt, int B, int N, int Hq, int Hkv, int hd, int max_len);
+
+/* Tree-masked attention of every node over the KV cache, in one pass.
+ *
+ * q [B][N][Hq][hd], out [B][N][Hq][hd] (device, dt); Kc, Vc [B][Hkv][Lcap][hd]
+ * (device, dt) hold the cached keys/values in slots [0, lens[b]) and the tree
+ * nodes' own keys/values in slots lens[b] + n. Node n, query head h attends
+ * to slots [0, lens[b]) and to lens[b] + j for every j that is n or an
+ * ancestor of n; it reads kv head h / (Hq / Hkv). Weights are
+ * softmax(scale * q.k). lens (device int32 [B]) must lie in [0, max_len]
+ * with max_len + N <= Lcap (values above max_len are read as max_len).
+ * Requires Hq % Hkv == 0, hd in {64, 128}. No positional encoding is applied:
+ * q and k are taken as already encoded. */
+int md_tree_attention(const md_tree* tree, int dt, int B, int Hq, int Hkv, int hd, int Lcap, int max_len,
+                      const void* q, const void* Kc, const void* Vc, const int32_t* lens, float scale, void* out,
+                      void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace for md_tree_accept. */
+size_t md_accept_workspace_bytes(int B, int N, int V);
+
+/* Greedy verification, acceptance and cache compaction.
+ *
+ * t*(b, n) = the first index of the maximum of logits[b][n][:] (device
+ * float32 [B][N][V]). A non-root node c matches when tree_tok[b][c] equals
+ * t* at its parent; a node is accepted when it and all its non-root
+ * ancestors match. With a the deepest accepted node (lowest index among
+ * equals): accept_len[b] = depth(a) + 1, path[b][j] = a's ancestor at depth j
+ * (-1 padded to K + 1), next_tok[b] = t*(b, a), compact_src[b][j] =
+ * lens[b] + path[b][j] (-1 padded). Then, for j < accept_len[b], cache slot
+ * lens[b] + j of K and V takes what slot lens[b] + path[b][j] held before
+ * the call (all kv heads), and lens[b] grows by accept_len[b]. Slots below
+ * lens[b] are untouched. K is the number of heads (the tree's depth <= K).
+ * Outputs are device int32: accept_len, next_tok [B]; path, compact_src
+ * [B][K + 1]. Kc, Vc, lens are updated in place. */
+int md_tree_accept(const md_tree* tree, int dt, int B, int K, int V, int Hkv, int hd, int Lcap,
+                   const float* logits, const int32_t* tree_tok, void* Kc, void* Vc, int32_t* lens,
+                   int32_t* accept_len, int32_t* path, int32_t* next_tok, int32_t* compact_src, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/* Timing hook for profiling: when both are non-NULL hipEvent_t handles, every
+ * later md_medusa_heads call on this thread records `start` on its stream
+ * right before its vocabulary-projection kernel and `stop` right after it.
+ * Pass NULL, NULL to stop. */
+int md_set_vocab_timing_events(void* start, void* stop);
+
+/* Thread-local text for the last non-MD_OK return on this thread. */
+const char* md_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MEDUSA_H */

@@ -1,0 +1,176 @@
+"""ctypes binding of libmedusa (include/medusa.h): argument marshalling only.
+
+Every function carries the C name and forwards to the C call; tensors are
+passed as raw device pointers and the stream as torch's current HIP stream.
+A non-zero status raises MedusaError with the library's message. There is no
+fallback: without the built library every call fails loudly.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmedusa.so")
+
+MD_OK, MD_EINVAL, MD_EUNSUPPORTED, MD_ERANGE, MD_EWORKSPACE, MD_EHIP = 0, -1, -2, -3, -4, -5
+MD_F32, MD_BF16 = 0, 1
+MD_HEADS_MEDUSA, MD_HEADS_HYDRA = 0, 1
+MD_MAX_NODES, MD_MAX_HEADS, MD_MAX_TOPK = 64, 8, 16
+
+EXPORTS = (
+    "md_tree_validate", "md_heads_weight_bytes", "md_heads_workspace_bytes", "md_medusa_heads", "md_tree_build",
+    "md_attention_workspace_bytes", "md_tree_attention", "md_accept_workspace_bytes", "md_tree_accept",
+    "md_set_vocab_timing_events", "md_last_error",
+)
+
+
+class MedusaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__("libmedusa status %d: %s" % (status, msg))
+        self.status = status
+
+
+class md_tree(ctypes.Structure):
+    _fields_ = [("n", ctypes.c_int32), ("parent", ctypes.c_int8 * MD_MAX_NODES), ("rank", ctypes.c_int8 * MD_MAX_NODES)]
+
+
+def make_tree(parent: Sequence[int], rank: Sequence[int]) -> md_tree:
+    t = md_tree()
+    t.n = len(parent)
+    for i, (p, r) in enumerate(zip(parent, rank)):
+        t.parent[i] = p
+        t.rank[i] = r
+    return t
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libmedusa.so is not built (run: python -m medusa_draft_heads_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        i, i64, sz, f, vp = ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float, ctypes.c_void_p
+        tp = ctypes.POINTER(md_tree)
+        sig = {
+            "md_tree_validate": ([tp, i, vp], i),
+            "md_heads_weight_bytes": ([i, i, i, i, i], i64),
+            "md_heads_workspace_bytes": ([i, i, i, i, i, i, i], sz),
+            "md_medusa_heads": ([i, i, i, i, i, i, vp, i, tp] + [vp] * 11 + [sz, vp], i),
+            "md_tree_build": ([tp, i, i, i, i, i, i] + [vp] * 6 + [vp], i),
+            "md_attention_workspace_bytes": ([i, i, i, i, i, i, i], sz),
+            "md_tree_attention": ([tp, i, i, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, sz, vp], i),
+            "md_accept_workspace_bytes": ([i, i, i], sz),
+            "md_tree_accept": ([tp, i, i, i, i, i, i, i] + [vp] * 10 + [sz, vp], i),
+            "md_set_vocab_timing_events": ([vp, vp], i),
+            "md_last_error": ([], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _lib = L
+    return _lib
+
+
+def _p(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is not None:
+        return stream
+    import torch
+
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(rc: int) -> None:
+    if rc != MD_OK:
+        raise MedusaError(rc, lib().md_last_error().decode())
+
+
+def dtype_code(t) -> int:
+    import torch
+
+    if t.dtype == torch.float32:
+        return MD_F32
+    if t.dtype == torch.bfloat16:
+        return MD_BF16
+    raise TypeError("storage dtype must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def md_tree_validate(tree: md_tree, K: int, k_per_head: Optional[Sequence[int]] = None) -> int:
+    kp = (ctypes.c_int32 * K)(*k_per_head) if k_per_head is not None else None
+    return lib().md_tree_validate(ctypes.byref(tree), K, ctypes.cast(kp, ctypes.c_void_p) if kp is not None else None)
+
+
+def md_last_error() -> str:
+    return lib().md_last_error().decode()
+
+
+def md_heads_weight_bytes(kind: int, dt: int, d: int, V: int, K: int) -> int:
+    return int(lib().md_heads_weight_bytes(kind, dt, d, V, K))
+
+
+def md_heads_workspace_bytes(kind: int, dt: int, M: int, d: int, V: int, K: int, kmax: int) -> int:
+    return int(lib().md_heads_workspace_bytes(kind, dt, M, d, V, K, kmax))
+
+
+def md_attention_workspace_bytes(dt: int, B: int, N: int, Hq: int, Hkv: int, hd: int, max_len: int) -> int:
+    return int(lib().md_attention_workspace_bytes(dt, B, N, Hq, Hkv, hd, max_len))
+
+
+def md_accept_workspace_bytes(B: int, N: int, V: int) -> int:
+    return int(lib().md_accept_workspace_bytes(B, N, V))
+
+
+def md_medusa_heads(kind, dt, M, d, V, K, k_per_head, level, tree, h, W, b, U, E, root_tok, tree_tok, topk_idx,
+                    topk_val, h_res, ws, ws_bytes=None, stream=None) -> None:
+    kp = (ctypes.c_int32 * K)(*k_per_head)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    rc = lib().md_medusa_heads(kind, dt, M, d, V, K, ctypes.cast(kp, ctypes.c_void_p), level,
+                               ctypes.byref(tree) if tree is not None else None, _p(h), _p(W), _p(b), _p(U), _p(E),
+                               _p(root_tok), _p(tree_tok), _p(topk_idx), _p(topk_val), _p(h_res), _p(ws), ws_bytes,
+                               _stream(stream))
+    _check(rc)
+
+
+def md_tree_build(tree, kind, B, M, K, kmax, level, topk_idx, src_row, root_tok, lens, tree_tok, tree_pos,
+                  stream=None) -> None:
+    rc = lib().md_tree_build(ctypes.byref(tree), kind, B, M, K, kmax, level, _p(topk_idx), _p(src_row),
+                             _p(root_tok), _p(lens), _p(tree_tok), _p(tree_pos), _stream(stream))
+    _check(rc)
+
+
+def md_tree_attention(tree, dt, B, Hq, Hkv, hd, Lcap, max_len, q, Kc, Vc, lens, scale, out, ws, ws_bytes=None,
+                      stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    rc = lib().md_tree_attention(ctypes.byref(tree), dt, B, Hq, Hkv, hd, Lcap, max_len, _p(q), _p(Kc), _p(Vc),
+                                 _p(lens), float(scale), _p(out), _p(ws), ws_bytes, _stream(stream))
+    _check(rc)
+
+
+def md_tree_accept(tree, dt, B, K, V, Hkv, hd, Lcap, logits, tree_tok, Kc, Vc, lens, accept_len, path, next_tok,
+                   compact_src, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    rc = lib().md_tree_accept(ctypes.byref(tree), dt, B, K, V, Hkv, hd, Lcap, _p(logits), _p(tree_tok), _p(Kc),
+                              _p(Vc), _p(lens), _p(accept_len), _p(path), _p(next_tok), _p(compact_src), _p(ws),
+                              ws_bytes, _stream(stream))
+    _check(rc)
+
+
+def md_set_vocab_timing_events(start, stop) -> None:
+    """start/stop: raw hipEvent_t handles (ints) or None."""
+    _check(lib().md_set_vocab_timing_events(start, stop))

@@ -1,0 +1,278 @@
+// libmedusa C-ABI: argument checks, tree expansion and kernel dispatch.
+//
+// Every check below runs on the host before any HIP call, so a rejected call
+// enqueues nothing. The library holds no device memory and no state besides a
+// thread-local error string and the optional thread-local timing events.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "../../include/medusa.h"
+#include "md_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+thread_local hipEvent_t g_ev0 = nullptr, g_ev1 = nullptr;
+
+int fail(int code, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return code;
+}
+
+int hip_status(hipError_t e, const char* where) {
+    if (e == hipSuccess) return MD_OK;
+    return fail(MD_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+// Checks the topology and expands it: depths, ancestor sets, and for Hydra
+// the parents of every level. k_per_head may be NULL (ranks unchecked).
+int expand_tree(const md_tree* t, int K, const int32_t* k_per_head, DevTree* out) {
+    if (!t) return fail(MD_EINVAL, "tree is NULL");
+    if (t->n < 1 || t->n > MD_MAX_NODES) return fail(MD_EINVAL, "tree has %d nodes (1..64 supported)", t->n);
+    if (K < 1 || K > MD_MAX_HEADS) return fail(MD_EINVAL, "K = %d heads (1..8 supported)", K);
+    if (t->parent[0] != -1 || t->rank[0] != 0) return fail(MD_EINVAL, "node 0 must be the root (parent -1, rank 0)");
+    DevTree d;
+    memset(&d, 0, sizeof(d));
+    d.n = t->n;
+    d.parent[0] = -1;
+    d.depth[0] = 0;
+    d.rank[0] = 0;
+    d.anc[0] = 1ull;
+    int maxd = 0;
+    for (int n = 1; n < t->n; ++n) {
+        const int p = t->parent[n];
+        if (p < 0 || p >= n) return fail(MD_EINVAL, "node %d: parent %d must precede it", n, p);
+        const int dep = d.depth[p] + 1;
+        if (dep < d.depth[n - 1]) return fail(MD_EINVAL, "node %d: nodes must be numbered breadth-first", n);
+        if (dep > K) return fail(MD_EINVAL, "node %d: depth %d exceeds the %d heads", n, dep, K);
+        const int r = t->rank[n];
+        if (r < 0 || r >= MD_MAX_TOPK) return fail(MD_EINVAL, "node %d: rank %d outside [0, 16)", n, r);
+        if (k_per_head && r >= k_per_head[dep - 1])
+            return fail(MD_EINVAL, "node %d: rank %d but head %d keeps only %d", n, r, dep, k_per_head[dep - 1]);
+        for (int s = 1; s < n; ++s)
+            if (t->parent[s] == p && t->rank[s] == r) return fail(MD_EINVAL, "nodes %d and %d: siblings share rank %d", s, n, r);
+        d.parent[n] = (int8_t)p;
+        d.depth[n] = (int8_t)dep;
+        d.rank[n] = (int8_t)r;
+        d.anc[n] = d.anc[p] | (1ull << n);
+        if (dep > maxd) maxd = dep;
+    }
+    d.max_depth = maxd;
+    // parents per level, in node order
+    int off = 0;
+    for (int i = 0; i < 64; ++i) d.prow[i] = -1;
+    for (int lvl = 1; lvl <= 9; ++lvl) {
+        d.level_off[lvl] = off;
+        if (lvl <= maxd) {
+            int cnt = 0;
+            for (int p = 0; p < t->n; ++p) {
+                if (d.depth[p] != lvl - 1) continue;
+                bool has_child = false;
+                for (int c = p + 1; c < t->n; ++c)
+                    if (d.parent[c] == p) has_child = true;
+                if (!has_child) continue;
+                d.lp[off] = (int8_t)p;
+                d.prow[p] = (int8_t)cnt;
+                ++off;
+                ++cnt;
+            }
+        }
+    }
+    d.level_off[0] = 0;
+    if (out) *out = d;
+    return MD_OK;
+}
+
+int check_dt(int dt) { return (dt == MD_F32 || dt == MD_BF16) ? MD_OK : fail(MD_EINVAL, "dt = %d (MD_F32 or MD_BF16)", dt); }
+
+}  // namespace
+
+extern "C" {
+
+const char* md_last_error(void) { return g_err.c_str(); }
+
+int md_tree_validate(const md_tree* t, int K, const int32_t* k_per_head) { return expand_tree(t, K, k_per_head, nullptr); }
+
+int64_t md_heads_weight_bytes(int kind, int dt, int d, int V, int K) {
+    if ((kind != MD_HEADS_MEDUSA && kind != MD_HEADS_HYDRA) || (dt != MD_F32 && dt != MD_BF16) || d < 1 || V < 1 ||
+        K < 1)
+        return -1;
+    const int64_t din = kind == MD_HEADS_HYDRA ? 2LL * d : (int64_t)d;
+    const int64_t per_head = (int64_t)d * din + d + (int64_t)V * d;
+    return (int64_t)K * per_head * (dt == MD_F32 ? 4 : 2);
+}
+
+size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, int kmax) {
+    (void)dt;
+    (void)V;
+    if (M <= 0 || d <= 0 || K <= 0 || kmax <= 0) return 0;
+    if (kind == MD_HEADS_HYDRA) return heads_ws_bound(M * MD_MAX_NODES, d, 1, kmax);
+    return heads_ws_bound(M, d, K, kmax);
+}
+
+int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t* k_per_head, int level,
+                    const md_tree* tree, const void* h, const void* W, const void* b, const void* U, const void* E,
+                    const int32_t* root_tok, const int32_t* tree_tok, int32_t* topk_idx, float* topk_val,
+                    float* h_res, void* ws, size_t ws_bytes, void* stream) {
+    if (kind != MD_HEADS_MEDUSA && kind != MD_HEADS_HYDRA) return fail(MD_EINVAL, "kind = %d", kind);
+    if (check_dt(dt)) return MD_EINVAL;
+    if (M < 0) return fail(MD_EINVAL, "M = %d", M);
+    if (K < 1 || K > MD_MAX_HEADS) return fail(MD_EINVAL, "K = %d heads (1..8 supported)", K);
+    if (!k_per_head) return fail(MD_EINVAL, "k_per_head is NULL");
+    int kmax = 0;
+    for (int i = 0; i < K; ++i) {
+        if (k_per_head[i] < 1 || k_per_head[i] > MD_MAX_TOPK)
+            return fail(MD_EINVAL, "k_per_head[%d] = %d (1..16 supported)", i, k_per_head[i]);
+        if (k_per_head[i] > kmax) kmax = k_per_head[i];
+    }
+    if (d < 8 || d % 8) return fail(MD_EUNSUPPORTED, "d = %d (a positive multiple of 8 is required)", d);
+    const int din = kind == MD_HEADS_HYDRA ? 2 * d : d;
+    if ((size_t)din * 4 > 160 * 1024) return fail(MD_EUNSUPPORTED, "input width %d exceeds one LDS row buffer", din);
+    if (V < kmax) return fail(MD_EINVAL, "V = %d is smaller than the widest top-k %d", V, kmax);
+    if (M == 0) return MD_OK;
+    if (!h || !W || !U || !topk_idx || !topk_val || !ws) return fail(MD_EINVAL, "a required pointer is NULL");
+
+    HeadsArgs a;
+    memset(&a, 0, sizeof(a));
+    DevTree dt_tree;
+    const DevTree* tp = nullptr;
+    a.kind = kind;
+    a.dt = dt;
+    a.d = d;
+    a.din = din;
+    a.V = V;
+    a.kmax = kmax;
+    a.level = level;
+    a.h = h;
+    a.W = W;
+    a.b = b;
+    a.U = U;
+    a.E = E;
+    a.root_tok = root_tok;
+    a.tree_tok = tree_tok;
+    a.topk_idx = topk_idx;
+    a.topk_val = topk_val;
+    a.h_res = h_res;
+    a.ws = ws;
+    size_t need;
+    if (kind == MD_HEADS_MEDUSA) {
+        if (level != 0) return fail(MD_EINVAL, "Medusa heads take level 0 (got %d)", level);
+        a.M = M;
+        a.B = M;
+        a.nh = K;
+        a.head0 = 0;
+        for (int i = 0; i < K; ++i) a.kk[i] = k_per_head[i];
+        need = heads_ws_bytes(M, d, d, K, kmax);
+    } else {
+        if (level < 1 || level > K) return fail(MD_EINVAL, "Hydra level %d outside 1..%d", level, K);
+        int rc = expand_tree(tree, K, k_per_head, &dt_tree);
+        if (rc) return rc;
+        if (!E || !root_tok) return fail(MD_EINVAL, "Hydra heads need E and root_tok");
+        if (level >= 2 && !tree_tok) return fail(MD_EINVAL, "Hydra level %d needs tree_tok", level);
+        const int P = dt_tree.level_off[level + 1] - dt_tree.level_off[level];
+        a.M = M * P;
+        a.B = M;
+        a.nh = 1;
+        a.head0 = level - 1;
+        a.kk[0] = k_per_head[level - 1];
+        tp = &dt_tree;
+        if (P == 0) return MD_OK;  // nothing at this depth
+        need = heads_ws_bytes(a.M, d, din, 1, kmax);
+    }
+    if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return hip_status(heads_launch(a, tp, (hipStream_t)stream, g_ev0, g_ev1), "md_medusa_heads");
+}
+
+int md_tree_build(const md_tree* tree, int kind, int B, int M, int K, int kmax, int level, const int32_t* topk_idx,
+                  const int32_t* src_row, const int32_t* root_tok, const int32_t* lens, int32_t* tree_tok,
+                  int32_t* tree_pos, void* stream) {
+    DevTree t;
+    int rc = expand_tree(tree, K, nullptr, &t);
+    if (rc) return rc;
+    if (kind != MD_HEADS_MEDUSA && kind != MD_HEADS_HYDRA) return fail(MD_EINVAL, "kind = %d", kind);
+    if (B < 0 || kmax < 1 || kmax > MD_MAX_TOPK) return fail(MD_EINVAL, "B = %d, kmax = %d", B, kmax);
+    for (int n = 1; n < t.n; ++n)
+        if (t.rank[n] >= kmax) return fail(MD_EINVAL, "node %d: rank %d but lists hold %d", n, t.rank[n], kmax);
+    if (kind == MD_HEADS_MEDUSA) {
+        if (level != 0) return fail(MD_EINVAL, "Medusa trees build all levels at once (level 0)");
+        if (M < 1) return fail(MD_EINVAL, "M = %d", M);
+        if (B > 0 && !src_row) return fail(MD_EINVAL, "src_row is NULL");
+    } else {
+        if (level < 1 || level > K) return fail(MD_EINVAL, "Hydra level %d outside 1..%d", level, K);
+        if (level > t.max_depth) return MD_OK;
+    }
+    if (B == 0) return MD_OK;
+    if (!topk_idx || !root_tok || !lens || !tree_tok || !tree_pos) return fail(MD_EINVAL, "a required pointer is NULL");
+    return hip_status(tree_build_launch(t, kind, B, M, K, kmax, level, topk_idx, src_row, root_tok, lens, tree_tok,
+                                        tree_pos, (hipStream_t)stream),
+                      "md_tree_build");
+}
+
+size_t md_attention_workspace_bytes(int dt, int B, int N, int Hq, int Hkv, int hd, int max_len) {
+    if (B <= 0 || N <= 0 || Hq <= 0 || Hkv <= 0 || hd <= 0 || max_len < 0 || Hq % Hkv) return 0;
+    return attention_ws_bytes(dt, B, N, Hq, Hkv, hd, max_len);
+}
+
+int md_tree_attention(const md_tree* tree, int dt, int B, int Hq, int Hkv, int hd, int Lcap, int max_len,
+                      const void* q, const void* Kc, const void* Vc, const int32_t* lens, float scale, void* out,
+                      void* ws, size_t ws_bytes, void* stream) {
+    DevTree t;
+    int rc = expand_tree(tree, MD_MAX_HEADS, nullptr, &t);
+    if (rc) return rc;
+    if (check_dt(dt)) return MD_EINVAL;
+    if (B < 0 || Hq < 1 || Hkv < 1) return fail(MD_EINVAL, "B = %d, Hq = %d, Hkv = %d", B, Hq, Hkv);
+    if (Hq % Hkv) return fail(MD_EINVAL, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
+    if (hd != 64 && hd != 128) return fail(MD_EUNSUPPORTED, "head_dim %d (64 or 128 supported)", hd);
+    if (max_len < 0) return fail(MD_EINVAL, "max_len = %d", max_len);
+    if ((int64_t)max_len + t.n > Lcap) return fail(MD_ERANGE, "max_len %d + %d nodes exceeds Lcap %d", max_len, t.n, Lcap);
+    if (B == 0) return MD_OK;
+    if (!q || !Kc || !Vc || !lens || !out || !ws) return fail(MD_EINVAL, "a required pointer is NULL");
+    const size_t need = attention_ws_bytes(dt, B, t.n, Hq, Hkv, hd, max_len);
+    if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return hip_status(attention_launch(t, dt, B, Hq, Hkv, hd, Lcap, max_len, q, Kc, Vc, lens, scale, out, ws,
+                                       (hipStream_t)stream),
+                      "md_tree_attention");
+}
+
+size_t md_accept_workspace_bytes(int B, int N, int V) {
+    if (B <= 0 || N <= 0 || V <= 0) return 0;
+    return accept_ws_bytes(B, N, V);
+}
+
+int md_tree_accept(const md_tree* tree, int dt, int B, int K, int V, int Hkv, int hd, int Lcap, const float* logits,
+                   const int32_t* tree_tok, void* Kc, void* Vc, int32_t* lens, int32_t* accept_len, int32_t* path,
+                   int32_t* next_tok, int32_t* compact_src, void* ws, size_t ws_bytes, void* stream) {
+    DevTree t;
+    int rc = expand_tree(tree, K, nullptr, &t);
+    if (rc) return rc;
+    if (check_dt(dt)) return MD_EINVAL;
+    if (B < 0 || V < 1 || Hkv < 1 || hd < 1) return fail(MD_EINVAL, "B = %d, V = %d, Hkv = %d, hd = %d", B, V, Hkv, hd);
+    if (hd > 256) return fail(MD_EUNSUPPORTED, "head_dim %d (at most 256)", hd);
+    if (Lcap < t.n) return fail(MD_ERANGE, "Lcap %d is smaller than the tree (%d nodes)", Lcap, t.n);
+    if (B == 0) return MD_OK;
+    if (!logits || !tree_tok || !Kc || !Vc || !lens || !accept_len || !path || !next_tok || !compact_src || !ws)
+        return fail(MD_EINVAL, "a required pointer is NULL");
+    const size_t need = accept_ws_bytes(B, t.n, V);
+    if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return hip_status(accept_launch(t, dt, B, K, V, Hkv, hd, Lcap, logits, tree_tok, Kc, Vc, lens, accept_len, path,
+                                    next_tok, compact_src, ws, (hipStream_t)stream),
+                      "md_tree_accept");
+}
+
+int md_set_vocab_timing_events(void* start, void* stop) {
+    if ((start == nullptr) != (stop == nullptr)) return fail(MD_EINVAL, "pass two events or none");
+    g_ev0 = (hipEvent_t)start;
+    g_ev1 = (hipEvent_t)stop;
+    return MD_OK;
+}
+
+}  // extern "C"

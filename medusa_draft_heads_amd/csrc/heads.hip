@@ -1,0 +1,493 @@
+// Draft heads on the hidden state, reduced straight to per-head top-k lists.
+//
+// "Medusa heads versus separate draft model", sections "What each one is" and
+// "Cost per step": a head is a residual block h' = h + SiLU(W h + b) (W is
+// d x d) followed by the head's own d x V vocabulary projection, and at batch
+// 1 its cost is the bytes it reads. "Trees": the step keeps only the best few
+// candidates of each head. Hydra (abstract; study.space summary): each head
+// also sees the token speculated before it, x = [h ; E[parent token]] with W
+// of size d x 2d.
+//
+// GEMV path, for a handful of rows (M <= 4 per pass). Every weight row is
+// streamed from HBM exactly once per pass with 16-byte non-temporal loads
+// (64 lanes x 16 B = 1 KiB per wave instruction, fully coalesced); the
+// activations sit in LDS as float32; each wave keeps RPW rows in flight and
+// unrolls the column loop so ~16 loads are outstanding per wave. The dot
+// products end in a butterfly reduction that leaves the same bits in every
+// lane, so the top-k update is wave-uniform: lanes 0..k-1 hold the sorted
+// list in registers and an insertion is one ballot plus one shift. Logits are
+// never written; each wave leaves its k best (value, index) pairs, and a merge
+// kernel reduces the lists of all waves of a head.
+#include <math.h>
+
+#include "md_internal.h"
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int RPW = 4;     // weight rows in flight per wave
+constexpr int UNROLL = 4;  // column steps per loop iteration
+constexpr int BLOCK = 256;
+constexpr int NWAVE = BLOCK / MD_WAVE;
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ float ldf(const float* p, int64_t i) { return p[i]; }
+__device__ __forceinline__ float ldf(const uint16_t* p, int64_t i) { return __uint_as_float((uint32_t)p[i] << 16); }
+
+// 16 bytes of weights: loaded raw (non-temporal), widened to float32 at use.
+template <typename T>
+struct Chunk;
+template <>
+struct Chunk<uint16_t> {
+    static constexpr int N = 8;
+    typedef u32x4 Raw;
+    __device__ __forceinline__ static Raw load(const uint16_t* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    }
+    __device__ __forceinline__ static float at(const Raw& v, int e) {
+        const uint32_t w = e < 2 ? v.x : (e < 4 ? v.y : (e < 6 ? v.z : v.w));
+        return (e & 1) ? bf_hi(w) : bf_lo(w);
+    }
+};
+template <>
+struct Chunk<float> {
+    static constexpr int N = 4;
+    typedef f32x4 Raw;
+    __device__ __forceinline__ static Raw load(const float* p) {
+        return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    }
+    __device__ __forceinline__ static float at(const Raw& v, int e) {
+        return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
+    }
+};
+
+// VEC consecutive float32 activations from LDS (16-byte aligned).
+template <int VEC>
+__device__ __forceinline__ void lds_vec(const float* p, float (&x)[VEC]) {
+#pragma unroll
+    for (int e = 0; e < VEC; e += 4) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(p + e);
+        x[e] = v.x;
+        x[e + 1] = v.y;
+        x[e + 2] = v.z;
+        x[e + 3] = v.w;
+    }
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, MD_WAVE);
+    return v;
+}
+
+// Total order of candidates: larger value first, equal values by lower index.
+__device__ __forceinline__ bool ranks_above(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
+
+// Sorted list in lanes 0..k-1 (lv, li); insert the wave-uniform candidate (x, xi).
+__device__ __forceinline__ void list_insert(float& lv, int& li, float x, int xi, int k, int lane) {
+    const bool above = lane < k && ranks_above(lv, li, x, xi);
+    const int pos = __popcll(__ballot(above));
+    if (pos >= k) return;
+    const float pv = __shfl_up(lv, 1, MD_WAVE);
+    const int pi = __shfl_up(li, 1, MD_WAVE);
+    if (lane == pos) {
+        lv = x;
+        li = xi;
+    } else if (lane > pos && lane < k) {
+        lv = pv;
+        li = pi;
+    }
+}
+
+// acc[rr][m] (per lane, partial) = sum over this lane's columns of
+// row(r + rr)[c] * xs[m][c]; rows past nvalid repeat the last valid row.
+template <typename T, int MR>
+__device__ __forceinline__ void rows_dot(const T* __restrict__ base, int64_t stride, int r, int nvalid,
+                                         const float* __restrict__ xs, int ncols, int lane,
+                                         float (&acc)[RPW][MR]) {
+    typedef Chunk<T> C;
+    constexpr int VEC = C::N;
+    constexpr int STEP = MD_WAVE * VEC;
+    const T* rp[RPW];
+#pragma unroll
+    for (int rr = 0; rr < RPW; ++rr) {
+        rp[rr] = base + (int64_t)(r + (rr < nvalid ? rr : nvalid - 1)) * stride;
+#pragma unroll
+        for (int m = 0; m < MR; ++m) acc[rr][m] = 0.f;
+    }
+    int c = lane * VEC;
+    for (; c + (UNROLL - 1) * STEP < ncols; c += UNROLL * STEP) {
+        typename C::Raw w[UNROLL][RPW];
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u)
+#pragma unroll
+            for (int rr = 0; rr < RPW; ++rr) w[u][rr] = C::load(rp[rr] + c + u * STEP);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                float x[VEC];
+                lds_vec<VEC>(xs + m * ncols + c + u * STEP, x);
+#pragma unroll
+                for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+                    for (int e = 0; e < VEC; ++e) acc[rr][m] = fmaf(C::at(w[u][rr], e), x[e], acc[rr][m]);
+            }
+        }
+    }
+    for (; c < ncols; c += STEP) {
+        typename C::Raw w[RPW];
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) w[rr] = C::load(rp[rr] + c);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+            float x[VEC];
+            lds_vec<VEC>(xs + m * ncols + c, x);
+#pragma unroll
+            for (int rr = 0; rr < RPW; ++rr)
+#pragma unroll
+                for (int e = 0; e < VEC; ++e) acc[rr][m] = fmaf(C::at(w[rr], e), x[e], acc[rr][m]);
+        }
+    }
+}
+
+// Where a row's activation comes from.
+struct RowSrc {
+    int kind;  // 0: x = h[m]; 1 (Hydra): x = [h[b] ; E[tok(parent)]]
+    int P;     // Hydra: rows per request at this level
+    int N;     // tree nodes
+    int V;     // vocabulary (token range for the E gather)
+    int8_t parents[64];
+    const void* h;
+    const void* E;
+    const int32_t* root_tok;
+    const int32_t* tree_tok;
+};
+
+struct KK {
+    int v[8];
+};
+
+// hres[hh][m][r] = x_m[r] + SiLU(sum_c W[head0+hh][r][c] x_m[c] + b[head0+hh][r])
+template <typename T, int MR>
+__global__ __launch_bounds__(BLOCK) void k_residual(const T* __restrict__ W, const T* __restrict__ bias, RowSrc src,
+                                                    int M, int m0, int d, int din, int nh, int head0,
+                                                    float* __restrict__ hres, float* __restrict__ hres_out) {
+    extern __shared__ float xs[];  // [MR][din]
+    const int mr = min(MR, M - m0);
+    const T* h = reinterpret_cast<const T*>(src.h);
+    for (int i = threadIdx.x; i < MR * din; i += BLOCK) {
+        const int mm = i / din, c = i - (i / din) * din;
+        float v = 0.f;
+        if (mm < mr) {
+            const int m = m0 + mm;
+            if (src.kind == 0) {
+                v = ldf(h, (int64_t)m * d + c);
+            } else {
+                const int b = m / src.P, j = m - (m / src.P) * src.P;
+                if (c < d) {
+                    v = ldf(h, (int64_t)b * d + c);
+                } else {
+                    const int p = src.parents[j];
+                    const int tok = p == 0 ? src.root_tok[b] : src.tree_tok[(int64_t)b * src.N + p];
+                    // a token outside the vocabulary (e.g. a -1 left by a failed
+                    // lookup) reads as a zero embedding instead of stray memory
+                    v = (tok >= 0 && tok < src.V) ? ldf(reinterpret_cast<const T*>(src.E), (int64_t)tok * d + (c - d))
+                                                  : 0.f;
+                }
+            }
+        }
+        xs[i] = v;
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & (MD_WAVE - 1);
+    const int gw = blockIdx.x * NWAVE + (threadIdx.x >> 6);
+    const int tw = gridDim.x * NWAVE;
+    const int R = nh * d;
+    const int r0 = (int)((int64_t)R * gw / tw), r1 = (int)((int64_t)R * (gw + 1) / tw);
+    const T* Wb = W + (int64_t)head0 * d * din;
+    for (int r = r0; r < r1; r += RPW) {
+        const int nv = min(RPW, r1 - r);
+        float acc[RPW][MR];
+        rows_dot<T, MR>(Wb, din, r, nv, xs, din, lane, acc);
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const float s = wave_sum(acc[rr][m]);
+                if (rr < nv && m < mr && lane == 0) {
+                    const int row = r + rr, hh = row / d, ri = row - (row / d) * d;
+                    const float z = s + (bias ? ldf(bias, (int64_t)(head0 + hh) * d + ri) : 0.f);
+                    const float hv = xs[m * din + ri] + z / (1.f + expf(-z));
+                    const int64_t o = ((int64_t)hh * M + m0 + m) * d + ri;
+                    hres[o] = hv;
+                    if (hres_out) hres_out[o] = hv;
+                }
+            }
+        }
+    }
+}
+
+// Per wave: the k best logits of U[head0+hh] hres[hh][m] over the wave's rows.
+template <typename T, int MR>
+__global__ __launch_bounds__(BLOCK) void k_vocab_topk(const T* __restrict__ U, const float* __restrict__ hres,
+                                                      int M, int m0, int d, int V, int nh, int head0,
+                                                      int wg_per_head, KK kk, int kmax,
+                                                      float* __restrict__ part_val, int* __restrict__ part_idx) {
+    extern __shared__ float xs[];  // [MR][d]
+    const int hh = blockIdx.x / wg_per_head;
+    const int wgi = blockIdx.x - hh * wg_per_head;
+    if (hh >= nh) return;
+    const int mr = min(MR, M - m0);
+    for (int i = threadIdx.x; i < MR * d; i += BLOCK) {
+        const int mm = i / d, c = i - (i / d) * d;
+        xs[i] = mm < mr ? hres[((int64_t)hh * M + m0 + mm) * d + c] : 0.f;
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & (MD_WAVE - 1);
+    const int wih = wgi * NWAVE + (threadIdx.x >> 6);
+    const int wph = wg_per_head * NWAVE;
+    const int r0 = (int)((int64_t)V * wih / wph), r1 = (int)((int64_t)V * (wih + 1) / wph);
+    const int k = kk.v[hh];
+    const T* Uh = U + (int64_t)(head0 + hh) * V * d;
+
+    float lv[MR], tv[MR];
+    int li[MR], ti[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        lv[m] = -INFINITY;
+        tv[m] = -INFINITY;
+        li[m] = INT_MAX;
+        ti[m] = INT_MAX;
+    }
+    for (int r = r0; r < r1; r += RPW) {
+        const int nv = min(RPW, r1 - r);
+        float acc[RPW][MR];
+        rows_dot<T, MR>(Uh, d, r, nv, xs, d, lane, acc);
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+#pragma unroll
+            for (int m = 0; m < MR; ++m) {
+                const float s = wave_sum(acc[rr][m]);
+                if (rr < nv && m < mr && ranks_above(s, r + rr, tv[m], ti[m])) {
+                    list_insert(lv[m], li[m], s, r + rr, k, lane);
+                    tv[m] = __shfl(lv[m], k - 1, MD_WAVE);
+                    ti[m] = __shfl(li[m], k - 1, MD_WAVE);
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        if (m < mr && lane < kmax) {
+            const int64_t o = (((int64_t)hh * M + m0 + m) * wph + wih) * kmax + lane;
+            part_val[o] = lv[m];
+            part_idx[o] = li[m];
+        }
+    }
+}
+
+// One block per (row m, head slot hh): merge the lists of all waves of the head.
+__global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ part_val,
+                                                      const int* __restrict__ part_idx, int M, int nh, int wph,
+                                                      KK kk, int kmax, int32_t* __restrict__ topk_idx,
+                                                      float* __restrict__ topk_val) {
+    __shared__ float sv[NWAVE][MD_WAVE];
+    __shared__ int si[NWAVE][MD_WAVE];
+    const int m = blockIdx.x / nh, hh = blockIdx.x - (blockIdx.x / nh) * nh;
+    const int k = kk.v[hh];
+    const int lane = threadIdx.x & (MD_WAVE - 1), wv = threadIdx.x >> 6;
+    const int64_t base = ((int64_t)hh * M + m) * wph * kmax;
+    const int total = wph * kmax;
+    const int q0 = (int)((int64_t)total * wv / NWAVE), q1 = (int)((int64_t)total * (wv + 1) / NWAVE);
+
+    float lv = -INFINITY, tv = -INFINITY;
+    int li = INT_MAX, ti = INT_MAX;
+    for (int c0 = q0; c0 < q1; c0 += MD_WAVE) {
+        const int c = c0 + lane;
+        const float cv = c < q1 ? part_val[base + c] : -INFINITY;
+        const int ci = c < q1 ? part_idx[base + c] : INT_MAX;
+        uint64_t bm = __ballot(ranks_above(cv, ci, tv, ti));
+        while (bm) {
+            const int src = __ffsll((long long)bm) - 1;
+            bm &= bm - 1;
+            const float x = __shfl(cv, src, MD_WAVE);
+            const int xi = __shfl(ci, src, MD_WAVE);
+            if (ranks_above(x, xi, tv, ti)) {
+                list_insert(lv, li, x, xi, k, lane);
+                tv = __shfl(lv, k - 1, MD_WAVE);
+                ti = __shfl(li, k - 1, MD_WAVE);
+            }
+        }
+    }
+    sv[wv][lane] = lane < k ? lv : -INFINITY;
+    si[wv][lane] = lane < k ? li : INT_MAX;
+    __syncthreads();
+    if (wv != 0) return;
+    lv = -INFINITY;
+    li = INT_MAX;
+    tv = -INFINITY;
+    ti = INT_MAX;
+    for (int w = 0; w < NWAVE; ++w) {
+        const float cv = sv[w][lane];
+        const int ci = si[w][lane];
+        uint64_t bm = __ballot(lane < k && ranks_above(cv, ci, tv, ti));
+        while (bm) {
+            const int src = __ffsll((long long)bm) - 1;
+            bm &= bm - 1;
+            const float x = __shfl(cv, src, MD_WAVE);
+            const int xi = __shfl(ci, src, MD_WAVE);
+            if (ranks_above(x, xi, tv, ti)) {
+                list_insert(lv, li, x, xi, k, lane);
+                tv = __shfl(lv, k - 1, MD_WAVE);
+                ti = __shfl(li, k - 1, MD_WAVE);
+            }
+        }
+    }
+    if (lane < kmax) {
+        const bool ok = lane < k && li != INT_MAX;
+        const int64_t o = ((int64_t)m * nh + hh) * kmax + lane;
+        topk_idx[o] = ok ? li : -1;
+        topk_val[o] = ok ? lv : -INFINITY;
+    }
+}
+
+struct Plan {
+    int MR;
+    int res_grid;
+    int voc_grid;
+    int wg_per_head;
+    int wph;
+    size_t res_lds, voc_lds;
+};
+
+constexpr int kCUs = 256;
+constexpr size_t kLDS = 160 * 1024;
+
+int pick_mr(int M, int din) {
+    int mr = M >= 4 ? 4 : (M >= 2 ? 2 : 1);
+    while (mr > 1 && (size_t)mr * din * 4 > kLDS) mr >>= 1;
+    return mr;
+}
+
+int blocks_per_cu(size_t lds) {
+    int n = lds ? (int)(kLDS / lds) : 4;
+    return n < 1 ? 1 : (n > 4 ? 4 : n);
+}
+
+Plan make_plan(int M, int d, int din, int nh) {
+    Plan p;
+    p.MR = pick_mr(M, din);
+    p.res_lds = (size_t)p.MR * din * 4;
+    p.voc_lds = (size_t)p.MR * d * 4;
+    p.res_grid = kCUs * blocks_per_cu(p.res_lds);
+    int vg = kCUs * blocks_per_cu(p.voc_lds);
+    p.wg_per_head = vg / nh;
+    if (p.wg_per_head < 1) p.wg_per_head = 1;
+    p.voc_grid = p.wg_per_head * nh;
+    p.wph = p.wg_per_head * NWAVE;
+    return p;
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+template <typename T>
+hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    const Plan p = make_plan(a.M, a.d, a.din, a.nh);
+    char* ws = reinterpret_cast<char*>(a.ws);
+    float* hres = reinterpret_cast<float*>(ws);
+    ws += align256((size_t)a.nh * a.M * a.d * 4);
+    float* pv = reinterpret_cast<float*>(ws);
+    ws += align256((size_t)a.nh * a.M * p.wph * a.kmax * 4);
+    int* pi = reinterpret_cast<int*>(ws);
+
+    RowSrc src;
+    src.kind = a.kind;
+    src.P = 1;
+    src.N = tree ? tree->n : 0;
+    src.V = a.V;
+    src.h = a.h;
+    src.E = a.E;
+    src.root_tok = a.root_tok;
+    src.tree_tok = a.tree_tok;
+    for (int i = 0; i < 64; ++i) src.parents[i] = 0;
+    if (a.kind == 1) {
+        const int off = tree->level_off[a.level];
+        src.P = tree->level_off[a.level + 1] - off;
+        for (int j = 0; j < src.P; ++j) src.parents[j] = tree->lp[off + j];
+    }
+    KK kk;
+    for (int i = 0; i < 8; ++i) kk.v[i] = i < a.nh ? a.kk[i] : 1;
+
+    const T* W = reinterpret_cast<const T*>(a.W);
+    const T* bias = reinterpret_cast<const T*>(a.b);
+    const T* U = reinterpret_cast<const T*>(a.U);
+    for (int m0 = 0; m0 < a.M; m0 += p.MR) {
+        switch (p.MR) {
+            case 4:
+                hipLaunchKernelGGL((k_residual<T, 4>), dim3(p.res_grid), dim3(BLOCK), p.res_lds, s, W, bias, src, a.M,
+                                   m0, a.d, a.din, a.nh, a.head0, hres, a.h_res);
+                break;
+            case 2:
+                hipLaunchKernelGGL((k_residual<T, 2>), dim3(p.res_grid), dim3(BLOCK), p.res_lds, s, W, bias, src, a.M,
+                                   m0, a.d, a.din, a.nh, a.head0, hres, a.h_res);
+                break;
+            default:
+                hipLaunchKernelGGL((k_residual<T, 1>), dim3(p.res_grid), dim3(BLOCK), p.res_lds, s, W, bias, src, a.M,
+                                   m0, a.d, a.din, a.nh, a.head0, hres, a.h_res);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (ev0) {
+        hipError_t e = hipEventRecord(ev0, s);
+        if (e != hipSuccess) return e;
+    }
+    for (int m0 = 0; m0 < a.M; m0 += p.MR) {
+        switch (p.MR) {
+            case 4:
+                hipLaunchKernelGGL((k_vocab_topk<T, 4>), dim3(p.voc_grid), dim3(BLOCK), p.voc_lds, s, U, hres, a.M,
+                                   m0, a.d, a.V, a.nh, a.head0, p.wg_per_head, kk, a.kmax, pv, pi);
+                break;
+            case 2:
+                hipLaunchKernelGGL((k_vocab_topk<T, 2>), dim3(p.voc_grid), dim3(BLOCK), p.voc_lds, s, U, hres, a.M,
+                                   m0, a.d, a.V, a.nh, a.head0, p.wg_per_head, kk, a.kmax, pv, pi);
+                break;
+            default:
+                hipLaunchKernelGGL((k_vocab_topk<T, 1>), dim3(p.voc_grid), dim3(BLOCK), p.voc_lds, s, U, hres, a.M,
+                                   m0, a.d, a.V, a.nh, a.head0, p.wg_per_head, kk, a.kmax, pv, pi);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (ev1) {
+        hipError_t e = hipEventRecord(ev1, s);
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(k_topk_merge, dim3(a.M * a.nh), dim3(BLOCK), 0, s, pv, pi, a.M, a.nh, p.wph, kk, a.kmax,
+                       a.topk_idx, a.topk_val);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+size_t heads_ws_bytes(int M, int d, int din, int nh, int kmax) {
+    const Plan p = make_plan(M, d, din, nh);
+    return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * p.wph * kmax * 4);
+}
+
+size_t heads_ws_bound(int M, int d, int nh, int kmax) {
+    const size_t wph_max = (size_t)kCUs * 4 * NWAVE;
+    return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * wph_max * kmax * 4);
+}
+
+hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    if (a.dt == 0) return launch_typed<float>(a, tree, s, ev0, ev1);
+    return launch_typed<uint16_t>(a, tree, s, ev0, ev1);
+}

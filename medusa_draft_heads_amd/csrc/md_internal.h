@@ -1,0 +1,79 @@
+// Internal declarations of libmedusa: the per-call tree description handed
+// to kernels and the launchers each kernel file exports to the dispatcher.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#define MD_WAVE 64
+
+// A validated tree, expanded on the host and passed to kernels by value.
+struct DevTree {
+    int32_t n;
+    int32_t max_depth;
+    int8_t parent[64];
+    int8_t depth[64];
+    int8_t rank[64];
+    // Hydra: the nodes that have children, ordered by depth then index;
+    // level i (children at depth i) owns lp[level_off[i] .. level_off[i+1]).
+    int8_t lp[64];
+    int8_t prow[64];        // a node's position among its level's parents (-1: leaf)
+    int32_t level_off[10];  // i = 1..9 used; level_off[i+1]-level_off[i] = P_i
+    uint64_t anc[64];       // bit j set: node j is this node or one of its ancestors
+};
+
+// ---- heads (heads.hip) ----
+struct HeadsArgs {
+    int kind;  // 0 Medusa, 1 Hydra
+    int dt;    // 0 f32, 1 bf16
+    int M;     // rows through the heads this call
+    int B;     // Hydra: requests
+    int d, din, V;
+    int nh;     // heads this call (K or 1)
+    int head0;  // first head's index in W, b, U
+    int kk[8];  // top-k width per head slot
+    int kmax;
+    int level;
+    const void* h;
+    const void* W;
+    const void* b;
+    const void* U;
+    const void* E;
+    const int32_t* root_tok;
+    const int32_t* tree_tok;
+    int32_t* topk_idx;
+    float* topk_val;
+    float* h_res;
+    void* ws;
+};
+
+size_t heads_ws_bytes(int M, int d, int din, int nh, int kmax);  // this plan
+size_t heads_ws_bound(int M, int d, int nh, int kmax);            // any plan
+hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+
+// ---- tree build (tree.hip) ----
+hipError_t tree_build_launch(const DevTree& t, int kind, int B, int M, int K, int kmax, int level,
+                             const int32_t* topk_idx,
+                             const int32_t* src_row, const int32_t* root_tok, const int32_t* lens,
+                             int32_t* tree_tok, int32_t* tree_pos, hipStream_t s);
+
+// ---- tree attention (attention.hip) ----
+struct AttnPlan {
+    int splits;     // key-range splits per (request, kv head, query tile)
+    int chunk;      // keys per split (multiple of the key tile)
+    int qtiles;     // query tiles per (request, kv head)
+    int rows;       // query rows per (request, kv head) = N * Hq / Hkv
+};
+AttnPlan attention_plan(int dt, int B, int N, int Hq, int Hkv, int hd, int max_len);
+size_t attention_ws_bytes(int dt, int B, int N, int Hq, int Hkv, int hd, int max_len);
+hipError_t attention_launch(const DevTree& t, int dt, int B, int Hq, int Hkv, int hd, int Lcap, int max_len,
+                            const void* q, const void* Kc, const void* Vc, const int32_t* lens, float scale,
+                            void* out, void* ws, hipStream_t s);
+
+// ---- accept (accept.hip) ----
+size_t accept_ws_bytes(int B, int N, int V);
+hipError_t accept_launch(const DevTree& t, int dt, int B, int K, int V, int Hkv, int hd, int Lcap,
+                         const float* logits, const int32_t* tree_tok, void* Kc, void* Vc, int32_t* lens,
+                         int32_t* accept_len, int32_t* path, int32_t* next_tok, int32_t* compact_src, void* ws,
+                         hipStream_t s);

@@ -1,0 +1,114 @@
+"""One Medusa (or Hydra) tree-decode step through libmedusa.
+
+MedusaStep owns the outputs and workspaces of a fixed configuration and issues
+the four library calls in the order the step needs them: heads -> tree ->
+tree attention -> accept. Hydra runs its heads level by level, each level's
+tree tokens feeding the next level's embedding lookup. Buffers are allocated
+once, so a step allocates nothing and issues no host synchronisation.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Dict, Optional, Sequence
+
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class StepConfig:
+    kind: int  # L.MD_HEADS_MEDUSA or L.MD_HEADS_HYDRA
+    dtype: torch.dtype  # storage type of activations, weights and cache
+    B: int  # requests
+    M: int  # rows of h through the heads (Medusa: B or B*N; Hydra: B)
+    d: int
+    V: int
+    K: int
+    k_per_head: Sequence[int]
+    parent: Sequence[int]
+    rank: Sequence[int]
+    Hq: int
+    Hkv: int
+    hd: int
+    Lcap: int
+    max_len: int
+
+
+class MedusaStep:
+    def __init__(self, cfg: StepConfig, device: str = "cuda"):
+        self.cfg = cfg
+        self.dev = torch.device(device)
+        self.dt = L.MD_F32 if cfg.dtype == torch.float32 else L.MD_BF16
+        self.tree = L.make_tree(cfg.parent, cfg.rank)
+        rc = L.md_tree_validate(self.tree, cfg.K, cfg.k_per_head)
+        if rc != L.MD_OK:
+            raise L.MedusaError(rc, L.md_last_error())
+        self.N = len(cfg.parent)
+        self.kmax = max(cfg.k_per_head)
+        i32 = dict(dtype=torch.int32, device=self.dev)
+        B, N, K = cfg.B, self.N, cfg.K
+        if cfg.kind == L.MD_HEADS_MEDUSA:
+            self.topk_idx = torch.empty(cfg.M, K, self.kmax, **i32)
+            self.topk_val = torch.empty(cfg.M, K, self.kmax, dtype=torch.float32, device=self.dev)
+        else:
+            # one list per (request, parent) row of the widest level
+            self.topk_idx = torch.empty(B * N, 1, self.kmax, **i32)
+            self.topk_val = torch.empty(B * N, 1, self.kmax, dtype=torch.float32, device=self.dev)
+        self.tree_tok = torch.empty(B, N, **i32)
+        self.tree_pos = torch.empty(B, N, **i32)
+        self.attn_out = torch.empty(B, N, cfg.Hq, cfg.hd, dtype=cfg.dtype, device=self.dev)
+        self.accept_len = torch.empty(B, **i32)
+        self.path = torch.empty(B, K + 1, **i32)
+        self.next_tok = torch.empty(B, **i32)
+        self.compact_src = torch.empty(B, K + 1, **i32)
+        u8 = dict(dtype=torch.uint8, device=self.dev)
+        self.ws_heads = torch.empty(max(1, L.md_heads_workspace_bytes(cfg.kind, self.dt, cfg.M, cfg.d, cfg.V, K,
+                                                                       self.kmax)), **u8)
+        self.ws_attn = torch.empty(max(1, L.md_attention_workspace_bytes(self.dt, B, N, cfg.Hq, cfg.Hkv, cfg.hd,
+                                                                          cfg.max_len)), **u8)
+        self.ws_acc = torch.empty(max(1, L.md_accept_workspace_bytes(B, N, cfg.V)), **u8)
+        self.scale = 1.0 / float(cfg.hd) ** 0.5
+        self.h_res = None
+
+    # -- the four calls -------------------------------------------------------
+    def heads(self, h, W, b, U, E=None, root_tok=None, level: int = 0, h_res=None) -> None:
+        c = self.cfg
+        L.md_medusa_heads(c.kind, self.dt, c.M, c.d, c.V, c.K, c.k_per_head, level, self.tree, h, W, b, U, E,
+                          root_tok, self.tree_tok, self.topk_idx, self.topk_val, h_res, self.ws_heads)
+
+    def build(self, src_row, root_tok, lens, level: int = 0) -> None:
+        c = self.cfg
+        L.md_tree_build(self.tree, c.kind, c.B, c.M, c.K, self.kmax, level, self.topk_idx, src_row, root_tok, lens,
+                        self.tree_tok, self.tree_pos)
+
+    def attention(self, q, Kc, Vc, lens) -> None:
+        c = self.cfg
+        L.md_tree_attention(self.tree, self.dt, c.B, c.Hq, c.Hkv, c.hd, c.Lcap, c.max_len, q, Kc, Vc, lens,
+                            self.scale, self.attn_out, self.ws_attn)
+
+    def accept(self, logits, Kc, Vc, lens) -> None:
+        c = self.cfg
+        L.md_tree_accept(self.tree, self.dt, c.B, c.K, c.V, c.Hkv, c.hd, c.Lcap, logits, self.tree_tok, Kc, Vc, lens,
+                         self.accept_len, self.path, self.next_tok, self.compact_src, self.ws_acc)
+
+    # -- a whole step -----------------------------------------------------------
+    def run(self, w: Dict[str, torch.Tensor], x: Dict[str, torch.Tensor]) -> None:
+        """w: W, b, U (and E for Hydra); x: h, q, Kc, Vc, lens, root_tok, src_row, logits."""
+        c = self.cfg
+        if c.kind == L.MD_HEADS_MEDUSA:
+            self.heads(x["h"], w["W"], w["b"], w["U"])
+            self.build(x["src_row"], x["root_tok"], x["lens"])
+        else:
+            depth = max(self._depths())
+            for level in range(1, depth + 1):
+                self.heads(x["h"], w["W"], w["b"], w["U"], E=w["E"], root_tok=x["root_tok"], level=level)
+                self.build(None, x["root_tok"], x["lens"], level=level)
+        self.attention(x["q"], x["Kc"], x["Vc"], x["lens"])
+        self.accept(x["logits"], x["Kc"], x["Vc"], x["lens"])
+
+    def _depths(self):
+        dep = []
+        for n, p in enumerate(self.cfg.parent):
+            dep.append(0 if p < 0 else dep[p] + 1)
+        return dep

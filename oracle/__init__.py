@@ -138,11 +138,13 @@ def vocab_topk(U_k: np.ndarray, hres: np.ndarray, k: int, want_logits: bool = Fa
     return idx, val, margin, logits
 
 
-def heads_medusa(W, b, U, h, topk: Sequence[int], rows: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
+def heads_medusa(W, b, U, h, topk: Sequence[int], rows: Optional[Sequence[int]] = None,
+                 want_logits: bool = False) -> Dict[str, np.ndarray]:
     """All K Medusa heads on hidden-state rows h [M, d].
 
     Returns hres [K, R, d], idx [R, K, kmax] (-1 padded), val [R, K, kmax]
-    (-inf padded), margin [R, K], for the R selected rows (all by default).
+    (-inf padded), margin [R, K], for the R selected rows (all by default),
+    and with want_logits the full logits [R, K, V].
     """
     K = W.shape[0]
     hd = to_double(h)
@@ -154,13 +156,19 @@ def heads_medusa(W, b, U, h, topk: Sequence[int], rows: Optional[Sequence[int]] 
     idx = np.full((R, K, kmax), -1, dtype=np.int32)
     val = np.full((R, K, kmax), -np.inf, dtype=np.float64)
     margin = np.empty((R, K), dtype=np.float64)
+    logits = np.empty((R, K, U.shape[1]), dtype=np.float64) if want_logits else None
     for k in range(K):
         hres[k] = residual(W[k], b[k], hd, hd)
-        i_, v_, m_, _ = vocab_topk(U[k], hres[k], topk[k])
+        i_, v_, m_, lg = vocab_topk(U[k], hres[k], topk[k], want_logits=want_logits)
         idx[:, k, : topk[k]] = i_
         val[:, k, : topk[k]] = v_
         margin[:, k] = m_
-    return {"hres": hres, "idx": idx, "val": val, "margin": margin}
+        if want_logits:
+            logits[:, k] = lg
+    out = {"hres": hres, "idx": idx, "val": val, "margin": margin}
+    if want_logits:
+        out["logits"] = logits
+    return out
 
 
 def _depths(parent: Sequence[int]):
@@ -181,7 +189,7 @@ def hydra_rows(parent: Sequence[int], level: int):
 
 
 def hydra_expand(W, b, U, E, h, topo_parent, topo_rank, topk: Sequence[int], root_tok, lens,
-                 requests: Optional[Sequence[int]] = None) -> Dict[str, object]:
+                 requests: Optional[Sequence[int]] = None, want_logits: bool = False) -> Dict[str, object]:
     """Hydra heads, level by level (the Hydra summary and abstract).
 
     Level i runs head i on one row per (request, parent at depth i - 1 with
@@ -218,13 +226,13 @@ def hydra_expand(W, b, U, E, h, topo_parent, topo_rank, topk: Sequence[int], roo
         x = np.stack([np.concatenate([hd[b_], emb(int(tok[b_, p]))]) for (b_, p) in rows])
         base = np.stack([hd[b_] for (b_, _) in rows])
         hres = residual(W[i - 1], b[i - 1], x, base)
-        idx, val, margin, _ = vocab_topk(U[i - 1], hres, topk[i - 1])
+        idx, val, margin, lg = vocab_topk(U[i - 1], hres, topk[i - 1], want_logits=want_logits)
         row_of = {rp: r for r, rp in enumerate(rows)}
         for b_ in reqs:
             for n in range(N):
                 if dep[n] == i:
                     tok[b_, n] = idx[row_of[(b_, topo_parent[n])], topo_rank[n]]
-        levels.append({"rows": rows, "hres": hres, "idx": idx, "val": val, "margin": margin})
+        levels.append({"rows": rows, "hres": hres, "idx": idx, "val": val, "margin": margin, "logits": lg})
     return {"tree_tok": tok, "tree_pos": pos, "levels": levels}
 
 

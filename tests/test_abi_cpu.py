@@ -1,0 +1,148 @@
+"""The C-ABI library on the CPU: it loads, exports what include/medusa.h
+declares, and rejects every invalid argument before touching HIP (no GPU is
+needed for any of these calls)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+md = pytest.importorskip("medusa_draft_heads_amd")
+from medusa_draft_heads_amd import _lib as L  # noqa: E402
+from synth.topology import chain, product_order_tree  # noqa: E402
+
+
+def header_functions():
+    with open(os.path.join(ROOT, "include", "medusa.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(md_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) == 11
+    lib = L.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(L.EXPORTS)
+
+
+def test_weight_bytes_match_page():
+    # four 70B-shaped heads: 4,471,160,832 parameters = 8.94 GB in bf16
+    assert md.md_heads_weight_bytes(0, 1, 8192, 128256, 4) == 8_942_321_664
+    assert md.md_heads_weight_bytes(0, 0, 8192, 128256, 1) == 4 * 1_117_790_208
+    assert md.md_heads_weight_bytes(1, 1, 4096, 128256, 1) == 2 * (2 * 4096 * 4096 + 4096 + 4096 * 128256)
+    assert md.md_heads_weight_bytes(2, 1, 8192, 128256, 4) == -1
+
+
+def _tree(parent, rank, n=None):
+    t = L.make_tree(parent, rank)
+    if n is not None:
+        t.n = n
+    return t
+
+
+@pytest.mark.parametrize("parent,rank,K,kph,why", [
+    ([-1, 0, 0], [0, 0, 0], 2, [2, 1], "siblings share a rank"),
+    ([-1, 0, 2], [0, 0, 0], 2, [2, 1], "parent after child"),
+    ([-1, 0, 1, 0], [0, 0, 0, 1], 2, [2, 1], "not breadth-first"),
+    ([-1, 0, 1, 2], [0, 0, 0, 0], 2, [1, 1], "deeper than K"),
+    ([-1, 0, 0], [0, 0, 2], 1, [2], "rank beyond the head's list"),
+    ([0, 0], [0, 0], 1, [1], "root has a parent"),
+])
+def test_tree_validation_rejects(parent, rank, K, kph, why):
+    assert md.md_tree_validate(_tree(parent, rank), K, kph) == L.MD_EINVAL, why
+    assert L.md_last_error()
+
+
+def test_tree_validation_accepts_page_topologies():
+    for kph, n in (((4, 2, 2, 1), 16), ((10, 4, 2, 1), 64), ((1, 1, 1, 1), 5)):
+        t = product_order_tree(kph, n)
+        assert md.md_tree_validate(L.make_tree(t.parent, t.rank), len(kph), kph) == L.MD_OK
+    assert md.md_tree_validate(_tree([-1], [0], n=0), 1, [1]) == L.MD_EINVAL
+    assert md.md_tree_validate(_tree([-1], [0], n=65), 1, [1]) == L.MD_EINVAL
+
+
+def _rc(fn, *args):
+    return fn(*args)
+
+
+def test_heads_argument_errors():
+    lib = L.lib()
+    kp = (ctypes.c_int32 * 4)(4, 2, 2, 1)
+    kpv = ctypes.cast(kp, ctypes.c_void_p)
+    P = 0x1000  # never dereferenced: every call below is rejected on the host
+    t = ctypes.byref(L.make_tree(*[list(x) for x in (product_order_tree((4, 2, 2, 1), 16).parent,
+                                                      product_order_tree((4, 2, 2, 1), 16).rank)]))
+
+    def call(kind=0, dt=1, M=1, d=256, V=4096, K=4, kph=kpv, level=0, tree=None, h=P, W=P, U=P, ws=P, ws_bytes=1 << 30,
+             E=None, root=None, tok=None):
+        return lib.md_medusa_heads(kind, dt, M, d, V, K, kph, level, tree, h, W, None, U, E, root, tok, P, P, None, ws,
+                                   ws_bytes, None)
+
+    assert call(kind=3) == L.MD_EINVAL
+    assert call(dt=7) == L.MD_EINVAL
+    assert call(K=9) == L.MD_EINVAL
+    assert call(kph=None) == L.MD_EINVAL
+    bad = (ctypes.c_int32 * 4)(4, 17, 2, 1)
+    assert call(kph=ctypes.cast(bad, ctypes.c_void_p)) == L.MD_EINVAL
+    assert call(d=100) == L.MD_EUNSUPPORTED
+    assert call(V=3) == L.MD_EINVAL
+    assert call(h=None) == L.MD_EINVAL
+    assert call(ws_bytes=16) == L.MD_EWORKSPACE
+    assert call(level=1) == L.MD_EINVAL  # Medusa takes level 0
+    assert call(kind=1, level=0, tree=t, E=P, root=P) == L.MD_EINVAL  # Hydra levels are 1..K
+    assert call(kind=1, level=2, tree=t, E=P, root=P, tok=None) == L.MD_EINVAL  # needs the parents' tokens
+    assert call(kind=1, level=1, tree=None, E=P, root=P) == L.MD_EINVAL
+    assert call(M=-1) == L.MD_EINVAL
+    assert call(M=0) == L.MD_OK  # an empty batch enqueues nothing
+
+
+def test_attention_and_accept_argument_errors():
+    lib = L.lib()
+    P = 0x1000
+    topo = product_order_tree((4, 2, 2, 1), 16)
+    t = ctypes.byref(L.make_tree(topo.parent, topo.rank))
+    need = md.md_attention_workspace_bytes(1, 1, 16, 4, 2, 128, 100)
+    assert need > 0
+
+    def att(dt=1, B=1, Hq=4, Hkv=2, hd=128, Lcap=200, max_len=100, ws_bytes=need, q=P):
+        return lib.md_tree_attention(t, dt, B, Hq, Hkv, hd, Lcap, max_len, q, P, P, P, 0.1, P, P, ws_bytes, None)
+
+    assert att(hd=96) == L.MD_EUNSUPPORTED
+    assert att(Hq=5) == L.MD_EINVAL
+    assert att(Lcap=110) == L.MD_ERANGE
+    assert att(max_len=-1) == L.MD_EINVAL
+    assert att(ws_bytes=need - 1) == L.MD_EWORKSPACE
+    assert att(q=None) == L.MD_EINVAL
+    assert att(B=0) == L.MD_OK
+
+    wsa = md.md_accept_workspace_bytes(1, 16, 4096)
+
+    def acc(dt=1, B=1, K=4, V=4096, Hkv=2, hd=128, Lcap=200, ws_bytes=wsa, logits=P):
+        return lib.md_tree_accept(t, dt, B, K, V, Hkv, hd, Lcap, logits, P, P, P, P, P, P, P, P, P, ws_bytes, None)
+
+    assert acc(hd=512) == L.MD_EUNSUPPORTED
+    assert acc(Lcap=10) == L.MD_ERANGE
+    assert acc(K=3) == L.MD_EINVAL  # the tree is 4 deep
+    assert acc(logits=None) == L.MD_EINVAL
+    assert acc(ws_bytes=wsa - 1) == L.MD_EWORKSPACE
+    assert acc(B=0) == L.MD_OK
+
+    def build(kind=0, B=1, M=1, K=4, kmax=4, level=0, src=P):
+        return lib.md_tree_build(t, kind, B, M, K, kmax, level, P, src, P, P, P, P, None)
+
+    assert build(kmax=2) == L.MD_EINVAL  # ranks up to 3 need lists of 4
+    assert build(level=1) == L.MD_EINVAL
+    assert build(M=0) == L.MD_EINVAL
+    assert build(src=None) == L.MD_EINVAL
+    assert build(kind=1, level=5) == L.MD_EINVAL
+    assert build(B=0) == L.MD_OK
+
+
+def test_timing_hook_pairs():
+    assert L.lib().md_set_vocab_timing_events(0x10, None) == L.MD_EINVAL
+    assert L.lib().md_set_vocab_timing_events(None, None) == L.MD_OK

@@ -1,0 +1,123 @@
+"""A whole decode step on the GPU against the oracle's whole step.
+
+The GPU runs heads -> tree -> tree attention -> accept + compaction through
+MedusaStep; the oracle runs the same step on the same inputs. The target's
+verification logits are planted from the oracle's tree tokens (per-depth
+acceptance a), so over several steps the GPU's accepted lengths must equal
+the oracle's one for one -- and their mean estimates the closed-form E.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from synth.workloads import HYDRA_B4, LLAMA70B, LLAMA70B_CHAIN, TINY_F32, plant, step_inputs, weights
+
+from _helpers import TAU, TOL, from_dev, rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def make_step(wl):
+    import torch
+
+    import medusa_draft_heads_amd as md
+
+    topo = wl.topology()
+    cfg = md.StepConfig(kind=md.MD_HEADS_MEDUSA if wl.kind == "medusa" else md.MD_HEADS_HYDRA,
+                        dtype=torch.float32 if wl.dtype == "f32" else torch.bfloat16, B=wl.B,
+                        M=wl.M if wl.kind == "medusa" else wl.B, d=wl.d, V=wl.V, K=wl.K, k_per_head=wl.topk,
+                        parent=topo.parent, rank=topo.rank, Hq=wl.Hq, Hkv=wl.Hkv, hd=wl.hd, Lcap=wl.Lcap,
+                        max_len=wl.L_max)
+    return md.MedusaStep(cfg), topo
+
+
+def oracle_tree(wl, w, x, topo):
+    """The oracle's heads and tree for this step (tokens needed to plant logits)."""
+    if wl.kind == "medusa":
+        rows = sorted(set(int(r) for r in x["src_row"]))
+        heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], wl.topk, rows=rows)
+        full = np.full((wl.M, wl.K, wl.kmax), -1, np.int32)
+        for j, r in enumerate(rows):
+            full[r] = heads["idx"][j]
+        tok, pos = oracle.tree_tokens_medusa(topo.parent, topo.rank, full, x["src_row"], x["root_tok"], x["lens"])
+        return tok, pos, heads, full
+    hy = oracle.hydra_expand(w["W"], w["b"], w["U"], w["E"], x["h"], topo.parent, topo.rank, wl.topk,
+                             x["root_tok"], x["lens"])
+    return hy["tree_tok"], hy["tree_pos"], hy, None
+
+
+def run_and_compare(wl, w, wd, step, topo, seed, s):
+    import torch
+
+    x = step_inputs(wl, seed, step=s)
+    tok, pos, heads, full = oracle_tree(wl, w, x, topo)
+    logits = plant(x["logits"], topo, tok, wl.a, seed=seed, step=s)
+    xd = {k: to_dev(v) for k, v in x.items() if k != "logits"}
+    xd["logits"] = to_dev(logits)
+    step.run(wd, xd)
+    torch.cuda.synchronize()
+    # heads (Medusa: margin rule on the rows the tree reads)
+    if wl.kind == "medusa":
+        gi = from_dev(step.topk_idx)
+        rows = sorted(set(int(r) for r in x["src_row"]))
+        for j, r in enumerate(rows):
+            for k in range(wl.K):
+                if heads["margin"][j, k] > TAU[wl.dtype]:
+                    assert np.array_equal(gi[r, k, : wl.topk[k]], heads["idx"][j, k, : wl.topk[k]])
+                else:
+                    pytest.skip("near-tie list in a chained step (margin %.2g)" % heads["margin"][j, k])
+    else:
+        for lvl in heads["levels"]:
+            if np.min(lvl["margin"]) <= TAU[wl.dtype]:
+                pytest.skip("near-tie Hydra list in a chained step")
+    assert np.array_equal(from_dev(step.tree_tok), tok)
+    assert np.array_equal(from_dev(step.tree_pos), pos)
+    ref_attn = oracle.tree_attention(topo.parent, x["q"], x["Kc"], x["Vc"], x["lens"])
+    ga = from_dev(step.attn_out)
+    ga = ga.astype(np.float64) if wl.dtype == "f32" else synth.bf16_to_f32(ga).astype(np.float64)
+    assert rel_err(ga, ref_attn) <= TOL[wl.dtype]
+    ref = oracle.accept(topo.parent, wl.K, tok, oracle.argmax(logits), x["lens"])
+    for key in ("accept_len", "path", "next_tok", "compact_src"):
+        assert np.array_equal(from_dev(getattr(step, key)), ref[key]), key
+    rK, rV, rl = oracle.compact(x["Kc"], x["Vc"], x["lens"], ref["accept_len"], ref["path"], wl.K)
+    assert np.array_equal(from_dev(xd["Kc"]), rK) and np.array_equal(from_dev(xd["Vc"]), rV)
+    assert np.array_equal(from_dev(xd["lens"]), rl)
+    return ref["accept_len"]
+
+
+def test_step_tiny_many_steps():
+    wl = TINY_F32
+    seed = 3
+    w = weights(wl, seed)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    step, topo = make_step(wl)
+    lens = [int(run_and_compare(wl, w, wd, step, topo, seed, s)[0]) for s in range(24)]
+    print("tiny accepted lengths:", lens, "mean", np.mean(lens))
+
+
+def test_step_70b_shaped():
+    wl = LLAMA70B
+    seed = 70
+    w = weights(wl, seed)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    step, topo = make_step(wl)
+    acc = run_and_compare(wl, w, wd, step, topo, seed, 0)
+    print("70B-shaped step accepted", acc)
+    # the top-1 chain runs on the same weights
+    wlc = LLAMA70B_CHAIN
+    stepc, topoc = make_step(wlc)
+    acc = run_and_compare(wlc, w, wd, stepc, topoc, seed, 1)
+    print("70B-shaped chain accepted", acc)
+
+
+def test_step_hydra_small():
+    from dataclasses import replace
+
+    wl = replace(HYDRA_B4, name="hydra small", B=2, d=256, V=2048, N=20, L=300)
+    seed = 12
+    w = weights(wl, seed)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    step, topo = make_step(wl)
+    for s in range(3):
+        run_and_compare(wl, w, wd, step, topo, seed, s)
