@@ -144,9 +144,21 @@ def main() -> int:
     ms_total = t_start.elapsed_time(t_end)
     ms_per_step = ms_total / args.steps
     vocab_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
-    for xd in sets:  # one more pass to report the accepted lengths per set
-        pass
     acc_len = step.accept_len.cpu().numpy().tolist()
+
+    # attainable HBM read bandwidth on this GPU: the library's plain streaming-read probe over 4 GiB
+    probe_buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(md.md_hbm_read_probe_blocks(), dtype=torch.int32, device=dev)
+    for _ in range(2):
+        md.md_hbm_read_probe(probe_buf, probe_buf.numel(), sink)
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record(stream)
+    for _ in range(10):
+        md.md_hbm_read_probe(probe_buf, probe_buf.numel(), sink)
+    p1.record(stream)
+    torch.cuda.synchronize()
+    stream_gbs = probe_buf.numel() * 10 / (p0.elapsed_time(p1) * 1e-3) / 1e9
+    del probe_buf
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -201,7 +213,9 @@ def main() -> int:
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                      "kernel": "k_vocab_topk (vocabulary projection + per-head top-k)",
-                     "kernel_ms": round(vocab_ms, 4), "bytes_per_launch": vocab_bytes},
+                     "kernel_ms": round(vocab_ms, 4), "bytes_per_launch": vocab_bytes,
+                     "stream_read_GBps": round(stream_gbs, 1),
+                     "frac_of_stream_read": round(achieved / stream_gbs, 4)},
         "step_hbm": {"bytes_per_step": step_bytes, "GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "acceptance": {"last_step_accept_len": acc_len, "oracle_accept_len": acc_oracle, "E_closed_form": round(E, 4)},

@@ -182,6 +182,16 @@ int md_tree_accept(const md_tree* tree, int dt, int B, int K, int V, int Hkv, in
  * Pass NULL, NULL to stop. */
 int md_set_vocab_timing_events(void* start, void* stop);
 
+/* Measurement utility, not a step of the method: streams `bytes` bytes of
+ * device memory `buf` once with 16-byte non-temporal loads spread over the
+ * whole GPU, and writes one word per block to `sink` (device, uint32,
+ * md_hbm_read_probe_blocks() entries). It gives the attainable HBM read
+ * bandwidth of the running GPU and a kernel of known traffic for scaling
+ * hardware byte counters. bytes must be a positive multiple of 16 and buf
+ * 16-byte aligned. */
+int md_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream);
+int md_hbm_read_probe_blocks(void);
+
 /* Thread-local text for the last non-MD_OK return on this thread. */
 const char* md_last_error(void);
 

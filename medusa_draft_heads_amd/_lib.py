@@ -22,7 +22,7 @@ MD_MAX_NODES, MD_MAX_HEADS, MD_MAX_TOPK = 64, 8, 16
 EXPORTS = (
     "md_tree_validate", "md_heads_weight_bytes", "md_heads_workspace_bytes", "md_medusa_heads", "md_tree_build",
     "md_attention_workspace_bytes", "md_tree_attention", "md_accept_workspace_bytes", "md_tree_accept",
-    "md_set_vocab_timing_events", "md_last_error",
+    "md_set_vocab_timing_events", "md_last_error", "md_hbm_read_probe", "md_hbm_read_probe_blocks",
 )
 
 
@@ -68,6 +68,8 @@ def lib() -> ctypes.CDLL:
             "md_tree_accept": ([tp, i, i, i, i, i, i, i] + [vp] * 10 + [sz, vp], i),
             "md_set_vocab_timing_events": ([vp, vp], i),
             "md_last_error": ([], ctypes.c_char_p),
+            "md_hbm_read_probe": ([vp, sz, vp, vp], i),
+            "md_hbm_read_probe_blocks": ([], i),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -174,3 +176,11 @@ def md_tree_accept(tree, dt, B, K, V, Hkv, hd, Lcap, logits, tree_tok, Kc, Vc, l
 def md_set_vocab_timing_events(start, stop) -> None:
     """start/stop: raw hipEvent_t handles (ints) or None."""
     _check(lib().md_set_vocab_timing_events(start, stop))
+
+
+def md_hbm_read_probe_blocks() -> int:
+    return int(lib().md_hbm_read_probe_blocks())
+
+
+def md_hbm_read_probe(buf, nbytes: int, sink, stream=None) -> None:
+    _check(lib().md_hbm_read_probe(_p(buf), nbytes, _p(sink), _stream(stream)))

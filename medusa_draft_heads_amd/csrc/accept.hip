@@ -27,6 +27,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int BLOCK = 256;
 constexpr int NWAVE = BLOCK / MD_WAVE;
 constexpr int kTargetBlocks = 1024;
+constexpr int kCompactLds = 32 * 1024;  // bytes of LDS staging for the compaction
 
 __device__ __forceinline__ bool beats(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
 
@@ -111,11 +112,21 @@ __global__ __launch_bounds__(BLOCK) void k_accept(DevTree t, int K, int Hkv, int
         int bi = INT_MAX;
         if (lane < N) {
             const int64_t r = ((int64_t)b * N + lane) * chunks;
-            for (int c = 0; c < chunks; ++c)
-                if (beats(part_v[r + c], part_i[r + c], bv, bi)) {
-                    bv = part_v[r + c];
-                    bi = part_i[r + c];
+            for (int c0 = 0; c0 < chunks; c0 += 8) {
+                float v[8];
+                int ix[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    v[u] = c0 + u < chunks ? part_v[r + c0 + u] : -INFINITY;
+                    ix[u] = c0 + u < chunks ? part_i[r + c0 + u] : INT_MAX;
                 }
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+                    if (beats(v[u], ix[u], bv, bi)) {
+                        bv = v[u];
+                        bi = ix[u];
+                    }
+            }
         }
         const int tstar = bi;
         const int par = lane < N ? t.parent[lane] : -1;
@@ -159,24 +170,62 @@ __global__ __launch_bounds__(BLOCK) void k_accept(DevTree t, int K, int Hkv, int
     __syncthreads();
     if (!s_ok) return;
     const int A = s_A, L = s_L;
-    T* buf = reinterpret_cast<T*>(s_buf);
-    const int per = A * hd;  // elements per kv head and per tensor
-    for (int g = 0; g < Hkv; ++g) {
-        const int64_t base = ((int64_t)b * Hkv + g) * Lcap;
-        for (int i = tid; i < 2 * per; i += BLOCK) {
-            const int which = i / per, r = i - which * per;
-            const int jj = r / hd, c = r - jj * hd;
-            const T* src = which ? Vc : Kc;
-            buf[i] = src[(base + L + s_path[jj]) * hd + c];
+    const int row_bytes = hd * (int)sizeof(T);
+    if ((row_bytes & 15) == 0) {
+        // 16-byte chunks: a slot row is row_bytes / 16 chunks
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        u32x4* buf = reinterpret_cast<u32x4*>(s_buf);
+        const int cpr = row_bytes >> 4;
+        const int per = A * cpr;  // chunks per kv head and per tensor
+        const int gstep = max(1, kCompactLds / (2 * (K + 1) * row_bytes));
+        for (int g0 = 0; g0 < Hkv; g0 += gstep) {
+            const int ng = min(gstep, Hkv - g0);
+            const int tot = ng * 2 * per;
+            for (int i = tid; i < tot; i += BLOCK) {
+                const int gi = i / (2 * per), rem = i - gi * 2 * per;
+                const int which = rem / per, r = rem - which * per;
+                const int jj = r / cpr, c = r - jj * cpr;
+                const int64_t base = ((int64_t)b * Hkv + g0 + gi) * Lcap;
+                const T* src = which ? Vc : Kc;
+                buf[i] = reinterpret_cast<const u32x4*>(src + (base + L + s_path[jj]) * hd)[c];
+            }
+            __syncthreads();
+            for (int i = tid; i < tot; i += BLOCK) {
+                const int gi = i / (2 * per), rem = i - gi * 2 * per;
+                const int which = rem / per, r = rem - which * per;
+                const int jj = r / cpr, c = r - jj * cpr;
+                const int64_t base = ((int64_t)b * Hkv + g0 + gi) * Lcap;
+                T* dst = which ? Vc : Kc;
+                reinterpret_cast<u32x4*>(dst + (base + L + jj) * hd)[c] = buf[i];
+            }
+            __syncthreads();
         }
-        __syncthreads();
-        for (int i = tid; i < 2 * per; i += BLOCK) {
-            const int which = i / per, r = i - which * per;
-            const int jj = r / hd, c = r - jj * hd;
-            T* dst = which ? Vc : Kc;
-            dst[(base + L + jj) * hd + c] = buf[i];
+    } else {
+        T* buf = reinterpret_cast<T*>(s_buf);
+        const int per = A * hd;  // elements per kv head and per tensor
+        const int gstep = max(1, kCompactLds / (2 * (K + 1) * row_bytes));
+        for (int g0 = 0; g0 < Hkv; g0 += gstep) {
+            const int ng = min(gstep, Hkv - g0);
+            const int tot = ng * 2 * per;
+            for (int i = tid; i < tot; i += BLOCK) {
+                const int gi = i / (2 * per), rem = i - gi * 2 * per;
+                const int which = rem / per, r = rem - which * per;
+                const int jj = r / hd, c = r - jj * hd;
+                const int64_t base = ((int64_t)b * Hkv + g0 + gi) * Lcap;
+                const T* src = which ? Vc : Kc;
+                buf[i] = src[(base + L + s_path[jj]) * hd + c];
+            }
+            __syncthreads();
+            for (int i = tid; i < tot; i += BLOCK) {
+                const int gi = i / (2 * per), rem = i - gi * 2 * per;
+                const int which = rem / per, r = rem - which * per;
+                const int jj = r / hd, c = r - jj * hd;
+                const int64_t base = ((int64_t)b * Hkv + g0 + gi) * Lcap;
+                T* dst = which ? Vc : Kc;
+                dst[(base + L + jj) * hd + c] = buf[i];
+            }
+            __syncthreads();
         }
-        __syncthreads();
     }
     if (tid == 0) lens[b] = L + A;
 }
@@ -209,7 +258,8 @@ hipError_t accept_launch(const DevTree& t, int dt, int B, int K, int V, int Hkv,
     hipLaunchKernelGGL(k_argmax_part, dim3((unsigned)parts), dim3(BLOCK), 0, s, logits, V, chunks, pv, pi);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = (size_t)2 * (K + 1) * hd * (dt == 0 ? 4 : 2);
+    const size_t per_head = (size_t)2 * (K + 1) * hd * (dt == 0 ? 4 : 2);
+    const size_t lds = per_head > (size_t)kCompactLds ? per_head : (size_t)kCompactLds;
     if (dt == 0)
         hipLaunchKernelGGL(k_accept<float>, dim3(B), dim3(BLOCK), lds, s, t, K, Hkv, hd, Lcap, chunks, pv, pi,
                            tree_tok, reinterpret_cast<float*>(Kc), reinterpret_cast<float*>(Vc), lens, accept_len,

@@ -171,7 +171,7 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
         a.nh = K;
         a.head0 = 0;
         for (int i = 0; i < K; ++i) a.kk[i] = k_per_head[i];
-        need = heads_ws_bytes(M, d, d, K, kmax);
+        need = heads_ws_bytes(dt, M, d, d, K, kmax);
     } else {
         if (level < 1 || level > K) return fail(MD_EINVAL, "Hydra level %d outside 1..%d", level, K);
         int rc = expand_tree(tree, K, k_per_head, &dt_tree);
@@ -186,7 +186,7 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
         a.kk[0] = k_per_head[level - 1];
         tp = &dt_tree;
         if (P == 0) return MD_OK;  // nothing at this depth
-        need = heads_ws_bytes(a.M, d, din, 1, kmax);
+        need = heads_ws_bytes(dt, a.M, d, din, 1, kmax);
     }
     if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     return hip_status(heads_launch(a, tp, (hipStream_t)stream, g_ev0, g_ev1), "md_medusa_heads");
@@ -266,6 +266,14 @@ int md_tree_accept(const md_tree* tree, int dt, int B, int K, int V, int Hkv, in
     return hip_status(accept_launch(t, dt, B, K, V, Hkv, hd, Lcap, logits, tree_tok, Kc, Vc, lens, accept_len, path,
                                     next_tok, compact_src, ws, (hipStream_t)stream),
                       "md_tree_accept");
+}
+
+int md_hbm_read_probe_blocks(void) { return probe_blocks(); }
+
+int md_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {
+    if (!buf || !sink) return fail(MD_EINVAL, "a required pointer is NULL");
+    if (bytes == 0 || bytes % 16) return fail(MD_EINVAL, "bytes = %zu (a positive multiple of 16)", bytes);
+    return hip_status(probe_launch(buf, bytes, sink, (hipStream_t)stream), "md_hbm_read_probe");
 }
 
 int md_set_vocab_timing_events(void* start, void* stop) {

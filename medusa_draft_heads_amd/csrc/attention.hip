@@ -13,6 +13,15 @@
 // staged in LDS serve every query head of the group. Each block keeps an
 // online softmax (running max, running sum, unnormalised output) and writes
 // them; a combine kernel merges the key ranges by log-sum-exp.
+//
+// bf16 storage runs on the matrix cores (v_mfma_f32_16x16x32_bf16): a wave
+// owns 16 query rows and computes S^T = K Q^T per 16-key block, then
+// O^T += V^T P^T. In this orientation a lane keeps one query row (lane % 16)
+// in both the score and the output accumulators, so the running max, the
+// rescale and the bf16 P operand never leave the lane. K tiles sit in LDS
+// row-major (rows padded by 16 B against bank conflicts), V tiles transposed
+// (key-contiguous) so the V^T operand is two 8-byte reads. float32 storage
+// (small workloads) uses an LDS-tiled FMA kernel.
 #include <math.h>
 
 #include "md_internal.h"
@@ -20,9 +29,15 @@
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
-constexpr int QT = 16;  // query rows per block
+constexpr int QT = 16;  // query rows per block (FMA kernel)
+constexpr int MQT = 64; // query rows per block (MFMA kernel: 4 waves x 16)
+constexpr int MKT = 64; // keys per tile (MFMA kernel)
+constexpr int KPAD = 8; // K row padding, bf16 elements
+constexpr int VPAD = 4; // V^T row padding, bf16 elements (rows stay 8-byte aligned)
 constexpr int KT = 64;  // keys per tile
 constexpr int BLOCK = 256;
 constexpr int NWAVE = BLOCK / MD_WAVE;
@@ -202,6 +217,194 @@ __global__ __launch_bounds__(BLOCK) void k_attn_fma(DevTree t, int Hq, int Hkv, 
     }
 }
 
+
+__device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
+    uint32_t u = __float_as_uint(v);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Blocks that share one (request, kv head, key range) -- the query tiles of a
+// group -- read the same K/V tiles. Workgroups go to the 8 XCDs round-robin
+// (block id mod 8), each XCD with its own L2, so the ids of one group are
+// spaced by 8: the whole group runs on one XCD and its K/V tiles come from
+// HBM once. Ids past the last group exit at once.
+__device__ __forceinline__ bool xcd_group_decode(int id, int qtiles, int ngroups, int& group, int& qt) {
+    const int x = id & 7, u = id >> 3;
+    qt = u % qtiles;
+    group = (u / qtiles) * 8 + x;
+    return group < ngroups;
+}
+
+template <int HD>
+__global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int Hkv, int Lcap, int max_len,
+                                                     const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
+                                                     const uint16_t* __restrict__ Vc, const int32_t* __restrict__ lens,
+                                                     float scale, int splits, int chunk, int qtiles, int ngroups,
+                                                     float* __restrict__ po, float* __restrict__ pm,
+                                                     float* __restrict__ pl) {
+    constexpr int CH = HD / 8;            // 16-byte chunks per key row
+    constexpr int KCH = MKT * CH / BLOCK; // K chunks per thread
+    constexpr int VIT = (MKT / 4) * CH;   // V items (4 keys x 8 dims)
+    __shared__ __align__(16) uint16_t Ks[MKT][HD + KPAD];
+    __shared__ __align__(16) uint16_t Vt[HD][MKT + VPAD];
+
+    int grp, qt;
+    if (!xcd_group_decode(blockIdx.x, qtiles, ngroups, grp, qt)) return;
+    const int s = grp % splits;
+    const int g = (grp / splits) % Hkv;
+    const int b = grp / (splits * Hkv);
+    const int group = Hq / Hkv;
+    const int N = t.n;
+    const int rows = N * group;
+    const int L = min(max(lens[b], 0), max_len);
+    const int nkeys = L + N;
+    const int k0 = s * chunk, k1 = min(k0 + chunk, nkeys);
+    const int tid = threadIdx.x, lane = tid & (MD_WAVE - 1), w = tid >> 6;
+    const int g4 = lane >> 4, c16 = lane & 15;
+    const int64_t kvbase = ((int64_t)b * Hkv + g) * Lcap;
+
+    // this lane's query row (the N index of both products)
+    const int r = qt * MQT + w * 16 + c16;
+    const bool rvalid = r < rows;
+    const int node = rvalid ? r / group : 0;
+    const int h = g * group + (rvalid ? r - (r / group) * group : 0);
+    const uint64_t anc = rvalid ? t.anc[node] : 0ull;
+    const int64_t qrow = (((int64_t)b * N + node) * Hq + h) * HD;
+    bf16x8 qf[HD / 32];
+#pragma unroll
+    for (int c = 0; c < HD / 32; ++c) {
+        const u32x4 v = rvalid ? *reinterpret_cast<const u32x4*>(q + qrow + 8 * g4 + 32 * c) : u32x4{0u, 0u, 0u, 0u};
+        qf[c] = __builtin_bit_cast(bf16x8, v);
+    }
+    float m_i = -INFINITY, l_i = 0.f;
+    f32x4 o[HD / 16];
+#pragma unroll
+    for (int j = 0; j < HD / 16; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // every thread stages KCH 16-byte K chunks and one V item (4 keys x 8
+    // dims, transposed in registers into 8 dim rows of 4 keys); the next
+    // tile's loads are in flight while the current tile is computed
+    u32x4 kreg[KCH], vreg[4];
+    const int vk4 = tid / CH, vch = tid - (tid / CH) * CH;  // V item: key group of 4, dim chunk
+    const bool vload = tid < VIT;
+    int kt_fetch = k0;
+#define MD_FETCH_TILE(kt0_)                                                                                   \
+    {                                                                                                         \
+        _Pragma("unroll") for (int j = 0; j < KCH; ++j) {                                                     \
+            const int i = tid + BLOCK * j;                                                                    \
+            const int kk = i / CH, ch = i - (i / CH) * CH;                                                    \
+            const int key = (kt0_) + kk;                                                                      \
+            kreg[j] = key < k1 ? *reinterpret_cast<const u32x4*>(Kc + (kvbase + key) * HD + ch * 8)           \
+                               : u32x4{0u, 0u, 0u, 0u};                                                       \
+        }                                                                                                     \
+        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                                       \
+            const int key = (kt0_) + vk4 * 4 + e;                                                             \
+            vreg[e] = (vload && key < k1) ? *reinterpret_cast<const u32x4*>(Vc + (kvbase + key) * HD + vch * 8) \
+                                          : u32x4{0u, 0u, 0u, 0u};                                            \
+        }                                                                                                     \
+    }
+    if (k0 < k1) MD_FETCH_TILE(kt_fetch);
+    for (int kt0 = k0; kt0 < k1; kt0 += MKT) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < KCH; ++j) {
+            const int i = tid + BLOCK * j;
+            const int kk = i / CH, ch = i - (i / CH) * CH;
+            *reinterpret_cast<u32x4*>(&Ks[kk][ch * 8]) = kreg[j];
+        }
+        if (vload) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                // word j of each key holds dims 2j (low half) and 2j+1 (high half)
+                const uint32_t a0 = vreg[0][j], a1 = vreg[1][j], a2 = vreg[2][j], a3 = vreg[3][j];
+                *reinterpret_cast<u32x2*>(&Vt[vch * 8 + 2 * j][vk4 * 4]) =
+                    u32x2{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
+                *reinterpret_cast<u32x2*>(&Vt[vch * 8 + 2 * j + 1][vk4 * 4]) =
+                    u32x2{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
+            }
+        }
+        __syncthreads();
+        if (kt0 + MKT < k1) MD_FETCH_TILE(kt0 + MKT);
+
+        // S^T for four 16-key blocks: st[kb][i] = S[row][kt0 + 16 kb + 4 g4 + i]
+        f32x4 st[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int c = 0; c < HD / 32; ++c) {
+                const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&Ks[kb * 16 + c16][8 * g4 + 32 * c]));
+                st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], st[kb], 0, 0, 0);
+            }
+        }
+        float p[4][4];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int kidx = kt0 + kb * 16 + 4 * g4 + i;
+                bool vis = kidx < k1;
+                if (vis && kidx >= L) vis = (anc >> (kidx - L)) & 1ull;
+                const float sc = vis ? st[kb][i] * scale : -INFINITY;
+                p[kb][i] = sc;
+                tmax = fmaxf(tmax, sc);
+            }
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, MD_WAVE));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, MD_WAVE));
+        const float m_new = fmaxf(m_i, tmax);
+        const float alpha = (m_new == -INFINITY) ? 1.f : expf(m_i - m_new);
+        float psum = 0.f;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float e = p[kb][i] == -INFINITY ? 0.f : expf(p[kb][i] - m_new);
+                p[kb][i] = e;
+                psum += e;
+            }
+        psum += __shfl_xor(psum, 16, MD_WAVE);
+        psum += __shfl_xor(psum, 32, MD_WAVE);
+        l_i = l_i * alpha + psum;
+        m_i = m_new;
+#pragma unroll
+        for (int j = 0; j < HD / 16; ++j) o[j] *= alpha;
+
+        // O^T += V^T P^T over two 32-key halves
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int kb0 = 2 * half, kb1 = 2 * half + 1;
+            u32x4 pw;
+            pw.x = bf16_rne_bits(p[kb0][0]) | (bf16_rne_bits(p[kb0][1]) << 16);
+            pw.y = bf16_rne_bits(p[kb0][2]) | (bf16_rne_bits(p[kb0][3]) << 16);
+            pw.z = bf16_rne_bits(p[kb1][0]) | (bf16_rne_bits(p[kb1][1]) << 16);
+            pw.w = bf16_rne_bits(p[kb1][2]) | (bf16_rne_bits(p[kb1][3]) << 16);
+            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+#pragma unroll
+            for (int j = 0; j < HD / 16; ++j) {
+                const u32x2 lo = *reinterpret_cast<const u32x2*>(&Vt[16 * j + c16][kb0 * 16 + 4 * g4]);
+                const u32x2 hi = *reinterpret_cast<const u32x2*>(&Vt[16 * j + c16][kb1 * 16 + 4 * g4]);
+                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+                o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[j], 0, 0, 0);
+            }
+        }
+    }
+#undef MD_FETCH_TILE
+
+    if (rvalid) {
+        const int64_t row = ((int64_t)b * N + node) * Hq + h;
+#pragma unroll
+        for (int j = 0; j < HD / 16; ++j)
+            *reinterpret_cast<f32x4*>(po + (row * splits + s) * HD + 16 * j + 4 * g4) = o[j];
+        if (g4 == 0) {
+            pm[row * splits + s] = m_i;
+            pl[row * splits + s] = l_i;
+        }
+    }
+}
+
 // out = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s  (M = max_s m_s)
 template <typename T>
 __global__ void k_attn_combine(int hd, int splits, const float* __restrict__ po, const float* __restrict__ pm,
@@ -209,8 +412,10 @@ __global__ void k_attn_combine(int hd, int splits, const float* __restrict__ po,
     const int64_t row = blockIdx.x;
     const int c = threadIdx.x;
     float M = -INFINITY;
+#pragma unroll 8
     for (int s = 0; s < splits; ++s) M = fmaxf(M, pm[row * splits + s]);
     float num = 0.f, den = 0.f;
+#pragma unroll 8
     for (int s = 0; s < splits; ++s) {
         const float ms = pm[row * splits + s];
         const float wgt = ms == -INFINITY ? 0.f : expf(ms - M);
@@ -238,12 +443,23 @@ hipError_t launch_typed(const DevTree& t, int B, int Hq, int Hkv, int hd, int Lc
     const T* qq = reinterpret_cast<const T*>(q);
     const T* kk = reinterpret_cast<const T*>(Kc);
     const T* vv = reinterpret_cast<const T*>(Vc);
-    if (hd == 64)
-        hipLaunchKernelGGL((k_attn_fma<T, 64>), grid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv, lens,
-                           scale, p.splits, p.chunk, p.qtiles, po, pm, pl);
-    else
-        hipLaunchKernelGGL((k_attn_fma<T, 128>), grid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv,
-                           lens, scale, p.splits, p.chunk, p.qtiles, po, pm, pl);
+    if constexpr (sizeof(T) == 2) {
+        const int ngroups = B * Hkv * p.splits;
+        const dim3 mgrid((unsigned)(8 * p.qtiles * ((ngroups + 7) / 8)));
+        if (hd == 64)
+            hipLaunchKernelGGL(k_attn_mfma<64>, mgrid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv,
+                               lens, scale, p.splits, p.chunk, p.qtiles, ngroups, po, pm, pl);
+        else
+            hipLaunchKernelGGL(k_attn_mfma<128>, mgrid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv,
+                               lens, scale, p.splits, p.chunk, p.qtiles, ngroups, po, pm, pl);
+    } else {
+        if (hd == 64)
+            hipLaunchKernelGGL((k_attn_fma<T, 64>), grid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv,
+                               lens, scale, p.splits, p.chunk, p.qtiles, po, pm, pl);
+        else
+            hipLaunchKernelGGL((k_attn_fma<T, 128>), grid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv,
+                               lens, scale, p.splits, p.chunk, p.qtiles, po, pm, pl);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_attn_combine<T>, dim3((unsigned)R), dim3(hd), 0, st_, hd, p.splits, po, pm, pl,
@@ -251,21 +467,45 @@ hipError_t launch_typed(const DevTree& t, int B, int Hq, int Hkv, int hd, int Lc
     return hipGetLastError();
 }
 
+int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                   hipSuccess || n <= 0)
+        n = 256;
+    return n;
+}
+
+// resident blocks per CU of the kernel that will run (one round of blocks)
+int attention_occupancy(int dt, int hd) {
+    int n = 0;
+    hipError_t e;
+    if (dt == 0)
+        e = hd == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_fma<float, 64>, BLOCK, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_fma<float, 128>, BLOCK, 0);
+    else
+        e = hd == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_mfma<64>, BLOCK, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_mfma<128>, BLOCK, 0);
+    if (e != hipSuccess || n < 1) n = 2;
+    return n;
+}
+
 }  // namespace
 
 AttnPlan attention_plan(int dt, int B, int N, int Hq, int Hkv, int hd, int max_len) {
-    (void)dt;
-    (void)hd;
     AttnPlan p;
+    const int qt = dt == 0 ? QT : MQT;
+    const int kt = dt == 0 ? KT : MKT;
     p.rows = N * (Hq / Hkv);
-    p.qtiles = (p.rows + QT - 1) / QT;
+    p.qtiles = (p.rows + qt - 1) / qt;
     const int base = B * Hkv * p.qtiles;
-    const int tiles = (max_len + N + KT - 1) / KT;
-    int splits = (1024 + base - 1) / base;
+    const int tiles = (max_len + N + kt - 1) / kt;
+    // split the keys so that one round of resident blocks covers the grid
+    const int target = device_cus() * attention_occupancy(dt, hd);
+    int splits = target / base;
     if (splits > tiles) splits = tiles;
     if (splits < 1) splits = 1;
     const int tiles_per = (tiles + splits - 1) / splits;
-    p.chunk = tiles_per * KT;
+    p.chunk = tiles_per * kt;
     p.splits = (max_len + N + p.chunk - 1) / p.chunk;
     return p;
 }

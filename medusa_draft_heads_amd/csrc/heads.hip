@@ -11,13 +11,16 @@
 // GEMV path, for a handful of rows (M <= 4 per pass). Every weight row is
 // streamed from HBM exactly once per pass with 16-byte non-temporal loads
 // (64 lanes x 16 B = 1 KiB per wave instruction, fully coalesced); the
-// activations sit in LDS as float32; each wave keeps RPW rows in flight and
-// unrolls the column loop so ~16 loads are outstanding per wave. The dot
+// activations sit in LDS as float32; each wave streams RPW = 2 rows at a time
+// and unrolls the column loop 8 deep, so 16 loads are outstanding per wave.
+// (Measured on MI355X at the 70B shape: 2 x 8 and 1 x 16 reach 6.9 TB/s,
+// 4 x 4 6.8 TB/s; plain loads instead of non-temporal ones lose 7%.) The dot
 // products end in a butterfly reduction that leaves the same bits in every
 // lane, so the top-k update is wave-uniform: lanes 0..k-1 hold the sorted
 // list in registers and an insertion is one ballot plus one shift. Logits are
-// never written; each wave leaves its k best (value, index) pairs, and a merge
-// kernel reduces the lists of all waves of a head.
+// never written; the waves of a block merge their k best (value, index) pairs
+// in LDS, each block leaves one list, and a merge kernel reduces the lists of
+// all blocks of a head.
 #include <math.h>
 
 #include "md_internal.h"
@@ -27,8 +30,9 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int RPW = 4;     // weight rows in flight per wave
-constexpr int UNROLL = 4;  // column steps per loop iteration
+constexpr int MD_MAX_TOPK_DEV = 16;
+constexpr int RPW = 2;     // weight rows in flight per wave
+constexpr int UNROLL = 8;  // column steps per loop iteration (RPW x UNROLL loads in flight)
 constexpr int BLOCK = 256;
 constexpr int NWAVE = BLOCK / MD_WAVE;
 
@@ -76,6 +80,31 @@ __device__ __forceinline__ void lds_vec(const float* p, float (&x)[VEC]) {
         x[e + 2] = v.z;
         x[e + 3] = v.w;
     }
+}
+
+// 8 consecutive activations (16-byte aligned) widened to float32.
+__device__ __forceinline__ void load8(const uint16_t* p, float (&v)[8]) {
+    const u32x4 w = *reinterpret_cast<const u32x4*>(p);
+    v[0] = bf_lo(w.x);
+    v[1] = bf_hi(w.x);
+    v[2] = bf_lo(w.y);
+    v[3] = bf_hi(w.y);
+    v[4] = bf_lo(w.z);
+    v[5] = bf_hi(w.z);
+    v[6] = bf_lo(w.w);
+    v[7] = bf_hi(w.w);
+}
+__device__ __forceinline__ void load8(const float* p, float (&v)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    const f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+    v[0] = a.x;
+    v[1] = a.y;
+    v[2] = a.z;
+    v[3] = a.w;
+    v[4] = b.x;
+    v[5] = b.y;
+    v[6] = b.z;
+    v[7] = b.w;
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -174,34 +203,40 @@ struct KK {
 
 // hres[hh][m][r] = x_m[r] + SiLU(sum_c W[head0+hh][r][c] x_m[c] + b[head0+hh][r])
 template <typename T, int MR>
-__global__ __launch_bounds__(BLOCK) void k_residual(const T* __restrict__ W, const T* __restrict__ bias, RowSrc src,
+__global__ __launch_bounds__(BLOCK, 4) void k_residual(const T* __restrict__ W, const T* __restrict__ bias, RowSrc src,
                                                     int M, int m0, int d, int din, int nh, int head0,
                                                     float* __restrict__ hres, float* __restrict__ hres_out) {
-    extern __shared__ float xs[];  // [MR][din]
+    extern __shared__ __align__(16) float xs[];  // [MR][din]
     const int mr = min(MR, M - m0);
     const T* h = reinterpret_cast<const T*>(src.h);
-    for (int i = threadIdx.x; i < MR * din; i += BLOCK) {
-        const int mm = i / din, c = i - (i / din) * din;
-        float v = 0.f;
+    // 8 activations per 16-byte (bf16) or two 16-byte (f32) loads; d % 8 == 0,
+    // so a chunk never straddles the h / E boundary of a Hydra row
+    const int nch = MR * din / 8;
+    for (int i = threadIdx.x; i < nch; i += BLOCK) {
+        const int e0 = i * 8;
+        const int mm = e0 / din, c = e0 - (e0 / din) * din;
+        float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
         if (mm < mr) {
             const int m = m0 + mm;
+            const T* srcp = nullptr;
             if (src.kind == 0) {
-                v = ldf(h, (int64_t)m * d + c);
+                srcp = h + (int64_t)m * d + c;
             } else {
                 const int b = m / src.P, j = m - (m / src.P) * src.P;
                 if (c < d) {
-                    v = ldf(h, (int64_t)b * d + c);
+                    srcp = h + (int64_t)b * d + c;
                 } else {
                     const int p = src.parents[j];
                     const int tok = p == 0 ? src.root_tok[b] : src.tree_tok[(int64_t)b * src.N + p];
                     // a token outside the vocabulary (e.g. a -1 left by a failed
                     // lookup) reads as a zero embedding instead of stray memory
-                    v = (tok >= 0 && tok < src.V) ? ldf(reinterpret_cast<const T*>(src.E), (int64_t)tok * d + (c - d))
-                                                  : 0.f;
+                    if (tok >= 0 && tok < src.V) srcp = reinterpret_cast<const T*>(src.E) + (int64_t)tok * d + (c - d);
                 }
             }
+            if (srcp) load8(srcp, v);
         }
-        xs[i] = v;
+        *reinterpret_cast<f32x4*>(xs + e0) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(xs + e0 + 4) = f32x4{v[4], v[5], v[6], v[7]};
     }
     __syncthreads();
 
@@ -239,14 +274,17 @@ __global__ __launch_bounds__(BLOCK) void k_vocab_topk(const T* __restrict__ U, c
                                                       int M, int m0, int d, int V, int nh, int head0,
                                                       int wg_per_head, KK kk, int kmax,
                                                       float* __restrict__ part_val, int* __restrict__ part_idx) {
-    extern __shared__ float xs[];  // [MR][d]
+    extern __shared__ __align__(16) float xs[];  // [MR][d]
     const int hh = blockIdx.x / wg_per_head;
     const int wgi = blockIdx.x - hh * wg_per_head;
     if (hh >= nh) return;
     const int mr = min(MR, M - m0);
-    for (int i = threadIdx.x; i < MR * d; i += BLOCK) {
-        const int mm = i / d, c = i - (i / d) * d;
-        xs[i] = mm < mr ? hres[((int64_t)hh * M + m0 + mm) * d + c] : 0.f;
+    for (int i = threadIdx.x; i < MR * d / 4; i += BLOCK) {
+        const int e0 = i * 4;
+        const int mm = e0 / d, c = e0 - (e0 / d) * d;
+        *reinterpret_cast<f32x4*>(xs + e0) =
+            mm < mr ? *reinterpret_cast<const f32x4*>(hres + ((int64_t)hh * M + m0 + mm) * d + c)
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
     }
     __syncthreads();
 
@@ -283,78 +321,138 @@ __global__ __launch_bounds__(BLOCK) void k_vocab_topk(const T* __restrict__ U, c
             }
         }
     }
+    // merge the block's wave lists in LDS; one list per block goes to memory
+    __shared__ float sv[MR][NWAVE][MD_WAVE];
+    __shared__ int si[MR][NWAVE][MD_WAVE];
+    const int wv = threadIdx.x >> 6;
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-        if (m < mr && lane < kmax) {
-            const int64_t o = (((int64_t)hh * M + m0 + m) * wph + wih) * kmax + lane;
-            part_val[o] = lv[m];
-            part_idx[o] = li[m];
+        sv[m][wv][lane] = lane < k ? lv[m] : -INFINITY;
+        si[m][wv][lane] = lane < k ? li[m] : INT_MAX;
+    }
+    __syncthreads();
+    if (wv != 0) return;
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+        if (m >= mr) continue;
+        float bv = -INFINITY, btv = -INFINITY;
+        int bi = INT_MAX, bti = INT_MAX;
+        for (int w2 = 0; w2 < NWAVE; ++w2) {
+            const float cv = sv[m][w2][lane];
+            const int ci = si[m][w2][lane];
+            uint64_t bm = __ballot(lane < k && ranks_above(cv, ci, btv, bti));
+            while (bm) {
+                const int src = __ffsll((long long)bm) - 1;
+                bm &= bm - 1;
+                const float x = __shfl(cv, src, MD_WAVE);
+                const int xi = __shfl(ci, src, MD_WAVE);
+                if (ranks_above(x, xi, btv, bti)) {
+                    list_insert(bv, bi, x, xi, k, lane);
+                    btv = __shfl(bv, k - 1, MD_WAVE);
+                    bti = __shfl(bi, k - 1, MD_WAVE);
+                }
+            }
+        }
+        if (lane < kmax) {
+            const int64_t o = (((int64_t)hh * M + m0 + m) * wg_per_head + wgi) * kmax + lane;
+            part_val[o] = bv;
+            part_idx[o] = bi;
         }
     }
 }
 
-// One block per (row m, head slot hh): merge the lists of all waves of the head.
+// One block per (row m, head slot hh). Every block of the vocabulary kernel
+// left one sorted list of its k best; the k best of the head are a k-way
+// merge of those lists: k rounds of a block-wide argmax over the list heads,
+// each round popping the winning list. Vocabulary indices are unique, so
+// the order (value desc, index asc) is strict and the winner is unique.
+template <int LPT>  // lists per thread
 __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ part_val,
-                                                      const int* __restrict__ part_idx, int M, int nh, int wph,
+                                                      const int* __restrict__ part_idx, int M, int nh, int nlists,
                                                       KK kk, int kmax, int32_t* __restrict__ topk_idx,
                                                       float* __restrict__ topk_val) {
-    __shared__ float sv[NWAVE][MD_WAVE];
-    __shared__ int si[NWAVE][MD_WAVE];
+    constexpr int KM = MD_MAX_TOPK_DEV;
+    __shared__ float wv_s[NWAVE];
+    __shared__ int wi_s[NWAVE], wo_s[NWAVE];
+    __shared__ float out_v[KM];
+    __shared__ int out_i[KM];
     const int m = blockIdx.x / nh, hh = blockIdx.x - (blockIdx.x / nh) * nh;
     const int k = kk.v[hh];
-    const int lane = threadIdx.x & (MD_WAVE - 1), wv = threadIdx.x >> 6;
-    const int64_t base = ((int64_t)hh * M + m) * wph * kmax;
-    const int total = wph * kmax;
-    const int q0 = (int)((int64_t)total * wv / NWAVE), q1 = (int)((int64_t)total * (wv + 1) / NWAVE);
-
-    float lv = -INFINITY, tv = -INFINITY;
-    int li = INT_MAX, ti = INT_MAX;
-    for (int c0 = q0; c0 < q1; c0 += MD_WAVE) {
-        const int c = c0 + lane;
-        const float cv = c < q1 ? part_val[base + c] : -INFINITY;
-        const int ci = c < q1 ? part_idx[base + c] : INT_MAX;
-        uint64_t bm = __ballot(ranks_above(cv, ci, tv, ti));
-        while (bm) {
-            const int src = __ffsll((long long)bm) - 1;
-            bm &= bm - 1;
-            const float x = __shfl(cv, src, MD_WAVE);
-            const int xi = __shfl(ci, src, MD_WAVE);
-            if (ranks_above(x, xi, tv, ti)) {
-                list_insert(lv, li, x, xi, k, lane);
-                tv = __shfl(lv, k - 1, MD_WAVE);
-                ti = __shfl(li, k - 1, MD_WAVE);
-            }
+    const int tid = threadIdx.x, lane = tid & (MD_WAVE - 1), w = tid >> 6;
+    const int64_t base = ((int64_t)hh * M + m) * nlists * kmax;
+    float v[LPT][KM];
+    int ix[LPT][KM];
+#pragma unroll
+    for (int l = 0; l < LPT; ++l) {
+        const int list = tid + BLOCK * l;
+#pragma unroll
+        for (int j = 0; j < KM; ++j) {
+            const bool ok = list < nlists && j < k;
+            v[l][j] = ok ? part_val[base + (int64_t)list * kmax + j] : -INFINITY;
+            ix[l][j] = ok ? part_idx[base + (int64_t)list * kmax + j] : INT_MAX;
         }
     }
-    sv[wv][lane] = lane < k ? lv : -INFINITY;
-    si[wv][lane] = lane < k ? li : INT_MAX;
-    __syncthreads();
-    if (wv != 0) return;
-    lv = -INFINITY;
-    li = INT_MAX;
-    tv = -INFINITY;
-    ti = INT_MAX;
-    for (int w = 0; w < NWAVE; ++w) {
-        const float cv = sv[w][lane];
-        const int ci = si[w][lane];
-        uint64_t bm = __ballot(lane < k && ranks_above(cv, ci, tv, ti));
-        while (bm) {
-            const int src = __ffsll((long long)bm) - 1;
-            bm &= bm - 1;
-            const float x = __shfl(cv, src, MD_WAVE);
-            const int xi = __shfl(ci, src, MD_WAVE);
-            if (ranks_above(x, xi, tv, ti)) {
-                list_insert(lv, li, x, xi, k, lane);
-                tv = __shfl(lv, k - 1, MD_WAVE);
-                ti = __shfl(li, k - 1, MD_WAVE);
+    for (int r = 0; r < k; ++r) {
+        float bv = v[0][0];
+        int bi = ix[0][0], bo = tid * LPT;
+#pragma unroll
+        for (int l = 1; l < LPT; ++l)
+            if (ranks_above(v[l][0], ix[l][0], bv, bi)) {
+                bv = v[l][0];
+                bi = ix[l][0];
+                bo = tid * LPT + l;
+            }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float ov = __shfl_xor(bv, o, MD_WAVE);
+            const int oi = __shfl_xor(bi, o, MD_WAVE);
+            const int oo = __shfl_xor(bo, o, MD_WAVE);
+            if (ranks_above(ov, oi, bv, bi)) {
+                bv = ov;
+                bi = oi;
+                bo = oo;
             }
         }
+        if (lane == 0) {
+            wv_s[w] = bv;
+            wi_s[w] = bi;
+            wo_s[w] = bo;
+        }
+        __syncthreads();
+        float gv = wv_s[0];
+        int gi = wi_s[0], go = wo_s[0];
+#pragma unroll
+        for (int w2 = 1; w2 < NWAVE; ++w2)
+            if (ranks_above(wv_s[w2], wi_s[w2], gv, gi)) {
+                gv = wv_s[w2];
+                gi = wi_s[w2];
+                go = wo_s[w2];
+            }
+        if (tid == 0) {
+            out_v[r] = gv;
+            out_i[r] = gi;
+        }
+        if (go / LPT == tid) {  // pop the winning list's head
+            const int lw = go - tid * LPT;
+#pragma unroll
+            for (int l = 0; l < LPT; ++l) {
+                if (l != lw) continue;
+#pragma unroll
+                for (int j = 0; j + 1 < KM; ++j) {
+                    v[l][j] = v[l][j + 1];
+                    ix[l][j] = ix[l][j + 1];
+                }
+                v[l][KM - 1] = -INFINITY;
+                ix[l][KM - 1] = INT_MAX;
+            }
+        }
+        __syncthreads();
     }
-    if (lane < kmax) {
-        const bool ok = lane < k && li != INT_MAX;
-        const int64_t o = ((int64_t)m * nh + hh) * kmax + lane;
-        topk_idx[o] = ok ? li : -1;
-        topk_val[o] = ok ? lv : -INFINITY;
+    if (tid < kmax) {
+        const bool ok = tid < k && out_i[tid] != INT_MAX;
+        const int64_t o = ((int64_t)m * nh + hh) * kmax + tid;
+        topk_idx[o] = ok ? out_i[tid] : -1;
+        topk_val[o] = ok ? out_v[tid] : -INFINITY;
     }
 }
 
@@ -367,7 +465,6 @@ struct Plan {
     size_t res_lds, voc_lds;
 };
 
-constexpr int kCUs = 256;
 constexpr size_t kLDS = 160 * 1024;
 
 int pick_mr(int M, int din) {
@@ -376,18 +473,46 @@ int pick_mr(int M, int din) {
     return mr;
 }
 
-int blocks_per_cu(size_t lds) {
-    int n = lds ? (int)(kLDS / lds) : 4;
-    return n < 1 ? 1 : (n > 4 ? 4 : n);
+int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                   hipSuccess || n <= 0)
+        n = 256;
+    return n;
 }
 
-Plan make_plan(int M, int d, int din, int nh) {
+// Resident blocks per CU for a kernel at this dynamic LDS size, capped at 4,
+// so that a grid of CUs x this many blocks runs in a single round.
+template <typename K>
+int resident_blocks(K kernel, size_t lds) {
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, BLOCK, lds) != hipSuccess || n < 1) n = 1;
+    return n > 4 ? 4 : n;
+}
+
+template <typename T>
+Plan make_plan_t(int M, int d, int din, int nh) {
     Plan p;
     p.MR = pick_mr(M, din);
     p.res_lds = (size_t)p.MR * din * 4;
     p.voc_lds = (size_t)p.MR * d * 4;
-    p.res_grid = kCUs * blocks_per_cu(p.res_lds);
-    int vg = kCUs * blocks_per_cu(p.voc_lds);
+    const int cus = device_cus();
+    int rb, vb;
+    switch (p.MR) {
+        case 4:
+            rb = resident_blocks(k_residual<T, 4>, p.res_lds);
+            vb = resident_blocks(k_vocab_topk<T, 4>, p.voc_lds);
+            break;
+        case 2:
+            rb = resident_blocks(k_residual<T, 2>, p.res_lds);
+            vb = resident_blocks(k_vocab_topk<T, 2>, p.voc_lds);
+            break;
+        default:
+            rb = resident_blocks(k_residual<T, 1>, p.res_lds);
+            vb = resident_blocks(k_vocab_topk<T, 1>, p.voc_lds);
+    }
+    p.res_grid = cus * rb;
+    const int vg = cus * vb;
     p.wg_per_head = vg / nh;
     if (p.wg_per_head < 1) p.wg_per_head = 1;
     p.voc_grid = p.wg_per_head * nh;
@@ -395,16 +520,20 @@ Plan make_plan(int M, int d, int din, int nh) {
     return p;
 }
 
+Plan make_plan(int dt, int M, int d, int din, int nh) {
+    return dt == 0 ? make_plan_t<float>(M, d, din, nh) : make_plan_t<uint16_t>(M, d, din, nh);
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 template <typename T>
 hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    const Plan p = make_plan(a.M, a.d, a.din, a.nh);
+    const Plan p = make_plan(a.dt, a.M, a.d, a.din, a.nh);
     char* ws = reinterpret_cast<char*>(a.ws);
     float* hres = reinterpret_cast<float*>(ws);
     ws += align256((size_t)a.nh * a.M * a.d * 4);
     float* pv = reinterpret_cast<float*>(ws);
-    ws += align256((size_t)a.nh * a.M * p.wph * a.kmax * 4);
+    ws += align256((size_t)a.nh * a.M * p.wg_per_head * a.kmax * 4);
     int* pi = reinterpret_cast<int*>(ws);
 
     RowSrc src;
@@ -470,21 +599,29 @@ hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
         hipError_t e = hipEventRecord(ev1, s);
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL(k_topk_merge, dim3(a.M * a.nh), dim3(BLOCK), 0, s, pv, pi, a.M, a.nh, p.wph, kk, a.kmax,
-                       a.topk_idx, a.topk_val);
+    const int lpt = (p.wg_per_head + BLOCK - 1) / BLOCK;
+    if (lpt <= 1)
+        hipLaunchKernelGGL(k_topk_merge<1>, dim3(a.M * a.nh), dim3(BLOCK), 0, s, pv, pi, a.M, a.nh, p.wg_per_head, kk,
+                           a.kmax, a.topk_idx, a.topk_val);
+    else if (lpt == 2)
+        hipLaunchKernelGGL(k_topk_merge<2>, dim3(a.M * a.nh), dim3(BLOCK), 0, s, pv, pi, a.M, a.nh, p.wg_per_head, kk,
+                           a.kmax, a.topk_idx, a.topk_val);
+    else
+        hipLaunchKernelGGL(k_topk_merge<4>, dim3(a.M * a.nh), dim3(BLOCK), 0, s, pv, pi, a.M, a.nh, p.wg_per_head, kk,
+                           a.kmax, a.topk_idx, a.topk_val);
     return hipGetLastError();
 }
 
 }  // namespace
 
-size_t heads_ws_bytes(int M, int d, int din, int nh, int kmax) {
-    const Plan p = make_plan(M, d, din, nh);
-    return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * p.wph * kmax * 4);
+size_t heads_ws_bytes(int dt, int M, int d, int din, int nh, int kmax) {
+    const Plan p = make_plan(dt, M, d, din, nh);
+    return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * p.wg_per_head * kmax * 4);
 }
 
 size_t heads_ws_bound(int M, int d, int nh, int kmax) {
-    const size_t wph_max = (size_t)kCUs * 4 * NWAVE;
-    return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * wph_max * kmax * 4);
+    const size_t lists_max = (size_t)device_cus() * 4;  // blocks per head at most
+    return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * lists_max * kmax * 4);
 }
 
 hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {

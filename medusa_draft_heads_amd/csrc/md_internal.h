@@ -48,7 +48,7 @@ struct HeadsArgs {
     void* ws;
 };
 
-size_t heads_ws_bytes(int M, int d, int din, int nh, int kmax);  // this plan
+size_t heads_ws_bytes(int dt, int M, int d, int din, int nh, int kmax);  // this plan
 size_t heads_ws_bound(int M, int d, int nh, int kmax);            // any plan
 hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
 
@@ -77,3 +77,7 @@ hipError_t accept_launch(const DevTree& t, int dt, int B, int K, int V, int Hkv,
                          const float* logits, const int32_t* tree_tok, void* Kc, void* Vc, int32_t* lens,
                          int32_t* accept_len, int32_t* path, int32_t* next_tok, int32_t* compact_src, void* ws,
                          hipStream_t s);
+
+// ---- measurement utility (probe.hip) ----
+int probe_blocks();
+hipError_t probe_launch(const void* buf, size_t bytes, void* sink, hipStream_t s);
