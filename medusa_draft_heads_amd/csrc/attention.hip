@@ -131,6 +131,7 @@ __global__ __launch_bounds__(BLOCK) void k_attn_fma(DevTree t, int Hq, int Hkv, 
         anc_s[tid] = r < rows ? t.anc[r / group] : 0ull;
     }
 
+    const float scale_log2 = scale * 1.44269504088896340736f;
     float m_i[ROWS_PER_WAVE], l_i[ROWS_PER_WAVE];
 #pragma unroll
     for (int j = 0; j < ROWS_PER_WAVE; ++j) {
@@ -170,11 +171,11 @@ __global__ __launch_bounds__(BLOCK) void k_attn_fma(DevTree t, int Hq, int Hkv, 
             for (int c = 0; c < HD; ++c) sc = fmaf(Qs[qi][c], Ks[lane][c], sc);
             bool vis = in_range;
             if (vis && key >= L) vis = (anc_s[qi] >> (key - L)) & 1ull;
-            sc = vis ? sc * scale : -INFINITY;
+            sc = vis ? sc * scale_log2 : -INFINITY;
             const float mx = wave_max(sc);
             const float m_new = fmaxf(m_i[j], mx);
-            const float alpha = (m_new == -INFINITY) ? 1.f : expf(m_i[j] - m_new);
-            const float p = vis ? expf(sc - m_new) : 0.f;
+            const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_i[j] - m_new);
+            const float p = vis ? exp2f(sc - m_new) : 0.f;
             l_i[j] = l_i[j] * alpha + wave_sum(p);
             m_i[j] = m_new;
             Ps[qi][lane] = p;
@@ -218,10 +219,19 @@ __global__ __launch_bounds__(BLOCK) void k_attn_fma(DevTree t, int Hq, int Hkv, 
 }
 
 
-__device__ __forceinline__ uint32_t bf16_rne_bits(float v) {
-    uint32_t u = __float_as_uint(v);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return u >> 16;
+// Value of lane ^ 16 / lane ^ 32. The gfx950 row swaps exchange 16-lane rows
+// between two registers; swapping a register with itself leaves the own row
+// in one result and the partner row in the other, in an order that depends
+// on the row -- so the pair is only combined symmetrically (max, +).
+__device__ __forceinline__ float xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+    return a == v ? b : a;
+}
+__device__ __forceinline__ float xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+    return a == v ? b : a;
 }
 
 // Blocks that share one (request, kv head, key range) -- the query tiles of a
@@ -277,6 +287,7 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
         const u32x4 v = rvalid ? *reinterpret_cast<const u32x4*>(q + qrow + 8 * g4 + 32 * c) : u32x4{0u, 0u, 0u, 0u};
         qf[c] = __builtin_bit_cast(bf16x8, v);
     }
+    const float scale_log2 = scale * 1.44269504088896340736f;
     float m_i = -INFINITY, l_i = 0.f;
     f32x4 o[HD / 16];
 #pragma unroll
@@ -338,50 +349,61 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
                 st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], st[kb], 0, 0, 0);
             }
         }
+        // scores in the log2 domain: s = scale * log2(e) * q.k, so that
+        // e^{scale q.k - m} = 2^{s - m'} with the native exp2
         float p[4][4];
         float tmax = -INFINITY;
+        if (kt0 + MKT <= k1 && kt0 + MKT <= L) {
+            // the whole tile lies in the cached prefix: every key is visible
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+            for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int kidx = kt0 + kb * 16 + 4 * g4 + i;
-                bool vis = kidx < k1;
-                if (vis && kidx >= L) vis = (anc >> (kidx - L)) & 1ull;
-                const float sc = vis ? st[kb][i] * scale : -INFINITY;
-                p[kb][i] = sc;
-                tmax = fmaxf(tmax, sc);
+                for (int i = 0; i < 4; ++i) {
+                    p[kb][i] = st[kb][i] * scale_log2;
+                    tmax = fmaxf(tmax, p[kb][i]);
+                }
+        } else {
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int kidx = kt0 + kb * 16 + 4 * g4 + i;
+                    bool vis = kidx < k1;
+                    if (vis && kidx >= L) vis = (anc >> (kidx - L)) & 1ull;
+                    p[kb][i] = vis ? st[kb][i] * scale_log2 : -INFINITY;
+                    tmax = fmaxf(tmax, p[kb][i]);
+                }
             }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, MD_WAVE));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, MD_WAVE));
+        tmax = fmaxf(tmax, xor16(tmax));
+        tmax = fmaxf(tmax, xor32(tmax));
         const float m_new = fmaxf(m_i, tmax);
-        const float alpha = (m_new == -INFINITY) ? 1.f : expf(m_i - m_new);
+        const float mref = m_new == -INFINITY ? 0.f : m_new;  // rows with no visible key yet
+        const float alpha = __builtin_amdgcn_exp2f(m_i - mref);
         float psum = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const float e = p[kb][i] == -INFINITY ? 0.f : expf(p[kb][i] - m_new);
-                p[kb][i] = e;
-                psum += e;
+                p[kb][i] = __builtin_amdgcn_exp2f(p[kb][i] - mref);
+                psum += p[kb][i];
             }
-        psum += __shfl_xor(psum, 16, MD_WAVE);
-        psum += __shfl_xor(psum, 32, MD_WAVE);
+        psum += xor16(psum);
+        psum += xor32(psum);
         l_i = l_i * alpha + psum;
-        m_i = m_new;
+        // the running max of most rows stops moving after the first tiles
+        if (__ballot(m_new != m_i)) {
 #pragma unroll
-        for (int j = 0; j < HD / 16; ++j) o[j] *= alpha;
+            for (int j = 0; j < HD / 16; ++j) o[j] *= alpha;
+        }
+        m_i = m_new;
 
         // O^T += V^T P^T over two 32-key halves
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const int kb0 = 2 * half, kb1 = 2 * half + 1;
-            u32x4 pw;
-            pw.x = bf16_rne_bits(p[kb0][0]) | (bf16_rne_bits(p[kb0][1]) << 16);
-            pw.y = bf16_rne_bits(p[kb0][2]) | (bf16_rne_bits(p[kb0][3]) << 16);
-            pw.z = bf16_rne_bits(p[kb1][0]) | (bf16_rne_bits(p[kb1][1]) << 16);
-            pw.w = bf16_rne_bits(p[kb1][2]) | (bf16_rne_bits(p[kb1][3]) << 16);
-            const bf16x8 pb = __builtin_bit_cast(bf16x8, pw);
+            const bf16x8 pb = {(__bf16)p[kb0][0], (__bf16)p[kb0][1], (__bf16)p[kb0][2], (__bf16)p[kb0][3],
+                               (__bf16)p[kb1][0], (__bf16)p[kb1][1], (__bf16)p[kb1][2], (__bf16)p[kb1][3]};
 #pragma unroll
             for (int j = 0; j < HD / 16; ++j) {
                 const u32x2 lo = *reinterpret_cast<const u32x2*>(&Vt[16 * j + c16][kb0 * 16 + 4 * g4]);
@@ -405,7 +427,8 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
     }
 }
 
-// out = sum_s e^{m_s - M} o_s / sum_s e^{m_s - M} l_s  (M = max_s m_s)
+// out = sum_s 2^{m_s - M} o_s / sum_s 2^{m_s - M} l_s  (M = max_s m_s; the row
+// statistics are kept in the log2 domain)
 template <typename T>
 __global__ void k_attn_combine(int hd, int splits, const float* __restrict__ po, const float* __restrict__ pm,
                                const float* __restrict__ pl, T* __restrict__ out) {
@@ -418,7 +441,7 @@ __global__ void k_attn_combine(int hd, int splits, const float* __restrict__ po,
 #pragma unroll 8
     for (int s = 0; s < splits; ++s) {
         const float ms = pm[row * splits + s];
-        const float wgt = ms == -INFINITY ? 0.f : expf(ms - M);
+        const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
         num = fmaf(wgt, po[(row * splits + s) * hd + c], num);
         den = fmaf(wgt, pl[row * splits + s], den);
     }
