@@ -112,11 +112,17 @@ int64_t md_heads_weight_bytes(int kind, int dt, int d, int V, int K) {
 }
 
 size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, int kmax) {
-    (void)dt;
-    (void)V;
-    if (M <= 0 || d <= 0 || K <= 0 || kmax <= 0) return 0;
-    if (kind == MD_HEADS_HYDRA) return heads_ws_bound(M * MD_MAX_NODES, d, 1, kmax);
-    return heads_ws_bound(M, d, K, kmax);
+    if (M <= 0 || d <= 0 || V <= 0 || K <= 0 || kmax <= 0) return 0;
+    if (kind == MD_HEADS_HYDRA) {
+        // any level has at most 63 parents per request; size for every row count up to that
+        size_t need = 0;
+        for (int rows = M; rows <= M * (MD_MAX_NODES - 1); rows += M) {
+            const size_t b = heads_ws_bound(dt, rows, d, 2 * d, V, 1, kmax);
+            if (b > need) need = b;
+        }
+        return need;
+    }
+    return heads_ws_bound(dt, M, d, d, V, K, kmax);
 }
 
 int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t* k_per_head, int level,
@@ -171,7 +177,7 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
         a.nh = K;
         a.head0 = 0;
         for (int i = 0; i < K; ++i) a.kk[i] = k_per_head[i];
-        need = heads_ws_bytes(dt, M, d, d, K, kmax);
+        need = heads_ws_bytes(dt, M, d, d, V, K, kmax);
     } else {
         if (level < 1 || level > K) return fail(MD_EINVAL, "Hydra level %d outside 1..%d", level, K);
         int rc = expand_tree(tree, K, k_per_head, &dt_tree);
@@ -186,7 +192,7 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
         a.kk[0] = k_per_head[level - 1];
         tp = &dt_tree;
         if (P == 0) return MD_OK;  // nothing at this depth
-        need = heads_ws_bytes(dt, a.M, d, din, 1, kmax);
+        need = heads_ws_bytes(dt, a.M, d, din, V, 1, kmax);
     }
     if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     return hip_status(heads_launch(a, tp, (hipStream_t)stream, g_ev0, g_ev1), "md_medusa_heads");

@@ -526,6 +526,22 @@ Plan make_plan(int dt, int M, int d, int din, int nh) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The k-way merge of nlists sorted lists per (row, head); at most 4 lists per thread.
+hipError_t launch_merge(const float* pv, const int* pi, int M, int nh, int nlists, KK kk, int kmax, int32_t* topk_idx,
+                        float* topk_val, hipStream_t s) {
+    const int lpt = (nlists + BLOCK - 1) / BLOCK;
+    if (lpt <= 1)
+        hipLaunchKernelGGL(k_topk_merge<1>, dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax, topk_idx,
+                           topk_val);
+    else if (lpt == 2)
+        hipLaunchKernelGGL(k_topk_merge<2>, dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax, topk_idx,
+                           topk_val);
+    else
+        hipLaunchKernelGGL(k_topk_merge<4>, dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax, topk_idx,
+                           topk_val);
+    return hipGetLastError();
+}
+
 template <typename T>
 hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     const Plan p = make_plan(a.dt, a.M, a.d, a.din, a.nh);
@@ -599,32 +615,36 @@ hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
         hipError_t e = hipEventRecord(ev1, s);
         if (e != hipSuccess) return e;
     }
-    const int lpt = (p.wg_per_head + BLOCK - 1) / BLOCK;
-    if (lpt <= 1)
-        hipLaunchKernelGGL(k_topk_merge<1>, dim3(a.M * a.nh), dim3(BLOCK), 0, s, pv, pi, a.M, a.nh, p.wg_per_head, kk,
-                           a.kmax, a.topk_idx, a.topk_val);
-    else if (lpt == 2)
-        hipLaunchKernelGGL(k_topk_merge<2>, dim3(a.M * a.nh), dim3(BLOCK), 0, s, pv, pi, a.M, a.nh, p.wg_per_head, kk,
-                           a.kmax, a.topk_idx, a.topk_val);
-    else
-        hipLaunchKernelGGL(k_topk_merge<4>, dim3(a.M * a.nh), dim3(BLOCK), 0, s, pv, pi, a.M, a.nh, p.wg_per_head, kk,
-                           a.kmax, a.topk_idx, a.topk_val);
-    return hipGetLastError();
+    return launch_merge(pv, pi, a.M, a.nh, p.wg_per_head, kk, a.kmax, a.topk_idx, a.topk_val, s);
 }
 
 }  // namespace
 
-size_t heads_ws_bytes(int dt, int M, int d, int din, int nh, int kmax) {
+size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax) {
+    if (heads_mfma_applicable(dt, M, d, din)) return heads_mfma_ws_bytes(M, d, V, nh, kmax);
     const Plan p = make_plan(dt, M, d, din, nh);
     return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * p.wg_per_head * kmax * 4);
 }
 
-size_t heads_ws_bound(int M, int d, int nh, int kmax) {
+size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax) {
+    const size_t mfma = heads_mfma_applicable(dt, M, d, din) ? heads_mfma_ws_bytes(M, d, V, nh, kmax) : 0;
     const size_t lists_max = (size_t)device_cus() * 4;  // blocks per head at most
-    return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * lists_max * kmax * 4);
+    const size_t gemv = align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * lists_max * kmax * 4);
+    return gemv > mfma ? gemv : mfma;
 }
 
 hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    if (heads_mfma_applicable(a.dt, a.M, a.d, a.din)) {
+        // many rows: the two contractions on the matrix cores, then the same k-way merge
+        float* pv;
+        int* pi;
+        int nlists;
+        hipError_t e = heads_mfma_launch(a, tree, s, ev0, ev1, &pv, &pi, &nlists);
+        if (e != hipSuccess) return e;
+        KK kk;
+        for (int i = 0; i < 8; ++i) kk.v[i] = i < a.nh ? a.kk[i] : 1;
+        return launch_merge(pv, pi, a.M, a.nh, nlists, kk, a.kmax, a.topk_idx, a.topk_val, s);
+    }
     if (a.dt == 0) return launch_typed<float>(a, tree, s, ev0, ev1);
     return launch_typed<uint16_t>(a, tree, s, ev0, ev1);
 }

@@ -1,0 +1,409 @@
+// Draft heads over many rows on the matrix cores.
+//
+// With one hidden state per tree node ("Medusa heads versus separate draft
+// model", section "Trees": a 64-node tree at batch 8 puts 512 tokens through
+// the weights, past the ridge point), the heads are two dense contractions
+// per head: the residual block z = W x (d x din times din x M) and the
+// vocabulary projection logits = U h' (V x d times d x M). Both run as bf16
+// MFMA GEMMs (v_mfma_f32_16x16x32_bf16):
+//
+// * phase 1 (residual): x is exact in bf16 (h, or Hydra's [h ; E[token]]),
+//   so one product per term. The epilogue forms h' = base + SiLU(z + b) in
+//   float32 and also stores it split as hi = bf16(h'), lo = bf16(h' - hi).
+// * phase 2 (vocabulary): logits = U hi + U lo, two products per term, so
+//   h' enters with ~16 mantissa bits (relative error <= 2^-17) instead of
+//   bf16's 8; rounding h' itself to bf16 would move logits by ~1e-3 and
+//   reorder near-equal candidates. The epilogue keeps, per column (row of
+//   h'), the 16 best logits of the block's 128 vocabulary rows in
+//   registers; logits never reach memory. The per-block lists then go
+//   through the same k-way merge as the GEMV path.
+//
+// Block tile: 128 weight rows x 128 activation rows, K step 64, 4 waves of
+// 64 x 64 (4 x 4 MFMA tiles each). Operand tiles are staged in LDS (rows
+// padded against bank conflicts) from registers loaded one K step ahead.
+// Both operands are row-major along the contraction, which is exactly the
+// MFMA operand layout (a lane reads 8 consecutive k of one row), so nothing
+// is transposed. Blocks that share a weight tile (the activation tiles of
+// one weight tile) get ids spaced by 8, i.e. the same XCD and L2.
+#include <math.h>
+
+#include "md_internal.h"
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+constexpr int BLOCK = 256;
+constexpr int TR = 128;       // weight rows per tile
+constexpr int TM = 128;       // activation rows per tile
+constexpr int KS = 64;        // contraction elements per step
+constexpr int LP = KS + 8;    // LDS row pitch (bf16 elements)
+constexpr int KL = 16;        // per-column list length kept by the epilogue
+constexpr int CH = KS / 8;    // 16-byte chunks per row and step
+constexpr int LDS_BYTES = TR * TM * 4;  // the epilogue's logit tile; covers 3 staged operand tiles
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ bool ranks_above(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
+
+// Sorted (value desc, index asc) list of KL in registers; insert (v, i).
+__device__ __forceinline__ void reg_insert(float (&lv)[KL], int (&li)[KL], float v, int i) {
+    bool above[KL];
+#pragma unroll
+    for (int j = 0; j < KL; ++j) above[j] = ranks_above(v, i, lv[j], li[j]);
+#pragma unroll
+    for (int j = KL - 1; j >= 1; --j) {
+        const float nv = above[j - 1] ? lv[j - 1] : v;
+        const int ni = above[j - 1] ? li[j - 1] : i;
+        lv[j] = above[j] ? nv : lv[j];
+        li[j] = above[j] ? ni : li[j];
+    }
+    lv[0] = above[0] ? v : lv[0];
+    li[0] = above[0] ? i : li[0];
+}
+
+// Hydra rows: (request, parent) -> the parent's token.
+struct GemmRows {
+    int kind;  // 0: activation row m is h[m]; 1: row m is [h[b] ; E[tok]] of (b, parent) = divmod(m, P)
+    int P, N, V;
+    int8_t parents[64];
+    const uint16_t* h;
+    const uint16_t* E;
+    const int32_t* root_tok;
+    const int32_t* tree_tok;
+};
+
+// XCD-grouped block ids: the activation tiles of one weight tile get ids
+// u%8 + 8*(..) so they run on one XCD and share its L2.
+__device__ __forceinline__ bool decode_tile(int id, int mtiles, int units, int& unit, int& mt) {
+    const int x = id & 7, u = id >> 3;
+    mt = u % mtiles;
+    unit = (u / mtiles) * 8 + x;
+    return unit < units;
+}
+
+// One K step of a 128 x 128 tile for this wave's 64 x 64 quadrant.
+template <int NS>
+__device__ __forceinline__ void tile_mma(const uint16_t (*As)[LP], const uint16_t (*Bs)[TM][LP], int wr, int wc,
+                                         int g4, int c16, f32x4 (&acc)[4][4]) {
+#pragma unroll
+    for (int kk = 0; kk < KS / 32; ++kk) {
+        bf16x8 a[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            a[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&As[64 * wr + 16 * rb + c16][32 * kk + 8 * g4]));
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const bf16x8 b = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(&Bs[s][64 * wc + 16 * cb + c16][32 * kk + 8 * g4]));
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b, acc[rb][cb], 0, 0, 0);
+            }
+        }
+    }
+}
+
+// Phase 1: z = W x for rows [0, nh*d) of the heads' residual matrices and
+// activation rows [0, M); epilogue h' = base + SiLU(z + b) -> hres (f32) and
+// its hi/lo bf16 split.
+__global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __restrict__ W,
+                                                            const uint16_t* __restrict__ bias, GemmRows rows, int M,
+                                                            int d, int din, int nh, int head0, int mtiles,
+                                                            float* __restrict__ hres, float* __restrict__ hres_out,
+                                                            uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo) {
+    __shared__ __align__(16) unsigned char smem[LDS_BYTES];
+    __shared__ int s_tok[TM];
+    __shared__ int s_b[TM];
+    uint16_t(*As)[LP] = reinterpret_cast<uint16_t(*)[LP]>(smem);
+    uint16_t(*Bs)[TM][LP] = reinterpret_cast<uint16_t(*)[TM][LP]>(smem + TR * LP * 2);
+    const int units = nh * d / TR;
+    int unit, mt;
+    if (!decode_tile(blockIdx.x, mtiles, units, unit, mt)) return;
+    const int row0 = unit * TR;  // over nh*d rows (a tile never straddles heads: d % 128 == 0)
+    const int hh = row0 / d, r0 = row0 - hh * d;
+    const int m0 = mt * TM;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g4 = lane >> 4, c16 = lane & 15, wr = w >> 1, wc = w & 1;
+
+    if (tid < TM) {
+        const int m = m0 + tid;
+        int b = m, tok = -1;
+        if (rows.kind == 1 && m < M) {
+            b = m / rows.P;
+            const int p = rows.parents[m - b * rows.P];
+            tok = p == 0 ? rows.root_tok[b] : rows.tree_tok[(int64_t)b * rows.N + p];
+            if (tok < 0 || tok >= rows.V) tok = -1;  // out-of-vocabulary token: zero embedding
+        }
+        s_b[tid] = b;
+        s_tok[tid] = tok;
+    }
+    __syncthreads();
+
+    const uint16_t* Wt = W + ((int64_t)head0 * d + row0) * din;
+    u32x4 ra[4], rb[4];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = tid + BLOCK * j;
+            const int r = i / CH, c = i - (i / CH) * CH;
+            ra[j] = *reinterpret_cast<const u32x4*>(Wt + (int64_t)r * din + k0 + 8 * c);
+            const int m = m0 + r;
+            const int kc = k0 + 8 * c;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (m < M) {
+                if (rows.kind == 0) {
+                    v = *reinterpret_cast<const u32x4*>(rows.h + (int64_t)m * d + kc);
+                } else if (kc < d) {
+                    v = *reinterpret_cast<const u32x4*>(rows.h + (int64_t)s_b[r] * d + kc);
+                } else if (s_tok[r] >= 0) {
+                    v = *reinterpret_cast<const u32x4*>(rows.E + (int64_t)s_tok[r] * d + (kc - d));
+                }
+            }
+            rb[j] = v;
+        }
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    fetch(0);
+    for (int k0 = 0; k0 < din; k0 += KS) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = tid + BLOCK * j;
+            const int r = i / CH, c = i - (i / CH) * CH;
+            *reinterpret_cast<u32x4*>(&As[r][8 * c]) = ra[j];
+            *reinterpret_cast<u32x4*>(&Bs[0][r][8 * c]) = rb[j];
+        }
+        __syncthreads();
+        if (k0 + KS < din) fetch(k0 + KS);
+        tile_mma<1>(As, Bs, wr, wc, g4, c16, acc);
+    }
+
+    // epilogue: lane holds z[row = 64wr + 16rb + 4g4 + i][col = 64wc + 16cb + c16]
+#pragma unroll
+    for (int rb_ = 0; rb_ < 4; ++rb_) {
+        const int r = r0 + 64 * wr + 16 * rb_ + 4 * g4;  // row within the head, 4 consecutive
+        float bb[4];
+        if (bias) {
+            const u32x2 bw = *reinterpret_cast<const u32x2*>(bias + (int64_t)(head0 + hh) * d + r);
+            bb[0] = bf_lo(bw.x);
+            bb[1] = bf_hi(bw.x);
+            bb[2] = bf_lo(bw.y);
+            bb[3] = bf_hi(bw.y);
+        } else {
+            bb[0] = bb[1] = bb[2] = bb[3] = 0.f;
+        }
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int mm = 64 * wc + 16 * cb + c16;
+            const int m = m0 + mm;
+            if (m >= M) continue;
+            const u32x2 hw = *reinterpret_cast<const u32x2*>(rows.h + (int64_t)(rows.kind == 0 ? m : s_b[mm]) * d + r);
+            const float base[4] = {bf_lo(hw.x), bf_hi(hw.x), bf_lo(hw.y), bf_hi(hw.y)};
+            f32x4 hv;
+            uint32_t hi2[2] = {0u, 0u}, lo2[2] = {0u, 0u};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float z = acc[rb_][cb][i] + bb[i];
+                const float v = base[i] + z / (1.f + expf(-z));
+                hv[i] = v;
+                const __bf16 hb = (__bf16)v;
+                const float rem = v - (float)hb;
+                const __bf16 lb = (__bf16)rem;
+                const uint32_t hbits = __builtin_bit_cast(uint16_t, hb), lbits = __builtin_bit_cast(uint16_t, lb);
+                hi2[i >> 1] |= hbits << (16 * (i & 1));
+                lo2[i >> 1] |= lbits << (16 * (i & 1));
+            }
+            const int64_t o = ((int64_t)hh * M + m) * d + r;
+            *reinterpret_cast<f32x4*>(hres + o) = hv;
+            if (hres_out) *reinterpret_cast<f32x4*>(hres_out + o) = hv;
+            *reinterpret_cast<u32x2*>(hhi + o) = u32x2{hi2[0], hi2[1]};
+            *reinterpret_cast<u32x2*>(hlo + o) = u32x2{lo2[0], lo2[1]};
+        }
+    }
+}
+
+// Phase 2: logits = U (hi + lo) for one head's 128 vocabulary rows x 128
+// activation rows; epilogue: per activation row, the block's best KL logits.
+__global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restrict__ U,
+                                                         const uint16_t* __restrict__ hhi,
+                                                         const uint16_t* __restrict__ hlo, int M, int d, int V,
+                                                         int nh, int head0, int vtiles, int mtiles, int kmax,
+                                                         float* __restrict__ part_val, int* __restrict__ part_idx) {
+    __shared__ __align__(16) unsigned char smem[LDS_BYTES];
+    uint16_t(*As)[LP] = reinterpret_cast<uint16_t(*)[LP]>(smem);
+    uint16_t(*Bs)[TM][LP] = reinterpret_cast<uint16_t(*)[TM][LP]>(smem + TR * LP * 2);
+    float(*S)[TM] = reinterpret_cast<float(*)[TM]>(smem);
+    const int units = nh * vtiles;
+    int unit, mt;
+    if (!decode_tile(blockIdx.x, mtiles, units, unit, mt)) return;
+    const int hh = unit / vtiles, vt = unit - hh * vtiles;
+    const int v0 = vt * TR, m0 = mt * TM;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g4 = lane >> 4, c16 = lane & 15, wr = w >> 1, wc = w & 1;
+    const uint16_t* Ut = U + ((int64_t)(head0 + hh) * V + v0) * d;
+    const int64_t hbase = (int64_t)hh * M * d;
+
+    u32x4 ra[4], rh[4], rl[4];
+    auto fetch = [&](int k0) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = tid + BLOCK * j;
+            const int r = i / CH, c = i - (i / CH) * CH;
+            ra[j] = v0 + r < V ? *reinterpret_cast<const u32x4*>(Ut + (int64_t)r * d + k0 + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+            const int m = m0 + r;
+            if (m < M) {
+                rh[j] = *reinterpret_cast<const u32x4*>(hhi + hbase + (int64_t)m * d + k0 + 8 * c);
+                rl[j] = *reinterpret_cast<const u32x4*>(hlo + hbase + (int64_t)m * d + k0 + 8 * c);
+            } else {
+                rh[j] = u32x4{0u, 0u, 0u, 0u};
+                rl[j] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+    };
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    fetch(0);
+    for (int k0 = 0; k0 < d; k0 += KS) {
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = tid + BLOCK * j;
+            const int r = i / CH, c = i - (i / CH) * CH;
+            *reinterpret_cast<u32x4*>(&As[r][8 * c]) = ra[j];
+            *reinterpret_cast<u32x4*>(&Bs[0][r][8 * c]) = rh[j];
+            *reinterpret_cast<u32x4*>(&Bs[1][r][8 * c]) = rl[j];
+        }
+        __syncthreads();
+        if (k0 + KS < d) fetch(k0 + KS);
+        tile_mma<2>(As, Bs, wr, wc, g4, c16, acc);
+    }
+    __syncthreads();  // operand tiles are dead; the logit tile takes their LDS
+#pragma unroll
+    for (int rb_ = 0; rb_ < 4; ++rb_)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[64 * wr + 16 * rb_ + 4 * g4 + i][64 * wc + 16 * cb + c16] = acc[rb_][cb][i];
+    __syncthreads();
+
+    // thread (column mm, half): its 64 vocabulary rows into a sorted list
+    const int mm = tid & (TM - 1), half = tid >> 7;
+    float lv[KL];
+    int li[KL];
+#pragma unroll
+    for (int j = 0; j < KL; ++j) {
+        lv[j] = -INFINITY;
+        li[j] = INT_MAX;
+    }
+    for (int r = 64 * half; r < 64 * half + 64; ++r) {
+        const int v = v0 + r;
+        const float x = S[r][mm];
+        if (v < V && ranks_above(x, v, lv[KL - 1], li[KL - 1])) reg_insert(lv, li, x, v);
+    }
+    __syncthreads();  // the logit tile is dead; lists of the upper halves take its LDS
+    float(*LV)[KL] = reinterpret_cast<float(*)[KL]>(smem);
+    int(*LI)[KL] = reinterpret_cast<int(*)[KL]>(smem + TM * KL * 4);
+    if (half == 1) {
+#pragma unroll
+        for (int j = 0; j < KL; ++j) {
+            LV[mm][j] = lv[j];
+            LI[mm][j] = li[j];
+        }
+    }
+    __syncthreads();
+    if (half == 0) {
+#pragma unroll
+        for (int j = 0; j < KL; ++j)
+            if (ranks_above(LV[mm][j], LI[mm][j], lv[KL - 1], li[KL - 1])) reg_insert(lv, li, LV[mm][j], LI[mm][j]);
+        const int m = m0 + mm;
+        if (m < M) {
+            const int64_t o = (((int64_t)hh * M + m) * vtiles + vt) * kmax;
+#pragma unroll
+            for (int j = 0; j < KL; ++j)
+                if (j < kmax) {
+                    part_val[o + j] = lv[j];
+                    part_idx[o + j] = li[j];
+                }
+        }
+    }
+}
+
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+bool heads_mfma_applicable(int dt, int M, int d, int din) {
+    return dt == 1 && M >= 8 && d % TR == 0 && din % KS == 0;
+}
+
+size_t heads_mfma_ws_bytes(int M, int d, int V, int nh, int kmax) {
+    const size_t vtiles = (size_t)(V + TR - 1) / TR;
+    const size_t e = (size_t)nh * M * d;
+    return align256(e * 4) + 2 * align256(e * 2) + 2 * align256((size_t)nh * M * vtiles * kmax * 4);
+}
+
+// Launches phase 1 and phase 2; the caller merges the lists (nlists = vtiles).
+hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
+                             float** part_val, int** part_idx, int* nlists) {
+    const int vtiles = (a.V + TR - 1) / TR;
+    const int mtiles = (a.M + TM - 1) / TM;
+    char* w = reinterpret_cast<char*>(a.ws);
+    const size_t e = (size_t)a.nh * a.M * a.d;
+    float* hres = reinterpret_cast<float*>(w);
+    w += align256(e * 4);
+    uint16_t* hhi = reinterpret_cast<uint16_t*>(w);
+    w += align256(e * 2);
+    uint16_t* hlo = reinterpret_cast<uint16_t*>(w);
+    w += align256(e * 2);
+    float* pv = reinterpret_cast<float*>(w);
+    w += align256((size_t)a.nh * a.M * vtiles * a.kmax * 4);
+    int* pi = reinterpret_cast<int*>(w);
+
+    GemmRows rows;
+    rows.kind = a.kind;
+    rows.P = 1;
+    rows.N = tree ? tree->n : 0;
+    rows.V = a.V;
+    for (int i = 0; i < 64; ++i) rows.parents[i] = 0;
+    if (a.kind == 1) {
+        const int off = tree->level_off[a.level];
+        rows.P = tree->level_off[a.level + 1] - off;
+        for (int j = 0; j < rows.P; ++j) rows.parents[j] = tree->lp[off + j];
+    }
+    rows.h = reinterpret_cast<const uint16_t*>(a.h);
+    rows.E = reinterpret_cast<const uint16_t*>(a.E);
+    rows.root_tok = a.root_tok;
+    rows.tree_tok = a.tree_tok;
+
+    const int units1 = a.nh * a.d / TR;
+    hipLaunchKernelGGL(k_residual_mfma, dim3(8 * mtiles * ((units1 + 7) / 8)), dim3(BLOCK), 0, s,
+                       reinterpret_cast<const uint16_t*>(a.W), reinterpret_cast<const uint16_t*>(a.b), rows, a.M, a.d,
+                       a.din, a.nh, a.head0, mtiles, hres, a.h_res, hhi, hlo);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
+    const int units2 = a.nh * vtiles;
+    hipLaunchKernelGGL(k_vocab_mfma, dim3(8 * mtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s,
+                       reinterpret_cast<const uint16_t*>(a.U), hhi, hlo, a.M, a.d, a.V, a.nh, a.head0, vtiles, mtiles,
+                       a.kmax, pv, pi);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
+    *part_val = pv;
+    *part_idx = pi;
+    *nlists = vtiles;
+    return hipSuccess;
+}

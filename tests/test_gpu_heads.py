@@ -160,3 +160,38 @@ def test_hydra_small():
 def test_hydra_full_size_sampled():
     # full Hydra shape (B = 4, d = 4096, V = 128,256); the oracle checks request 0's 41 rows
     check_hydra(HYDRA_B4, 41, requests=[0])
+
+
+# ------------------------------------------------- many rows: matrix cores
+
+MFMA_BF16 = Workload("mfma bf16: d=256 V=1000 K=3", "medusa", B=1, d=256, V=1000, K=3, dtype="bf16",
+                     topk=(6, 3, 1), N=10, Hq=4, Hkv=1, hd=64, L=10)
+
+
+@pytest.mark.parametrize("wl,M", [(MFMA_BF16, 8), (MFMA_BF16, 130),
+                                  (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9)), 37)])
+def test_heads_medusa_mfma_rows(wl, M):
+    """Eight or more bf16 rows run the MFMA path (ragged row and vocabulary tiles)."""
+    seed = 2000 + M
+    w = weights(wl, seed)
+    h = synth.normal(seed, 78, (M, wl.d), 1.0, wl.dtype)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), M)
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, want_logits=True)
+    compare_medusa(wl, gi, gv, gh, ref, label="%s M=%d" % (wl.name, M))
+    gi2, gv2, gh2 = gpu_heads_medusa(wl, wd, to_dev(h), M)
+    assert np.array_equal(gi, gi2) and np.array_equal(gv.view(np.uint32), gv2.view(np.uint32))
+
+
+@pytest.mark.parametrize("wl_name,M,rows", [("8b", 64, [0, 31, 63]), ("70b", 512, [0, 300, 511])])
+def test_heads_medusa_mfma_full_size_sampled(wl_name, M, rows):
+    """The 70B-shaped heads over all 512 tree nodes of a batch of 8 (the oracle checks sampled rows)."""
+    wl = LLAMA8B if wl_name == "8b" else LLAMA70B
+    w = weights(wl, 8 if wl_name == "8b" else 70)
+    h = synth.normal(91, 79, (M, wl.d), 1.0, wl.dtype)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), M)
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, rows=rows, want_logits=True)
+    ref["hres"] = ref["hres"]
+    compare_medusa(wl, gi[rows], gv[rows], gh[:, rows], ref, label="%s M=%d rows %s" % (wl.name, M, rows))
+    del wd
