@@ -6,10 +6,14 @@ top-k) -> candidate tree -> tree attention over the KV cache -> target argmax,
 greedy acceptance and KV compaction. Default workload: 70B-shaped heads at
 batch 1 (d = 8,192, V = 128,256, 4 heads in bf16 = 8.94 GB of weights, top-k
 (10, 4, 2, 1), 64-node tree, GQA 64/8 heads of 128, 4,096 cached positions).
+Other workloads (--workload) are secondary measurements: the batch-8 step
+whose heads run over all 512 tree nodes on the matrix cores, the Hydra step
+(four sequential head levels), the 8B-shaped step and the top-1 chain.
 
 Prints one JSON line: steps/s, the roofline of the dominant kernel (the
-vocabulary projection + top-k, timed live with HIP events on the stream it
-runs on) and the CPU oracle's own throughput on the same inputs.
+vocabulary projection + top-k, timed live with HIP events that the library
+records around that kernel on the stream it runs on) and the CPU oracle's
+own throughput on the same inputs.
 """
 from __future__ import annotations
 
@@ -26,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
+PEAK_BF16_TFLOPS = 2500.0
 PMC_FILE = os.path.join(ROOT, "profiles", "vocab_topk_70b_pmc.json")
 
 
@@ -61,10 +66,9 @@ def main() -> int:
     from synth.workloads import ALL, plant, step_inputs, weights
 
     wl = ALL[args.workload]
-    if wl.kind != "medusa" or wl.rows_per_request != 1:
-        print("bench.py: the timed step covers the batch-1 Medusa workloads", file=sys.stderr)
-        return 2
+    hydra = wl.kind == "hydra"
     topo = wl.topology()
+    depth = max(len(p) for p in topo.paths)
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
 
@@ -80,17 +84,32 @@ def main() -> int:
     torch.cuda.synchronize()
     log("weights on the GPU (%.1f GB)" % (sum(v.numel() * v.element_size() for v in wd.values()) / 1e9))
 
-    # input sets; each set's logits are planted from the oracle's own tree tokens,
-    # and the oracle's whole step on the first --cpu-steps sets is the CPU baseline
+    # Input sets. Each set's verification logits are planted from the oracle's
+    # own tree tokens; the oracle's step on the first --cpu-steps sets is the
+    # CPU baseline. With heads over many rows the oracle runs the rows that
+    # build the trees and its per-row time is scaled to all rows.
     sets, cpu_times, acc_oracle = [], [], []
     threads = oracle.threads()
+    sample_note = ""
     for s in range(args.sets):
         x = step_inputs(wl, args.seed, step=s)
         ta = time.perf_counter()
-        heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], wl.topk)
-        tok, pos = oracle.tree_tokens_medusa(topo.parent, topo.rank, heads["idx"], x["src_row"], x["root_tok"],
-                                             x["lens"])
-        tb = time.perf_counter()
+        if hydra:
+            hy = oracle.hydra_expand(w["W"], w["b"], w["U"], w["E"], x["h"], topo.parent, topo.rank, wl.topk,
+                                     x["root_tok"], x["lens"])
+            tok = hy["tree_tok"]
+            heads_time = time.perf_counter() - ta
+        else:
+            rows = sorted(set(int(r) for r in x["src_row"]))
+            heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], wl.topk, rows=rows)
+            full = np.full((wl.M, wl.K, wl.kmax), -1, np.int32)
+            for j, r in enumerate(rows):
+                full[r] = heads["idx"][j]
+            tok, _ = oracle.tree_tokens_medusa(topo.parent, topo.rank, full, x["src_row"], x["root_tok"], x["lens"])
+            heads_time = (time.perf_counter() - ta) * (wl.M / len(rows))
+            if wl.M != len(rows):
+                sample_note = " (heads timed on the %d rows that build the trees, scaled to all %d rows)" % (
+                    len(rows), wl.M)
         logits = plant(x["logits"], topo, tok, wl.a, seed=args.seed, step=s)
         if s < args.cpu_steps:
             tc = time.perf_counter()
@@ -99,9 +118,9 @@ def main() -> int:
             r = oracle.accept(topo.parent, wl.K, tok, tstar, x["lens"])
             oracle.compact(x["Kc"], x["Vc"], x["lens"], r["accept_len"], r["path"], wl.K)
             td = time.perf_counter()
-            cpu_times.append((tb - ta) + (td - tc))
-            acc_oracle.append(int(r["accept_len"][0]))
-            log("oracle step %d: %.2f s (accept_len %d)" % (s, cpu_times[-1], acc_oracle[-1]))
+            cpu_times.append(heads_time + (td - tc))
+            acc_oracle.append([int(v) for v in r["accept_len"]])
+            log("oracle step %d: %.2f s (accept_len %s)" % (s, cpu_times[-1], acc_oracle[-1]))
         xd = {k: to_dev(v) for k, v in x.items() if k != "logits"}
         xd["logits"] = to_dev(logits)
         xd["lens0"] = xd["lens"].clone()
@@ -109,41 +128,50 @@ def main() -> int:
     torch.cuda.synchronize()
     log("%d input sets on the GPU" % len(sets))
 
-    cfg = md.StepConfig(kind=md.MD_HEADS_MEDUSA, dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32,
-                        B=wl.B, M=wl.M, d=wl.d, V=wl.V, K=wl.K, k_per_head=wl.topk, parent=topo.parent,
+    cfg = md.StepConfig(kind=md.MD_HEADS_HYDRA if hydra else md.MD_HEADS_MEDUSA,
+                        dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, B=wl.B,
+                        M=wl.B if hydra else wl.M, d=wl.d, V=wl.V, K=wl.K, k_per_head=wl.topk, parent=topo.parent,
                         rank=topo.rank, Hq=wl.Hq, Hkv=wl.Hkv, hd=wl.hd, Lcap=wl.Lcap, max_len=wl.L_max)
     step = md.MedusaStep(cfg)
     stream = torch.cuda.current_stream()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for a, b in ev:  # materialise the underlying hipEvent_t handles
-        a.record(stream)
-        b.record(stream)
+    calls = depth if hydra else 1  # heads calls per step, each with its own event pair
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+          for _ in range(args.steps)]
+    for pairs in ev:  # materialise the underlying hipEvent_t handles
+        for a, b in pairs:
+            a.record(stream)
+            b.record(stream)
     torch.cuda.synchronize()
 
-    accepted = []
-
-    def one_step(i: int, timed_pair=None):
+    def one_step(i: int, pairs=None):
         xd = sets[i % len(sets)]
-        xd["lens"].copy_(xd["lens0"])  # every step starts from the same cached length
-        if timed_pair is not None:
-            md.md_set_vocab_timing_events(timed_pair[0].cuda_event, timed_pair[1].cuda_event)
-        step.run(wd, xd)
-        if timed_pair is not None:
-            md.md_set_vocab_timing_events(None, None)
+        xd["lens"].copy_(xd["lens0"])  # every step starts from the same cached lengths
+        for lvl in range(calls):
+            if pairs is not None:
+                md.md_set_vocab_timing_events(pairs[lvl][0].cuda_event, pairs[lvl][1].cuda_event)
+            if hydra:
+                step.heads(xd["h"], wd["W"], wd["b"], wd["U"], E=wd["E"], root_tok=xd["root_tok"], level=lvl + 1)
+                step.build(None, xd["root_tok"], xd["lens"], level=lvl + 1)
+            else:
+                step.heads(xd["h"], wd["W"], wd["b"], wd["U"])
+            if pairs is not None:
+                md.md_set_vocab_timing_events(None, None)
+        if not hydra:
+            step.build(xd["src_row"], xd["root_tok"], xd["lens"])
+        step.attention(xd["q"], xd["Kc"], xd["Vc"], xd["lens"])
+        step.accept(xd["logits"], xd["Kc"], xd["Vc"], xd["lens"])
 
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
         one_step(args.warmup + i, ev[i])
     t_end.record(stream)
     torch.cuda.synchronize()
-    ms_total = t_start.elapsed_time(t_end)
-    ms_per_step = ms_total / args.steps
-    vocab_ms = sum(a.elapsed_time(b) for a, b in ev) / args.steps
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    vocab_ms = sum(a.elapsed_time(b) for pairs in ev for a, b in pairs) / args.steps
     acc_len = step.accept_len.cpu().numpy().tolist()
 
     # attainable HBM read bandwidth on this GPU: the library's plain streaming-read probe over 4 GiB
@@ -168,27 +196,48 @@ def main() -> int:
         torch.cuda.synchronize()
         log("copy calibration: 3 x 1 GiB device copies done")
 
-    # algorithmic bytes: the vocabulary projections once plus h' once (float32)
-    vocab_bytes = wl.K * wl.V * wl.d * (2 if wl.dtype == "bf16" else 4) + wl.K * wl.M * wl.d * 4
-    achieved = vocab_bytes / (vocab_ms * 1e-3) / 1e9
     esz = 2 if wl.dtype == "bf16" else 4
-    step_bytes = (md.md_heads_weight_bytes(0, 1 if esz == 2 else 0, wl.d, wl.V, wl.K)
-                  + 2 * wl.B * wl.Hkv * (wl.L_max + wl.N) * wl.hd * esz  # K and V of prefix + tree
+    # heads rows per step: Medusa M; Hydra the parents of every level of every request
+    if hydra:
+        head_rows = [wl.B * len(oracle.hydra_rows(topo.parent, lvl)) for lvl in range(1, depth + 1)]
+    else:
+        head_rows = [wl.M] * wl.K
+    vocab_bytes = wl.K * wl.V * wl.d * esz if not hydra else depth * wl.V * wl.d * esz
+    vocab_bytes += sum(head_rows) * wl.d * 4
+    vocab_flops = 2.0 * wl.V * wl.d * sum(head_rows)  # algorithmic multiply-adds of the projections
+    kernel = "vocabulary projection + per-head top-k"
+    mfma_rows = min(head_rows) >= 8 and wl.dtype == "bf16"
+    if mfma_rows:
+        achieved = vocab_flops / (vocab_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                    "kernel": "k_vocab_mfma (%s; each product issued twice, h' as hi + lo bf16)" % kernel,
+                    "kernel_ms": round(vocab_ms, 4), "flops_per_step": vocab_flops}
+    else:
+        achieved = vocab_bytes / (vocab_ms * 1e-3) / 1e9
+        traffic = None
+        if os.path.exists(PMC_FILE):
+            with open(PMC_FILE) as f:
+                pmc = json.load(f)
+            if pmc.get("heads_hip_sha256") == file_sha(os.path.join(ROOT, "medusa_draft_heads_amd", "csrc",
+                                                                     "heads.hip")) \
+                    and pmc.get("workload") == args.workload:
+                traffic = pmc.get("hbm_bytes_per_launch")
+        roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
+                    "kernel": "k_vocab_topk (%s)" % kernel if not hydra else "vocabulary kernels of the 4 levels",
+                    "kernel_ms": round(vocab_ms, 4), "bytes_per_launch": vocab_bytes,
+                    "stream_read_GBps": round(stream_gbs, 1), "frac_of_stream_read": round(achieved / stream_gbs, 4)}
+    step_bytes = (md.md_heads_weight_bytes(1 if hydra else 0, 1 if esz == 2 else 0, wl.d, wl.V, wl.K)
+                  + 2 * wl.B * wl.Hkv * (wl.L_max + wl.N) * wl.hd * esz  # K and V of prefix + tree (upper bound)
                   + 2 * wl.B * wl.N * wl.Hq * wl.hd * esz  # q in, attention out
                   + wl.B * wl.N * wl.V * 4)  # verification logits
-    traffic = None
-    if os.path.exists(PMC_FILE):
-        with open(PMC_FILE) as f:
-            pmc = json.load(f)
-        if pmc.get("heads_hip_sha256") == file_sha(os.path.join(ROOT, "medusa_draft_heads_amd", "csrc", "heads.hip")) \
-                and pmc.get("workload") == args.workload:
-            traffic = pmc.get("hbm_bytes_per_launch")
     cpu = None
     if cpu_times:
         cpu = {"value": round(1.0 / float(np.median(cpu_times)), 4), "unit": "steps/s", "cores": threads,
                "kind": "oracle",
                "sample": "%d whole oracle steps (heads, tree, attention, argmax, accept, compaction) on the same "
-                         "seeded inputs, median" % len(cpu_times)}
+                         "seeded inputs, median%s" % (len(cpu_times), sample_note)}
     E = 1.0
     run = 1.0
     for ai in wl.a:
@@ -208,16 +257,12 @@ def main() -> int:
         "dtype": wl.dtype,
         "data": "synthetic (seeded Philox inputs, random-init heads of the workload's shape)",
         "config": {"workload": wl.name, "batch": wl.B, "d": wl.d, "V": wl.V, "heads": wl.K, "topk": list(wl.topk),
-                   "tree_nodes": wl.N, "Hq": wl.Hq, "Hkv": wl.Hkv, "head_dim": wl.hd, "L": wl.L_max,
-                   "input_sets": len(sets)},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                     "kernel": "k_vocab_topk (vocabulary projection + per-head top-k)",
-                     "kernel_ms": round(vocab_ms, 4), "bytes_per_launch": vocab_bytes,
-                     "stream_read_GBps": round(stream_gbs, 1),
-                     "frac_of_stream_read": round(achieved / stream_gbs, 4)},
+                   "tree_nodes": wl.N, "heads_rows_per_step": sum(head_rows), "Hq": wl.Hq, "Hkv": wl.Hkv,
+                   "head_dim": wl.hd, "L": wl.L_max, "input_sets": len(sets)},
+        "roofline": roofline,
         "step_hbm": {"bytes_per_step": step_bytes, "GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
+        "stream_read_GBps": round(stream_gbs, 1),
         "acceptance": {"last_step_accept_len": acc_len, "oracle_accept_len": acc_oracle, "E_closed_form": round(E, 4)},
         "cpu_baseline": cpu,
     }

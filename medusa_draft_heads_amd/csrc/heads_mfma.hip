@@ -13,10 +13,12 @@
 // * phase 2 (vocabulary): logits = U hi + U lo, two products per term, so
 //   h' enters with ~16 mantissa bits (relative error <= 2^-17) instead of
 //   bf16's 8; rounding h' itself to bf16 would move logits by ~1e-3 and
-//   reorder near-equal candidates. The epilogue keeps, per column (row of
-//   h'), the 16 best logits of the block's 128 vocabulary rows in
-//   registers; logits never reach memory. The per-block lists then go
-//   through the same k-way merge as the GEMV path.
+//   reorder near-equal candidates. The epilogue takes, per column (row of
+//   h'), the block's best k logits of its 128 vocabulary rows; logits never
+//   reach memory. A running lower bound of each column's k-th best logit
+//   (atomicMax of every block's k-th) filters candidates first, so most
+//   blocks select almost nothing. The per-block lists then go through the
+//   same k-way merge as the GEMV path.
 //
 // Block tile: 128 weight rows x 128 activation rows, K step 64, 4 waves of
 // 64 x 64 (4 x 4 MFMA tiles each). Operand tiles are staged in LDS (rows
@@ -41,30 +43,29 @@ constexpr int TR = 128;       // weight rows per tile
 constexpr int TM = 128;       // activation rows per tile
 constexpr int KS = 64;        // contraction elements per step
 constexpr int LP = KS + 8;    // LDS row pitch (bf16 elements)
-constexpr int KL = 16;        // per-column list length kept by the epilogue
 constexpr int CH = KS / 8;    // 16-byte chunks per row and step
-constexpr int LDS_BYTES = TR * TM * 4;  // the epilogue's logit tile; covers 3 staged operand tiles
+constexpr int NLD = TR * CH / BLOCK;  // 16-byte operand chunks per thread and step
+static_assert(TR == TM, "operand loops stage A and B rows with the same index");
+static_assert((TR * CH) % BLOCK == 0 && NLD >= 1, "each thread stages a whole number of chunks");
+constexpr int SP = TR + 4;    // logit tile pitch: one column (activation row) of 128 logits, padded
+constexpr int LDS_BYTES = TM * SP * 4;  // the epilogue's logit tile; covers 3 staged operand tiles
+static_assert(3 * TR * LP * 2 <= LDS_BYTES, "operand tiles fit in the logit tile's LDS");
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
 __device__ __forceinline__ bool ranks_above(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
 
-// Sorted (value desc, index asc) list of KL in registers; insert (v, i).
-__device__ __forceinline__ void reg_insert(float (&lv)[KL], int (&li)[KL], float v, int i) {
-    bool above[KL];
-#pragma unroll
-    for (int j = 0; j < KL; ++j) above[j] = ranks_above(v, i, lv[j], li[j]);
-#pragma unroll
-    for (int j = KL - 1; j >= 1; --j) {
-        const float nv = above[j - 1] ? lv[j - 1] : v;
-        const int ni = above[j - 1] ? li[j - 1] : i;
-        lv[j] = above[j] ? nv : lv[j];
-        li[j] = above[j] ? ni : li[j];
-    }
-    lv[0] = above[0] ? v : lv[0];
-    li[0] = above[0] ? i : li[0];
+// Float <-> int with the same order (for atomicMax on a float bound).
+__device__ __forceinline__ int f2o(float f) {
+    const int b = __float_as_int(f);
+    return b >= 0 ? b : b ^ 0x7FFFFFFF;
 }
+__device__ __forceinline__ float o2f(int k) { return __int_as_float(k >= 0 ? k : k ^ 0x7FFFFFFF); }
+
+struct KW {
+    int v[8];
+};
 
 // Hydra rows: (request, parent) -> the parent's token.
 struct GemmRows {
@@ -117,7 +118,8 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __re
                                                             const uint16_t* __restrict__ bias, GemmRows rows, int M,
                                                             int d, int din, int nh, int head0, int mtiles,
                                                             float* __restrict__ hres, float* __restrict__ hres_out,
-                                                            uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo) {
+                                                            uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo,
+                                                            int* __restrict__ bound) {
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
     __shared__ int s_tok[TM];
     __shared__ int s_b[TM];
@@ -132,6 +134,10 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __re
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g4 = lane >> 4, c16 = lane & 15, wr = w >> 1, wc = w & 1;
 
+    // the vocabulary kernel that follows keeps a lower bound of each (head, row)'s
+    // k-th best logit here; start from -inf
+    if (blockIdx.x == 0)
+        for (int j = tid; j < nh * M; j += BLOCK) bound[j] = f2o(-INFINITY);
     if (tid < TM) {
         const int m = m0 + tid;
         int b = m, tok = -1;
@@ -147,10 +153,10 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __re
     __syncthreads();
 
     const uint16_t* Wt = W + ((int64_t)head0 * d + row0) * din;
-    u32x4 ra[4], rb[4];
+    u32x4 ra[NLD], rb[NLD];
     auto fetch = [&](int k0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NLD; ++j) {
             const int i = tid + BLOCK * j;
             const int r = i / CH, c = i - (i / CH) * CH;
             ra[j] = *reinterpret_cast<const u32x4*>(Wt + (int64_t)r * din + k0 + 8 * c);
@@ -178,7 +184,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __re
     for (int k0 = 0; k0 < din; k0 += KS) {
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NLD; ++j) {
             const int i = tid + BLOCK * j;
             const int r = i / CH, c = i - (i / CH) * CH;
             *reinterpret_cast<u32x4*>(&As[r][8 * c]) = ra[j];
@@ -234,16 +240,17 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __re
 }
 
 // Phase 2: logits = U (hi + lo) for one head's 128 vocabulary rows x 128
-// activation rows; epilogue: per activation row, the block's best KL logits.
+// activation rows; epilogue: per activation row, the block's best k logits.
 __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restrict__ U,
                                                          const uint16_t* __restrict__ hhi,
                                                          const uint16_t* __restrict__ hlo, int M, int d, int V,
                                                          int nh, int head0, int vtiles, int mtiles, int kmax,
-                                                         float* __restrict__ part_val, int* __restrict__ part_idx) {
+                                                         KW kk, float* __restrict__ part_val, int* __restrict__ part_idx,
+                                                         int* __restrict__ bound) {
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
     uint16_t(*As)[LP] = reinterpret_cast<uint16_t(*)[LP]>(smem);
     uint16_t(*Bs)[TM][LP] = reinterpret_cast<uint16_t(*)[TM][LP]>(smem + TR * LP * 2);
-    float(*S)[TM] = reinterpret_cast<float(*)[TM]>(smem);
+    float(*S)[SP] = reinterpret_cast<float(*)[SP]>(smem);  // S[column][vocabulary row]
     const int units = nh * vtiles;
     int unit, mt;
     if (!decode_tile(blockIdx.x, mtiles, units, unit, mt)) return;
@@ -254,10 +261,10 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restr
     const uint16_t* Ut = U + ((int64_t)(head0 + hh) * V + v0) * d;
     const int64_t hbase = (int64_t)hh * M * d;
 
-    u32x4 ra[4], rh[4], rl[4];
+    u32x4 ra[NLD], rh[NLD], rl[NLD];
     auto fetch = [&](int k0) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NLD; ++j) {
             const int i = tid + BLOCK * j;
             const int r = i / CH, c = i - (i / CH) * CH;
             ra[j] = v0 + r < V ? *reinterpret_cast<const u32x4*>(Ut + (int64_t)r * d + k0 + 8 * c) : u32x4{0u, 0u, 0u, 0u};
@@ -280,7 +287,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restr
     for (int k0 = 0; k0 < d; k0 += KS) {
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < NLD; ++j) {
             const int i = tid + BLOCK * j;
             const int r = i / CH, c = i - (i / CH) * CH;
             *reinterpret_cast<u32x4*>(&As[r][8 * c]) = ra[j];
@@ -292,53 +299,70 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restr
         tile_mma<2>(As, Bs, wr, wc, g4, c16, acc);
     }
     __syncthreads();  // operand tiles are dead; the logit tile takes their LDS
+    // lane holds logits of vocabulary rows 64wr + 16rb + 4g4 + i (4 consecutive)
+    // for column 64wc + 16cb + c16: one 16-byte store per (rb, cb)
 #pragma unroll
     for (int rb_ = 0; rb_ < 4; ++rb_)
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) S[64 * wr + 16 * rb_ + 4 * g4 + i][64 * wc + 16 * cb + c16] = acc[rb_][cb][i];
+            *reinterpret_cast<f32x4*>(&S[64 * wc + 16 * cb + c16][64 * wr + 16 * rb_ + 4 * g4]) = acc[rb_][cb];
+    // the current bounds of this block's columns, read once, in parallel
+    __shared__ float s_bound[TM];
+    if (tid < TM)
+        s_bound[tid] = m0 + tid < M ? o2f(__hip_atomic_load(bound + (int64_t)hh * M + m0 + tid, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT))
+                                    : INFINITY;
     __syncthreads();
 
-    // thread (column mm, half): its 64 vocabulary rows into a sorted list
-    const int mm = tid & (TM - 1), half = tid >> 7;
-    float lv[KL];
-    int li[KL];
+    // Per column (row of h'), this block's best k of its 128 vocabulary rows.
+    // Candidates below the bound of the k-th best (any block's k-th best is a
+    // lower bound of the final one, so nothing of the final top-k is lost)
+    // are dropped first; the rest are taken by rounds of a wave argmax. Wave w
+    // owns columns w, w + 4, ...; control flow is uniform across the wave.
+    const int k = kk.v[hh];
+    const int va = v0 + lane, vb = v0 + lane + 64;
+    for (int col = w; col < TM; col += 4) {
+        const int m = m0 + col;
+        if (m >= M) break;  // uniform: columns past M are padding
+        const float T = s_bound[col];
+        float x0 = va < V ? S[col][lane] : -INFINITY;
+        float x1 = vb < V ? S[col][lane + 64] : -INFINITY;
+        if (x0 < T) x0 = -INFINITY;
+        if (x1 < T) x1 = -INFINITY;
+        const int cnt = __popcll(__ballot(x0 != -INFINITY)) + __popcll(__ballot(x1 != -INFINITY));
+        const int rounds = cnt < k ? cnt : k;
+        float ov = -INFINITY;
+        int oi = INT_MAX;
+        for (int r = 0; r < rounds; ++r) {
+            float bv = x0;
+            int bi = va;
+            if (ranks_above(x1, vb, bv, bi)) {
+                bv = x1;
+                bi = vb;
+            }
 #pragma unroll
-    for (int j = 0; j < KL; ++j) {
-        lv[j] = -INFINITY;
-        li[j] = INT_MAX;
-    }
-    for (int r = 64 * half; r < 64 * half + 64; ++r) {
-        const int v = v0 + r;
-        const float x = S[r][mm];
-        if (v < V && ranks_above(x, v, lv[KL - 1], li[KL - 1])) reg_insert(lv, li, x, v);
-    }
-    __syncthreads();  // the logit tile is dead; lists of the upper halves take its LDS
-    float(*LV)[KL] = reinterpret_cast<float(*)[KL]>(smem);
-    int(*LI)[KL] = reinterpret_cast<int(*)[KL]>(smem + TM * KL * 4);
-    if (half == 1) {
-#pragma unroll
-        for (int j = 0; j < KL; ++j) {
-            LV[mm][j] = lv[j];
-            LI[mm][j] = li[j];
-        }
-    }
-    __syncthreads();
-    if (half == 0) {
-#pragma unroll
-        for (int j = 0; j < KL; ++j)
-            if (ranks_above(LV[mm][j], LI[mm][j], lv[KL - 1], li[KL - 1])) reg_insert(lv, li, LV[mm][j], LI[mm][j]);
-        const int m = m0 + mm;
-        if (m < M) {
-            const int64_t o = (((int64_t)hh * M + m) * vtiles + vt) * kmax;
-#pragma unroll
-            for (int j = 0; j < KL; ++j)
-                if (j < kmax) {
-                    part_val[o + j] = lv[j];
-                    part_idx[o + j] = li[j];
+            for (int o = 32; o > 0; o >>= 1) {
+                const float tv = __shfl_xor(bv, o, 64);
+                const int ti = __shfl_xor(bi, o, 64);
+                if (ranks_above(tv, ti, bv, bi)) {
+                    bv = tv;
+                    bi = ti;
                 }
+            }
+            if (lane == r) {
+                ov = bv;
+                oi = bi;
+            }
+            if (bi == va) x0 = -INFINITY;
+            if (bi == vb) x1 = -INFINITY;
         }
+        if (lane < kmax) {
+            const int64_t o = (((int64_t)hh * M + m) * vtiles + vt) * kmax + lane;
+            part_val[o] = lane < rounds ? ov : -INFINITY;
+            part_idx[o] = lane < rounds ? oi : INT_MAX;
+        }
+        // with k candidates taken, the k-th is a lower bound for every later block
+        if (rounds == k && lane == k - 1) atomicMax(bound + (int64_t)hh * M + m, f2o(ov));
     }
 }
 
@@ -353,7 +377,8 @@ bool heads_mfma_applicable(int dt, int M, int d, int din) {
 size_t heads_mfma_ws_bytes(int M, int d, int V, int nh, int kmax) {
     const size_t vtiles = (size_t)(V + TR - 1) / TR;
     const size_t e = (size_t)nh * M * d;
-    return align256(e * 4) + 2 * align256(e * 2) + 2 * align256((size_t)nh * M * vtiles * kmax * 4);
+    return align256(e * 4) + 2 * align256(e * 2) + 2 * align256((size_t)nh * M * vtiles * kmax * 4) +
+           align256((size_t)nh * M * 4);
 }
 
 // Launches phase 1 and phase 2; the caller merges the lists (nlists = vtiles).
@@ -372,6 +397,10 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     float* pv = reinterpret_cast<float*>(w);
     w += align256((size_t)a.nh * a.M * vtiles * a.kmax * 4);
     int* pi = reinterpret_cast<int*>(w);
+    w += align256((size_t)a.nh * a.M * vtiles * a.kmax * 4);
+    int* bound = reinterpret_cast<int*>(w);
+    KW kk;
+    for (int i = 0; i < 8; ++i) kk.v[i] = i < a.nh ? a.kk[i] : 1;
 
     GemmRows rows;
     rows.kind = a.kind;
@@ -392,14 +421,14 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     const int units1 = a.nh * a.d / TR;
     hipLaunchKernelGGL(k_residual_mfma, dim3(8 * mtiles * ((units1 + 7) / 8)), dim3(BLOCK), 0, s,
                        reinterpret_cast<const uint16_t*>(a.W), reinterpret_cast<const uint16_t*>(a.b), rows, a.M, a.d,
-                       a.din, a.nh, a.head0, mtiles, hres, a.h_res, hhi, hlo);
+                       a.din, a.nh, a.head0, mtiles, hres, a.h_res, hhi, hlo, bound);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
     const int units2 = a.nh * vtiles;
     hipLaunchKernelGGL(k_vocab_mfma, dim3(8 * mtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s,
                        reinterpret_cast<const uint16_t*>(a.U), hhi, hlo, a.M, a.d, a.V, a.nh, a.head0, vtiles, mtiles,
-                       a.kmax, pv, pi);
+                       a.kmax, kk, pv, pi, bound);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
     *part_val = pv;
