@@ -27,9 +27,17 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip"))) + [os.path.join(CSRC, "api.cpp")]
 
 
+# Per-file flags. The vocabulary GEMM keeps 128 accumulators a lane; with the
+# MFMA accumulators in ordinary VGPRs the register allocator leaves them in
+# place instead of copying them between register files every K step.
+FILE_FLAGS = {
+    "heads_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + FLAGS + FILE_FLAGS.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if src.endswith(".cpp"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -366,7 +366,9 @@ __global__ __launch_bounds__(BLOCK) void k_vocab_topk(const T* __restrict__ U, c
 // merge of those lists: k rounds of a block-wide argmax over the list heads,
 // each round popping the winning list. Vocabulary indices are unique, so
 // the order (value desc, index asc) is strict and the winner is unique.
-template <int LPT>  // lists per thread
+// LPT lists per thread; LPT = 0 takes any number of lists: each thread first
+// folds lists tid, tid + BLOCK, ... into one sorted list of its k best.
+template <int LPT>
 __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ part_val,
                                                       const int* __restrict__ part_idx, int M, int nh, int nlists,
                                                       KK kk, int kmax, int32_t* __restrict__ topk_idx,
@@ -380,27 +382,55 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
     const int k = kk.v[hh];
     const int tid = threadIdx.x, lane = tid & (MD_WAVE - 1), w = tid >> 6;
     const int64_t base = ((int64_t)hh * M + m) * nlists * kmax;
-    float v[LPT][KM];
-    int ix[LPT][KM];
+    constexpr int NL = LPT > 0 ? LPT : 1;
+    float v[NL][KM];
+    int ix[NL][KM];
+    if constexpr (LPT > 0) {
 #pragma unroll
-    for (int l = 0; l < LPT; ++l) {
-        const int list = tid + BLOCK * l;
+        for (int l = 0; l < LPT; ++l) {
+            const int list = tid + BLOCK * l;
+#pragma unroll
+            for (int j = 0; j < KM; ++j) {
+                const bool ok = list < nlists && j < k;
+                v[l][j] = ok ? part_val[base + (int64_t)list * kmax + j] : -INFINITY;
+                ix[l][j] = ok ? part_idx[base + (int64_t)list * kmax + j] : INT_MAX;
+            }
+        }
+    } else {
 #pragma unroll
         for (int j = 0; j < KM; ++j) {
-            const bool ok = list < nlists && j < k;
-            v[l][j] = ok ? part_val[base + (int64_t)list * kmax + j] : -INFINITY;
-            ix[l][j] = ok ? part_idx[base + (int64_t)list * kmax + j] : INT_MAX;
+            v[0][j] = -INFINITY;
+            ix[0][j] = INT_MAX;
+        }
+        for (int list = tid; list < nlists; list += BLOCK) {
+            for (int j = 0; j < k; ++j) {
+                const float cv = part_val[base + (int64_t)list * kmax + j];
+                const int ci = part_idx[base + (int64_t)list * kmax + j];
+                // a sorted list: once an entry misses this thread's KM best, so do the rest
+                if (!ranks_above(cv, ci, v[0][KM - 1], ix[0][KM - 1])) break;
+#pragma unroll
+                for (int q = KM - 1; q >= 0; --q) {  // insertion; v[0][q - 1] is read before it moves
+                    if (!ranks_above(cv, ci, v[0][q], ix[0][q])) continue;
+                    if (q > 0 && ranks_above(cv, ci, v[0][q - 1], ix[0][q - 1])) {
+                        v[0][q] = v[0][q - 1];
+                        ix[0][q] = ix[0][q - 1];
+                    } else {
+                        v[0][q] = cv;
+                        ix[0][q] = ci;
+                    }
+                }
+            }
         }
     }
     for (int r = 0; r < k; ++r) {
         float bv = v[0][0];
-        int bi = ix[0][0], bo = tid * LPT;
+        int bi = ix[0][0], bo = tid * NL;
 #pragma unroll
-        for (int l = 1; l < LPT; ++l)
+        for (int l = 1; l < NL; ++l)
             if (ranks_above(v[l][0], ix[l][0], bv, bi)) {
                 bv = v[l][0];
                 bi = ix[l][0];
-                bo = tid * LPT + l;
+                bo = tid * NL + l;
             }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
@@ -432,10 +462,10 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
             out_v[r] = gv;
             out_i[r] = gi;
         }
-        if (go / LPT == tid) {  // pop the winning list's head
-            const int lw = go - tid * LPT;
+        if (go / NL == tid) {  // pop the winning list's head
+            const int lw = go - tid * NL;
 #pragma unroll
-            for (int l = 0; l < LPT; ++l) {
+            for (int l = 0; l < NL; ++l) {
                 if (l != lw) continue;
 #pragma unroll
                 for (int j = 0; j + 1 < KM; ++j) {
@@ -526,7 +556,7 @@ Plan make_plan(int dt, int M, int d, int din, int nh) {
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// The k-way merge of nlists sorted lists per (row, head); at most 4 lists per thread.
+// The k-way merge of nlists sorted lists per (row, head).
 hipError_t launch_merge(const float* pv, const int* pi, int M, int nh, int nlists, KK kk, int kmax, int32_t* topk_idx,
                         float* topk_val, hipStream_t s) {
     const int lpt = (nlists + BLOCK - 1) / BLOCK;
@@ -536,8 +566,11 @@ hipError_t launch_merge(const float* pv, const int* pi, int M, int nh, int nlist
     else if (lpt == 2)
         hipLaunchKernelGGL(k_topk_merge<2>, dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax, topk_idx,
                            topk_val);
-    else
+    else if (lpt <= 4)
         hipLaunchKernelGGL(k_topk_merge<4>, dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax, topk_idx,
+                           topk_val);
+    else
+        hipLaunchKernelGGL(k_topk_merge<0>, dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax, topk_idx,
                            topk_val);
     return hipGetLastError();
 }

@@ -20,13 +20,17 @@
 //   blocks select almost nothing. The per-block lists then go through the
 //   same k-way merge as the GEMV path.
 //
-// Block tile: 128 weight rows x 128 activation rows, K step 64, 4 waves of
-// 64 x 64 (4 x 4 MFMA tiles each). Operand tiles are staged in LDS (rows
+// Residual: block tile 128 weight rows x 128 activation rows, K step 64, 4
+// waves of 64 x 64 (4 x 4 MFMA tiles each), operands staged in LDS (rows
 // padded against bank conflicts) from registers loaded one K step ahead.
-// Both operands are row-major along the contraction, which is exactly the
-// MFMA operand layout (a lane reads 8 consecutive k of one row), so nothing
-// is transposed. Blocks that share a weight tile (the activation tiles of
-// one weight tile) get ids spaced by 8, i.e. the same XCD and L2.
+// Vocabulary: block tile 256 vocabulary rows x 128 activation rows, K step
+// 32, 4 waves of 128 x 64 (8 x 4 MFMA tiles, hi and lo), operands loaded
+// straight from memory into LDS two stages deep, two blocks per CU (details
+// at the kernel). Both operands are row-major along the contraction, which
+// is exactly the MFMA operand layout (a lane reads 8 consecutive k of one
+// row), so nothing is transposed. Blocks that share a weight tile (the
+// activation tiles of one weight tile) get ids spaced by 8, i.e. the same
+// XCD and L2.
 #include <math.h>
 
 #include "md_internal.h"
@@ -47,9 +51,7 @@ constexpr int CH = KS / 8;    // 16-byte chunks per row and step
 constexpr int NLD = TR * CH / BLOCK;  // 16-byte operand chunks per thread and step
 static_assert(TR == TM, "operand loops stage A and B rows with the same index");
 static_assert((TR * CH) % BLOCK == 0 && NLD >= 1, "each thread stages a whole number of chunks");
-constexpr int SP = TR + 4;    // logit tile pitch: one column (activation row) of 128 logits, padded
-constexpr int LDS_BYTES = TM * SP * 4;  // the epilogue's logit tile; covers 3 staged operand tiles
-static_assert(3 * TR * LP * 2 <= LDS_BYTES, "operand tiles fit in the logit tile's LDS");
+constexpr int LDS_BYTES = (TR + TM) * LP * 2;  // the residual's staged operand tiles
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -239,130 +241,201 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __re
     }
 }
 
-// Phase 2: logits = U (hi + lo) for one head's 128 vocabulary rows x 128
-// activation rows; epilogue: per activation row, the block's best k logits.
+// Phase 2: logits = U (hi + lo) for one head's VR vocabulary rows x VM
+// activation rows; epilogue: per activation row and 128-row half of the
+// tile, the best k logits.
+//
+// Operands reach LDS by direct buffer->LDS loads (16 bytes a lane; one
+// instruction fills 1 KB: 16 rows x 64 bytes), two stages deep, so the next
+// stage is in flight while the matrix cores work on this one; two blocks
+// share a CU, so one block's waits and epilogue overlap the other's MFMAs.
+// A row's 16-byte chunk c sits in slot c ^ ((row / 2) % 4) of its 64-byte
+// LDS row; with that permutation the 16 rows of an MFMA operand read meet no
+// bank conflict (the counters read zero).
+// Buffer resources bound each operand tile to its valid rows: loads past V
+// or M are dropped by the hardware, and their products are never selected.
+constexpr int VR = 256;            // vocabulary rows per tile
+constexpr int VM = 128;            // activation rows per tile
+constexpr int VK = 32;             // contraction elements per stage (64 bytes a row)
+constexpr int ROWB = VK * 2;
+constexpr int A_BYTES = VR * ROWB;         // 16 KB
+constexpr int B_BYTES = VM * ROWB;         // 8 KB (hi; lo follows)
+constexpr int STAGE = A_BYTES + 2 * B_BYTES;  // 32 KB
+constexpr int NPA = A_BYTES / 4096;        // 1 KB pieces a wave loads per stage: A
+constexpr int NPB = B_BYTES / 4096;        // and each of hi, lo
+static_assert(2 * (2 * STAGE + 4 * VM) <= 160 * 1024, "two blocks fit the LDS of one CU");
+static_assert(VM * 512 == 2 * STAGE, "a half of the logit tile fills both stage buffers");
+static_assert(NPA * 4096 == A_BYTES && NPB * 4096 == B_BYTES, "each wave fills whole 1 KB pieces");
+
+// word 3 of a raw buffer resource on this chip family (32-bit data format, no swizzle)
+constexpr int RSRC3 = 0x00020000;
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__device__ __forceinline__ void dmab(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, off, 0, 0, 0);
+}
+
 __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restrict__ U,
                                                          const uint16_t* __restrict__ hhi,
                                                          const uint16_t* __restrict__ hlo, int M, int d, int V,
                                                          int nh, int head0, int vtiles, int mtiles, int kmax,
                                                          KW kk, float* __restrict__ part_val, int* __restrict__ part_idx,
                                                          int* __restrict__ bound) {
-    __shared__ __align__(16) unsigned char smem[LDS_BYTES];
-    uint16_t(*As)[LP] = reinterpret_cast<uint16_t(*)[LP]>(smem);
-    uint16_t(*Bs)[TM][LP] = reinterpret_cast<uint16_t(*)[TM][LP]>(smem + TR * LP * 2);
-    float(*S)[SP] = reinterpret_cast<float(*)[SP]>(smem);  // S[column][vocabulary row]
+    __shared__ __align__(1024) unsigned char sbuf0[STAGE];
+    __shared__ __align__(1024) unsigned char sbuf1[STAGE];
+    __shared__ float s_bound[VM];
     const int units = nh * vtiles;
     int unit, mt;
     if (!decode_tile(blockIdx.x, mtiles, units, unit, mt)) return;
     const int hh = unit / vtiles, vt = unit - hh * vtiles;
-    const int v0 = vt * TR, m0 = mt * TM;
+    const int v0 = vt * VR, m0 = mt * VM;
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const int g4 = lane >> 4, c16 = lane & 15, wr = w >> 1, wc = w & 1;
-    const uint16_t* Ut = U + ((int64_t)(head0 + hh) * V + v0) * d;
     const int64_t hbase = (int64_t)hh * M * d;
 
-    u32x4 ra[NLD], rh[NLD], rl[NLD];
-    auto fetch = [&](int k0) {
+    // DMA: in 1 KB piece p = w + 4 j the lane loads row 16 p + lane / 4 =
+    // r0 + 64 j, chunk (lane % 4) ^ ((row / 2) % 4), the same for every j
+    const int r0 = 16 * w + (lane >> 2);
+    const uint32_t voff0 = (uint32_t)r0 * d * 2 + 16 * ((lane & 3) ^ ((r0 >> 1) & 3));
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(U + ((int64_t)(head0 + hh) * V + v0) * d), 0, min(V - v0, VR) * d * 2, RSRC3);
+    const __amdgpu_buffer_rsrc_t rH =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(hhi + hbase + (int64_t)m0 * d), 0, min(M - m0, VM) * d * 2, RSRC3);
+    const __amdgpu_buffer_rsrc_t rL =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(hlo + hbase + (int64_t)m0 * d), 0, min(M - m0, VM) * d * 2, RSRC3);
+    auto issue = [&](int k0, unsigned char* base) {
 #pragma unroll
-        for (int j = 0; j < NLD; ++j) {
-            const int i = tid + BLOCK * j;
-            const int r = i / CH, c = i - (i / CH) * CH;
-            ra[j] = v0 + r < V ? *reinterpret_cast<const u32x4*>(Ut + (int64_t)r * d + k0 + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-            const int m = m0 + r;
-            if (m < M) {
-                rh[j] = *reinterpret_cast<const u32x4*>(hhi + hbase + (int64_t)m * d + k0 + 8 * c);
-                rl[j] = *reinterpret_cast<const u32x4*>(hlo + hbase + (int64_t)m * d + k0 + 8 * c);
-            } else {
-                rh[j] = u32x4{0u, 0u, 0u, 0u};
-                rl[j] = u32x4{0u, 0u, 0u, 0u};
+        for (int j = 0; j < NPA; ++j) dmab(rA, base + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
+#pragma unroll
+        for (int j = 0; j < NPB; ++j) {
+            dmab(rH, base + A_BYTES + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
+            dmab(rL, base + A_BYTES + B_BYTES + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
+        }
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // operand rows of this lane: 16 apart, so all share the slot of row c16
+    const int slot = (g4 ^ ((c16 >> 1) & 3)) * 16;
+    auto compute = [&](const unsigned char* sA) {
+        const unsigned char* sB = sA + A_BYTES;
+        bf16x8 a[8];
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb)
+            a[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sA + (128 * wr + 16 * rb + c16) * ROWB + slot));
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const bf16x8 b = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(sB + s * B_BYTES + (64 * wc + 16 * cb + c16) * ROWB + slot));
+#pragma unroll
+                for (int rb = 0; rb < 8; ++rb)
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b, acc[rb][cb], 0, 0, 0);
             }
         }
     };
-    f32x4 acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    fetch(0);
-    for (int k0 = 0; k0 < d; k0 += KS) {
+
+    // two stages, unrolled so each half of the loop names its buffer (the
+    // stage count d / VK is even)
+    const int nk = d / VK;
+    issue(0, sbuf0);
+    for (int ks = 0; ks < nk; ks += 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-#pragma unroll
-        for (int j = 0; j < NLD; ++j) {
-            const int i = tid + BLOCK * j;
-            const int r = i / CH, c = i - (i / CH) * CH;
-            *reinterpret_cast<u32x4*>(&As[r][8 * c]) = ra[j];
-            *reinterpret_cast<u32x4*>(&Bs[0][r][8 * c]) = rh[j];
-            *reinterpret_cast<u32x4*>(&Bs[1][r][8 * c]) = rl[j];
-        }
+        issue((ks + 1) * VK, sbuf1);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this stage's work
+        compute(sbuf0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
         __syncthreads();
-        if (k0 + KS < d) fetch(k0 + KS);
-        tile_mma<2>(As, Bs, wr, wc, g4, c16, acc);
+        issue(min(ks + 2, nk - 1) * VK, sbuf0);  // the last pass reloads a stage nobody reads: no branch in the loop
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sbuf1);
     }
-    __syncthreads();  // operand tiles are dead; the logit tile takes their LDS
-    // lane holds logits of vocabulary rows 64wr + 16rb + 4g4 + i (4 consecutive)
-    // for column 64wc + 16cb + c16: one 16-byte store per (rb, cb)
-#pragma unroll
-    for (int rb_ = 0; rb_ < 4; ++rb_)
-#pragma unroll
-        for (int cb = 0; cb < 4; ++cb)
-            *reinterpret_cast<f32x4*>(&S[64 * wc + 16 * cb + c16][64 * wr + 16 * rb_ + 4 * g4]) = acc[rb_][cb];
-    // the current bounds of this block's columns, read once, in parallel
-    __shared__ float s_bound[TM];
-    if (tid < TM)
+    if (tid < VM)
         s_bound[tid] = m0 + tid < M ? o2f(__hip_atomic_load(bound + (int64_t)hh * M + m0 + tid, __ATOMIC_RELAXED,
                                                             __HIP_MEMORY_SCOPE_AGENT))
                                     : INFINITY;
-    __syncthreads();
-
-    // Per column (row of h'), this block's best k of its 128 vocabulary rows.
-    // Candidates below the bound of the k-th best (any block's k-th best is a
-    // lower bound of the final one, so nothing of the final top-k is lost)
-    // are dropped first; the rest are taken by rounds of a wave argmax. Wave w
-    // owns columns w, w + 4, ...; control flow is uniform across the wave.
     const int k = kk.v[hh];
-    const int va = v0 + lane, vb = v0 + lane + 64;
-    for (int col = w; col < TM; col += 4) {
-        const int m = m0 + col;
-        if (m >= M) break;  // uniform: columns past M are padding
-        const float T = s_bound[col];
-        float x0 = va < V ? S[col][lane] : -INFINITY;
-        float x1 = vb < V ? S[col][lane + 64] : -INFINITY;
-        if (x0 < T) x0 = -INFINITY;
-        if (x1 < T) x1 = -INFINITY;
-        const int cnt = __popcll(__ballot(x0 != -INFINITY)) + __popcll(__ballot(x1 != -INFINITY));
-        const int rounds = cnt < k ? cnt : k;
-        float ov = -INFINITY;
-        int oi = INT_MAX;
-        for (int r = 0; r < rounds; ++r) {
-            float bv = x0;
-            int bi = va;
-            if (ranks_above(x1, vb, bv, bi)) {
-                bv = x1;
-                bi = vb;
-            }
+    // Two passes, one per 128-row half of the tile (the waves with wr == h
+    // hold it). The half's logits go to LDS: column c (row of h') takes 512
+    // bytes in buffer c / 64, its 16-byte groups permuted by c % 16.
 #pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const float tv = __shfl_xor(bv, o, 64);
-                const int ti = __shfl_xor(bi, o, 64);
-                if (ranks_above(tv, ti, bv, bi)) {
-                    bv = tv;
-                    bi = ti;
+    for (int h = 0; h < 2; ++h) {
+        __syncthreads();  // operand stages, or the previous half's logits, are dead
+        if (wr == h) {
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    const int col = 64 * wc + 16 * cb + c16;
+                    *reinterpret_cast<f32x4*>((wc ? sbuf1 : sbuf0) + (col & 63) * 512 + (((4 * rb + g4) ^ (col & 15)) * 16)) =
+                        acc[rb][cb];
                 }
-            }
-            if (lane == r) {
-                ov = bv;
-                oi = bi;
-            }
-            if (bi == va) x0 = -INFINITY;
-            if (bi == vb) x1 = -INFINITY;
         }
-        if (lane < kmax) {
-            const int64_t o = (((int64_t)hh * M + m) * vtiles + vt) * kmax + lane;
-            part_val[o] = lane < rounds ? ov : -INFINITY;
-            part_idx[o] = lane < rounds ? oi : INT_MAX;
+        __syncthreads();
+        // Per column, the best k of this half's 128 vocabulary rows.
+        // Candidates below the bound of the k-th best (any list's k-th best
+        // is a lower bound of the final one, so nothing of the final top-k is
+        // lost) are dropped first; the rest are taken by rounds of a wave
+        // argmax. Wave w owns columns w, w + 4, ...; control flow is uniform
+        // across the wave.
+        const int vh = v0 + 128 * h;
+        const int list = 2 * vt + h;
+        for (int col = w; col < VM; col += 4) {
+            const int m = m0 + col;
+            if (m >= M) break;  // uniform: columns past M are padding
+            const float T = s_bound[col];
+            const unsigned char* Sc = (col < 64 ? sbuf0 : sbuf1) + (col & 63) * 512;
+            float x[2];
+            int cnt = 0;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int rr = lane + 64 * q;
+                x[q] = vh + rr < V ? *reinterpret_cast<const float*>(Sc + (((rr >> 2) ^ (col & 15)) * 16) + (rr & 3) * 4)
+                                   : -INFINITY;
+                if (x[q] < T) x[q] = -INFINITY;
+                cnt += __popcll(__ballot(x[q] != -INFINITY));
+            }
+            const int rounds = cnt < k ? cnt : k;
+            float ov = -INFINITY;
+            int oi = INT_MAX;
+            for (int r = 0; r < rounds; ++r) {
+                float bv = x[0];
+                int bi = vh + lane;
+                if (ranks_above(x[1], vh + lane + 64, bv, bi)) {
+                    bv = x[1];
+                    bi = vh + lane + 64;
+                }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    const float tv = __shfl_xor(bv, o, 64);
+                    const int ti = __shfl_xor(bi, o, 64);
+                    if (ranks_above(tv, ti, bv, bi)) {
+                        bv = tv;
+                        bi = ti;
+                    }
+                }
+                if (lane == r) {
+                    ov = bv;
+                    oi = bi;
+                }
+                if (bi == vh + lane) x[0] = -INFINITY;
+                if (bi == vh + lane + 64) x[1] = -INFINITY;
+            }
+            if (lane < kmax) {
+                const int64_t o = (((int64_t)hh * M + m) * (2 * vtiles) + list) * kmax + lane;
+                part_val[o] = lane < rounds ? ov : -INFINITY;
+                part_idx[o] = lane < rounds ? oi : INT_MAX;
+            }
+            // with k candidates taken, the k-th is a lower bound for every later list
+            if (rounds == k && lane == k - 1) atomicMax(bound + (int64_t)hh * M + m, f2o(ov));
         }
-        // with k candidates taken, the k-th is a lower bound for every later block
-        if (rounds == k && lane == k - 1) atomicMax(bound + (int64_t)hh * M + m, f2o(ov));
     }
 }
 
@@ -371,21 +444,23 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 bool heads_mfma_applicable(int dt, int M, int d, int din) {
-    return dt == 1 && M >= 8 && d % TR == 0 && din % KS == 0;
+    // d % 128: whole residual tiles, and an even number of vocabulary stages
+    return dt == 1 && M >= 8 && d % TR == 0 && din % KS == 0 && d % (2 * VK) == 0;
 }
 
 size_t heads_mfma_ws_bytes(int M, int d, int V, int nh, int kmax) {
-    const size_t vtiles = (size_t)(V + TR - 1) / TR;
+    const size_t vtiles = (size_t)(V + VR - 1) / VR;
     const size_t e = (size_t)nh * M * d;
-    return align256(e * 4) + 2 * align256(e * 2) + 2 * align256((size_t)nh * M * vtiles * kmax * 4) +
+    return align256(e * 4) + 2 * align256(e * 2) + 2 * align256((size_t)nh * M * 2 * vtiles * kmax * 4) +
            align256((size_t)nh * M * 4);
 }
 
-// Launches phase 1 and phase 2; the caller merges the lists (nlists = vtiles).
+// Launches phase 1 and phase 2; the caller merges the lists (two per vocabulary tile).
 hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                              float** part_val, int** part_idx, int* nlists) {
-    const int vtiles = (a.V + TR - 1) / TR;
+    const int vtiles = (a.V + VR - 1) / VR;
     const int mtiles = (a.M + TM - 1) / TM;
+    const int vmtiles = (a.M + VM - 1) / VM;
     char* w = reinterpret_cast<char*>(a.ws);
     const size_t e = (size_t)a.nh * a.M * a.d;
     float* hres = reinterpret_cast<float*>(w);
@@ -395,9 +470,9 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     uint16_t* hlo = reinterpret_cast<uint16_t*>(w);
     w += align256(e * 2);
     float* pv = reinterpret_cast<float*>(w);
-    w += align256((size_t)a.nh * a.M * vtiles * a.kmax * 4);
+    w += align256((size_t)a.nh * a.M * 2 * vtiles * a.kmax * 4);
     int* pi = reinterpret_cast<int*>(w);
-    w += align256((size_t)a.nh * a.M * vtiles * a.kmax * 4);
+    w += align256((size_t)a.nh * a.M * 2 * vtiles * a.kmax * 4);
     int* bound = reinterpret_cast<int*>(w);
     KW kk;
     for (int i = 0; i < 8; ++i) kk.v[i] = i < a.nh ? a.kk[i] : 1;
@@ -426,13 +501,13 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     if (err != hipSuccess) return err;
     if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
     const int units2 = a.nh * vtiles;
-    hipLaunchKernelGGL(k_vocab_mfma, dim3(8 * mtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s,
-                       reinterpret_cast<const uint16_t*>(a.U), hhi, hlo, a.M, a.d, a.V, a.nh, a.head0, vtiles, mtiles,
+    hipLaunchKernelGGL(k_vocab_mfma, dim3(8 * vmtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s,
+                       reinterpret_cast<const uint16_t*>(a.U), hhi, hlo, a.M, a.d, a.V, a.nh, a.head0, vtiles, vmtiles,
                        a.kmax, kk, pv, pi, bound);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
     *part_val = pv;
     *part_idx = pi;
-    *nlists = vtiles;
+    *nlists = 2 * vtiles;
     return hipSuccess;
 }

@@ -169,9 +169,11 @@ MFMA_BF16 = Workload("mfma bf16: d=256 V=1000 K=3", "medusa", B=1, d=256, V=1000
 
 
 @pytest.mark.parametrize("wl,M", [(MFMA_BF16, 8), (MFMA_BF16, 130),
-                                  (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9)), 37)])
+                                  (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9)), 37),
+                                  (replace(MFMA_BF16, d=128, V=140001, K=2, topk=(10, 3)), 9)])
 def test_heads_medusa_mfma_rows(wl, M):
-    """Eight or more bf16 rows run the MFMA path (ragged row and vocabulary tiles)."""
+    """Eight or more bf16 rows run the MFMA path (ragged row and vocabulary tiles; V = 140,001
+    leaves more than 1,024 partial lists per row for the merge)."""
     seed = 2000 + M
     w = weights(wl, seed)
     h = synth.normal(seed, 78, (M, wl.d), 1.0, wl.dtype)
