@@ -8,7 +8,8 @@ batch 1 (d = 8,192, V = 128,256, 4 heads in bf16 = 8.94 GB of weights, top-k
 (10, 4, 2, 1), 64-node tree, GQA 64/8 heads of 128, 4,096 cached positions).
 Other workloads (--workload) are secondary measurements: the batch-8 step
 whose heads run over all 512 tree nodes on the matrix cores, the Hydra step
-(four sequential head levels), the 8B-shaped step and the top-1 chain.
+(four sequential head levels), the 8B-shaped step, the top-1 chain, and the
+70B-shaped step with one vocabulary projection shared by the four heads.
 
 Prints one JSON line: steps/s, the roofline of the dominant kernel (the
 vocabulary projection + top-k, timed live with HIP events that the library
@@ -48,7 +49,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="70b", choices=["70b", "70b_chain", "8b", "tiny", "70b_b8", "hydra_b4"])
+    ap.add_argument("--workload", default="70b",
+                    choices=["70b", "70b_chain", "8b", "tiny", "70b_b8", "hydra_b4", "70b_shared"])
     ap.add_argument("--sets", type=int, default=8, help="input sets rotated to keep them out of the 256 MB MALL")
     ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps timed for the CPU baseline (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -128,7 +130,8 @@ def main() -> int:
     torch.cuda.synchronize()
     log("%d input sets on the GPU" % len(sets))
 
-    cfg = md.StepConfig(kind=md.MD_HEADS_HYDRA if hydra else md.MD_HEADS_MEDUSA,
+    kind = md.MD_HEADS_HYDRA if hydra else (md.MD_HEADS_MEDUSA_SHARED if wl.shared_u else md.MD_HEADS_MEDUSA)
+    cfg = md.StepConfig(kind=kind,
                         dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, B=wl.B,
                         M=wl.B if hydra else wl.M, d=wl.d, V=wl.V, K=wl.K, k_per_head=wl.topk, parent=topo.parent,
                         rank=topo.rank, Hq=wl.Hq, Hkv=wl.Hkv, hd=wl.hd, Lcap=wl.Lcap, max_len=wl.L_max)
@@ -202,7 +205,9 @@ def main() -> int:
         head_rows = [wl.B * len(oracle.hydra_rows(topo.parent, lvl)) for lvl in range(1, depth + 1)]
     else:
         head_rows = [wl.M] * wl.K
-    vocab_bytes = wl.K * wl.V * wl.d * esz if not hydra else depth * wl.V * wl.d * esz
+    # U bytes read per step: one matrix per head (per level for Hydra), or one shared by the heads
+    u_reads = depth if hydra else (1 if wl.shared_u else wl.K)
+    vocab_bytes = u_reads * wl.V * wl.d * esz
     vocab_bytes += sum(head_rows) * wl.d * 4
     vocab_flops = 2.0 * wl.V * wl.d * sum(head_rows)  # algorithmic multiply-adds of the projections
     kernel = "vocabulary projection + per-head top-k"
@@ -225,10 +230,12 @@ def main() -> int:
                 traffic = pmc.get("hbm_bytes_per_launch")
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
-                    "kernel": "k_vocab_topk (%s)" % kernel if not hydra else "vocabulary kernels of the 4 levels",
+                    "kernel": ("vocabulary kernels of the 4 levels" if hydra else
+                               "k_vocab_topk (%s%s)" % (kernel, "; one U for the %d heads" % wl.K if wl.shared_u
+                                                        else "")),
                     "kernel_ms": round(vocab_ms, 4), "bytes_per_launch": vocab_bytes,
                     "stream_read_GBps": round(stream_gbs, 1), "frac_of_stream_read": round(achieved / stream_gbs, 4)}
-    step_bytes = (md.md_heads_weight_bytes(1 if hydra else 0, 1 if esz == 2 else 0, wl.d, wl.V, wl.K)
+    step_bytes = (md.md_heads_weight_bytes(kind, 1 if esz == 2 else 0, wl.d, wl.V, wl.K)
                   + 2 * wl.B * wl.Hkv * (wl.L_max + wl.N) * wl.hd * esz  # K and V of prefix + tree (upper bound)
                   + 2 * wl.B * wl.N * wl.Hq * wl.hd * esz  # q in, attention out
                   + wl.B * wl.N * wl.V * 4)  # verification logits

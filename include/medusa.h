@@ -58,7 +58,7 @@ typedef enum {
 } md_status;
 
 typedef enum { MD_F32 = 0, MD_BF16 = 1 } md_dtype;
-typedef enum { MD_HEADS_MEDUSA = 0, MD_HEADS_HYDRA = 1 } md_heads_kind;
+typedef enum { MD_HEADS_MEDUSA = 0, MD_HEADS_HYDRA = 1, MD_HEADS_MEDUSA_SHARED = 2 } md_heads_kind;
 
 #define MD_MAX_NODES 64 /* a tree fits one 64-lane wavefront and one 64-bit mask */
 #define MD_MAX_HEADS 8
@@ -86,11 +86,15 @@ int md_tree_validate(const md_tree* t, int K, const int32_t* k_per_head);
 /* Bytes of weights one call of the heads reads: K heads of (d x din residual
  * matrix + d bias + V x d projection), din = d (Medusa) or 2d (Hydra), at the
  * storage size of dt ("Cost per step": 1,117.8M parameters per head at
- * d = 8,192, V = 128,256). Returns -1 on invalid arguments. */
+ * d = 8,192, V = 128,256). With one projection shared by the heads
+ * (MD_HEADS_MEDUSA_SHARED) the V x d matrix counts once ("What interviewers
+ * probe next": sharing saves 3.15B of the 4.47B). Returns -1 on invalid
+ * arguments. */
 int64_t md_heads_weight_bytes(int kind, int dt, int d, int V, int K);
 
-/* Workspace the heads need for M rows (Medusa) or the largest level's rows
- * (Hydra: B requests times the most parents on one level, at most 64 * B). */
+/* Workspace the heads need for M rows (Medusa, shared or not) or the largest
+ * level's rows (Hydra: B requests times the most parents on one level, at
+ * most 64 * B). */
 size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, int kmax);
 
 /* The draft heads and their top-k lists.
@@ -102,7 +106,13 @@ size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, in
  * topk_idx[m][k][j], topk_val[m][k][j] (device int32 / float32, [M][K][kmax])
  * receive the k_per_head[k] best logits ordered by value descending, equal
  * values by index ascending; entries j >= k_per_head[k] are -1 / -inf.
- * h' enters the projection in float32.
+ * h' enters the projection in float32 (with 8 or more bf16 rows, as the sum
+ * of two bf16 terms hi + lo, |h' - hi - lo| <= 2^-17 |h'|).
+ *
+ * Medusa with one shared projection (kind = MD_HEADS_MEDUSA_SHARED, level =
+ * 0; "What interviewers probe next": the heads keep their residual blocks
+ * and use a single vocabulary matrix): as Medusa, with logit = U h'_k[m] for
+ * every head and U [V][d]. The K M vectors h' share one pass over U.
  *
  * Hydra (kind = MD_HEADS_HYDRA, level = i in 1..K): head i-1 only, one row per
  * (request b < M, parent p at depth i-1 that has children in `tree`, in node
@@ -123,7 +133,8 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
 
 /* The candidate tree's tokens and positions ("Trees").
  *
- * Medusa (kind = MD_HEADS_MEDUSA, level = 0): tree_tok[b][n] = root_tok[b] for
+ * Medusa (kind = MD_HEADS_MEDUSA or MD_HEADS_MEDUSA_SHARED, level = 0):
+ * tree_tok[b][n] = root_tok[b] for
  * the root, else topk_idx[src_row[b]][depth(n) - 1][rank(n)] with topk_idx
  * [M][K][kmax]; tree_pos[b][n] = lens[b] + depth(n). A src_row entry outside
  * [0, M) yields -1 tokens for that request's non-root nodes.

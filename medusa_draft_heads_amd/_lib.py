@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(HERE, "libmedusa.so")
 
 MD_OK, MD_EINVAL, MD_EUNSUPPORTED, MD_ERANGE, MD_EWORKSPACE, MD_EHIP = 0, -1, -2, -3, -4, -5
 MD_F32, MD_BF16 = 0, 1
-MD_HEADS_MEDUSA, MD_HEADS_HYDRA = 0, 1
+MD_HEADS_MEDUSA, MD_HEADS_HYDRA, MD_HEADS_MEDUSA_SHARED = 0, 1, 2
 MD_MAX_NODES, MD_MAX_HEADS, MD_MAX_TOPK = 64, 8, 16
 
 EXPORTS = (

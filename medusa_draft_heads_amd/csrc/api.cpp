@@ -102,13 +102,16 @@ const char* md_last_error(void) { return g_err.c_str(); }
 
 int md_tree_validate(const md_tree* t, int K, const int32_t* k_per_head) { return expand_tree(t, K, k_per_head, nullptr); }
 
+static bool known_kind(int kind) {
+    return kind == MD_HEADS_MEDUSA || kind == MD_HEADS_HYDRA || kind == MD_HEADS_MEDUSA_SHARED;
+}
+
 int64_t md_heads_weight_bytes(int kind, int dt, int d, int V, int K) {
-    if ((kind != MD_HEADS_MEDUSA && kind != MD_HEADS_HYDRA) || (dt != MD_F32 && dt != MD_BF16) || d < 1 || V < 1 ||
-        K < 1)
-        return -1;
+    if (!known_kind(kind) || (dt != MD_F32 && dt != MD_BF16) || d < 1 || V < 1 || K < 1) return -1;
     const int64_t din = kind == MD_HEADS_HYDRA ? 2LL * d : (int64_t)d;
-    const int64_t per_head = (int64_t)d * din + d + (int64_t)V * d;
-    return (int64_t)K * per_head * (dt == MD_F32 ? 4 : 2);
+    const int64_t residual = (int64_t)d * din + d, projection = (int64_t)V * d;
+    const int64_t params = kind == MD_HEADS_MEDUSA_SHARED ? K * residual + projection : K * (residual + projection);
+    return params * (dt == MD_F32 ? 4 : 2);
 }
 
 size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, int kmax) {
@@ -117,19 +120,19 @@ size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, in
         // any level has at most 63 parents per request; size for every row count up to that
         size_t need = 0;
         for (int rows = M; rows <= M * (MD_MAX_NODES - 1); rows += M) {
-            const size_t b = heads_ws_bound(dt, rows, d, 2 * d, V, 1, kmax);
+            const size_t b = heads_ws_bound(dt, rows, d, 2 * d, V, 1, kmax, 0);
             if (b > need) need = b;
         }
         return need;
     }
-    return heads_ws_bound(dt, M, d, d, V, K, kmax);
+    return heads_ws_bound(dt, M, d, d, V, K, kmax, kind == MD_HEADS_MEDUSA_SHARED);
 }
 
 int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t* k_per_head, int level,
                     const md_tree* tree, const void* h, const void* W, const void* b, const void* U, const void* E,
                     const int32_t* root_tok, const int32_t* tree_tok, int32_t* topk_idx, float* topk_val,
                     float* h_res, void* ws, size_t ws_bytes, void* stream) {
-    if (kind != MD_HEADS_MEDUSA && kind != MD_HEADS_HYDRA) return fail(MD_EINVAL, "kind = %d", kind);
+    if (!known_kind(kind)) return fail(MD_EINVAL, "kind = %d", kind);
     if (check_dt(dt)) return MD_EINVAL;
     if (M < 0) return fail(MD_EINVAL, "M = %d", M);
     if (K < 1 || K > MD_MAX_HEADS) return fail(MD_EINVAL, "K = %d heads (1..8 supported)", K);
@@ -151,7 +154,8 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
     memset(&a, 0, sizeof(a));
     DevTree dt_tree;
     const DevTree* tp = nullptr;
-    a.kind = kind;
+    a.kind = kind == MD_HEADS_HYDRA ? 1 : 0;
+    a.shared_u = kind == MD_HEADS_MEDUSA_SHARED;
     a.dt = dt;
     a.d = d;
     a.din = din;
@@ -170,14 +174,14 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
     a.h_res = h_res;
     a.ws = ws;
     size_t need;
-    if (kind == MD_HEADS_MEDUSA) {
+    if (kind != MD_HEADS_HYDRA) {
         if (level != 0) return fail(MD_EINVAL, "Medusa heads take level 0 (got %d)", level);
         a.M = M;
         a.B = M;
         a.nh = K;
         a.head0 = 0;
         for (int i = 0; i < K; ++i) a.kk[i] = k_per_head[i];
-        need = heads_ws_bytes(dt, M, d, d, V, K, kmax);
+        need = heads_ws_bytes(dt, M, d, d, V, K, kmax, a.shared_u);
     } else {
         if (level < 1 || level > K) return fail(MD_EINVAL, "Hydra level %d outside 1..%d", level, K);
         int rc = expand_tree(tree, K, k_per_head, &dt_tree);
@@ -192,7 +196,7 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
         a.kk[0] = k_per_head[level - 1];
         tp = &dt_tree;
         if (P == 0) return MD_OK;  // nothing at this depth
-        need = heads_ws_bytes(dt, a.M, d, din, V, 1, kmax);
+        need = heads_ws_bytes(dt, a.M, d, din, V, 1, kmax, 0);
     }
     if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     return hip_status(heads_launch(a, tp, (hipStream_t)stream, g_ev0, g_ev1), "md_medusa_heads");
@@ -204,11 +208,11 @@ int md_tree_build(const md_tree* tree, int kind, int B, int M, int K, int kmax, 
     DevTree t;
     int rc = expand_tree(tree, K, nullptr, &t);
     if (rc) return rc;
-    if (kind != MD_HEADS_MEDUSA && kind != MD_HEADS_HYDRA) return fail(MD_EINVAL, "kind = %d", kind);
+    if (!known_kind(kind)) return fail(MD_EINVAL, "kind = %d", kind);
     if (B < 0 || kmax < 1 || kmax > MD_MAX_TOPK) return fail(MD_EINVAL, "B = %d, kmax = %d", B, kmax);
     for (int n = 1; n < t.n; ++n)
         if (t.rank[n] >= kmax) return fail(MD_EINVAL, "node %d: rank %d but lists hold %d", n, t.rank[n], kmax);
-    if (kind == MD_HEADS_MEDUSA) {
+    if (kind != MD_HEADS_HYDRA) {
         if (level != 0) return fail(MD_EINVAL, "Medusa trees build all levels at once (level 0)");
         if (M < 1) return fail(MD_EINVAL, "M = %d", M);
         if (B > 0 && !src_row) return fail(MD_EINVAL, "src_row is NULL");
@@ -218,7 +222,7 @@ int md_tree_build(const md_tree* tree, int kind, int B, int M, int K, int kmax, 
     }
     if (B == 0) return MD_OK;
     if (!topk_idx || !root_tok || !lens || !tree_tok || !tree_pos) return fail(MD_EINVAL, "a required pointer is NULL");
-    return hip_status(tree_build_launch(t, kind, B, M, K, kmax, level, topk_idx, src_row, root_tok, lens, tree_tok,
+    return hip_status(tree_build_launch(t, kind == MD_HEADS_HYDRA ? 1 : 0, B, M, K, kmax, level, topk_idx, src_row, root_tok, lens, tree_tok,
                                         tree_pos, (hipStream_t)stream),
                       "md_tree_build");
 }

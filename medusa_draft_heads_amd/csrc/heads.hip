@@ -23,6 +23,8 @@
 // all blocks of a head.
 #include <math.h>
 
+#include <algorithm>
+
 #include "md_internal.h"
 
 namespace {
@@ -269,17 +271,22 @@ __global__ __launch_bounds__(BLOCK, 4) void k_residual(const T* __restrict__ W, 
 }
 
 // Per wave: the k best logits of U[head0+hh] hres[hh][m] over the wave's rows.
-template <typename T, int MR>
-__global__ __launch_bounds__(BLOCK) void k_vocab_topk(const T* __restrict__ U, const float* __restrict__ hres,
+// With one projection shared by the heads (Mh > 0) there is a single U and
+// row m of hres ([heads][Mh][d] read as [M][d]) belongs to head m / Mh,
+// whose top-k width it takes. NW waves per block share one copy of the MR
+// rows of h' in LDS (4 rows of d = 8,192 take 128 KB, so more waves per block
+// is the only way to more waves per CU).
+template <typename T, int MR, int NW>
+__global__ __launch_bounds__(NW * MD_WAVE) void k_vocab_topk(const T* __restrict__ U, const float* __restrict__ hres,
                                                       int M, int m0, int d, int V, int nh, int head0,
-                                                      int wg_per_head, KK kk, int kmax,
+                                                      int wg_per_head, KK kk, int kmax, int Mh,
                                                       float* __restrict__ part_val, int* __restrict__ part_idx) {
-    extern __shared__ __align__(16) float xs[];  // [MR][d]
+    extern __shared__ __align__(16) float xs[];  // [MR][d]; later the wave lists
     const int hh = blockIdx.x / wg_per_head;
     const int wgi = blockIdx.x - hh * wg_per_head;
     if (hh >= nh) return;
     const int mr = min(MR, M - m0);
-    for (int i = threadIdx.x; i < MR * d / 4; i += BLOCK) {
+    for (int i = threadIdx.x; i < MR * d / 4; i += NW * MD_WAVE) {
         const int e0 = i * 4;
         const int mm = e0 / d, c = e0 - (e0 / d) * d;
         *reinterpret_cast<f32x4*>(xs + e0) =
@@ -289,10 +296,12 @@ __global__ __launch_bounds__(BLOCK) void k_vocab_topk(const T* __restrict__ U, c
     __syncthreads();
 
     const int lane = threadIdx.x & (MD_WAVE - 1);
-    const int wih = wgi * NWAVE + (threadIdx.x >> 6);
-    const int wph = wg_per_head * NWAVE;
+    const int wih = wgi * NW + (threadIdx.x >> 6);
+    const int wph = wg_per_head * NW;
     const int r0 = (int)((int64_t)V * wih / wph), r1 = (int)((int64_t)V * (wih + 1) / wph);
-    const int k = kk.v[hh];
+    int km[MR];  // top-k width of each row
+#pragma unroll
+    for (int m = 0; m < MR; ++m) km[m] = kk.v[Mh > 0 ? min((m0 + m) / Mh, 7) : hh];
     const T* Uh = U + (int64_t)(head0 + hh) * V * d;
 
     float lv[MR], tv[MR];
@@ -314,21 +323,23 @@ __global__ __launch_bounds__(BLOCK) void k_vocab_topk(const T* __restrict__ U, c
             for (int m = 0; m < MR; ++m) {
                 const float s = wave_sum(acc[rr][m]);
                 if (rr < nv && m < mr && ranks_above(s, r + rr, tv[m], ti[m])) {
-                    list_insert(lv[m], li[m], s, r + rr, k, lane);
-                    tv[m] = __shfl(lv[m], k - 1, MD_WAVE);
-                    ti[m] = __shfl(li[m], k - 1, MD_WAVE);
+                    list_insert(lv[m], li[m], s, r + rr, km[m], lane);
+                    tv[m] = __shfl(lv[m], km[m] - 1, MD_WAVE);
+                    ti[m] = __shfl(li[m], km[m] - 1, MD_WAVE);
                 }
             }
         }
     }
-    // merge the block's wave lists in LDS; one list per block goes to memory
-    __shared__ float sv[MR][NWAVE][MD_WAVE];
-    __shared__ int si[MR][NWAVE][MD_WAVE];
+    // merge the block's wave lists in LDS (over h', now dead); one list per
+    // block goes to memory
+    __syncthreads();
+    float* sv = xs;                                        // [MR][NW][64]
+    int* si = reinterpret_cast<int*>(xs + MR * NW * MD_WAVE);  // [MR][NW][64]
     const int wv = threadIdx.x >> 6;
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
-        sv[m][wv][lane] = lane < k ? lv[m] : -INFINITY;
-        si[m][wv][lane] = lane < k ? li[m] : INT_MAX;
+        sv[(m * NW + wv) * MD_WAVE + lane] = lane < km[m] ? lv[m] : -INFINITY;
+        si[(m * NW + wv) * MD_WAVE + lane] = lane < km[m] ? li[m] : INT_MAX;
     }
     __syncthreads();
     if (wv != 0) return;
@@ -337,19 +348,19 @@ __global__ __launch_bounds__(BLOCK) void k_vocab_topk(const T* __restrict__ U, c
         if (m >= mr) continue;
         float bv = -INFINITY, btv = -INFINITY;
         int bi = INT_MAX, bti = INT_MAX;
-        for (int w2 = 0; w2 < NWAVE; ++w2) {
-            const float cv = sv[m][w2][lane];
-            const int ci = si[m][w2][lane];
-            uint64_t bm = __ballot(lane < k && ranks_above(cv, ci, btv, bti));
+        for (int w2 = 0; w2 < NW; ++w2) {
+            const float cv = sv[(m * NW + w2) * MD_WAVE + lane];
+            const int ci = si[(m * NW + w2) * MD_WAVE + lane];
+            uint64_t bm = __ballot(lane < km[m] && ranks_above(cv, ci, btv, bti));
             while (bm) {
                 const int src = __ffsll((long long)bm) - 1;
                 bm &= bm - 1;
                 const float x = __shfl(cv, src, MD_WAVE);
                 const int xi = __shfl(ci, src, MD_WAVE);
                 if (ranks_above(x, xi, btv, bti)) {
-                    list_insert(bv, bi, x, xi, k, lane);
-                    btv = __shfl(bv, k - 1, MD_WAVE);
-                    bti = __shfl(bi, k - 1, MD_WAVE);
+                    list_insert(bv, bi, x, xi, km[m], lane);
+                    btv = __shfl(bv, km[m] - 1, MD_WAVE);
+                    bti = __shfl(bi, km[m] - 1, MD_WAVE);
                 }
             }
         }
@@ -487,11 +498,13 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
 }
 
 struct Plan {
-    int MR;
+    int MR;   // rows per residual pass
+    int MRv;  // rows per vocabulary pass
     int res_grid;
     int voc_grid;
     int wg_per_head;
     int wph;
+    int voc_nw;  // waves per vocabulary block
     size_t res_lds, voc_lds;
 };
 
@@ -514,44 +527,52 @@ int device_cus() {
 // Resident blocks per CU for a kernel at this dynamic LDS size, capped at 4,
 // so that a grid of CUs x this many blocks runs in a single round.
 template <typename K>
-int resident_blocks(K kernel, size_t lds) {
+int resident_blocks(K kernel, size_t lds, int threads = BLOCK) {
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, BLOCK, lds) != hipSuccess || n < 1) n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, threads, lds) != hipSuccess || n < 1) n = 1;
     return n > 4 ? 4 : n;
 }
 
+// Waves per vocabulary block for MR rows per pass. Four rows of h' fill
+// 128 KB of LDS, one block per CU; 12 waves (3 per SIMD, 170 VGPRs each) beat
+// 8 and 16 (16 spills): 5.9 vs 5.1 and 4.9 TB/s on the 70B-shaped shared
+// projection.
+constexpr int vocab_waves(int mr) { return mr == 4 ? 12 : NWAVE; }
+
+// nh heads over M rows; with a shared projection the vocabulary stage is one
+// matrix over nh * M rows.
 template <typename T>
-Plan make_plan_t(int M, int d, int din, int nh) {
+Plan make_plan_t(int M, int d, int din, int nh, int shared_u) {
     Plan p;
+    const int rows_v = shared_u ? nh * M : M, nh_u = shared_u ? 1 : nh;
     p.MR = pick_mr(M, din);
+    p.MRv = pick_mr(rows_v, d);
     p.res_lds = (size_t)p.MR * din * 4;
-    p.voc_lds = (size_t)p.MR * d * 4;
+    p.voc_nw = vocab_waves(p.MRv);
+    p.voc_lds = std::max((size_t)p.MRv * d * 4, (size_t)p.MRv * p.voc_nw * MD_WAVE * 8);  // h', then the wave lists
     const int cus = device_cus();
     int rb, vb;
     switch (p.MR) {
-        case 4:
-            rb = resident_blocks(k_residual<T, 4>, p.res_lds);
-            vb = resident_blocks(k_vocab_topk<T, 4>, p.voc_lds);
-            break;
-        case 2:
-            rb = resident_blocks(k_residual<T, 2>, p.res_lds);
-            vb = resident_blocks(k_vocab_topk<T, 2>, p.voc_lds);
-            break;
-        default:
-            rb = resident_blocks(k_residual<T, 1>, p.res_lds);
-            vb = resident_blocks(k_vocab_topk<T, 1>, p.voc_lds);
+        case 4: rb = resident_blocks(k_residual<T, 4>, p.res_lds); break;
+        case 2: rb = resident_blocks(k_residual<T, 2>, p.res_lds); break;
+        default: rb = resident_blocks(k_residual<T, 1>, p.res_lds);
+    }
+    switch (p.MRv) {
+        case 4: vb = resident_blocks(k_vocab_topk<T, 4, vocab_waves(4)>, p.voc_lds, p.voc_nw * MD_WAVE); break;
+        case 2: vb = resident_blocks(k_vocab_topk<T, 2, vocab_waves(2)>, p.voc_lds, p.voc_nw * MD_WAVE); break;
+        default: vb = resident_blocks(k_vocab_topk<T, 1, vocab_waves(1)>, p.voc_lds, p.voc_nw * MD_WAVE);
     }
     p.res_grid = cus * rb;
     const int vg = cus * vb;
-    p.wg_per_head = vg / nh;
+    p.wg_per_head = vg / nh_u;
     if (p.wg_per_head < 1) p.wg_per_head = 1;
-    p.voc_grid = p.wg_per_head * nh;
-    p.wph = p.wg_per_head * NWAVE;
+    p.voc_grid = p.wg_per_head * nh_u;
+    p.wph = p.wg_per_head * p.voc_nw;
     return p;
 }
 
-Plan make_plan(int dt, int M, int d, int din, int nh) {
-    return dt == 0 ? make_plan_t<float>(M, d, din, nh) : make_plan_t<uint16_t>(M, d, din, nh);
+Plan make_plan(int dt, int M, int d, int din, int nh, int shared_u) {
+    return dt == 0 ? make_plan_t<float>(M, d, din, nh, shared_u) : make_plan_t<uint16_t>(M, d, din, nh, shared_u);
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -577,7 +598,7 @@ hipError_t launch_merge(const float* pv, const int* pi, int M, int nh, int nlist
 
 template <typename T>
 hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    const Plan p = make_plan(a.dt, a.M, a.d, a.din, a.nh);
+    const Plan p = make_plan(a.dt, a.M, a.d, a.din, a.nh, a.shared_u);
     char* ws = reinterpret_cast<char*>(a.ws);
     float* hres = reinterpret_cast<float*>(ws);
     ws += align256((size_t)a.nh * a.M * a.d * 4);
@@ -627,19 +648,25 @@ hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
         hipError_t e = hipEventRecord(ev0, s);
         if (e != hipSuccess) return e;
     }
-    for (int m0 = 0; m0 < a.M; m0 += p.MR) {
-        switch (p.MR) {
+    // a shared projection is one matrix over the heads' nh * M rows
+    const int rows_v = a.shared_u ? a.nh * a.M : a.M, nh_u = a.shared_u ? 1 : a.nh;
+    const int head0_u = a.shared_u ? 0 : a.head0, Mh = a.shared_u ? a.M : 0;
+    for (int m0 = 0; m0 < rows_v; m0 += p.MRv) {
+        switch (p.MRv) {
             case 4:
-                hipLaunchKernelGGL((k_vocab_topk<T, 4>), dim3(p.voc_grid), dim3(BLOCK), p.voc_lds, s, U, hres, a.M,
-                                   m0, a.d, a.V, a.nh, a.head0, p.wg_per_head, kk, a.kmax, pv, pi);
+                hipLaunchKernelGGL((k_vocab_topk<T, 4, vocab_waves(4)>), dim3(p.voc_grid), dim3(p.voc_nw * MD_WAVE),
+                                   p.voc_lds, s, U, hres, rows_v,
+                                   m0, a.d, a.V, nh_u, head0_u, p.wg_per_head, kk, a.kmax, Mh, pv, pi);
                 break;
             case 2:
-                hipLaunchKernelGGL((k_vocab_topk<T, 2>), dim3(p.voc_grid), dim3(BLOCK), p.voc_lds, s, U, hres, a.M,
-                                   m0, a.d, a.V, a.nh, a.head0, p.wg_per_head, kk, a.kmax, pv, pi);
+                hipLaunchKernelGGL((k_vocab_topk<T, 2, vocab_waves(2)>), dim3(p.voc_grid), dim3(p.voc_nw * MD_WAVE),
+                                   p.voc_lds, s, U, hres, rows_v,
+                                   m0, a.d, a.V, nh_u, head0_u, p.wg_per_head, kk, a.kmax, Mh, pv, pi);
                 break;
             default:
-                hipLaunchKernelGGL((k_vocab_topk<T, 1>), dim3(p.voc_grid), dim3(BLOCK), p.voc_lds, s, U, hres, a.M,
-                                   m0, a.d, a.V, a.nh, a.head0, p.wg_per_head, kk, a.kmax, pv, pi);
+                hipLaunchKernelGGL((k_vocab_topk<T, 1, vocab_waves(1)>), dim3(p.voc_grid), dim3(p.voc_nw * MD_WAVE),
+                                   p.voc_lds, s, U, hres, rows_v,
+                                   m0, a.d, a.V, nh_u, head0_u, p.wg_per_head, kk, a.kmax, Mh, pv, pi);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -653,13 +680,14 @@ hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
 
 }  // namespace
 
-size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax) {
+size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u) {
     if (heads_mfma_applicable(dt, M, d, din)) return heads_mfma_ws_bytes(M, d, V, nh, kmax);
-    const Plan p = make_plan(dt, M, d, din, nh);
+    const Plan p = make_plan(dt, M, d, din, nh, shared_u);
     return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * p.wg_per_head * kmax * 4);
 }
 
-size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax) {
+size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u) {
+    (void)shared_u;  // a shared projection has at most as many lists per row as a head of its own
     const size_t mfma = heads_mfma_applicable(dt, M, d, din) ? heads_mfma_ws_bytes(M, d, V, nh, kmax) : 0;
     const size_t lists_max = (size_t)device_cus() * 4;  // blocks per head at most
     const size_t gemv = align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * lists_max * kmax * 4);

@@ -276,12 +276,14 @@ __device__ __forceinline__ void dmab(__amdgpu_buffer_rsrc_t r, unsigned char* ds
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, off, 0, 0, 0);
 }
 
+// With one projection shared by the heads (Mh > 0) there is a single U and
+// activation row m ([heads][Mh][d] read as [M][d]) belongs to head m / Mh.
 __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restrict__ U,
                                                          const uint16_t* __restrict__ hhi,
                                                          const uint16_t* __restrict__ hlo, int M, int d, int V,
                                                          int nh, int head0, int vtiles, int mtiles, int kmax,
-                                                         KW kk, float* __restrict__ part_val, int* __restrict__ part_idx,
-                                                         int* __restrict__ bound) {
+                                                         KW kk, int Mh, float* __restrict__ part_val,
+                                                         int* __restrict__ part_idx, int* __restrict__ bound) {
     __shared__ __align__(1024) unsigned char sbuf0[STAGE];
     __shared__ __align__(1024) unsigned char sbuf1[STAGE];
     __shared__ float s_bound[VM];
@@ -361,7 +363,6 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restr
         s_bound[tid] = m0 + tid < M ? o2f(__hip_atomic_load(bound + (int64_t)hh * M + m0 + tid, __ATOMIC_RELAXED,
                                                             __HIP_MEMORY_SCOPE_AGENT))
                                     : INFINITY;
-    const int k = kk.v[hh];
     // Two passes, one per 128-row half of the tile (the waves with wr == h
     // hold it). The half's logits go to LDS: column c (row of h') takes 512
     // bytes in buffer c / 64, its 16-byte groups permuted by c % 16.
@@ -390,6 +391,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restr
         for (int col = w; col < VM; col += 4) {
             const int m = m0 + col;
             if (m >= M) break;  // uniform: columns past M are padding
+            const int k = kk.v[Mh > 0 ? min(m / Mh, 7) : hh];
             const float T = s_bound[col];
             const unsigned char* Sc = (col < 64 ? sbuf0 : sbuf1) + (col & 63) * 512;
             float x[2];
@@ -460,7 +462,6 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
                              float** part_val, int** part_idx, int* nlists) {
     const int vtiles = (a.V + VR - 1) / VR;
     const int mtiles = (a.M + TM - 1) / TM;
-    const int vmtiles = (a.M + VM - 1) / VM;
     char* w = reinterpret_cast<char*>(a.ws);
     const size_t e = (size_t)a.nh * a.M * a.d;
     float* hres = reinterpret_cast<float*>(w);
@@ -500,10 +501,13 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
-    const int units2 = a.nh * vtiles;
+    // a shared projection is one matrix over the heads' nh * M rows
+    const int rows_v = a.shared_u ? a.nh * a.M : a.M, nh_u = a.shared_u ? 1 : a.nh;
+    const int vmtiles = (rows_v + VM - 1) / VM;
+    const int units2 = nh_u * vtiles;
     hipLaunchKernelGGL(k_vocab_mfma, dim3(8 * vmtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s,
-                       reinterpret_cast<const uint16_t*>(a.U), hhi, hlo, a.M, a.d, a.V, a.nh, a.head0, vtiles, vmtiles,
-                       a.kmax, kk, pv, pi, bound);
+                       reinterpret_cast<const uint16_t*>(a.U), hhi, hlo, rows_v, a.d, a.V, nh_u,
+                       a.shared_u ? 0 : a.head0, vtiles, vmtiles, a.kmax, kk, a.shared_u ? a.M : 0, pv, pi, bound);
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
     *part_val = pv;

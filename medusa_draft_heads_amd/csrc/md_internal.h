@@ -25,7 +25,8 @@ struct DevTree {
 
 // ---- heads (heads.hip) ----
 struct HeadsArgs {
-    int kind;  // 0 Medusa, 1 Hydra
+    int kind;  // 0 Medusa, 1 Hydra (a shared projection is Medusa with shared_u)
+    int shared_u;  // 1: one U [V][d] for every head
     int dt;    // 0 f32, 1 bf16
     int M;     // rows through the heads this call
     int B;     // Hydra: requests
@@ -48,8 +49,8 @@ struct HeadsArgs {
     void* ws;
 };
 
-size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax);  // this plan
-size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax);  // any plan of these sizes
+size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u);  // this plan
+size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u);  // any plan of these sizes
 // matrix-core path for many rows (heads_mfma.hip)
 bool heads_mfma_applicable(int dt, int M, int d, int din);
 size_t heads_mfma_ws_bytes(int M, int d, int V, int nh, int kmax);

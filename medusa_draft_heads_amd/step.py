@@ -18,7 +18,7 @@ from . import _lib as L
 
 @dataclass
 class StepConfig:
-    kind: int  # L.MD_HEADS_MEDUSA or L.MD_HEADS_HYDRA
+    kind: int  # L.MD_HEADS_MEDUSA, L.MD_HEADS_HYDRA or L.MD_HEADS_MEDUSA_SHARED (U is [V][d])
     dtype: torch.dtype  # storage type of activations, weights and cache
     B: int  # requests
     M: int  # rows of h through the heads (Medusa: B or B*N; Hydra: B)
@@ -48,7 +48,7 @@ class MedusaStep:
         self.kmax = max(cfg.k_per_head)
         i32 = dict(dtype=torch.int32, device=self.dev)
         B, N, K = cfg.B, self.N, cfg.K
-        if cfg.kind == L.MD_HEADS_MEDUSA:
+        if cfg.kind != L.MD_HEADS_HYDRA:
             self.topk_idx = torch.empty(cfg.M, K, self.kmax, **i32)
             self.topk_val = torch.empty(cfg.M, K, self.kmax, dtype=torch.float32, device=self.dev)
         else:
@@ -96,7 +96,7 @@ class MedusaStep:
     def run(self, w: Dict[str, torch.Tensor], x: Dict[str, torch.Tensor]) -> None:
         """w: W, b, U (and E for Hydra); x: h, q, Kc, Vc, lens, root_tok, src_row, logits."""
         c = self.cfg
-        if c.kind == L.MD_HEADS_MEDUSA:
+        if c.kind != L.MD_HEADS_HYDRA:
             self.heads(x["h"], w["W"], w["b"], w["U"])
             self.build(x["src_row"], x["root_tok"], x["lens"])
         else:

@@ -142,6 +142,8 @@ def heads_medusa(W, b, U, h, topk: Sequence[int], rows: Optional[Sequence[int]] 
                  want_logits: bool = False) -> Dict[str, np.ndarray]:
     """All K Medusa heads on hidden-state rows h [M, d].
 
+    U is [K, V, d], or [V, d] for one projection shared by every head ("Medusa
+    heads versus separate draft model", What interviewers probe next).
     Returns hres [K, R, d], idx [R, K, kmax] (-1 padded), val [R, K, kmax]
     (-inf padded), margin [R, K], for the R selected rows (all by default),
     and with want_logits the full logits [R, K, V].
@@ -156,10 +158,10 @@ def heads_medusa(W, b, U, h, topk: Sequence[int], rows: Optional[Sequence[int]] 
     idx = np.full((R, K, kmax), -1, dtype=np.int32)
     val = np.full((R, K, kmax), -np.inf, dtype=np.float64)
     margin = np.empty((R, K), dtype=np.float64)
-    logits = np.empty((R, K, U.shape[1]), dtype=np.float64) if want_logits else None
+    logits = np.empty((R, K, U.shape[-2]), dtype=np.float64) if want_logits else None
     for k in range(K):
         hres[k] = residual(W[k], b[k], hd, hd)
-        i_, v_, m_, lg = vocab_topk(U[k], hres[k], topk[k], want_logits=want_logits)
+        i_, v_, m_, lg = vocab_topk(U if U.ndim == 2 else U[k], hres[k], topk[k], want_logits=want_logits)
         idx[:, k, : topk[k]] = i_
         val[:, k, : topk[k]] = v_
         margin[:, k] = m_

@@ -47,6 +47,7 @@ class Workload:
     rows_per_request: int = 1  # 1: heads on the last hidden state; N: on every tree node
     bias_zero: bool = False
     chain: bool = False
+    shared_u: bool = False  # one vocabulary projection U [V, d] for every head
 
     @property
     def kmax(self) -> int:
@@ -93,16 +94,19 @@ LLAMA70B_B8 = Workload("70B-shaped bf16 heads, batch 8 over all 512 tree nodes: 
                        "GQA 64/8 hd128, L~U[1024,4096]", "medusa",
                        B=8, d=8192, V=128256, K=4, dtype="bf16", topk=(10, 4, 2, 1), N=64,
                        Hq=64, Hkv=8, hd=128, L_range=(1024, 4096), rows_per_request=64)
+LLAMA70B_SHARED = replace(LLAMA70B, name="70B-shaped bf16 heads sharing one vocabulary projection, batch 1: "
+                          "d=8192 V=128256 K=4, 64-node tree, GQA 64/8 hd128, L=4096", shared_u=True)
 HYDRA_B4 = Workload("Hydra bf16, batch 4: d=4096 V=128256 K=4 sequential heads, GQA 32/8 hd128, L=8192",
                     "hydra", B=4, d=4096, V=128256, K=4, dtype="bf16", topk=(10, 4, 2, 1), N=64,
                     Hq=32, Hkv=8, hd=128, L=8192, a=(0.85, 0.75, 0.65, 0.55))
 
 ALL = {"tiny": TINY_F32, "8b": LLAMA8B, "70b": LLAMA70B, "70b_chain": LLAMA70B_CHAIN,
-       "70b_b8": LLAMA70B_B8, "hydra_b4": HYDRA_B4}
+       "70b_b8": LLAMA70B_B8, "hydra_b4": HYDRA_B4, "70b_shared": LLAMA70B_SHARED}
 
 
 def weights(wl: Workload, seed: int, heads: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
-    """W [K,d,din], b [K,d], U [K,V,d] (and E [V,d] for Hydra), all ~N(0, 1/d)."""
+    """W [K,d,din], b [K,d], U [K,V,d] ([V,d] when shared; it then equals head 0's U of the
+    unshared workload) and E [V,d] for Hydra, all ~N(0, 1/d)."""
     std = 1.0 / np.sqrt(wl.d)
     out: Dict[str, np.ndarray] = {}
     out["W"] = normal(seed, stream(S_W), (wl.K, wl.d, wl.din), std, wl.dtype)
@@ -110,7 +114,7 @@ def weights(wl: Workload, seed: int, heads: Optional[Sequence[int]] = None) -> D
         out["b"] = np.zeros((wl.K, wl.d), dtype=np.float32 if wl.dtype == "f32" else np.uint16)
     else:
         out["b"] = normal(seed, stream(S_B), (wl.K, wl.d), std, wl.dtype)
-    out["U"] = normal(seed, stream(S_U), (wl.K, wl.V, wl.d), std, wl.dtype)
+    out["U"] = normal(seed, stream(S_U), ((wl.V, wl.d) if wl.shared_u else (wl.K, wl.V, wl.d)), std, wl.dtype)
     if wl.kind == "hydra":
         out["E"] = normal(seed, stream(S_E), (wl.V, wl.d), std, wl.dtype)
     return out

@@ -35,7 +35,12 @@ def test_weight_bytes_match_page():
     assert md.md_heads_weight_bytes(0, 1, 8192, 128256, 4) == 8_942_321_664
     assert md.md_heads_weight_bytes(0, 0, 8192, 128256, 1) == 4 * 1_117_790_208
     assert md.md_heads_weight_bytes(1, 1, 4096, 128256, 1) == 2 * (2 * 4096 * 4096 + 4096 + 4096 * 128256)
-    assert md.md_heads_weight_bytes(2, 1, 8192, 128256, 4) == -1
+    # one shared projection: 4 x 67.1M residual parameters + 1,050.7M once = 1.32B
+    # ("What interviewers probe next": sharing saves 3.15B of the 4.47B)
+    shared = md.md_heads_weight_bytes(md.MD_HEADS_MEDUSA_SHARED, 1, 8192, 128256, 4)
+    assert shared == 2 * (4 * (8192 * 8192 + 8192) + 128256 * 8192)
+    assert round((8_942_321_664 - shared) / 2 / 1e9, 2) == 3.15
+    assert md.md_heads_weight_bytes(3, 1, 8192, 128256, 4) == -1
 
 
 def _tree(parent, rank, n=None):
@@ -84,6 +89,7 @@ def test_heads_argument_errors():
                                    ws_bytes, None)
 
     assert call(kind=3) == L.MD_EINVAL
+    assert call(kind=2, level=1) == L.MD_EINVAL  # a shared projection is Medusa: level 0
     assert call(dt=7) == L.MD_EINVAL
     assert call(K=9) == L.MD_EINVAL
     assert call(kph=None) == L.MD_EINVAL

@@ -14,7 +14,7 @@ import pytest
 import oracle
 import synth
 from synth.topology import product_order_tree
-from synth.workloads import HYDRA_B4, LLAMA8B, LLAMA70B, TINY_F32, Workload, step_inputs, weights
+from synth.workloads import HYDRA_B4, LLAMA8B, LLAMA70B, LLAMA70B_SHARED, TINY_F32, Workload, step_inputs, weights
 
 from _helpers import TAU, TOL, check_topk, from_dev, rel_err, to_dev
 
@@ -32,13 +32,14 @@ def gpu_heads_medusa(wl: Workload, wd, h_dev, M):
 
     md = _md()
     K, kmax = wl.K, wl.kmax
+    kind = md.MD_HEADS_MEDUSA_SHARED if wl.shared_u else md.MD_HEADS_MEDUSA
     dt = md.MD_F32 if wl.dtype == "f32" else md.MD_BF16
     idx = torch.empty(M, K, kmax, dtype=torch.int32, device="cuda")
     val = torch.empty(M, K, kmax, dtype=torch.float32, device="cuda")
     hres = torch.empty(K, M, wl.d, dtype=torch.float32, device="cuda")
-    ws = torch.empty(md.md_heads_workspace_bytes(0, dt, M, wl.d, wl.V, K, kmax), dtype=torch.uint8, device="cuda")
-    md.md_medusa_heads(0, dt, M, wl.d, wl.V, K, wl.topk, 0, None, h_dev, wd["W"], wd["b"], wd["U"], None, None, None,
-                       idx, val, hres, ws)
+    ws = torch.empty(md.md_heads_workspace_bytes(kind, dt, M, wl.d, wl.V, K, kmax), dtype=torch.uint8, device="cuda")
+    md.md_medusa_heads(kind, dt, M, wl.d, wl.V, K, wl.topk, 0, None, h_dev, wd["W"], wd["b"], wd["U"], None, None,
+                       None, idx, val, hres, ws)
     torch.cuda.synchronize()
     return from_dev(idx), from_dev(val), from_dev(hres)
 
@@ -195,5 +196,49 @@ def test_heads_medusa_mfma_full_size_sampled(wl_name, M, rows):
     gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), M)
     ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, rows=rows, want_logits=True)
     ref["hres"] = ref["hres"]
+    compare_medusa(wl, gi[rows], gv[rows], gh[:, rows], ref, label="%s M=%d rows %s" % (wl.name, M, rows))
+    del wd
+
+
+# ------------------------------------------- one projection shared by the heads
+
+@pytest.mark.parametrize("wl,M", [(replace(TINY_F32, shared_u=True), 1), (replace(TINY_F32, shared_u=True), 3),
+                                  (replace(SMALL_BF16, shared_u=True), 1), (replace(SMALL_BF16, shared_u=True), 2),
+                                  (replace(MFMA_BF16, shared_u=True), 8),
+                                  (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9), shared_u=True), 37)])
+def test_heads_shared_projection(wl, M):
+    """One U [V, d] for every head: the K x M vectors h' share the pass over U (GEMV rows and MFMA
+    columns of several heads, each with its own top-k width)."""
+    seed = 3000 + M
+    w = weights(wl, seed)
+    assert w["U"].ndim == 2
+    h = synth.normal(seed, 80, (M, wl.d), 1.0, wl.dtype)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), M)
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, want_logits=True)
+    compare_medusa(wl, gi, gv, gh, ref, label="shared %s M=%d" % (wl.name, M))
+
+
+def test_heads_shared_projection_full_size():
+    """The 70B-shaped heads with one 2.1 GB projection, batch 1 (the whole vocabulary checked)."""
+    wl = LLAMA70B_SHARED
+    w = weights(wl, 71)
+    h = step_inputs(wl, 71)["h"]
+    wd = {k: to_dev(v) for k, v in w.items()}
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), 1)
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, want_logits=True)
+    compare_medusa(wl, gi, gv, gh, ref, label=wl.name)
+    del wd
+
+
+def test_heads_shared_projection_many_rows_sampled():
+    """512 rows x 4 heads through one projection on the matrix cores (sampled rows)."""
+    wl = LLAMA70B_SHARED
+    M, rows = 512, [0, 257, 511]
+    w = weights(wl, 72)
+    h = synth.normal(92, 79, (M, wl.d), 1.0, wl.dtype)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), M)
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, rows=rows, want_logits=True)
     compare_medusa(wl, gi[rows], gv[rows], gh[:, rows], ref, label="%s M=%d rows %s" % (wl.name, M, rows))
     del wd

@@ -24,7 +24,8 @@ def make_step(wl):
     import medusa_draft_heads_amd as md
 
     topo = wl.topology()
-    cfg = md.StepConfig(kind=md.MD_HEADS_MEDUSA if wl.kind == "medusa" else md.MD_HEADS_HYDRA,
+    kind = md.MD_HEADS_HYDRA if wl.kind == "hydra" else (md.MD_HEADS_MEDUSA_SHARED if wl.shared_u else md.MD_HEADS_MEDUSA)
+    cfg = md.StepConfig(kind=kind,
                         dtype=torch.float32 if wl.dtype == "f32" else torch.bfloat16, B=wl.B,
                         M=wl.M if wl.kind == "medusa" else wl.B, d=wl.d, V=wl.V, K=wl.K, k_per_head=wl.topk,
                         parent=topo.parent, rank=topo.rank, Hq=wl.Hq, Hkv=wl.Hkv, hd=wl.hd, Lcap=wl.Lcap,
@@ -94,6 +95,18 @@ def test_step_tiny_many_steps():
     step, topo = make_step(wl)
     lens = [int(run_and_compare(wl, w, wd, step, topo, seed, s)[0]) for s in range(24)]
     print("tiny accepted lengths:", lens, "mean", np.mean(lens))
+
+
+def test_step_tiny_shared_projection():
+    from dataclasses import replace
+
+    wl = replace(TINY_F32, shared_u=True)
+    seed = 4
+    w = weights(wl, seed)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    step, topo = make_step(wl)
+    lens = [int(run_and_compare(wl, w, wd, step, topo, seed, s)[0]) for s in range(6)]
+    print("tiny shared-projection accepted lengths:", lens)
 
 
 def test_step_70b_shaped():

@@ -164,6 +164,27 @@ def test_topk_matches_library_sort_bf16():
         assert np.allclose(val[m], logits[m][ref], rtol=0, atol=1e-12)
 
 
+def test_shared_projection_with_zero_residual_is_one_library_sort():
+    # one U for every head ("What interviewers probe next"); with W = 0 and
+    # b = 0 every head's h' is h, so head k's list is the first k_k entries of
+    # a single library sort of U h, and h' equals h exactly
+    d, V, K = 64, 2000, 3
+    topk = (7, 3, 1)
+    W = np.zeros((K, d, d), np.uint16)
+    b = np.zeros((K, d), np.uint16)
+    U = _rand_bf16(21, (V, d), 1 / math.sqrt(d))
+    h = _rand_bf16(22, (4, d), 1.0)
+    out = oracle.heads_medusa(W, b, U, h, topk)
+    hf = synth.bf16_to_f32(h).astype(np.float64)
+    logits = hf @ synth.bf16_to_f32(U).astype(np.float64).T
+    for k in range(K):
+        assert np.array_equal(out["hres"][k], hf)
+        for m in range(4):
+            ref = np.argsort(-logits[m], kind="stable")[: topk[k]]
+            assert np.array_equal(out["idx"][m, k, : topk[k]], ref)
+            assert np.all(out["idx"][m, k, topk[k]:] == -1)
+
+
 def test_hydra_level1_with_zero_embedding_half_is_medusa():
     # Hydra's input is [h ; E[token]]; with the E half of W zeroed, level 1
     # computes exactly a Medusa head with the h half of W
