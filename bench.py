@@ -8,8 +8,10 @@ batch 1 (d = 8,192, V = 128,256, 4 heads in bf16 = 8.94 GB of weights, top-k
 (10, 4, 2, 1), 64-node tree, GQA 64/8 heads of 128, 4,096 cached positions).
 Other workloads (--workload) are secondary measurements: the batch-8 step
 whose heads run over all 512 tree nodes on the matrix cores, the Hydra step
-(four sequential head levels), the 8B-shaped step, the top-1 chain, and the
-70B-shaped step with one vocabulary projection shared by the four heads.
+(four sequential head levels), the 8B-shaped step, the top-1 chain, the
+70B-shaped step with one vocabulary projection shared by the four heads, and
+the 70B-shaped step verified from the target's hidden states through its LM
+head with a fused argmax (no logits in memory).
 
 Prints one JSON line: steps/s, the roofline of the dominant kernel (the
 vocabulary projection + top-k, timed live with HIP events that the library
@@ -50,7 +52,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="70b",
-                    choices=["70b", "70b_chain", "8b", "tiny", "70b_b8", "hydra_b4", "70b_shared"])
+                    choices=["70b", "70b_chain", "8b", "tiny", "70b_b8", "hydra_b4", "70b_shared", "70b_lmhead"])
     ap.add_argument("--sets", type=int, default=8, help="input sets rotated to keep them out of the 256 MB MALL")
     ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps timed for the CPU baseline (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -65,7 +67,7 @@ def main() -> int:
 
     import medusa_draft_heads_amd as md
     import oracle
-    from synth.workloads import ALL, plant, step_inputs, weights
+    from synth.workloads import ALL, plant, plant_hidden, step_inputs, weights
 
     wl = ALL[args.workload]
     hydra = wl.kind == "hydra"
@@ -112,11 +114,17 @@ def main() -> int:
             if wl.M != len(rows):
                 sample_note = " (heads timed on the %d rows that build the trees, scaled to all %d rows)" % (
                     len(rows), wl.M)
-        logits = plant(x["logits"], topo, tok, wl.a, seed=args.seed, step=s)
+        if wl.target_head:  # verification through the target's LM head: plant its hidden states
+            plant_hidden(x["Ht"], w["Wt"], topo, tok, wl.a, seed=args.seed, step=s)
+        else:
+            logits = plant(x["logits"], topo, tok, wl.a, seed=args.seed, step=s)
         if s < args.cpu_steps:
             tc = time.perf_counter()
             oracle.tree_attention(topo.parent, x["q"], x["Kc"], x["Vc"], x["lens"])
-            tstar = oracle.argmax(logits)
+            if wl.target_head:
+                tstar = oracle.target_argmax(x["Ht"].reshape(wl.B * topo.n, wl.d), w["Wt"])[0].reshape(wl.B, topo.n)
+            else:
+                tstar = oracle.argmax(logits)
             r = oracle.accept(topo.parent, wl.K, tok, tstar, x["lens"])
             oracle.compact(x["Kc"], x["Vc"], x["lens"], r["accept_len"], r["path"], wl.K)
             td = time.perf_counter()
@@ -124,7 +132,8 @@ def main() -> int:
             acc_oracle.append([int(v) for v in r["accept_len"]])
             log("oracle step %d: %.2f s (accept_len %s)" % (s, cpu_times[-1], acc_oracle[-1]))
         xd = {k: to_dev(v) for k, v in x.items() if k != "logits"}
-        xd["logits"] = to_dev(logits)
+        if not wl.target_head:
+            xd["logits"] = to_dev(logits)
         xd["lens0"] = xd["lens"].clone()
         sets.append(xd)
     torch.cuda.synchronize()
@@ -134,19 +143,22 @@ def main() -> int:
     cfg = md.StepConfig(kind=kind,
                         dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, B=wl.B,
                         M=wl.B if hydra else wl.M, d=wl.d, V=wl.V, K=wl.K, k_per_head=wl.topk, parent=topo.parent,
-                        rank=topo.rank, Hq=wl.Hq, Hkv=wl.Hkv, hd=wl.hd, Lcap=wl.Lcap, max_len=wl.L_max)
+                        rank=topo.rank, Hq=wl.Hq, Hkv=wl.Hkv, hd=wl.hd, Lcap=wl.Lcap, max_len=wl.L_max,
+                        target_head=wl.target_head)
     step = md.MedusaStep(cfg)
     stream = torch.cuda.current_stream()
     calls = depth if hydra else 1  # heads calls per step, each with its own event pair
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
           for _ in range(args.steps)]
-    for pairs in ev:  # materialise the underlying hipEvent_t handles
+    lm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)] if wl.target_head else None
+    for pairs in ev + ([lm_ev] if lm_ev else []):  # materialise the underlying hipEvent_t handles
         for a, b in pairs:
             a.record(stream)
             b.record(stream)
     torch.cuda.synchronize()
 
-    def one_step(i: int, pairs=None):
+    def one_step(i: int, pairs=None, lm=None):
         xd = sets[i % len(sets)]
         xd["lens"].copy_(xd["lens0"])  # every step starts from the same cached lengths
         for lvl in range(calls):
@@ -162,7 +174,15 @@ def main() -> int:
         if not hydra:
             step.build(xd["src_row"], xd["root_tok"], xd["lens"])
         step.attention(xd["q"], xd["Kc"], xd["Vc"], xd["lens"])
-        step.accept(xd["logits"], xd["Kc"], xd["Vc"], xd["lens"])
+        if wl.target_head:
+            if lm is not None:
+                lm[0].record(stream)
+            step.verify(xd["Ht"], wd["Wt"])
+            if lm is not None:
+                lm[1].record(stream)
+            step.accept_tokens(xd["Kc"], xd["Vc"], xd["lens"])
+        else:
+            step.accept(xd["logits"], xd["Kc"], xd["Vc"], xd["lens"])
 
     for i in range(args.warmup):
         one_step(i)
@@ -170,7 +190,7 @@ def main() -> int:
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(args.steps):
-        one_step(args.warmup + i, ev[i])
+        one_step(args.warmup + i, ev[i], lm_ev[i] if lm_ev else None)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
@@ -235,10 +255,19 @@ def main() -> int:
                                                         else "")),
                     "kernel_ms": round(vocab_ms, 4), "bytes_per_launch": vocab_bytes,
                     "stream_read_GBps": round(stream_gbs, 1), "frac_of_stream_read": round(achieved / stream_gbs, 4)}
+    # verification input: the logits, or the hidden states plus the LM head through the fused argmax
+    verify_bytes = (wl.V * wl.d * esz + wl.B * wl.N * wl.d * esz) if wl.target_head else wl.B * wl.N * wl.V * 4
     step_bytes = (md.md_heads_weight_bytes(kind, 1 if esz == 2 else 0, wl.d, wl.V, wl.K)
                   + 2 * wl.B * wl.Hkv * (wl.L_max + wl.N) * wl.hd * esz  # K and V of prefix + tree (upper bound)
                   + 2 * wl.B * wl.N * wl.Hq * wl.hd * esz  # q in, attention out
-                  + wl.B * wl.N * wl.V * 4)  # verification logits
+                  + verify_bytes)
+    lm_head = None
+    if lm_ev:
+        lm_ms = sum(a.elapsed_time(b) for a, b in lm_ev) / args.steps
+        lm_gbs = verify_bytes / (lm_ms * 1e-3) / 1e9
+        lm_head = {"kernels": "target LM head + fused argmax (md_target_argmax)", "ms": round(lm_ms, 4),
+                   "bytes": verify_bytes, "GBps": round(lm_gbs, 1), "frac": round(lm_gbs / PEAK_HBM_GBS, 4),
+                   "flops": 2.0 * wl.B * wl.N * wl.V * wl.d}
     cpu = None
     if cpu_times:
         cpu = {"value": round(1.0 / float(np.median(cpu_times)), 4), "unit": "steps/s", "cores": threads,
@@ -273,6 +302,8 @@ def main() -> int:
         "acceptance": {"last_step_accept_len": acc_len, "oracle_accept_len": acc_oracle, "E_closed_form": round(E, 4)},
         "cpu_baseline": cpu,
     }
+    if lm_head:
+        out["lm_head"] = lm_head
     print(json.dumps(out), flush=True)
     return 0
 

@@ -187,6 +187,30 @@ int md_tree_accept(const md_tree* tree, int dt, int B, int K, int V, int Hkv, in
                    int32_t* accept_len, int32_t* path, int32_t* next_tok, int32_t* compact_src, void* ws,
                    size_t ws_bytes, void* stream);
 
+/* Workspace for md_target_argmax at these sizes. */
+size_t md_target_argmax_workspace_bytes(int dt, int R, int d, int V);
+
+/* The target's greedy choice at every tree node from its final hidden
+ * states: the last step of the one verification pass ("Trees"), the target's
+ * LM head, with the argmax fused so the R x V logits never reach memory.
+ *     tok[r] = the first index of the maximum over v of Wt[v] . H[r]
+ *     val[r] = that maximum
+ * H [R][d] (device, dt; for a step R = B * N rows in (request, node) order),
+ * Wt [V][d] (device, dt), tok [R] (device int32), val [R] (device float32,
+ * or NULL). Products of the stored values are exact and summed in float32.
+ * ws (device) must hold md_target_argmax_workspace_bytes(...). Requires
+ * d % 8 == 0 and d * 4 bytes <= 160 KB. Errors: MD_EINVAL (negative sizes,
+ * NULL pointers, unknown dt), MD_EUNSUPPORTED (d), MD_EWORKSPACE. */
+int md_target_argmax(int dt, int R, int d, int V, const void* H, const void* Wt, int32_t* tok, float* val, void* ws,
+                     size_t ws_bytes, void* stream);
+
+/* md_tree_accept with the target's choices given instead of its logits:
+ * target_tok [B][N] (device int32; t*(b, n), e.g. from md_target_argmax).
+ * Same outputs, cache update and errors; no workspace. */
+int md_tree_accept_tokens(const md_tree* tree, int dt, int B, int K, int Hkv, int hd, int Lcap,
+                          const int32_t* target_tok, const int32_t* tree_tok, void* Kc, void* Vc, int32_t* lens,
+                          int32_t* accept_len, int32_t* path, int32_t* next_tok, int32_t* compact_src, void* stream);
+
 /* Timing hook for profiling: when both are non-NULL hipEvent_t handles, every
  * later md_medusa_heads call on this thread records `start` on its stream
  * right before its vocabulary-projection kernel and `stop` right after it.

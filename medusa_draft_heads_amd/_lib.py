@@ -23,6 +23,7 @@ EXPORTS = (
     "md_tree_validate", "md_heads_weight_bytes", "md_heads_workspace_bytes", "md_medusa_heads", "md_tree_build",
     "md_attention_workspace_bytes", "md_tree_attention", "md_accept_workspace_bytes", "md_tree_accept",
     "md_set_vocab_timing_events", "md_last_error", "md_hbm_read_probe", "md_hbm_read_probe_blocks",
+    "md_target_argmax_workspace_bytes", "md_target_argmax", "md_tree_accept_tokens",
 )
 
 
@@ -70,6 +71,9 @@ def lib() -> ctypes.CDLL:
             "md_last_error": ([], ctypes.c_char_p),
             "md_hbm_read_probe": ([vp, sz, vp, vp], i),
             "md_hbm_read_probe_blocks": ([], i),
+            "md_target_argmax_workspace_bytes": ([i, i, i, i], sz),
+            "md_target_argmax": ([i, i, i, i] + [vp] * 5 + [sz, vp], i),
+            "md_tree_accept_tokens": ([tp, i, i, i, i, i, i] + [vp] * 10, i),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -170,6 +174,24 @@ def md_tree_accept(tree, dt, B, K, V, Hkv, hd, Lcap, logits, tree_tok, Kc, Vc, l
     rc = lib().md_tree_accept(ctypes.byref(tree), dt, B, K, V, Hkv, hd, Lcap, _p(logits), _p(tree_tok), _p(Kc),
                               _p(Vc), _p(lens), _p(accept_len), _p(path), _p(next_tok), _p(compact_src), _p(ws),
                               ws_bytes, _stream(stream))
+    _check(rc)
+
+
+def md_target_argmax_workspace_bytes(dt, R, d, V) -> int:
+    return int(lib().md_target_argmax_workspace_bytes(dt, R, d, V))
+
+
+def md_target_argmax(dt, R, d, V, H, Wt, tok, val, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().md_target_argmax(dt, R, d, V, _p(H), _p(Wt), _p(tok), _p(val), _p(ws), ws_bytes, _stream(stream)))
+
+
+def md_tree_accept_tokens(tree, dt, B, K, Hkv, hd, Lcap, target_tok, tree_tok, Kc, Vc, lens, accept_len, path,
+                          next_tok, compact_src, stream=None) -> None:
+    rc = lib().md_tree_accept_tokens(ctypes.byref(tree), dt, B, K, Hkv, hd, Lcap, _p(target_tok), _p(tree_tok), _p(Kc),
+                                     _p(Vc), _p(lens), _p(accept_len), _p(path), _p(next_tok), _p(compact_src),
+                                     _stream(stream))
     _check(rc)
 
 

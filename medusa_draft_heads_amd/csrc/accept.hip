@@ -91,9 +91,12 @@ __global__ __launch_bounds__(BLOCK) void k_argmax_part(const float* __restrict__
     }
 }
 
+// The target's choice per node comes from the argmax parts (chunks per row),
+// or ready-made from target_tok [B][N] when that is given.
 template <typename T>
 __global__ __launch_bounds__(BLOCK) void k_accept(DevTree t, int K, int Hkv, int hd, int Lcap, int chunks,
                                                   const float* __restrict__ part_v, const int* __restrict__ part_i,
+                                                  const int32_t* __restrict__ target_tok,
                                                   const int32_t* __restrict__ tree_tok, T* __restrict__ Kc,
                                                   T* __restrict__ Vc, int32_t* __restrict__ lens,
                                                   int32_t* __restrict__ accept_len, int32_t* __restrict__ path,
@@ -110,7 +113,9 @@ __global__ __launch_bounds__(BLOCK) void k_accept(DevTree t, int K, int Hkv, int
         // the target's choice at this lane's node
         float bv = -INFINITY;
         int bi = INT_MAX;
-        if (lane < N) {
+        if (target_tok) {
+            if (lane < N) bi = target_tok[(int64_t)b * N + lane];
+        } else if (lane < N) {
             const int64_t r = ((int64_t)b * N + lane) * chunks;
             for (int c0 = 0; c0 < chunks; c0 += 8) {
                 float v[8];
@@ -262,11 +267,28 @@ hipError_t accept_launch(const DevTree& t, int dt, int B, int K, int V, int Hkv,
     const size_t lds = per_head > (size_t)kCompactLds ? per_head : (size_t)kCompactLds;
     if (dt == 0)
         hipLaunchKernelGGL(k_accept<float>, dim3(B), dim3(BLOCK), lds, s, t, K, Hkv, hd, Lcap, chunks, pv, pi,
-                           tree_tok, reinterpret_cast<float*>(Kc), reinterpret_cast<float*>(Vc), lens, accept_len,
-                           path, next_tok, compact_src);
+                           nullptr, tree_tok, reinterpret_cast<float*>(Kc), reinterpret_cast<float*>(Vc), lens,
+                           accept_len, path, next_tok, compact_src);
     else
         hipLaunchKernelGGL(k_accept<uint16_t>, dim3(B), dim3(BLOCK), lds, s, t, K, Hkv, hd, Lcap, chunks, pv, pi,
-                           tree_tok, reinterpret_cast<uint16_t*>(Kc), reinterpret_cast<uint16_t*>(Vc), lens,
+                           nullptr, tree_tok, reinterpret_cast<uint16_t*>(Kc), reinterpret_cast<uint16_t*>(Vc), lens,
                            accept_len, path, next_tok, compact_src);
+    return hipGetLastError();
+}
+
+hipError_t accept_tokens_launch(const DevTree& t, int dt, int B, int K, int Hkv, int hd, int Lcap,
+                                const int32_t* target_tok, const int32_t* tree_tok, void* Kc, void* Vc,
+                                int32_t* lens, int32_t* accept_len, int32_t* path, int32_t* next_tok,
+                                int32_t* compact_src, hipStream_t s) {
+    const size_t per_head = (size_t)2 * (K + 1) * hd * (dt == 0 ? 4 : 2);
+    const size_t lds = per_head > (size_t)kCompactLds ? per_head : (size_t)kCompactLds;
+    if (dt == 0)
+        hipLaunchKernelGGL(k_accept<float>, dim3(B), dim3(BLOCK), lds, s, t, K, Hkv, hd, Lcap, 0, nullptr, nullptr,
+                           target_tok, tree_tok, reinterpret_cast<float*>(Kc), reinterpret_cast<float*>(Vc), lens,
+                           accept_len, path, next_tok, compact_src);
+    else
+        hipLaunchKernelGGL(k_accept<uint16_t>, dim3(B), dim3(BLOCK), lds, s, t, K, Hkv, hd, Lcap, 0, nullptr, nullptr,
+                           target_tok, tree_tok, reinterpret_cast<uint16_t*>(Kc), reinterpret_cast<uint16_t*>(Vc),
+                           lens, accept_len, path, next_tok, compact_src);
     return hipGetLastError();
 }

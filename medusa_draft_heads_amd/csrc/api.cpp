@@ -278,6 +278,42 @@ int md_tree_accept(const md_tree* tree, int dt, int B, int K, int V, int Hkv, in
                       "md_tree_accept");
 }
 
+size_t md_target_argmax_workspace_bytes(int dt, int R, int d, int V) {
+    if ((dt != MD_F32 && dt != MD_BF16) || R <= 0 || d <= 0 || V <= 0) return 0;
+    return target_argmax_ws_bound(dt, R, d, V);
+}
+
+int md_target_argmax(int dt, int R, int d, int V, const void* H, const void* Wt, int32_t* tok, float* val, void* ws,
+                     size_t ws_bytes, void* stream) {
+    if (check_dt(dt)) return MD_EINVAL;
+    if (R < 0 || V < 1) return fail(MD_EINVAL, "R = %d, V = %d", R, V);
+    if (d < 8 || d % 8) return fail(MD_EUNSUPPORTED, "d = %d (a positive multiple of 8 is required)", d);
+    if ((size_t)d * 4 > 160 * 1024) return fail(MD_EUNSUPPORTED, "width %d exceeds one LDS row buffer", d);
+    if (R == 0) return MD_OK;
+    if (!H || !Wt || !tok || !ws) return fail(MD_EINVAL, "a required pointer is NULL");
+    const size_t need = target_argmax_ws_bound(dt, R, d, V);
+    if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return hip_status(target_argmax_launch(dt, R, d, V, H, Wt, tok, val, ws, (hipStream_t)stream), "md_target_argmax");
+}
+
+int md_tree_accept_tokens(const md_tree* tree, int dt, int B, int K, int Hkv, int hd, int Lcap,
+                          const int32_t* target_tok, const int32_t* tree_tok, void* Kc, void* Vc, int32_t* lens,
+                          int32_t* accept_len, int32_t* path, int32_t* next_tok, int32_t* compact_src, void* stream) {
+    DevTree t;
+    int rc = expand_tree(tree, K, nullptr, &t);
+    if (rc) return rc;
+    if (check_dt(dt)) return MD_EINVAL;
+    if (B < 0 || Hkv < 1 || hd < 1) return fail(MD_EINVAL, "B = %d, Hkv = %d, hd = %d", B, Hkv, hd);
+    if (hd > 256) return fail(MD_EUNSUPPORTED, "head_dim %d (at most 256)", hd);
+    if (Lcap < t.n) return fail(MD_ERANGE, "Lcap %d is smaller than the tree (%d nodes)", Lcap, t.n);
+    if (B == 0) return MD_OK;
+    if (!target_tok || !tree_tok || !Kc || !Vc || !lens || !accept_len || !path || !next_tok || !compact_src)
+        return fail(MD_EINVAL, "a required pointer is NULL");
+    return hip_status(accept_tokens_launch(t, dt, B, K, Hkv, hd, Lcap, target_tok, tree_tok, Kc, Vc, lens, accept_len,
+                                           path, next_tok, compact_src, (hipStream_t)stream),
+                      "md_tree_accept_tokens");
+}
+
 int md_hbm_read_probe_blocks(void) { return probe_blocks(); }
 
 int md_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

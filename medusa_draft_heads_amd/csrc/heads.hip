@@ -694,6 +694,86 @@ size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax, in
     return gemv > mfma ? gemv : mfma;
 }
 
+namespace {
+
+__global__ void k_widen_bf16(const uint16_t* __restrict__ x, float* __restrict__ y, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) y[i] = __uint_as_float((uint32_t)x[i] << 16);
+}
+
+// GEMV path of the target argmax: R rows of hidden states (float32 in LDS)
+// against the LM head, k = 1 per row, then the k-way merge.
+template <typename T>
+hipError_t target_argmax_gemv(int dt, int R, int d, int V, const void* H, const void* Wt, int32_t* tok, float* val,
+                              void* ws, hipStream_t s) {
+    const Plan p = make_plan(dt, R, d, d, 1, 0);
+    char* w = reinterpret_cast<char*>(ws);
+    const float* hf = reinterpret_cast<const float*>(H);
+    if (dt == 1) {
+        float* buf = reinterpret_cast<float*>(w);
+        w += align256((size_t)R * d * 4);
+        const int64_t n = (int64_t)R * d;
+        hipLaunchKernelGGL(k_widen_bf16, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                           reinterpret_cast<const uint16_t*>(H), buf, n);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hf = buf;
+    }
+    float* pv = reinterpret_cast<float*>(w);
+    w += align256((size_t)R * p.wg_per_head * 4);
+    int* pi = reinterpret_cast<int*>(w);
+    w += align256((size_t)R * p.wg_per_head * 4);
+    float* vs = reinterpret_cast<float*>(w);  // values when the caller wants none
+    KK kk;
+    for (int i = 0; i < 8; ++i) kk.v[i] = 1;
+    const T* U = reinterpret_cast<const T*>(Wt);
+    for (int m0 = 0; m0 < R; m0 += p.MRv) {
+        switch (p.MRv) {
+            case 4:
+                hipLaunchKernelGGL((k_vocab_topk<T, 4, vocab_waves(4)>), dim3(p.voc_grid), dim3(p.voc_nw * MD_WAVE),
+                                   p.voc_lds, s, U, hf, R, m0, d, V, 1, 0, p.wg_per_head, kk, 1, 0, pv, pi);
+                break;
+            case 2:
+                hipLaunchKernelGGL((k_vocab_topk<T, 2, vocab_waves(2)>), dim3(p.voc_grid), dim3(p.voc_nw * MD_WAVE),
+                                   p.voc_lds, s, U, hf, R, m0, d, V, 1, 0, p.wg_per_head, kk, 1, 0, pv, pi);
+                break;
+            default:
+                hipLaunchKernelGGL((k_vocab_topk<T, 1, vocab_waves(1)>), dim3(p.voc_grid), dim3(p.voc_nw * MD_WAVE),
+                                   p.voc_lds, s, U, hf, R, m0, d, V, 1, 0, p.wg_per_head, kk, 1, 0, pv, pi);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return launch_merge(pv, pi, R, 1, p.wg_per_head, kk, 1, tok, val ? val : vs, s);
+}
+
+}  // namespace
+
+size_t target_argmax_ws_bound(int dt, int R, int d, int V) {
+    const size_t vals = align256((size_t)R * 4);
+    const size_t mfma = argmax_mfma_applicable(dt, R, d) ? argmax_mfma_ws_bytes(R, V) + vals : 0;
+    const size_t lists_max = (size_t)device_cus() * 4;
+    const size_t gemv = (dt == 1 ? align256((size_t)R * d * 4) : 0) + 2 * align256((size_t)R * lists_max * 4) + vals;
+    return gemv > mfma ? gemv : mfma;
+}
+
+hipError_t target_argmax_launch(int dt, int R, int d, int V, const void* H, const void* Wt, int32_t* tok, float* val,
+                                void* ws, hipStream_t s) {
+    KK kk;
+    for (int i = 0; i < 8; ++i) kk.v[i] = 1;
+    if (argmax_mfma_applicable(dt, R, d)) {
+        float* pv;
+        int* pi;
+        int nlists;
+        hipError_t e = argmax_mfma_launch(R, d, V, H, Wt, ws, s, &pv, &pi, &nlists);
+        if (e != hipSuccess) return e;
+        float* vs = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + argmax_mfma_ws_bytes(R, V));
+        return launch_merge(pv, pi, R, 1, nlists, kk, 1, tok, val ? val : vs, s);
+    }
+    if (dt == 0) return target_argmax_gemv<float>(dt, R, d, V, H, Wt, tok, val, ws, s);
+    return target_argmax_gemv<uint16_t>(dt, R, d, V, H, Wt, tok, val, ws, s);
+}
+
 hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
     if (heads_mfma_applicable(a.dt, a.M, a.d, a.din)) {
         // many rows: the two contractions on the matrix cores, then the same k-way merge

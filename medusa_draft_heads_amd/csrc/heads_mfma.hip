@@ -278,6 +278,9 @@ __device__ __forceinline__ void dmab(__amdgpu_buffer_rsrc_t r, unsigned char* ds
 
 // With one projection shared by the heads (Mh > 0) there is a single U and
 // activation row m ([heads][Mh][d] read as [M][d]) belongs to head m / Mh.
+// NS = 2: the activations are h' = hi + lo (two products per term); NS = 1:
+// they are exact in bf16 (hlo unused), e.g. the target's own hidden states.
+template <int NS>
 __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restrict__ U,
                                                          const uint16_t* __restrict__ hhi,
                                                          const uint16_t* __restrict__ hlo, int M, int d, int V,
@@ -312,7 +315,8 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restr
 #pragma unroll
         for (int j = 0; j < NPB; ++j) {
             dmab(rH, base + A_BYTES + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
-            dmab(rL, base + A_BYTES + B_BYTES + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
+            if constexpr (NS == 2)
+                dmab(rL, base + A_BYTES + B_BYTES + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
         }
     };
 
@@ -331,7 +335,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restr
         for (int rb = 0; rb < 8; ++rb)
             a[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sA + (128 * wr + 16 * rb + c16) * ROWB + slot));
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
+        for (int s = 0; s < NS; ++s) {
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
                 const bf16x8 b = __builtin_bit_cast(
@@ -443,7 +447,47 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restr
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+__global__ void k_fill_bound(int* __restrict__ bound, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) bound[i] = f2o(-INFINITY);
+}
+
 }  // namespace
+
+bool argmax_mfma_applicable(int dt, int R, int d) { return dt == 1 && R >= 8 && d % (2 * VK) == 0; }
+
+size_t argmax_mfma_ws_bytes(int R, int V) {
+    const size_t vtiles = (size_t)(V + VR - 1) / VR;
+    return 2 * align256((size_t)R * 2 * vtiles * 4) + align256((size_t)R * 4);
+}
+
+// The target's choice per row: one bf16 product per term (hidden states and
+// LM head are exact in bf16), the same epilogue with k = 1; the caller merges
+// the lists (two per vocabulary tile).
+hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt, void* ws, hipStream_t s,
+                              float** part_val, int** part_idx, int* nlists) {
+    const int vtiles = (V + VR - 1) / VR, vmtiles = (R + VM - 1) / VM;
+    char* w = reinterpret_cast<char*>(ws);
+    float* pv = reinterpret_cast<float*>(w);
+    w += align256((size_t)R * 2 * vtiles * 4);
+    int* pi = reinterpret_cast<int*>(w);
+    w += align256((size_t)R * 2 * vtiles * 4);
+    int* bound = reinterpret_cast<int*>(w);
+    hipLaunchKernelGGL(k_fill_bound, dim3((R + 255) / 256), dim3(256), 0, s, bound, R);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    KW kk;
+    for (int i = 0; i < 8; ++i) kk.v[i] = 1;
+    const uint16_t* h = reinterpret_cast<const uint16_t*>(H);
+    hipLaunchKernelGGL(k_vocab_mfma<1>, dim3(8 * vmtiles * ((vtiles + 7) / 8)), dim3(BLOCK), 0, s,
+                       reinterpret_cast<const uint16_t*>(Wt), h, h, R, d, V, 1, 0, vtiles, vmtiles, 1, kk, 0, pv, pi,
+                       bound);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    *part_val = pv;
+    *part_idx = pi;
+    *nlists = 2 * vtiles;
+    return hipSuccess;
+}
 
 bool heads_mfma_applicable(int dt, int M, int d, int din) {
     // d % 128: whole residual tiles, and an even number of vocabulary stages
@@ -505,7 +549,7 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     const int rows_v = a.shared_u ? a.nh * a.M : a.M, nh_u = a.shared_u ? 1 : a.nh;
     const int vmtiles = (rows_v + VM - 1) / VM;
     const int units2 = nh_u * vtiles;
-    hipLaunchKernelGGL(k_vocab_mfma, dim3(8 * vmtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s,
+    hipLaunchKernelGGL(k_vocab_mfma<2>, dim3(8 * vmtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s,
                        reinterpret_cast<const uint16_t*>(a.U), hhi, hlo, rows_v, a.d, a.V, nh_u,
                        a.shared_u ? 0 : a.head0, vtiles, vmtiles, a.kmax, kk, a.shared_u ? a.M : 0, pv, pi, bound);
     if ((err = hipGetLastError()) != hipSuccess) return err;

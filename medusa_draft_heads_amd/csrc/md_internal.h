@@ -57,6 +57,15 @@ size_t heads_mfma_ws_bytes(int M, int d, int V, int nh, int kmax);
 hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                              float** part_val, int** part_idx, int* nlists);
 hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+bool argmax_mfma_applicable(int dt, int R, int d);
+size_t argmax_mfma_ws_bytes(int R, int V);
+hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt, void* ws, hipStream_t s,
+                              float** part_val, int** part_idx, int* nlists);
+
+// ---- the target's LM head with a fused argmax (heads.hip) ----
+size_t target_argmax_ws_bound(int dt, int R, int d, int V);
+hipError_t target_argmax_launch(int dt, int R, int d, int V, const void* H, const void* Wt, int32_t* tok, float* val,
+                                void* ws, hipStream_t s);
 
 // ---- tree build (tree.hip) ----
 hipError_t tree_build_launch(const DevTree& t, int kind, int B, int M, int K, int kmax, int level,
@@ -83,6 +92,10 @@ hipError_t accept_launch(const DevTree& t, int dt, int B, int K, int V, int Hkv,
                          const float* logits, const int32_t* tree_tok, void* Kc, void* Vc, int32_t* lens,
                          int32_t* accept_len, int32_t* path, int32_t* next_tok, int32_t* compact_src, void* ws,
                          hipStream_t s);
+hipError_t accept_tokens_launch(const DevTree& t, int dt, int B, int K, int Hkv, int hd, int Lcap,
+                                const int32_t* target_tok, const int32_t* tree_tok, void* Kc, void* Vc,
+                                int32_t* lens, int32_t* accept_len, int32_t* path, int32_t* next_tok,
+                                int32_t* compact_src, hipStream_t s);
 
 // ---- measurement utility (probe.hip) ----
 int probe_blocks();

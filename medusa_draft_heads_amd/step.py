@@ -3,7 +3,9 @@
 MedusaStep owns the outputs and workspaces of a fixed configuration and issues
 the four library calls in the order the step needs them: heads -> tree ->
 tree attention -> accept. Hydra runs its heads level by level, each level's
-tree tokens feeding the next level's embedding lookup. Buffers are allocated
+tree tokens feeding the next level's embedding lookup. With target_head the
+verification starts from the target's final hidden states: its LM head with
+a fused argmax gives the target's choice per node, then acceptance. Buffers are allocated
 once, so a step allocates nothing and issues no host synchronisation.
 """
 from __future__ import annotations
@@ -33,6 +35,7 @@ class StepConfig:
     hd: int
     Lcap: int
     max_len: int
+    target_head: bool = False  # verify from hidden states Ht [B, N, d] through the LM head Wt [V, d]
 
 
 class MedusaStep:
@@ -68,6 +71,11 @@ class MedusaStep:
         self.ws_attn = torch.empty(max(1, L.md_attention_workspace_bytes(self.dt, B, N, cfg.Hq, cfg.Hkv, cfg.hd,
                                                                           cfg.max_len)), **u8)
         self.ws_acc = torch.empty(max(1, L.md_accept_workspace_bytes(B, N, cfg.V)), **u8)
+        if cfg.target_head:
+            self.target_tok = torch.empty(B, N, **i32)
+            self.target_val = torch.empty(B, N, dtype=torch.float32, device=self.dev)
+            self.ws_target = torch.empty(max(1, L.md_target_argmax_workspace_bytes(self.dt, B * N, cfg.d, cfg.V)),
+                                         **u8)
         self.scale = 1.0 / float(cfg.hd) ** 0.5
         self.h_res = None
 
@@ -92,9 +100,20 @@ class MedusaStep:
         L.md_tree_accept(self.tree, self.dt, c.B, c.K, c.V, c.Hkv, c.hd, c.Lcap, logits, self.tree_tok, Kc, Vc, lens,
                          self.accept_len, self.path, self.next_tok, self.compact_src, self.ws_acc)
 
+    def verify(self, Ht, Wt) -> None:
+        """The target's choice at every node: LM head + fused argmax over Ht [B, N, d]."""
+        c = self.cfg
+        L.md_target_argmax(self.dt, c.B * self.N, c.d, c.V, Ht, Wt, self.target_tok, self.target_val, self.ws_target)
+
+    def accept_tokens(self, Kc, Vc, lens) -> None:
+        c = self.cfg
+        L.md_tree_accept_tokens(self.tree, self.dt, c.B, c.K, c.Hkv, c.hd, c.Lcap, self.target_tok, self.tree_tok, Kc,
+                                Vc, lens, self.accept_len, self.path, self.next_tok, self.compact_src)
+
     # -- a whole step -----------------------------------------------------------
     def run(self, w: Dict[str, torch.Tensor], x: Dict[str, torch.Tensor]) -> None:
-        """w: W, b, U (and E for Hydra); x: h, q, Kc, Vc, lens, root_tok, src_row, logits."""
+        """w: W, b, U (E for Hydra, Wt with target_head); x: h, q, Kc, Vc, lens, root_tok, src_row, and
+        logits (or Ht with target_head)."""
         c = self.cfg
         if c.kind != L.MD_HEADS_HYDRA:
             self.heads(x["h"], w["W"], w["b"], w["U"])
@@ -105,7 +124,11 @@ class MedusaStep:
                 self.heads(x["h"], w["W"], w["b"], w["U"], E=w["E"], root_tok=x["root_tok"], level=level)
                 self.build(None, x["root_tok"], x["lens"], level=level)
         self.attention(x["q"], x["Kc"], x["Vc"], x["lens"])
-        self.accept(x["logits"], x["Kc"], x["Vc"], x["lens"])
+        if c.target_head:
+            self.verify(x["Ht"], w["Wt"])
+            self.accept_tokens(x["Kc"], x["Vc"], x["lens"])
+        else:
+            self.accept(x["logits"], x["Kc"], x["Vc"], x["lens"])
 
     def _depths(self):
         dep = []

@@ -138,6 +138,16 @@ def vocab_topk(U_k: np.ndarray, hres: np.ndarray, k: int, want_logits: bool = Fa
     return idx, val, margin, logits
 
 
+def target_argmax(H, Wt):
+    """The target's greedy choice per row of its final hidden states H [R, d]
+    through its LM head Wt [V, d] ("Medusa heads versus separate draft model",
+    Trees: one verification pass over the tree): the first index of the
+    largest logit, with that logit and the gap to the runner-up (the top-1
+    list and its margin)."""
+    i_, v_, m_, _ = vocab_topk(Wt, to_double(H), 1)
+    return i_[:, 0], v_[:, 0], m_
+
+
 def heads_medusa(W, b, U, h, topk: Sequence[int], rows: Optional[Sequence[int]] = None,
                  want_logits: bool = False) -> Dict[str, np.ndarray]:
     """All K Medusa heads on hidden-state rows h [M, d].

@@ -7,7 +7,9 @@ drawn from its own Philox stream (see ``synth.c``); per-step tensors fold the
 step index into the stream so a bench can rotate independent input sets.
 
 Nothing here computes the decode step. ``plant`` builds verification logits
-with a prescribed per-depth acceptance from the tree tokens it is handed.
+with a prescribed per-depth acceptance from the tree tokens it is handed;
+``plant_hidden`` does the same in the target's hidden states when the
+verification runs through the target's LM head.
 """
 from __future__ import annotations
 
@@ -20,7 +22,7 @@ from . import normal, randint, uniform01
 from .topology import Topology, product_order_tree
 
 # stream ids (low byte); the step index is folded in above it
-S_H, S_W, S_B, S_U, S_E, S_Q, S_K, S_V, S_LOGITS, S_ROOT, S_LENS, S_PLANT, S_SRC = range(1, 14)
+S_H, S_W, S_B, S_U, S_E, S_Q, S_K, S_V, S_LOGITS, S_ROOT, S_LENS, S_PLANT, S_SRC, S_WT, S_HT, S_ALT = range(1, 17)
 
 
 def stream(sid: int, step: int = 0) -> int:
@@ -48,6 +50,7 @@ class Workload:
     bias_zero: bool = False
     chain: bool = False
     shared_u: bool = False  # one vocabulary projection U [V, d] for every head
+    target_head: bool = False  # verify from the target's hidden states Ht [B, N, d] through its LM head Wt [V, d]
 
     @property
     def kmax(self) -> int:
@@ -100,8 +103,12 @@ HYDRA_B4 = Workload("Hydra bf16, batch 4: d=4096 V=128256 K=4 sequential heads, 
                     "hydra", B=4, d=4096, V=128256, K=4, dtype="bf16", topk=(10, 4, 2, 1), N=64,
                     Hq=32, Hkv=8, hd=128, L=8192, a=(0.85, 0.75, 0.65, 0.55))
 
+LLAMA70B_LMHEAD = replace(LLAMA70B, name="70B-shaped bf16 heads, batch 1, verified through the target's LM head "
+                          "(128256 x 8192) with a fused argmax: d=8192 V=128256 K=4, 64-node tree, GQA 64/8 hd128, "
+                          "L=4096", target_head=True)
+
 ALL = {"tiny": TINY_F32, "8b": LLAMA8B, "70b": LLAMA70B, "70b_chain": LLAMA70B_CHAIN,
-       "70b_b8": LLAMA70B_B8, "hydra_b4": HYDRA_B4, "70b_shared": LLAMA70B_SHARED}
+       "70b_b8": LLAMA70B_B8, "hydra_b4": HYDRA_B4, "70b_shared": LLAMA70B_SHARED, "70b_lmhead": LLAMA70B_LMHEAD}
 
 
 def weights(wl: Workload, seed: int, heads: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
@@ -117,6 +124,8 @@ def weights(wl: Workload, seed: int, heads: Optional[Sequence[int]] = None) -> D
     out["U"] = normal(seed, stream(S_U), ((wl.V, wl.d) if wl.shared_u else (wl.K, wl.V, wl.d)), std, wl.dtype)
     if wl.kind == "hydra":
         out["E"] = normal(seed, stream(S_E), (wl.V, wl.d), std, wl.dtype)
+    if wl.target_head:
+        out["Wt"] = normal(seed, stream(S_WT), (wl.V, wl.d), std, wl.dtype)
     return out
 
 
@@ -137,7 +146,10 @@ def step_inputs(wl: Workload, seed: int, step: int = 0) -> Dict[str, np.ndarray]
     else:
         node = randint(seed, stream(S_SRC, step), wl.B, 0, wl.rows_per_request - 1)
         out["src_row"] = (np.arange(wl.B, dtype=np.int32) * wl.rows_per_request + node).astype(np.int32)
-    out["logits"] = normal(seed, stream(S_LOGITS, step), (wl.B, wl.N, wl.V), 1.0, "f32")
+    if wl.target_head:
+        out["Ht"] = normal(seed, stream(S_HT, step), (wl.B, wl.N, wl.d), 1.0, wl.dtype)
+    else:
+        out["logits"] = normal(seed, stream(S_LOGITS, step), (wl.B, wl.N, wl.V), 1.0, "f32")
     return out
 
 
@@ -179,3 +191,49 @@ def plant(logits: np.ndarray, topo: Topology, tree_tok: np.ndarray, a: Sequence[
                 row[toks] = np.minimum(row[toks], cap)
                 break
     return logits
+
+
+def plant_hidden(Ht: np.ndarray, Wt: np.ndarray, topo: Topology, tree_tok: np.ndarray, a: Sequence[float],
+                 seed: int, step: int = 0, alpha: float = 16.0) -> np.ndarray:
+    """The acceptance plant of `plant`, made in the target's hidden states.
+
+    Same draws and walk as `plant`. Where the walk accepts the child c of p,
+    row p of Ht gets alpha * Wt[token of c] added: that token's logit grows by
+    about alpha (|Wt[v]| ~ 1) while every other logit moves by ~alpha/sqrt(d),
+    so the target picks it. Where the walk stops, row p gets alpha * Wt[x] for
+    a drawn token x that no child of p carries. Ht and Wt are storage arrays
+    (float32 or bf16 bits), Ht [B, N, d] is changed in place; the result is
+    rounded back to the storage type, and both sides of a comparison read it.
+    """
+    from . import bf16_to_f32, f32_to_bf16
+
+    B, N, d = Ht.shape
+    V = Wt.shape[0]
+    bf = Ht.dtype == np.uint16
+    H = bf16_to_f32(Ht).astype(np.float64) if bf else Ht.astype(np.float64)
+    W = (lambda v: bf16_to_f32(Wt[v]).astype(np.float64)) if bf else (lambda v: Wt[v].astype(np.float64))
+    depth = [len(p) for p in topo.paths]
+    D = max(depth)
+    deepest = [i for i in range(N) if depth[i] == D]
+    children = [[c for c in range(N) if topo.parent[c] == p] for p in range(N)]
+    u = uniform01(seed, stream(S_PLANT, step), B * (D + 1)).reshape(B, D + 1)
+    alt = randint(seed, stream(S_ALT, step), B * D * 4, 0, V - 1).reshape(B, D, 4)
+    for b in range(B):
+        leaf = deepest[min(int(u[b, 0] * len(deepest)), len(deepest) - 1)]
+        path = [leaf]
+        while topo.parent[path[-1]] >= 0:
+            path.append(topo.parent[path[-1]])
+        path.reverse()
+        for i in range(1, D + 1):
+            p, c = path[i - 1], path[i]
+            if u[b, i] < a[i - 1]:
+                H[b, p] += alpha * W(int(tree_tok[b, c]))
+            else:
+                taken = {int(tree_tok[b, cc]) for cc in children[p]}
+                x = next((int(v) for v in alt[b, i - 1] if int(v) not in taken), None)
+                if x is None:  # four draws all hit a child token: take the lowest free index
+                    x = next(v for v in range(V) if v not in taken)
+                H[b, p] += alpha * W(x)
+                break
+    Ht[...] = f32_to_bf16(H.astype(np.float32)) if bf else H.astype(Ht.dtype)
+    return Ht

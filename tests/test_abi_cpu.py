@@ -23,7 +23,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 13
+    assert len(names) == 16
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -147,6 +147,36 @@ def test_attention_and_accept_argument_errors():
     assert build(src=None) == L.MD_EINVAL
     assert build(kind=1, level=5) == L.MD_EINVAL
     assert build(B=0) == L.MD_OK
+
+
+def test_target_argmax_and_accept_tokens_argument_errors():
+    lib = L.lib()
+    P = 0x1000
+    need = md.md_target_argmax_workspace_bytes(1, 64, 512, 5000)
+    assert need > 0
+
+    def am(dt=1, R=64, d=512, V=5000, H=P, ws_bytes=need):
+        return lib.md_target_argmax(dt, R, d, V, H, P, P, None, P, ws_bytes, None)
+
+    assert am(dt=5) == L.MD_EINVAL
+    assert am(R=-1) == L.MD_EINVAL
+    assert am(V=0) == L.MD_EINVAL
+    assert am(d=100) == L.MD_EUNSUPPORTED
+    assert am(d=65536) == L.MD_EUNSUPPORTED
+    assert am(H=None) == L.MD_EINVAL
+    assert am(ws_bytes=need - 1) == L.MD_EWORKSPACE
+    assert am(R=0) == L.MD_OK
+    topo = product_order_tree((4, 2, 2, 1), 16)
+    t = ctypes.byref(L.make_tree(topo.parent, topo.rank))
+
+    def acc(B=1, K=4, hd=128, Lcap=200, tt=P):
+        return lib.md_tree_accept_tokens(t, 1, B, K, 2, hd, Lcap, tt, P, P, P, P, P, P, P, P, None)
+
+    assert acc(hd=512) == L.MD_EUNSUPPORTED
+    assert acc(Lcap=10) == L.MD_ERANGE
+    assert acc(K=3) == L.MD_EINVAL  # the tree is 4 deep
+    assert acc(tt=None) == L.MD_EINVAL
+    assert acc(B=0) == L.MD_OK
 
 
 def test_timing_hook_pairs():

@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 import synth
-from synth.workloads import HYDRA_B4, LLAMA70B, LLAMA70B_CHAIN, TINY_F32, plant, step_inputs, weights
+from synth.workloads import (HYDRA_B4, LLAMA70B, LLAMA70B_CHAIN, LLAMA70B_LMHEAD, TINY_F32, plant, plant_hidden,
+                             step_inputs, weights)
 
 from _helpers import TAU, TOL, from_dev, rel_err, to_dev
 
@@ -29,7 +30,7 @@ def make_step(wl):
                         dtype=torch.float32 if wl.dtype == "f32" else torch.bfloat16, B=wl.B,
                         M=wl.M if wl.kind == "medusa" else wl.B, d=wl.d, V=wl.V, K=wl.K, k_per_head=wl.topk,
                         parent=topo.parent, rank=topo.rank, Hq=wl.Hq, Hkv=wl.Hkv, hd=wl.hd, Lcap=wl.Lcap,
-                        max_len=wl.L_max)
+                        max_len=wl.L_max, target_head=wl.target_head)
     return md.MedusaStep(cfg), topo
 
 
@@ -53,9 +54,16 @@ def run_and_compare(wl, w, wd, step, topo, seed, s):
 
     x = step_inputs(wl, seed, step=s)
     tok, pos, heads, full = oracle_tree(wl, w, x, topo)
-    logits = plant(x["logits"], topo, tok, wl.a, seed=seed, step=s)
+    if wl.target_head:
+        # verification through the target's LM head: plant the hidden states
+        Ht = plant_hidden(x["Ht"], w["Wt"], topo, tok, wl.a, seed=seed, step=s)
+        tstar, tval, tmargin = oracle.target_argmax(Ht.reshape(wl.B * topo.n, wl.d), w["Wt"])
+    else:
+        logits = plant(x["logits"], topo, tok, wl.a, seed=seed, step=s)
+        tstar = oracle.argmax(logits)
     xd = {k: to_dev(v) for k, v in x.items() if k != "logits"}
-    xd["logits"] = to_dev(logits)
+    if not wl.target_head:
+        xd["logits"] = to_dev(logits)
     step.run(wd, xd)
     torch.cuda.synchronize()
     # heads (Medusa: margin rule on the rows the tree reads)
@@ -78,7 +86,23 @@ def run_and_compare(wl, w, wd, step, topo, seed, s):
     ga = from_dev(step.attn_out)
     ga = ga.astype(np.float64) if wl.dtype == "f32" else synth.bf16_to_f32(ga).astype(np.float64)
     assert rel_err(ga, ref_attn) <= TOL[wl.dtype]
-    ref = oracle.accept(topo.parent, wl.K, tok, oracle.argmax(logits), x["lens"])
+    if wl.target_head:
+        # the GPU's choices must be the oracle's, or within tau of the best where the oracle's top two
+        # are closer than that; acceptance is then checked on the GPU's (valid) choices
+        gt = from_dev(step.target_tok).reshape(-1)
+        f64 = (lambda a: synth.bf16_to_f32(a).astype(np.float64)) if wl.dtype == "bf16" else (lambda a: a.astype(np.float64))
+        Hf = f64(Ht.reshape(wl.B * topo.n, wl.d))
+        near = 0
+        for r in range(gt.size):
+            if tmargin[r] > TAU[wl.dtype]:
+                assert gt[r] == tstar[r], (r, gt[r], tstar[r])
+            else:
+                near += 1
+                assert tval[r] - float(f64(w["Wt"][gt[r]]) @ Hf[r]) <= TAU[wl.dtype]
+        if near:
+            print("target choices within tau of a tie: %d of %d" % (near, gt.size))
+        tstar = gt.reshape(wl.B, topo.n)
+    ref = oracle.accept(topo.parent, wl.K, tok, tstar, x["lens"])
     for key in ("accept_len", "path", "next_tok", "compact_src"):
         assert np.array_equal(from_dev(getattr(step, key)), ref[key]), key
     rK, rV, rl = oracle.compact(x["Kc"], x["Vc"], x["lens"], ref["accept_len"], ref["path"], wl.K)
@@ -107,6 +131,28 @@ def test_step_tiny_shared_projection():
     step, topo = make_step(wl)
     lens = [int(run_and_compare(wl, w, wd, step, topo, seed, s)[0]) for s in range(6)]
     print("tiny shared-projection accepted lengths:", lens)
+
+
+def test_step_tiny_target_head():
+    from dataclasses import replace
+
+    wl = replace(TINY_F32, target_head=True)
+    seed = 5
+    w = weights(wl, seed)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    step, topo = make_step(wl)
+    lens = [int(run_and_compare(wl, w, wd, step, topo, seed, s)[0]) for s in range(6)]
+    print("tiny, verified through the LM head: accepted lengths", lens)
+
+
+def test_step_70b_lm_head():
+    wl = LLAMA70B_LMHEAD
+    seed = 73
+    w = weights(wl, seed)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    step, topo = make_step(wl)
+    acc = run_and_compare(wl, w, wd, step, topo, seed, 0)
+    print("70B-shaped step verified through the LM head accepted", acc)
 
 
 def test_step_70b_shaped():

@@ -17,7 +17,7 @@ import torch
 import oracle
 import synth
 from synth.topology import chain, product_order_tree
-from synth.workloads import plant
+from synth.workloads import plant, plant_hidden
 
 from conftest import GOLDEN
 
@@ -183,6 +183,18 @@ def test_shared_projection_with_zero_residual_is_one_library_sort():
             ref = np.argsort(-logits[m], kind="stable")[: topk[k]]
             assert np.array_equal(out["idx"][m, k, : topk[k]], ref)
             assert np.all(out["idx"][m, k, topk[k]:] == -1)
+
+
+def test_target_argmax_identity_head_is_library_argmax():
+    # an identity LM head (V = d) makes the logits the hidden state itself: the
+    # choice is the library's first-index argmax, ties included
+    d = 64
+    H = synth.normal(23, 1, (5, d), 1.0, "f32")
+    H[1, 10] = H[1, 40] = np.float32(9.0)  # an exact tie: the lower index wins
+    tok, val, margin = oracle.target_argmax(H, np.eye(d, dtype=np.float32))
+    assert np.array_equal(tok, np.argmax(H, axis=1))
+    assert tok[1] == 10 and margin[1] == 0.0
+    assert np.array_equal(val, H.max(axis=1).astype(np.float64))
 
 
 def test_hydra_level1_with_zero_embedding_half_is_medusa():
@@ -400,3 +412,31 @@ def test_planted_acceptance_reproduces_page_table(row):
         cost = 1 + hp["heads"] * oracle.head_weight_elems(hp["d"], hp["d"], hp["V"]) * 2 / (hp["target_bytes_GB"] * 1e9)
         assert round(cost, 3) == g["cost"]
         assert abs(emp / cost - g["speedup"]) < tol / cost + 0.006
+
+
+def test_planted_hidden_states_reproduce_page_table():
+    """Verification through the target's LM head: hidden states planted with
+    a = (0.80, 0.65, 0.50, 0.40) give, through the oracle's LM-head argmax and
+    acceptance, the mean accepted length of the page's tree row (E = 2.68)."""
+    g = golden("acceptance_table.json")["rows"][2]
+    a, K = g["a"], 4
+    topo = product_order_tree((4, 2, 2, 1), 16)
+    B, V, d = 2000, 512, 64
+    tok, _ = _random_tree_case(300, B, topo, V)
+    Wt = synth.normal(301, 1, (V, d), 1 / math.sqrt(d), "f32")
+    Ht = synth.normal(301, 2, (B, topo.n, d), 1.0, "f32")
+    plant_hidden(Ht, Wt, topo, tok, a, seed=302)
+    ts, _, margin = oracle.target_argmax(Ht.reshape(B * topo.n, d), Wt)
+    acc = oracle.accept(topo.parent, K, tok, ts.reshape(B, topo.n), np.zeros(B, np.int32))["accept_len"]
+    p, run = [], 1.0
+    for j in range(K + 1):
+        p.append(run * (1 - a[j]) if j < K else run)
+        if j < K:
+            run *= a[j]
+    p = np.array(p)
+    mean_model = float(np.sum(p * np.arange(1, K + 2)))
+    var_model = float(np.sum(p * np.arange(1, K + 2) ** 2)) - mean_model ** 2
+    tol = 4 * math.sqrt(var_model / B) + 0.005
+    assert abs(float(acc.mean()) - g["E"]) < tol, (float(acc.mean()), g["E"], tol)
+    counts = np.bincount(acc, minlength=K + 2)[1:]
+    assert float(np.sum((counts - B * p) ** 2 / (B * p))) < 20.5
