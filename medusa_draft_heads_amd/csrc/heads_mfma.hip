@@ -445,6 +445,195 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restr
     }
 }
 
+// Few activation rows (the target's LM head over one tree, Hydra's levels):
+// the vocabulary GEMM is HBM-bound there, and with one 16 KB operand stage
+// per block in flight the wide kernel's blocks wait on memory latency. This
+// kernel keeps two stages in flight out of three: block tile 256 vocabulary
+// rows x 64 activation rows, each wave 64 x 64 (4 x 4 MFMA tiles), stages of
+// 24 KB (A 16 KB, hi 4 KB, lo 4 KB) in three separately named LDS buffers,
+// two blocks per CU. Same operand layout, swizzle and bounds as the wide
+// kernel; one list per (activation row, vocabulary tile).
+constexpr int NM = 64;                       // activation rows per tile
+constexpr int NB_BYTES = NM * ROWB;          // 4 KB (hi; lo follows)
+constexpr int NSTAGE = A_BYTES + 2 * NB_BYTES;  // 24 KB
+static_assert(NB_BYTES == 4096, "one 1 KB piece of each of hi, lo per wave");
+static_assert(2 * (3 * NSTAGE + 4 * NM) <= 160 * 1024, "two blocks fit the LDS of one CU");
+static_assert(NM * VR * 4 <= 3 * NSTAGE, "the logit tile fits the three stage buffers");
+constexpr int NCOLS_PER_BUF = NSTAGE / (VR * 4);  // 24 columns of 256 logits per stage buffer
+constexpr int kNarrowRows = 128;  // up to this many activation rows the narrow kernel runs (1 or 2 row tiles)
+
+template <int NS>
+__global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* __restrict__ U,
+                                                                const uint16_t* __restrict__ hhi,
+                                                                const uint16_t* __restrict__ hlo, int M, int d, int V,
+                                                                int nh, int head0, int vtiles, int mtiles, int kmax,
+                                                                KW kk, int Mh, float* __restrict__ part_val,
+                                                                int* __restrict__ part_idx, int* __restrict__ bound) {
+    __shared__ __align__(1024) unsigned char nbuf0[NSTAGE];
+    __shared__ __align__(1024) unsigned char nbuf1[NSTAGE];
+    __shared__ __align__(1024) unsigned char nbuf2[NSTAGE];
+    __shared__ float s_bound[NM];
+    const int units = nh * vtiles;
+    int unit, mt;
+    if (!decode_tile(blockIdx.x, mtiles, units, unit, mt)) return;
+    const int hh = unit / vtiles, vt = unit - hh * vtiles;
+    const int v0 = vt * VR, m0 = mt * NM;
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int g4 = lane >> 4, c16 = lane & 15;
+    const int64_t hbase = (int64_t)hh * M * d;
+
+    // DMA as in the wide kernel: in 1 KB piece p = w + 4 j the lane loads row
+    // r0 + 64 j of A; hi and lo are one piece each (rows r0 < 64)
+    const int r0 = 16 * w + (lane >> 2);
+    const uint32_t voff0 = (uint32_t)r0 * d * 2 + 16 * ((lane & 3) ^ ((r0 >> 1) & 3));
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(U + ((int64_t)(head0 + hh) * V + v0) * d), 0, min(V - v0, VR) * d * 2, RSRC3);
+    const __amdgpu_buffer_rsrc_t rH =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(hhi + hbase + (int64_t)m0 * d), 0, min(M - m0, NM) * d * 2, RSRC3);
+    const __amdgpu_buffer_rsrc_t rL =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(hlo + hbase + (int64_t)m0 * d), 0, min(M - m0, NM) * d * 2, RSRC3);
+    auto issue = [&](int k0, unsigned char* base) {
+#pragma unroll
+        for (int j = 0; j < NPA; ++j) dmab(rA, base + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
+        dmab(rH, base + A_BYTES + w * 1024, voff0 + (uint32_t)k0 * 2);
+        if constexpr (NS == 2) dmab(rL, base + A_BYTES + NB_BYTES + w * 1024, voff0 + (uint32_t)k0 * 2);
+    };
+
+    f32x4 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int slot = (g4 ^ ((c16 >> 1) & 3)) * 16;
+    auto compute = [&](const unsigned char* sA) {
+        const unsigned char* sB = sA + A_BYTES;
+        bf16x8 a[4];
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            a[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sA + (64 * w + 16 * rb + c16) * ROWB + slot));
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const bf16x8 b = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(sB + s * NB_BYTES + (16 * cb + c16) * ROWB + slot));
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+                    acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b, acc[rb][cb], 0, 0, 0);
+            }
+        }
+    };
+
+    // Stage s lives in buffer s % 3; two stages are always in flight (past
+    // the last one the loads repeat it, keeping the count uniform), so the
+    // wait before a stage leaves one stage's loads, NPA + NS per wave, open.
+    const int nk = d / VK;
+    // The barrier is LDS-only (no release fence): a fence would also wait for
+    // the loads still in flight. Each wave's own wait makes its part of stage
+    // s land before it arrives; lgkmcnt(0) retires its reads of the buffer the
+    // next loads overwrite; the clobber keeps the compiler's memory operations
+    // on their side of it.
+    auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
+        if constexpr (NS == 2)
+            asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue(min(s + 2, nk - 1) * VK, nxt);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this stage's work
+        compute(cur);
+    };
+    static_assert(NPA + 2 == 6, "the wait counts above assume 4 A pieces per wave");
+    issue(0, nbuf0);
+    issue(min(1, nk - 1) * VK, nbuf1);
+    // three whole steps per iteration (no branch inside, so the compiler's
+    // wait insertion sees the same load order on every path), then the tail
+    int ks = 0;
+    for (; ks + 3 <= nk; ks += 3) {
+        step(ks, nbuf0, nbuf2);
+        step(ks + 1, nbuf1, nbuf0);
+        step(ks + 2, nbuf2, nbuf1);
+    }
+    if (ks < nk) step(ks, nbuf0, nbuf2);
+    if (ks + 1 < nk) step(ks + 1, nbuf1, nbuf0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads land before the buffers are reused
+    if (tid < NM)
+        s_bound[tid] = m0 + tid < M ? o2f(__hip_atomic_load(bound + (int64_t)hh * M + m0 + tid, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT))
+                                    : INFINITY;
+    __syncthreads();  // operand stages are dead; the logit tile takes their LDS
+    // Column c (row of h') takes 1 KB in buffer c / 24; its 16-byte groups are
+    // permuted by c % 16. Lane holds rows 64 w + 16 rb + 4 g4 + i of column
+    // 16 cb + c16.
+    auto colp = [&](int c) -> unsigned char* {
+        unsigned char* b = c < NCOLS_PER_BUF ? nbuf0 : (c < 2 * NCOLS_PER_BUF ? nbuf1 : nbuf2);
+        return b + (c % NCOLS_PER_BUF) * (VR * 4);
+    };
+#pragma unroll
+    for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const int col = 16 * cb + c16;
+            *reinterpret_cast<f32x4*>(colp(col) + (((16 * w + 4 * rb + g4) ^ (col & 15)) * 16)) = acc[rb][cb];
+        }
+    __syncthreads();
+    // Per column, the block's best k of its 256 vocabulary rows, filtered by
+    // the running bound as in the wide kernel. Wave w owns columns w, w + 4, ...
+    for (int col = w; col < NM; col += 4) {
+        const int m = m0 + col;
+        if (m >= M) break;  // uniform: columns past M are padding
+        const int k = kk.v[Mh > 0 ? min(m / Mh, 7) : hh];
+        const float T = s_bound[col];
+        const unsigned char* Sc = colp(col);
+        float x[4];
+        int cnt = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int rr = lane + 64 * q;
+            x[q] = v0 + rr < V ? *reinterpret_cast<const float*>(Sc + (((rr >> 2) ^ (col & 15)) * 16) + (rr & 3) * 4)
+                               : -INFINITY;
+            if (x[q] < T) x[q] = -INFINITY;
+            cnt += __popcll(__ballot(x[q] != -INFINITY));
+        }
+        const int rounds = cnt < k ? cnt : k;
+        float ov = -INFINITY;
+        int oi = INT_MAX;
+        for (int r = 0; r < rounds; ++r) {
+            float bv = x[0];
+            int bi = v0 + lane;
+#pragma unroll
+            for (int q = 1; q < 4; ++q)
+                if (ranks_above(x[q], v0 + lane + 64 * q, bv, bi)) {
+                    bv = x[q];
+                    bi = v0 + lane + 64 * q;
+                }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+                const float tv = __shfl_xor(bv, o, 64);
+                const int ti = __shfl_xor(bi, o, 64);
+                if (ranks_above(tv, ti, bv, bi)) {
+                    bv = tv;
+                    bi = ti;
+                }
+            }
+            if (lane == r) {
+                ov = bv;
+                oi = bi;
+            }
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (bi == v0 + lane + 64 * q) x[q] = -INFINITY;
+        }
+        if (lane < kmax) {
+            const int64_t o = (((int64_t)hh * M + m) * vtiles + vt) * kmax + lane;
+            part_val[o] = lane < rounds ? ov : -INFINITY;
+            part_idx[o] = lane < rounds ? oi : INT_MAX;
+        }
+        if (rounds == k && lane == k - 1) atomicMax(bound + (int64_t)hh * M + m, f2o(ov));
+    }
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 __global__ void k_fill_bound(int* __restrict__ bound, int n) {
@@ -479,13 +668,20 @@ hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt
     KW kk;
     for (int i = 0; i < 8; ++i) kk.v[i] = 1;
     const uint16_t* h = reinterpret_cast<const uint16_t*>(H);
-    hipLaunchKernelGGL(k_vocab_mfma<1>, dim3(8 * vmtiles * ((vtiles + 7) / 8)), dim3(BLOCK), 0, s,
-                       reinterpret_cast<const uint16_t*>(Wt), h, h, R, d, V, 1, 0, vtiles, vmtiles, 1, kk, 0, pv, pi,
-                       bound);
+    const uint16_t* wt = reinterpret_cast<const uint16_t*>(Wt);
+    if (R <= kNarrowRows) {
+        const int nmt = (R + NM - 1) / NM;
+        hipLaunchKernelGGL(k_vocab_mfma_narrow<1>, dim3(8 * nmt * ((vtiles + 7) / 8)), dim3(BLOCK), 0, s, wt, h, h, R, d,
+                           V, 1, 0, vtiles, nmt, 1, kk, 0, pv, pi, bound);
+        *nlists = vtiles;
+    } else {
+        hipLaunchKernelGGL(k_vocab_mfma<1>, dim3(8 * vmtiles * ((vtiles + 7) / 8)), dim3(BLOCK), 0, s, wt, h, h, R, d, V,
+                           1, 0, vtiles, vmtiles, 1, kk, 0, pv, pi, bound);
+        *nlists = 2 * vtiles;
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     *part_val = pv;
     *part_idx = pi;
-    *nlists = 2 * vtiles;
     return hipSuccess;
 }
 
@@ -547,15 +743,23 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
     // a shared projection is one matrix over the heads' nh * M rows
     const int rows_v = a.shared_u ? a.nh * a.M : a.M, nh_u = a.shared_u ? 1 : a.nh;
-    const int vmtiles = (rows_v + VM - 1) / VM;
     const int units2 = nh_u * vtiles;
-    hipLaunchKernelGGL(k_vocab_mfma<2>, dim3(8 * vmtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s,
-                       reinterpret_cast<const uint16_t*>(a.U), hhi, hlo, rows_v, a.d, a.V, nh_u,
-                       a.shared_u ? 0 : a.head0, vtiles, vmtiles, a.kmax, kk, a.shared_u ? a.M : 0, pv, pi, bound);
+    const uint16_t* U = reinterpret_cast<const uint16_t*>(a.U);
+    const int head0 = a.shared_u ? 0 : a.head0, Mh = a.shared_u ? a.M : 0;
+    if (rows_v <= kNarrowRows) {  // few rows: HBM-bound, the deeper pipeline wins
+        const int nmt = (rows_v + NM - 1) / NM;
+        hipLaunchKernelGGL(k_vocab_mfma_narrow<2>, dim3(8 * nmt * ((units2 + 7) / 8)), dim3(BLOCK), 0, s, U, hhi, hlo,
+                           rows_v, a.d, a.V, nh_u, head0, vtiles, nmt, a.kmax, kk, Mh, pv, pi, bound);
+        *nlists = vtiles;
+    } else {
+        const int vmtiles = (rows_v + VM - 1) / VM;
+        hipLaunchKernelGGL(k_vocab_mfma<2>, dim3(8 * vmtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s, U, hhi, hlo,
+                           rows_v, a.d, a.V, nh_u, head0, vtiles, vmtiles, a.kmax, kk, Mh, pv, pi, bound);
+        *nlists = 2 * vtiles;
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
     *part_val = pv;
     *part_idx = pi;
-    *nlists = 2 * vtiles;
     return hipSuccess;
 }
