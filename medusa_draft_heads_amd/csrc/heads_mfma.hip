@@ -113,12 +113,53 @@ __device__ __forceinline__ void tile_mma(const uint16_t (*As)[LP], const uint16_
     }
 }
 
+// h' = base + SiLU(z + b) for 4 consecutive rows r.. of head hh, activation
+// row m, stored as float32 and as its hi/lo bf16 split.
+__device__ __forceinline__ void residual_out(const f32x4& z, const uint16_t* __restrict__ bias, const GemmRows& rows,
+                                             int brow, int M, int d, int head0, int hh, int m, int r,
+                                             float* __restrict__ hres, float* __restrict__ hres_out,
+                                             uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo) {
+    float bb[4] = {0.f, 0.f, 0.f, 0.f};
+    if (bias) {
+        const u32x2 bw = *reinterpret_cast<const u32x2*>(bias + (int64_t)(head0 + hh) * d + r);
+        bb[0] = bf_lo(bw.x);
+        bb[1] = bf_hi(bw.x);
+        bb[2] = bf_lo(bw.y);
+        bb[3] = bf_hi(bw.y);
+    }
+    const u32x2 hw = *reinterpret_cast<const u32x2*>(rows.h + (int64_t)brow * d + r);
+    const float base[4] = {bf_lo(hw.x), bf_hi(hw.x), bf_lo(hw.y), bf_hi(hw.y)};
+    f32x4 hv;
+    uint32_t hi2[2] = {0u, 0u}, lo2[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float zi = z[i] + bb[i];
+        const float v = base[i] + zi / (1.f + expf(-zi));
+        hv[i] = v;
+        const __bf16 hb = (__bf16)v;
+        const float rem = v - (float)hb;
+        const __bf16 lb = (__bf16)rem;
+        const uint32_t hbits = __builtin_bit_cast(uint16_t, hb), lbits = __builtin_bit_cast(uint16_t, lb);
+        hi2[i >> 1] |= hbits << (16 * (i & 1));
+        lo2[i >> 1] |= lbits << (16 * (i & 1));
+    }
+    const int64_t o = ((int64_t)hh * M + m) * d + r;
+    *reinterpret_cast<f32x4*>(hres + o) = hv;
+    if (hres_out) *reinterpret_cast<f32x4*>(hres_out + o) = hv;
+    *reinterpret_cast<u32x2*>(hhi + o) = u32x2{hi2[0], hi2[1]};
+    *reinterpret_cast<u32x2*>(hlo + o) = u32x2{lo2[0], lo2[1]};
+}
+
 // Phase 1: z = W x for rows [0, nh*d) of the heads' residual matrices and
 // activation rows [0, M); epilogue h' = base + SiLU(z + b) -> hres (f32) and
-// its hi/lo bf16 split.
+// its hi/lo bf16 split. With few rows the tiles alone leave most CUs idle,
+// so the contraction is split in ksplit chunks: block (tile, chunk) stores
+// its partial z to zpart [ksplit][nh][M][d], and k_residual_finish adds the
+// chunks in a fixed order (the result does not depend on timing).
 __global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __restrict__ W,
                                                             const uint16_t* __restrict__ bias, GemmRows rows, int M,
-                                                            int d, int din, int nh, int head0, int mtiles,
+                                                            int d, int din, int nh, int head0, int mtiles, int ksplit,
+                                                            float* __restrict__ zpart,
                                                             float* __restrict__ hres, float* __restrict__ hres_out,
                                                             uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo,
                                                             int* __restrict__ bound) {
@@ -128,8 +169,11 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __re
     uint16_t(*As)[LP] = reinterpret_cast<uint16_t(*)[LP]>(smem);
     uint16_t(*Bs)[TM][LP] = reinterpret_cast<uint16_t(*)[TM][LP]>(smem + TR * LP * 2);
     const int units = nh * d / TR;
+    const int per_split = 8 * mtiles * ((units + 7) / 8);  // block ids of one contraction chunk
+    const int kc = blockIdx.x / per_split;
+    const int kspan = din / ksplit, kbeg = kc * kspan;
     int unit, mt;
-    if (!decode_tile(blockIdx.x, mtiles, units, unit, mt)) return;
+    if (!decode_tile(blockIdx.x - kc * per_split, mtiles, units, unit, mt)) return;
     const int row0 = unit * TR;  // over nh*d rows (a tile never straddles heads: d % 128 == 0)
     const int hh = row0 / d, r0 = row0 - hh * d;
     const int m0 = mt * TM;
@@ -182,8 +226,8 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __re
     for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    fetch(0);
-    for (int k0 = 0; k0 < din; k0 += KS) {
+    fetch(kbeg);
+    for (int k0 = kbeg; k0 < kbeg + kspan; k0 += KS) {
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < NLD; ++j) {
@@ -193,52 +237,55 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __re
             *reinterpret_cast<u32x4*>(&Bs[0][r][8 * c]) = rb[j];
         }
         __syncthreads();
-        if (k0 + KS < din) fetch(k0 + KS);
+        if (k0 + KS < kbeg + kspan) fetch(k0 + KS);
         tile_mma<1>(As, Bs, wr, wc, g4, c16, acc);
+    }
+    if (ksplit > 1) {  // partial z of this chunk: lane holds rows 64wr + 16rb + 4g4 + i of column 64wc + 16cb + c16
+#pragma unroll
+        for (int rb_ = 0; rb_ < 4; ++rb_)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb) {
+                const int m = m0 + 64 * wc + 16 * cb + c16;
+                if (m < M)
+                    *reinterpret_cast<f32x4*>(zpart + (((int64_t)kc * nh + hh) * M + m) * d + r0 + 64 * wr + 16 * rb_ +
+                                              4 * g4) = acc[rb_][cb];
+            }
+        return;
     }
 
     // epilogue: lane holds z[row = 64wr + 16rb + 4g4 + i][col = 64wc + 16cb + c16]
 #pragma unroll
     for (int rb_ = 0; rb_ < 4; ++rb_) {
         const int r = r0 + 64 * wr + 16 * rb_ + 4 * g4;  // row within the head, 4 consecutive
-        float bb[4];
-        if (bias) {
-            const u32x2 bw = *reinterpret_cast<const u32x2*>(bias + (int64_t)(head0 + hh) * d + r);
-            bb[0] = bf_lo(bw.x);
-            bb[1] = bf_hi(bw.x);
-            bb[2] = bf_lo(bw.y);
-            bb[3] = bf_hi(bw.y);
-        } else {
-            bb[0] = bb[1] = bb[2] = bb[3] = 0.f;
-        }
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb) {
             const int mm = 64 * wc + 16 * cb + c16;
             const int m = m0 + mm;
             if (m >= M) continue;
-            const u32x2 hw = *reinterpret_cast<const u32x2*>(rows.h + (int64_t)(rows.kind == 0 ? m : s_b[mm]) * d + r);
-            const float base[4] = {bf_lo(hw.x), bf_hi(hw.x), bf_lo(hw.y), bf_hi(hw.y)};
-            f32x4 hv;
-            uint32_t hi2[2] = {0u, 0u}, lo2[2] = {0u, 0u};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float z = acc[rb_][cb][i] + bb[i];
-                const float v = base[i] + z / (1.f + expf(-z));
-                hv[i] = v;
-                const __bf16 hb = (__bf16)v;
-                const float rem = v - (float)hb;
-                const __bf16 lb = (__bf16)rem;
-                const uint32_t hbits = __builtin_bit_cast(uint16_t, hb), lbits = __builtin_bit_cast(uint16_t, lb);
-                hi2[i >> 1] |= hbits << (16 * (i & 1));
-                lo2[i >> 1] |= lbits << (16 * (i & 1));
-            }
-            const int64_t o = ((int64_t)hh * M + m) * d + r;
-            *reinterpret_cast<f32x4*>(hres + o) = hv;
-            if (hres_out) *reinterpret_cast<f32x4*>(hres_out + o) = hv;
-            *reinterpret_cast<u32x2*>(hhi + o) = u32x2{hi2[0], hi2[1]};
-            *reinterpret_cast<u32x2*>(hlo + o) = u32x2{lo2[0], lo2[1]};
+            residual_out(acc[rb_][cb], bias, rows, rows.kind == 0 ? m : s_b[mm], M, d, head0, hh, m, r, hres, hres_out,
+                         hhi, hlo);
         }
     }
+}
+
+// Sums the ksplit partial z of each (head, row, 4 consecutive outputs) in
+// chunk order and applies the residual epilogue.
+__global__ __launch_bounds__(BLOCK) void k_residual_finish(const float* __restrict__ zpart, int ksplit,
+                                                           const uint16_t* __restrict__ bias, GemmRows rows, int M,
+                                                           int d, int nh, int head0, float* __restrict__ hres,
+                                                           float* __restrict__ hres_out, uint16_t* __restrict__ hhi,
+                                                           uint16_t* __restrict__ hlo) {
+    const int64_t q = (int64_t)blockIdx.x * BLOCK + threadIdx.x;  // index of 4 outputs over [nh][M][d]
+    const int64_t total = (int64_t)nh * M * d / 4;
+    if (q >= total) return;
+    const int64_t e = q * 4;
+    const int r = (int)(e % d);
+    const int64_t hm = e / d;
+    const int m = (int)(hm % M), hh = (int)(hm / M);
+    f32x4 z = *reinterpret_cast<const f32x4*>(zpart + e);
+    for (int c = 1; c < ksplit; ++c) z += *reinterpret_cast<const f32x4*>(zpart + (int64_t)c * nh * M * d + e);
+    const int brow = rows.kind == 0 ? m : m / rows.P;
+    residual_out(z, bias, rows, brow, M, d, head0, hh, m, r, hres, hres_out, hhi, hlo);
 }
 
 // Phase 2: logits = U (hi + lo) for one head's VR vocabulary rows x VM
@@ -690,11 +737,22 @@ bool heads_mfma_applicable(int dt, int M, int d, int din) {
     return dt == 1 && M >= 8 && d % TR == 0 && din % KS == 0 && d % (2 * VK) == 0;
 }
 
-size_t heads_mfma_ws_bytes(int M, int d, int V, int nh, int kmax) {
+// Contraction chunks of the residual: enough (tile, chunk) blocks for two per
+// CU of a 256-CU part, each chunk a whole number of K steps (a power of two
+// dividing din / KS).
+int residual_ksplit(int M, int d, int din, int nh) {
+    const int blocks = ((M + TM - 1) / TM) * (nh * d / TR);
+    int ks = 1;
+    while (blocks * ks < 512 && (din / KS) % (2 * ks) == 0 && 2 * ks <= 64) ks *= 2;
+    return ks;
+}
+
+size_t heads_mfma_ws_bytes(int M, int d, int din, int V, int nh, int kmax) {
     const size_t vtiles = (size_t)(V + VR - 1) / VR;
     const size_t e = (size_t)nh * M * d;
+    const int ks = residual_ksplit(M, d, din, nh);
     return align256(e * 4) + 2 * align256(e * 2) + 2 * align256((size_t)nh * M * 2 * vtiles * kmax * 4) +
-           align256((size_t)nh * M * 4);
+           align256((size_t)nh * M * 4) + (ks > 1 ? align256((size_t)ks * e * 4) : 0);
 }
 
 // Launches phase 1 and phase 2; the caller merges the lists (two per vocabulary tile).
@@ -715,6 +773,8 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     int* pi = reinterpret_cast<int*>(w);
     w += align256((size_t)a.nh * a.M * 2 * vtiles * a.kmax * 4);
     int* bound = reinterpret_cast<int*>(w);
+    w += align256((size_t)a.nh * a.M * 4);
+    float* zpart = reinterpret_cast<float*>(w);  // split contraction partials (when ksplit > 1)
     KW kk;
     for (int i = 0; i < 8; ++i) kk.v[i] = i < a.nh ? a.kk[i] : 1;
 
@@ -735,11 +795,19 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     rows.tree_tok = a.tree_tok;
 
     const int units1 = a.nh * a.d / TR;
-    hipLaunchKernelGGL(k_residual_mfma, dim3(8 * mtiles * ((units1 + 7) / 8)), dim3(BLOCK), 0, s,
-                       reinterpret_cast<const uint16_t*>(a.W), reinterpret_cast<const uint16_t*>(a.b), rows, a.M, a.d,
-                       a.din, a.nh, a.head0, mtiles, hres, a.h_res, hhi, hlo, bound);
+    const int ksplit = residual_ksplit(a.M, a.d, a.din, a.nh);
+    const uint16_t* bias = reinterpret_cast<const uint16_t*>(a.b);
+    hipLaunchKernelGGL(k_residual_mfma, dim3(ksplit * 8 * mtiles * ((units1 + 7) / 8)), dim3(BLOCK), 0, s,
+                       reinterpret_cast<const uint16_t*>(a.W), bias, rows, a.M, a.d, a.din, a.nh, a.head0, mtiles,
+                       ksplit, zpart, hres, a.h_res, hhi, hlo, bound);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
+    if (ksplit > 1) {
+        const int64_t quads = e / 4;
+        hipLaunchKernelGGL(k_residual_finish, dim3((unsigned)((quads + BLOCK - 1) / BLOCK)), dim3(BLOCK), 0, s, zpart,
+                           ksplit, bias, rows, a.M, a.d, a.nh, a.head0, hres, a.h_res, hhi, hlo);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
     if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
     // a shared projection is one matrix over the heads' nh * M rows
     const int rows_v = a.shared_u ? a.nh * a.M : a.M, nh_u = a.shared_u ? 1 : a.nh;
