@@ -236,7 +236,8 @@ def main() -> int:
         achieved = vocab_flops / (vocab_ms * 1e-3) / 1e12
         roofline = {"bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                     "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
-                    "kernel": "k_vocab_mfma (%s; each product issued twice, h' as hi + lo bf16)" % kernel,
+                    "kernel": "k_vocab_mfma_cert (%s; one bf16 product per term, the candidates that a "
+                              "Cauchy-Schwarz bound cannot exclude re-scored in float32 by k_rescore)" % kernel,
                     "kernel_ms": round(vocab_ms, 4), "flops_per_step": vocab_flops}
     else:
         achieved = vocab_bytes / (vocab_ms * 1e-3) / 1e9

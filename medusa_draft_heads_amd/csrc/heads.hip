@@ -681,14 +681,13 @@ hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
 }  // namespace
 
 size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u) {
-    if (heads_mfma_applicable(dt, M, d, din)) return heads_mfma_ws_bytes(M, d, din, V, nh, kmax);
+    if (heads_mfma_applicable(dt, M, d, din)) return heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u);
     const Plan p = make_plan(dt, M, d, din, nh, shared_u);
     return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * p.wg_per_head * kmax * 4);
 }
 
 size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u) {
-    (void)shared_u;  // a shared projection has at most as many lists per row as a head of its own
-    const size_t mfma = heads_mfma_applicable(dt, M, d, din) ? heads_mfma_ws_bytes(M, d, din, V, nh, kmax) : 0;
+    const size_t mfma = heads_mfma_applicable(dt, M, d, din) ? heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u) : 0;
     const size_t lists_max = (size_t)device_cus() * 4;  // blocks per head at most
     const size_t gemv = align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * lists_max * kmax * 4);
     return gemv > mfma ? gemv : mfma;
@@ -782,6 +781,7 @@ hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
         int nlists;
         hipError_t e = heads_mfma_launch(a, tree, s, ev0, ev1, &pv, &pi, &nlists);
         if (e != hipSuccess) return e;
+        if (nlists == 0) return hipSuccess;  // the certified pass wrote the lists
         KK kk;
         for (int i = 0; i < 8; ++i) kk.v[i] = i < a.nh ? a.kk[i] : 1;
         return launch_merge(pv, pi, a.M, a.nh, nlists, kk, a.kmax, a.topk_idx, a.topk_val, s);

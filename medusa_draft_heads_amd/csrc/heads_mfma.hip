@@ -10,23 +10,26 @@
 // * phase 1 (residual): x is exact in bf16 (h, or Hydra's [h ; E[token]]),
 //   so one product per term. The epilogue forms h' = base + SiLU(z + b) in
 //   float32 and also stores it split as hi = bf16(h'), lo = bf16(h' - hi).
-// * phase 2 (vocabulary): logits = U hi + U lo, two products per term, so
-//   h' enters with ~16 mantissa bits (relative error <= 2^-17) instead of
-//   bf16's 8; rounding h' itself to bf16 would move logits by ~1e-3 and
-//   reorder near-equal candidates. The epilogue takes, per column (row of
-//   h'), the block's best k logits of its 128 vocabulary rows; logits never
-//   reach memory. A running lower bound of each column's k-th best logit
-//   (atomicMax of every block's k-th) filters candidates first, so most
-//   blocks select almost nothing. The per-block lists then go through the
-//   same k-way merge as the GEMV path.
+// * phase 2 (vocabulary): h' must enter with more than bf16's 8 mantissa
+//   bits (rounding it to bf16 moves logits by ~1e-3 and reorders near-equal
+//   candidates); as hi + lo it enters with ~16 (relative error <= 2^-17).
+//   - up to 128 rows (HBM-bound): logits = U hi + U lo, two products per
+//     term, in the narrow kernel; per column (row of h') the block's best k
+//     logits, filtered first by a running lower bound of the k-th best;
+//     the per-block lists go through the same k-way merge as the GEMV path;
+//   - more rows (matrix-bound): one product, U hi, and a certificate: every
+//     logit of a vocabulary tile is within E of U hi (Cauchy-Schwarz with
+//     the tile's largest row norm and |lo|), so only entries whose U hi + E
+//     reaches a lower bound of the k-th best are kept, then re-scored in
+//     float32 from hi + lo; the top k are taken over the re-scored values
+//     (details at k_vocab_mfma_cert). Logits never reach memory.
 //
 // Residual: block tile 128 weight rows x 128 activation rows, K step 64, 4
 // waves of 64 x 64 (4 x 4 MFMA tiles each), operands staged in LDS (rows
 // padded against bank conflicts) from registers loaded one K step ahead.
-// Vocabulary: block tile 256 vocabulary rows x 128 activation rows, K step
-// 32, 4 waves of 128 x 64 (8 x 4 MFMA tiles, hi and lo), operands loaded
-// straight from memory into LDS two stages deep, two blocks per CU (details
-// at the kernel). Both operands are row-major along the contraction, which
+// Vocabulary: block tile 256 vocabulary rows x 128 (many rows) or 64 (few
+// rows) activation rows, K step 32, operands loaded straight from memory
+// into LDS, two blocks per CU (details at the kernels). Both operands are row-major along the contraction, which
 // is exactly the MFMA operand layout (a lane reads 8 consecutive k of one
 // row), so nothing is transposed. Blocks that share a weight tile (the
 // activation tiles of one weight tile) get ids spaced by 8, i.e. the same
@@ -681,6 +684,481 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* 
     }
 }
 
+// ---- certified single-product vocabulary pass (many rows) ----
+//
+// With h' = hi + lo' (hi = bf16(h'), lo' the exact rest), the logit is
+// l = U.hi + U.lo'. The matrix cores compute only l~ = U.hi; by
+// Cauchy-Schwarz |U_v.lo'| <= |U_v| |lo'|, so with N the largest row norm of
+// U in a vocabulary tile every logit of that tile satisfies
+//     |l~_v - l_v| <= E = N (|lo'| + 2^-14 |h'|)
+// where the second term covers float32 rounding of both the product sums
+// and the exact re-scoring below (<= 2^-15 |U_v| |h'| each for sums of
+// 8,192 terms in blocks of 32). A tile's k-th best l~ minus E is then a
+// lower bound T of the row's k-th best logit; only entries with
+// l~ + E >= T can belong to the top k. Those candidates are re-scored in
+// float32 from U and h' and the top k taken over the re-scored values.
+constexpr int kCertCap = 8192;  // candidates kept per (head, row); more -> exact full scan of that row
+constexpr int kSlots = 64;      // per-row maxima of half-tile lower bounds (their k-th largest bounds the k-th best)
+
+// Per (head, row): |h' - bf16(h')| and |h'| (one wave per row, fixed order).
+__global__ __launch_bounds__(BLOCK) void k_row_norms(const float* __restrict__ hres, int rows, int d,
+                                                     float* __restrict__ lo_norm, float* __restrict__ h_norm) {
+    const int row = blockIdx.x * (BLOCK / 64) + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+    if (row >= rows) return;
+    const float* x = hres + (int64_t)row * d;
+    float sl = 0.f, sh = 0.f;
+    for (int c = lane * 4; c < d; c += 256) {
+        const f32x4 v = *reinterpret_cast<const f32x4*>(x + c);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float r = v[i] - (float)(__bf16)v[i];
+            sl = fmaf(r, r, sl);
+            sh = fmaf(v[i], v[i], sh);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        sl += __shfl_xor(sl, o, 64);
+        sh += __shfl_xor(sh, o, 64);
+    }
+    if (lane == 0) {
+        lo_norm[row] = sqrtf(sl) * (1.f + 0x1p-10f);  // the sums' own rounding, rounded up
+        h_norm[row] = sqrtf(sh) * (1.f + 0x1p-10f);
+    }
+}
+
+__global__ void k_cert_prep(int* __restrict__ bound, int* __restrict__ slots, int* __restrict__ count, int n) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) {
+        bound[i] = f2o(-INFINITY);
+        count[i] = 0;
+    }
+    if (i < n * kSlots) slots[i] = f2o(-INFINITY);
+}
+
+// float32 dot of a bf16 row of U with h' = hi + lo (bf16 each; products
+// exact) by one wave: each lane sums its 8-element chunks in order, then a
+// butterfly.
+__device__ __forceinline__ float wave_dot2(const uint16_t* __restrict__ u, const uint16_t* __restrict__ xh,
+                                           const uint16_t* __restrict__ xl, int d, int lane) {
+    float s = 0.f;
+    for (int c = lane * 8; c < d; c += 512) {
+        const u32x4 w = *reinterpret_cast<const u32x4*>(u + c);
+        const u32x4 h = *reinterpret_cast<const u32x4*>(xh + c), l = *reinterpret_cast<const u32x4*>(xl + c);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            s = fmaf(bf_lo(w[e]), bf_lo(h[e]) + bf_lo(l[e]), s);
+            s = fmaf(bf_hi(w[e]), bf_hi(h[e]) + bf_hi(l[e]), s);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+    return s;
+}
+
+// One block per (head, row m). The candidates' lower bounds give T*, the
+// k-th best of them: a lower bound of the row's k-th best logit at least as
+// good as the running one. Candidates whose upper bound reaches max(T, T*)
+// are re-scored in float32 and the row's top k taken over the re-scored
+// values. If the candidate buffer overflowed, or more than kSurv survive,
+// every vocabulary row is re-scored instead (one pass, each wave keeping its
+// own k best).
+constexpr int kSurv = 512;
+__global__ __launch_bounds__(BLOCK) void k_rescore(const uint16_t* __restrict__ U, const uint16_t* __restrict__ hhi,
+                                                   const uint16_t* __restrict__ hlo, int M, int d, int V, int nh,
+                                                   int head0, int shared_u, KW kk, int kmax,
+                                                   const int* __restrict__ bound, const int* __restrict__ count,
+                                                   const float* __restrict__ cand_ub, const float* __restrict__ cand_lb,
+                                                   const int* __restrict__ cand_idx, int32_t* __restrict__ topk_idx,
+                                                   float* __restrict__ topk_val) {
+    __shared__ float s_v[kSurv];  // re-scored values
+    __shared__ int s_i[kSurv];    // survivors' indices
+    __shared__ int s_n;
+    __shared__ float wv_s[BLOCK / 64];
+    __shared__ int wi_s[BLOCK / 64];
+    const int hh = blockIdx.x / M, m = blockIdx.x - hh * M;
+    const int row = hh * M + m;  // row of h' and of the candidate arrays
+    const int k = kk.v[hh];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const uint16_t* Uh = U + (shared_u ? 0 : (int64_t)(head0 + hh) * V * d);
+    const uint16_t* xh = hhi + (int64_t)row * d;
+    const uint16_t* xl = hlo + (int64_t)row * d;
+    const int cnt = count[row];
+    // block argmax of (value, index) strictly below (pv, pi) over one value per thread
+    auto block_pick1 = [&](float v, int i, float& ov, int& oi) {
+        float bv = v;
+        int bi = i;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            const float tv = __shfl_xor(bv, o, 64);
+            const int ti = __shfl_xor(bi, o, 64);
+            if (ranks_above(tv, ti, bv, bi)) {
+                bv = tv;
+                bi = ti;
+            }
+        }
+        if (lane == 0) {
+            wv_s[w] = bv;
+            wi_s[w] = bi;
+        }
+        __syncthreads();
+        bv = wv_s[0];
+        bi = wi_s[0];
+        for (int w2 = 1; w2 < BLOCK / 64; ++w2)
+            if (ranks_above(wv_s[w2], wi_s[w2], bv, bi)) {
+                bv = wv_s[w2];
+                bi = wi_s[w2];
+            }
+        __syncthreads();
+        ov = bv;
+        oi = bi;
+    };
+    if (tid == 0) s_n = 0;
+    __syncthreads();
+    bool full = cnt > kCertCap;
+    if (!full) {
+        float Tf = o2f(bound[row]);
+        if (cnt >= k) {
+            // T*: each thread keeps its k best lower bounds (sorted, kk <= 16), then
+            // k rounds pop the block's best thread head
+            float tl[16];
+            int ti[16];
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+                tl[q] = -INFINITY;
+                ti[q] = INT_MAX;
+            }
+            for (int j = tid; j < cnt; j += BLOCK) {
+                const float v = cand_lb[(int64_t)row * kCertCap + j];
+                if (!ranks_above(v, j, tl[15], ti[15])) continue;
+#pragma unroll
+                for (int q = 15; q >= 0; --q) {  // insertion; tl[q - 1] is read before it moves
+                    if (!ranks_above(v, j, tl[q], ti[q])) continue;
+                    if (q > 0 && ranks_above(v, j, tl[q - 1], ti[q - 1])) {
+                        tl[q] = tl[q - 1];
+                        ti[q] = ti[q - 1];
+                    } else {
+                        tl[q] = v;
+                        ti[q] = j;
+                    }
+                }
+            }
+            float kth = -INFINITY;
+            for (int r = 0; r < k; ++r) {
+                float ov;
+                int oi;
+                block_pick1(tl[0], ti[0], ov, oi);
+                kth = ov;
+                if (oi == ti[0] && oi != INT_MAX) {  // the winner pops its head (candidate ids are unique)
+#pragma unroll
+                    for (int q = 0; q < 15; ++q) {
+                        tl[q] = tl[q + 1];
+                        ti[q] = ti[q + 1];
+                    }
+                    tl[15] = -INFINITY;
+                    ti[15] = INT_MAX;
+                }
+            }
+            Tf = fmaxf(Tf, kth);
+        }
+        for (int j = tid; j < cnt; j += BLOCK)
+            if (cand_ub[(int64_t)row * kCertCap + j] >= Tf) {
+                const int p = atomicAdd(&s_n, 1);
+                if (p < kSurv) s_i[p] = cand_idx[(int64_t)row * kCertCap + j];
+            }
+        __syncthreads();
+        full = s_n > kSurv;  // uniform
+        __syncthreads();     // every thread has read s_n before the fallback may rewrite it
+        if (!full) {
+            for (int j = w; j < s_n; j += BLOCK / 64) {
+                const float v = wave_dot2(Uh + (int64_t)s_i[j] * d, xh, xl, d, lane);
+                if (lane == 0) s_v[j] = v;
+            }
+            __syncthreads();
+        }
+    }
+    if (full) {
+        // overflow: one pass over the vocabulary, each wave keeping its k best
+        // in lanes 0..k-1 (sorted), then the wave lists go to LDS
+        float lv = -INFINITY;
+        int li = INT_MAX;
+        for (int v0 = w; v0 < V; v0 += BLOCK / 64) {
+            const float v = wave_dot2(Uh + (int64_t)v0 * d, xh, xl, d, lane);
+            const uint64_t above = __ballot(lane < k && ranks_above(v, v0, lv, li));
+            if (above) {  // the lanes v ranks above form a suffix [pos, k)
+                const int pos = __ffsll((long long)above) - 1;
+                const float uv = __shfl_up(lv, 1, 64);
+                const int ui = __shfl_up(li, 1, 64);
+                if (lane > pos && lane < k) {
+                    lv = uv;
+                    li = ui;
+                }
+                if (lane == pos) {
+                    lv = v;
+                    li = v0;
+                }
+            }
+        }
+        if (lane < k) {
+            s_v[w * 16 + lane] = lv;
+            s_i[w * 16 + lane] = li;
+        } else if (lane < 16) {
+            s_v[w * 16 + lane] = -INFINITY;
+            s_i[w * 16 + lane] = INT_MAX;
+        }
+        if (tid == 0) s_n = (BLOCK / 64) * 16;
+        __syncthreads();
+    }
+    // k rounds of a block argmax over the re-scored values (at most kSurv)
+    float out_v = -INFINITY;
+    int out_i = INT_MAX;
+    {
+        float pv = INFINITY;
+        int pi = -1;
+        for (int r = 0; r < k; ++r) {
+            float bv = -INFINITY;
+            int bi = INT_MAX;
+            for (int j = tid; j < s_n; j += BLOCK)
+                if (ranks_above(pv, pi, s_v[j], s_i[j]) && ranks_above(s_v[j], s_i[j], bv, bi)) {
+                    bv = s_v[j];
+                    bi = s_i[j];
+                }
+            float ov;
+            int oi;
+            block_pick1(bv, bi, ov, oi);
+            if (tid == r) {
+                out_v = ov;
+                out_i = oi;
+            }
+            pv = ov;
+            pi = oi;
+        }
+    }
+    if (tid < kmax) {
+        const bool ok = tid < k && out_i != INT_MAX;
+        const int64_t o = ((int64_t)m * nh + hh) * kmax + tid;
+        topk_idx[o] = ok ? out_i : -1;
+        topk_val[o] = ok ? out_v : -INFINITY;
+    }
+}
+
+// The wide kernel's tiling with one product per term (hi), the tile's
+// largest U row norm accumulated from the operand fragments, and the
+// certified epilogue: per activation row, the bound E of this tile, a lower
+// bound of the row's k-th best logit (atomicMax), and every entry that can
+// still reach the top k appended to the row's candidate buffer.
+__global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __restrict__ U,
+                                                              const uint16_t* __restrict__ hhi, int M, int d, int V,
+                                                              int nh, int head0, int vtiles, int mtiles, KW kk, int Mh,
+                                                              const float* __restrict__ lo_norm,
+                                                              const float* __restrict__ h_norm,
+                                                              int* __restrict__ bound, int* __restrict__ slots,
+                                                              int* __restrict__ count,
+                                                              float* __restrict__ cand_ub, float* __restrict__ cand_lb,
+                                                              int* __restrict__ cand_idx) {
+    __shared__ __align__(1024) unsigned char sbuf0[STAGE];
+    __shared__ __align__(1024) unsigned char sbuf1[STAGE];
+    __shared__ float s_bound[VM];
+    __shared__ float s_E[VM];
+    __shared__ float s_nrm[4];
+    const int units = nh * vtiles;
+    int unit, mt;
+    if (!decode_tile(blockIdx.x, mtiles, units, unit, mt)) return;
+    // heads interleaved in dispatch order, so the first blocks to finish tighten every head's bounds
+    const int hh = unit % nh, vt = unit / nh;
+    const int v0 = vt * VR, m0 = mt * VM;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int g4 = lane >> 4, c16 = lane & 15, wr = w >> 1, wc = w & 1;
+    const int64_t hbase = (int64_t)hh * M * d;
+
+    const int r0 = 16 * w + (lane >> 2);
+    const uint32_t voff0 = (uint32_t)r0 * d * 2 + 16 * ((lane & 3) ^ ((r0 >> 1) & 3));
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(U + ((int64_t)(head0 + hh) * V + v0) * d), 0, min(V - v0, VR) * d * 2, RSRC3);
+    const __amdgpu_buffer_rsrc_t rH =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(hhi + hbase + (int64_t)m0 * d), 0, min(M - m0, VM) * d * 2, RSRC3);
+    auto issue = [&](int k0, unsigned char* base) {
+#pragma unroll
+        for (int j = 0; j < NPA; ++j) dmab(rA, base + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
+#pragma unroll
+        for (int j = 0; j < NPB; ++j) dmab(rH, base + A_BYTES + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
+    };
+
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // Gram blocks A A^T of this wave's operand rows 16 (4 wc + j) .. + 15 (j < 4):
+    // their diagonals are the squared row norms of U over the whole contraction
+    f32x4 gram[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) gram[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int slot = (g4 ^ ((c16 >> 1) & 3)) * 16;
+    auto compute = [&](const unsigned char* sA) {
+        const unsigned char* sB = sA + A_BYTES;
+        bf16x8 a[8];
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb)
+            a[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sA + (128 * wr + 16 * rb + c16) * ROWB + slot));
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const bf16x8 b =
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sB + (64 * wc + 16 * cb + c16) * ROWB + slot));
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb)
+                acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b, acc[rb][cb], 0, 0, 0);
+        }
+        // the two waves of a row band split its Gram blocks: wc takes row blocks 4 wc .. 4 wc + 3
+        if (wc == 0) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) gram[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], a[j], gram[j], 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                gram[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[4 + j], a[4 + j], gram[j], 0, 0, 0);
+        }
+    };
+
+    const int nk = d / VK;
+    issue(0, sbuf0);
+    for (int ks = 0; ks < nk; ks += 2) {
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        issue((ks + 1) * VK, sbuf1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sbuf0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();
+        issue(min(ks + 2, nk - 1) * VK, sbuf0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(sbuf1);
+    }
+    // the tile's largest squared row norm (rows past V loaded nothing: norm 0).
+    // Lane (g4, c16) holds Gram rows 4 g4 + i of column c16: the diagonal entry
+    // when c16 - 4 g4 = i is in 0..3.
+    {
+        float mx = 0.f;
+        const int di = c16 - 4 * g4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float dv = di == 0 ? gram[j][0] : di == 1 ? gram[j][1] : di == 2 ? gram[j][2] : di == 3 ? gram[j][3] : 0.f;
+            mx = fmaxf(mx, dv);
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        if (lane == 0) s_nrm[w] = mx;
+    }
+    __syncthreads();
+    if (tid < VM) {
+        const int m = m0 + tid;
+        if (m < M) {
+            const float N = sqrtf(fmaxf(fmaxf(s_nrm[0], s_nrm[1]), fmaxf(s_nrm[2], s_nrm[3]))) * (1.f + 0x1p-10f);
+            const int row = hh * M + m;
+            s_E[tid] = N * (lo_norm[row] + 0x1p-14f * h_norm[row]);
+            s_bound[tid] = o2f(__hip_atomic_load(bound + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+        } else {
+            s_E[tid] = 0.f;
+            s_bound[tid] = INFINITY;
+        }
+    }
+    for (int h = 0; h < 2; ++h) {
+        __syncthreads();
+        if (wr == h) {
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb)
+#pragma unroll
+                for (int cb = 0; cb < 4; ++cb) {
+                    const int col = 64 * wc + 16 * cb + c16;
+                    *reinterpret_cast<f32x4*>((wc ? sbuf1 : sbuf0) + (col & 63) * 512 + (((4 * rb + g4) ^ (col & 15)) * 16)) =
+                        acc[rb][cb];
+                }
+        }
+        __syncthreads();
+        const int vh = v0 + 128 * h;
+        for (int col = w; col < VM; col += 4) {
+            const int m = m0 + col;
+            if (m >= M) break;  // uniform
+            const int row = hh * M + m;
+            const int k = kk.v[Mh > 0 ? min(m / Mh, 7) : hh];
+            const float E = s_E[col];
+            const float lim = s_bound[col] - E;  // entries below cannot reach the top k
+            const unsigned char* Sc = (col < 64 ? sbuf0 : sbuf1) + (col & 63) * 512;
+            float x0[2];
+            int cnt = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int rr = lane + 64 * e;
+                x0[e] = vh + rr < V ? *reinterpret_cast<const float*>(Sc + (((rr >> 2) ^ (col & 15)) * 16) + (rr & 3) * 4)
+                                    : -INFINITY;
+                if (x0[e] < lim) x0[e] = -INFINITY;
+                cnt += __popcll(__ballot(x0[e] != -INFINITY));
+            }
+            if (cnt == 0) continue;  // uniform
+            // This half tile's best entry is within E of a logit it bounds from
+            // below: it raises slot (half-tile id % 64) of the row. The k-th
+            // largest slot comes from k distinct entries, so it bounds the row's
+            // k-th best logit from below; it only moves when a slot does.
+            float best = fmaxf(x0[0], x0[1]);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) best = fmaxf(best, __shfl_xor(best, o, 64));
+            float thr = lim;
+            int old = 0;
+            if (lane == 0) old = atomicMax(slots + (int64_t)row * kSlots + ((2 * vt + h) & (kSlots - 1)), f2o(best - E));
+            old = __shfl(old, 0, 64);
+            if (f2o(best - E) > old) {  // uniform: the slot rose; recompute the k-th largest slot
+                float sv = o2f(__hip_atomic_load(slots + (int64_t)row * kSlots + lane, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT));
+                float kth = -INFINITY;
+                for (int r = 0; r < k; ++r) {
+                    float bv = sv;
+                    int bl = lane;
+#pragma unroll
+                    for (int o = 32; o > 0; o >>= 1) {
+                        const float tv = __shfl_xor(bv, o, 64);
+                        const int tl = __shfl_xor(bl, o, 64);
+                        if (tv > bv || (tv == bv && tl < bl)) {
+                            bv = tv;
+                            bl = tl;
+                        }
+                    }
+                    kth = bv;
+                    if (bl == lane) sv = -INFINITY;
+                }
+                if (kth != -INFINITY) {
+                    if (lane == 0) atomicMax(bound + row, f2o(kth));
+                    thr = fmaxf(thr, kth - E);
+                }
+            }
+            // append every entry >= thr (value + E is its upper bound)
+            const uint64_t b0 = __ballot(x0[0] != -INFINITY && x0[0] >= thr);
+            const uint64_t b1 = __ballot(x0[1] != -INFINITY && x0[1] >= thr);
+            const int n0 = __popcll(b0), n = n0 + __popcll(b1);
+            int base = 0;
+            if (lane == 0) base = atomicAdd(count + row, n);
+            base = __shfl(base, 0, 64);
+            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+            if ((b0 >> lane) & 1) {
+                const int p = base + __popcll(b0 & below);
+                if (p < kCertCap) {
+                    cand_ub[(int64_t)row * kCertCap + p] = x0[0] + E;
+                    cand_lb[(int64_t)row * kCertCap + p] = x0[0] - E;
+                    cand_idx[(int64_t)row * kCertCap + p] = vh + lane;
+                }
+            }
+            if ((b1 >> lane) & 1) {
+                const int p = base + n0 + __popcll(b1 & below);
+                if (p < kCertCap) {
+                    cand_ub[(int64_t)row * kCertCap + p] = x0[1] + E;
+                    cand_lb[(int64_t)row * kCertCap + p] = x0[1] - E;
+                    cand_idx[(int64_t)row * kCertCap + p] = vh + lane + 64;
+                }
+            }
+        }
+    }
+}
+
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 __global__ void k_fill_bound(int* __restrict__ bound, int n) {
@@ -747,36 +1225,80 @@ int residual_ksplit(int M, int d, int din, int nh) {
     return ks;
 }
 
-size_t heads_mfma_ws_bytes(int M, int d, int din, int V, int nh, int kmax) {
-    const size_t vtiles = (size_t)(V + VR - 1) / VR;
-    const size_t e = (size_t)nh * M * d;
+// Workspace: h' (float32, hi, lo), the per-row bounds, the split-contraction
+// partials, then either the narrow kernel's partial lists or the certified
+// pass's norms, slots and candidate buffers.
+struct MfmaWs {
+    float* hres;
+    uint16_t *hhi, *hlo;
+    int* bound;
+    float* zpart;
+    float *pv;  // narrow: partial lists [rows][vtiles][kmax]
+    int* pi;
+    float *lo_norm, *h_norm;  // certified: per row
+    int *count, *slots;
+    float *cand_ub, *cand_lb;
+    int* cand_idx;
+    size_t bytes;
+};
+
+MfmaWs mfma_ws_layout(char* base, int M, int d, int din, int V, int nh, int kmax, bool certified) {
+    MfmaWs L = {};
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        char* p = base ? base + off : nullptr;
+        off += align256(n);
+        return p;
+    };
+    const size_t e = (size_t)nh * M * d, rows = (size_t)nh * M;
     const int ks = residual_ksplit(M, d, din, nh);
-    return align256(e * 4) + 2 * align256(e * 2) + 2 * align256((size_t)nh * M * 2 * vtiles * kmax * 4) +
-           align256((size_t)nh * M * 4) + (ks > 1 ? align256((size_t)ks * e * 4) : 0);
+    L.hres = reinterpret_cast<float*>(take(e * 4));
+    L.hhi = reinterpret_cast<uint16_t*>(take(e * 2));
+    L.hlo = reinterpret_cast<uint16_t*>(take(e * 2));
+    L.bound = reinterpret_cast<int*>(take(rows * 4));
+    L.zpart = ks > 1 ? reinterpret_cast<float*>(take((size_t)ks * e * 4)) : nullptr;
+    if (!certified) {
+        const size_t lists = rows * (size_t)((V + VR - 1) / VR) * kmax * 4;
+        L.pv = reinterpret_cast<float*>(take(lists));
+        L.pi = reinterpret_cast<int*>(take(lists));
+    } else {
+        L.lo_norm = reinterpret_cast<float*>(take(rows * 4));
+        L.h_norm = reinterpret_cast<float*>(take(rows * 4));
+        L.count = reinterpret_cast<int*>(take(rows * 4));
+        L.slots = reinterpret_cast<int*>(take(rows * kSlots * 4));
+        L.cand_ub = reinterpret_cast<float*>(take(rows * kCertCap * 4));
+        L.cand_lb = reinterpret_cast<float*>(take(rows * kCertCap * 4));
+        L.cand_idx = reinterpret_cast<int*>(take(rows * kCertCap * 4));
+    }
+    L.bytes = off;
+    return L;
 }
 
-// Launches phase 1 and phase 2; the caller merges the lists (two per vocabulary tile).
+// the certified pass runs when the vocabulary GEMM sees more than kNarrowRows rows
+bool certified_rows(int M, int nh, int shared_u) { return (shared_u ? nh * M : M) > kNarrowRows; }
+
+size_t heads_mfma_ws_bytes(int M, int d, int din, int V, int nh, int kmax, int shared_u) {
+    return mfma_ws_layout(nullptr, M, d, din, V, nh, kmax, certified_rows(M, nh, shared_u)).bytes;
+}
+
+// Launches phase 1 and phase 2. With few rows the caller merges the lists
+// (*nlists of them per row); with many rows the certified pass writes the
+// top-k lists itself (*nlists = 0).
 hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                              float** part_val, int** part_idx, int* nlists) {
     const int vtiles = (a.V + VR - 1) / VR;
     const int mtiles = (a.M + TM - 1) / TM;
-    char* w = reinterpret_cast<char*>(a.ws);
-    const size_t e = (size_t)a.nh * a.M * a.d;
-    float* hres = reinterpret_cast<float*>(w);
-    w += align256(e * 4);
-    uint16_t* hhi = reinterpret_cast<uint16_t*>(w);
-    w += align256(e * 2);
-    uint16_t* hlo = reinterpret_cast<uint16_t*>(w);
-    w += align256(e * 2);
-    float* pv = reinterpret_cast<float*>(w);
-    w += align256((size_t)a.nh * a.M * 2 * vtiles * a.kmax * 4);
-    int* pi = reinterpret_cast<int*>(w);
-    w += align256((size_t)a.nh * a.M * 2 * vtiles * a.kmax * 4);
-    int* bound = reinterpret_cast<int*>(w);
-    w += align256((size_t)a.nh * a.M * 4);
-    float* zpart = reinterpret_cast<float*>(w);  // split contraction partials (when ksplit > 1)
+    const bool cert = certified_rows(a.M, a.nh, a.shared_u);
+    const MfmaWs L = mfma_ws_layout(reinterpret_cast<char*>(a.ws), a.M, a.d, a.din, a.V, a.nh, a.kmax, cert);
+    const size_t e = (size_t)a.nh * a.M * a.d, crow = (size_t)a.nh * a.M;
     KW kk;
     for (int i = 0; i < 8; ++i) kk.v[i] = i < a.nh ? a.kk[i] : 1;
+    hipError_t err;
+    if (cert) {
+        hipLaunchKernelGGL(k_cert_prep, dim3((unsigned)((crow * kSlots + 255) / 256)), dim3(256), 0, s, L.bound, L.slots,
+                           L.count, (int)crow);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
 
     GemmRows rows;
     rows.kind = a.kind;
@@ -799,13 +1321,17 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     const uint16_t* bias = reinterpret_cast<const uint16_t*>(a.b);
     hipLaunchKernelGGL(k_residual_mfma, dim3(ksplit * 8 * mtiles * ((units1 + 7) / 8)), dim3(BLOCK), 0, s,
                        reinterpret_cast<const uint16_t*>(a.W), bias, rows, a.M, a.d, a.din, a.nh, a.head0, mtiles,
-                       ksplit, zpart, hres, a.h_res, hhi, hlo, bound);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+                       ksplit, L.zpart, L.hres, a.h_res, L.hhi, L.hlo, L.bound);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ksplit > 1) {
         const int64_t quads = e / 4;
-        hipLaunchKernelGGL(k_residual_finish, dim3((unsigned)((quads + BLOCK - 1) / BLOCK)), dim3(BLOCK), 0, s, zpart,
-                           ksplit, bias, rows, a.M, a.d, a.nh, a.head0, hres, a.h_res, hhi, hlo);
+        hipLaunchKernelGGL(k_residual_finish, dim3((unsigned)((quads + BLOCK - 1) / BLOCK)), dim3(BLOCK), 0, s, L.zpart,
+                           ksplit, bias, rows, a.M, a.d, a.nh, a.head0, L.hres, a.h_res, L.hhi, L.hlo);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    if (cert) {
+        hipLaunchKernelGGL(k_row_norms, dim3((unsigned)((crow + 3) / 4)), dim3(BLOCK), 0, s, L.hres, (int)crow, a.d,
+                           L.lo_norm, L.h_norm);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
@@ -814,20 +1340,27 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     const int units2 = nh_u * vtiles;
     const uint16_t* U = reinterpret_cast<const uint16_t*>(a.U);
     const int head0 = a.shared_u ? 0 : a.head0, Mh = a.shared_u ? a.M : 0;
-    if (rows_v <= kNarrowRows) {  // few rows: HBM-bound, the deeper pipeline wins
+    if (!cert) {  // few rows: HBM-bound, two products and the deeper pipeline
         const int nmt = (rows_v + NM - 1) / NM;
-        hipLaunchKernelGGL(k_vocab_mfma_narrow<2>, dim3(8 * nmt * ((units2 + 7) / 8)), dim3(BLOCK), 0, s, U, hhi, hlo,
-                           rows_v, a.d, a.V, nh_u, head0, vtiles, nmt, a.kmax, kk, Mh, pv, pi, bound);
+        hipLaunchKernelGGL(k_vocab_mfma_narrow<2>, dim3(8 * nmt * ((units2 + 7) / 8)), dim3(BLOCK), 0, s, U, L.hhi,
+                           L.hlo, rows_v, a.d, a.V, nh_u, head0, vtiles, nmt, a.kmax, kk, Mh, L.pv, L.pi, L.bound);
         *nlists = vtiles;
-    } else {
+    } else {  // many rows: one product and the certificate
         const int vmtiles = (rows_v + VM - 1) / VM;
-        hipLaunchKernelGGL(k_vocab_mfma<2>, dim3(8 * vmtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s, U, hhi, hlo,
-                           rows_v, a.d, a.V, nh_u, head0, vtiles, vmtiles, a.kmax, kk, Mh, pv, pi, bound);
-        *nlists = 2 * vtiles;
+        hipLaunchKernelGGL(k_vocab_mfma_cert, dim3(8 * vmtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s, U, L.hhi,
+                           rows_v, a.d, a.V, nh_u, head0, vtiles, vmtiles, kk, Mh, L.lo_norm, L.h_norm, L.bound,
+                           L.slots, L.count, L.cand_ub, L.cand_lb, L.cand_idx);
+        *nlists = 0;
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (ev1 && (err = hipEventRecord(ev1, s)) != hipSuccess) return err;
-    *part_val = pv;
-    *part_idx = pi;
+    if (cert) {
+        hipLaunchKernelGGL(k_rescore, dim3((unsigned)crow), dim3(BLOCK), 0, s, U, L.hhi, L.hlo, a.M, a.d, a.V, a.nh,
+                           a.head0, a.shared_u, kk, a.kmax, L.bound, L.count, L.cand_ub, L.cand_lb, L.cand_idx,
+                           a.topk_idx, a.topk_val);
+        if ((err = hipGetLastError()) != hipSuccess) return err;
+    }
+    *part_val = L.pv;
+    *part_idx = L.pi;
     return hipSuccess;
 }

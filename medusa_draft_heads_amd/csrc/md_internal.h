@@ -53,7 +53,7 @@ size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, in
 size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u);  // any plan of these sizes
 // matrix-core path for many rows (heads_mfma.hip)
 bool heads_mfma_applicable(int dt, int M, int d, int din);
-size_t heads_mfma_ws_bytes(int M, int d, int din, int V, int nh, int kmax);
+size_t heads_mfma_ws_bytes(int M, int d, int din, int V, int nh, int kmax, int shared_u);
 hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                              float** part_val, int** part_idx, int* nlists);
 hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);

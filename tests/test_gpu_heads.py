@@ -242,3 +242,53 @@ def test_heads_shared_projection_many_rows_sampled():
     ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, rows=rows, want_logits=True)
     compare_medusa(wl, gi[rows], gv[rows], gh[:, rows], ref, label="%s M=%d rows %s" % (wl.name, M, rows))
     del wd
+
+
+# ------------------------------------------------------------- edge cases
+
+EIGHT = Workload("eight heads: d=256 V=3001 K=8", "medusa", B=1, d=256, V=3001, K=8, dtype="bf16",
+                 topk=(16, 9, 5, 4, 3, 2, 1, 1), N=10, Hq=4, Hkv=1, hd=64, L=10)
+
+
+@pytest.mark.parametrize("M", [2, 16])
+def test_heads_eight_heads(M):
+    """The largest head count the boundary takes (K = 8), on the GEMV (2 rows) and MFMA (16 rows) paths."""
+    wl = EIGHT
+    w = weights(wl, 4000 + M)
+    h = synth.normal(4000 + M, 81, (M, wl.d), 1.0, wl.dtype)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), M)
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, want_logits=True)
+    compare_medusa(wl, gi, gv, gh, ref, label="K=8 M=%d" % M)
+
+
+def test_heads_many_rows_without_matrix_cores():
+    """Nine bf16 rows at d = 200 (not a whole number of 128-wide tiles): the GEMV path in several passes."""
+    wl = Workload("d=200 bf16", "medusa", B=1, d=200, V=2500, K=2, dtype="bf16", topk=(7, 3), N=4, Hq=4, Hkv=1,
+                  hd=64, L=10)
+    M = 9
+    w = weights(wl, 4100)
+    h = synth.normal(4100, 82, (M, wl.d), 1.0, wl.dtype)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), M)
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, want_logits=True)
+    compare_medusa(wl, gi, gv, gh, ref, label="d=200 M=9")
+
+
+@pytest.mark.parametrize("V", [3000, 10000])
+def test_heads_many_rows_all_logits_tied(V):
+    """Every vocabulary row equal: every logit of a row ties, so the certified pass over 136 rows keeps
+    more than 512 survivors (V = 3000) or overflows its candidate buffer (V = 10000); both fall back to
+    the exact scan and must return the lowest indices."""
+    wl = Workload("tied vocabulary", "medusa", B=1, d=256, V=V, K=2, dtype="bf16", topk=(5, 3), N=4, Hq=4, Hkv=1,
+                  hd=64, L=10)
+    M = 136
+    w = weights(wl, 4200)
+    w["U"][:] = w["U"][:, :1, :]  # one row repeated
+    h = synth.normal(4200, 83, (M, wl.d), 1.0, wl.dtype)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), M)
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, want_logits=True)
+    compare_medusa(wl, gi, gv, gh, ref, label="tied V=%d" % V)
+    for k, kk in enumerate(wl.topk):
+        assert np.all(gi[:, k, :kk] == np.arange(kk))
