@@ -17,7 +17,10 @@ pages give them:
 * greedy acceptance and the cache entries of the accepted branch -- same
   page, "Trees" and "Acceptance";
 * Hydra heads -- the Hydra summary and abstract: each head also sees the
-  token speculated before it.
+  token speculated before it;
+* sampled decoding -- same page, "Training": rejection sampling with the
+  heads' probabilities (exact) and typical acceptance (not exact); the
+  readings for a tree are stated at that section below.
 
 bf16 arrays are numpy uint16 bit patterns; float32 arrays are float32.
 """
@@ -332,3 +335,197 @@ def step_medusa(wl, wts: Dict[str, np.ndarray], inp: Dict[str, np.ndarray], topo
     Kc2, Vc2, lens2 = compact(inp["Kc"], inp["Vc"], inp["lens"], acc["accept_len"], acc["path"], K)
     return {"heads": heads, "tree_tok": tok, "tree_pos": pos, "attn": out, "tstar": tstar, **acc,
             "Kc": Kc2, "Vc": Vc2, "lens": lens2}
+
+
+# ------------------------------------------------ sampled decoding
+#
+# "Medusa heads versus separate draft model", Training: for sampled decoding
+# at a temperature, an exact match of the target's distribution needs
+# standard rejection sampling with the heads' probabilities; Medusa's
+# "typical acceptance" takes more drafts but gives that up. The pages do not
+# spell out either procedure on a tree; the readings taken here:
+#
+# * a head's draft distribution is q = softmax(logits / T), the target's at
+#   node n is p_n = softmax(target_logits[n] / T);
+# * a head's draft tokens are a sample of k distinct tokens from q in draw
+#   order (Gumbel-top-k: the k largest of logits / T + Gumbel noise);
+# * verification walks down from the root; at a node, its children are tried
+#   in rank order with the rejection rule for candidates drawn without
+#   replacement: accept child x with probability min(1, p(x) / q(x)); on
+#   rejection p <- normalise(max(0, p - q)) and x leaves q (q renormalised).
+#   An accepted child becomes the node; when every child is rejected, or the
+#   node is a leaf, the step's last token is drawn from the current p;
+# * typical acceptance: a node matches when its parent's p gives its token
+#   more than min(eps, delta * exp(-entropy(p))); the deepest node whose
+#   whole root path matches ends the step, and the last token is drawn from
+#   that node's p.
+#
+# Random numbers come in as 32-bit words: uniforms u = (w / 2^9 + 1/2) 2^-23
+# in (0, 1) and Gumbel noise -log(-log u).
+
+
+def unit_from_words(w) -> np.ndarray:
+    """Uniforms in the open interval (0, 1): the top 23 bits of each word plus one half, times 2^-23."""
+    w = np.asarray(w, dtype=np.uint32)
+    return ((w >> np.uint32(9)).astype(np.float64) + 0.5) * 2.0 ** -23
+
+
+def gumbel_from_words(w) -> np.ndarray:
+    """Standard Gumbel noise -log(-log u) of the uniforms above."""
+    return -np.log(-np.log(unit_from_words(w)))
+
+
+def softmax_t(x, T: float) -> np.ndarray:
+    z = np.asarray(x, dtype=np.float64) / T
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def logsumexp_t(x, T: float) -> float:
+    z = np.asarray(x, dtype=np.float64) / T
+    m = z.max()
+    return float(m + np.log(np.exp(z - m).sum()))
+
+
+def _order_desc(s: np.ndarray) -> np.ndarray:
+    """Indices by (value desc, index asc)."""
+    return np.lexsort((np.arange(s.size), -s))
+
+
+def draft_sample(logits: np.ndarray, words: np.ndarray, topk: Sequence[int], T: float) -> Dict[str, np.ndarray]:
+    """Per (row, head): k_head distinct tokens drawn without replacement from
+    softmax(logits / T), in draw order (the k largest of logits / T + Gumbel
+    noise), and log sum exp(logits / T).
+
+    logits [R, K, V], words [R, K, V] uint32. Returns tok [R, K, kmax] (-1
+    padded), score [R, K, kmax] (the perturbed values), lse [R, K] and
+    margin [R, K]: the smallest gap among the k + 1 best perturbed values.
+    """
+    R, K, V = logits.shape
+    kmax = max(topk)
+    tok = np.full((R, K, kmax), -1, dtype=np.int32)
+    score = np.full((R, K, kmax), -np.inf)
+    lse = np.empty((R, K))
+    margin = np.empty((R, K))
+    for r in range(R):
+        for k in range(K):
+            s = np.asarray(logits[r, k], dtype=np.float64) / T + gumbel_from_words(words[r, k])
+            o = _order_desc(s)
+            kk = topk[k]
+            tok[r, k, :kk] = o[:kk]
+            score[r, k, :kk] = s[o[:kk]]
+            top = s[o[: min(kk + 1, V)]]
+            margin[r, k] = np.min(top[:-1] - top[1:]) if top.size > 1 else np.inf
+            lse[r, k] = logsumexp_t(logits[r, k], T)
+    return {"tok": tok, "score": score, "lse": lse, "margin": margin}
+
+
+def _children(parent: Sequence[int]):
+    ch = [[] for _ in parent]
+    for n in range(1, len(parent)):
+        ch[parent[n]].append(n)  # breadth-first numbering: siblings in rank order
+    return ch
+
+
+def _gumbel_max(p: np.ndarray, gw: np.ndarray):
+    """A draw from p (Gumbel-max over log p) and the gap between the two best perturbed values."""
+    with np.errstate(divide="ignore"):
+        s = np.log(p) + gumbel_from_words(gw)
+    o = _order_desc(s)
+    gap = s[o[0]] - s[o[1]] if s.size > 1 else np.inf
+    return int(o[0]), float(gap)
+
+
+def verify_sampled(parent: Sequence[int], tree_tok: np.ndarray, target_logits: np.ndarray, head_logits: np.ndarray,
+                   T: float, u_words: np.ndarray, g_words: np.ndarray) -> Dict[str, np.ndarray]:
+    """Rejection-sampling verification of the tree (readings above).
+
+    tree_tok [B, N]; target_logits [B, N, V] (the target at every node);
+    head_logits [B, K, V] (the heads that drafted request b's tree: head i
+    supplies the depth-(i+1) tokens); u_words [B, N] (node n's acceptance
+    test); g_words [B, V] (the final draw). Returns chosen [B, N] (the token
+    emitted after each node the walk passed through, -1 elsewhere; node a's
+    entry is the step's last token) and margin [B]: the smallest distance
+    between a test's uniform and its acceptance probability, and the gap of
+    the final draw's two best perturbed values.
+    """
+    B, N = tree_tok.shape
+    dep = _depths(parent)
+    ch = _children(parent)
+    chosen = np.full((B, N), -1, dtype=np.int32)
+    margin = np.full(B, np.inf)
+    for b_ in range(B):
+        node = 0
+        while True:
+            p = softmax_t(target_logits[b_, node], T)
+            kids = ch[node]
+            q = softmax_t(head_logits[b_, dep[node]], T) if kids else None
+            nxt = None
+            for c in kids:
+                x = int(tree_tok[b_, c])
+                u = float(unit_from_words(u_words[b_, c]))
+                a = min(1.0, p[x] / q[x]) if q[x] > 0.0 else 1.0
+                margin[b_] = min(margin[b_], abs(u - a))
+                if u < a:
+                    nxt = c
+                    break
+                r = np.maximum(p - q, 0.0)
+                p = r / r.sum()
+                q = q.copy()
+                q[x] = 0.0
+                q = q / q.sum()
+            if nxt is not None:
+                chosen[b_, node] = tree_tok[b_, nxt]
+                node = nxt
+                continue
+            y, gap = _gumbel_max(p, g_words[b_])
+            chosen[b_, node] = y
+            margin[b_] = min(margin[b_], gap)
+            break
+    return {"chosen": chosen, "margin": margin}
+
+
+def typical_accept(parent: Sequence[int], tree_tok: np.ndarray, target_logits: np.ndarray, T: float, eps: float,
+                   delta: float, g_words: np.ndarray) -> Dict[str, np.ndarray]:
+    """Typical acceptance (reading above). Returns chosen [B, N] as
+    verify_sampled does, match [B, N] (bool), the threshold and p(token) of
+    every non-root node, and margin [B]: the smallest |p(token) - threshold|
+    and the final draw's gap."""
+    B, N = tree_tok.shape
+    dep = _depths(parent)
+    chosen = np.full((B, N), -1, dtype=np.int32)
+    match = np.zeros((B, N), dtype=bool)
+    thr = np.full((B, N), np.nan)
+    ptok = np.full((B, N), np.nan)
+    margin = np.full(B, np.inf)
+    for b_ in range(B):
+        P = {}
+        for n in range(1, N):
+            a = parent[n]
+            if a not in P:
+                p = softmax_t(target_logits[b_, a], T)
+                with np.errstate(divide="ignore", invalid="ignore"):
+                    H = -np.sum(np.where(p > 0.0, p * np.log(p), 0.0))
+                P[a] = (p, min(eps, delta * np.exp(-H)))
+            p, t = P[a]
+            thr[b_, n] = t
+            ptok[b_, n] = p[tree_tok[b_, n]]
+            match[b_, n] = ptok[b_, n] > t
+            margin[b_] = min(margin[b_], abs(ptok[b_, n] - t))
+        # deepest node whose whole root path matches; lowest index among equals
+        best = 0
+        for n in range(1, N):
+            ok, c = True, n
+            while c > 0:
+                ok &= bool(match[b_, c])
+                c = parent[c]
+            if ok and dep[n] > dep[best]:
+                best = n
+        c = best
+        while c > 0:
+            chosen[b_, parent[c]] = tree_tok[b_, c]
+            c = parent[c]
+        y, gap = _gumbel_max(softmax_t(target_logits[b_, best], T), g_words[b_])
+        chosen[b_, best] = y
+        margin[b_] = min(margin[b_], gap)
+    return {"chosen": chosen, "match": match, "thr": thr, "ptok": ptok, "margin": margin}
