@@ -211,6 +211,90 @@ int md_tree_accept_tokens(const md_tree* tree, int dt, int B, int K, int Hkv, in
                           const int32_t* target_tok, const int32_t* tree_tok, void* Kc, void* Vc, int32_t* lens,
                           int32_t* accept_len, int32_t* path, int32_t* next_tok, int32_t* compact_src, void* stream);
 
+/* ---------------------------------------------------------------- sampled decoding
+ *
+ * "Medusa heads versus separate draft model", section "Training": with
+ * sampling at a temperature T, rejection sampling with the heads'
+ * probabilities keeps the target's distribution exactly; "typical
+ * acceptance" takes more drafts and does not. The pages give neither rule on
+ * a tree; the calls below implement these readings:
+ *   q_i = softmax(l_i / T) is head i's draft distribution, p_n =
+ *   softmax(target_logits[n] / T) the target's at node n;
+ *   head i's draft tokens are k_i distinct tokens drawn from q_i without
+ *   replacement, in draw order (md_draft_sample); they fill the tree exactly
+ *   as top-k lists do (md_tree_build);
+ *   verification (md_tree_verify_sampled) walks from the root and tries a
+ *   node's children in rank order, accepting child x with probability
+ *   min(1, p(x) / q(x)); on rejection p <- normalise(max(0, p - q)) and x
+ *   leaves q (renormalised). An accepted child becomes the node; with every
+ *   child rejected, or at a leaf, the step's last token is drawn from p;
+ *   typical acceptance (md_tree_accept_typical): node n matches when its
+ *   parent's p gives tok(n) more than min(eps, delta * exp(-H(p))), H the
+ *   entropy; the deepest node whose root path matches (lowest index among
+ *   equals) ends the step and its p gives the last token;
+ *   a tree token outside [0, V) is never accepted and changes nothing.
+ * Random numbers are inputs: 32-bit words w give uniforms
+ * u = (floor(w / 2^9) + 1/2) * 2^-23 in (0, 1) and Gumbel noise -log(-log u);
+ * draws from a distribution are Gumbel-max (the largest log-probability plus
+ * noise), ties to the lowest index. The caller supplies fresh words for every
+ * step. Temperatures must be positive and finite. */
+
+/* Workspace for md_medusa_heads_logits. */
+size_t md_heads_logits_workspace_bytes(int kind, int M, int d, int K);
+
+/* md_medusa_heads (Medusa kinds only) writing every logit instead of the top-k:
+ * logits [M][K][V] (device float32), logits[m][i][v] = U_i[v] . h'_i(m).
+ * Same inputs, checks and errors; the GEMV path at any M. */
+int md_medusa_heads_logits(int kind, int dt, int M, int d, int V, int K, const void* h, const void* W, const void* b,
+                           const void* U, float* logits, float* h_res, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace for md_draft_sample. */
+size_t md_draft_sample_workspace_bytes(int M, int K, int V, int kmax);
+
+/* Draft tokens drawn from the heads: for every (row m, head i), the k_i
+ * largest of logits[m][i][v] / T + G(words[m][i][v]) by (value desc, index
+ * asc), i.e. k_i distinct tokens drawn without replacement from
+ * softmax(logits / T) in draw order, written to tok[m][i][0..k_i) (device
+ * int32 [M][K][kmax], -1 padded; the layout of md_medusa_heads' topk_idx),
+ * and lse[m][i] = log sum_v exp(logits[m][i][v] / T) (device float32 [M][K]).
+ * logits, words: device [M][K][V]. Errors: MD_EINVAL (sizes, k_per_head
+ * outside 1..16 or above V, T not positive, NULL pointers), MD_EWORKSPACE. */
+int md_draft_sample(int M, int K, int V, const int32_t* k_per_head, float temperature, const float* logits,
+                    const uint32_t* words, int32_t* tok, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace for md_tree_verify_sampled. */
+size_t md_verify_sampled_workspace_bytes(int B, int N);
+
+/* Rejection-sampling verification, acceptance and cache compaction.
+ * target_logits [B][N][V] (device float32: the target at every node);
+ * head_logits [B][K][V] and head_lse [B][K] (device float32: the heads that
+ * drafted request b's tree and their log-sum-exp at T, as md_draft_sample
+ * gives them); u_words [B][N] (device uint32: word of node n's acceptance
+ * test); g_words [B][V] (device uint32: the last token's draw). The accepted
+ * path, accept_len, path, next_tok (the step's last token), compact_src and
+ * the cache update are as md_tree_accept defines them for the path this walk
+ * takes. Errors as md_tree_accept's, and MD_EINVAL for T. */
+int md_tree_verify_sampled(const md_tree* tree, int dt, int B, int K, int V, int Hkv, int hd, int Lcap,
+                           float temperature, const float* target_logits, const float* head_logits,
+                           const float* head_lse, const int32_t* tree_tok, const uint32_t* u_words,
+                           const uint32_t* g_words, void* Kc, void* Vc, int32_t* lens, int32_t* accept_len,
+                           int32_t* path, int32_t* next_tok, int32_t* compact_src, void* ws, size_t ws_bytes,
+                           void* stream);
+
+/* Workspace for md_tree_accept_typical. */
+size_t md_accept_typical_workspace_bytes(int B, int N);
+
+/* Typical acceptance, acceptance and cache compaction (not exact in
+ * distribution). target_logits [B][N][V] (device float32), g_words [B][V]
+ * (device uint32: the last token's draw at the final node); eps, delta >= 0.
+ * Outputs and cache update as md_tree_accept defines them for the node this
+ * rule picks. Errors as md_tree_accept's, and MD_EINVAL for T, eps, delta. */
+int md_tree_accept_typical(const md_tree* tree, int dt, int B, int K, int V, int Hkv, int hd, int Lcap,
+                           float temperature, float eps, float delta, const float* target_logits,
+                           const int32_t* tree_tok, const uint32_t* g_words, void* Kc, void* Vc, int32_t* lens,
+                           int32_t* accept_len, int32_t* path, int32_t* next_tok, int32_t* compact_src, void* ws,
+                           size_t ws_bytes, void* stream);
+
 /* Timing hook for profiling: when both are non-NULL hipEvent_t handles, every
  * later md_medusa_heads call on this thread records `start` on its stream
  * right before its vocabulary-projection kernel and `stop` right after it.

@@ -8,7 +8,10 @@ from ._lib import (MD_BF16, MD_F32, MD_HEADS_HYDRA, MD_HEADS_MEDUSA, MD_HEADS_ME
                    md_accept_workspace_bytes, md_attention_workspace_bytes, md_hbm_read_probe,
                    md_hbm_read_probe_blocks, md_heads_weight_bytes, md_heads_workspace_bytes, md_last_error,
                    md_medusa_heads, md_set_vocab_timing_events, md_target_argmax, md_target_argmax_workspace_bytes,
-                   md_tree, md_tree_accept, md_tree_accept_tokens, md_tree_attention, md_tree_build, md_tree_validate)
+                   md_tree, md_tree_accept, md_tree_accept_tokens, md_tree_attention, md_tree_build, md_tree_validate,
+                   md_heads_logits_workspace_bytes, md_medusa_heads_logits, md_draft_sample_workspace_bytes,
+                   md_draft_sample, md_verify_sampled_workspace_bytes, md_tree_verify_sampled,
+                   md_accept_typical_workspace_bytes, md_tree_accept_typical)
 from .step import MedusaStep, StepConfig
 
 __all__ = [
@@ -17,5 +20,8 @@ __all__ = [
     "md_heads_weight_bytes", "md_heads_workspace_bytes", "md_attention_workspace_bytes", "md_accept_workspace_bytes",
     "md_set_vocab_timing_events", "md_last_error", "md_hbm_read_probe", "md_hbm_read_probe_blocks",
     "md_target_argmax", "md_target_argmax_workspace_bytes", "md_tree_accept_tokens",
+    "md_heads_logits_workspace_bytes", "md_medusa_heads_logits", "md_draft_sample_workspace_bytes", "md_draft_sample",
+    "md_verify_sampled_workspace_bytes", "md_tree_verify_sampled", "md_accept_typical_workspace_bytes",
+    "md_tree_accept_typical",
     "MedusaStep", "StepConfig",
 ]

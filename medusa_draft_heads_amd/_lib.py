@@ -24,6 +24,9 @@ EXPORTS = (
     "md_attention_workspace_bytes", "md_tree_attention", "md_accept_workspace_bytes", "md_tree_accept",
     "md_set_vocab_timing_events", "md_last_error", "md_hbm_read_probe", "md_hbm_read_probe_blocks",
     "md_target_argmax_workspace_bytes", "md_target_argmax", "md_tree_accept_tokens",
+    "md_heads_logits_workspace_bytes", "md_medusa_heads_logits", "md_draft_sample_workspace_bytes", "md_draft_sample",
+    "md_verify_sampled_workspace_bytes", "md_tree_verify_sampled", "md_accept_typical_workspace_bytes",
+    "md_tree_accept_typical",
 )
 
 
@@ -74,6 +77,14 @@ def lib() -> ctypes.CDLL:
             "md_target_argmax_workspace_bytes": ([i, i, i, i], sz),
             "md_target_argmax": ([i, i, i, i] + [vp] * 5 + [sz, vp], i),
             "md_tree_accept_tokens": ([tp, i, i, i, i, i, i] + [vp] * 10, i),
+            "md_heads_logits_workspace_bytes": ([i, i, i, i], sz),
+            "md_medusa_heads_logits": ([i, i, i, i, i, i] + [vp] * 7 + [sz, vp], i),
+            "md_draft_sample_workspace_bytes": ([i, i, i, i], sz),
+            "md_draft_sample": ([i, i, i, vp, f] + [vp] * 5 + [sz, vp], i),
+            "md_verify_sampled_workspace_bytes": ([i, i], sz),
+            "md_tree_verify_sampled": ([tp, i, i, i, i, i, i, i, f] + [vp] * 14 + [sz, vp], i),
+            "md_accept_typical_workspace_bytes": ([i, i], sz),
+            "md_tree_accept_typical": ([tp, i, i, i, i, i, i, i, f, f, f] + [vp] * 11 + [sz, vp], i),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -193,6 +204,59 @@ def md_tree_accept_tokens(tree, dt, B, K, Hkv, hd, Lcap, target_tok, tree_tok, K
                                      _p(Vc), _p(lens), _p(accept_len), _p(path), _p(next_tok), _p(compact_src),
                                      _stream(stream))
     _check(rc)
+
+
+def md_heads_logits_workspace_bytes(kind: int, M: int, d: int, K: int) -> int:
+    return int(lib().md_heads_logits_workspace_bytes(kind, M, d, K))
+
+
+def md_medusa_heads_logits(kind, dt, M, d, V, K, h, W, b, U, logits, h_res, ws, ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().md_medusa_heads_logits(kind, dt, M, d, V, K, _p(h), _p(W), _p(b), _p(U), _p(logits), _p(h_res),
+                                        _p(ws), ws_bytes, _stream(stream)))
+
+
+def md_draft_sample_workspace_bytes(M: int, K: int, V: int, kmax: int) -> int:
+    return int(lib().md_draft_sample_workspace_bytes(M, K, V, kmax))
+
+
+def md_draft_sample(M, K, V, k_per_head, temperature, logits, words, tok, lse, ws, ws_bytes=None, stream=None) -> None:
+    kp = (ctypes.c_int32 * K)(*k_per_head)
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().md_draft_sample(M, K, V, ctypes.cast(kp, ctypes.c_void_p), float(temperature), _p(logits), _p(words),
+                                 _p(tok), _p(lse), _p(ws), ws_bytes, _stream(stream)))
+
+
+def md_verify_sampled_workspace_bytes(B: int, N: int) -> int:
+    return int(lib().md_verify_sampled_workspace_bytes(B, N))
+
+
+def md_tree_verify_sampled(tree, dt, B, K, V, Hkv, hd, Lcap, temperature, target_logits, head_logits, head_lse,
+                           tree_tok, u_words, g_words, Kc, Vc, lens, accept_len, path, next_tok, compact_src, ws,
+                           ws_bytes=None, stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().md_tree_verify_sampled(ctypes.byref(tree), dt, B, K, V, Hkv, hd, Lcap, float(temperature),
+                                        _p(target_logits), _p(head_logits), _p(head_lse), _p(tree_tok), _p(u_words),
+                                        _p(g_words), _p(Kc), _p(Vc), _p(lens), _p(accept_len), _p(path), _p(next_tok),
+                                        _p(compact_src), _p(ws), ws_bytes, _stream(stream)))
+
+
+def md_accept_typical_workspace_bytes(B: int, N: int) -> int:
+    return int(lib().md_accept_typical_workspace_bytes(B, N))
+
+
+def md_tree_accept_typical(tree, dt, B, K, V, Hkv, hd, Lcap, temperature, eps, delta, target_logits, tree_tok, g_words,
+                           Kc, Vc, lens, accept_len, path, next_tok, compact_src, ws, ws_bytes=None,
+                           stream=None) -> None:
+    if ws_bytes is None:
+        ws_bytes = ws.numel() * ws.element_size()
+    _check(lib().md_tree_accept_typical(ctypes.byref(tree), dt, B, K, V, Hkv, hd, Lcap, float(temperature),
+                                        float(eps), float(delta), _p(target_logits), _p(tree_tok), _p(g_words), _p(Kc),
+                                        _p(Vc), _p(lens), _p(accept_len), _p(path), _p(next_tok), _p(compact_src),
+                                        _p(ws), ws_bytes, _stream(stream)))
 
 
 def md_set_vocab_timing_events(start, stop) -> None:

@@ -314,6 +314,146 @@ int md_tree_accept_tokens(const md_tree* tree, int dt, int B, int K, int Hkv, in
                       "md_tree_accept_tokens");
 }
 
+static bool good_temperature(float T) { return T > 0.0f && T <= 3.0e38f; }
+
+size_t md_heads_logits_workspace_bytes(int kind, int M, int d, int K) {
+    if ((kind != MD_HEADS_MEDUSA && kind != MD_HEADS_MEDUSA_SHARED) || M <= 0 || d <= 0 || K <= 0) return 0;
+    return heads_logits_ws_bytes(M, d, K);
+}
+
+int md_medusa_heads_logits(int kind, int dt, int M, int d, int V, int K, const void* h, const void* W, const void* b,
+                           const void* U, float* logits, float* h_res, void* ws, size_t ws_bytes, void* stream) {
+    if (kind != MD_HEADS_MEDUSA && kind != MD_HEADS_MEDUSA_SHARED)
+        return fail(MD_EINVAL, "kind = %d (Medusa kinds only)", kind);
+    if (check_dt(dt)) return MD_EINVAL;
+    if (M < 0 || V < 1) return fail(MD_EINVAL, "M = %d, V = %d", M, V);
+    if (K < 1 || K > MD_MAX_HEADS) return fail(MD_EINVAL, "K = %d heads (1..8 supported)", K);
+    if (d < 8 || d % 8) return fail(MD_EUNSUPPORTED, "d = %d (a positive multiple of 8 is required)", d);
+    if ((size_t)d * 4 > 160 * 1024) return fail(MD_EUNSUPPORTED, "input width %d exceeds one LDS row buffer", d);
+    if (M == 0) return MD_OK;
+    if (!h || !W || !U || !logits || !ws) return fail(MD_EINVAL, "a required pointer is NULL");
+    const size_t need = heads_logits_ws_bytes(M, d, K);
+    if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    HeadsArgs a;
+    memset(&a, 0, sizeof(a));
+    a.kind = 0;
+    a.shared_u = kind == MD_HEADS_MEDUSA_SHARED;
+    a.dt = dt;
+    a.M = M;
+    a.B = M;
+    a.d = d;
+    a.din = d;
+    a.V = V;
+    a.nh = K;
+    a.kmax = 1;
+    for (int i = 0; i < K; ++i) a.kk[i] = 1;
+    a.h = h;
+    a.W = W;
+    a.b = b;
+    a.U = U;
+    a.h_res = h_res;
+    a.ws = ws;
+    a.logits = logits;
+    a.logits_k = K;
+    return hip_status(heads_launch(a, nullptr, (hipStream_t)stream, nullptr, nullptr), "md_medusa_heads_logits");
+}
+
+size_t md_draft_sample_workspace_bytes(int M, int K, int V, int kmax) {
+    if (M <= 0 || K <= 0 || K > MD_MAX_HEADS || V <= 0 || kmax <= 0 || kmax > MD_MAX_TOPK) return 0;
+    return draft_sample_ws_bytes(M, K, V, kmax);
+}
+
+int md_draft_sample(int M, int K, int V, const int32_t* k_per_head, float temperature, const float* logits,
+                    const uint32_t* words, int32_t* tok, float* lse, void* ws, size_t ws_bytes, void* stream) {
+    if (M < 0 || V < 1) return fail(MD_EINVAL, "M = %d, V = %d", M, V);
+    if (K < 1 || K > MD_MAX_HEADS) return fail(MD_EINVAL, "K = %d heads (1..8 supported)", K);
+    if (!k_per_head) return fail(MD_EINVAL, "k_per_head is NULL");
+    int kk[MD_MAX_HEADS], kmax = 0;
+    for (int i = 0; i < K; ++i) {
+        if (k_per_head[i] < 1 || k_per_head[i] > MD_MAX_TOPK)
+            return fail(MD_EINVAL, "k_per_head[%d] = %d (1..16 supported)", i, k_per_head[i]);
+        kk[i] = k_per_head[i];
+        if (kk[i] > kmax) kmax = kk[i];
+    }
+    if (V < kmax) return fail(MD_EINVAL, "V = %d is smaller than the widest draw %d", V, kmax);
+    if (!good_temperature(temperature)) return fail(MD_EINVAL, "temperature %g (positive and finite)", (double)temperature);
+    if (M == 0) return MD_OK;
+    if (!logits || !words || !tok || !lse || !ws) return fail(MD_EINVAL, "a required pointer is NULL");
+    const size_t need = draft_sample_ws_bytes(M, K, V, kmax);
+    if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return hip_status(draft_sample_launch(M, K, V, kk, kmax, temperature, logits, words, tok, lse, ws,
+                                          (hipStream_t)stream),
+                      "md_draft_sample");
+}
+
+// the checks md_tree_accept_tokens makes, shared by the sampled verifiers
+static int check_accept_args(const DevTree& t, int dt, int B, int V, int Hkv, int hd, int Lcap) {
+    if (check_dt(dt)) return MD_EINVAL;
+    if (B < 0 || V < 1 || Hkv < 1 || hd < 1) return fail(MD_EINVAL, "B = %d, V = %d, Hkv = %d, hd = %d", B, V, Hkv, hd);
+    if (hd > 256) return fail(MD_EUNSUPPORTED, "head_dim %d (at most 256)", hd);
+    if (Lcap < t.n) return fail(MD_ERANGE, "Lcap %d is smaller than the tree (%d nodes)", Lcap, t.n);
+    return MD_OK;
+}
+
+size_t md_verify_sampled_workspace_bytes(int B, int N) {
+    if (B <= 0 || N <= 0 || N > MD_MAX_NODES) return 0;
+    return verify_sampled_ws_bytes(B, N);
+}
+
+int md_tree_verify_sampled(const md_tree* tree, int dt, int B, int K, int V, int Hkv, int hd, int Lcap,
+                           float temperature, const float* target_logits, const float* head_logits,
+                           const float* head_lse, const int32_t* tree_tok, const uint32_t* u_words,
+                           const uint32_t* g_words, void* Kc, void* Vc, int32_t* lens, int32_t* accept_len,
+                           int32_t* path, int32_t* next_tok, int32_t* compact_src, void* ws, size_t ws_bytes,
+                           void* stream) {
+    DevTree t;
+    int rc = expand_tree(tree, K, nullptr, &t);
+    if (rc) return rc;
+    rc = check_accept_args(t, dt, B, V, Hkv, hd, Lcap);
+    if (rc) return rc;
+    if (!good_temperature(temperature)) return fail(MD_EINVAL, "temperature %g (positive and finite)", (double)temperature);
+    if (B == 0) return MD_OK;
+    if (!target_logits || !head_logits || !head_lse || !tree_tok || !u_words || !g_words || !Kc || !Vc || !lens ||
+        !accept_len || !path || !next_tok || !compact_src || !ws)
+        return fail(MD_EINVAL, "a required pointer is NULL");
+    const size_t need = verify_sampled_ws_bytes(B, t.n);
+    if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return hip_status(verify_sampled_launch(t, dt, B, K, V, Hkv, hd, Lcap, temperature, target_logits, head_logits,
+                                            head_lse, tree_tok, u_words, g_words, Kc, Vc, lens, accept_len, path,
+                                            next_tok, compact_src, ws, (hipStream_t)stream),
+                      "md_tree_verify_sampled");
+}
+
+size_t md_accept_typical_workspace_bytes(int B, int N) {
+    if (B <= 0 || N <= 0 || N > MD_MAX_NODES) return 0;
+    return accept_typical_ws_bytes(B, N);
+}
+
+int md_tree_accept_typical(const md_tree* tree, int dt, int B, int K, int V, int Hkv, int hd, int Lcap,
+                           float temperature, float eps, float delta, const float* target_logits,
+                           const int32_t* tree_tok, const uint32_t* g_words, void* Kc, void* Vc, int32_t* lens,
+                           int32_t* accept_len, int32_t* path, int32_t* next_tok, int32_t* compact_src, void* ws,
+                           size_t ws_bytes, void* stream) {
+    DevTree t;
+    int rc = expand_tree(tree, K, nullptr, &t);
+    if (rc) return rc;
+    rc = check_accept_args(t, dt, B, V, Hkv, hd, Lcap);
+    if (rc) return rc;
+    if (!good_temperature(temperature)) return fail(MD_EINVAL, "temperature %g (positive and finite)", (double)temperature);
+    if (!(eps >= 0.0f && eps <= 3.0e38f) || !(delta >= 0.0f && delta <= 3.0e38f))
+        return fail(MD_EINVAL, "eps = %g, delta = %g (non-negative and finite)", (double)eps, (double)delta);
+    if (B == 0) return MD_OK;
+    if (!target_logits || !tree_tok || !g_words || !Kc || !Vc || !lens || !accept_len || !path || !next_tok ||
+        !compact_src || !ws)
+        return fail(MD_EINVAL, "a required pointer is NULL");
+    const size_t need = accept_typical_ws_bytes(B, t.n);
+    if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    return hip_status(accept_typical_launch(t, dt, B, K, V, Hkv, hd, Lcap, temperature, eps, delta, target_logits,
+                                            tree_tok, g_words, Kc, Vc, lens, accept_len, path, next_tok, compact_src,
+                                            ws, (hipStream_t)stream),
+                      "md_tree_accept_typical");
+}
+
 int md_hbm_read_probe_blocks(void) { return probe_blocks(); }
 
 int md_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* stream) {

@@ -275,12 +275,15 @@ __global__ __launch_bounds__(BLOCK, 4) void k_residual(const T* __restrict__ W, 
 // row m of hres ([heads][Mh][d] read as [M][d]) belongs to head m / Mh,
 // whose top-k width it takes. NW waves per block share one copy of the MR
 // rows of h' in LDS (4 rows of d = 8,192 take 128 KB, so more waves per block
-// is the only way to more waves per CU).
-template <typename T, int MR, int NW>
+// is the only way to more waves per CU). LOGITS: every logit goes to
+// logits_out [row][Ktot][V] instead (sampled decoding needs the heads' whole
+// distributions), and no lists are kept.
+template <typename T, int MR, int NW, bool LOGITS = false>
 __global__ __launch_bounds__(NW * MD_WAVE) void k_vocab_topk(const T* __restrict__ U, const float* __restrict__ hres,
                                                       int M, int m0, int d, int V, int nh, int head0,
                                                       int wg_per_head, KK kk, int kmax, int Mh,
-                                                      float* __restrict__ part_val, int* __restrict__ part_idx) {
+                                                      float* __restrict__ part_val, int* __restrict__ part_idx,
+                                                      float* __restrict__ logits_out = nullptr, int Ktot = 0) {
     extern __shared__ __align__(16) float xs[];  // [MR][d]; later the wave lists
     const int hh = blockIdx.x / wg_per_head;
     const int wgi = blockIdx.x - hh * wg_per_head;
@@ -322,7 +325,14 @@ __global__ __launch_bounds__(NW * MD_WAVE) void k_vocab_topk(const T* __restrict
 #pragma unroll
             for (int m = 0; m < MR; ++m) {
                 const float s = wave_sum(acc[rr][m]);
-                if (rr < nv && m < mr && ranks_above(s, r + rr, tv[m], ti[m])) {
+                if constexpr (LOGITS) {
+                    if (rr < nv && m < mr && lane == 0) {
+                        const int mv = m0 + m;
+                        const int head = Mh > 0 ? mv / Mh : head0 + hh;
+                        const int row = Mh > 0 ? mv - head * Mh : mv;
+                        logits_out[((int64_t)row * Ktot + head) * V + r + rr] = s;
+                    }
+                } else if (rr < nv && m < mr && ranks_above(s, r + rr, tv[m], ti[m])) {
                     list_insert(lv[m], li[m], s, r + rr, km[m], lane);
                     tv[m] = __shfl(lv[m], km[m] - 1, MD_WAVE);
                     ti[m] = __shfl(li[m], km[m] - 1, MD_WAVE);
@@ -330,6 +340,7 @@ __global__ __launch_bounds__(NW * MD_WAVE) void k_vocab_topk(const T* __restrict
             }
         }
     }
+    if constexpr (LOGITS) return;
     // merge the block's wave lists in LDS (over h', now dead); one list per
     // block goes to memory
     __syncthreads();
@@ -627,6 +638,8 @@ hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
     const T* W = reinterpret_cast<const T*>(a.W);
     const T* bias = reinterpret_cast<const T*>(a.b);
     const T* U = reinterpret_cast<const T*>(a.U);
+    // the logits mode takes the K in the output's layout from the call
+    const int ktot = a.logits_k;
     for (int m0 = 0; m0 < a.M; m0 += p.MR) {
         switch (p.MR) {
             case 4:
@@ -651,6 +664,27 @@ hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
     // a shared projection is one matrix over the heads' nh * M rows
     const int rows_v = a.shared_u ? a.nh * a.M : a.M, nh_u = a.shared_u ? 1 : a.nh;
     const int head0_u = a.shared_u ? 0 : a.head0, Mh = a.shared_u ? a.M : 0;
+    for (int m0 = 0; m0 < rows_v && a.logits; m0 += p.MRv) {
+        switch (p.MRv) {
+            case 4:
+                hipLaunchKernelGGL((k_vocab_topk<T, 4, vocab_waves(4), true>), dim3(p.voc_grid),
+                                   dim3(p.voc_nw * MD_WAVE), p.voc_lds, s, U, hres, rows_v, m0, a.d, a.V, nh_u, head0_u,
+                                   p.wg_per_head, kk, a.kmax, Mh, pv, pi, a.logits, ktot);
+                break;
+            case 2:
+                hipLaunchKernelGGL((k_vocab_topk<T, 2, vocab_waves(2), true>), dim3(p.voc_grid),
+                                   dim3(p.voc_nw * MD_WAVE), p.voc_lds, s, U, hres, rows_v, m0, a.d, a.V, nh_u, head0_u,
+                                   p.wg_per_head, kk, a.kmax, Mh, pv, pi, a.logits, ktot);
+                break;
+            default:
+                hipLaunchKernelGGL((k_vocab_topk<T, 1, vocab_waves(1), true>), dim3(p.voc_grid),
+                                   dim3(p.voc_nw * MD_WAVE), p.voc_lds, s, U, hres, rows_v, m0, a.d, a.V, nh_u, head0_u,
+                                   p.wg_per_head, kk, a.kmax, Mh, pv, pi, a.logits, ktot);
+        }
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (a.logits) return hipSuccess;
     for (int m0 = 0; m0 < rows_v; m0 += p.MRv) {
         switch (p.MRv) {
             case 4:
@@ -684,6 +718,15 @@ size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, in
     if (heads_mfma_applicable(dt, M, d, din)) return heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u);
     const Plan p = make_plan(dt, M, d, din, nh, shared_u);
     return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * p.wg_per_head * kmax * 4);
+}
+
+size_t heads_logits_ws_bytes(int M, int d, int nh) { return align256((size_t)nh * M * d * 4); }
+
+hipError_t topk_merge_launch(const float* pv, const int* pi, int M, int nh, int nlists, const int* kk, int kmax,
+                             int32_t* idx, float* val, hipStream_t s) {
+    KK k;
+    for (int i = 0; i < 8; ++i) k.v[i] = i < nh ? kk[i] : 1;
+    return launch_merge(pv, pi, M, nh, nlists, k, kmax, idx, val, s);
 }
 
 size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u) {
@@ -774,7 +817,7 @@ hipError_t target_argmax_launch(int dt, int R, int d, int V, const void* H, cons
 }
 
 hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (heads_mfma_applicable(a.dt, a.M, a.d, a.din)) {
+    if (!a.logits && heads_mfma_applicable(a.dt, a.M, a.d, a.din)) {
         // many rows: the two contractions on the matrix cores, then the same k-way merge
         float* pv;
         int* pi;

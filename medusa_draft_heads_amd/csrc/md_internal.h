@@ -47,6 +47,8 @@ struct HeadsArgs {
     float* topk_val;
     float* h_res;
     void* ws;
+    float* logits;  // non-null: write every logit [M][logits_k][V] instead of the top-k (GEMV path)
+    int logits_k;
 };
 
 size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u);  // this plan
@@ -57,6 +59,10 @@ size_t heads_mfma_ws_bytes(int M, int d, int din, int V, int nh, int kmax, int s
 hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                              float** part_val, int** part_idx, int* nlists);
 hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);
+size_t heads_logits_ws_bytes(int M, int d, int nh);
+// the k-way merge of nlists sorted lists per (row, head): lists [nh][M][nlists][kmax] -> [M][nh][kmax]
+hipError_t topk_merge_launch(const float* pv, const int* pi, int M, int nh, int nlists, const int* kk, int kmax,
+                             int32_t* idx, float* val, hipStream_t s);
 bool argmax_mfma_applicable(int dt, int R, int d);
 size_t argmax_mfma_ws_bytes(int R, int V);
 hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt, void* ws, hipStream_t s,
@@ -96,6 +102,22 @@ hipError_t accept_tokens_launch(const DevTree& t, int dt, int B, int K, int Hkv,
                                 const int32_t* target_tok, const int32_t* tree_tok, void* Kc, void* Vc,
                                 int32_t* lens, int32_t* accept_len, int32_t* path, int32_t* next_tok,
                                 int32_t* compact_src, hipStream_t s);
+
+// ---- sampled decoding (sample.hip) ----
+size_t draft_sample_ws_bytes(int M, int K, int V, int kmax);
+hipError_t draft_sample_launch(int M, int K, int V, const int* kk, int kmax, float T, const float* logits,
+                               const uint32_t* words, int32_t* tok, float* lse, void* ws, hipStream_t s);
+size_t verify_sampled_ws_bytes(int B, int N);
+hipError_t verify_sampled_launch(const DevTree& t, int dt, int B, int K, int V, int Hkv, int hd, int Lcap, float T,
+                                 const float* target_logits, const float* head_logits, const float* head_lse,
+                                 const int32_t* tree_tok, const uint32_t* u_words, const uint32_t* g_words,
+                                 void* Kc, void* Vc, int32_t* lens, int32_t* accept_len, int32_t* path,
+                                 int32_t* next_tok, int32_t* compact_src, void* ws, hipStream_t s);
+size_t accept_typical_ws_bytes(int B, int N);
+hipError_t accept_typical_launch(const DevTree& t, int dt, int B, int K, int V, int Hkv, int hd, int Lcap, float T,
+                                 float eps, float delta, const float* target_logits, const int32_t* tree_tok,
+                                 const uint32_t* g_words, void* Kc, void* Vc, int32_t* lens, int32_t* accept_len,
+                                 int32_t* path, int32_t* next_tok, int32_t* compact_src, void* ws, hipStream_t s);
 
 // ---- measurement utility (probe.hip) ----
 int probe_blocks();

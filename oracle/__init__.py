@@ -354,7 +354,8 @@ def step_medusa(wl, wts: Dict[str, np.ndarray], inp: Dict[str, np.ndarray], topo
 #   replacement: accept child x with probability min(1, p(x) / q(x)); on
 #   rejection p <- normalise(max(0, p - q)) and x leaves q (q renormalised).
 #   An accepted child becomes the node; when every child is rejected, or the
-#   node is a leaf, the step's last token is drawn from the current p;
+#   node is a leaf, the step's last token is drawn from the current p; a
+#   tree token outside [0, V) is never accepted and changes nothing;
 # * typical acceptance: a node matches when its parent's p gives its token
 #   more than min(eps, delta * exp(-entropy(p))); the deepest node whose
 #   whole root path matches ends the step, and the last token is drawn from
@@ -463,6 +464,8 @@ def verify_sampled(parent: Sequence[int], tree_tok: np.ndarray, target_logits: n
             nxt = None
             for c in kids:
                 x = int(tree_tok[b_, c])
+                if not 0 <= x < p.size:
+                    continue  # not a token: never accepted, changes nothing
                 u = float(unit_from_words(u_words[b_, c]))
                 a = min(1.0, p[x] / q[x]) if q[x] > 0.0 else 1.0
                 margin[b_] = min(margin[b_], abs(u - a))
@@ -489,8 +492,8 @@ def typical_accept(parent: Sequence[int], tree_tok: np.ndarray, target_logits: n
                    delta: float, g_words: np.ndarray) -> Dict[str, np.ndarray]:
     """Typical acceptance (reading above). Returns chosen [B, N] as
     verify_sampled does, match [B, N] (bool), the threshold and p(token) of
-    every non-root node, and margin [B]: the smallest |p(token) - threshold|
-    and the final draw's gap."""
+    every non-root node, and margin [B]: the smallest |p(token) / threshold
+    - 1| and the final draw's gap."""
     B, N = tree_tok.shape
     dep = _depths(parent)
     chosen = np.full((B, N), -1, dtype=np.int32)
@@ -509,9 +512,11 @@ def typical_accept(parent: Sequence[int], tree_tok: np.ndarray, target_logits: n
                 P[a] = (p, min(eps, delta * np.exp(-H)))
             p, t = P[a]
             thr[b_, n] = t
-            ptok[b_, n] = p[tree_tok[b_, n]]
+            x = int(tree_tok[b_, n])
+            ptok[b_, n] = p[x] if 0 <= x < p.size else 0.0  # not a token: probability 0
             match[b_, n] = ptok[b_, n] > t
-            margin[b_] = min(margin[b_], abs(ptok[b_, n] - t))
+            if t > 0.0:
+                margin[b_] = min(margin[b_], abs(ptok[b_, n] / t - 1.0))
         # deepest node whose whole root path matches; lowest index among equals
         best = 0
         for n in range(1, N):

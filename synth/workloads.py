@@ -18,11 +18,12 @@ from typing import Dict, Optional, Sequence, Tuple
 
 import numpy as np
 
-from . import normal, randint, uniform01
+from . import normal, randint, u32, uniform01
 from .topology import Topology, product_order_tree
 
 # stream ids (low byte); the step index is folded in above it
 S_H, S_W, S_B, S_U, S_E, S_Q, S_K, S_V, S_LOGITS, S_ROOT, S_LENS, S_PLANT, S_SRC, S_WT, S_HT, S_ALT = range(1, 17)
+S_DRAFTW, S_UW, S_GW = range(17, 20)  # random words of sampled decoding
 
 
 def stream(sid: int, step: int = 0) -> int:
@@ -51,6 +52,12 @@ class Workload:
     chain: bool = False
     shared_u: bool = False  # one vocabulary projection U [V, d] for every head
     target_head: bool = False  # verify from the target's hidden states Ht [B, N, d] through its LM head Wt [V, d]
+    # "greedy": argmax matching; "sampled": drafts drawn from the heads and
+    # rejection-sampling verification; "typical": top-k drafts and typical acceptance
+    verify: str = "greedy"
+    temperature: float = 1.0
+    eps: float = 0.09    # typical acceptance: threshold min(eps, delta exp(-H))
+    delta: float = 0.3
 
     @property
     def kmax(self) -> int:
@@ -107,8 +114,18 @@ LLAMA70B_LMHEAD = replace(LLAMA70B, name="70B-shaped bf16 heads, batch 1, verifi
                           "(128256 x 8192) with a fused argmax: d=8192 V=128256 K=4, 64-node tree, GQA 64/8 hd128, "
                           "L=4096", target_head=True)
 
+LLAMA70B_SAMPLED = replace(LLAMA70B, name="70B-shaped bf16 heads, batch 1, sampled at T = 1: drafts drawn from "
+                          "the heads, rejection-sampling verification: d=8192 V=128256 K=4, 64-node tree, GQA 64/8 "
+                          "hd128, L=4096", verify="sampled")
+LLAMA70B_TYPICAL = replace(LLAMA70B, name="70B-shaped bf16 heads, batch 1, typical acceptance at T = 1 (eps 0.09, "
+                           "delta 0.3): d=8192 V=128256 K=4, 64-node tree, GQA 64/8 hd128, L=4096", verify="typical")
+TINY_SAMPLED = replace(TINY_F32, name="tiny f32, sampled at T = 1", verify="sampled")
+TINY_TYPICAL = replace(TINY_F32, name="tiny f32, typical acceptance at T = 1", verify="typical")
+
 ALL = {"tiny": TINY_F32, "8b": LLAMA8B, "70b": LLAMA70B, "70b_chain": LLAMA70B_CHAIN,
-       "70b_b8": LLAMA70B_B8, "hydra_b4": HYDRA_B4, "70b_shared": LLAMA70B_SHARED, "70b_lmhead": LLAMA70B_LMHEAD}
+       "70b_b8": LLAMA70B_B8, "hydra_b4": HYDRA_B4, "70b_shared": LLAMA70B_SHARED, "70b_lmhead": LLAMA70B_LMHEAD,
+       "70b_sampled": LLAMA70B_SAMPLED, "70b_typical": LLAMA70B_TYPICAL, "tiny_sampled": TINY_SAMPLED,
+       "tiny_typical": TINY_TYPICAL}
 
 
 def weights(wl: Workload, seed: int, heads: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
@@ -150,6 +167,11 @@ def step_inputs(wl: Workload, seed: int, step: int = 0) -> Dict[str, np.ndarray]
         out["Ht"] = normal(seed, stream(S_HT, step), (wl.B, wl.N, wl.d), 1.0, wl.dtype)
     else:
         out["logits"] = normal(seed, stream(S_LOGITS, step), (wl.B, wl.N, wl.V), 1.0, "f32")
+    if wl.verify == "sampled":
+        out["draft_words"] = u32(seed, stream(S_DRAFTW, step), wl.M * wl.K * wl.V).reshape(wl.M, wl.K, wl.V)
+        out["u_words"] = u32(seed, stream(S_UW, step), wl.B * wl.N).reshape(wl.B, wl.N)
+    if wl.verify in ("sampled", "typical"):
+        out["g_words"] = u32(seed, stream(S_GW, step), wl.B * wl.V).reshape(wl.B, wl.V)
     return out
 
 

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 16
+    assert len(names) == 24
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -177,6 +177,74 @@ def test_target_argmax_and_accept_tokens_argument_errors():
     assert acc(K=3) == L.MD_EINVAL  # the tree is 4 deep
     assert acc(tt=None) == L.MD_EINVAL
     assert acc(B=0) == L.MD_OK
+
+
+def test_sampled_decoding_argument_errors():
+    lib = L.lib()
+    P = 0x1000
+    # heads writing logits: Medusa kinds only
+    need = md.md_heads_logits_workspace_bytes(0, 2, 512, 4)
+    assert need > 0 and md.md_heads_logits_workspace_bytes(1, 2, 512, 4) == 0
+
+    def hl(kind=0, dt=1, M=2, d=512, V=5000, K=4, lg=P, ws_bytes=need):
+        return lib.md_medusa_heads_logits(kind, dt, M, d, V, K, P, P, P, P, lg, None, P, ws_bytes, None)
+
+    assert hl(kind=1) == L.MD_EINVAL
+    assert hl(dt=4) == L.MD_EINVAL
+    assert hl(K=9) == L.MD_EINVAL
+    assert hl(d=100) == L.MD_EUNSUPPORTED
+    assert hl(lg=None) == L.MD_EINVAL
+    assert hl(ws_bytes=need - 1) == L.MD_EWORKSPACE
+    assert hl(M=0) == L.MD_OK
+    # draft sampling
+    need = md.md_draft_sample_workspace_bytes(2, 4, 5000, 10)
+    assert need > 0 and md.md_draft_sample_workspace_bytes(2, 4, 5000, 17) == 0
+
+    def ds(M=2, K=4, V=5000, kph=(10, 4, 2, 1), T=1.0, words=P, ws_bytes=need):
+        kp = (ctypes.c_int32 * len(kph))(*kph)
+        return lib.md_draft_sample(M, K, V, ctypes.cast(kp, ctypes.c_void_p), T, P, words, P, P, P, ws_bytes, None)
+
+    assert ds(kph=(10, 4, 2, 17)) == L.MD_EINVAL
+    assert ds(kph=(10, 4, 2, 0)) == L.MD_EINVAL
+    assert ds(V=8) == L.MD_EINVAL  # smaller than the widest draw
+    assert ds(T=0.0) == L.MD_EINVAL
+    assert ds(T=-1.0) == L.MD_EINVAL
+    assert ds(T=float("inf")) == L.MD_EINVAL
+    assert ds(T=float("nan")) == L.MD_EINVAL
+    assert ds(words=None) == L.MD_EINVAL
+    assert ds(ws_bytes=need - 1) == L.MD_EWORKSPACE
+    assert ds(M=0) == L.MD_OK
+    # verification
+    topo = product_order_tree((4, 2, 2, 1), 16)
+    t = ctypes.byref(L.make_tree(topo.parent, topo.rank))
+    need = md.md_verify_sampled_workspace_bytes(1, 16)
+    assert need > 0 and md.md_verify_sampled_workspace_bytes(1, 65) == 0
+
+    def vs(B=1, K=4, V=5000, hd=128, Lcap=200, T=1.0, uw=P, ws_bytes=need):
+        return lib.md_tree_verify_sampled(t, 1, B, K, V, 2, hd, Lcap, T, P, P, P, P, uw, P, P, P, P, P, P, P, P, P,
+                                          ws_bytes, None)
+
+    assert vs(K=3) == L.MD_EINVAL
+    assert vs(V=0) == L.MD_EINVAL
+    assert vs(hd=512) == L.MD_EUNSUPPORTED
+    assert vs(Lcap=10) == L.MD_ERANGE
+    assert vs(T=0.0) == L.MD_EINVAL
+    assert vs(uw=None) == L.MD_EINVAL
+    assert vs(ws_bytes=need - 1) == L.MD_EWORKSPACE
+    assert vs(B=0) == L.MD_OK
+    need = md.md_accept_typical_workspace_bytes(1, 16)
+    assert need > 0
+
+    def ty(B=1, T=1.0, eps=0.09, delta=0.3, gw=P, ws_bytes=need):
+        return lib.md_tree_accept_typical(t, 1, B, 4, 5000, 2, 128, 200, T, eps, delta, P, P, gw, P, P, P, P, P, P, P,
+                                          P, ws_bytes, None)
+
+    assert ty(T=-2.0) == L.MD_EINVAL
+    assert ty(eps=-0.1) == L.MD_EINVAL
+    assert ty(delta=float("nan")) == L.MD_EINVAL
+    assert ty(gw=None) == L.MD_EINVAL
+    assert ty(ws_bytes=need - 1) == L.MD_EWORKSPACE
+    assert ty(B=0) == L.MD_OK
 
 
 def test_timing_hook_pairs():
