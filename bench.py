@@ -9,9 +9,12 @@ batch 1 (d = 8,192, V = 128,256, 4 heads in bf16 = 8.94 GB of weights, top-k
 Other workloads (--workload) are secondary measurements: the batch-8 step
 whose heads run over all 512 tree nodes on the matrix cores, the Hydra step
 (four sequential head levels), the 8B-shaped step, the top-1 chain, the
-70B-shaped step with one vocabulary projection shared by the four heads, and
-the 70B-shaped step verified from the target's hidden states through its LM
-head with a fused argmax (no logits in memory).
+70B-shaped step with one vocabulary projection shared by the four heads, the
+70B-shaped step verified from the target's hidden states through its LM head
+with a fused argmax (no logits in memory), and the 70B-shaped step sampled at
+temperature 1: drafts drawn from the heads' distributions and verified by
+rejection sampling ("70b_sampled"), or top-k drafts under typical acceptance
+("70b_typical").
 
 Prints one JSON line: steps/s, the roofline of the dominant kernel (the
 vocabulary projection + top-k, timed live with HIP events that the library
@@ -52,7 +55,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="70b",
-                    choices=["70b", "70b_chain", "8b", "tiny", "70b_b8", "hydra_b4", "70b_shared", "70b_lmhead"])
+                    choices=["70b", "70b_chain", "8b", "tiny", "70b_b8", "hydra_b4", "70b_shared", "70b_lmhead",
+                             "70b_sampled", "70b_typical"])
     ap.add_argument("--sets", type=int, default=8, help="input sets rotated to keep them out of the 256 MB MALL")
     ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps timed for the CPU baseline (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -103,6 +107,11 @@ def main() -> int:
                                      x["root_tok"], x["lens"])
             tok = hy["tree_tok"]
             heads_time = time.perf_counter() - ta
+        elif wl.verify == "sampled":  # one row per request: the heads' logits, then the drafts drawn from them
+            heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], [1] * wl.K, want_logits=True)
+            full = oracle.draft_sample(heads["logits"], x["draft_words"], wl.topk, wl.temperature)["tok"]
+            tok, _ = oracle.tree_tokens_medusa(topo.parent, topo.rank, full, x["src_row"], x["root_tok"], x["lens"])
+            heads_time = time.perf_counter() - ta
         else:
             rows = sorted(set(int(r) for r in x["src_row"]))
             heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], wl.topk, rows=rows)
@@ -116,13 +125,21 @@ def main() -> int:
                     len(rows), wl.M)
         if wl.target_head:  # verification through the target's LM head: plant its hidden states
             plant_hidden(x["Ht"], w["Wt"], topo, tok, wl.a, seed=args.seed, step=s)
-        else:
+        elif wl.verify == "greedy":
             logits = plant(x["logits"], topo, tok, wl.a, seed=args.seed, step=s)
+        else:  # sampled decoding: the target's logits as drawn, N(0, 1)
+            logits = x["logits"]
         if s < args.cpu_steps:
             tc = time.perf_counter()
             oracle.tree_attention(topo.parent, x["q"], x["Kc"], x["Vc"], x["lens"])
             if wl.target_head:
                 tstar = oracle.target_argmax(x["Ht"].reshape(wl.B * topo.n, wl.d), w["Wt"])[0].reshape(wl.B, topo.n)
+            elif wl.verify == "sampled":  # the token after every node the walk passes through
+                tstar = oracle.verify_sampled(topo.parent, tok, logits, heads["logits"], wl.temperature, x["u_words"],
+                                              x["g_words"])["chosen"]
+            elif wl.verify == "typical":
+                tstar = oracle.typical_accept(topo.parent, tok, logits, wl.temperature, wl.eps, wl.delta,
+                                              x["g_words"])["chosen"]
             else:
                 tstar = oracle.argmax(logits)
             r = oracle.accept(topo.parent, wl.K, tok, tstar, x["lens"])
@@ -144,14 +161,15 @@ def main() -> int:
                         dtype=torch.bfloat16 if wl.dtype == "bf16" else torch.float32, B=wl.B,
                         M=wl.B if hydra else wl.M, d=wl.d, V=wl.V, K=wl.K, k_per_head=wl.topk, parent=topo.parent,
                         rank=topo.rank, Hq=wl.Hq, Hkv=wl.Hkv, hd=wl.hd, Lcap=wl.Lcap, max_len=wl.L_max,
-                        target_head=wl.target_head)
+                        target_head=wl.target_head, verify=wl.verify, temperature=wl.temperature, eps=wl.eps,
+                        delta=wl.delta)
     step = md.MedusaStep(cfg)
     stream = torch.cuda.current_stream()
     calls = depth if hydra else 1  # heads calls per step, each with its own event pair
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
           for _ in range(args.steps)]
     lm_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(args.steps)] if wl.target_head else None
+             for _ in range(args.steps)] if (wl.target_head or wl.verify != "greedy") else None
     for pairs in ev + ([lm_ev] if lm_ev else []):  # materialise the underlying hipEvent_t handles
         for a, b in pairs:
             a.record(stream)
@@ -167,22 +185,32 @@ def main() -> int:
             if hydra:
                 step.heads(xd["h"], wd["W"], wd["b"], wd["U"], E=wd["E"], root_tok=xd["root_tok"], level=lvl + 1)
                 step.build(None, xd["root_tok"], xd["lens"], level=lvl + 1)
+            elif wl.verify == "sampled":
+                step.heads_logits(xd["h"], wd["W"], wd["b"], wd["U"])
             else:
                 step.heads(xd["h"], wd["W"], wd["b"], wd["U"])
             if pairs is not None:
                 md.md_set_vocab_timing_events(None, None)
+        if wl.verify == "sampled":
+            step.draft(xd["draft_words"])
         if not hydra:
             step.build(xd["src_row"], xd["root_tok"], xd["lens"])
         step.attention(xd["q"], xd["Kc"], xd["Vc"], xd["lens"])
+        if lm is not None:
+            lm[0].record(stream)
         if wl.target_head:
-            if lm is not None:
-                lm[0].record(stream)
             step.verify(xd["Ht"], wd["Wt"])
             if lm is not None:
                 lm[1].record(stream)
             step.accept_tokens(xd["Kc"], xd["Vc"], xd["lens"])
+        elif wl.verify == "sampled":
+            step.verify_sampled(xd["logits"], xd["u_words"], xd["g_words"], xd["Kc"], xd["Vc"], xd["lens"])
+        elif wl.verify == "typical":
+            step.accept_typical(xd["logits"], xd["g_words"], xd["Kc"], xd["Vc"], xd["lens"])
         else:
             step.accept(xd["logits"], xd["Kc"], xd["Vc"], xd["lens"])
+        if lm is not None and not wl.target_head:
+            lm[1].record(stream)
 
     for i in range(args.warmup):
         one_step(i)
@@ -229,6 +257,8 @@ def main() -> int:
     u_reads = depth if hydra else (1 if wl.shared_u else wl.K)
     vocab_bytes = u_reads * wl.V * wl.d * esz
     vocab_bytes += sum(head_rows) * wl.d * 4
+    if wl.verify == "sampled":  # the logits kernel writes every logit
+        vocab_bytes += sum(head_rows) * wl.V * 4
     vocab_flops = 2.0 * wl.V * wl.d * sum(head_rows)  # algorithmic multiply-adds of the projections
     kernel = "vocabulary projection + per-head top-k"
     mfma_rows = min(head_rows) >= 8 and wl.dtype == "bf16"
@@ -252,18 +282,32 @@ def main() -> int:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                     "kernel": ("vocabulary kernels of the 4 levels" if hydra else
+                               "k_vocab_topk<..., LOGITS> (vocabulary projection writing every logit)"
+                               if wl.verify == "sampled" else
                                "k_vocab_topk (%s%s)" % (kernel, "; one U for the %d heads" % wl.K if wl.shared_u
                                                         else "")),
                     "kernel_ms": round(vocab_ms, 4), "bytes_per_launch": vocab_bytes,
                     "stream_read_GBps": round(stream_gbs, 1), "frac_of_stream_read": round(achieved / stream_gbs, 4)}
     # verification input: the logits, or the hidden states plus the LM head through the fused argmax
     verify_bytes = (wl.V * wl.d * esz + wl.B * wl.N * wl.d * esz) if wl.target_head else wl.B * wl.N * wl.V * 4
+    if wl.verify == "sampled":  # head logits written and read back, the draft words, the final draw's words
+        verify_bytes += 2 * wl.M * wl.K * wl.V * 4 + wl.M * wl.K * wl.V * 4 + wl.B * wl.V * 4
+    elif wl.verify == "typical":
+        verify_bytes += wl.B * wl.V * 4
     step_bytes = (md.md_heads_weight_bytes(kind, 1 if esz == 2 else 0, wl.d, wl.V, wl.K)
                   + 2 * wl.B * wl.Hkv * (wl.L_max + wl.N) * wl.hd * esz  # K and V of prefix + tree (upper bound)
                   + 2 * wl.B * wl.N * wl.Hq * wl.hd * esz  # q in, attention out
                   + verify_bytes)
-    lm_head = None
-    if lm_ev:
+    lm_head = verification = None
+    if lm_ev and not wl.target_head:
+        vms = sum(a.elapsed_time(b) for a, b in lm_ev) / args.steps
+        verification = {"kernels": "rejection-sampling walk + acceptance and compaction (md_tree_verify_sampled)"
+                        if wl.verify == "sampled" else
+                        "row statistics + typical acceptance + acceptance and compaction (md_tree_accept_typical)",
+                        "ms": round(vms, 4), "temperature": wl.temperature}
+        if wl.verify == "typical":
+            verification.update({"eps": wl.eps, "delta": wl.delta})
+    elif lm_ev:
         lm_ms = sum(a.elapsed_time(b) for a, b in lm_ev) / args.steps
         lm_gbs = verify_bytes / (lm_ms * 1e-3) / 1e9
         lm_head = {"kernels": "target LM head + fused argmax (md_target_argmax)", "ms": round(lm_ms, 4),
@@ -305,6 +349,9 @@ def main() -> int:
     }
     if lm_head:
         out["lm_head"] = lm_head
+    if verification:
+        out["verification"] = verification
+        out["acceptance"].pop("E_closed_form")
     print(json.dumps(out), flush=True)
     return 0
 

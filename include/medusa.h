@@ -296,8 +296,9 @@ int md_tree_accept_typical(const md_tree* tree, int dt, int B, int K, int V, int
                            size_t ws_bytes, void* stream);
 
 /* Timing hook for profiling: when both are non-NULL hipEvent_t handles, every
- * later md_medusa_heads call on this thread records `start` on its stream
- * right before its vocabulary-projection kernel and `stop` right after it.
+ * later md_medusa_heads or md_medusa_heads_logits call on this thread records
+ * `start` on its stream right before its vocabulary-projection kernel and
+ * `stop` right after it.
  * Pass NULL, NULL to stop. */
 int md_set_vocab_timing_events(void* start, void* stop);
 

@@ -355,7 +355,7 @@ int md_medusa_heads_logits(int kind, int dt, int M, int d, int V, int K, const v
     a.ws = ws;
     a.logits = logits;
     a.logits_k = K;
-    return hip_status(heads_launch(a, nullptr, (hipStream_t)stream, nullptr, nullptr), "md_medusa_heads_logits");
+    return hip_status(heads_launch(a, nullptr, (hipStream_t)stream, g_ev0, g_ev1), "md_medusa_heads_logits");
 }
 
 size_t md_draft_sample_workspace_bytes(int M, int K, int V, int kmax) {

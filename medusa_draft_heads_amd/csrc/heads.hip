@@ -684,7 +684,7 @@ hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    if (a.logits) return hipSuccess;
+    if (a.logits) return ev1 ? hipEventRecord(ev1, s) : hipSuccess;
     for (int m0 = 0; m0 < rows_v; m0 += p.MRv) {
         switch (p.MRv) {
             case 4:

@@ -41,6 +41,8 @@
 
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int BLOCK = 256;
 constexpr int NWAVE = BLOCK / MD_WAVE;
 constexpr int KM = 16;     // longest draft list
@@ -204,16 +206,21 @@ __global__ __launch_bounds__(BLOCK) void k_draft_part(const float* __restrict__ 
     if (tid == 0) part_lse[(int64_t)rh * chunks + ch] = (float)lse;  // -inf for an empty chunk
 }
 
-__global__ void k_lse_merge(const float* __restrict__ part_lse, int rows, int chunks, float* __restrict__ lse) {
-    const int r = blockIdx.x * blockDim.x + threadIdx.x;
-    if (r >= rows) return;
+// One wave per row-head: log-sum-exp of the chunks' log-sum-exps.
+__global__ __launch_bounds__(MD_WAVE) void k_lse_merge(const float* __restrict__ part_lse, int chunks,
+                                                       float* __restrict__ lse) {
+    const int r = blockIdx.x, lane = threadIdx.x;
     const float* pl = part_lse + (int64_t)r * chunks;
-    double M = -INFINITY;
-    for (int c = 0; c < chunks; ++c) M = fmax(M, (double)pl[c]);
+    float m = -INFINITY;
+    for (int c = lane; c < chunks; c += MD_WAVE) m = fmaxf(m, pl[c]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, MD_WAVE));
     double S = 0.0;
-    for (int c = 0; c < chunks; ++c)
-        if (pl[c] > -INFINITY) S += exp((double)pl[c] - M);
-    lse[r] = (float)(M + log(S));
+    for (int c = lane; c < chunks; c += MD_WAVE)
+        if (pl[c] > -INFINITY) S += exp((double)pl[c] - (double)m);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) S += __shfl_xor(S, o, MD_WAVE);
+    if (lane == 0) lse[r] = (float)((double)m + log(S));
 }
 
 int draft_chunks(int rows, int V) {
@@ -226,6 +233,151 @@ int draft_chunks(int rows, int V) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // ------------------------------------------------------------- the walk
+
+// The nodes with children, in node order (passed by value).
+struct Parents {
+    int n;
+    int8_t node[64];
+};
+
+Parents parents_of(const DevTree& t) {
+    Parents p;
+    p.n = 0;
+    for (int n = 0; n < t.n; ++n) {
+        bool has = false;
+        for (int c = n + 1; c < t.n; ++c) has |= t.parent[c] == n;
+        if (has) p.node[p.n++] = (int8_t)n;
+    }
+    return p;
+}
+
+// What the step's last draw samples from: the target at `node`, and with
+// head >= 0 the residual max(0, p - c q) against that head's q.
+struct DrawSpec {
+    int node;
+    int head;
+    float c;
+    float lse_t;
+    float lse_h;
+};
+
+constexpr int kStatBlocks = 2048;  // row statistics: blocks over all rows
+constexpr int kDrawBlocks = 1024;  // final draws: blocks over all requests
+
+int split_chunks(int rows, int V, int target_blocks) {
+    int c = (target_blocks + rows - 1) / rows;
+    const int max_c = (V + 16 * BLOCK - 1) / (16 * BLOCK);  // at least 16 elements a thread
+    if (c > max_c) c = max_c;
+    return c < 1 ? 1 : c;
+}
+
+// Calls f(y, x) for every element y of row x[] in [a, e): 16-byte loads,
+// two in flight per thread, when rows are 16-byte aligned (V % 4 == 0).
+template <int NT, typename F>
+__device__ __forceinline__ void sweep(const float* __restrict__ x, int V, int a, int e, F&& f) {
+    const int tid = threadIdx.x;
+    if ((V & 3) == 0) {
+        const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
+        const int a4 = (a + 3) >> 2, e4 = e >> 2;  // chunks split on multiples of 4 below
+        int j = a4 + tid;
+        for (; j + NT < e4; j += 2 * NT) {
+            const f32x4 u = x4[j], w = x4[j + NT];
+            f(4 * j, u.x); f(4 * j + 1, u.y); f(4 * j + 2, u.z); f(4 * j + 3, u.w);
+            const int k = j + NT;
+            f(4 * k, w.x); f(4 * k + 1, w.y); f(4 * k + 2, w.z); f(4 * k + 3, w.w);
+        }
+        if (j < e4) {
+            const f32x4 u = x4[j];
+            f(4 * j, u.x); f(4 * j + 1, u.y); f(4 * j + 2, u.z); f(4 * j + 3, u.w);
+        }
+    } else {
+        for (int y = a + tid; y < e; y += NT) f(y, x[y]);
+    }
+}
+
+// chunk ch of nc over [0, V): bounds on multiples of 4 so the 16-byte sweep covers it exactly
+__device__ __forceinline__ void chunk_range(int V, int ch, int nc, int& a, int& e) {
+    const int V4 = (V + 3) >> 2;
+    a = (int)((int64_t)V4 * ch / nc) * 4;
+    e = min(V, (int)((int64_t)V4 * (ch + 1) / nc) * 4);
+}
+
+// Block (row r = (request b, j-th parent), chunk ch): the chunk's
+// (largest z, sum e^(z - m), sum e^(z - m) z) with z = l / T.
+__global__ __launch_bounds__(BLOCK) void k_row_stats_part(Parents pl, int N, int V, float invT, int chunks,
+                                                          const float* __restrict__ target_logits,
+                                                          float* __restrict__ part) {
+    __shared__ float shm[NWAVE];
+    __shared__ double shs[NWAVE];
+    const int r = blockIdx.x / chunks, ch = blockIdx.x - r * chunks;
+    const int b = r / pl.n, node = pl.node[r - b * pl.n];
+    const float* lt = target_logits + ((int64_t)b * N + node) * V;
+    int a, e;
+    chunk_range(V, ch, chunks, a, e);
+    float m = -INFINITY, s = 0.0f, wz = 0.0f;
+    sweep<BLOCK>(lt, V, a, e, [&](int, float l) {
+        const float z = l * invT;
+        if (z > m) {
+            const float q = __expf(m - z);
+            s = s * q + 1.0f;
+            wz = wz * q + z;
+            m = z;
+        } else {
+            const float q = __expf(z - m);
+            s += q;
+            wz += q * z;
+        }
+    });
+    float bm = m;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o, MD_WAVE));
+    if ((threadIdx.x & 63) == 0) shm[threadIdx.x >> 6] = bm;
+    __syncthreads();
+    float M = shm[0];
+#pragma unroll
+    for (int i = 1; i < NWAVE; ++i) M = fmaxf(M, shm[i]);
+    const double f = s > 0.0f ? exp((double)m - (double)M) : 0.0;
+    const double S = block_sum<NWAVE>((double)s * f, shs);
+    const double W = block_sum<NWAVE>((double)wz * f, shs);
+    if (threadIdx.x == 0) {
+        float* o = part + ((int64_t)r * chunks + ch) * 3;
+        o[0] = M;
+        o[1] = (float)S;
+        o[2] = (float)W;
+    }
+}
+
+// One wave per row: combine the chunks; lse = M + log S, entropy = lse - W / S.
+__global__ __launch_bounds__(MD_WAVE) void k_row_stats_merge(Parents pl, int N, int chunks,
+                                                             const float* __restrict__ part,
+                                                             float* __restrict__ lse_out,
+                                                             float* __restrict__ ent_out) {
+    const int r = blockIdx.x, lane = threadIdx.x;
+    const int b = r / pl.n, node = pl.node[r - b * pl.n];
+    const float* pr = part + (int64_t)r * chunks * 3;
+    float M = -INFINITY;
+    for (int c = lane; c < chunks; c += MD_WAVE) M = fmaxf(M, pr[3 * c]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, MD_WAVE));
+    double S = 0.0, W = 0.0;
+    for (int c = lane; c < chunks; c += MD_WAVE) {
+        if (pr[3 * c + 1] > 0.0f) {
+            const double f = exp((double)pr[3 * c] - (double)M);
+            S += (double)pr[3 * c + 1] * f;
+            W += (double)pr[3 * c + 2] * f;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        S += __shfl_xor(S, o, MD_WAVE);
+        W += __shfl_xor(W, o, MD_WAVE);
+    }
+    if (lane == 0) {
+        const double lse = (double)M + log(S);
+        lse_out[(int64_t)b * N + node] = (float)lse;
+        if (ent_out) ent_out[(int64_t)b * N + node] = (float)(lse - W / S);
+    }
+}
 
 __device__ __forceinline__ int first_child(const DevTree& t, int node) {
     for (int n = node + 1; n < t.n; ++n)
@@ -240,61 +392,75 @@ __device__ __forceinline__ int next_sibling(const DevTree& t, int n) {
 }
 
 // One block per request. Every thread runs the same walk on the same
-// scalars; the vocabulary sweeps are block reductions.
+// scalars; the residual masses are block reductions over the vocabulary.
+// The walk ends by describing the last draw (spec), made by k_draw_*.
 __global__ __launch_bounds__(WALK) void k_walk_sampled(DevTree t, int K, int V, float invT,
                                                        const float* __restrict__ target_logits,
                                                        const float* __restrict__ head_logits,
                                                        const float* __restrict__ head_lse,
+                                                       const float* __restrict__ lse_rows,
                                                        const int32_t* __restrict__ tree_tok,
                                                        const uint32_t* __restrict__ u_words,
-                                                       const uint32_t* __restrict__ g_words,
-                                                       int32_t* __restrict__ chosen) {
-    __shared__ float shv[WWAVES], shm[WWAVES];
-    __shared__ int shi[WWAVES];
+                                                       int32_t* __restrict__ chosen, DrawSpec* __restrict__ spec) {
     __shared__ double shs[WWAVES];
     const int b = blockIdx.x, N = t.n, tid = threadIdx.x;
     if (tid < N) chosen[(int64_t)b * N + tid] = -1;
-    const uint32_t* gw = g_words + (int64_t)b * V;
+    __syncthreads();  // thread 0 may later write any node's entry
     int node = 0;
     while (true) {
-        const float* lt = target_logits + ((int64_t)b * N + node) * V;
         const int c0 = first_child(t, node);
-        double c = 0.0;  // residual R(y) = max(0, p(y) - c q(y)); the sweeps use it in float
-        const float* lh = nullptr;
-        float lse_t = 0.0f, lse_h = 0.0f;
+        if (c0 < 0) {  // a leaf: the last token is drawn from p
+            if (tid == 0) spec[b] = DrawSpec{node, -1, 0.0f, 0.0f, 0.0f};
+            return;
+        }
+        const float* lt = target_logits + ((int64_t)b * N + node) * V;
+        const float lse_t = lse_rows[(int64_t)b * N + node];
+        const int hd = t.depth[node];  // head hd drafted the children (depth hd + 1)
+        const float* lh = head_logits + ((int64_t)b * K + hd) * V;
+        const float lse_h = head_lse[(int64_t)b * K + hd];
+        double c = 0.0, mass = 1.0, S = 1.0;  // residual R(y) = max(0, p(y) - c q(y)), mass M, q-mass S
         int next = -1;
-        if (c0 >= 0) {
-            float lm = -INFINITY, ls = 0.0f;
-            for (int y = tid; y < V; y += WALK) lse_add(lm, ls, lt[y] * invT);
-            lse_t = (float)block_lse<WWAVES>(lm, ls, shm, shs);
-            const int hd = t.depth[node];  // head hd drafted the children (depth hd + 1)
-            lh = head_logits + ((int64_t)b * K + hd) * V;
-            lse_h = head_lse[(int64_t)b * K + hd];
-            double mass = 1.0, S = 1.0;
-            for (int j = c0; j >= 0; j = next_sibling(t, j)) {
-                const int x = tree_tok[(int64_t)b * N + j];
-                if (x < 0 || x >= V) continue;  // not a token: never accepted, changes nothing
-                const double px = (double)__expf(lt[x] * invT - lse_t);
-                const double qx = (double)__expf(lh[x] * invT - lse_h);
-                const double rx = fmax(0.0, px - c * qx);
-                const double ratio = qx > 0.0 ? (rx / mass) * (S / qx) : INFINITY;
-                const double u = (double)unit_f(u_words[(int64_t)b * N + j]);
-                if (u < ratio) {
-                    next = j;
-                    break;
-                }
-                c += mass / S;
-                S -= qx;
-                if (next_sibling(t, j) >= 0) {  // another child may follow: the new residual's mass
-                    const float cf = (float)c;
-                    float acc = 0.0f;
-                    for (int y = tid; y < V; y += WALK) {
-                        const float p = __expf(lt[y] * invT - lse_t);
-                        const float q = __expf(lh[y] * invT - lse_h);
-                        acc += fmaxf(0.0f, p - cf * q);
+        for (int j = c0; j >= 0; j = next_sibling(t, j)) {
+            const int x = tree_tok[(int64_t)b * N + j];
+            if (x < 0 || x >= V) continue;  // not a token: never accepted, changes nothing
+            const double px = (double)__expf(lt[x] * invT - lse_t);
+            const double qx = (double)__expf(lh[x] * invT - lse_h);
+            const double rx = fmax(0.0, px - c * qx);
+            const double ratio = qx > 0.0 ? (rx / mass) * (S / qx) : INFINITY;
+            const double u = (double)unit_f(u_words[(int64_t)b * N + j]);
+            if (u < ratio) {
+                next = j;
+                break;
+            }
+            c += mass / S;
+            S -= qx;
+            if (next_sibling(t, j) >= 0) {  // another child may follow: the new residual's mass
+                const float cf = (float)c;
+                float acc = 0.0f;
+                if ((V & 3) == 0) {
+                    const f32x4* lt4 = reinterpret_cast<const f32x4*>(lt);
+                    const f32x4* lh4 = reinterpret_cast<const f32x4*>(lh);
+                    const int V4 = V >> 2;
+                    int i = tid;
+                    for (; i + WALK < V4; i += 2 * WALK) {
+                        const f32x4 ta = lt4[i], ha = lh4[i], tb = lt4[i + WALK], hb = lh4[i + WALK];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            acc += fmaxf(0.0f, __expf(ta[q] * invT - lse_t) - cf * __expf(ha[q] * invT - lse_h));
+                            acc += fmaxf(0.0f, __expf(tb[q] * invT - lse_t) - cf * __expf(hb[q] * invT - lse_h));
+                        }
                     }
-                    mass = block_sum<WWAVES>((double)acc, shs);
+                    if (i < V4) {
+                        const f32x4 ta = lt4[i], ha = lh4[i];
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            acc += fmaxf(0.0f, __expf(ta[q] * invT - lse_t) - cf * __expf(ha[q] * invT - lse_h));
+                    }
+                } else {
+                    for (int y = tid; y < V; y += WALK)
+                        acc += fmaxf(0.0f, __expf(lt[y] * invT - lse_t) - cf * __expf(lh[y] * invT - lse_h));
                 }
+                mass = block_sum<WWAVES>((double)acc, shs);
             }
         }
         if (next >= 0) {
@@ -302,157 +468,177 @@ __global__ __launch_bounds__(WALK) void k_walk_sampled(DevTree t, int K, int V, 
             node = next;
             continue;
         }
-        // the step's last token: Gumbel-max over log R (a leaf: over log p)
-        float bv = -INFINITY;
-        int bi = INT_MAX;
-        const float cf = (float)c;
-        for (int y = tid; y < V; y += WALK) {
-            float s;
-            if (c0 < 0) {
-                s = lt[y] * invT + gumbel_f(gw[y]);
-            } else {
-                const float p = __expf(lt[y] * invT - lse_t);
-                const float q = __expf(lh[y] * invT - lse_h);
-                const float r = p - cf * q;
-                s = r > 0.0f ? __logf(r) + gumbel_f(gw[y]) : -INFINITY;
-            }
+        if (tid == 0) spec[b] = DrawSpec{node, hd, (float)c, lse_t, lse_h};  // every child rejected
+        return;
+    }
+}
+
+// The last draws: Gumbel-max over log R (or log p), split over the
+// vocabulary; block (request b, chunk ch) leaves its best (value, index).
+__global__ __launch_bounds__(BLOCK) void k_draw_part(int N, int K, int V, float invT, int chunks,
+                                                     const DrawSpec* __restrict__ spec,
+                                                     const float* __restrict__ target_logits,
+                                                     const float* __restrict__ head_logits,
+                                                     const uint32_t* __restrict__ g_words,
+                                                     float* __restrict__ pv, int* __restrict__ pi) {
+    __shared__ float shv[NWAVE];
+    __shared__ int shi[NWAVE];
+    const int b = blockIdx.x / chunks, ch = blockIdx.x - b * chunks;
+    const DrawSpec sp = spec[b];
+    const float* lt = target_logits + ((int64_t)b * N + sp.node) * V;
+    const float* lh = sp.head >= 0 ? head_logits + ((int64_t)b * K + sp.head) * V : nullptr;
+    const uint32_t* gw = g_words + (int64_t)b * V;
+    int a, e;
+    chunk_range(V, ch, chunks, a, e);
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    if (sp.head < 0) {
+        sweep<BLOCK>(lt, V, a, e, [&](int y, float l) {
+            const float s = l * invT + gumbel_f(gw[y]);
             if (above(s, y, bv, bi)) {
                 bv = s;
                 bi = y;
             }
-        }
-        block_argmax<WWAVES>(bv, bi, shv, shi);
-        if (tid == 0) chosen[(int64_t)b * N + node] = bi == INT_MAX ? -1 : bi;
-        break;
+        });
+    } else {
+        sweep<BLOCK>(lt, V, a, e, [&](int y, float l) {
+            const float r = __expf(l * invT - sp.lse_t) - sp.c * __expf(lh[y] * invT - sp.lse_h);
+            if (r > 0.0f) {
+                const float s = __logf(r) + gumbel_f(gw[y]);
+                if (above(s, y, bv, bi)) {
+                    bv = s;
+                    bi = y;
+                }
+            }
+        });
     }
+    block_argmax<NWAVE>(bv, bi, shv, shi);
+    if (threadIdx.x == 0) {
+        pv[blockIdx.x] = bv;
+        pi[blockIdx.x] = bi;
+    }
+}
+
+// One wave per request: the best of the chunks is the token after spec.node.
+__global__ __launch_bounds__(MD_WAVE) void k_draw_merge(int N, int chunks, const DrawSpec* __restrict__ spec,
+                                                        const float* __restrict__ pv, const int* __restrict__ pi,
+                                                        int32_t* __restrict__ chosen) {
+    const int b = blockIdx.x, lane = threadIdx.x;
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int c = lane; c < chunks; c += MD_WAVE) {
+        const float v = pv[(int64_t)b * chunks + c];
+        const int i = pi[(int64_t)b * chunks + c];
+        if (above(v, i, bv, bi)) {
+            bv = v;
+            bi = i;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        const float ov = __shfl_xor(bv, o, MD_WAVE);
+        const int oi = __shfl_xor(bi, o, MD_WAVE);
+        if (above(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    if (lane == 0) chosen[(int64_t)b * N + spec[b].node] = bi == INT_MAX ? -1 : bi;
 }
 
 // ------------------------------------------------------- typical acceptance
 
-// Block (request b, j-th node with children): log-sum-exp and entropy of the
-// target's p at that node. H = lse - sum p z with z = l / T.
-__global__ __launch_bounds__(BLOCK) void k_row_stats(DevTree t, int V, float invT, int P,
+// One wave per request: match bits (one node per lane), the deepest accepted
+// node, the tokens along its path; the last draw is at that node's p.
+__global__ __launch_bounds__(MD_WAVE) void k_typical(DevTree t, int V, float invT, float eps, float delta,
                                                      const float* __restrict__ target_logits,
-                                                     float* __restrict__ lse_out, float* __restrict__ ent_out) {
-    __shared__ float shm[NWAVE];
-    __shared__ double shs[NWAVE];
-    __shared__ int s_has[MD_WAVE], s_node;
-    const int b = blockIdx.x / P, j = blockIdx.x - b * P;
-    const int N = t.n;
-    if (threadIdx.x < MD_WAVE) s_has[threadIdx.x] = 0;
-    __syncthreads();
-    if (threadIdx.x > 0 && threadIdx.x < N) s_has[t.parent[threadIdx.x]] = 1;
-    __syncthreads();
-    if (threadIdx.x < MD_WAVE) {
-        // the j-th node with children, in node order
-        uint64_t has = __ballot(s_has[threadIdx.x] != 0);
-        for (int i = 0; i < j && has; ++i) has &= has - 1ull;
-        if (threadIdx.x == 0) s_node = has ? __ffsll((long long)has) - 1 : -1;
+                                                     const float* __restrict__ lse, const float* __restrict__ ent,
+                                                     const int32_t* __restrict__ tree_tok,
+                                                     int32_t* __restrict__ chosen, DrawSpec* __restrict__ spec) {
+    const int b = blockIdx.x, N = t.n, lane = threadIdx.x;
+    bool match = false;
+    int tok = -1;
+    if (lane < N) tok = tree_tok[(int64_t)b * N + lane];
+    if (lane > 0 && lane < N && tok >= 0 && tok < V) {  // a value outside [0, V) never matches
+        const int a = t.parent[lane];
+        const int64_t ra = (int64_t)b * N + a;
+        const double p = exp((double)(target_logits[ra * V + tok] * invT) - (double)lse[ra]);
+        const double thr = fmin((double)eps, (double)delta * exp(-(double)ent[ra]));
+        match = p > thr;
     }
-    __syncthreads();
-    const int node = s_node;
-    if (node < 0) return;  // uniform: fewer parents than blocks
-    const float* lt = target_logits + ((int64_t)b * N + node) * V;
-    float m = -INFINITY, s = 0.0f, wz = 0.0f;  // s = sum e^(z-m), wz = sum e^(z-m) z
-    for (int y = threadIdx.x; y < V; y += BLOCK) {
-        const float z = lt[y] * invT;
-        if (z > m) {
-            const float r = __expf(m - z);
-            s = s * r + 1.0f;
-            wz = wz * r + z;
-            m = z;
-        } else {
-            const float e = __expf(z - m);
-            s += e;
-            wz += e * z;
-        }
-    }
-    float bm = m;
+    const uint64_t mset = __ballot(match);
+    const uint64_t anc = lane < N ? t.anc[lane] : 0ull;
+    const bool accepted = lane < N && ((anc & ~1ull) & ~mset) == 0ull;
+    int key = accepted ? t.depth[lane] * 64 + (63 - lane) : -1;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o, MD_WAVE));
-    if ((threadIdx.x & 63) == 0) shm[threadIdx.x >> 6] = bm;
-    __syncthreads();
-    float Mx = shm[0];
-#pragma unroll
-    for (int i = 1; i < NWAVE; ++i) Mx = fmaxf(Mx, shm[i]);
-    const double f = s > 0.0f ? exp((double)m - (double)Mx) : 0.0;
-    const double S = block_sum<NWAVE>((double)s * f, shs);
-    const double W = block_sum<NWAVE>((double)wz * f, shs);
-    if (threadIdx.x == 0) {
-        const double lse = (double)Mx + log(S);
-        lse_out[(int64_t)b * N + node] = (float)lse;
-        ent_out[(int64_t)b * N + node] = (float)(lse - W / S);
-    }
+    for (int o = 32; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o, MD_WAVE));
+    const int a = 63 - (key & 63);
+    const uint64_t pa = __shfl(anc, a, MD_WAVE);
+    // a node on the path (not the root) names its parent's emitted token
+    int child_on_path = -1;
+    for (int n = 1; n < N; ++n)
+        if (((pa >> n) & 1ull) && t.parent[n] == lane) child_on_path = n;
+    const int ct = __shfl(tok, child_on_path < 0 ? 0 : child_on_path, MD_WAVE);  // the whole wave takes part
+    if (lane < N) chosen[(int64_t)b * N + lane] = child_on_path >= 0 ? ct : -1;
+    if (lane == 0) spec[b] = DrawSpec{a, -1, 0.0f, 0.0f, 0.0f};
 }
 
-// One block per request: match bits (wave 0, one node per lane), the deepest
-// accepted node, the tokens along its path, and the draw at that node.
-__global__ __launch_bounds__(WALK) void k_typical(DevTree t, int V, float invT, float eps, float delta,
-                                                  const float* __restrict__ target_logits,
-                                                  const float* __restrict__ lse, const float* __restrict__ ent,
-                                                  const int32_t* __restrict__ tree_tok,
-                                                  const uint32_t* __restrict__ g_words,
-                                                  int32_t* __restrict__ chosen) {
-    __shared__ float shv[WWAVES];
-    __shared__ int shi[WWAVES];
-    __shared__ int s_a;
-    const int b = blockIdx.x, N = t.n, tid = threadIdx.x;
-    if (tid < MD_WAVE) {
-        const int lane = tid;
-        bool match = false;
-        int tok = -1;
-        if (lane < N) tok = tree_tok[(int64_t)b * N + lane];
-        if (lane > 0 && lane < N && tok >= 0 && tok < V) {  // a value outside [0, V) never matches
-            const int a = t.parent[lane];
-            const int64_t ra = (int64_t)b * N + a;
-            const double p = exp((double)(target_logits[ra * V + tok] * invT) - (double)lse[ra]);
-            const double thr = fmin((double)eps, (double)delta * exp(-(double)ent[ra]));
-            match = p > thr;
-        }
-        const uint64_t mset = __ballot(match);
-        const uint64_t anc = lane < N ? t.anc[lane] : 0ull;
-        const bool accepted = lane < N && ((anc & ~1ull) & ~mset) == 0ull;
-        int key = accepted ? t.depth[lane] * 64 + (63 - lane) : -1;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o, MD_WAVE));
-        const int a = 63 - (key & 63);
-        const uint64_t pa = __shfl(anc, a, MD_WAVE);
-        // a node on the path (not the root) names its parent's emitted token
-        const int child_on_path = [&] {
-            int r = -1;
-            for (int n = 1; n < N; ++n)
-                if (((pa >> n) & 1ull) && t.parent[n] == lane) r = n;
-            return r;
-        }();
-        const int ct = __shfl(tok, child_on_path < 0 ? 0 : child_on_path, MD_WAVE);  // the whole wave takes part
-        if (lane < N) chosen[(int64_t)b * N + lane] = child_on_path >= 0 ? ct : -1;
-        if (lane == 0) s_a = a;
-    }
-    __syncthreads();
-    const int a = s_a;
-    const float* lt = target_logits + ((int64_t)b * N + a) * V;
-    const uint32_t* gw = g_words + (int64_t)b * V;
-    float bv = -INFINITY;
-    int bi = INT_MAX;
-    for (int y = tid; y < V; y += WALK) {
-        const float s = lt[y] * invT + gumbel_f(gw[y]);
-        if (above(s, y, bv, bi)) {
-            bv = s;
-            bi = y;
-        }
-    }
-    block_argmax<WWAVES>(bv, bi, shv, shi);
-    if (tid == 0) chosen[(int64_t)b * N + a] = bi;
+// Workspace of both verifiers: chosen [B][N], lse and entropy [B][N], the
+// row-statistics partials, the draw specs and the draw partials.
+struct VerifyWs {
+    int32_t* chosen;
+    float* lse;
+    float* ent;
+    float* stat_part;
+    DrawSpec* spec;
+    float* draw_v;
+    int* draw_i;
+};
+
+VerifyWs verify_ws_layout(void* base, int B, int N, size_t* total) {
+    char* w = reinterpret_cast<char*>(base);
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        char* p = w ? w + off : nullptr;
+        off += align256(bytes);
+        return p;
+    };
+    VerifyWs L;
+    L.chosen = reinterpret_cast<int32_t*>(take((size_t)B * N * 4));
+    L.lse = reinterpret_cast<float*>(take((size_t)B * N * 4));
+    L.ent = reinterpret_cast<float*>(take((size_t)B * N * 4));
+    // rows x chunks <= kStatBlocks + rows whatever V is (chunks = ceil(kStatBlocks / rows) at most)
+    L.stat_part = reinterpret_cast<float*>(take(((size_t)kStatBlocks + (size_t)B * N) * 3 * 4));
+    L.spec = reinterpret_cast<DrawSpec*>(take((size_t)B * sizeof(DrawSpec)));
+    L.draw_v = reinterpret_cast<float*>(take(((size_t)kDrawBlocks + B) * 4));
+    L.draw_i = reinterpret_cast<int*>(take(((size_t)kDrawBlocks + B) * 4));
+    if (total) *total = off;
+    return L;
 }
 
-int count_parents(const DevTree& t) {
-    int P = 0;
-    for (int n = 0; n < t.n; ++n) {
-        bool has = false;
-        for (int c = n + 1; c < t.n; ++c) has |= t.parent[c] == n;
-        P += has;
-    }
-    return P;
+hipError_t row_stats_launch(const Parents& pl, int B, int N, int V, float invT, const float* target_logits,
+                            const VerifyWs& L, bool entropy, hipStream_t s) {
+    if (pl.n == 0) return hipSuccess;
+    const int rows = B * pl.n, ch = split_chunks(rows, V, kStatBlocks);
+    hipLaunchKernelGGL(k_row_stats_part, dim3((unsigned)(rows * ch)), dim3(BLOCK), 0, s, pl, N, V, invT, ch,
+                       target_logits, L.stat_part);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_row_stats_merge, dim3((unsigned)rows), dim3(MD_WAVE), 0, s, pl, N, ch, L.stat_part, L.lse,
+                       entropy ? L.ent : nullptr);
+    return hipGetLastError();
+}
+
+hipError_t draw_launch(int B, int N, int K, int V, float invT, const float* target_logits, const float* head_logits,
+                       const uint32_t* g_words, const VerifyWs& L, hipStream_t s) {
+    const int ch = split_chunks(B, V, kDrawBlocks);
+    hipLaunchKernelGGL(k_draw_part, dim3((unsigned)(B * ch)), dim3(BLOCK), 0, s, N, K, V, invT, ch, L.spec,
+                       target_logits, head_logits, g_words, L.draw_v, L.draw_i);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_draw_merge, dim3((unsigned)B), dim3(MD_WAVE), 0, s, N, ch, L.spec, L.draw_v, L.draw_i,
+                       L.chosen);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -479,52 +665,55 @@ hipError_t draft_sample_launch(int M, int K, int V, const int* kk, int kmax, flo
                        ch, ks, kmax, pv, pi, pl);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_lse_merge, dim3((rows + 255) / 256), dim3(256), 0, s, pl, rows, ch, lse);
+    hipLaunchKernelGGL(k_lse_merge, dim3(rows), dim3(MD_WAVE), 0, s, pl, ch, lse);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     return topk_merge_launch(pv, pi, M, K, ch, kk, kmax, tok, score, s);
 }
 
-size_t verify_sampled_ws_bytes(int B, int N) { return align256((size_t)B * N * 4); }
+size_t verify_sampled_ws_bytes(int B, int N) {
+    size_t total = 0;
+    verify_ws_layout(nullptr, B, N, &total);
+    return total;
+}
 
 hipError_t verify_sampled_launch(const DevTree& t, int dt, int B, int K, int V, int Hkv, int hd, int Lcap, float T,
                                  const float* target_logits, const float* head_logits, const float* head_lse,
                                  const int32_t* tree_tok, const uint32_t* u_words, const uint32_t* g_words,
                                  void* Kc, void* Vc, int32_t* lens, int32_t* accept_len, int32_t* path,
                                  int32_t* next_tok, int32_t* compact_src, void* ws, hipStream_t s) {
-    int32_t* chosen = reinterpret_cast<int32_t*>(ws);
-    hipLaunchKernelGGL(k_walk_sampled, dim3(B), dim3(WALK), 0, s, t, K, V, 1.0f / T, target_logits, head_logits,
-                       head_lse, tree_tok, u_words, g_words, chosen);
-    hipError_t e = hipGetLastError();
+    const VerifyWs L = verify_ws_layout(ws, B, t.n, nullptr);
+    const float invT = 1.0f / T;
+    const Parents pl = parents_of(t);
+    hipError_t e = row_stats_launch(pl, B, t.n, V, invT, target_logits, L, false, s);
     if (e != hipSuccess) return e;
-    return accept_tokens_launch(t, dt, B, K, Hkv, hd, Lcap, chosen, tree_tok, Kc, Vc, lens, accept_len, path,
+    hipLaunchKernelGGL(k_walk_sampled, dim3(B), dim3(WALK), 0, s, t, K, V, invT, target_logits, head_logits,
+                       head_lse, L.lse, tree_tok, u_words, L.chosen, L.spec);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = draw_launch(B, t.n, K, V, invT, target_logits, head_logits, g_words, L, s);
+    if (e != hipSuccess) return e;
+    return accept_tokens_launch(t, dt, B, K, Hkv, hd, Lcap, L.chosen, tree_tok, Kc, Vc, lens, accept_len, path,
                                 next_tok, compact_src, s);
 }
 
-size_t accept_typical_ws_bytes(int B, int N) { return 3 * align256((size_t)B * N * 4); }
+size_t accept_typical_ws_bytes(int B, int N) { return verify_sampled_ws_bytes(B, N); }
 
 hipError_t accept_typical_launch(const DevTree& t, int dt, int B, int K, int V, int Hkv, int hd, int Lcap, float T,
                                  float eps, float delta, const float* target_logits, const int32_t* tree_tok,
                                  const uint32_t* g_words, void* Kc, void* Vc, int32_t* lens, int32_t* accept_len,
                                  int32_t* path, int32_t* next_tok, int32_t* compact_src, void* ws, hipStream_t s) {
-    char* w = reinterpret_cast<char*>(ws);
-    int32_t* chosen = reinterpret_cast<int32_t*>(w);
-    w += align256((size_t)B * t.n * 4);
-    float* lse = reinterpret_cast<float*>(w);
-    w += align256((size_t)B * t.n * 4);
-    float* ent = reinterpret_cast<float*>(w);
-    const int P = count_parents(t);
+    const VerifyWs L = verify_ws_layout(ws, B, t.n, nullptr);
     const float invT = 1.0f / T;
-    if (P > 0) {
-        hipLaunchKernelGGL(k_row_stats, dim3((unsigned)(B * P)), dim3(BLOCK), 0, s, t, V, invT, P, target_logits, lse,
-                           ent);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(k_typical, dim3(B), dim3(WALK), 0, s, t, V, invT, eps, delta, target_logits, lse, ent,
-                       tree_tok, g_words, chosen);
-    hipError_t e = hipGetLastError();
+    const Parents pl = parents_of(t);
+    hipError_t e = row_stats_launch(pl, B, t.n, V, invT, target_logits, L, true, s);
     if (e != hipSuccess) return e;
-    return accept_tokens_launch(t, dt, B, K, Hkv, hd, Lcap, chosen, tree_tok, Kc, Vc, lens, accept_len, path,
+    hipLaunchKernelGGL(k_typical, dim3(B), dim3(MD_WAVE), 0, s, t, V, invT, eps, delta, target_logits, L.lse, L.ent,
+                       tree_tok, L.chosen, L.spec);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = draw_launch(B, t.n, K, V, invT, target_logits, nullptr, g_words, L, s);
+    if (e != hipSuccess) return e;
+    return accept_tokens_launch(t, dt, B, K, Hkv, hd, Lcap, L.chosen, tree_tok, Kc, Vc, lens, accept_len, path,
                                 next_tok, compact_src, s);
 }

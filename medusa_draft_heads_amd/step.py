@@ -5,8 +5,11 @@ the four library calls in the order the step needs them: heads -> tree ->
 tree attention -> accept. Hydra runs its heads level by level, each level's
 tree tokens feeding the next level's embedding lookup. With target_head the
 verification starts from the target's final hidden states: its LM head with
-a fused argmax gives the target's choice per node, then acceptance. Buffers are allocated
-once, so a step allocates nothing and issues no host synchronisation.
+a fused argmax gives the target's choice per node, then acceptance. Sampled
+decoding ("sampled") draws the drafts from the heads' full logits and verifies
+by rejection sampling; "typical" keeps the top-k drafts and verifies by
+typical acceptance. Buffers are allocated once, so a step allocates nothing
+and issues no host synchronisation.
 """
 from __future__ import annotations
 
@@ -36,6 +39,10 @@ class StepConfig:
     Lcap: int
     max_len: int
     target_head: bool = False  # verify from hidden states Ht [B, N, d] through the LM head Wt [V, d]
+    verify: str = "greedy"  # "greedy", "sampled" (Medusa kinds, M == B) or "typical"
+    temperature: float = 1.0
+    eps: float = 0.09
+    delta: float = 0.3
 
 
 class MedusaStep:
@@ -76,6 +83,19 @@ class MedusaStep:
             self.target_val = torch.empty(B, N, dtype=torch.float32, device=self.dev)
             self.ws_target = torch.empty(max(1, L.md_target_argmax_workspace_bytes(self.dt, B * N, cfg.d, cfg.V)),
                                          **u8)
+        if cfg.verify == "sampled":
+            if cfg.kind == L.MD_HEADS_HYDRA or cfg.M != B or cfg.target_head:
+                raise ValueError("sampled verification takes Medusa heads on one row per request")
+            f32 = dict(dtype=torch.float32, device=self.dev)
+            self.head_logits = torch.empty(B, K, cfg.V, **f32)
+            self.head_lse = torch.empty(B, K, **f32)
+            self.ws_logits = torch.empty(max(1, L.md_heads_logits_workspace_bytes(cfg.kind, B, cfg.d, K)), **u8)
+            self.ws_draft = torch.empty(max(1, L.md_draft_sample_workspace_bytes(B, K, cfg.V, self.kmax)), **u8)
+            self.ws_vs = torch.empty(max(1, L.md_verify_sampled_workspace_bytes(B, N)), **u8)
+        elif cfg.verify == "typical":
+            self.ws_typ = torch.empty(max(1, L.md_accept_typical_workspace_bytes(B, N)), **u8)
+        elif cfg.verify != "greedy":
+            raise ValueError("verify = %r" % cfg.verify)
         self.scale = 1.0 / float(cfg.hd) ** 0.5
         self.h_res = None
 
@@ -110,11 +130,42 @@ class MedusaStep:
         L.md_tree_accept_tokens(self.tree, self.dt, c.B, c.K, c.Hkv, c.hd, c.Lcap, self.target_tok, self.tree_tok, Kc,
                                 Vc, lens, self.accept_len, self.path, self.next_tok, self.compact_src)
 
+    # -- sampled decoding ---------------------------------------------------------
+    def heads_logits(self, h, W, b, U) -> None:
+        c = self.cfg
+        L.md_medusa_heads_logits(c.kind, self.dt, c.M, c.d, c.V, c.K, h, W, b, U, self.head_logits, None,
+                                 self.ws_logits)
+
+    def draft(self, words) -> None:
+        c = self.cfg
+        L.md_draft_sample(c.M, c.K, c.V, c.k_per_head, c.temperature, self.head_logits, words, self.topk_idx,
+                          self.head_lse, self.ws_draft)
+
+    def verify_sampled(self, logits, u_words, g_words, Kc, Vc, lens) -> None:
+        c = self.cfg
+        L.md_tree_verify_sampled(self.tree, self.dt, c.B, c.K, c.V, c.Hkv, c.hd, c.Lcap, c.temperature, logits,
+                                 self.head_logits, self.head_lse, self.tree_tok, u_words, g_words, Kc, Vc, lens,
+                                 self.accept_len, self.path, self.next_tok, self.compact_src, self.ws_vs)
+
+    def accept_typical(self, logits, g_words, Kc, Vc, lens) -> None:
+        c = self.cfg
+        L.md_tree_accept_typical(self.tree, self.dt, c.B, c.K, c.V, c.Hkv, c.hd, c.Lcap, c.temperature, c.eps, c.delta,
+                                 logits, self.tree_tok, g_words, Kc, Vc, lens, self.accept_len, self.path,
+                                 self.next_tok, self.compact_src, self.ws_typ)
+
     # -- a whole step -----------------------------------------------------------
     def run(self, w: Dict[str, torch.Tensor], x: Dict[str, torch.Tensor]) -> None:
         """w: W, b, U (E for Hydra, Wt with target_head); x: h, q, Kc, Vc, lens, root_tok, src_row, and
-        logits (or Ht with target_head)."""
+        logits (or Ht with target_head); sampled decoding adds draft_words, u_words and g_words, typical
+        acceptance g_words."""
         c = self.cfg
+        if c.verify == "sampled":
+            self.heads_logits(x["h"], w["W"], w["b"], w["U"])
+            self.draft(x["draft_words"])
+            self.build(x["src_row"], x["root_tok"], x["lens"])
+            self.attention(x["q"], x["Kc"], x["Vc"], x["lens"])
+            self.verify_sampled(x["logits"], x["u_words"], x["g_words"], x["Kc"], x["Vc"], x["lens"])
+            return
         if c.kind != L.MD_HEADS_HYDRA:
             self.heads(x["h"], w["W"], w["b"], w["U"])
             self.build(x["src_row"], x["root_tok"], x["lens"])
@@ -127,6 +178,8 @@ class MedusaStep:
         if c.target_head:
             self.verify(x["Ht"], w["Wt"])
             self.accept_tokens(x["Kc"], x["Vc"], x["lens"])
+        elif c.verify == "typical":
+            self.accept_typical(x["logits"], x["g_words"], x["Kc"], x["Vc"], x["lens"])
         else:
             self.accept(x["logits"], x["Kc"], x["Vc"], x["lens"])
 

@@ -180,3 +180,59 @@ def test_step_hydra_small():
     step, topo = make_step(wl)
     for s in range(3):
         run_and_compare(wl, w, wd, step, topo, seed, s)
+
+
+@pytest.mark.parametrize("wlname", ["tiny_sampled", "tiny_typical"])
+def test_sampled_step_tiny(wlname):
+    """A whole sampled step (heads' logits -> drafts drawn -> tree -> attention
+    -> rejection-sampling walk or typical acceptance -> compaction) against the
+    oracle's, over three steps. Each stage of the oracle is fed its own
+    upstream values; near ties (margin rule) are counted and checked valid."""
+    import torch
+
+    import medusa_draft_heads_amd as md
+    from synth.workloads import ALL
+
+    wl = ALL[wlname]
+    topo = wl.topology()
+    cfg = md.StepConfig(kind=md.MD_HEADS_MEDUSA, dtype=torch.float32, B=wl.B, M=wl.M, d=wl.d, V=wl.V, K=wl.K,
+                        k_per_head=wl.topk, parent=topo.parent, rank=topo.rank, Hq=wl.Hq, Hkv=wl.Hkv, hd=wl.hd,
+                        Lcap=wl.Lcap, max_len=wl.L_max, verify=wl.verify, temperature=wl.temperature, eps=wl.eps,
+                        delta=wl.delta)
+    step = md.MedusaStep(cfg)
+    seed = 12
+    w = weights(wl, seed)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    lens_seen = []
+    for s in range(3):
+        x = step_inputs(wl, seed, step=s)
+        if wl.verify == "sampled":
+            heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], [1] * wl.K, want_logits=True)
+            dr = oracle.draft_sample(heads["logits"], x["draft_words"], wl.topk, wl.temperature)
+            full = dr["tok"]
+        else:
+            heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], wl.topk)
+            full = heads["idx"]
+        tok, pos = oracle.tree_tokens_medusa(topo.parent, topo.rank, full, x["src_row"], x["root_tok"], x["lens"])
+        xd = {k: to_dev(v) for k, v in x.items()}
+        step.run(wd, xd)
+        torch.cuda.synchronize()
+        if wl.verify == "sampled":
+            assert float(np.max(np.abs(from_dev(step.head_logits) - heads["logits"]))) <= 1e-5 * float(
+                np.max(np.abs(heads["logits"])))
+            assert np.min(dr["margin"]) > TAU["f32"] or pytest.skip("near-tie draft list")
+            ref = oracle.verify_sampled(topo.parent, tok, x["logits"], heads["logits"], wl.temperature, x["u_words"],
+                                        x["g_words"])
+        else:
+            assert np.min(heads["margin"]) > TAU["f32"] or pytest.skip("near-tie top-k list")
+            ref = oracle.typical_accept(topo.parent, tok, x["logits"], wl.temperature, wl.eps, wl.delta,
+                                        x["g_words"])
+        assert np.array_equal(from_dev(step.tree_tok), tok)
+        acc = oracle.accept(topo.parent, wl.K, tok, ref["chosen"], x["lens"])
+        if ref["margin"][0] > 1e-4:
+            for key in ("accept_len", "path", "next_tok", "compact_src"):
+                assert np.array_equal(from_dev(getattr(step, key)), acc[key]), key
+            rK, rV, rl = oracle.compact(x["Kc"], x["Vc"], x["lens"], acc["accept_len"], acc["path"], wl.K)
+            assert np.array_equal(from_dev(xd["Kc"]), rK) and np.array_equal(from_dev(xd["lens"]), rl)
+        lens_seen.append(int(from_dev(step.accept_len)[0]))
+    print(wlname, "accept_len per step", lens_seen)
