@@ -311,6 +311,9 @@ constexpr int ROWB = VK * 2;
 constexpr int A_BYTES = VR * ROWB;         // 16 KB
 constexpr int B_BYTES = VM * ROWB;         // 8 KB (hi; lo follows)
 constexpr int STAGE = A_BYTES + 2 * B_BYTES;  // 32 KB
+constexpr int CSTAGE = A_BYTES + B_BYTES;  // 24 KB: the certified pass's single product
+constexpr int CCOLS = CSTAGE / 512;          // 48 logit columns of 128 rows per stage buffer
+static_assert(3 * CCOLS >= VM && 2 * (3 * CSTAGE + 4 * (2 * VM + 4)) <= 160 * 1024, "three stages, two blocks a CU");
 constexpr int NPA = A_BYTES / 4096;        // 1 KB pieces a wave loads per stage: A
 constexpr int NPB = B_BYTES / 4096;        // and each of hi, lo
 static_assert(2 * (2 * STAGE + 4 * VM) <= 160 * 1024, "two blocks fit the LDS of one CU");
@@ -942,11 +945,27 @@ __global__ __launch_bounds__(BLOCK) void k_rescore(const uint16_t* __restrict__ 
     }
 }
 
-// The wide kernel's tiling with one product per term (hi), the tile's
-// largest U row norm accumulated from the operand fragments, and the
-// certified epilogue: per activation row, the bound E of this tile, a lower
-// bound of the row's k-th best logit (atomicMax), and every entry that can
-// still reach the top k appended to the row's candidate buffer.
+// The k-th largest of the wave's 64 values (one per lane) in the
+// order-preserving int encoding: the largest t with at least k values >= t,
+// built bit by bit from the top (32 ballots; cost independent of k).
+__device__ __forceinline__ int wave_kth_largest_ordered(int v, int k) {
+    const uint32_t u = (uint32_t)v ^ 0x80000000u;  // signed order -> unsigned order
+    uint32_t res = 0u;
+#pragma unroll
+    for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t t = res | (1u << bit);
+        if (__popcll(__ballot(u >= t)) >= k) res = t;
+    }
+    return (int)(res ^ 0x80000000u);
+}
+
+// The wide kernel's tiling with one product per term (hi) in three 24 KB
+// stages, the tile's largest U row norm accumulated from the operand
+// fragments, and the certified epilogue: per activation row, the bound E of
+// this tile, a lower bound of the row's k-th best logit (atomicMax), and
+// every entry that can still reach the top k appended to the row's candidate
+// buffer. The epilogue's global atomics go out for all of a wave's columns at
+// once rather than one column after another.
 __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __restrict__ U,
                                                               const uint16_t* __restrict__ hhi, int M, int d, int V,
                                                               int nh, int head0, int vtiles, int mtiles, KW kk, int Mh,
@@ -956,8 +975,9 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
                                                               int* __restrict__ count,
                                                               float* __restrict__ cand_ub, float* __restrict__ cand_lb,
                                                               int* __restrict__ cand_idx) {
-    __shared__ __align__(1024) unsigned char sbuf0[STAGE];
-    __shared__ __align__(1024) unsigned char sbuf1[STAGE];
+    __shared__ __align__(1024) unsigned char sbuf0[CSTAGE];
+    __shared__ __align__(1024) unsigned char sbuf1[CSTAGE];
+    __shared__ __align__(1024) unsigned char sbuf2[CSTAGE];
     __shared__ float s_bound[VM];
     __shared__ float s_E[VM];
     __shared__ float s_nrm[4];
@@ -1021,20 +1041,34 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
         }
     };
 
+    // Three stage buffers with two stages in flight, as in the narrow kernel:
+    // the wait leaves the newer stage's loads (NPA + NPB per wave) open; the
+    // barrier is LDS-only, so it does not wait for them either.
     const int nk = d / VK;
+    auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
+        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue(min(s + 2, nk - 1) * VK, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cur);
+    };
+    static_assert(NPA + NPB == 6, "the wait count above assumes 6 pieces per wave and stage");
     issue(0, sbuf0);
-    for (int ks = 0; ks < nk; ks += 2) {
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        issue((ks + 1) * VK, sbuf1);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(sbuf0);
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        issue(min(ks + 2, nk - 1) * VK, sbuf0);
-        __builtin_amdgcn_sched_barrier(0);
-        compute(sbuf1);
+    issue(min(1, nk - 1) * VK, sbuf1);
+    int ks = 0;
+    for (; ks + 3 <= nk; ks += 3) {
+        step(ks, sbuf0, sbuf2);
+        step(ks + 1, sbuf1, sbuf0);
+        step(ks + 2, sbuf2, sbuf1);
     }
+    if (ks < nk) step(ks, sbuf0, sbuf2);
+    if (ks + 1 < nk) step(ks + 1, sbuf1, sbuf0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads land before the buffers are reused
+    // a half tile's logits: column c (row of h') takes 512 bytes in buffer c / 48
+    auto colp = [&](int c) -> unsigned char* {
+        unsigned char* bb = c < CCOLS ? sbuf0 : (c < 2 * CCOLS ? sbuf1 : sbuf2);
+        return bb + (c % CCOLS) * 512;
+    };
     // the tile's largest squared row norm (rows past V loaded nothing: norm 0).
     // Lane (g4, c16) holds Gram rows 4 g4 + i of column c16: the diagonal entry
     // when c16 - 4 g4 = i is in 0..3.
@@ -1071,47 +1105,88 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) {
                     const int col = 64 * wc + 16 * cb + c16;
-                    *reinterpret_cast<f32x4*>((wc ? sbuf1 : sbuf0) + (col & 63) * 512 + (((4 * rb + g4) ^ (col & 15)) * 16)) =
-                        acc[rb][cb];
+                    *reinterpret_cast<f32x4*>(colp(col) + (((4 * rb + g4) ^ (col & 15)) * 16)) = acc[rb][cb];
                 }
         }
         __syncthreads();
         const int vh = v0 + 128 * h;
-        for (int col = w; col < VM; col += 4) {
-            const int m = m0 + col;
-            if (m >= M) break;  // uniform
-            const int row = hh * M + m;
-            const int k = kk.v[Mh > 0 ? min(m / Mh, 7) : hh];
-            const float E = s_E[col];
-            const float lim = s_bound[col] - E;  // entries below cannot reach the top k
-            const unsigned char* Sc = (col < 64 ? sbuf0 : sbuf1) + (col & 63) * 512;
-            float x0[2];
-            int cnt = 0;
+        // Lane i owns column w + 4 i (i < 32). Pass 1 reads the tile from LDS
+        // only: per column, the entries that may reach the top k (>= lim) and
+        // their best. The global atomics of all columns then go out together.
+        auto load2 = [&](int col, float (&x)[2]) {
+            const unsigned char* Sc = colp(col);
 #pragma unroll
             for (int e = 0; e < 2; ++e) {
                 const int rr = lane + 64 * e;
-                x0[e] = vh + rr < V ? *reinterpret_cast<const float*>(Sc + (((rr >> 2) ^ (col & 15)) * 16) + (rr & 3) * 4)
-                                    : -INFINITY;
+                x[e] = vh + rr < V ? *reinterpret_cast<const float*>(Sc + (((rr >> 2) ^ (col & 15)) * 16) + (rr & 3) * 4)
+                                   : -INFINITY;
+            }
+        };
+        float my_best = -INFINITY, my_lim = INFINITY, my_E = 0.f;
+        int my_cnt = 0;
+        for (int i = 0; i < 32; ++i) {
+            const int col = w + 4 * i;
+            if (m0 + col >= M) break;  // uniform: columns past M are padding
+            const float E = s_E[col];
+            const float lim = s_bound[col] - E;  // entries below cannot reach the top k
+            float x0[2];
+            load2(col, x0);
+            int cnt = 0;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
                 if (x0[e] < lim) x0[e] = -INFINITY;
                 cnt += __popcll(__ballot(x0[e] != -INFINITY));
             }
-            if (cnt == 0) continue;  // uniform
-            // This half tile's best entry is within E of a logit it bounds from
-            // below: it raises slot (half-tile id % 64) of the row. The k-th
-            // largest slot comes from k distinct entries, so it bounds the row's
-            // k-th best logit from below; it only moves when a slot does.
             float best = fmaxf(x0[0], x0[1]);
 #pragma unroll
             for (int o = 32; o > 0; o >>= 1) best = fmaxf(best, __shfl_xor(best, o, 64));
-            float thr = lim;
-            int old = 0;
-            if (lane == 0) old = atomicMax(slots + (int64_t)row * kSlots + ((2 * vt + h) & (kSlots - 1)), f2o(best - E));
-            old = __shfl(old, 0, 64);
-            if (f2o(best - E) > old) {  // uniform: the slot rose; recompute the k-th largest slot
-                float sv = o2f(__hip_atomic_load(slots + (int64_t)row * kSlots + lane, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT));
+            if (lane == i) {
+                my_best = best;
+                my_cnt = cnt;
+                my_lim = lim;
+                my_E = E;
+            }
+        }
+        // This half tile's best entry is within E of a logit it bounds from
+        // below: it raises slot (half-tile id % 64) of the row. The k-th largest
+        // slot comes from k distinct entries, so it bounds the row's k-th best
+        // logit from below; it only moves when a slot does.
+        const int my_row = hh * M + m0 + w + 4 * lane;
+        bool rose = false;
+        if (lane < 32 && my_cnt > 0) {
+            const int nv = f2o(my_best - my_E);
+            const int old = atomicMax(slots + (int64_t)my_row * kSlots + ((2 * vt + h) & (kSlots - 1)), nv);
+            rose = nv > old;
+            // a slot value at or below the bound read at the tile's start cannot raise the bound
+            rose = rose && (my_best - my_E > my_lim + my_E);
+        }
+        float my_thr = my_lim;
+        // The k-th largest slot of every column whose slot rose: the slot rows
+        // of up to 8 columns are loaded together (one memory round trip), then
+        // each is reduced by a bit search (k > 2) or k rounds of a wave argmax.
+        for (uint64_t rm = __ballot(rose); rm;) {
+            int ids[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                ids[q] = rm ? __ffsll((long long)rm) - 1 : -1;
+                rm &= rm ? rm - 1 : 0ull;
+            }
+            float svs[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                svs[q] = ids[q] >= 0 ? o2f(__hip_atomic_load(slots + (int64_t)(hh * M + m0 + w + 4 * ids[q]) * kSlots + lane,
+                                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+                                     : -INFINITY;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                if (ids[q] < 0) break;  // uniform
+                const int i = ids[q];
+                const int m = m0 + w + 4 * i, row = hh * M + m;
+                const int k = kk.v[Mh > 0 ? min(m / Mh, 7) : hh];
+                float sv = svs[q];
                 float kth = -INFINITY;
-                for (int r = 0; r < k; ++r) {
+                if (k > 2) kth = o2f(wave_kth_largest_ordered(f2o(sv), k));
+                for (int r = 0; k <= 2 && r < k; ++r) {
                     float bv = sv;
                     int bl = lane;
 #pragma unroll
@@ -1128,17 +1203,40 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
                 }
                 if (kth != -INFINITY) {
                     if (lane == 0) atomicMax(bound + row, f2o(kth));
-                    thr = fmaxf(thr, kth - E);
+                    if (lane == i) my_thr = fmaxf(my_thr, kth - my_E);
                 }
             }
-            // append every entry >= thr (value + E is its upper bound)
-            const uint64_t b0 = __ballot(x0[0] != -INFINITY && x0[0] >= thr);
-            const uint64_t b1 = __ballot(x0[1] != -INFINITY && x0[1] >= thr);
-            const int n0 = __popcll(b0), n = n0 + __popcll(b1);
-            int base = 0;
-            if (lane == 0) base = atomicAdd(count + row, n);
-            base = __shfl(base, 0, 64);
-            const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        }
+        // per column, the entries >= thr (value + E is their upper bound): count, reserve, write
+        uint64_t my_b0 = 0ull, my_b1 = 0ull;
+        const uint64_t with = __ballot(lane < 32 && my_cnt > 0);
+        for (uint64_t cm = with; cm; cm &= cm - 1) {
+            const int i = __ffsll((long long)cm) - 1;
+            const int col = w + 4 * i;
+            const float thr = __shfl(my_thr, i, 64), lim = __shfl(my_lim, i, 64);
+            float x0[2];
+            load2(col, x0);
+            // rows past V read as -inf and never qualify, whatever lim and thr are
+            const uint64_t b0 = __ballot(x0[0] != -INFINITY && x0[0] >= lim && x0[0] >= thr);
+            const uint64_t b1 = __ballot(x0[1] != -INFINITY && x0[1] >= lim && x0[1] >= thr);
+            if (lane == i) {
+                my_b0 = b0;
+                my_b1 = b1;
+            }
+        }
+        int my_base = 0;
+        const int my_n = __popcll(my_b0) + __popcll(my_b1);
+        if (my_n > 0) my_base = atomicAdd(count + my_row, my_n);
+        const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+        for (uint64_t cm = __ballot(my_n > 0); cm; cm &= cm - 1) {
+            const int i = __ffsll((long long)cm) - 1;
+            const int col = w + 4 * i, row = hh * M + m0 + col;
+            const uint64_t b0 = __shfl(my_b0, i, 64), b1 = __shfl(my_b1, i, 64);
+            const int base = __shfl(my_base, i, 64);
+            const float E = __shfl(my_E, i, 64);
+            float x0[2];
+            load2(col, x0);
+            const int n0 = __popcll(b0);
             if ((b0 >> lane) & 1) {
                 const int p = base + __popcll(b0 & below);
                 if (p < kCertCap) {
