@@ -490,14 +490,6 @@ hipError_t launch_typed(const DevTree& t, int B, int Hq, int Hkv, int hd, int Lc
     return hipGetLastError();
 }
 
-int device_cus() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                   hipSuccess || n <= 0)
-        n = 256;
-    return n;
-}
-
 // resident blocks per CU of the kernel that will run (one round of blocks)
 int attention_occupancy(int dt, int hd) {
     int n = 0;

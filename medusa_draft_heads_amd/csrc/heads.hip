@@ -527,14 +527,6 @@ int pick_mr(int M, int din) {
     return mr;
 }
 
-int device_cus() {
-    int dev = 0, n = 0;
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
-                                                   hipSuccess || n <= 0)
-        n = 256;
-    return n;
-}
-
 // Resident blocks per CU for a kernel at this dynamic LDS size, capped at 4,
 // so that a grid of CUs x this many blocks runs in a single round.
 template <typename K>

@@ -36,6 +36,8 @@
 // XCD and L2.
 #include <math.h>
 
+#include <algorithm>
+
 #include "md_internal.h"
 
 namespace {
@@ -1372,11 +1374,22 @@ MfmaWs mfma_ws_layout(char* base, int M, int d, int din, int V, int nh, int kmax
     return L;
 }
 
-// the certified pass runs when the vocabulary GEMM sees more than kNarrowRows rows
-bool certified_rows(int M, int nh, int shared_u) { return (shared_u ? nh * M : M) > kNarrowRows; }
+// The certified pass runs when the vocabulary GEMM sees more than
+// kNarrowRows rows, and only if its bounds can work: the vocabulary tiles of
+// one (head, row tile) that run in the first round of resident blocks (two a
+// CU) all start from an empty bound, and their entries (2 x 128 half-tile
+// columns each) must fit the candidate buffer; past that the exact fallback
+// scan would take over. Other shapes run the two-product narrow kernel.
+bool use_certified(int M, int V, int nh, int shared_u) {
+    const int rows = shared_u ? nh * M : M, nh_u = shared_u ? 1 : nh;
+    if (rows <= kNarrowRows) return false;
+    const int vtiles = (V + VR - 1) / VR, mtiles = (rows + VM - 1) / VM;
+    const int first_round = (2 * device_cus() + nh_u * mtiles - 1) / (nh_u * mtiles);
+    return std::min(vtiles, first_round) * 2 * VM <= kCertCap;
+}
 
 size_t heads_mfma_ws_bytes(int M, int d, int din, int V, int nh, int kmax, int shared_u) {
-    return mfma_ws_layout(nullptr, M, d, din, V, nh, kmax, certified_rows(M, nh, shared_u)).bytes;
+    return mfma_ws_layout(nullptr, M, d, din, V, nh, kmax, use_certified(M, V, nh, shared_u)).bytes;
 }
 
 // Launches phase 1 and phase 2. With few rows the caller merges the lists
@@ -1386,7 +1399,7 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
                              float** part_val, int** part_idx, int* nlists) {
     const int vtiles = (a.V + VR - 1) / VR;
     const int mtiles = (a.M + TM - 1) / TM;
-    const bool cert = certified_rows(a.M, a.nh, a.shared_u);
+    const bool cert = use_certified(a.M, a.V, a.nh, a.shared_u);
     const MfmaWs L = mfma_ws_layout(reinterpret_cast<char*>(a.ws), a.M, a.d, a.din, a.V, a.nh, a.kmax, cert);
     const size_t e = (size_t)a.nh * a.M * a.d, crow = (size_t)a.nh * a.M;
     KW kk;

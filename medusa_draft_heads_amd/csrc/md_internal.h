@@ -23,6 +23,15 @@ struct DevTree {
     uint64_t anc[64];       // bit j set: node j is this node or one of its ancestors
 };
 
+// Compute units of the current device (256 if the query fails).
+inline int device_cus() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) !=
+                                                   hipSuccess || n <= 0)
+        n = 256;
+    return n;
+}
+
 // ---- heads (heads.hip) ----
 struct HeadsArgs {
     int kind;  // 0 Medusa, 1 Hydra (a shared projection is Medusa with shared_u)

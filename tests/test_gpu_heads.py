@@ -171,10 +171,13 @@ MFMA_BF16 = Workload("mfma bf16: d=256 V=1000 K=3", "medusa", B=1, d=256, V=1000
 
 @pytest.mark.parametrize("wl,M", [(MFMA_BF16, 8), (MFMA_BF16, 130),
                                   (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9)), 37),
-                                  (replace(MFMA_BF16, d=128, V=140001, K=2, topk=(10, 3)), 9)])
+                                  (replace(MFMA_BF16, d=128, V=140001, K=2, topk=(10, 3)), 9),
+                                  (replace(MFMA_BF16, V=20011, K=1, topk=(10,)), 250)])
 def test_heads_medusa_mfma_rows(wl, M):
     """Eight or more bf16 rows run the MFMA path (ragged row and vocabulary tiles; V = 140,001
-    leaves more than 1,024 partial lists per row for the merge)."""
+    leaves more than 1,024 partial lists per row for the merge). 250 rows of one head over 79
+    vocabulary tiles would run every tile of a row before any bound exists, so they take the
+    two-product narrow kernel (four row tiles) instead of the certified pass."""
     seed = 2000 + M
     w = weights(wl, seed)
     h = synth.normal(seed, 78, (M, wl.d), 1.0, wl.dtype)
@@ -275,14 +278,14 @@ def test_heads_many_rows_without_matrix_cores():
     compare_medusa(wl, gi, gv, gh, ref, label="d=200 M=9")
 
 
-@pytest.mark.parametrize("V", [3000, 10000])
-def test_heads_many_rows_all_logits_tied(V):
-    """Every vocabulary row equal: every logit of a row ties, so the certified pass over 136 rows keeps
-    more than 512 survivors (V = 3000) or overflows its candidate buffer (V = 10000); both fall back to
-    the exact scan and must return the lowest indices."""
-    wl = Workload("tied vocabulary", "medusa", B=1, d=256, V=V, K=2, dtype="bf16", topk=(5, 3), N=4, Hq=4, Hkv=1,
-                  hd=64, L=10)
-    M = 136
+@pytest.mark.parametrize("V,M,topk", [(3000, 136, (5, 3)), (10000, 520, (5, 3, 2, 1))])
+def test_heads_many_rows_all_logits_tied(V, M, topk):
+    """Every vocabulary row equal: every logit of a row ties, so the certified pass keeps more than 512
+    survivors (V = 3000, 136 rows) or overflows its candidate buffer (V = 10000 over 520 rows and 4
+    heads: 20 row tiles, so few enough vocabulary tiles per row run before the bounds exist for the
+    certified pass to be chosen); both fall back to the exact scan and must return the lowest indices."""
+    wl = Workload("tied vocabulary", "medusa", B=1, d=256, V=V, K=len(topk), dtype="bf16", topk=topk, N=4, Hq=4,
+                  Hkv=1, hd=64, L=10)
     w = weights(wl, 4200)
     w["U"][:] = w["U"][:, :1, :]  # one row repeated
     h = synth.normal(4200, 83, (M, wl.d), 1.0, wl.dtype)
