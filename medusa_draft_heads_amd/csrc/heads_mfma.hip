@@ -22,16 +22,20 @@
 //     the tile's largest row norm and |lo|), so only entries whose U hi + E
 //     reaches a lower bound of the k-th best are kept, then re-scored in
 //     float32 from hi + lo; the top k are taken over the re-scored values
-//     (details at k_vocab_mfma_cert). Logits never reach memory.
+//     (details at k_vocab_mfma_cert). The bounds need tiles that have
+//     finished, so shapes whose row tiles would all run in the first round
+//     of blocks stay on the two-product kernel (use_certified). Logits never
+//     reach memory.
 //
 // Residual: block tile 128 weight rows x 128 activation rows, K step 64, 4
 // waves of 64 x 64 (4 x 4 MFMA tiles each), operands staged in LDS (rows
 // padded against bank conflicts) from registers loaded one K step ahead.
 // Vocabulary: block tile 256 vocabulary rows x 128 (many rows) or 64 (few
 // rows) activation rows, K step 32, operands loaded straight from memory
-// into LDS, two blocks per CU (details at the kernels). Both operands are row-major along the contraction, which
-// is exactly the MFMA operand layout (a lane reads 8 consecutive k of one
-// row), so nothing is transposed. Blocks that share a weight tile (the
+// into LDS in three stages with two in flight, two blocks per CU (details at
+// the kernels). Both operands are row-major along the contraction, which is
+// exactly the MFMA operand layout (a lane reads 8 consecutive k of one row),
+// so nothing is transposed. Blocks that share a weight tile (the
 // activation tiles of one weight tile) get ids spaced by 8, i.e. the same
 // XCD and L2.
 #include <math.h>
