@@ -45,6 +45,17 @@ def log(msg: str) -> None:
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def file_sha(path: str) -> str:
     with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()
@@ -58,11 +69,14 @@ def main() -> int:
     ap.add_argument("--workload", default="70b",
                     choices=["70b", "70b_chain", "8b", "tiny", "70b_b8", "hydra_b4", "70b_shared", "70b_lmhead",
                              "70b_sampled", "70b_typical"])
-    ap.add_argument("--sets", type=int, default=8, help="input sets rotated to keep them out of the 256 MB MALL")
+    ap.add_argument("--sets", type=int, default=0,
+                    help="input sets rotated per step (0: enough that the non-weight bytes exceed twice the 256 MB "
+                         "Infinity Cache, at most 16)")
     ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps timed for the CPU baseline (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (scale factor for HBM counters)")
     ap.add_argument("--seed", type=int, default=70)
+    ap.add_argument("--cpu-1thread", type=int, default=1, help="also time one oracle step on one thread (0: skip)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only; --gpus %d is not supported" % args.gpus, file=sys.stderr)
@@ -100,55 +114,72 @@ def main() -> int:
     sets, cpu_times, acc_oracle = [], [], []
     threads = oracle.threads()
     sample_note = ""
-    for s in range(args.sets):
-        x = step_inputs(wl, args.seed, step=s)
+    if args.sets <= 0:  # rotate past the 256 MB Infinity Cache: non-weight bytes >= 2 x 256 MB
+        per_set = sum(v.nbytes for v in step_inputs(wl, args.seed, step=0).values())
+        args.sets = int(min(16, max(2, -(-2 * (256 << 20) // per_set))))
+        log("%d input sets of %.1f MB" % (args.sets, per_set / 1e6))
+
+    def oracle_tree(x):
+        """The oracle's heads and tree tokens for one input set, and their time."""
+        nonlocal sample_note
         ta = time.perf_counter()
+        heads = None
         if hydra:
             hy = oracle.hydra_expand(w["W"], w["b"], w["U"], w["E"], x["h"], topo.parent, topo.rank, wl.topk,
                                      x["root_tok"], x["lens"])
-            tok = hy["tree_tok"]
-            heads_time = time.perf_counter() - ta
-        elif wl.verify == "sampled":  # one row per request: the heads' logits, then the drafts drawn from them
+            return hy["tree_tok"], None, time.perf_counter() - ta
+        if wl.verify == "sampled":  # one row per request: the heads' logits, then the drafts drawn from them
             heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], [1] * wl.K, want_logits=True)
             full = oracle.draft_sample(heads["logits"], x["draft_words"], wl.topk, wl.temperature)["tok"]
             tok, _ = oracle.tree_tokens_medusa(topo.parent, topo.rank, full, x["src_row"], x["root_tok"], x["lens"])
-            heads_time = time.perf_counter() - ta
+            return tok, heads, time.perf_counter() - ta
+        rows = sorted(set(int(r) for r in x["src_row"]))
+        heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], wl.topk, rows=rows)
+        full = np.full((wl.M, wl.K, wl.kmax), -1, np.int32)
+        for j, r in enumerate(rows):
+            full[r] = heads["idx"][j]
+        tok, _ = oracle.tree_tokens_medusa(topo.parent, topo.rank, full, x["src_row"], x["root_tok"], x["lens"])
+        if wl.M != len(rows):
+            sample_note = " (heads timed on the %d rows that build the trees, scaled to all %d rows)" % (
+                len(rows), wl.M)
+        return tok, heads, (time.perf_counter() - ta) * (wl.M / len(rows))
+
+    def oracle_rest(x, tok, heads, logits):
+        """The rest of the oracle's step (attention, verification, acceptance, compaction), and its time."""
+        tc = time.perf_counter()
+        oracle.tree_attention(topo.parent, x["q"], x["Kc"], x["Vc"], x["lens"])
+        if wl.target_head:
+            tstar = oracle.target_argmax(x["Ht"].reshape(wl.B * topo.n, wl.d), w["Wt"])[0].reshape(wl.B, topo.n)
+        elif wl.verify == "sampled":  # the token after every node the walk passes through
+            tstar = oracle.verify_sampled(topo.parent, tok, logits, heads["logits"], wl.temperature, x["u_words"],
+                                          x["g_words"])["chosen"]
+        elif wl.verify == "typical":
+            tstar = oracle.typical_accept(topo.parent, tok, logits, wl.temperature, wl.eps, wl.delta,
+                                          x["g_words"])["chosen"]
         else:
-            rows = sorted(set(int(r) for r in x["src_row"]))
-            heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], wl.topk, rows=rows)
-            full = np.full((wl.M, wl.K, wl.kmax), -1, np.int32)
-            for j, r in enumerate(rows):
-                full[r] = heads["idx"][j]
-            tok, _ = oracle.tree_tokens_medusa(topo.parent, topo.rank, full, x["src_row"], x["root_tok"], x["lens"])
-            heads_time = (time.perf_counter() - ta) * (wl.M / len(rows))
-            if wl.M != len(rows):
-                sample_note = " (heads timed on the %d rows that build the trees, scaled to all %d rows)" % (
-                    len(rows), wl.M)
+            tstar = oracle.argmax(logits)
+        r = oracle.accept(topo.parent, wl.K, tok, tstar, x["lens"])
+        oracle.compact(x["Kc"], x["Vc"], x["lens"], r["accept_len"], r["path"], wl.K)
+        return r, time.perf_counter() - tc
+
+    first = None
+    for s in range(args.sets):
+        x = step_inputs(wl, args.seed, step=s)
+        tok, heads, heads_time = oracle_tree(x)
         if wl.target_head:  # verification through the target's LM head: plant its hidden states
             plant_hidden(x["Ht"], w["Wt"], topo, tok, wl.a, seed=args.seed, step=s)
+            logits = None
         elif wl.verify == "greedy":
             logits = plant(x["logits"], topo, tok, wl.a, seed=args.seed, step=s)
         else:  # sampled decoding: the target's logits as drawn, N(0, 1)
             logits = x["logits"]
         if s < args.cpu_steps:
-            tc = time.perf_counter()
-            oracle.tree_attention(topo.parent, x["q"], x["Kc"], x["Vc"], x["lens"])
-            if wl.target_head:
-                tstar = oracle.target_argmax(x["Ht"].reshape(wl.B * topo.n, wl.d), w["Wt"])[0].reshape(wl.B, topo.n)
-            elif wl.verify == "sampled":  # the token after every node the walk passes through
-                tstar = oracle.verify_sampled(topo.parent, tok, logits, heads["logits"], wl.temperature, x["u_words"],
-                                              x["g_words"])["chosen"]
-            elif wl.verify == "typical":
-                tstar = oracle.typical_accept(topo.parent, tok, logits, wl.temperature, wl.eps, wl.delta,
-                                              x["g_words"])["chosen"]
-            else:
-                tstar = oracle.argmax(logits)
-            r = oracle.accept(topo.parent, wl.K, tok, tstar, x["lens"])
-            oracle.compact(x["Kc"], x["Vc"], x["lens"], r["accept_len"], r["path"], wl.K)
-            td = time.perf_counter()
-            cpu_times.append(heads_time + (td - tc))
+            r, rest_time = oracle_rest(x, tok, heads, logits)
+            cpu_times.append(heads_time + rest_time)
             acc_oracle.append([int(v) for v in r["accept_len"]])
             log("oracle step %d: %.2f s (accept_len %s)" % (s, cpu_times[-1], acc_oracle[-1]))
+            if first is None:
+                first = x
         xd = {k: to_dev(v) for k, v in x.items() if k != "logits"}
         if not wl.target_head:
             xd["logits"] = to_dev(logits)
@@ -156,6 +187,14 @@ def main() -> int:
         sets.append(xd)
     torch.cuda.synchronize()
     log("%d input sets on the GPU" % len(sets))
+    cpu_1thread = None
+    if first is not None and args.cpu_1thread:  # the same oracle step on one thread
+        oracle.set_threads(1)
+        tok1, heads1, t1 = oracle_tree(first)
+        _, t2 = oracle_rest(first, tok1, heads1, first.get("logits"))  # the logits were planted in place
+        oracle.set_threads(threads)
+        cpu_1thread = t1 + t2
+        log("oracle step on 1 thread: %.2f s" % cpu_1thread)
 
     kind = md.MD_HEADS_HYDRA if hydra else (md.MD_HEADS_MEDUSA_SHARED if wl.shared_u else md.MD_HEADS_MEDUSA)
     cfg = md.StepConfig(kind=kind,
@@ -231,10 +270,15 @@ def main() -> int:
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
     # the same number of steps again, now with HIP events around the vocabulary
-    # kernel (recorded by the library on its stream) and the verification
+    # kernel (recorded by the library on its stream) and the verification, and
+    # one at every step boundary for the distribution of step times
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    bounds[0].record(stream)
     for i in range(args.steps):
         one_step(args.warmup + args.steps + i, ev[i], lm_ev[i] if lm_ev else None)
+        bounds[i + 1].record(stream)
     torch.cuda.synchronize()
+    per_step = np.array([bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)])
     vocab_ms = sum(a.elapsed_time(b) for pairs in ev for a, b in pairs) / args.steps
     acc_len = step.accept_len.cpu().numpy().tolist()
 
@@ -331,7 +375,10 @@ def main() -> int:
         cpu = {"value": round(1.0 / float(np.median(cpu_times)), 4), "unit": "steps/s", "cores": threads,
                "kind": "oracle",
                "sample": "%d whole oracle steps (heads, tree, attention, argmax, accept, compaction) on the same "
-                         "seeded inputs, median%s" % (len(cpu_times), sample_note)}
+                         "seeded inputs, median%s" % (len(cpu_times), sample_note),
+               "cpu_model": cpu_model()}
+        if cpu_1thread:
+            cpu["value_1_thread"] = round(1.0 / cpu_1thread, 4)
     E = 1.0
     run = 1.0
     for ai in wl.a:
@@ -345,6 +392,11 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "step_ms_distribution": {"median": round(float(np.median(per_step)), 4),
+                                 "p10": round(float(np.percentile(per_step, 10)), 4),
+                                 "p90": round(float(np.percentile(per_step, 90)), 4),
+                                 "pass": "the instrumented pass: every step also records its boundary event and the "
+                                         "kernel events (~6 us of GPU time each)"},
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
