@@ -14,9 +14,11 @@
 //   bits (rounding it to bf16 moves logits by ~1e-3 and reorders near-equal
 //   candidates); as hi + lo it enters with ~16 (relative error <= 2^-17).
 //   - up to 128 rows (HBM-bound): logits = U hi + U lo, two products per
-//     term, in the narrow kernel; per column (row of h') the block's best k
-//     logits, filtered first by a running lower bound of the k-th best;
-//     the per-block lists go through the same k-way merge as the GEMV path;
+//     term, in the narrow kernel (up to 64 rows) or the register-streamed
+//     one (65 to 128, one row tile so U is read once); per column (row of
+//     h') the block's best k logits, filtered first by a running lower
+//     bound of the k-th best; the per-block lists go through the same k-way
+//     merge as the GEMV path;
 //   - more rows (matrix-bound): one product, U hi, and a certificate: every
 //     logit of a vocabulary tile is within E of U hi (Cauchy-Schwarz with
 //     the tile's largest row norm and |lo|), so only entries whose U hi + E
@@ -32,8 +34,9 @@
 // padded against bank conflicts) from registers loaded one K step ahead.
 // Vocabulary: block tile 256 vocabulary rows x 128 (many rows) or 64 (few
 // rows) activation rows, K step 32, operands loaded straight from memory
-// into LDS in three stages with two in flight, two blocks per CU (details at
-// the kernels). Both operands are row-major along the contraction, which is
+// into LDS in three stages with two in flight, two blocks per CU; from 65
+// to 128 rows, all activation rows in one tile with U streamed into
+// registers (details at the kernels). Both operands are row-major along the contraction, which is
 // exactly the MFMA operand layout (a lane reads 8 consecutive k of one row),
 // so nothing is transposed. Blocks that share a weight tile (the
 // activation tiles of one weight tile) get ids spaced by 8, i.e. the same
@@ -519,7 +522,7 @@ static_assert(NB_BYTES == 4096, "one 1 KB piece of each of hi, lo per wave");
 static_assert(2 * (3 * NSTAGE + 4 * NM) <= 160 * 1024, "two blocks fit the LDS of one CU");
 static_assert(NM * VR * 4 <= 3 * NSTAGE, "the logit tile fits the three stage buffers");
 constexpr int NCOLS_PER_BUF = NSTAGE / (VR * 4);  // 24 columns of 256 logits per stage buffer
-constexpr int kNarrowRows = 128;  // up to this many activation rows the narrow kernel runs (1 or 2 row tiles)
+constexpr int kNarrowRows = 128;  // up to this many activation rows the two-product kernels run (narrow to 64, then direct)
 
 template <int NS>
 __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* __restrict__ U,
@@ -691,6 +694,292 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* 
         }
         if (rounds == k && lane == k - 1) atomicMax(bound + (int64_t)hh * M + m, f2o(ov));
     }
+}
+
+// ---- 65 to 128 activation rows: the projection streamed into registers ----
+//
+// Past 64 activation rows the narrow kernel needs two row tiles, and each
+// re-reads the whole projection. This kernel takes all activation rows
+// (5 to 8 column blocks of 16) in one tile, so U is read once: each wave
+// streams its 64 vocabulary rows of U as MFMA A fragments straight into a
+// ring of P register stages (16 bytes a lane per 16-row block and K step,
+// P K steps of 4 KB in flight per wave). The activation rows (hi and, with
+// NS = 2, lo) form the B operand, shared by the four waves; they reach LDS
+// by buffer->LDS loads issued in the same stream as the A loads, P - 1 steps
+// ahead, one stage per step in P separately named buffers. Block tile: 256
+// vocabulary rows (one list per activation row and tile, as in the narrow
+// kernel); two blocks per CU. Both kernels read U in the MFMA operand shape
+// (16 rows x 64 bytes a load), which streams at about 4.8 TB/s on this part
+// against 7.1 TB/s for runs of 256 bytes a row; the products and their order
+// are the same, so both give the same logits bit for bit.
+// N 16-byte LDS reads at la + 1024 i (i < N), in blocks of up to four that
+// each end with their own wait (the results are complete when a block ends).
+__device__ __forceinline__ void lds4(u32x4& a, u32x4& b, u32x4& c, u32x4& e, uint32_t la) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:1024\n\tds_read_b128 %2, %4 offset:2048\n\t"
+        "ds_read_b128 %3, %4 offset:3072\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(e)
+        : "v"(la)
+        : "memory");
+}
+__device__ __forceinline__ void lds2(u32x4& a, u32x4& b, uint32_t la) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %2 offset:1024\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(a), "=&v"(b)
+                 : "v"(la)
+                 : "memory");
+}
+__device__ __forceinline__ void lds1(u32x4& a, uint32_t la) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(a) : "v"(la) : "memory");
+}
+template <int N>
+__device__ __forceinline__ void lds_frags(u32x4 (&f)[N], uint32_t la) {
+#pragma unroll
+    for (int i = 0; i + 4 <= N; i += 4) lds4(f[i], f[i + 1], f[i + 2], f[i + 3], la + 1024 * i);
+    constexpr int r = N & 3, b = N - r;
+    if constexpr (r >= 2) lds2(f[b], f[b + 1], la + 1024 * b);
+    if constexpr (r & 1) lds1(f[N - 1], la + 1024 * (N - 1));
+}
+
+template <int NS, int CB>
+struct DirectCfg {
+    static constexpr int STG = NS * CB * 1024;               // LDS bytes of one B stage (16 columns x 64 B a piece)
+    static constexpr int NPC = NS * CB;                       // 1 KB pieces a stage
+    static constexpr int NB = (NPC + 3) / 4;                  // pieces each wave loads a stage (the last repeats)
+    static constexpr int P = (NPC <= 9 && CB <= 5) ? 8 : ((NPC <= 12 && CB <= 6) ? 6 : 4);  // K steps in flight
+    static constexpr int CPP = (P * STG) / 16384 < 1 ? 1 : ((P * STG) / 16384 > CB ? CB : (P * STG) / 16384);
+    static constexpr int SB = STG > (16384 * CPP) / P ? STG : (16384 * CPP) / P;  // bytes of each named buffer
+    static constexpr int COLS_PER_BUF = SB / 1024;             // logit columns of 256 rows per buffer
+    static constexpr int WAIT = 4 + (P - 2) * (NB + 4);       // loads left open when a stage is consumed
+    static_assert(SB % 1024 == 0 && WAIT <= 63, "whole 1 KB columns; the wait fits the counter");
+    static_assert(COLS_PER_BUF * P >= 16 * CPP, "a pass of the logit tile fits the stage buffers");
+    static_assert(2 * P * SB + 2 * 4 * 128 <= 160 * 1024, "two blocks fit the LDS of one CU");
+};
+
+template <int NS, int CB>
+__global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* __restrict__ U,
+                                                                const uint16_t* __restrict__ hhi,
+                                                                const uint16_t* __restrict__ hlo, int M, int d, int V,
+                                                                int nh, int head0, int vtiles, int kmax, KW kk, int Mh,
+                                                                float* __restrict__ part_val,
+                                                                int* __restrict__ part_idx, int* __restrict__ bound) {
+    typedef DirectCfg<NS, CB> C;
+    constexpr int P = C::P;
+    __shared__ __align__(1024) unsigned char db0[C::SB];
+    __shared__ __align__(1024) unsigned char db1[C::SB];
+    __shared__ __align__(1024) unsigned char db2[C::SB];
+    __shared__ __align__(1024) unsigned char db3[C::SB];
+    __shared__ __align__(1024) unsigned char db4[P > 4 ? C::SB : 16];
+    __shared__ __align__(1024) unsigned char db5[P > 5 ? C::SB : 16];
+    __shared__ __align__(1024) unsigned char db6[P > 6 ? C::SB : 16];
+    __shared__ __align__(1024) unsigned char db7[P > 7 ? C::SB : 16];
+    __shared__ float s_bound[CB * 16];
+    auto buf = [&](int j) -> unsigned char* {
+        switch (j) {
+            case 0: return db0;
+            case 1: return db1;
+            case 2: return db2;
+            case 3: return db3;
+            case 4: return db4;
+            case 5: return db5;
+            case 6: return db6;
+            default: return db7;
+        }
+    };
+    const int hh = blockIdx.x / vtiles, vt = blockIdx.x - hh * vtiles;
+    if (hh >= nh) return;
+    const int v0 = vt * VR;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int g4 = lane >> 4, c16 = lane & 15;
+    const int64_t hbase = (int64_t)hh * M * d;
+    const int nk = d / VK;
+
+    // A: the lane's rows are 64 w + 16 rb + c16, its 16 bytes the chunk g4 of
+    // the K step (the MFMA A layout); rows past V read as zero
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(U + ((int64_t)(head0 + hh) * V + v0) * d), 0, min(V - v0, VR) * d * 2, RSRC3);
+    const uint32_t aoff = (uint32_t)(64 * w + c16) * d * 2 + 16 * g4;
+    // B: piece p of a stage is operand p / CB (hi, lo), column block p % CB;
+    // the lane loads column 16 (p % CB) + lane / 4, chunk (lane % 4) ^
+    // ((column / 2) % 4) (the LDS swizzle of the other kernels)
+    const __amdgpu_buffer_rsrc_t rH =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(hhi + hbase), 0, M * d * 2, RSRC3);
+    const __amdgpu_buffer_rsrc_t rL =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(hlo + hbase), 0, M * d * 2, RSRC3);
+    const int bc = lane >> 2;
+    const uint32_t boff = (uint32_t)bc * d * 2 + 16 * ((lane & 3) ^ ((bc >> 1) & 3));
+
+    u32x4 ra[P][4];
+    auto issue_a = [&](int s, u32x4 (&r)[4]) {
+        const uint32_t o = aoff + (uint32_t)min(s, nk - 1) * (VK * 2);
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+            r[rb] = __builtin_amdgcn_raw_buffer_load_b128(rA, o + (uint32_t)(16 * rb) * d * 2, 0, 0);
+    };
+    auto issue_b = [&](int s, unsigned char* dst) {
+        const uint32_t ko = (uint32_t)min(s, nk - 1) * (VK * 2);
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j) {
+            const int p = min(w + 4 * j, C::NPC - 1);
+            const int op = p / CB, cb = p - (p / CB) * CB;
+            const uint32_t o = boff + (uint32_t)(16 * cb) * d * 2 + ko;
+            dmab((NS == 2 && op) ? rL : rH, dst + p * 1024, o);
+        }
+    };
+
+    f32x4 acc[4][CB];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < CB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    const int slot = (g4 ^ ((c16 >> 1) & 3)) * 16;
+    // The B fragments are read by inline assembly that waits for them in the
+    // same block: the compiler does not see these LDS reads, so it adds no
+    // waits of its own for the buffer->LDS loads still in flight into other
+    // stages (the explicit wait and barrier of each step order them).
+    auto compute = [&](const u32x4 (&r)[4], const unsigned char* sB) {
+        u32x4 bf[C::NPC];
+        const uint32_t la = (uint32_t)(uintptr_t)(sB + c16 * ROWB + slot);
+        lds_frags<C::NPC>(bf, la);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) {
+#pragma unroll
+            for (int cb = 0; cb < CB; ++cb) {
+                const bf16x8 b = __builtin_bit_cast(bf16x8, bf[s * CB + cb]);
+#pragma unroll
+                for (int rb = 0; rb < 4; ++rb)
+                    acc[rb][cb] =
+                        __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, r[rb]), b, acc[rb][cb], 0, 0, 0);
+            }
+        }
+    };
+
+    // Issue order: A(0), then per step t < 0 ... each step s issues B(s + P - 1)
+    // into the buffer read at step s - 1 and, after its MFMAs, A(s + P) into
+    // the ring slot it just consumed. When step s starts, everything up to
+    // B(s) must have landed; issued after it are A(s + 1) and P - 2 steps of
+    // (B, A): 4 + (P - 2) (NB + 4) loads.
+    issue_a(0, ra[0]);
+#pragma unroll
+    for (int j = 1; j < P; ++j) {
+        issue_b(j - 1, buf(j - 1));
+        issue_a(j, ra[j]);
+    }
+    auto step = [&](int s, int j) {
+        __builtin_amdgcn_s_waitcnt((C::WAIT & 15) | ((C::WAIT >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue_b(s + P - 1, buf((j + P - 1) % P));
+        __builtin_amdgcn_sched_barrier(0);
+        compute(ra[j], buf(j));
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a(s + P, ra[j]);
+    };
+    // whole rounds of P steps with no branch inside (the compiler's waits for
+    // the ring registers then match on every path), then the tail
+    int s0 = 0;
+    for (; s0 + P <= nk; s0 += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) step(s0 + j, j);
+    }
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+        if (s0 + j < nk) step(s0 + j, j);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads land before the buffers are reused
+    if (tid < CB * 16)
+        s_bound[tid] = tid < M ? o2f(__hip_atomic_load(bound + (int64_t)hh * M + tid, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT))
+                               : INFINITY;
+    // Logits tile in passes of CPP column blocks: column c of a pass takes
+    // 1 KB in buffer c / COLS_PER_BUF, its 16-byte groups permuted by c % 16.
+    auto colp = [&](int c) -> unsigned char* { return buf(c / C::COLS_PER_BUF) + (c % C::COLS_PER_BUF) * 1024; };
+#pragma unroll
+    for (int cb0 = 0; cb0 < CB; cb0 += C::CPP) {
+        __syncthreads();  // operand stages, or the previous pass's logits, are dead
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+#pragma unroll
+            for (int cq = 0; cq < C::CPP; ++cq) {
+                if (cb0 + cq < CB) {
+                    const int col = 16 * cq + c16;
+                    *reinterpret_cast<f32x4*>(colp(col) + (((16 * w + 4 * rb + g4) ^ (col & 15)) * 16)) =
+                        acc[rb][cb0 + cq];
+                }
+            }
+        __syncthreads();
+        const int ncol = 16 * min(C::CPP, CB - cb0);
+        for (int col = w; col < ncol; col += 4) {
+            const int m = 16 * cb0 + col;
+            if (m >= M) break;  // uniform: columns past M are padding
+            const int k = kk.v[Mh > 0 ? min(m / Mh, 7) : hh];
+            const float T = s_bound[m];
+            const unsigned char* Sc = colp(col);
+            float x[4];
+            int cnt = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int rr = lane + 64 * q;
+                x[q] = v0 + rr < V ? *reinterpret_cast<const float*>(Sc + (((rr >> 2) ^ (col & 15)) * 16) + (rr & 3) * 4)
+                                   : -INFINITY;
+                if (x[q] < T) x[q] = -INFINITY;
+                cnt += __popcll(__ballot(x[q] != -INFINITY));
+            }
+            const int rounds = cnt < k ? cnt : k;
+            float ov = -INFINITY;
+            int oi = INT_MAX;
+            for (int r = 0; r < rounds; ++r) {
+                float bv = x[0];
+                int bi = v0 + lane;
+#pragma unroll
+                for (int q = 1; q < 4; ++q)
+                    if (ranks_above(x[q], v0 + lane + 64 * q, bv, bi)) {
+                        bv = x[q];
+                        bi = v0 + lane + 64 * q;
+                    }
+#pragma unroll
+                for (int o = 32; o > 0; o >>= 1) {
+                    const float tv = __shfl_xor(bv, o, 64);
+                    const int ti = __shfl_xor(bi, o, 64);
+                    if (ranks_above(tv, ti, bv, bi)) {
+                        bv = tv;
+                        bi = ti;
+                    }
+                }
+                if (lane == r) {
+                    ov = bv;
+                    oi = bi;
+                }
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    if (bi == v0 + lane + 64 * q) x[q] = -INFINITY;
+            }
+            if (lane < kmax) {
+                const int64_t o = (((int64_t)hh * M + m) * vtiles + vt) * kmax + lane;
+                part_val[o] = lane < rounds ? ov : -INFINITY;
+                part_idx[o] = lane < rounds ? oi : INT_MAX;
+            }
+            if (rounds == k && lane == k - 1) atomicMax(bound + (int64_t)hh * M + m, f2o(ov));
+        }
+    }
+}
+
+template <int NS>
+hipError_t launch_direct(int cb, dim3 grid, hipStream_t s, const uint16_t* U, const uint16_t* hhi, const uint16_t* hlo,
+                         int M, int d, int V, int nh, int head0, int vtiles, int kmax, KW kk, int Mh, float* pv,
+                         int* pi, int* bound) {
+#define MD_DIRECT(CBV)                                                                                               \
+    case CBV:                                                                                                        \
+        hipLaunchKernelGGL((k_vocab_mfma_direct<NS, CBV>), grid, dim3(BLOCK), 0, s, U, hhi, hlo, M, d, V, nh, head0, \
+                           vtiles, kmax, kk, Mh, pv, pi, bound);                                                     \
+        break;
+    switch (cb) {
+        MD_DIRECT(5)
+        MD_DIRECT(6)
+        MD_DIRECT(7)
+        MD_DIRECT(8)
+        default: return hipErrorInvalidValue;
+    }
+#undef MD_DIRECT
+    return hipGetLastError();
 }
 
 // ---- certified single-product vocabulary pass (many rows) ----
@@ -1299,9 +1588,13 @@ hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt
     const uint16_t* h = reinterpret_cast<const uint16_t*>(H);
     const uint16_t* wt = reinterpret_cast<const uint16_t*>(Wt);
     if (R <= kNarrowRows) {
-        const int nmt = (R + NM - 1) / NM;
-        hipLaunchKernelGGL(k_vocab_mfma_narrow<1>, dim3(8 * nmt * ((vtiles + 7) / 8)), dim3(BLOCK), 0, s, wt, h, h, R, d,
-                           V, 1, 0, vtiles, nmt, 1, kk, 0, pv, pi, bound);
+        if (R > NM) {
+            err = launch_direct<1>((R + 15) / 16, dim3(vtiles), s, wt, h, h, R, d, V, 1, 0, vtiles, 1, kk, 0, pv, pi, bound);
+            if (err != hipSuccess) return err;
+        } else {
+            hipLaunchKernelGGL(k_vocab_mfma_narrow<1>, dim3(8 * ((vtiles + 7) / 8)), dim3(BLOCK), 0, s, wt, h, h, R, d, V,
+                               1, 0, vtiles, 1, 1, kk, 0, pv, pi, bound);
+        }
         *nlists = vtiles;
     } else {
         hipLaunchKernelGGL(k_vocab_mfma<1>, dim3(8 * vmtiles * ((vtiles + 7) / 8)), dim3(BLOCK), 0, s, wt, h, h, R, d, V,
@@ -1456,9 +1749,17 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     const uint16_t* U = reinterpret_cast<const uint16_t*>(a.U);
     const int head0 = a.shared_u ? 0 : a.head0, Mh = a.shared_u ? a.M : 0;
     if (!cert) {  // few rows: HBM-bound, two products and the deeper pipeline
-        const int nmt = (rows_v + NM - 1) / NM;
-        hipLaunchKernelGGL(k_vocab_mfma_narrow<2>, dim3(8 * nmt * ((units2 + 7) / 8)), dim3(BLOCK), 0, s, U, L.hhi,
-                           L.hlo, rows_v, a.d, a.V, nh_u, head0, vtiles, nmt, a.kmax, kk, Mh, L.pv, L.pi, L.bound);
+        // 65 to 128 rows: one register-streamed tile; otherwise 64-row tiles
+        // (more than 128 rows only where the certified pass cannot work)
+        if (rows_v > NM && rows_v <= kNarrowRows) {
+            err = launch_direct<2>((rows_v + 15) / 16, dim3(units2), s, U, L.hhi, L.hlo, rows_v, a.d, a.V, nh_u, head0,
+                                   vtiles, a.kmax, kk, Mh, L.pv, L.pi, L.bound);
+            if (err != hipSuccess) return err;
+        } else {
+            const int nmt = (rows_v + NM - 1) / NM;
+            hipLaunchKernelGGL(k_vocab_mfma_narrow<2>, dim3(8 * nmt * ((units2 + 7) / 8)), dim3(BLOCK), 0, s, U, L.hhi,
+                               L.hlo, rows_v, a.d, a.V, nh_u, head0, vtiles, nmt, a.kmax, kk, Mh, L.pv, L.pi, L.bound);
+        }
         *nlists = vtiles;
     } else {  // many rows: one product and the certificate
         const int vmtiles = (rows_v + VM - 1) / VM;

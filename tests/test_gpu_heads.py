@@ -172,12 +172,19 @@ MFMA_BF16 = Workload("mfma bf16: d=256 V=1000 K=3", "medusa", B=1, d=256, V=1000
 @pytest.mark.parametrize("wl,M", [(MFMA_BF16, 8), (MFMA_BF16, 130),
                                   (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9)), 37),
                                   (replace(MFMA_BF16, d=128, V=140001, K=2, topk=(10, 3)), 9),
-                                  (replace(MFMA_BF16, V=20011, K=1, topk=(10,)), 250)])
+                                  (replace(MFMA_BF16, V=20011, K=1, topk=(10,)), 250),
+                                  (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9)), 65),
+                                  (replace(MFMA_BF16, V=4099, topk=(10, 4, 1)), 72),
+                                  (replace(MFMA_BF16, d=128, V=3001, topk=(5, 2, 1)), 100),
+                                  (replace(MFMA_BF16, V=2053, K=1, topk=(7,)), 128)])
 def test_heads_medusa_mfma_rows(wl, M):
     """Eight or more bf16 rows run the MFMA path (ragged row and vocabulary tiles; V = 140,001
     leaves more than 1,024 partial lists per row for the merge). 250 rows of one head over 79
     vocabulary tiles would run every tile of a row before any bound exists, so they take the
-    two-product narrow kernel (four row tiles) instead of the certified pass."""
+    two-product narrow kernel (four row tiles) instead of the certified pass. 65 to 128 rows run
+    the register-streamed kernel with all rows in one tile (5 to 8 column blocks; 65 leaves one
+    valid column in the last block; at d = 128, 100 rows fill exactly one prefetch ring of 4 K
+    steps; at d = 256, 72 rows end their ring of 6 steps with a tail of 2)."""
     seed = 2000 + M
     w = weights(wl, seed)
     h = synth.normal(seed, 78, (M, wl.d), 1.0, wl.dtype)
@@ -208,10 +215,12 @@ def test_heads_medusa_mfma_full_size_sampled(wl_name, M, rows):
 @pytest.mark.parametrize("wl,M", [(replace(TINY_F32, shared_u=True), 1), (replace(TINY_F32, shared_u=True), 3),
                                   (replace(SMALL_BF16, shared_u=True), 1), (replace(SMALL_BF16, shared_u=True), 2),
                                   (replace(MFMA_BF16, shared_u=True), 8),
-                                  (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9), shared_u=True), 37)])
+                                  (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9), shared_u=True), 37),
+                                  (replace(MFMA_BF16, V=3001, topk=(6, 3, 1), shared_u=True), 30)])
 def test_heads_shared_projection(wl, M):
     """One U [V, d] for every head: the K x M vectors h' share the pass over U (GEMV rows and MFMA
-    columns of several heads, each with its own top-k width)."""
+    columns of several heads, each with its own top-k width; 3 heads x 30 rows = 90 columns run
+    the register-streamed kernel)."""
     seed = 3000 + M
     w = weights(wl, seed)
     assert w["U"].ndim == 2

@@ -5,8 +5,9 @@ The argmax follows the margin rule with k = 1: where the oracle's top two
 logits are more than tau apart the token must match, otherwise the GPU's
 token must be within tau of the maximum. Values follow the relative
 tolerance. Sizes cover the GEMV path (float32, few rows), the MFMA path
-(bf16, ragged rows and vocabulary tiles, more than 1,024 partial lists) and
-the 70B-shaped LM head over a 64-node tree.
+(bf16, ragged rows and vocabulary tiles, more than 1,024 partial lists; 65 to
+128 rows in one register-streamed tile) and the 70B-shaped LM head over a
+64-node tree.
 """
 import math
 
@@ -26,6 +27,9 @@ CASES = [
     ("f32 gemv R=16", "f32", 16, 256, 4096),
     ("bf16 gemv R=5", "bf16", 5, 512, 5003),
     ("bf16 mfma R=64", "bf16", 64, 512, 5003),
+    ("bf16 mfma R=100 one tile", "bf16", 100, 256, 4099),
+    ("bf16 mfma R=128 one tile", "bf16", 128, 128, 2053),
+    ("bf16 mfma R=72 fewer K steps than the ring", "bf16", 72, 128, 3001),
     ("bf16 mfma R=130 ragged", "bf16", 130, 256, 3001),
     ("bf16 mfma many lists R=9", "bf16", 9, 128, 140001),
     ("70B-shaped LM head, 64 nodes", "bf16", 64, 8192, 128256),
