@@ -353,33 +353,33 @@ __global__ __launch_bounds__(NW * MD_WAVE) void k_vocab_topk(const T* __restrict
         si[(m * NW + wv) * MD_WAVE + lane] = lane < km[m] ? li[m] : INT_MAX;
     }
     __syncthreads();
-    if (wv != 0) return;
-#pragma unroll
-    for (int m = 0; m < MR; ++m) {
-        if (m >= mr) continue;
-        float bv = -INFINITY, btv = -INFINITY;
-        int bi = INT_MAX, bti = INT_MAX;
-        for (int w2 = 0; w2 < NW; ++w2) {
-            const float cv = sv[(m * NW + w2) * MD_WAVE + lane];
-            const int ci = si[(m * NW + w2) * MD_WAVE + lane];
-            uint64_t bm = __ballot(lane < km[m] && ranks_above(cv, ci, btv, bti));
-            while (bm) {
-                const int src = __ffsll((long long)bm) - 1;
-                bm &= bm - 1;
-                const float x = __shfl(cv, src, MD_WAVE);
-                const int xi = __shfl(ci, src, MD_WAVE);
-                if (ranks_above(x, xi, btv, bti)) {
-                    list_insert(bv, bi, x, xi, km[m], lane);
-                    btv = __shfl(bv, km[m] - 1, MD_WAVE);
-                    bti = __shfl(bi, km[m] - 1, MD_WAVE);
-                }
+    // wave m merges the lists of activation row m (the rows in parallel)
+    static_assert(NW >= MR, "one wave per activation row");
+    const int m = wv;
+    if (m >= mr) return;
+    const int k = kk.v[Mh > 0 ? min((m0 + m) / Mh, 7) : hh];
+    float bv = -INFINITY, btv = -INFINITY;
+    int bi = INT_MAX, bti = INT_MAX;
+    for (int w2 = 0; w2 < NW; ++w2) {
+        const float cv = sv[(m * NW + w2) * MD_WAVE + lane];
+        const int ci = si[(m * NW + w2) * MD_WAVE + lane];
+        uint64_t bm = __ballot(lane < k && ranks_above(cv, ci, btv, bti));
+        while (bm) {
+            const int src = __ffsll((long long)bm) - 1;
+            bm &= bm - 1;
+            const float x = __shfl(cv, src, MD_WAVE);
+            const int xi = __shfl(ci, src, MD_WAVE);
+            if (ranks_above(x, xi, btv, bti)) {
+                list_insert(bv, bi, x, xi, k, lane);
+                btv = __shfl(bv, k - 1, MD_WAVE);
+                bti = __shfl(bi, k - 1, MD_WAVE);
             }
         }
-        if (lane < kmax) {
-            const int64_t o = (((int64_t)hh * M + m0 + m) * wg_per_head + wgi) * kmax + lane;
-            part_val[o] = bv;
-            part_idx[o] = bi;
-        }
+    }
+    if (lane < kmax) {
+        const int64_t o = (((int64_t)hh * M + m0 + m) * wg_per_head + wgi) * kmax + lane;
+        part_val[o] = bv;
+        part_idx[o] = bi;
     }
 }
 
