@@ -18,10 +18,12 @@
 // owns 16 query rows and computes S^T = K Q^T per 16-key block, then
 // O^T += V^T P^T. In this orientation a lane keeps one query row (lane % 16)
 // in both the score and the output accumulators, so the running max, the
-// rescale and the bf16 P operand never leave the lane. K tiles sit in LDS
-// row-major (rows padded by 16 B against bank conflicts), V tiles transposed
-// (key-contiguous) so the V^T operand is two 8-byte reads. float32 storage
-// (small workloads) uses an LDS-tiled FMA kernel.
+// rescale and the bf16 P operand never leave the lane. K and V tiles of 32
+// keys go from memory straight into LDS (buffer->LDS loads) in the cache's
+// own row layout, chunks permuted per row against bank conflicts, three
+// stages with two in flight; the V^T operand comes from gfx950's
+// transposing LDS read (ds_read_b64_tr_b16), so V is never transposed by
+// hand. float32 storage (small workloads) uses an LDS-tiled FMA kernel.
 #include <math.h>
 
 #include "md_internal.h"
@@ -35,9 +37,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int QT = 16;  // query rows per block (FMA kernel)
 constexpr int MQT = 64; // query rows per block (MFMA kernel: 4 waves x 16)
-constexpr int MKT = 64; // keys per tile (MFMA kernel)
-constexpr int KPAD = 8; // K row padding, bf16 elements
-constexpr int VPAD = 4; // V^T row padding, bf16 elements (rows stay 8-byte aligned)
+constexpr int DKT = 32; // keys per tile (MFMA kernel)
 constexpr int KT = 64;  // keys per tile
 constexpr int BLOCK = 256;
 constexpr int NWAVE = BLOCK / MD_WAVE;
@@ -246,6 +246,46 @@ __device__ __forceinline__ bool xcd_group_decode(int id, int qtiles, int ngroups
     return group < ngroups;
 }
 
+// word 3 of a raw buffer resource on this chip family (32-bit data format, no swizzle)
+constexpr int RSRC3 = 0x00020000;
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ void dmab(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, off, 0, 0, 0);
+}
+
+// K and V tiles keep the cache's row layout in LDS (one key a row, HD * 2
+// bytes), with the 16-byte chunks of key row k permuted: chunk c sits in
+// slot c ^ swz(k). K fragments are 16 rows x one chunk (swzK spreads 16
+// consecutive rows over 16 slots); V^T fragments come from the transposing
+// read below, 4 rows x 2 chunks per 16 lanes (swzV spreads 8 consecutive
+// rows over distinct chunk pairs).
+template <int CPR>
+__device__ __forceinline__ int swzK(int k) {
+    return k % CPR;
+}
+template <int CPR>
+__device__ __forceinline__ int swzV(int k) {
+    return (2 * (k % 4) + 8 * ((k / 4) % 2)) % CPR;
+}
+
+// ds_read_b64_tr_b16: within each 16-lane group, lane 4r + j receives as its
+// element e the 16-bit word j of the 8 bytes addressed by lane 4e + r of the
+// group. So if lane a of group g addresses V[key0 + 4g + a/4][d0 + 4(a%4)],
+// lane c of the group receives V[key0 + 4g + e][d0 + c], e = 0..3: four
+// consecutive keys of one dimension, the layout of a V^T operand fragment.
+__device__ __forceinline__ u32x2 lds_tr4(const unsigned char* p) {
+    const v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)(p));
+    return __builtin_bit_cast(u32x2, v);
+}
+
+// One block: 64 query rows (4 waves x 16) of one (request, kv head) against
+// the keys [k0, k1) of its split, DKT keys a tile. K and V tiles go from
+// memory straight into LDS (buffer->LDS loads, 16 bytes a lane, one
+// instruction per 1 KB piece) in three separately named stage buffers with
+// two tiles in flight, so no register staging, no transposing writes and one
+// barrier per tile.
 template <int HD>
 __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int Hkv, int Lcap, int max_len,
                                                      const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
@@ -253,11 +293,16 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
                                                      float scale, int splits, int chunk, int qtiles, int ngroups,
                                                      float* __restrict__ po, float* __restrict__ pm,
                                                      float* __restrict__ pl) {
-    constexpr int CH = HD / 8;            // 16-byte chunks per key row
-    constexpr int KCH = MKT * CH / BLOCK; // K chunks per thread
-    constexpr int VIT = (MKT / 4) * CH;   // V items (4 keys x 8 dims)
-    __shared__ __align__(16) uint16_t Ks[MKT][HD + KPAD];
-    __shared__ __align__(16) uint16_t Vt[HD][MKT + VPAD];
+    constexpr int CPR = HD / 8;          // 16-byte chunks per key row
+    constexpr int ROWB = HD * 2;         // bytes per key row
+    constexpr int TILEB = DKT * ROWB;    // bytes of one K (or V) tile
+    constexpr int NPK = TILEB / 1024;    // 1 KB pieces per tile
+    constexpr int KPP = 1024 / ROWB;     // keys per piece
+    constexpr int PPW = 2 * (NPK / 4);   // pieces each wave loads per stage (K and V)
+    static_assert(NPK % 4 == 0 && KPP * CPR == MD_WAVE, "whole pieces, one lane per 16-byte chunk");
+    __shared__ __align__(1024) unsigned char sb0[2 * TILEB];
+    __shared__ __align__(1024) unsigned char sb1[2 * TILEB];
+    __shared__ __align__(1024) unsigned char sb2[2 * TILEB];
 
     int grp, qt;
     if (!xcd_group_decode(blockIdx.x, qtiles, ngroups, grp, qt)) return;
@@ -270,7 +315,8 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
     const int L = min(max(lens[b], 0), max_len);
     const int nkeys = L + N;
     const int k0 = s * chunk, k1 = min(k0 + chunk, nkeys);
-    const int tid = threadIdx.x, lane = tid & (MD_WAVE - 1), w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & (MD_WAVE - 1);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
     const int g4 = lane >> 4, c16 = lane & 15;
     const int64_t kvbase = ((int64_t)b * Hkv + g) * Lcap;
 
@@ -293,70 +339,52 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
 #pragma unroll
     for (int j = 0; j < HD / 16; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // every thread stages KCH 16-byte K chunks and one V item (4 keys x 8
-    // dims, transposed in registers into 8 dim rows of 4 keys); the next
-    // tile's loads are in flight while the current tile is computed
-    u32x4 kreg[KCH], vreg[4];
-    const int vk4 = tid / CH, vch = tid - (tid / CH) * CH;  // V item: key group of 4, dim chunk
-    const bool vload = tid < VIT;
-    int kt_fetch = k0;
-#define MD_FETCH_TILE(kt0_)                                                                                   \
-    {                                                                                                         \
-        _Pragma("unroll") for (int j = 0; j < KCH; ++j) {                                                     \
-            const int i = tid + BLOCK * j;                                                                    \
-            const int kk = i / CH, ch = i - (i / CH) * CH;                                                    \
-            const int key = (kt0_) + kk;                                                                      \
-            kreg[j] = key < k1 ? *reinterpret_cast<const u32x4*>(Kc + (kvbase + key) * HD + ch * 8)           \
-                               : u32x4{0u, 0u, 0u, 0u};                                                       \
-        }                                                                                                     \
-        _Pragma("unroll") for (int e = 0; e < 4; ++e) {                                                       \
-            const int key = (kt0_) + vk4 * 4 + e;                                                             \
-            vreg[e] = (vload && key < k1) ? *reinterpret_cast<const u32x4*>(Vc + (kvbase + key) * HD + vch * 8) \
-                                          : u32x4{0u, 0u, 0u, 0u};                                            \
-        }                                                                                                     \
-    }
-    if (k0 < k1) MD_FETCH_TILE(kt_fetch);
-    for (int kt0 = k0; kt0 < k1; kt0 += MKT) {
-        __syncthreads();
+    // keys past nkeys read as zero (and are masked); the cache rows of this
+    // (request, kv head) bound every load
+    const __amdgpu_buffer_rsrc_t rK =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Kc + kvbase * HD), 0, nkeys * ROWB, RSRC3);
+    const __amdgpu_buffer_rsrc_t rV =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(Vc + kvbase * HD), 0, nkeys * ROWB, RSRC3);
+    // piece p of a tile holds keys KPP p .. KPP p + KPP - 1; the lane writes
+    // slot lane % CPR of key KPP p + lane / CPR and loads the chunk that
+    // belongs there
+    const int lkey = lane / CPR, lslot = lane % CPR;
+    auto issue = [&](int kt0, unsigned char* stg) {
 #pragma unroll
-        for (int j = 0; j < KCH; ++j) {
-            const int i = tid + BLOCK * j;
-            const int kk = i / CH, ch = i - (i / CH) * CH;
-            *reinterpret_cast<u32x4*>(&Ks[kk][ch * 8]) = kreg[j];
+        for (int jj = 0; jj < NPK / 4; ++jj) {
+            const int p = w + 4 * jj, key = KPP * p + lkey;
+            dmab(rK, stg + p * 1024, (uint32_t)(kt0 + key) * ROWB + 16 * (lslot ^ swzK<CPR>(key)));
         }
-        if (vload) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                // word j of each key holds dims 2j (low half) and 2j+1 (high half)
-                const uint32_t a0 = vreg[0][j], a1 = vreg[1][j], a2 = vreg[2][j], a3 = vreg[3][j];
-                *reinterpret_cast<u32x2*>(&Vt[vch * 8 + 2 * j][vk4 * 4]) =
-                    u32x2{(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-                *reinterpret_cast<u32x2*>(&Vt[vch * 8 + 2 * j + 1][vk4 * 4]) =
-                    u32x2{(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-            }
+        for (int jj = 0; jj < NPK / 4; ++jj) {
+            const int p = w + 4 * jj, key = KPP * p + lkey;
+            dmab(rV, stg + TILEB + p * 1024, (uint32_t)(kt0 + key) * ROWB + 16 * (lslot ^ swzV<CPR>(key)));
         }
-        __syncthreads();
-        if (kt0 + MKT < k1) MD_FETCH_TILE(kt0 + MKT);
+    };
 
-        // S^T for four 16-key blocks: st[kb][i] = S[row][kt0 + 16 kb + 4 g4 + i]
-        f32x4 st[4];
+    auto compute = [&](int kt0, const unsigned char* sK) {
+        const unsigned char* sV = sK + TILEB;
+        // S^T for two 16-key blocks: st[kb][i] = S[row][kt0 + 16 kb + 4 g4 + i]
+        f32x4 st[2];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
             st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            const int key = 16 * kb + c16;
 #pragma unroll
             for (int c = 0; c < HD / 32; ++c) {
-                const bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(&Ks[kb * 16 + c16][8 * g4 + 32 * c]));
+                const bf16x8 a = __builtin_bit_cast(
+                    bf16x8, *reinterpret_cast<const u32x4*>(sK + key * ROWB + 16 * ((g4 + 4 * c) ^ swzK<CPR>(key))));
                 st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], st[kb], 0, 0, 0);
             }
         }
         // scores in the log2 domain: s = scale * log2(e) * q.k, so that
         // e^{scale q.k - m} = 2^{s - m'} with the native exp2
-        float p[4][4];
+        float p[2][4];
         float tmax = -INFINITY;
-        if (kt0 + MKT <= k1 && kt0 + MKT <= L) {
+        if (kt0 + DKT <= k1 && kt0 + DKT <= L) {
             // the whole tile lies in the cached prefix: every key is visible
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     p[kb][i] = st[kb][i] * scale_log2;
@@ -364,7 +392,7 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
                 }
         } else {
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb) {
+            for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int kidx = kt0 + kb * 16 + 4 * g4 + i;
@@ -382,7 +410,7 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
         const float alpha = __builtin_amdgcn_exp2f(m_i - mref);
         float psum = 0.f;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 p[kb][i] = __builtin_amdgcn_exp2f(p[kb][i] - mref);
@@ -398,22 +426,53 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
         }
         m_i = m_new;
 
-        // O^T += V^T P^T over two 32-key halves
+        // O^T += V^T P^T over the tile's 32 keys: operand k index 8 g4 + e is
+        // key 4 g4 + e (e < 4) or 16 + 4 g4 + e - 4 (e >= 4), in both operands
+        const bf16x8 pb = {(__bf16)p[0][0], (__bf16)p[0][1], (__bf16)p[0][2], (__bf16)p[0][3],
+                           (__bf16)p[1][0], (__bf16)p[1][1], (__bf16)p[1][2], (__bf16)p[1][3]};
+        const int vk = 4 * g4 + (c16 >> 2);  // the key this lane addresses (first 16-key block)
+        const int vq = c16 & 3;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int kb0 = 2 * half, kb1 = 2 * half + 1;
-            const bf16x8 pb = {(__bf16)p[kb0][0], (__bf16)p[kb0][1], (__bf16)p[kb0][2], (__bf16)p[kb0][3],
-                               (__bf16)p[kb1][0], (__bf16)p[kb1][1], (__bf16)p[kb1][2], (__bf16)p[kb1][3]};
-#pragma unroll
-            for (int j = 0; j < HD / 16; ++j) {
-                const u32x2 lo = *reinterpret_cast<const u32x2*>(&Vt[16 * j + c16][kb0 * 16 + 4 * g4]);
-                const u32x2 hi = *reinterpret_cast<const u32x2*>(&Vt[16 * j + c16][kb1 * 16 + 4 * g4]);
-                const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-                o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[j], 0, 0, 0);
-            }
+        for (int j = 0; j < HD / 16; ++j) {
+            const int ch = 2 * j + (vq >> 1), bo = 8 * (vq & 1);
+            const u32x2 lo = lds_tr4(sV + vk * ROWB + 16 * (ch ^ swzV<CPR>(vk)) + bo);
+            const u32x2 hi = lds_tr4(sV + (vk + 16) * ROWB + 16 * (ch ^ swzV<CPR>(vk + 16)) + bo);
+            const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
+            o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[j], 0, 0, 0);
         }
+    };
+
+    // Tile i lives in buffer i % 3; two tiles are always in flight (past the
+    // last one the loads repeat it, keeping the count uniform), so the wait
+    // before a tile leaves one tile's loads, PPW per wave, open. The barrier
+    // is LDS-only: each wave's own wait makes its pieces land, lgkmcnt(0)
+    // retires its reads of the buffer the next loads overwrite.
+    const int ntile = k1 > k0 ? (k1 - k0 + DKT - 1) / DKT : 0;
+    auto tile_at = [&](int i) { return k0 + min(i, max(ntile - 1, 0)) * DKT; };
+    auto step = [&](int i, const unsigned char* cur, unsigned char* nxt) {
+        static_assert(PPW == 4 || PPW == 2, "the waits below assume 2 or 4 pieces a wave");
+        if constexpr (PPW == 4)
+            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+        else
+            asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue(tile_at(i + 2), nxt);
+        __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this tile's work
+        compute(k0 + i * DKT, cur);
+    };
+    if (ntile > 0) {
+        issue(tile_at(0), sb0);
+        issue(tile_at(1), sb1);
+        int i = 0;
+        for (; i + 3 <= ntile; i += 3) {
+            step(i, sb0, sb2);
+            step(i + 1, sb1, sb0);
+            step(i + 2, sb2, sb1);
+        }
+        if (i < ntile) step(i, sb0, sb2);
+        if (i + 1 < ntile) step(i + 1, sb1, sb0);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads land before the block ends
     }
-#undef MD_FETCH_TILE
 
     if (rvalid) {
         const int64_t row = ((int64_t)b * N + node) * Hq + h;
@@ -509,7 +568,7 @@ int attention_occupancy(int dt, int hd) {
 AttnPlan attention_plan(int dt, int B, int N, int Hq, int Hkv, int hd, int max_len) {
     AttnPlan p;
     const int qt = dt == 0 ? QT : MQT;
-    const int kt = dt == 0 ? KT : MKT;
+    const int kt = dt == 0 ? KT : DKT;
     p.rows = N * (Hq / Hkv);
     p.qtiles = (p.rows + qt - 1) / qt;
     const int base = B * Hkv * p.qtiles;
