@@ -403,28 +403,29 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
                 }
             }
         }
-        tmax = fmaxf(tmax, xor16(tmax));
-        tmax = fmaxf(tmax, xor32(tmax));
-        const float m_new = fmaxf(m_i, tmax);
-        const float mref = m_new == -INFINITY ? 0.f : m_new;  // rows with no visible key yet
-        const float alpha = __builtin_amdgcn_exp2f(m_i - mref);
-        float psum = 0.f;
+        // Lazy reference: P = 2^(s - m_i) with m_i the row's reference, moved
+        // only when a score passes it by more than 8 (P stays below 2^8); the
+        // four lanes of a row always share m_i. l_i sums this lane's keys
+        // only (one reduction at the end).
+        if (__ballot(tmax > m_i + 8.f)) {
+            tmax = fmaxf(tmax, xor16(tmax));
+            tmax = fmaxf(tmax, xor32(tmax));
+            if (tmax > m_i) {  // the same for the row's four lanes
+                const float alpha = __builtin_amdgcn_exp2f(m_i - tmax);  // 0 while m_i is -inf
+                l_i *= alpha;
+#pragma unroll
+                for (int j = 0; j < HD / 16; ++j) o[j] *= alpha;
+                m_i = tmax;
+            }
+        }
+        const float mref = m_i == -INFINITY ? 0.f : m_i;  // rows with no visible key yet
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 p[kb][i] = __builtin_amdgcn_exp2f(p[kb][i] - mref);
-                psum += p[kb][i];
+                l_i += p[kb][i];
             }
-        psum += xor16(psum);
-        psum += xor32(psum);
-        l_i = l_i * alpha + psum;
-        // the running max of most rows stops moving after the first tiles
-        if (__ballot(m_new != m_i)) {
-#pragma unroll
-            for (int j = 0; j < HD / 16; ++j) o[j] *= alpha;
-        }
-        m_i = m_new;
 
         // O^T += V^T P^T over the tile's 32 keys: operand k index 8 g4 + e is
         // key 4 g4 + e (e < 4) or 16 + 4 g4 + e - 4 (e >= 4), in both operands
@@ -474,6 +475,8 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads land before the block ends
     }
 
+    l_i += xor16(l_i);  // the row's sum over its four lanes
+    l_i += xor32(l_i);
     if (rvalid) {
         const int64_t row = ((int64_t)b * N + node) * Hq + h;
 #pragma unroll
