@@ -19,6 +19,7 @@
 #include <math.h>
 
 #include "md_internal.h"
+#include "md_wave.h"
 
 namespace {
 
@@ -32,15 +33,7 @@ constexpr int kCompactLds = 32 * 1024;  // bytes of LDS staging for the compacti
 __device__ __forceinline__ bool beats(float v, int i, float w, int j) { return v > w || (v == w && i < j); }
 
 __device__ __forceinline__ void wave_argmax(float& v, int& i) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(v, o, MD_WAVE);
-        const int oi = __shfl_xor(i, o, MD_WAVE);
-        if (beats(ov, oi, v, i)) {
-            v = ov;
-            i = oi;
-        }
-    }
+    md_wave::wave_argmax(v, i);
 }
 
 __global__ __launch_bounds__(BLOCK) void k_argmax_part(const float* __restrict__ logits, int V, int chunks,
@@ -144,8 +137,7 @@ __global__ __launch_bounds__(BLOCK) void k_accept(DevTree t, int K, int Hkv, int
         const int dep = lane < N ? t.depth[lane] : 0;
         // deepest accepted node, lowest index among equals: maximise depth*64 + (63 - lane)
         int key = accepted ? dep * 64 + (63 - lane) : -1;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o, MD_WAVE));
+        key = md_wave::wave_max(key);
         const int a = 63 - (key & 63);
         const int da = key >> 6;
         const uint64_t pa = __shfl(anc, a, MD_WAVE);  // a's root path as a node set

@@ -26,6 +26,7 @@
 #include <algorithm>
 
 #include "md_internal.h"
+#include "md_wave.h"
 
 namespace {
 
@@ -385,9 +386,11 @@ __global__ __launch_bounds__(NW * MD_WAVE) void k_vocab_topk(const T* __restrict
 
 // One block per (row m, head slot hh). Every block of the vocabulary kernel
 // left one sorted list of its k best; the k best of the head are a k-way
-// merge of those lists: k rounds of a block-wide argmax over the list heads,
-// each round popping the winning list. Vocabulary indices are unique, so
-// the order (value desc, index asc) is strict and the winner is unique.
+// merge of those lists: each wave takes k rounds of a wave-wide argmax over
+// its lanes' list heads, each round popping the winning list, and one wave
+// merges the waves' sorted lists the same way (no block barrier per round).
+// Vocabulary indices are unique, so the order (value desc, index asc) is
+// strict and the winner is unique.
 // LPT lists per thread; LPT = 0 takes any number of lists: each thread first
 // folds lists tid, tid + BLOCK, ... into one sorted list of its k best.
 template <int LPT>
@@ -396,10 +399,8 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
                                                       KK kk, int kmax, int32_t* __restrict__ topk_idx,
                                                       float* __restrict__ topk_val) {
     constexpr int KM = MD_MAX_TOPK_DEV;
-    __shared__ float wv_s[NWAVE];
-    __shared__ int wi_s[NWAVE], wo_s[NWAVE];
-    __shared__ float out_v[KM];
-    __shared__ int out_i[KM];
+    __shared__ float wl_v[NWAVE][KM];
+    __shared__ int wl_i[NWAVE][KM];
     const int m = blockIdx.x / nh, hh = blockIdx.x - (blockIdx.x / nh) * nh;
     const int k = kk.v[hh];
     const int tid = threadIdx.x, lane = tid & (MD_WAVE - 1), w = tid >> 6;
@@ -444,6 +445,9 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
             }
         }
     }
+    // Each wave first pops its own k best from its lanes' lists (no block
+    // barrier per round), then wave 0 merges the NWAVE sorted wave lists:
+    // NWAVE * k <= 64 candidates, one per lane.
     for (int r = 0; r < k; ++r) {
         float bv = v[0][0];
         int bi = ix[0][0], bo = tid * NL;
@@ -454,38 +458,13 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
                 bi = ix[l][0];
                 bo = tid * NL + l;
             }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float ov = __shfl_xor(bv, o, MD_WAVE);
-            const int oi = __shfl_xor(bi, o, MD_WAVE);
-            const int oo = __shfl_xor(bo, o, MD_WAVE);
-            if (ranks_above(ov, oi, bv, bi)) {
-                bv = ov;
-                bi = oi;
-                bo = oo;
-            }
-        }
+        md_wave::wave_argmax(bv, bi, bo);
         if (lane == 0) {
-            wv_s[w] = bv;
-            wi_s[w] = bi;
-            wo_s[w] = bo;
+            wl_v[w][r] = bv;
+            wl_i[w][r] = bi;
         }
-        __syncthreads();
-        float gv = wv_s[0];
-        int gi = wi_s[0], go = wo_s[0];
-#pragma unroll
-        for (int w2 = 1; w2 < NWAVE; ++w2)
-            if (ranks_above(wv_s[w2], wi_s[w2], gv, gi)) {
-                gv = wv_s[w2];
-                gi = wi_s[w2];
-                go = wo_s[w2];
-            }
-        if (tid == 0) {
-            out_v[r] = gv;
-            out_i[r] = gi;
-        }
-        if (go / NL == tid) {  // pop the winning list's head
-            const int lw = go - tid * NL;
+        if (bo / NL == tid) {  // pop the winning list's head
+            const int lw = bo - tid * NL;
 #pragma unroll
             for (int l = 0; l < NL; ++l) {
                 if (l != lw) continue;
@@ -498,13 +477,32 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
                 ix[l][KM - 1] = INT_MAX;
             }
         }
-        __syncthreads();
     }
-    if (tid < kmax) {
-        const bool ok = tid < k && out_i[tid] != INT_MAX;
-        const int64_t o = ((int64_t)m * nh + hh) * kmax + tid;
-        topk_idx[o] = ok ? out_i[tid] : -1;
-        topk_val[o] = ok ? out_v[tid] : -INFINITY;
+    __syncthreads();
+    if (w != 0) return;
+    static_assert(NWAVE * KM <= MD_WAVE, "one wave list entry per lane");
+    float cv = lane < NWAVE * k ? wl_v[lane / k][lane % k] : -INFINITY;
+    int ci = lane < NWAVE * k ? wl_i[lane / k][lane % k] : INT_MAX;
+    float ov = -INFINITY;
+    int oi = INT_MAX;
+    for (int r = 0; r < k; ++r) {
+        float bv = cv;
+        int bi = ci;
+        md_wave::wave_argmax(bv, bi);
+        if (lane == r) {
+            ov = bv;
+            oi = bi;
+        }
+        if (ci == bi) {  // indices are unique: exactly the winner drops out
+            cv = -INFINITY;
+            ci = INT_MAX;
+        }
+    }
+    if (lane < kmax) {
+        const bool ok = lane < k && oi != INT_MAX;
+        const int64_t o = ((int64_t)m * nh + hh) * kmax + lane;
+        topk_idx[o] = ok ? oi : -1;
+        topk_val[o] = ok ? ov : -INFINITY;
     }
 }
 

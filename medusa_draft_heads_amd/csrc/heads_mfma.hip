@@ -46,6 +46,7 @@
 #include <algorithm>
 
 #include "md_internal.h"
+#include "md_wave.h"
 
 namespace {
 
@@ -480,15 +481,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restr
                     bv = x[1];
                     bi = vh + lane + 64;
                 }
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) {
-                    const float tv = __shfl_xor(bv, o, 64);
-                    const int ti = __shfl_xor(bi, o, 64);
-                    if (ranks_above(tv, ti, bv, bi)) {
-                        bv = tv;
-                        bi = ti;
-                    }
-                }
+                md_wave::wave_argmax(bv, bi);
                 if (lane == r) {
                     ov = bv;
                     oi = bi;
@@ -670,15 +663,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* 
                     bv = x[q];
                     bi = v0 + lane + 64 * q;
                 }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-                const float tv = __shfl_xor(bv, o, 64);
-                const int ti = __shfl_xor(bi, o, 64);
-                if (ranks_above(tv, ti, bv, bi)) {
-                    bv = tv;
-                    bi = ti;
-                }
-            }
+            md_wave::wave_argmax(bv, bi);
             if (lane == r) {
                 ov = bv;
                 oi = bi;
@@ -935,15 +920,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* 
                         bv = x[q];
                         bi = v0 + lane + 64 * q;
                     }
-#pragma unroll
-                for (int o = 32; o > 0; o >>= 1) {
-                    const float tv = __shfl_xor(bv, o, 64);
-                    const int ti = __shfl_xor(bi, o, 64);
-                    if (ranks_above(tv, ti, bv, bi)) {
-                        bv = tv;
-                        bi = ti;
-                    }
-                }
+                md_wave::wave_argmax(bv, bi);
                 if (lane == r) {
                     ov = bv;
                     oi = bi;
@@ -1086,15 +1063,7 @@ __global__ __launch_bounds__(BLOCK) void k_rescore(const uint16_t* __restrict__ 
     auto block_pick1 = [&](float v, int i, float& ov, int& oi) {
         float bv = v;
         int bi = i;
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) {
-            const float tv = __shfl_xor(bv, o, 64);
-            const int ti = __shfl_xor(bi, o, 64);
-            if (ranks_above(tv, ti, bv, bi)) {
-                bv = tv;
-                bi = ti;
-            }
-        }
+        md_wave::wave_argmax(bv, bi);
         if (lane == 0) {
             wv_s[w] = bv;
             wi_s[w] = bi;
@@ -1375,8 +1344,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
             const float dv = di == 0 ? gram[j][0] : di == 1 ? gram[j][1] : di == 2 ? gram[j][2] : di == 3 ? gram[j][3] : 0.f;
             mx = fmaxf(mx, dv);
         }
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        mx = md_wave::wave_max(mx);
         if (lane == 0) s_nrm[w] = mx;
     }
     __syncthreads();
@@ -1433,8 +1401,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
                 cnt += __popcll(__ballot(x0[e] != -INFINITY));
             }
             float best = fmaxf(x0[0], x0[1]);
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) best = fmaxf(best, __shfl_xor(best, o, 64));
+            best = md_wave::wave_max(best);
             if (lane == i) {
                 my_best = best;
                 my_cnt = cnt;
@@ -1484,15 +1451,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
                 for (int r = 0; k <= 2 && r < k; ++r) {
                     float bv = sv;
                     int bl = lane;
-#pragma unroll
-                    for (int o = 32; o > 0; o >>= 1) {
-                        const float tv = __shfl_xor(bv, o, 64);
-                        const int tl = __shfl_xor(bl, o, 64);
-                        if (tv > bv || (tv == bv && tl < bl)) {
-                            bv = tv;
-                            bl = tl;
-                        }
-                    }
+                    md_wave::wave_argmax(bv, bl);
                     kth = bv;
                     if (bl == lane) sv = -INFINITY;
                 }

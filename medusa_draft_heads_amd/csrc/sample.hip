@@ -38,6 +38,7 @@
 #include <math.h>
 
 #include "md_internal.h"
+#include "md_wave.h"
 
 namespace {
 
@@ -84,8 +85,7 @@ __device__ double block_sum(double x, double* sh) {
 template <int NW>
 __device__ double block_lse(float m, float s, float* shm, double* shs) {
     float bm = m;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o, MD_WAVE));
+    bm = md_wave::wave_max(bm);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) shm[w] = bm;
     __syncthreads();
@@ -100,15 +100,7 @@ __device__ double block_lse(float m, float s, float* shm, double* shs) {
 // Block argmax over (value desc, index asc); every thread gets the winner.
 template <int NW>
 __device__ void block_argmax(float& v, int& i, float* shv, int* shi) {
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(v, o, MD_WAVE);
-        const int oi = __shfl_xor(i, o, MD_WAVE);
-        if (above(ov, oi, v, i)) {
-            v = ov;
-            i = oi;
-        }
-    }
+    md_wave::wave_argmax(v, i);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
         shv[w] = v;
@@ -213,8 +205,7 @@ __global__ __launch_bounds__(MD_WAVE) void k_lse_merge(const float* __restrict__
     const float* pl = part_lse + (int64_t)r * chunks;
     float m = -INFINITY;
     for (int c = lane; c < chunks; c += MD_WAVE) m = fmaxf(m, pl[c]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, MD_WAVE));
+    m = md_wave::wave_max(m);
     double S = 0.0;
     for (int c = lane; c < chunks; c += MD_WAVE)
         if (pl[c] > -INFINITY) S += exp((double)pl[c] - (double)m);
@@ -329,8 +320,7 @@ __global__ __launch_bounds__(BLOCK) void k_row_stats_part(Parents pl, int N, int
         }
     });
     float bm = m;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) bm = fmaxf(bm, __shfl_xor(bm, o, MD_WAVE));
+    bm = md_wave::wave_max(bm);
     if ((threadIdx.x & 63) == 0) shm[threadIdx.x >> 6] = bm;
     __syncthreads();
     float M = shm[0];
@@ -357,8 +347,7 @@ __global__ __launch_bounds__(MD_WAVE) void k_row_stats_merge(Parents pl, int N, 
     const float* pr = part + (int64_t)r * chunks * 3;
     float M = -INFINITY;
     for (int c = lane; c < chunks; c += MD_WAVE) M = fmaxf(M, pr[3 * c]);
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, MD_WAVE));
+    M = md_wave::wave_max(M);
     double S = 0.0, W = 0.0;
     for (int c = lane; c < chunks; c += MD_WAVE) {
         if (pr[3 * c + 1] > 0.0f) {
@@ -534,15 +523,7 @@ __global__ __launch_bounds__(MD_WAVE) void k_draw_merge(int N, int chunks, const
             bi = i;
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        const float ov = __shfl_xor(bv, o, MD_WAVE);
-        const int oi = __shfl_xor(bi, o, MD_WAVE);
-        if (above(ov, oi, bv, bi)) {
-            bv = ov;
-            bi = oi;
-        }
-    }
+    md_wave::wave_argmax(bv, bi);
     if (lane == 0) chosen[(int64_t)b * N + spec[b].node] = bi == INT_MAX ? -1 : bi;
 }
 
@@ -570,8 +551,7 @@ __global__ __launch_bounds__(MD_WAVE) void k_typical(DevTree t, int V, float inv
     const uint64_t anc = lane < N ? t.anc[lane] : 0ull;
     const bool accepted = lane < N && ((anc & ~1ull) & ~mset) == 0ull;
     int key = accepted ? t.depth[lane] * 64 + (63 - lane) : -1;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o, MD_WAVE));
+    key = md_wave::wave_max(key);
     const int a = 63 - (key & 63);
     const uint64_t pa = __shfl(anc, a, MD_WAVE);
     // a node on the path (not the root) names its parent's emitted token
