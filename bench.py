@@ -75,6 +75,9 @@ def main() -> int:
     ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps timed for the CPU baseline (0: skip)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (scale factor for HBM counters)")
+    ap.add_argument("--operand-order", default="auto", choices=["auto", "on", "off"],
+                    help="also keep operand-order copies of the vocabulary matrices for the few-row matrix-core "
+                         "kernels (auto: bf16 Hydra levels and LM-head verification, where 2 to 128 rows meet them)")
     ap.add_argument("--seed", type=int, default=70)
     ap.add_argument("--cpu-1thread", type=int, default=1, help="also time one oracle step on one thread (0: skip)")
     args = ap.parse_args()
@@ -204,6 +207,12 @@ def main() -> int:
                         target_head=wl.target_head, verify=wl.verify, temperature=wl.temperature, eps=wl.eps,
                         delta=wl.delta)
     step = md.MedusaStep(cfg)
+    use_op = args.operand_order == "on" or (args.operand_order == "auto" and wl.dtype == "bf16"
+                                             and (hydra or wl.target_head))
+    if use_op:  # made once with the weights, outside every timed region
+        wd.update(step.operand_order_weights(wd))
+        torch.cuda.synchronize()
+        log("operand-order copies: %s" % ", ".join(k for k in ("U_op", "Wt_op") if k in wd))
     stream = torch.cuda.current_stream()
     calls = depth if hydra else 1  # heads calls per step, each with its own event pair
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
@@ -228,12 +237,13 @@ def main() -> int:
             if pairs is not None:
                 md.md_set_vocab_timing_events(pairs[lvl][0].cuda_event, pairs[lvl][1].cuda_event)
             if hydra:
-                step.heads(xd["h"], wd["W"], wd["b"], wd["U"], E=wd["E"], root_tok=xd["root_tok"], level=lvl + 1)
+                step.heads(xd["h"], wd["W"], wd["b"], wd["U"], E=wd["E"], root_tok=xd["root_tok"], level=lvl + 1,
+                           U_op=wd.get("U_op"))
                 step.build(None, xd["root_tok"], xd["lens"], level=lvl + 1)
             elif wl.verify == "sampled":
                 step.heads_logits(xd["h"], wd["W"], wd["b"], wd["U"])
             else:
-                step.heads(xd["h"], wd["W"], wd["b"], wd["U"])
+                step.heads(xd["h"], wd["W"], wd["b"], wd["U"], U_op=wd.get("U_op"))
             if pairs is not None:
                 md.md_set_vocab_timing_events(None, None)
         if wl.verify == "sampled":
@@ -244,7 +254,7 @@ def main() -> int:
         if lm is not None:
             lm[0].record(stream)
         if wl.target_head:
-            step.verify(xd["Ht"], wd["Wt"])
+            step.verify(xd["Ht"], wd["Wt"], wd.get("Wt_op"))
             if lm is not None:
                 lm[1].record(stream)
             step.accept_tokens(xd["Kc"], xd["Vc"], xd["lens"])
@@ -404,7 +414,8 @@ def main() -> int:
         "data": "synthetic (seeded Philox inputs, random-init heads of the workload's shape)",
         "config": {"workload": wl.name, "batch": wl.B, "d": wl.d, "V": wl.V, "heads": wl.K, "topk": list(wl.topk),
                    "tree_nodes": wl.N, "heads_rows_per_step": sum(head_rows), "Hq": wl.Hq, "Hkv": wl.Hkv,
-                   "head_dim": wl.hd, "L": wl.L_max, "input_sets": len(sets)},
+                   "head_dim": wl.hd, "L": wl.L_max, "input_sets": len(sets),
+                   "weights_layout": "row-major + operand-order copy" if use_op else "row-major"},
         "roofline": roofline,
         "step_hbm": {"bytes_per_step": step_bytes, "GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},

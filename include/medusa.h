@@ -94,8 +94,29 @@ int64_t md_heads_weight_bytes(int kind, int dt, int d, int V, int K);
 
 /* Workspace the heads need for M rows (Medusa, shared or not) or the largest
  * level's rows (Hydra: B requests times the most parents on one level, at
- * most 64 * B). */
+ * most 64 * B), with or without an operand-order copy of U. */
 size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, int kmax);
+
+/* Operand order: a copy of nmat row-major bf16 matrices [rows][cols] laid
+ * out for the matrix cores, written once when the weights load. Every MFMA
+ * operand fragment (16 rows x 32 contraction elements, 1 KB) is contiguous
+ * in lane order (lane l: row l % 16, elements 8 (l / 16) .. + 7), ordered
+ * [tile of 256 rows][step of 32 columns][16-row block][64 lanes][8]; rows
+ * past `rows` are zero. The heads and the LM head read such a copy, when
+ * given one, in their few-row matrix-core kernels: one step of a 256-row
+ * tile is then 16 KB of consecutive memory instead of 16 runs of 64 bytes
+ * per load (the row-major reads of those kernels stream at ~4.8 TB/s on
+ * MI355X, consecutive 1 KB loads at ~7). The row-major matrix stays the
+ * primary input (the GEMV path and the re-scoring of the certified pass read
+ * rows of it). */
+/* Bytes of the copy: nmat * ceil(rows / 256) * 256 * cols * 2; 0 when
+ * nmat < 1, rows < 1 or cols is not a positive multiple of 32. */
+size_t md_operand_order_bytes(int nmat, int rows, int cols);
+/* Writes the copy of src (device, bf16, [nmat][rows][cols]) to dst (device,
+ * md_operand_order_bytes(...) bytes; caller-owned, must not overlap src).
+ * Errors: MD_EINVAL (nmat or rows < 1, NULL pointers), MD_EUNSUPPORTED
+ * (cols not a positive multiple of 32), MD_EHIP. */
+int md_operand_order(int nmat, int rows, int cols, const void* src, void* dst, void* stream);
 
 /* The draft heads and their top-k lists.
  *
@@ -125,9 +146,15 @@ size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, in
  * b may be NULL (zero bias). h_res (device float32, optional) receives h'
  * as [K][M][d] (Medusa) or [rows][d] (Hydra). ws (device) must hold
  * md_heads_workspace_bytes(...). k_per_head (host) has K entries in [1, 16],
- * kmax = their maximum. Requires d % 8 == 0, K <= 8. */
+ * kmax = their maximum. Requires d % 8 == 0, K <= 8.
+ *
+ * U_op (optional, NULL for none): the operand-order copy of U (bf16 only;
+ * md_operand_order over the K matrices [V][d], or the one shared matrix).
+ * With it the matrix-core path runs from 2 bf16 rows (else from 8) and its
+ * few-row kernels (up to 128 rows) read U_op instead of U; the results are
+ * the same bit for bit. MD_EINVAL if given with dt = MD_F32. */
 int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t* k_per_head, int level,
-                    const md_tree* tree, const void* h, const void* W, const void* b, const void* U,
+                    const md_tree* tree, const void* h, const void* W, const void* b, const void* U, const void* U_op,
                     const void* E, const int32_t* root_tok, const int32_t* tree_tok, int32_t* topk_idx,
                     float* topk_val, float* h_res, void* ws, size_t ws_bytes, void* stream);
 
@@ -198,11 +225,14 @@ size_t md_target_argmax_workspace_bytes(int dt, int R, int d, int V);
  * H [R][d] (device, dt; for a step R = B * N rows in (request, node) order),
  * Wt [V][d] (device, dt), tok [R] (device int32), val [R] (device float32,
  * or NULL). Products of the stored values are exact and summed in float32.
- * ws (device) must hold md_target_argmax_workspace_bytes(...). Requires
- * d % 8 == 0 and d * 4 bytes <= 160 KB. Errors: MD_EINVAL (negative sizes,
- * NULL pointers, unknown dt), MD_EUNSUPPORTED (d), MD_EWORKSPACE. */
-int md_target_argmax(int dt, int R, int d, int V, const void* H, const void* Wt, int32_t* tok, float* val, void* ws,
-                     size_t ws_bytes, void* stream);
+ * ws (device) must hold md_target_argmax_workspace_bytes(...). Wt_op
+ * (optional, NULL for none): the operand-order copy of Wt (bf16 only, see
+ * md_operand_order); with it 2 to 128 rows run on the matrix cores reading
+ * Wt_op, with the same results. Requires d % 8 == 0 and d * 4 bytes <=
+ * 160 KB. Errors: MD_EINVAL (negative sizes, NULL pointers, unknown dt,
+ * Wt_op with MD_F32), MD_EUNSUPPORTED (d), MD_EWORKSPACE. */
+int md_target_argmax(int dt, int R, int d, int V, const void* H, const void* Wt, const void* Wt_op, int32_t* tok,
+                     float* val, void* ws, size_t ws_bytes, void* stream);
 
 /* md_tree_accept with the target's choices given instead of its logits:
  * target_tok [B][N] (device int32; t*(b, n), e.g. from md_target_argmax).

@@ -11,7 +11,8 @@ from ._lib import (MD_BF16, MD_F32, MD_HEADS_HYDRA, MD_HEADS_MEDUSA, MD_HEADS_ME
                    md_tree, md_tree_accept, md_tree_accept_tokens, md_tree_attention, md_tree_build, md_tree_validate,
                    md_heads_logits_workspace_bytes, md_medusa_heads_logits, md_draft_sample_workspace_bytes,
                    md_draft_sample, md_verify_sampled_workspace_bytes, md_tree_verify_sampled,
-                   md_accept_typical_workspace_bytes, md_tree_accept_typical)
+                   md_accept_typical_workspace_bytes, md_tree_accept_typical, md_operand_order_bytes,
+                   md_operand_order, operand_order)
 from .step import MedusaStep, StepConfig
 
 __all__ = [
@@ -22,6 +23,6 @@ __all__ = [
     "md_target_argmax", "md_target_argmax_workspace_bytes", "md_tree_accept_tokens",
     "md_heads_logits_workspace_bytes", "md_medusa_heads_logits", "md_draft_sample_workspace_bytes", "md_draft_sample",
     "md_verify_sampled_workspace_bytes", "md_tree_verify_sampled", "md_accept_typical_workspace_bytes",
-    "md_tree_accept_typical",
+    "md_tree_accept_typical", "md_operand_order_bytes", "md_operand_order", "operand_order",
     "MedusaStep", "StepConfig",
 ]

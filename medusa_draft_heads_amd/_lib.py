@@ -26,7 +26,7 @@ EXPORTS = (
     "md_target_argmax_workspace_bytes", "md_target_argmax", "md_tree_accept_tokens",
     "md_heads_logits_workspace_bytes", "md_medusa_heads_logits", "md_draft_sample_workspace_bytes", "md_draft_sample",
     "md_verify_sampled_workspace_bytes", "md_tree_verify_sampled", "md_accept_typical_workspace_bytes",
-    "md_tree_accept_typical",
+    "md_tree_accept_typical", "md_operand_order_bytes", "md_operand_order",
 )
 
 
@@ -64,7 +64,7 @@ def lib() -> ctypes.CDLL:
             "md_tree_validate": ([tp, i, vp], i),
             "md_heads_weight_bytes": ([i, i, i, i, i], i64),
             "md_heads_workspace_bytes": ([i, i, i, i, i, i, i], sz),
-            "md_medusa_heads": ([i, i, i, i, i, i, vp, i, tp] + [vp] * 11 + [sz, vp], i),
+            "md_medusa_heads": ([i, i, i, i, i, i, vp, i, tp] + [vp] * 12 + [sz, vp], i),
             "md_tree_build": ([tp, i, i, i, i, i, i] + [vp] * 6 + [vp], i),
             "md_attention_workspace_bytes": ([i, i, i, i, i, i, i], sz),
             "md_tree_attention": ([tp, i, i, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, sz, vp], i),
@@ -75,7 +75,7 @@ def lib() -> ctypes.CDLL:
             "md_hbm_read_probe": ([vp, sz, vp, vp], i),
             "md_hbm_read_probe_blocks": ([], i),
             "md_target_argmax_workspace_bytes": ([i, i, i, i], sz),
-            "md_target_argmax": ([i, i, i, i] + [vp] * 5 + [sz, vp], i),
+            "md_target_argmax": ([i, i, i, i] + [vp] * 6 + [sz, vp], i),
             "md_tree_accept_tokens": ([tp, i, i, i, i, i, i] + [vp] * 10, i),
             "md_heads_logits_workspace_bytes": ([i, i, i, i], sz),
             "md_medusa_heads_logits": ([i, i, i, i, i, i] + [vp] * 7 + [sz, vp], i),
@@ -85,6 +85,8 @@ def lib() -> ctypes.CDLL:
             "md_tree_verify_sampled": ([tp, i, i, i, i, i, i, i, f] + [vp] * 14 + [sz, vp], i),
             "md_accept_typical_workspace_bytes": ([i, i], sz),
             "md_tree_accept_typical": ([tp, i, i, i, i, i, i, i, f, f, f] + [vp] * 11 + [sz, vp], i),
+            "md_operand_order_bytes": ([i, i, i], sz),
+            "md_operand_order": ([i, i, i, vp, vp, vp], i),
         }
         for name, (args, res) in sig.items():
             fn = getattr(L, name)
@@ -151,14 +153,15 @@ def md_accept_workspace_bytes(B: int, N: int, V: int) -> int:
 
 
 def md_medusa_heads(kind, dt, M, d, V, K, k_per_head, level, tree, h, W, b, U, E, root_tok, tree_tok, topk_idx,
-                    topk_val, h_res, ws, ws_bytes=None, stream=None) -> None:
+                    topk_val, h_res, ws, ws_bytes=None, stream=None, U_op=None) -> None:
+    """U_op: optional operand-order copy of U (see md_operand_order)."""
     kp = (ctypes.c_int32 * K)(*k_per_head)
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
     rc = lib().md_medusa_heads(kind, dt, M, d, V, K, ctypes.cast(kp, ctypes.c_void_p), level,
-                               ctypes.byref(tree) if tree is not None else None, _p(h), _p(W), _p(b), _p(U), _p(E),
-                               _p(root_tok), _p(tree_tok), _p(topk_idx), _p(topk_val), _p(h_res), _p(ws), ws_bytes,
-                               _stream(stream))
+                               ctypes.byref(tree) if tree is not None else None, _p(h), _p(W), _p(b), _p(U), _p(U_op),
+                               _p(E), _p(root_tok), _p(tree_tok), _p(topk_idx), _p(topk_val), _p(h_res), _p(ws),
+                               ws_bytes, _stream(stream))
     _check(rc)
 
 
@@ -192,10 +195,37 @@ def md_target_argmax_workspace_bytes(dt, R, d, V) -> int:
     return int(lib().md_target_argmax_workspace_bytes(dt, R, d, V))
 
 
-def md_target_argmax(dt, R, d, V, H, Wt, tok, val, ws, ws_bytes=None, stream=None) -> None:
+def md_target_argmax(dt, R, d, V, H, Wt, tok, val, ws, ws_bytes=None, stream=None, Wt_op=None) -> None:
+    """Wt_op: optional operand-order copy of Wt (see md_operand_order)."""
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
-    _check(lib().md_target_argmax(dt, R, d, V, _p(H), _p(Wt), _p(tok), _p(val), _p(ws), ws_bytes, _stream(stream)))
+    _check(lib().md_target_argmax(dt, R, d, V, _p(H), _p(Wt), _p(Wt_op), _p(tok), _p(val), _p(ws), ws_bytes,
+                                  _stream(stream)))
+
+
+def md_operand_order_bytes(nmat, rows, cols) -> int:
+    return int(lib().md_operand_order_bytes(nmat, rows, cols))
+
+
+def md_operand_order(nmat, rows, cols, src, dst, stream=None) -> None:
+    _check(lib().md_operand_order(nmat, rows, cols, _p(src), _p(dst), _stream(stream)))
+
+
+def operand_order(mat):
+    """A new device tensor holding the operand-order copy of a bf16 tensor
+    [rows, cols] or [nmat, rows, cols] (allocated once, when weights load)."""
+    import torch
+
+    if mat.dtype != torch.bfloat16:
+        raise MedusaError(-1, "operand order exists for bf16 matrices only")
+    m3 = mat if mat.dim() == 3 else mat.unsqueeze(0)
+    nmat, rows, cols = m3.shape
+    n = md_operand_order_bytes(nmat, rows, cols)
+    if n == 0:
+        raise MedusaError(-2, "operand order needs cols a positive multiple of 32 (got %d)" % cols)
+    dst = torch.empty(n // 2, dtype=torch.bfloat16, device=mat.device)
+    md_operand_order(nmat, rows, cols, m3.contiguous(), dst)
+    return dst
 
 
 def md_tree_accept_tokens(tree, dt, B, K, Hkv, hd, Lcap, target_tok, tree_tok, Kc, Vc, lens, accept_len, path,

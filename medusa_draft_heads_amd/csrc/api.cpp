@@ -129,11 +129,12 @@ size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, in
 }
 
 int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t* k_per_head, int level,
-                    const md_tree* tree, const void* h, const void* W, const void* b, const void* U, const void* E,
-                    const int32_t* root_tok, const int32_t* tree_tok, int32_t* topk_idx, float* topk_val,
-                    float* h_res, void* ws, size_t ws_bytes, void* stream) {
+                    const md_tree* tree, const void* h, const void* W, const void* b, const void* U, const void* U_op,
+                    const void* E, const int32_t* root_tok, const int32_t* tree_tok, int32_t* topk_idx,
+                    float* topk_val, float* h_res, void* ws, size_t ws_bytes, void* stream) {
     if (!known_kind(kind)) return fail(MD_EINVAL, "kind = %d", kind);
     if (check_dt(dt)) return MD_EINVAL;
+    if (U_op && dt != MD_BF16) return fail(MD_EINVAL, "an operand-order copy of U exists for bf16 only");
     if (M < 0) return fail(MD_EINVAL, "M = %d", M);
     if (K < 1 || K > MD_MAX_HEADS) return fail(MD_EINVAL, "K = %d heads (1..8 supported)", K);
     if (!k_per_head) return fail(MD_EINVAL, "k_per_head is NULL");
@@ -166,6 +167,7 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
     a.W = W;
     a.b = b;
     a.U = U;
+    a.U_op = U_op;
     a.E = E;
     a.root_tok = root_tok;
     a.tree_tok = tree_tok;
@@ -181,7 +183,7 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
         a.nh = K;
         a.head0 = 0;
         for (int i = 0; i < K; ++i) a.kk[i] = k_per_head[i];
-        need = heads_ws_bytes(dt, M, d, d, V, K, kmax, a.shared_u);
+        need = heads_ws_bytes(dt, M, d, d, V, K, kmax, a.shared_u, U_op != nullptr);
     } else {
         if (level < 1 || level > K) return fail(MD_EINVAL, "Hydra level %d outside 1..%d", level, K);
         int rc = expand_tree(tree, K, k_per_head, &dt_tree);
@@ -196,7 +198,7 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
         a.kk[0] = k_per_head[level - 1];
         tp = &dt_tree;
         if (P == 0) return MD_OK;  // nothing at this depth
-        need = heads_ws_bytes(dt, a.M, d, din, V, 1, kmax, 0);
+        need = heads_ws_bytes(dt, a.M, d, din, V, 1, kmax, 0, U_op != nullptr);
     }
     if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     return hip_status(heads_launch(a, tp, (hipStream_t)stream, g_ev0, g_ev1), "md_medusa_heads");
@@ -283,9 +285,10 @@ size_t md_target_argmax_workspace_bytes(int dt, int R, int d, int V) {
     return target_argmax_ws_bound(dt, R, d, V);
 }
 
-int md_target_argmax(int dt, int R, int d, int V, const void* H, const void* Wt, int32_t* tok, float* val, void* ws,
-                     size_t ws_bytes, void* stream) {
+int md_target_argmax(int dt, int R, int d, int V, const void* H, const void* Wt, const void* Wt_op, int32_t* tok,
+                     float* val, void* ws, size_t ws_bytes, void* stream) {
     if (check_dt(dt)) return MD_EINVAL;
+    if (Wt_op && dt != MD_BF16) return fail(MD_EINVAL, "an operand-order copy of Wt exists for bf16 only");
     if (R < 0 || V < 1) return fail(MD_EINVAL, "R = %d, V = %d", R, V);
     if (d < 8 || d % 8) return fail(MD_EUNSUPPORTED, "d = %d (a positive multiple of 8 is required)", d);
     if ((size_t)d * 4 > 160 * 1024) return fail(MD_EUNSUPPORTED, "width %d exceeds one LDS row buffer", d);
@@ -293,7 +296,20 @@ int md_target_argmax(int dt, int R, int d, int V, const void* H, const void* Wt,
     if (!H || !Wt || !tok || !ws) return fail(MD_EINVAL, "a required pointer is NULL");
     const size_t need = target_argmax_ws_bound(dt, R, d, V);
     if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
-    return hip_status(target_argmax_launch(dt, R, d, V, H, Wt, tok, val, ws, (hipStream_t)stream), "md_target_argmax");
+    return hip_status(target_argmax_launch(dt, R, d, V, H, Wt, Wt_op, tok, val, ws, (hipStream_t)stream),
+                      "md_target_argmax");
+}
+
+size_t md_operand_order_bytes(int nmat, int rows, int cols) {
+    if (nmat < 1 || rows < 1 || cols < 32 || cols % 32) return 0;
+    return operand_order_bytes(nmat, rows, cols);
+}
+
+int md_operand_order(int nmat, int rows, int cols, const void* src, void* dst, void* stream) {
+    if (nmat < 1 || rows < 1) return fail(MD_EINVAL, "nmat = %d, rows = %d", nmat, rows);
+    if (cols < 32 || cols % 32) return fail(MD_EUNSUPPORTED, "cols = %d (a positive multiple of 32 is required)", cols);
+    if (!src || !dst) return fail(MD_EINVAL, "a required pointer is NULL");
+    return hip_status(operand_order_launch(nmat, rows, cols, src, dst, (hipStream_t)stream), "md_operand_order");
 }
 
 int md_tree_accept_tokens(const md_tree* tree, int dt, int B, int K, int Hkv, int hd, int Lcap,

@@ -704,8 +704,8 @@ hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
 
 }  // namespace
 
-size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u) {
-    if (heads_mfma_applicable(dt, M, d, din)) return heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u);
+size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u, bool op) {
+    if (heads_mfma_applicable(dt, M, d, din, op)) return heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u);
     const Plan p = make_plan(dt, M, d, din, nh, shared_u);
     return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * p.wg_per_head * kmax * 4);
 }
@@ -720,7 +720,9 @@ hipError_t topk_merge_launch(const float* pv, const int* pi, int M, int nh, int 
 }
 
 size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u) {
-    const size_t mfma = heads_mfma_applicable(dt, M, d, din) ? heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u) : 0;
+    // with or without an operand-order copy of U
+    const size_t mfma =
+        heads_mfma_applicable(dt, M, d, din, true) ? heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u) : 0;
     const size_t lists_max = (size_t)device_cus() * 4;  // blocks per head at most
     const size_t gemv = align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * lists_max * kmax * 4);
     return gemv > mfma ? gemv : mfma;
@@ -783,21 +785,21 @@ hipError_t target_argmax_gemv(int dt, int R, int d, int V, const void* H, const 
 
 size_t target_argmax_ws_bound(int dt, int R, int d, int V) {
     const size_t vals = align256((size_t)R * 4);
-    const size_t mfma = argmax_mfma_applicable(dt, R, d) ? argmax_mfma_ws_bytes(R, V) + vals : 0;
+    const size_t mfma = argmax_mfma_applicable(dt, R, d, true) ? argmax_mfma_ws_bytes(R, V) + vals : 0;
     const size_t lists_max = (size_t)device_cus() * 4;
     const size_t gemv = (dt == 1 ? align256((size_t)R * d * 4) : 0) + 2 * align256((size_t)R * lists_max * 4) + vals;
     return gemv > mfma ? gemv : mfma;
 }
 
-hipError_t target_argmax_launch(int dt, int R, int d, int V, const void* H, const void* Wt, int32_t* tok, float* val,
-                                void* ws, hipStream_t s) {
+hipError_t target_argmax_launch(int dt, int R, int d, int V, const void* H, const void* Wt, const void* Wt_op,
+                                int32_t* tok, float* val, void* ws, hipStream_t s) {
     KK kk;
     for (int i = 0; i < 8; ++i) kk.v[i] = 1;
-    if (argmax_mfma_applicable(dt, R, d)) {
+    if (argmax_mfma_applicable(dt, R, d, Wt_op != nullptr)) {
         float* pv;
         int* pi;
         int nlists;
-        hipError_t e = argmax_mfma_launch(R, d, V, H, Wt, ws, s, &pv, &pi, &nlists);
+        hipError_t e = argmax_mfma_launch(R, d, V, H, Wt, Wt_op, ws, s, &pv, &pi, &nlists);
         if (e != hipSuccess) return e;
         float* vs = reinterpret_cast<float*>(reinterpret_cast<char*>(ws) + argmax_mfma_ws_bytes(R, V));
         return launch_merge(pv, pi, R, 1, nlists, kk, 1, tok, val ? val : vs, s);
@@ -807,7 +809,7 @@ hipError_t target_argmax_launch(int dt, int R, int d, int V, const void* H, cons
 }
 
 hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (!a.logits && heads_mfma_applicable(a.dt, a.M, a.d, a.din)) {
+    if (!a.logits && heads_mfma_applicable(a.dt, a.M, a.d, a.din, a.U_op != nullptr)) {
         // many rows: the two contractions on the matrix cores, then the same k-way merge
         float* pv;
         int* pi;

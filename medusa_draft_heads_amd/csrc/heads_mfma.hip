@@ -338,6 +338,24 @@ typedef __attribute__((address_space(3))) void* lds_ptr;
 __device__ __forceinline__ void dmab(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t off) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, off, 0, 0, 0);
 }
+// Non-temporal: for loads that consume whole 128-byte lines (operand-order
+// fragments). With half lines (the row-major operand shape) the other half
+// would be fetched again.
+__device__ __forceinline__ void dmab_nt(__amdgpu_buffer_rsrc_t r, unsigned char* dst, uint32_t off) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, off, 0, 0, 2);
+}
+
+// Operand order: a copy of a row-major [rows][d] bf16 matrix in which every
+// MFMA A fragment (16 rows x 32 contraction elements, 1 KB) is contiguous in
+// lane order (lane l: row l % 16, elements 8 (l / 16) .. + 7), laid out
+// [tile of 256 rows][K step of 32][16-row block][64 lanes][8]; rows past the
+// end are zero. One K step of a 256-row tile is then 16 KB of consecutive
+// memory, where the row-major layout gives 16 runs of 64 bytes per load
+// instruction (the streaming rate of that shape is ~4.8 TB/s on this part,
+// of consecutive 1 KB loads ~7 TB/s). Written once, when the weights load.
+constexpr int OP_TILE = 256;  // rows per tile of the operand order (the vocabulary tile)
+static_assert(OP_TILE == VR, "an operand-order tile is a vocabulary tile");
+__device__ __forceinline__ uint32_t op_frag(int step, int rb) { return (uint32_t)(step * (OP_TILE / 16) + rb) * 1024; }
 
 // With one projection shared by the heads (Mh > 0) there is a single U and
 // activation row m ([heads][Mh][d] read as [M][d]) belongs to head m / Mh.
@@ -517,7 +535,7 @@ static_assert(NM * VR * 4 <= 3 * NSTAGE, "the logit tile fits the three stage bu
 constexpr int NCOLS_PER_BUF = NSTAGE / (VR * 4);  // 24 columns of 256 logits per stage buffer
 constexpr int kNarrowRows = 128;  // up to this many activation rows the two-product kernels run (narrow to 64, then direct)
 
-template <int NS>
+template <int NS, bool OP>
 __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* __restrict__ U,
                                                                 const uint16_t* __restrict__ hhi,
                                                                 const uint16_t* __restrict__ hlo, int M, int d, int V,
@@ -541,15 +559,26 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* 
     // r0 + 64 j of A; hi and lo are one piece each (rows r0 < 64)
     const int r0 = 16 * w + (lane >> 2);
     const uint32_t voff0 = (uint32_t)r0 * d * 2 + 16 * ((lane & 3) ^ ((r0 >> 1) & 3));
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(U + ((int64_t)(head0 + hh) * V + v0) * d), 0, min(V - v0, VR) * d * 2, RSRC3);
+    // OP: U in operand order ([head][vtiles * VR][d], tile vt contiguous):
+    // piece p of a stage is the fragment of row block p, 1 KB in place
+    const __amdgpu_buffer_rsrc_t rA =
+        OP ? __builtin_amdgcn_make_buffer_rsrc((void*)(U + ((int64_t)(head0 + hh) * vtiles * VR + v0) * d), 0, VR * d * 2,
+                                               RSRC3)
+           : __builtin_amdgcn_make_buffer_rsrc((void*)(U + ((int64_t)(head0 + hh) * V + v0) * d), 0,
+                                               min(V - v0, VR) * d * 2, RSRC3);
     const __amdgpu_buffer_rsrc_t rH =
         __builtin_amdgcn_make_buffer_rsrc((void*)(hhi + hbase + (int64_t)m0 * d), 0, min(M - m0, NM) * d * 2, RSRC3);
     const __amdgpu_buffer_rsrc_t rL =
         __builtin_amdgcn_make_buffer_rsrc((void*)(hlo + hbase + (int64_t)m0 * d), 0, min(M - m0, NM) * d * 2, RSRC3);
     auto issue = [&](int k0, unsigned char* base) {
+        if constexpr (OP) {
 #pragma unroll
-        for (int j = 0; j < NPA; ++j) dmab(rA, base + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
+            for (int j = 0; j < NPA; ++j)
+                dmab_nt(rA, base + (w + 4 * j) * 1024, op_frag(k0 / VK, w + 4 * j) + lane * 16);
+        } else {
+#pragma unroll
+            for (int j = 0; j < NPA; ++j) dmab(rA, base + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
+        }
         dmab(rH, base + A_BYTES + w * 1024, voff0 + (uint32_t)k0 * 2);
         if constexpr (NS == 2) dmab(rL, base + A_BYTES + NB_BYTES + w * 1024, voff0 + (uint32_t)k0 * 2);
     };
@@ -566,7 +595,9 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* 
         bf16x8 a[4];
 #pragma unroll
         for (int rb = 0; rb < 4; ++rb)
-            a[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sA + (64 * w + 16 * rb + c16) * ROWB + slot));
+            a[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(
+                                                   OP ? sA + (4 * w + rb) * 1024 + lane * 16
+                                                      : sA + (64 * w + 16 * rb + c16) * ROWB + slot));
 #pragma unroll
         for (int s = 0; s < NS; ++s) {
 #pragma unroll
@@ -740,7 +771,7 @@ struct DirectCfg {
     static_assert(2 * P * SB + 2 * 4 * 128 <= 160 * 1024, "two blocks fit the LDS of one CU");
 };
 
-template <int NS, int CB>
+template <int NS, int CB, bool OP>
 __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* __restrict__ U,
                                                                 const uint16_t* __restrict__ hhi,
                                                                 const uint16_t* __restrict__ hlo, int M, int d, int V,
@@ -780,8 +811,11 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* 
 
     // A: the lane's rows are 64 w + 16 rb + c16, its 16 bytes the chunk g4 of
     // the K step (the MFMA A layout); rows past V read as zero
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(U + ((int64_t)(head0 + hh) * V + v0) * d), 0, min(V - v0, VR) * d * 2, RSRC3);
+    const __amdgpu_buffer_rsrc_t rA =
+        OP ? __builtin_amdgcn_make_buffer_rsrc((void*)(U + ((int64_t)(head0 + hh) * vtiles * VR + v0) * d), 0, VR * d * 2,
+                                               RSRC3)
+           : __builtin_amdgcn_make_buffer_rsrc((void*)(U + ((int64_t)(head0 + hh) * V + v0) * d), 0,
+                                               min(V - v0, VR) * d * 2, RSRC3);
     const uint32_t aoff = (uint32_t)(64 * w + c16) * d * 2 + 16 * g4;
     // B: piece p of a stage is operand p / CB (hi, lo), column block p % CB;
     // the lane loads column 16 (p % CB) + lane / 4, chunk (lane % 4) ^
@@ -795,10 +829,16 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* 
 
     u32x4 ra[P][4];
     auto issue_a = [&](int s, u32x4 (&r)[4]) {
-        const uint32_t o = aoff + (uint32_t)min(s, nk - 1) * (VK * 2);
+        if constexpr (OP) {  // the wave's four fragments of a K step: 4 KB in place, non-temporal
+            const uint32_t o = op_frag(min(s, nk - 1), 4 * w) + lane * 16;
 #pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-            r[rb] = __builtin_amdgcn_raw_buffer_load_b128(rA, o + (uint32_t)(16 * rb) * d * 2, 0, 0);
+            for (int rb = 0; rb < 4; ++rb) r[rb] = __builtin_amdgcn_raw_buffer_load_b128(rA, o + rb * 1024, 0, 2);
+        } else {
+            const uint32_t o = aoff + (uint32_t)min(s, nk - 1) * (VK * 2);
+#pragma unroll
+            for (int rb = 0; rb < 4; ++rb)
+                r[rb] = __builtin_amdgcn_raw_buffer_load_b128(rA, o + (uint32_t)(16 * rb) * d * 2, 0, 0);
+        }
     };
     auto issue_b = [&](int s, unsigned char* dst) {
         const uint32_t ko = (uint32_t)min(s, nk - 1) * (VK * 2);
@@ -939,13 +979,13 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* 
     }
 }
 
-template <int NS>
+template <int NS, bool OP>
 hipError_t launch_direct(int cb, dim3 grid, hipStream_t s, const uint16_t* U, const uint16_t* hhi, const uint16_t* hlo,
                          int M, int d, int V, int nh, int head0, int vtiles, int kmax, KW kk, int Mh, float* pv,
                          int* pi, int* bound) {
 #define MD_DIRECT(CBV)                                                                                               \
     case CBV:                                                                                                        \
-        hipLaunchKernelGGL((k_vocab_mfma_direct<NS, CBV>), grid, dim3(BLOCK), 0, s, U, hhi, hlo, M, d, V, nh, head0, \
+        hipLaunchKernelGGL((k_vocab_mfma_direct<NS, CBV, OP>), grid, dim3(BLOCK), 0, s, U, hhi, hlo, M, d, V, nh, head0, \
                            vtiles, kmax, kk, Mh, pv, pi, bound);                                                     \
         break;
     switch (cb) {
@@ -1520,7 +1560,11 @@ __global__ void k_fill_bound(int* __restrict__ bound, int n) {
 
 }  // namespace
 
-bool argmax_mfma_applicable(int dt, int R, int d) { return dt == 1 && R >= 8 && d % (2 * VK) == 0; }
+// With an operand-order copy of the LM head, 2 to 7 rows run on the matrix
+// cores too (the few-row kernels then read at the streaming rate).
+bool argmax_mfma_applicable(int dt, int R, int d, bool op) {
+    return dt == 1 && (R >= 8 || (op && R >= 2 && R <= kNarrowRows)) && d % (2 * VK) == 0;
+}
 
 size_t argmax_mfma_ws_bytes(int R, int V) {
     const size_t vtiles = (size_t)(V + VR - 1) / VR;
@@ -1530,8 +1574,8 @@ size_t argmax_mfma_ws_bytes(int R, int V) {
 // The target's choice per row: one bf16 product per term (hidden states and
 // LM head are exact in bf16), the same epilogue with k = 1; the caller merges
 // the lists (two per vocabulary tile).
-hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt, void* ws, hipStream_t s,
-                              float** part_val, int** part_idx, int* nlists) {
+hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt, const void* Wt_op, void* ws,
+                              hipStream_t s, float** part_val, int** part_idx, int* nlists) {
     const int vtiles = (V + VR - 1) / VR, vmtiles = (R + VM - 1) / VM;
     char* w = reinterpret_cast<char*>(ws);
     float* pv = reinterpret_cast<float*>(w);
@@ -1545,18 +1589,27 @@ hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt
     KW kk;
     for (int i = 0; i < 8; ++i) kk.v[i] = 1;
     const uint16_t* h = reinterpret_cast<const uint16_t*>(H);
-    const uint16_t* wt = reinterpret_cast<const uint16_t*>(Wt);
+    const bool op = Wt_op != nullptr;
+    const uint16_t* wt = reinterpret_cast<const uint16_t*>(op ? Wt_op : Wt);
     if (R <= kNarrowRows) {
         if (R > NM) {
-            err = launch_direct<1>((R + 15) / 16, dim3(vtiles), s, wt, h, h, R, d, V, 1, 0, vtiles, 1, kk, 0, pv, pi, bound);
+            const int cb = (R + 15) / 16;
+            err = op ? launch_direct<1, true>(cb, dim3(vtiles), s, wt, h, h, R, d, V, 1, 0, vtiles, 1, kk, 0, pv, pi, bound)
+                     : launch_direct<1, false>(cb, dim3(vtiles), s, wt, h, h, R, d, V, 1, 0, vtiles, 1, kk, 0, pv, pi, bound);
             if (err != hipSuccess) return err;
         } else {
-            hipLaunchKernelGGL(k_vocab_mfma_narrow<1>, dim3(8 * ((vtiles + 7) / 8)), dim3(BLOCK), 0, s, wt, h, h, R, d, V,
-                               1, 0, vtiles, 1, 1, kk, 0, pv, pi, bound);
+            const dim3 grid(8 * ((vtiles + 7) / 8));
+            if (op)
+                hipLaunchKernelGGL((k_vocab_mfma_narrow<1, true>), grid, dim3(BLOCK), 0, s, wt, h, h, R, d, V, 1, 0, vtiles,
+                                   1, 1, kk, 0, pv, pi, bound);
+            else
+                hipLaunchKernelGGL((k_vocab_mfma_narrow<1, false>), grid, dim3(BLOCK), 0, s, wt, h, h, R, d, V, 1, 0,
+                                   vtiles, 1, 1, kk, 0, pv, pi, bound);
         }
         *nlists = vtiles;
-    } else {
-        hipLaunchKernelGGL(k_vocab_mfma<1>, dim3(8 * vmtiles * ((vtiles + 7) / 8)), dim3(BLOCK), 0, s, wt, h, h, R, d, V,
+    } else {  // row-major LM head: the many-row kernel stages its tiles through LDS
+        hipLaunchKernelGGL(k_vocab_mfma<1>, dim3(8 * vmtiles * ((vtiles + 7) / 8)), dim3(BLOCK), 0, s,
+                           reinterpret_cast<const uint16_t*>(Wt), h, h, R, d, V,
                            1, 0, vtiles, vmtiles, 1, kk, 0, pv, pi, bound);
         *nlists = 2 * vtiles;
     }
@@ -1566,9 +1619,47 @@ hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt
     return hipSuccess;
 }
 
-bool heads_mfma_applicable(int dt, int M, int d, int din) {
-    // d % 128: whole residual tiles, and an even number of vocabulary stages
-    return dt == 1 && M >= 8 && d % TR == 0 && din % KS == 0 && d % (2 * VK) == 0;
+namespace {
+// One thread per 16-byte chunk of the operand-order copy.
+__global__ __launch_bounds__(BLOCK) void k_operand_order(const uint16_t* __restrict__ src, uint16_t* __restrict__ dst,
+                                                         int rows, int cols, int tiles, int64_t chunks) {
+    const int ks = cols / VK;
+    for (int64_t i = (int64_t)blockIdx.x * BLOCK + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * BLOCK) {
+        int64_t q = i;
+        const int lane = (int)(q % 64);
+        q /= 64;
+        const int rb = (int)(q % (OP_TILE / 16));
+        q /= OP_TILE / 16;
+        const int step = (int)(q % ks);
+        q /= ks;
+        const int t = (int)(q % tiles);
+        const int64_t mat = q / tiles;
+        const int row = t * OP_TILE + rb * 16 + (lane & 15);
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (row < rows)
+            v = *reinterpret_cast<const u32x4*>(src + (mat * rows + row) * cols + step * VK + 8 * (lane >> 4));
+        *reinterpret_cast<u32x4*>(dst + i * 8) = v;
+    }
+}
+}  // namespace
+
+size_t operand_order_bytes(int nmat, int rows, int cols) {
+    return (size_t)nmat * ((rows + OP_TILE - 1) / OP_TILE) * OP_TILE * cols * 2;
+}
+
+hipError_t operand_order_launch(int nmat, int rows, int cols, const void* src, void* dst, hipStream_t s) {
+    const int tiles = (rows + OP_TILE - 1) / OP_TILE;
+    const int64_t chunks = (int64_t)nmat * tiles * OP_TILE * cols / 8;
+    const int64_t blocks = std::min<int64_t>((chunks + BLOCK - 1) / BLOCK, 8 * device_cus());
+    hipLaunchKernelGGL(k_operand_order, dim3((unsigned)blocks), dim3(BLOCK), 0, s, reinterpret_cast<const uint16_t*>(src),
+                       reinterpret_cast<uint16_t*>(dst), rows, cols, tiles, chunks);
+    return hipGetLastError();
+}
+
+bool heads_mfma_applicable(int dt, int M, int d, int din, bool op) {
+    // d % 128: whole residual tiles, and an even number of vocabulary stages;
+    // with an operand-order copy of U from 2 rows (the GEMV stays for 1)
+    return dt == 1 && (M >= 8 || (op && M >= 2)) && d % TR == 0 && din % KS == 0 && d % (2 * VK) == 0;
 }
 
 // Contraction chunks of the residual: enough (tile, chunk) blocks for two per
@@ -1709,15 +1800,26 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     const int head0 = a.shared_u ? 0 : a.head0, Mh = a.shared_u ? a.M : 0;
     if (!cert) {  // few rows: HBM-bound, two products and the deeper pipeline
         // 65 to 128 rows: one register-streamed tile; otherwise 64-row tiles
-        // (more than 128 rows only where the certified pass cannot work)
+        // (more than 128 rows only where the certified pass cannot work). With
+        // an operand-order copy of U both read that instead.
+        const bool op = a.U_op != nullptr;
+        const uint16_t* UA = op ? reinterpret_cast<const uint16_t*>(a.U_op) : U;
         if (rows_v > NM && rows_v <= kNarrowRows) {
-            err = launch_direct<2>((rows_v + 15) / 16, dim3(units2), s, U, L.hhi, L.hlo, rows_v, a.d, a.V, nh_u, head0,
-                                   vtiles, a.kmax, kk, Mh, L.pv, L.pi, L.bound);
+            const int cb = (rows_v + 15) / 16;
+            err = op ? launch_direct<2, true>(cb, dim3(units2), s, UA, L.hhi, L.hlo, rows_v, a.d, a.V, nh_u, head0, vtiles,
+                                              a.kmax, kk, Mh, L.pv, L.pi, L.bound)
+                     : launch_direct<2, false>(cb, dim3(units2), s, UA, L.hhi, L.hlo, rows_v, a.d, a.V, nh_u, head0,
+                                               vtiles, a.kmax, kk, Mh, L.pv, L.pi, L.bound);
             if (err != hipSuccess) return err;
         } else {
             const int nmt = (rows_v + NM - 1) / NM;
-            hipLaunchKernelGGL(k_vocab_mfma_narrow<2>, dim3(8 * nmt * ((units2 + 7) / 8)), dim3(BLOCK), 0, s, U, L.hhi,
-                               L.hlo, rows_v, a.d, a.V, nh_u, head0, vtiles, nmt, a.kmax, kk, Mh, L.pv, L.pi, L.bound);
+            const dim3 grid(8 * nmt * ((units2 + 7) / 8));
+            if (op)
+                hipLaunchKernelGGL((k_vocab_mfma_narrow<2, true>), grid, dim3(BLOCK), 0, s, UA, L.hhi, L.hlo, rows_v, a.d,
+                                   a.V, nh_u, head0, vtiles, nmt, a.kmax, kk, Mh, L.pv, L.pi, L.bound);
+            else
+                hipLaunchKernelGGL((k_vocab_mfma_narrow<2, false>), grid, dim3(BLOCK), 0, s, UA, L.hhi, L.hlo, rows_v,
+                                   a.d, a.V, nh_u, head0, vtiles, nmt, a.kmax, kk, Mh, L.pv, L.pi, L.bound);
         }
         *nlists = vtiles;
     } else {  // many rows: one product and the certificate

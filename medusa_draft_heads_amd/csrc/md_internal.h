@@ -49,6 +49,7 @@ struct HeadsArgs {
     const void* W;
     const void* b;
     const void* U;
+    const void* U_op;  // optional operand-order copy of U (bf16), read by the few-row matrix-core kernels
     const void* E;
     const int32_t* root_tok;
     const int32_t* tree_tok;
@@ -60,10 +61,10 @@ struct HeadsArgs {
     int logits_k;
 };
 
-size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u);  // this plan
+size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u, bool op);  // this plan
 size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u);  // any plan of these sizes
 // matrix-core path for many rows (heads_mfma.hip)
-bool heads_mfma_applicable(int dt, int M, int d, int din);
+bool heads_mfma_applicable(int dt, int M, int d, int din, bool op);
 size_t heads_mfma_ws_bytes(int M, int d, int din, int V, int nh, int kmax, int shared_u);
 hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                              float** part_val, int** part_idx, int* nlists);
@@ -72,15 +73,18 @@ size_t heads_logits_ws_bytes(int M, int d, int nh);
 // the k-way merge of nlists sorted lists per (row, head): lists [nh][M][nlists][kmax] -> [M][nh][kmax]
 hipError_t topk_merge_launch(const float* pv, const int* pi, int M, int nh, int nlists, const int* kk, int kmax,
                              int32_t* idx, float* val, hipStream_t s);
-bool argmax_mfma_applicable(int dt, int R, int d);
+bool argmax_mfma_applicable(int dt, int R, int d, bool op);
 size_t argmax_mfma_ws_bytes(int R, int V);
-hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt, void* ws, hipStream_t s,
-                              float** part_val, int** part_idx, int* nlists);
+hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt, const void* Wt_op, void* ws,
+                              hipStream_t s, float** part_val, int** part_idx, int* nlists);
+// the operand-order copy of nmat row-major [rows][cols] bf16 matrices (heads_mfma.hip)
+size_t operand_order_bytes(int nmat, int rows, int cols);
+hipError_t operand_order_launch(int nmat, int rows, int cols, const void* src, void* dst, hipStream_t s);
 
 // ---- the target's LM head with a fused argmax (heads.hip) ----
 size_t target_argmax_ws_bound(int dt, int R, int d, int V);
-hipError_t target_argmax_launch(int dt, int R, int d, int V, const void* H, const void* Wt, int32_t* tok, float* val,
-                                void* ws, hipStream_t s);
+hipError_t target_argmax_launch(int dt, int R, int d, int V, const void* H, const void* Wt, const void* Wt_op,
+                                int32_t* tok, float* val, void* ws, hipStream_t s);
 
 // ---- tree build (tree.hip) ----
 hipError_t tree_build_launch(const DevTree& t, int kind, int B, int M, int K, int kmax, int level,

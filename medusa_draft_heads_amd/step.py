@@ -100,10 +100,10 @@ class MedusaStep:
         self.h_res = None
 
     # -- the four calls -------------------------------------------------------
-    def heads(self, h, W, b, U, E=None, root_tok=None, level: int = 0, h_res=None) -> None:
+    def heads(self, h, W, b, U, E=None, root_tok=None, level: int = 0, h_res=None, U_op=None) -> None:
         c = self.cfg
         L.md_medusa_heads(c.kind, self.dt, c.M, c.d, c.V, c.K, c.k_per_head, level, self.tree, h, W, b, U, E,
-                          root_tok, self.tree_tok, self.topk_idx, self.topk_val, h_res, self.ws_heads)
+                          root_tok, self.tree_tok, self.topk_idx, self.topk_val, h_res, self.ws_heads, U_op=U_op)
 
     def build(self, src_row, root_tok, lens, level: int = 0) -> None:
         c = self.cfg
@@ -120,10 +120,21 @@ class MedusaStep:
         L.md_tree_accept(self.tree, self.dt, c.B, c.K, c.V, c.Hkv, c.hd, c.Lcap, logits, self.tree_tok, Kc, Vc, lens,
                          self.accept_len, self.path, self.next_tok, self.compact_src, self.ws_acc)
 
-    def verify(self, Ht, Wt) -> None:
+    def verify(self, Ht, Wt, Wt_op=None) -> None:
         """The target's choice at every node: LM head + fused argmax over Ht [B, N, d]."""
         c = self.cfg
-        L.md_target_argmax(self.dt, c.B * self.N, c.d, c.V, Ht, Wt, self.target_tok, self.target_val, self.ws_target)
+        L.md_target_argmax(self.dt, c.B * self.N, c.d, c.V, Ht, Wt, self.target_tok, self.target_val, self.ws_target,
+                           Wt_op=Wt_op)
+
+    def operand_order_weights(self, w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
+        """Operand-order copies of the vocabulary matrices (U_op, and Wt_op with target_head), made once
+        when the weights load; bf16 only. run() passes them on when w holds them."""
+        if self.dt != L.MD_BF16:
+            raise ValueError("operand-order copies exist for bf16 weights only")
+        out = {"U_op": L.operand_order(w["U"])}
+        if self.cfg.target_head:
+            out["Wt_op"] = L.operand_order(w["Wt"])
+        return out
 
     def accept_tokens(self, Kc, Vc, lens) -> None:
         c = self.cfg
@@ -155,9 +166,9 @@ class MedusaStep:
 
     # -- a whole step -----------------------------------------------------------
     def run(self, w: Dict[str, torch.Tensor], x: Dict[str, torch.Tensor]) -> None:
-        """w: W, b, U (E for Hydra, Wt with target_head); x: h, q, Kc, Vc, lens, root_tok, src_row, and
-        logits (or Ht with target_head); sampled decoding adds draft_words, u_words and g_words, typical
-        acceptance g_words."""
+        """w: W, b, U (E for Hydra, Wt with target_head; optionally U_op and Wt_op from
+        operand_order_weights); x: h, q, Kc, Vc, lens, root_tok, src_row, and logits (or Ht with
+        target_head); sampled decoding adds draft_words, u_words and g_words, typical acceptance g_words."""
         c = self.cfg
         if c.verify == "sampled":
             self.heads_logits(x["h"], w["W"], w["b"], w["U"])
@@ -167,16 +178,17 @@ class MedusaStep:
             self.verify_sampled(x["logits"], x["u_words"], x["g_words"], x["Kc"], x["Vc"], x["lens"])
             return
         if c.kind != L.MD_HEADS_HYDRA:
-            self.heads(x["h"], w["W"], w["b"], w["U"])
+            self.heads(x["h"], w["W"], w["b"], w["U"], U_op=w.get("U_op"))
             self.build(x["src_row"], x["root_tok"], x["lens"])
         else:
             depth = max(self._depths())
             for level in range(1, depth + 1):
-                self.heads(x["h"], w["W"], w["b"], w["U"], E=w["E"], root_tok=x["root_tok"], level=level)
+                self.heads(x["h"], w["W"], w["b"], w["U"], E=w["E"], root_tok=x["root_tok"], level=level,
+                           U_op=w.get("U_op"))
                 self.build(None, x["root_tok"], x["lens"], level=level)
         self.attention(x["q"], x["Kc"], x["Vc"], x["lens"])
         if c.target_head:
-            self.verify(x["Ht"], w["Wt"])
+            self.verify(x["Ht"], w["Wt"], w.get("Wt_op"))
             self.accept_tokens(x["Kc"], x["Vc"], x["lens"])
         elif c.verify == "typical":
             self.accept_typical(x["logits"], x["g_words"], x["Kc"], x["Vc"], x["lens"])

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 24
+    assert len(names) == 26
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -84,9 +84,9 @@ def test_heads_argument_errors():
                                                       product_order_tree((4, 2, 2, 1), 16).rank)]))
 
     def call(kind=0, dt=1, M=1, d=256, V=4096, K=4, kph=kpv, level=0, tree=None, h=P, W=P, U=P, ws=P, ws_bytes=1 << 30,
-             E=None, root=None, tok=None):
-        return lib.md_medusa_heads(kind, dt, M, d, V, K, kph, level, tree, h, W, None, U, E, root, tok, P, P, None, ws,
-                                   ws_bytes, None)
+             E=None, root=None, tok=None, U_op=None):
+        return lib.md_medusa_heads(kind, dt, M, d, V, K, kph, level, tree, h, W, None, U, U_op, E, root, tok, P, P, None,
+                                   ws, ws_bytes, None)
 
     assert call(kind=3) == L.MD_EINVAL
     assert call(kind=2, level=1) == L.MD_EINVAL  # a shared projection is Medusa: level 0
@@ -104,6 +104,7 @@ def test_heads_argument_errors():
     assert call(kind=1, level=2, tree=t, E=P, root=P, tok=None) == L.MD_EINVAL  # needs the parents' tokens
     assert call(kind=1, level=1, tree=None, E=P, root=P) == L.MD_EINVAL
     assert call(M=-1) == L.MD_EINVAL
+    assert call(dt=0, U_op=P) == L.MD_EINVAL  # the operand-order copy is bf16 only
     assert call(M=0) == L.MD_OK  # an empty batch enqueues nothing
 
 
@@ -155,8 +156,8 @@ def test_target_argmax_and_accept_tokens_argument_errors():
     need = md.md_target_argmax_workspace_bytes(1, 64, 512, 5000)
     assert need > 0
 
-    def am(dt=1, R=64, d=512, V=5000, H=P, ws_bytes=need):
-        return lib.md_target_argmax(dt, R, d, V, H, P, P, None, P, ws_bytes, None)
+    def am(dt=1, R=64, d=512, V=5000, H=P, ws_bytes=need, Wt_op=None):
+        return lib.md_target_argmax(dt, R, d, V, H, P, Wt_op, P, None, P, ws_bytes, None)
 
     assert am(dt=5) == L.MD_EINVAL
     assert am(R=-1) == L.MD_EINVAL
@@ -165,6 +166,7 @@ def test_target_argmax_and_accept_tokens_argument_errors():
     assert am(d=65536) == L.MD_EUNSUPPORTED
     assert am(H=None) == L.MD_EINVAL
     assert am(ws_bytes=need - 1) == L.MD_EWORKSPACE
+    assert am(dt=0, Wt_op=P) == L.MD_EINVAL  # the operand-order copy is bf16 only
     assert am(R=0) == L.MD_OK
     topo = product_order_tree((4, 2, 2, 1), 16)
     t = ctypes.byref(L.make_tree(topo.parent, topo.rank))
@@ -177,6 +179,24 @@ def test_target_argmax_and_accept_tokens_argument_errors():
     assert acc(K=3) == L.MD_EINVAL  # the tree is 4 deep
     assert acc(tt=None) == L.MD_EINVAL
     assert acc(B=0) == L.MD_OK
+
+
+def test_operand_order_sizes_and_argument_errors():
+    lib = L.lib()
+    P = 0x1000
+    # whole 256-row tiles per matrix, zero-padded
+    assert md.md_operand_order_bytes(1, 256, 32) == 256 * 32 * 2
+    assert md.md_operand_order_bytes(4, 1000, 4096) == 4 * 1024 * 4096 * 2
+    assert md.md_operand_order_bytes(2, 1, 64) == 2 * 256 * 64 * 2
+    assert md.md_operand_order_bytes(0, 256, 32) == 0
+    assert md.md_operand_order_bytes(1, 0, 32) == 0
+    assert md.md_operand_order_bytes(1, 256, 48) == 0
+    assert md.md_operand_order_bytes(1, 256, 0) == 0
+    assert lib.md_operand_order(0, 256, 64, P, P, None) == L.MD_EINVAL
+    assert lib.md_operand_order(1, -3, 64, P, P, None) == L.MD_EINVAL
+    assert lib.md_operand_order(1, 256, 40, P, P, None) == L.MD_EUNSUPPORTED
+    assert lib.md_operand_order(1, 256, 64, None, P, None) == L.MD_EINVAL
+    assert lib.md_operand_order(1, 256, 64, P, None, None) == L.MD_EINVAL
 
 
 def test_sampled_decoding_argument_errors():

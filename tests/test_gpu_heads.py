@@ -27,7 +27,7 @@ def _md():
     return md
 
 
-def gpu_heads_medusa(wl: Workload, wd, h_dev, M):
+def gpu_heads_medusa(wl: Workload, wd, h_dev, M, U_op=None):
     import torch
 
     md = _md()
@@ -39,7 +39,7 @@ def gpu_heads_medusa(wl: Workload, wd, h_dev, M):
     hres = torch.empty(K, M, wl.d, dtype=torch.float32, device="cuda")
     ws = torch.empty(md.md_heads_workspace_bytes(kind, dt, M, wl.d, wl.V, K, kmax), dtype=torch.uint8, device="cuda")
     md.md_medusa_heads(kind, dt, M, wl.d, wl.V, K, wl.topk, 0, None, h_dev, wd["W"], wd["b"], wd["U"], None, None,
-                       None, idx, val, hres, ws)
+                       None, idx, val, hres, ws, U_op=U_op)
     torch.cuda.synchronize()
     return from_dev(idx), from_dev(val), from_dev(hres)
 
@@ -109,7 +109,7 @@ def test_heads_medusa_full_size(wl_name):
 
 # ---------------------------------------------------------------- Hydra
 
-def gpu_hydra_level(wl, wd, h_dev, root_dev, tok_dev, tree, level, rows):
+def gpu_hydra_level(wl, wd, h_dev, root_dev, tok_dev, tree, level, rows, U_op=None):
     import torch
 
     md = _md()
@@ -120,12 +120,12 @@ def gpu_hydra_level(wl, wd, h_dev, root_dev, tok_dev, tree, level, rows):
     ws = torch.empty(md.md_heads_workspace_bytes(1, dt, wl.B, wl.d, wl.V, wl.K, wl.kmax), dtype=torch.uint8,
                      device="cuda")
     md.md_medusa_heads(1, dt, wl.B, wl.d, wl.V, wl.K, wl.topk, level, tree, h_dev, wd["W"], wd["b"], wd["U"], wd["E"],
-                       root_dev, tok_dev, idx, val, hres, ws)
+                       root_dev, tok_dev, idx, val, hres, ws, U_op=U_op)
     torch.cuda.synchronize()
     return from_dev(idx), from_dev(val), from_dev(hres)
 
 
-def check_hydra(wl, seed, requests=None):
+def check_hydra(wl, seed, requests=None, op=False):
     md = _md()
     topo = wl.topology()
     w = weights(wl, seed)
@@ -133,6 +133,7 @@ def check_hydra(wl, seed, requests=None):
     ref = oracle.hydra_expand(w["W"], w["b"], w["U"], w["E"], x["h"], topo.parent, topo.rank, wl.topk,
                               x["root_tok"], x["lens"], requests=requests, want_logits=True)
     wd = {k: to_dev(v) for k, v in w.items()}
+    U_op = md.operand_order(wd["U"]) if op else None
     tree = md.make_tree(topo.parent, topo.rank)
     tok_dev = to_dev(np.where(ref["tree_tok"] < 0, 0, ref["tree_tok"]).astype(np.int32))  # oracle's upstream tokens
     h_dev, root_dev = to_dev(x["h"]), to_dev(x["root_tok"])
@@ -141,7 +142,7 @@ def check_hydra(wl, seed, requests=None):
     for li, lvl in enumerate(ref["levels"]):
         level = li + 1
         P = len(oracle.hydra_rows(topo.parent, level))
-        gi, gv, gh = gpu_hydra_level(wl, wd, h_dev, root_dev, tok_dev, tree, level, wl.B * P)
+        gi, gv, gh = gpu_hydra_level(wl, wd, h_dev, root_dev, tok_dev, tree, level, wl.B * P, U_op=U_op)
         # GPU rows are (b, parent) over all requests; pick the oracle's rows
         sel = [b * P + j for b in reqs for j in range(P)]
         assert len(sel) == len(lvl["rows"])
@@ -161,6 +162,17 @@ def test_hydra_small():
 def test_hydra_full_size_sampled():
     # full Hydra shape (B = 4, d = 4096, V = 128,256); the oracle checks request 0's 41 rows
     check_hydra(HYDRA_B4, 41, requests=[0])
+
+
+def test_hydra_small_operand_order():
+    # batch 3: levels of 3, 15, 24 and 30 rows, all on the matrix cores with the operand-order copy
+    wl = replace(HYDRA_B4, name="hydra small", B=3, d=256, V=3001, topk=(5, 3, 2, 1), N=20)
+    check_hydra(wl, 32, op=True)
+
+
+def test_hydra_full_size_sampled_operand_order():
+    # the full Hydra shape reading the operand-order copy of U (4 / 32 / 56 / 72 rows per level)
+    check_hydra(HYDRA_B4, 42, requests=[1], op=True)
 
 
 # ------------------------------------------------- many rows: matrix cores
@@ -208,6 +220,59 @@ def test_heads_medusa_mfma_full_size_sampled(wl_name, M, rows):
     ref["hres"] = ref["hres"]
     compare_medusa(wl, gi[rows], gv[rows], gh[:, rows], ref, label="%s M=%d rows %s" % (wl.name, M, rows))
     del wd
+
+
+# ------------------------------------- operand-order copy of the projection
+
+def test_operand_order_layout():
+    """The copy's layout, bit for bit: [matrix][tile of 256 rows][step of 32 columns][16-row block]
+    [lane][8] with lane l holding row l % 16 and columns 8 (l / 16) .. + 7; padded rows are zero."""
+    md = _md()
+    nmat, rows, cols = 2, 300, 96
+    src = synth.normal(7, 5, (nmat, rows, cols), 1.0, "bf16")
+    dst = from_dev(md.operand_order(to_dev(src)))
+    tiles = (rows + 255) // 256
+    pad = np.zeros((nmat, tiles * 256, cols), dtype=src.dtype)
+    pad[:, :rows] = src
+    # rows -> (tile, block, r); columns -> (step, g, e); lane = 16 g + r
+    x = pad.reshape(nmat, tiles, 16, 16, cols // 32, 4, 8)
+    want = x.transpose(0, 1, 4, 2, 5, 3, 6).reshape(-1)
+    assert dst.dtype == src.dtype and dst.size == md.md_operand_order_bytes(nmat, rows, cols) // 2
+    assert np.array_equal(dst.reshape(-1), want)
+
+
+OP_CASES = [(SMALL_BF16, 2), (SMALL_BF16, 4), (replace(SMALL_BF16, V=1111), 7), (MFMA_BF16, 8),
+            (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9)), 37),
+            (replace(MFMA_BF16, d=128, V=140001, K=2, topk=(10, 3)), 9),
+            (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9)), 65),
+            (replace(MFMA_BF16, V=4099, topk=(10, 4, 1)), 72),
+            (replace(MFMA_BF16, d=128, V=3001, topk=(5, 2, 1)), 100),
+            (replace(MFMA_BF16, V=2053, K=1, topk=(7,)), 128),
+            (replace(MFMA_BF16, V=20011, K=1, topk=(10,)), 250),
+            (replace(MFMA_BF16, V=3001, topk=(6, 3, 1), shared_u=True), 30),
+            (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9), shared_u=True), 3)]
+
+
+@pytest.mark.parametrize("wl,M", OP_CASES, ids=["%s%s M=%d" % (w.name, " shared" if w.shared_u else "", m)
+                                                 for w, m in OP_CASES])
+def test_heads_operand_order(wl, M):
+    """The heads reading the operand-order copy of U: 2 to 7 rows move from the GEMV to the matrix
+    cores; from 8 rows on the same kernels run on the packed copy, so the lists and values are
+    the row-major run's, bit for bit (the copy only moves where each fragment is loaded from)."""
+    md = _md()
+    seed = 5000 + M
+    w = weights(wl, seed)
+    h = synth.normal(seed, 84, (M, wl.d), 1.0, wl.dtype)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    U_op = md.operand_order(wd["U"])
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), M, U_op=U_op)
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, want_logits=True)
+    compare_medusa(wl, gi, gv, gh, ref, label="operand order %s M=%d" % (wl.name, M))
+    gi2, gv2, _ = gpu_heads_medusa(wl, wd, to_dev(h), M, U_op=U_op)
+    assert np.array_equal(gi, gi2) and np.array_equal(gv.view(np.uint32), gv2.view(np.uint32))
+    if M >= 8:
+        gi3, gv3, _ = gpu_heads_medusa(wl, wd, to_dev(h), M)
+        assert np.array_equal(gi, gi3) and np.array_equal(gv.view(np.uint32), gv3.view(np.uint32))
 
 
 # ------------------------------------------- one projection shared by the heads

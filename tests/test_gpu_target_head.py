@@ -36,7 +36,7 @@ CASES = [
 ]
 
 
-def gpu_argmax(dtype, R, d, V, H, Wt):
+def gpu_argmax(dtype, R, d, V, H, Wt, op=False):
     import torch
 
     import medusa_draft_heads_amd as md
@@ -45,18 +45,36 @@ def gpu_argmax(dtype, R, d, V, H, Wt):
     tok = torch.full((R,), -7, dtype=torch.int32, device="cuda")
     val = torch.empty(R, dtype=torch.float32, device="cuda")
     ws = torch.empty(md.md_target_argmax_workspace_bytes(dt, R, d, V), dtype=torch.uint8, device="cuda")
-    md.md_target_argmax(dt, R, d, V, to_dev(H), to_dev(Wt), tok, val, ws)
+    Wt_dev = to_dev(Wt)
+    Wt_op = md.operand_order(Wt_dev) if op else None
+    md.md_target_argmax(dt, R, d, V, to_dev(H), Wt_dev, tok, val, ws, Wt_op=Wt_op)
     torch.cuda.synchronize()
     return from_dev(tok), from_dev(val)
 
 
-@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+OP_CASES = [
+    ("bf16 operand order R=2", "bf16", 2, 512, 5003, True),
+    ("bf16 operand order R=7", "bf16", 7, 256, 4099, True),
+    ("bf16 operand order R=64", "bf16", 64, 512, 5003, True),
+    ("bf16 operand order R=100 one tile", "bf16", 100, 256, 4099, True),
+    ("bf16 operand order R=128 one tile", "bf16", 128, 128, 2053, True),
+    ("bf16 operand order R=130 row-major kernel", "bf16", 130, 256, 3001, True),
+    ("bf16 operand order many lists R=9", "bf16", 9, 128, 140001, True),
+    ("70B-shaped LM head in operand order, 64 nodes", "bf16", 64, 8192, 128256, True),
+]
+
+
+@pytest.mark.parametrize("case", [c + (False,) for c in CASES] + OP_CASES,
+                         ids=[c[0] for c in CASES] + [c[0] for c in OP_CASES])
 def test_target_argmax(case):
-    name, dtype, R, d, V = case
+    """With an operand-order copy of the LM head, 2 to 128 rows run the few-row matrix-core kernels
+    on it (more rows keep the row-major kernel); from 8 rows the result is the row-major run's, bit
+    for bit."""
+    name, dtype, R, d, V, op = case
     seed = R + d
     Wt = synth.normal(seed, 1, (V, d), 1 / math.sqrt(d), dtype)
     H = synth.normal(seed, 2, (R, d), 1.0, dtype)
-    tok, val = gpu_argmax(dtype, R, d, V, H, Wt)
+    tok, val = gpu_argmax(dtype, R, d, V, H, Wt, op)
     rtok, rval, margin = oracle.target_argmax(H, Wt)
     tau, tol = TAU[dtype], TOL[dtype]
     ties = 0
@@ -70,8 +88,11 @@ def test_target_argmax(case):
             assert rval[r] - float(w @ Hf[r]) <= tau
     assert np.max(np.abs(val - rval)) <= tol * np.max(np.abs(rval))
     # bit-identical on a second call
-    tok2, val2 = gpu_argmax(dtype, R, d, V, H, Wt)
+    tok2, val2 = gpu_argmax(dtype, R, d, V, H, Wt, op)
     assert np.array_equal(tok, tok2) and np.array_equal(val.view(np.uint32), val2.view(np.uint32))
+    if op and R >= 8:
+        tok3, val3 = gpu_argmax(dtype, R, d, V, H, Wt)
+        assert np.array_equal(tok, tok3) and np.array_equal(val.view(np.uint32), val3.view(np.uint32))
     print("%s: near ties %d of %d" % (name, ties, R))
 
 
