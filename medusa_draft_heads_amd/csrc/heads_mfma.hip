@@ -128,19 +128,11 @@ __device__ __forceinline__ void tile_mma(const uint16_t (*As)[LP], const uint16_
 
 // h' = base + SiLU(z + b) for 4 consecutive rows r.. of head hh, activation
 // row m, stored as float32 and as its hi/lo bf16 split.
-__device__ __forceinline__ void residual_out(const f32x4& z, const uint16_t* __restrict__ bias, const GemmRows& rows,
-                                             int brow, int M, int d, int head0, int hh, int m, int r,
-                                             float* __restrict__ hres, float* __restrict__ hres_out,
-                                             uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo) {
-    float bb[4] = {0.f, 0.f, 0.f, 0.f};
-    if (bias) {
-        const u32x2 bw = *reinterpret_cast<const u32x2*>(bias + (int64_t)(head0 + hh) * d + r);
-        bb[0] = bf_lo(bw.x);
-        bb[1] = bf_hi(bw.x);
-        bb[2] = bf_lo(bw.y);
-        bb[3] = bf_hi(bw.y);
-    }
-    const u32x2 hw = *reinterpret_cast<const u32x2*>(rows.h + (int64_t)brow * d + r);
+// bw, hw: the 4 bias and base values (bf16 pairs; bw zero without a bias).
+__device__ __forceinline__ void residual_out_w(const f32x4& z, u32x2 bw, u32x2 hw, int M, int d, int hh, int m, int r,
+                                               float* __restrict__ hres, float* __restrict__ hres_out,
+                                               uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo) {
+    const float bb[4] = {bf_lo(bw.x), bf_hi(bw.x), bf_lo(bw.y), bf_hi(bw.y)};
     const float base[4] = {bf_lo(hw.x), bf_hi(hw.x), bf_lo(hw.y), bf_hi(hw.y)};
     f32x4 hv;
     uint32_t hi2[2] = {0u, 0u}, lo2[2] = {0u, 0u};
@@ -161,6 +153,17 @@ __device__ __forceinline__ void residual_out(const f32x4& z, const uint16_t* __r
     if (hres_out) *reinterpret_cast<f32x4*>(hres_out + o) = hv;
     *reinterpret_cast<u32x2*>(hhi + o) = u32x2{hi2[0], hi2[1]};
     *reinterpret_cast<u32x2*>(hlo + o) = u32x2{lo2[0], lo2[1]};
+}
+__device__ __forceinline__ u32x2 bias_words(const uint16_t* __restrict__ bias, int head0, int hh, int d, int r) {
+    return bias ? *reinterpret_cast<const u32x2*>(bias + (int64_t)(head0 + hh) * d + r) : u32x2{0u, 0u};
+}
+__device__ __forceinline__ void residual_out(const f32x4& z, const uint16_t* __restrict__ bias, const GemmRows& rows,
+                                             int brow, int M, int d, int head0, int hh, int m, int r,
+                                             float* __restrict__ hres, float* __restrict__ hres_out,
+                                             uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo) {
+    const u32x2 bw = bias_words(bias, head0, hh, d, r);
+    const u32x2 hw = *reinterpret_cast<const u32x2*>(rows.h + (int64_t)brow * d + r);
+    residual_out_w(z, bw, hw, M, d, hh, m, r, hres, hres_out, hhi, hlo);
 }
 
 // Phase 1: z = W x for rows [0, nh*d) of the heads' residual matrices and
@@ -295,10 +298,32 @@ __global__ __launch_bounds__(BLOCK) void k_residual_finish(const float* __restri
     const int r = (int)(e % d);
     const int64_t hm = e / d;
     const int m = (int)(hm % M), hh = (int)(hm / M);
-    f32x4 z = *reinterpret_cast<const f32x4*>(zpart + e);
-    for (int c = 1; c < ksplit; ++c) z += *reinterpret_cast<const f32x4*>(zpart + (int64_t)c * nh * M * d + e);
     const int brow = rows.kind == 0 ? m : m / rows.P;
-    residual_out(z, bias, rows, brow, M, d, head0, hh, m, r, hres, hres_out, hhi, hlo);
+    // the epilogue's own loads go out first, then the partials 16 at a time
+    // before they are added (in chunk order): one memory round trip per 16
+    // chunks instead of one each
+    const u32x2 bw = bias_words(bias, head0, hh, d, r);
+    const u32x2 hw = *reinterpret_cast<const u32x2*>(rows.h + (int64_t)brow * d + r);
+    const int64_t cs = (int64_t)nh * M * d;
+    f32x4 z = *reinterpret_cast<const f32x4*>(zpart + e);
+    int c = 1;
+    for (; c + 16 <= ksplit; c += 16) {
+        f32x4 p[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) p[j] = *reinterpret_cast<const f32x4*>(zpart + (c + j) * cs + e);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) z += p[j];
+    }
+    if (c < ksplit) {
+        f32x4 p[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (c + j < ksplit) p[j] = *reinterpret_cast<const f32x4*>(zpart + (c + j) * cs + e);
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (c + j < ksplit) z += p[j];
+    }
+    residual_out_w(z, bw, hw, M, d, hh, m, r, hres, hres_out, hhi, hlo);
 }
 
 // Phase 2: logits = U (hi + lo) for one head's VR vocabulary rows x VM
