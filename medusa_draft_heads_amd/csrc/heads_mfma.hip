@@ -1578,6 +1578,105 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The residual over many rows (Medusa heads on every node of a batch): the
+// same GEMM shape as the certified pass, so the same pipeline. Block tile 256
+// rows of W x 128 activation rows, 4 waves of 128 x 64 (8 x 4 MFMA tiles),
+// stages of 24 KB (W 16 KB, h 8 KB) by buffer->LDS loads into three named
+// buffers with two in flight, the 64-byte LDS rows swizzled as there; one
+// product (h is exact in bf16). The epilogue applies h' = h + SiLU(z + b)
+// per 4 outputs of a lane. Tiles never straddle heads (d % 256 == 0).
+__global__ __launch_bounds__(BLOCK, 2) void k_residual_wide(const uint16_t* __restrict__ W,
+                                                            const uint16_t* __restrict__ bias, GemmRows rows, int M,
+                                                            int d, int nh, int head0, int mtiles,
+                                                            float* __restrict__ hres, float* __restrict__ hres_out,
+                                                            uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo,
+                                                            int* __restrict__ bound) {
+    __shared__ __align__(1024) unsigned char wbuf0[CSTAGE];
+    __shared__ __align__(1024) unsigned char wbuf1[CSTAGE];
+    __shared__ __align__(1024) unsigned char wbuf2[CSTAGE];
+    const int units = nh * (d / VR);
+    int unit, mt;
+    if (!decode_tile(blockIdx.x, mtiles, units, unit, mt)) return;
+    const int row0 = unit * VR;  // over nh * d rows
+    const int hh = row0 / d, rt0 = row0 - hh * d;
+    const int m0 = mt * VM;
+    const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g4 = lane >> 4, c16 = lane & 15, wr = w >> 1, wc = w & 1;
+
+    // the vocabulary kernel that follows keeps a lower bound of each (head, row)'s
+    // k-th best logit here; start from -inf
+    if (blockIdx.x == 0)
+        for (int j = tid; j < nh * M; j += BLOCK) bound[j] = f2o(-INFINITY);
+
+    const int r0 = 16 * w + (lane >> 2);
+    const uint32_t voff0 = (uint32_t)r0 * d * 2 + 16 * ((lane & 3) ^ ((r0 >> 1) & 3));
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(W + ((int64_t)head0 * d + row0) * d), 0, VR * d * 2, RSRC3);
+    const __amdgpu_buffer_rsrc_t rH = __builtin_amdgcn_make_buffer_rsrc((void*)(rows.h + (int64_t)m0 * d), 0,
+                                                                        min(M - m0, VM) * d * 2, RSRC3);
+    auto issue = [&](int k0, unsigned char* base) {
+#pragma unroll
+        for (int j = 0; j < NPA; ++j) dmab(rA, base + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
+#pragma unroll
+        for (int j = 0; j < NPB; ++j) dmab(rH, base + A_BYTES + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
+    };
+    f32x4 acc[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int slot = (g4 ^ ((c16 >> 1) & 3)) * 16;
+    auto compute = [&](const unsigned char* sA) {
+        const unsigned char* sB = sA + A_BYTES;
+        bf16x8 a[8];
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb)
+            a[rb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sA + (128 * wr + 16 * rb + c16) * ROWB + slot));
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            const bf16x8 b =
+                __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(sB + (64 * wc + 16 * cb + c16) * ROWB + slot));
+#pragma unroll
+            for (int rb = 0; rb < 8; ++rb)
+                acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b, acc[rb][cb], 0, 0, 0);
+        }
+    };
+    // the certified pass's schedule: the wait leaves the newer stage's NPA + NPB
+    // loads per wave open; an LDS-only barrier; past the last stage the loads
+    // repeat it
+    const int nk = d / VK;
+    auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
+        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        issue(min(s + 2, nk - 1) * VK, nxt);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(cur);
+    };
+    static_assert(NPA + NPB == 6, "the wait count above assumes 6 pieces per wave and stage");
+    issue(0, wbuf0);
+    issue(min(1, nk - 1) * VK, wbuf1);
+    int ks = 0;
+    for (; ks + 3 <= nk; ks += 3) {
+        step(ks, wbuf0, wbuf2);
+        step(ks + 1, wbuf1, wbuf0);
+        step(ks + 2, wbuf2, wbuf1);
+    }
+    if (ks < nk) step(ks, wbuf0, wbuf2);
+    if (ks + 1 < nk) step(ks + 1, wbuf1, wbuf0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads land before the block ends
+
+    // lane holds z[row rt0 + 128 wr + 16 rb + 4 g4 + i][activation row m0 + 64 wc + 16 cb + c16]
+#pragma unroll
+    for (int cb = 0; cb < 4; ++cb) {
+        const int m = m0 + 64 * wc + 16 * cb + c16;
+        if (m >= M) continue;
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb)
+            residual_out(acc[rb][cb], bias, rows, m, M, d, head0, hh, m, rt0 + 128 * wr + 16 * rb + 4 * g4, hres,
+                         hres_out, hhi, hlo);
+    }
+}
+
 __global__ void k_fill_bound(int* __restrict__ bound, int n) {
     const int i = blockIdx.x * blockDim.x + threadIdx.x;
     if (i < n) bound[i] = f2o(-INFINITY);
@@ -1697,6 +1796,13 @@ int residual_ksplit(int M, int d, int din, int nh) {
     return ks;
 }
 
+// Many Medusa rows with whole 256-row tiles of W and enough of them to fill
+// the GPU without a split contraction: the certified pass's pipeline
+// (k_residual_wide); otherwise the 128 x 128 register-staged tiles.
+bool residual_wide(int kind, int M, int d, int din, int nh) {
+    return kind == 0 && din == d && M > kNarrowRows && d % VR == 0 && residual_ksplit(M, d, din, nh) == 1;
+}
+
 // Workspace: h' (float32, hi, lo), the per-row bounds, the split-contraction
 // partials, then either the narrow kernel's partial lists or the certified
 // pass's norms, slots and candidate buffers.
@@ -1802,11 +1908,18 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     const int units1 = a.nh * a.d / TR;
     const int ksplit = residual_ksplit(a.M, a.d, a.din, a.nh);
     const uint16_t* bias = reinterpret_cast<const uint16_t*>(a.b);
-    hipLaunchKernelGGL(k_residual_mfma, dim3(ksplit * 8 * mtiles * ((units1 + 7) / 8)), dim3(BLOCK), 0, s,
-                       reinterpret_cast<const uint16_t*>(a.W), bias, rows, a.M, a.d, a.din, a.nh, a.head0, mtiles,
-                       ksplit, L.zpart, L.hres, a.h_res, L.hhi, L.hlo, L.bound);
+    if (residual_wide(a.kind, a.M, a.d, a.din, a.nh)) {
+        const int wm = (a.M + VM - 1) / VM, wu = a.nh * (a.d / VR);
+        hipLaunchKernelGGL(k_residual_wide, dim3(8 * wm * ((wu + 7) / 8)), dim3(BLOCK), 0, s,
+                           reinterpret_cast<const uint16_t*>(a.W), bias, rows, a.M, a.d, a.nh, a.head0, wm, L.hres,
+                           a.h_res, L.hhi, L.hlo, L.bound);
+    } else {
+        hipLaunchKernelGGL(k_residual_mfma, dim3(ksplit * 8 * mtiles * ((units1 + 7) / 8)), dim3(BLOCK), 0, s,
+                           reinterpret_cast<const uint16_t*>(a.W), bias, rows, a.M, a.d, a.din, a.nh, a.head0, mtiles,
+                           ksplit, L.zpart, L.hres, a.h_res, L.hhi, L.hlo, L.bound);
+    }
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (ksplit > 1) {
+    if (ksplit > 1 && !residual_wide(a.kind, a.M, a.d, a.din, a.nh)) {
         const int64_t quads = e / 4;
         hipLaunchKernelGGL(k_residual_finish, dim3((unsigned)((quads + BLOCK - 1) / BLOCK)), dim3(BLOCK), 0, s, L.zpart,
                            ksplit, bias, rows, a.M, a.d, a.nh, a.head0, L.hres, a.h_res, L.hhi, L.hlo);

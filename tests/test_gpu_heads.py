@@ -275,6 +275,22 @@ def test_heads_operand_order(wl, M):
         assert np.array_equal(gi, gi3) and np.array_equal(gv.view(np.uint32), gv3.view(np.uint32))
 
 
+def test_heads_many_rows_wide_residual():
+    """2,000 rows x 4 heads at d = 1,024: enough whole 256 x 128 tiles that the residual runs the
+    pipelined wide kernel without a split contraction (the last row tile holds 80 rows); every 7th
+    row and the last are checked against the oracle, h' and lists."""
+    wl = Workload("wide residual: d=1024 V=3001 K=4", "medusa", B=1, d=1024, V=3001, K=4, dtype="bf16",
+                  topk=(10, 4, 2, 1), N=10, Hq=4, Hkv=1, hd=64, L=10)
+    M = 2000
+    rows = list(range(0, M, 7)) + [M - 1]
+    w = weights(wl, 4300)
+    h = synth.normal(4300, 85, (M, wl.d), 1.0, wl.dtype)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), M)
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, rows=rows, want_logits=True)
+    compare_medusa(wl, gi[rows], gv[rows], gh[:, rows], ref, label="wide residual M=%d" % M)
+
+
 # ------------------------------------------- one projection shared by the heads
 
 @pytest.mark.parametrize("wl,M", [(replace(TINY_F32, shared_u=True), 1), (replace(TINY_F32, shared_u=True), 3),
