@@ -216,13 +216,13 @@ def operand_order(mat):
     [rows, cols] or [nmat, rows, cols] (allocated once, when weights load)."""
     import torch
 
-    if mat.dtype != torch.bfloat16:
-        raise MedusaError(-1, "operand order exists for bf16 matrices only")
+    if mat.dtype != torch.bfloat16 or mat.dim() not in (2, 3):
+        raise MedusaError(MD_EINVAL, "operand order takes a bf16 [rows, cols] or [nmat, rows, cols] tensor")
     m3 = mat if mat.dim() == 3 else mat.unsqueeze(0)
     nmat, rows, cols = m3.shape
     n = md_operand_order_bytes(nmat, rows, cols)
     if n == 0:
-        raise MedusaError(-2, "operand order needs cols a positive multiple of 32 (got %d)" % cols)
+        raise MedusaError(MD_EUNSUPPORTED, "operand order needs cols a positive multiple of 32 (got %d)" % cols)
     dst = torch.empty(n // 2, dtype=torch.bfloat16, device=mat.device)
     md_operand_order(nmat, rows, cols, m3.contiguous(), dst)
     return dst
