@@ -12,7 +12,9 @@
 // a kv head are its Hq/Hkv query heads times the N nodes, so K and V tiles
 // staged in LDS serve every query head of the group. Each block keeps an
 // online softmax (running max, running sum, unnormalised output) and writes
-// them; a combine kernel merges the key ranges by log-sum-exp.
+// them (the bf16 path writes its output rows divided by the running sum, as
+// 16-bit floats: half the bytes, rounding 2^-11 against the 2^-9 of the bf16
+// result); a combine kernel merges the key ranges by log-sum-exp.
 //
 // bf16 storage runs on the matrix cores (v_mfma_f32_16x16x32_bf16): a wave
 // owns 16 query rows and computes S^T = K Q^T per 16-key block, then
@@ -24,6 +26,7 @@
 // stages with two in flight; the V^T operand comes from gfx950's
 // transposing LDS read (ds_read_b64_tr_b16), so V is never transposed by
 // hand. float32 storage (small workloads) uses an LDS-tiled FMA kernel.
+#include <type_traits>
 #include <math.h>
 
 #include "md_internal.h"
@@ -291,7 +294,7 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
                                                      const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
                                                      const uint16_t* __restrict__ Vc, const int32_t* __restrict__ lens,
                                                      float scale, int splits, int chunk, int qtiles, int ngroups,
-                                                     float* __restrict__ po, float* __restrict__ pm,
+                                                     uint16_t* __restrict__ po, float* __restrict__ pm,
                                                      float* __restrict__ pl) {
     constexpr int CPR = HD / 8;          // 16-byte chunks per key row
     constexpr int ROWB = HD * 2;         // bytes per key row
@@ -479,9 +482,18 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
     l_i += xor32(l_i);
     if (rvalid) {
         const int64_t row = ((int64_t)b * N + node) * Hq + h;
+        // the key range's output row normalised (o / l, bounded by max |V|) as
+        // 16-bit floats: half the bytes of the split's partial rows
+        const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
 #pragma unroll
-        for (int j = 0; j < HD / 16; ++j)
-            *reinterpret_cast<f32x4*>(po + (row * splits + s) * HD + 16 * j + 4 * g4) = o[j];
+        for (int j = 0; j < HD / 16; ++j) {
+            const f32x4 v = o[j] * inv;
+            const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
+            const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
+            *reinterpret_cast<u32x2*>(po + (row * splits + s) * HD + 16 * j + 4 * g4) = u32x2{w0, w1};
+        }
         if (g4 == 0) {
             pm[row * splits + s] = m_i;
             pl[row * splits + s] = l_i;
@@ -490,9 +502,14 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
 }
 
 // out = sum_s 2^{m_s - M} o_s / sum_s 2^{m_s - M} l_s  (M = max_s m_s; the row
-// statistics are kept in the log2 domain)
-template <typename T>
-__global__ void k_attn_combine(int hd, int splits, const float* __restrict__ po, const float* __restrict__ pm,
+// statistics are kept in the log2 domain). P = float: o_s as accumulated;
+// P = uint16_t: o_s / l_s as 16-bit floats (the matrix-core kernel's rows).
+__device__ __forceinline__ float partial_o(const float* po, int64_t i, float l) { return po[i]; }
+__device__ __forceinline__ float partial_o(const uint16_t* po, int64_t i, float l) {
+    return l * (float)__builtin_bit_cast(_Float16, po[i]);
+}
+template <typename T, typename P>
+__global__ void k_attn_combine(int hd, int splits, const P* __restrict__ po, const float* __restrict__ pm,
                                const float* __restrict__ pl, T* __restrict__ out) {
     const int64_t row = blockIdx.x;
     const int c = threadIdx.x;
@@ -504,8 +521,9 @@ __global__ void k_attn_combine(int hd, int splits, const float* __restrict__ po,
     for (int s = 0; s < splits; ++s) {
         const float ms = pm[row * splits + s];
         const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
-        num = fmaf(wgt, po[(row * splits + s) * hd + c], num);
-        den = fmaf(wgt, pl[row * splits + s], den);
+        const float ls = pl[row * splits + s];
+        num = fmaf(wgt, partial_o(po, (row * splits + s) * hd + c, ls), num);
+        den = fmaf(wgt, ls, den);
     }
     st(out, row * hd + c, num / den);
 }
@@ -518,9 +536,13 @@ hipError_t launch_typed(const DevTree& t, int B, int Hq, int Hkv, int hd, int Lc
                         hipStream_t st_) {
     const AttnPlan p = attention_plan(sizeof(T) == 2, B, t.n, Hq, Hkv, hd, max_len);
     const int64_t R = (int64_t)B * t.n * Hq;
+    // partial output rows: float32 as accumulated, or (matrix-core path)
+    // normalised 16-bit floats
+    constexpr bool kHalfRows = sizeof(T) == 2;
+    typedef typename std::conditional<kHalfRows, uint16_t, float>::type P;
     char* w = reinterpret_cast<char*>(ws);
-    float* po = reinterpret_cast<float*>(w);
-    w += align256((size_t)R * p.splits * hd * 4);
+    P* po = reinterpret_cast<P*>(w);
+    w += align256((size_t)R * p.splits * hd * sizeof(P));
     float* pm = reinterpret_cast<float*>(w);
     w += align256((size_t)R * p.splits * 4);
     float* pl = reinterpret_cast<float*>(w);
@@ -547,7 +569,7 @@ hipError_t launch_typed(const DevTree& t, int B, int Hq, int Hkv, int hd, int Lc
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_attn_combine<T>, dim3((unsigned)R), dim3(hd), 0, st_, hd, p.splits, po, pm, pl,
+    hipLaunchKernelGGL((k_attn_combine<T, P>), dim3((unsigned)R), dim3(hd), 0, st_, hd, p.splits, po, pm, pl,
                        reinterpret_cast<T*>(out));
     return hipGetLastError();
 }
@@ -590,7 +612,7 @@ AttnPlan attention_plan(int dt, int B, int N, int Hq, int Hkv, int hd, int max_l
 size_t attention_ws_bytes(int dt, int B, int N, int Hq, int Hkv, int hd, int max_len) {
     const AttnPlan p = attention_plan(dt, B, N, Hq, Hkv, hd, max_len);
     const size_t R = (size_t)B * N * Hq;
-    return align256(R * p.splits * hd * 4) + 2 * align256(R * p.splits * 4);
+    return align256(R * p.splits * hd * (dt == 0 ? 4 : 2)) + 2 * align256(R * p.splits * 4);
 }
 
 hipError_t attention_launch(const DevTree& t, int dt, int B, int Hq, int Hkv, int hd, int Lcap, int max_len,
