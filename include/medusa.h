@@ -141,7 +141,8 @@ int md_operand_order(int nmat, int rows, int cols, const void* src, void* dst, v
  * tok(p) = tree_tok[b][p] otherwise; h' = h[b] + SiLU(W[i-1] x + b[i-1]) with
  * W [K][d][2d]; logits = U[i-1] h'. Row r = b * P_i + (index of p among the
  * level's parents). Outputs are [rows][1][kmax]. E [V][d] (device, dt),
- * root_tok [M], tree_tok [M][tree->n] (device int32); tree (host).
+ * root_tok [M], tree_tok [M][tree->n] (device int32); tree (host). A
+ * parent token outside [0, V) reads as a zero embedding.
  *
  * b may be NULL (zero bias). h_res (device float32, optional) receives h'
  * as [K][M][d] (Medusa) or [rows][d] (Hydra). ws (device) must hold

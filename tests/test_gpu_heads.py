@@ -164,8 +164,48 @@ def test_hydra_full_size_sampled():
     check_hydra(HYDRA_B4, 41, requests=[0])
 
 
+@pytest.mark.parametrize("B", [1, 3])
+def test_hydra_out_of_vocabulary_parent_tokens(B):
+    """A parent token outside [0, V) reads as a zero embedding: level 2 with parent tokens -1 and
+    V + 5 planted among valid ones, against the oracle's residual on x = [h ; 0] for those rows.
+    B = 1 runs its 3 rows on the GEMV, B = 3 its 9 rows on the matrix cores."""
+    import torch
+
+    md = _md()
+    wl = replace(HYDRA_B4, name="hydra oov", B=B, d=256, V=3001, topk=(5, 3, 2, 1), N=20)
+    topo = wl.topology()
+    w = weights(wl, 33)
+    x = step_inputs(wl, 33)
+    level = 2
+    parents = oracle.hydra_rows(topo.parent, level)
+    P = len(parents)
+    tok = synth.randint(33, 86, B * topo.n, 0, wl.V - 1).reshape(B, topo.n)  # inclusive bounds
+    bad = {}
+    for bi in range(B):
+        for j, p in enumerate(parents):
+            if (bi + j) % 3 == 0:
+                tok[bi, p] = -1 if j % 2 == 0 else wl.V + 5
+                bad[(bi, j)] = True
+    wd = {k: to_dev(v) for k, v in w.items()}
+    tree = md.make_tree(topo.parent, topo.rank)
+    gi, gv, gh = gpu_hydra_level(wl, wd, to_dev(x["h"]), to_dev(x["root_tok"]), to_dev(tok), tree, level, B * P)
+    hd = synth.bf16_to_f32(x["h"]).astype(np.float64)
+    Ed = synth.bf16_to_f32(w["E"]).astype(np.float64)
+    xs, base = [], []
+    for bi in range(B):
+        for j, p in enumerate(parents):
+            e = np.zeros(wl.d) if (bi, j) in bad else Ed[tok[bi, p]]
+            xs.append(np.concatenate([hd[bi], e]))
+            base.append(hd[bi])
+    ref = oracle.residual(w["W"][level - 1], w["b"][level - 1], np.array(xs), np.array(base))
+    err = rel_err(gh, ref)
+    assert err <= TOL[wl.dtype], "h' relative error %.3g" % err
+    assert bad and len(bad) < B * P
+    torch.cuda.synchronize()
+
+
 def test_hydra_small_operand_order():
-    # batch 3: levels of 3, 15, 24 and 30 rows, all on the matrix cores with the operand-order copy
+    # batch 3: levels of 3, 9, 15 and 15 rows, all on the matrix cores with the operand-order copy
     wl = replace(HYDRA_B4, name="hydra small", B=3, d=256, V=3001, topk=(5, 3, 2, 1), N=20)
     check_hydra(wl, 32, op=True)
 
