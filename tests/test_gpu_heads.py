@@ -281,7 +281,7 @@ def test_operand_order_layout():
     assert np.array_equal(dst.reshape(-1), want)
 
 
-OP_CASES = [(SMALL_BF16, 2), (SMALL_BF16, 4), (replace(SMALL_BF16, V=1111), 7), (MFMA_BF16, 8),
+OP_CASES = [(SMALL_BF16, 1), (SMALL_BF16, 2), (SMALL_BF16, 4), (replace(SMALL_BF16, V=1111), 7), (MFMA_BF16, 8),
             (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9)), 37),
             (replace(MFMA_BF16, d=128, V=140001, K=2, topk=(10, 3)), 9),
             (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9)), 65),
@@ -296,8 +296,8 @@ OP_CASES = [(SMALL_BF16, 2), (SMALL_BF16, 4), (replace(SMALL_BF16, V=1111), 7), 
 @pytest.mark.parametrize("wl,M", OP_CASES, ids=["%s%s M=%d" % (w.name, " shared" if w.shared_u else "", m)
                                                  for w, m in OP_CASES])
 def test_heads_operand_order(wl, M):
-    """The heads reading the operand-order copy of U: 2 to 7 rows move from the GEMV to the matrix
-    cores; from 8 rows on the same kernels run on the packed copy, so the lists and values are
+    """The heads reading the operand-order copy of U: one row keeps the GEMV (the copy is not read),
+    2 to 7 rows move from the GEMV to the matrix cores; from 8 rows on the same kernels run on the packed copy, so the lists and values are
     the row-major run's, bit for bit (the copy only moves where each fragment is loaded from)."""
     md = _md()
     seed = 5000 + M

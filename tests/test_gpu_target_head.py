@@ -53,6 +53,7 @@ def gpu_argmax(dtype, R, d, V, H, Wt, op=False):
 
 
 OP_CASES = [
+    ("bf16 operand order R=1 (GEMV, copy unused)", "bf16", 1, 512, 5003, True),
     ("bf16 operand order R=2", "bf16", 2, 512, 5003, True),
     ("bf16 operand order R=7", "bf16", 7, 256, 4099, True),
     ("bf16 operand order R=64", "bf16", 64, 512, 5003, True),
