@@ -49,13 +49,24 @@ __global__ __launch_bounds__(BLOCK) void k_argmax_part(const float* __restrict__
         const int V4 = V >> 2;
         const int a = (int)((int64_t)V4 * ch / chunks), e = (int)((int64_t)V4 * (ch + 1) / chunks);
         const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
-        for (int j = a + threadIdx.x; j < e; j += BLOCK) {
-            const f32x4 v = __builtin_nontemporal_load(x4 + j);
+        auto take = [&](const f32x4& v, int j) {
             const int i0 = 4 * j;
             if (beats(v.x, i0, bv, bi)) { bv = v.x; bi = i0; }
             if (beats(v.y, i0 + 1, bv, bi)) { bv = v.y; bi = i0 + 1; }
             if (beats(v.z, i0 + 2, bv, bi)) { bv = v.z; bi = i0 + 2; }
             if (beats(v.w, i0 + 3, bv, bi)) { bv = v.w; bi = i0 + 3; }
+        };
+        // 8 loads in flight per thread before any compare ("beats" is a total
+        // order, so the order the entries are visited in does not matter);
+        // past the chunk's end a load repeats its last chunk of 4 (in bounds)
+        // and is not compared
+        for (int j = a + (int)threadIdx.x; j < e; j += 8 * BLOCK) {
+            f32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(x4 + min(j + u * BLOCK, e - 1));
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                if (j + u * BLOCK < e) take(v[u], j + u * BLOCK);
         }
     } else {
         const int a = (int)((int64_t)V * ch / chunks), e = (int)((int64_t)V * (ch + 1) / chunks);
