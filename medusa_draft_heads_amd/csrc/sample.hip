@@ -152,11 +152,11 @@ __global__ __launch_bounds__(BLOCK) void k_draft_part(const float* __restrict__ 
         ix[j] = INT_MAX;
     }
     float lm = -INFINITY, ls = 0.0f;
-    for (int y = a + tid; y < e; y += BLOCK) {
-        const float z = lg[y] * invT;
+    auto take = [&](int y, float l, uint32_t word) {
+        const float z = l * invT;
         lse_add(lm, ls, z);
-        const float s = z + gumbel_f(wd[y]);
-        if (!above(s, y, v[KM - 1], ix[KM - 1])) continue;
+        const float s = z + gumbel_f(word);
+        if (!above(s, y, v[KM - 1], ix[KM - 1])) return;
 #pragma unroll
         for (int q = KM - 1; q >= 0; --q) {  // insertion; v[q - 1] is read before it moves
             if (!above(s, y, v[q], ix[q])) continue;
@@ -168,6 +168,22 @@ __global__ __launch_bounds__(BLOCK) void k_draft_part(const float* __restrict__ 
                 ix[q] = y;
             }
         }
+    };
+    // 8 logits and words loaded per thread before they are taken, in the same
+    // order as one at a time (past the chunk's end the loads repeat its last
+    // element and are not taken)
+    for (int y0 = a + tid; y0 < e; y0 += 8 * BLOCK) {
+        float lv[8];
+        uint32_t wv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int y = min(y0 + u * BLOCK, e - 1);
+            lv[u] = lg[y];
+            wv[u] = wd[y];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (y0 + u * BLOCK < e) take(y0 + u * BLOCK, lv[u], wv[u]);
     }
     const double lse = block_lse<NWAVE>(lm, ls, shm, shs);
     // k rounds of a block argmax over the thread lists' heads
@@ -263,23 +279,26 @@ int split_chunks(int rows, int V, int target_blocks) {
 }
 
 // Calls f(y, x) for every element y of row x[] in [a, e): 16-byte loads,
-// two in flight per thread, when rows are 16-byte aligned (V % 4 == 0).
+// eight in flight per thread, when rows are 16-byte aligned (V % 4 == 0);
+// each thread visits its elements in increasing order either way (past the
+// range's end the loads repeat its last 16 bytes and are not visited).
 template <int NT, typename F>
 __device__ __forceinline__ void sweep(const float* __restrict__ x, int V, int a, int e, F&& f) {
     const int tid = threadIdx.x;
     if ((V & 3) == 0) {
         const f32x4* x4 = reinterpret_cast<const f32x4*>(x);
         const int a4 = (a + 3) >> 2, e4 = e >> 2;  // chunks split on multiples of 4 below
-        int j = a4 + tid;
-        for (; j + NT < e4; j += 2 * NT) {
-            const f32x4 u = x4[j], w = x4[j + NT];
-            f(4 * j, u.x); f(4 * j + 1, u.y); f(4 * j + 2, u.z); f(4 * j + 3, u.w);
-            const int k = j + NT;
-            f(4 * k, w.x); f(4 * k + 1, w.y); f(4 * k + 2, w.z); f(4 * k + 3, w.w);
-        }
-        if (j < e4) {
-            const f32x4 u = x4[j];
-            f(4 * j, u.x); f(4 * j + 1, u.y); f(4 * j + 2, u.z); f(4 * j + 3, u.w);
+        for (int j = a4 + tid; j < e4; j += 8 * NT) {
+            f32x4 u[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) u[q] = x4[min(j + q * NT, e4 - 1)];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int k = j + q * NT;
+                if (k < e4) {
+                    f(4 * k, u[q].x); f(4 * k + 1, u[q].y); f(4 * k + 2, u[q].z); f(4 * k + 3, u[q].w);
+                }
+            }
         }
     } else {
         for (int y = a + tid; y < e; y += NT) f(y, x[y]);
