@@ -1082,15 +1082,30 @@ __global__ void k_cert_prep(int* __restrict__ bound, int* __restrict__ slots, in
 __device__ __forceinline__ float wave_dot2(const uint16_t* __restrict__ u, const uint16_t* __restrict__ xh,
                                            const uint16_t* __restrict__ xl, int d, int lane) {
     float s = 0.f;
-    for (int c = lane * 8; c < d; c += 512) {
-        const u32x4 w = *reinterpret_cast<const u32x4*>(u + c);
-        const u32x4 h = *reinterpret_cast<const u32x4*>(xh + c), l = *reinterpret_cast<const u32x4*>(xl + c);
+    auto acc = [&](const u32x4& w, const u32x4& h, const u32x4& l) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             s = fmaf(bf_lo(w[e]), bf_lo(h[e]) + bf_lo(l[e]), s);
             s = fmaf(bf_hi(w[e]), bf_hi(h[e]) + bf_hi(l[e]), s);
         }
+    };
+    // eight column steps' loads in flight before their products, added in the
+    // same order as one step at a time (the same sum, bit for bit)
+    int c = lane * 8;
+    for (; c + 7 * 512 < d; c += 8 * 512) {
+        u32x4 w[8], h[8], l[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            w[q] = *reinterpret_cast<const u32x4*>(u + c + q * 512);
+            h[q] = *reinterpret_cast<const u32x4*>(xh + c + q * 512);
+            l[q] = *reinterpret_cast<const u32x4*>(xl + c + q * 512);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) acc(w[q], h[q], l[q]);
     }
+    for (; c < d; c += 512)
+        acc(*reinterpret_cast<const u32x4*>(u + c), *reinterpret_cast<const u32x4*>(xh + c),
+            *reinterpret_cast<const u32x4*>(xl + c));
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
     return s;
