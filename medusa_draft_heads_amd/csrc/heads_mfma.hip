@@ -1680,15 +1680,25 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_wide(const uint16_t* __re
     if (ks + 1 < nk) step(ks + 1, wbuf1, wbuf0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads land before the block ends
 
-    // lane holds z[row rt0 + 128 wr + 16 rb + 4 g4 + i][activation row m0 + 64 wc + 16 cb + c16]
+    // lane holds z[row rt0 + 128 wr + 16 rb + 4 g4 + i][activation row m0 + 64 wc + 16 cb + c16].
+    // The epilogue's loads go out in batches (the 8 bias pairs once, then a
+    // column block's 8 base pairs) before the values that use them: 4 memory
+    // round trips per lane instead of one per 4 outputs.
+    u32x2 bw[8];
+#pragma unroll
+    for (int rb = 0; rb < 8; ++rb) bw[rb] = bias_words(bias, head0, hh, d, rt0 + 128 * wr + 16 * rb + 4 * g4);
 #pragma unroll
     for (int cb = 0; cb < 4; ++cb) {
         const int m = m0 + 64 * wc + 16 * cb + c16;
         if (m >= M) continue;
+        u32x2 hw[8];
 #pragma unroll
         for (int rb = 0; rb < 8; ++rb)
-            residual_out(acc[rb][cb], bias, rows, m, M, d, head0, hh, m, rt0 + 128 * wr + 16 * rb + 4 * g4, hres,
-                         hres_out, hhi, hlo);
+            hw[rb] = *reinterpret_cast<const u32x2*>(rows.h + (int64_t)m * d + rt0 + 128 * wr + 16 * rb + 4 * g4);
+#pragma unroll
+        for (int rb = 0; rb < 8; ++rb)
+            residual_out_w(acc[rb][cb], bw[rb], hw[rb], M, d, hh, m, rt0 + 128 * wr + 16 * rb + 4 * g4, hres,
+                           hres_out, hhi, hlo);
     }
 }
 
