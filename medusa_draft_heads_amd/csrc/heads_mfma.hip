@@ -31,14 +31,18 @@
 //
 // Residual: block tile 128 weight rows x 128 activation rows, K step 64, 4
 // waves of 64 x 64 (4 x 4 MFMA tiles each), operands staged in LDS (rows
-// padded against bank conflicts) from registers loaded one K step ahead.
-// Vocabulary: block tile 256 vocabulary rows x 128 (many rows) or 64 (few
-// rows) activation rows, K step 32, operands loaded straight from memory
-// into LDS in three stages with two in flight, two blocks per CU; from 65
-// to 128 rows, all activation rows in one tile with U streamed into
-// registers (details at the kernels). Both operands are row-major along the contraction, which is
-// exactly the MFMA operand layout (a lane reads 8 consecutive k of one row),
-// so nothing is transposed. Blocks that share a weight tile (the
+// padded against bank conflicts) from registers loaded one K step ahead,
+// the contraction split when the tiles alone cannot fill the GPU; over
+// many Medusa rows the vocabulary kernels' pipeline instead (256 x 128
+// tiles, k_residual_wide). Vocabulary: block tile 256 vocabulary rows x 128
+// (many rows) or 64 (few rows) activation rows, K step 32, operands loaded
+// straight from memory into LDS in three stages with two in flight, two
+// blocks per CU; from 65 to 128 rows, all activation rows in one tile with
+// U streamed into registers (details at the kernels). Both operands are
+// row-major along the contraction, which is exactly the MFMA operand layout
+// (a lane reads 8 consecutive k of one row), so nothing is transposed; an
+// optional operand-order copy of U makes every fragment of the few-row
+// kernels one contiguous 1 KB load. Blocks that share a weight tile (the
 // activation tiles of one weight tile) get ids spaced by 8, i.e. the same
 // XCD and L2.
 #include <math.h>
