@@ -77,7 +77,8 @@ def main() -> int:
                     help="after timing, run a plain 1 GiB device copy (scale factor for HBM counters)")
     ap.add_argument("--operand-order", default="auto", choices=["auto", "on", "off"],
                     help="also keep operand-order copies of the vocabulary matrices for the few-row matrix-core "
-                         "kernels (auto: bf16 Hydra levels and LM-head verification, where 2 to 128 rows meet them)")
+                         "kernels (auto: bf16 Hydra levels, LM-head verification and the shared projection, where "
+                         "2 to 128 projection columns meet them)")
     ap.add_argument("--seed", type=int, default=70)
     ap.add_argument("--cpu-1thread", type=int, default=1, help="also time one oracle step on one thread (0: skip)")
     args = ap.parse_args()
@@ -208,7 +209,7 @@ def main() -> int:
                         delta=wl.delta)
     step = md.MedusaStep(cfg)
     use_op = args.operand_order == "on" or (args.operand_order == "auto" and wl.dtype == "bf16"
-                                             and (hydra or wl.target_head))
+                                             and (hydra or wl.target_head or wl.shared_u))
     if use_op:  # made once with the weights, outside every timed region
         wd.update(step.operand_order_weights(wd))
         torch.cuda.synchronize()

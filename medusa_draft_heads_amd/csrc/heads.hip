@@ -206,12 +206,19 @@ struct KK {
 
 // hres[hh][m][r] = x_m[r] + SiLU(sum_c W[head0+hh][r][c] x_m[c] + b[head0+hh][r])
 template <typename T, int MR>
+// With hhi (bf16 only, for the matrix-core vocabulary kernels) h' is also
+// stored split as hi = bf16(h'), lo = bf16(h' - hi), and block 0 of the
+// first pass sets the nh * M row bounds those kernels keep to bound_init.
 __global__ __launch_bounds__(BLOCK, 4) void k_residual(const T* __restrict__ W, const T* __restrict__ bias, RowSrc src,
                                                     int M, int m0, int d, int din, int nh, int head0,
-                                                    float* __restrict__ hres, float* __restrict__ hres_out) {
+                                                    float* __restrict__ hres, float* __restrict__ hres_out,
+                                                    uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo,
+                                                    int* __restrict__ bound, int bound_init) {
     extern __shared__ __align__(16) float xs[];  // [MR][din]
     const int mr = min(MR, M - m0);
     const T* h = reinterpret_cast<const T*>(src.h);
+    if (bound && m0 == 0 && blockIdx.x == 0)
+        for (int j = threadIdx.x; j < nh * M; j += BLOCK) bound[j] = bound_init;
     // 8 activations per 16-byte (bf16) or two 16-byte (f32) loads; d % 8 == 0,
     // so a chunk never straddles the h / E boundary of a Hydra row
     const int nch = MR * din / 8;
@@ -265,6 +272,11 @@ __global__ __launch_bounds__(BLOCK, 4) void k_residual(const T* __restrict__ W, 
                     const int64_t o = ((int64_t)hh * M + m0 + m) * d + ri;
                     hres[o] = hv;
                     if (hres_out) hres_out[o] = hv;
+                    if (hhi) {
+                        const __bf16 hb = (__bf16)hv;
+                        hhi[o] = __builtin_bit_cast(uint16_t, hb);
+                        hlo[o] = __builtin_bit_cast(uint16_t, (__bf16)(hv - (float)hb));
+                    }
                 }
             }
         }
@@ -597,16 +609,7 @@ hipError_t launch_merge(const float* pv, const int* pi, int M, int nh, int nlist
     return hipGetLastError();
 }
 
-template <typename T>
-hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    const Plan p = make_plan(a.dt, a.M, a.d, a.din, a.nh, a.shared_u);
-    char* ws = reinterpret_cast<char*>(a.ws);
-    float* hres = reinterpret_cast<float*>(ws);
-    ws += align256((size_t)a.nh * a.M * a.d * 4);
-    float* pv = reinterpret_cast<float*>(ws);
-    ws += align256((size_t)a.nh * a.M * p.wg_per_head * a.kmax * 4);
-    int* pi = reinterpret_cast<int*>(ws);
-
+RowSrc row_src(const HeadsArgs& a, const DevTree* tree) {
     RowSrc src;
     src.kind = a.kind;
     src.P = 1;
@@ -622,6 +625,20 @@ hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
         src.P = tree->level_off[a.level + 1] - off;
         for (int j = 0; j < src.P; ++j) src.parents[j] = tree->lp[off + j];
     }
+    return src;
+}
+
+template <typename T>
+hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    const Plan p = make_plan(a.dt, a.M, a.d, a.din, a.nh, a.shared_u);
+    char* ws = reinterpret_cast<char*>(a.ws);
+    float* hres = reinterpret_cast<float*>(ws);
+    ws += align256((size_t)a.nh * a.M * a.d * 4);
+    float* pv = reinterpret_cast<float*>(ws);
+    ws += align256((size_t)a.nh * a.M * p.wg_per_head * a.kmax * 4);
+    int* pi = reinterpret_cast<int*>(ws);
+
+    const RowSrc src = row_src(a, tree);
     KK kk;
     for (int i = 0; i < 8; ++i) kk.v[i] = i < a.nh ? a.kk[i] : 1;
 
@@ -634,15 +651,15 @@ hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
         switch (p.MR) {
             case 4:
                 hipLaunchKernelGGL((k_residual<T, 4>), dim3(p.res_grid), dim3(BLOCK), p.res_lds, s, W, bias, src, a.M,
-                                   m0, a.d, a.din, a.nh, a.head0, hres, a.h_res);
+                                   m0, a.d, a.din, a.nh, a.head0, hres, a.h_res, nullptr, nullptr, nullptr, 0);
                 break;
             case 2:
                 hipLaunchKernelGGL((k_residual<T, 2>), dim3(p.res_grid), dim3(BLOCK), p.res_lds, s, W, bias, src, a.M,
-                                   m0, a.d, a.din, a.nh, a.head0, hres, a.h_res);
+                                   m0, a.d, a.din, a.nh, a.head0, hres, a.h_res, nullptr, nullptr, nullptr, 0);
                 break;
             default:
                 hipLaunchKernelGGL((k_residual<T, 1>), dim3(p.res_grid), dim3(BLOCK), p.res_lds, s, W, bias, src, a.M,
-                                   m0, a.d, a.din, a.nh, a.head0, hres, a.h_res);
+                                   m0, a.d, a.din, a.nh, a.head0, hres, a.h_res, nullptr, nullptr, nullptr, 0);
         }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
@@ -704,8 +721,40 @@ hipError_t launch_typed(const HeadsArgs& a, const DevTree* tree, hipStream_t s, 
 
 }  // namespace
 
+// One Medusa row (its heads' h' through a shared projection are several
+// columns): the GEMV residual streams W at ~5.6 TB/s, where a one-row
+// matrix-core residual would stage 128-row tiles for a single column. With
+// 4 rows the GEMV's 128 KB of LDS a block leaves one block a CU; the
+// matrix-core residual stays there.
+bool residual_on_gemv(int dt, int kind, int M, int d, int din, bool op) {
+    return dt == 1 && kind == 0 && din == d && op && M == 1;
+}
+
+hipError_t residual_gemv_split(const HeadsArgs& a, const DevTree* tree, float* hres, uint16_t* hhi, uint16_t* hlo,
+                               int* bound, int bound_init, hipStream_t s) {
+    const Plan p = make_plan(a.dt, a.M, a.d, a.din, a.nh, a.shared_u);
+    const RowSrc src = row_src(a, tree);
+    const uint16_t* W = reinterpret_cast<const uint16_t*>(a.W);
+    const uint16_t* bias = reinterpret_cast<const uint16_t*>(a.b);
+    switch (p.MR) {  // one pass: residual_on_gemv admits only M <= MR
+        case 4:
+            hipLaunchKernelGGL((k_residual<uint16_t, 4>), dim3(p.res_grid), dim3(BLOCK), p.res_lds, s, W, bias, src, a.M,
+                               0, a.d, a.din, a.nh, a.head0, hres, a.h_res, hhi, hlo, bound, bound_init);
+            break;
+        case 2:
+            hipLaunchKernelGGL((k_residual<uint16_t, 2>), dim3(p.res_grid), dim3(BLOCK), p.res_lds, s, W, bias, src, a.M,
+                               0, a.d, a.din, a.nh, a.head0, hres, a.h_res, hhi, hlo, bound, bound_init);
+            break;
+        default:
+            hipLaunchKernelGGL((k_residual<uint16_t, 1>), dim3(p.res_grid), dim3(BLOCK), p.res_lds, s, W, bias, src, a.M,
+                               0, a.d, a.din, a.nh, a.head0, hres, a.h_res, hhi, hlo, bound, bound_init);
+    }
+    return hipGetLastError();
+}
+
 size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u, bool op) {
-    if (heads_mfma_applicable(dt, M, d, din, op)) return heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u);
+    if (heads_mfma_applicable(dt, M, d, din, op, shared_u ? nh * M : M))
+        return heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u);
     const Plan p = make_plan(dt, M, d, din, nh, shared_u);
     return align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * p.wg_per_head * kmax * 4);
 }
@@ -722,7 +771,8 @@ hipError_t topk_merge_launch(const float* pv, const int* pi, int M, int nh, int 
 size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u) {
     // with or without an operand-order copy of U
     const size_t mfma =
-        heads_mfma_applicable(dt, M, d, din, true) ? heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u) : 0;
+        heads_mfma_applicable(dt, M, d, din, true, shared_u ? nh * M : M) ? heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u)
+                                                                          : 0;
     const size_t lists_max = (size_t)device_cus() * 4;  // blocks per head at most
     const size_t gemv = align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * lists_max * kmax * 4);
     return gemv > mfma ? gemv : mfma;
@@ -809,7 +859,8 @@ hipError_t target_argmax_launch(int dt, int R, int d, int V, const void* H, cons
 }
 
 hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
-    if (!a.logits && heads_mfma_applicable(a.dt, a.M, a.d, a.din, a.U_op != nullptr)) {
+    if (!a.logits &&
+        heads_mfma_applicable(a.dt, a.M, a.d, a.din, a.U_op != nullptr, a.shared_u ? a.nh * a.M : a.M)) {
         // many rows: the two contractions on the matrix cores, then the same k-way merge
         float* pv;
         int* pi;

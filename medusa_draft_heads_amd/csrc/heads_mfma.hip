@@ -46,6 +46,7 @@
 // activation tiles of one weight tile) get ids spaced by 8, i.e. the same
 // XCD and L2.
 #include <math.h>
+#include <string.h>
 
 #include <algorithm>
 
@@ -1809,10 +1810,12 @@ hipError_t operand_order_launch(int nmat, int rows, int cols, const void* src, v
     return hipGetLastError();
 }
 
-bool heads_mfma_applicable(int dt, int M, int d, int din, bool op) {
+bool heads_mfma_applicable(int dt, int M, int d, int din, bool op, int rows_v) {
     // d % 128: whole residual tiles, and an even number of vocabulary stages;
-    // with an operand-order copy of U from 2 rows (the GEMV stays for 1)
-    return dt == 1 && (M >= 8 || (op && M >= 2)) && d % TR == 0 && din % KS == 0 && d % (2 * VK) == 0;
+    // with an operand-order copy of U from 2 projection columns (rows_v: the
+    // rows, or heads x rows through one shared projection; the GEMV stays
+    // for 1)
+    return dt == 1 && (M >= 8 || (op && rows_v >= 2)) && d % TR == 0 && din % KS == 0 && d % (2 * VK) == 0;
 }
 
 // Contraction chunks of the residual: enough (tile, chunk) blocks for two per
@@ -1937,7 +1940,17 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     const int units1 = a.nh * a.d / TR;
     const int ksplit = residual_ksplit(a.M, a.d, a.din, a.nh);
     const uint16_t* bias = reinterpret_cast<const uint16_t*>(a.b);
-    if (residual_wide(a.kind, a.M, a.d, a.din, a.nh)) {
+    // one Medusa row (a shared projection) with an operand-order copy: the GEMV residual
+    // (one pass over W, HBM-bound) writes h' and its hi/lo split for the
+    // matrix-core vocabulary kernel; otherwise a matrix-core residual
+    const bool on_gemv = residual_on_gemv(a.dt, a.kind, a.M, a.d, a.din, a.U_op != nullptr);
+    if (on_gemv) {
+        float ninf = -INFINITY;
+        int nb;
+        memcpy(&nb, &ninf, 4);
+        nb = nb >= 0 ? nb : nb ^ 0x7FFFFFFF;  // the bounds' order-preserving encoding of -inf
+        if ((err = residual_gemv_split(a, tree, L.hres, L.hhi, L.hlo, L.bound, nb, s)) != hipSuccess) return err;
+    } else if (residual_wide(a.kind, a.M, a.d, a.din, a.nh)) {
         const int wm = (a.M + VM - 1) / VM, wu = a.nh * (a.d / VR);
         hipLaunchKernelGGL(k_residual_wide, dim3(8 * wm * ((wu + 7) / 8)), dim3(BLOCK), 0, s,
                            reinterpret_cast<const uint16_t*>(a.W), bias, rows, a.M, a.d, a.nh, a.head0, wm, L.hres,
@@ -1948,7 +1961,7 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
                            ksplit, L.zpart, L.hres, a.h_res, L.hhi, L.hlo, L.bound);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (ksplit > 1 && !residual_wide(a.kind, a.M, a.d, a.din, a.nh)) {
+    if (!on_gemv && ksplit > 1 && !residual_wide(a.kind, a.M, a.d, a.din, a.nh)) {
         const int64_t quads = e / 4;
         hipLaunchKernelGGL(k_residual_finish, dim3((unsigned)((quads + BLOCK - 1) / BLOCK)), dim3(BLOCK), 0, s, L.zpart,
                            ksplit, bias, rows, a.M, a.d, a.nh, a.head0, L.hres, a.h_res, L.hhi, L.hlo);

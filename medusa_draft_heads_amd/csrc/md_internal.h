@@ -64,7 +64,11 @@ struct HeadsArgs {
 size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u, bool op);  // this plan
 size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u);  // any plan of these sizes
 // matrix-core path for many rows (heads_mfma.hip)
-bool heads_mfma_applicable(int dt, int M, int d, int din, bool op);
+bool heads_mfma_applicable(int dt, int M, int d, int din, bool op, int rows_v);  // rows_v: projection columns
+// one Medusa row with an operand-order copy (shared projection): the GEMV residual feeds the matrix cores
+bool residual_on_gemv(int dt, int kind, int M, int d, int din, bool op);
+hipError_t residual_gemv_split(const HeadsArgs& a, const DevTree* tree, float* hres, uint16_t* hhi, uint16_t* hlo,
+                               int* bound, int bound_init, hipStream_t s);
 size_t heads_mfma_ws_bytes(int M, int d, int din, int V, int nh, int kmax, int shared_u);
 hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                              float** part_val, int** part_idx, int* nlists);

@@ -290,14 +290,17 @@ OP_CASES = [(SMALL_BF16, 1), (SMALL_BF16, 2), (SMALL_BF16, 4), (replace(SMALL_BF
             (replace(MFMA_BF16, V=2053, K=1, topk=(7,)), 128),
             (replace(MFMA_BF16, V=20011, K=1, topk=(10,)), 250),
             (replace(MFMA_BF16, V=3001, topk=(6, 3, 1), shared_u=True), 30),
-            (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9), shared_u=True), 3)]
+            (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9), shared_u=True), 3),
+            (replace(MFMA_BF16, V=3001, topk=(6, 3, 1), shared_u=True), 1),
+            (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9), shared_u=True), 4)]
 
 
 @pytest.mark.parametrize("wl,M", OP_CASES, ids=["%s%s M=%d" % (w.name, " shared" if w.shared_u else "", m)
                                                  for w, m in OP_CASES])
 def test_heads_operand_order(wl, M):
     """The heads reading the operand-order copy of U: one row keeps the GEMV (the copy is not read),
-    2 to 7 rows move from the GEMV to the matrix cores; from 8 rows on the same kernels run on the packed copy, so the lists and values are
+    2 to 7 rows move from the GEMV to the matrix cores (one row through a shared projection keeps the
+    GEMV residual, which then also writes the hi/lo split); from 8 rows on the same kernels run on the packed copy, so the lists and values are
     the row-major run's, bit for bit (the copy only moves where each fragment is loaded from)."""
     md = _md()
     seed = 5000 + M
@@ -362,6 +365,21 @@ def test_heads_shared_projection_full_size():
     ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, want_logits=True)
     compare_medusa(wl, gi, gv, gh, ref, label=wl.name)
     del wd
+
+
+def test_heads_shared_projection_full_size_operand_order():
+    """The 70B-shaped shared projection at batch 1 with an operand-order copy of U: the GEMV
+    residual, then the 4 heads' h' as 4 columns of the narrow matrix-core kernel."""
+    md = _md()
+    wl = LLAMA70B_SHARED
+    w = weights(wl, 73)
+    h = step_inputs(wl, 73)["h"]
+    wd = {k: to_dev(v) for k, v in w.items()}
+    U_op = md.operand_order(wd["U"])
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), 1, U_op=U_op)
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, want_logits=True)
+    compare_medusa(wl, gi, gv, gh, ref, label=wl.name + " operand order")
+    del wd, U_op
 
 
 def test_heads_shared_projection_many_rows_sampled():
