@@ -72,7 +72,9 @@ def main() -> int:
     ap.add_argument("--sets", type=int, default=0,
                     help="input sets rotated per step (0: enough that the non-weight bytes exceed twice the 256 MB "
                          "Infinity Cache, at most 16)")
-    ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps timed for the CPU baseline (0: skip)")
+    ap.add_argument("--cpu-steps", type=int, default=11,
+                    help="oracle steps timed for the CPU baseline, one per input set (0: skip); the default takes every "
+                         "set of the 70B-shaped workload, ~5 s on 16 host threads plus ~6 s for one step on one thread")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (scale factor for HBM counters)")
     ap.add_argument("--operand-order", default="auto", choices=["auto", "on", "off"],
