@@ -601,6 +601,11 @@ AttnPlan attention_plan(int dt, int B, int N, int Hq, int Hkv, int hd, int max_l
     // split the keys so that one round of resident blocks covers the grid
     const int target = device_cus() * attention_occupancy(dt, hd);
     int splits = target / base;
+    // short ranges cost more in the split (partial rows written and combined)
+    // than they gain in parallelism: under 8 tiles a range on average, half as
+    // many (at the 70B shape, B = 1: L = 2,048 24.1 -> 21.1 us with the
+    // combine, L = 4,096 with 11 tiles a range 26.0 -> 27.1 us, so kept)
+    if (splits >= 2 && tiles < 8 * splits) splits /= 2;
     if (splits > tiles) splits = tiles;
     if (splits < 1) splits = 1;
     const int tiles_per = (tiles + splits - 1) / splits;
