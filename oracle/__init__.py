@@ -221,9 +221,15 @@ def hydra_expand(W, b, U, E, h, topo_parent, topo_rank, topk: Sequence[int], roo
     hd = to_double(h)
     Ed_cache: Dict[int, np.ndarray] = {}
 
+    V = E.shape[0]
+
     def emb(tok: int) -> np.ndarray:
+        # a token outside [0, V) names no row of E: it embeds as zeros
         if tok not in Ed_cache:
-            Ed_cache[tok] = to_double(np.ascontiguousarray(E[tok]))
+            if 0 <= tok < V:
+                Ed_cache[tok] = to_double(np.ascontiguousarray(E[tok]))
+            else:
+                Ed_cache[tok] = np.zeros(E.shape[1], dtype=np.float64)
         return Ed_cache[tok]
 
     tok = np.full((B, N), -1, dtype=np.int32)

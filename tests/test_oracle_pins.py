@@ -224,6 +224,99 @@ def test_hydra_level1_with_zero_embedding_half_is_medusa():
                 assert hy["tree_tok"][b_, n] == me["idx"][b_, 0, topo.rank[n]]
 
 
+def _hydra_planted(V, K, seed):
+    # V = d; the h half of every W is zero and its E half a permutation matrix
+    # Q_i, b_i = c_i (a positive constant per head), h = 0, and head i's
+    # projection is a permutation matrix P_i. Level i then gives the parent's
+    # row hres[r] = SiLU(E[t][sigma_i(r)] + c_i), t the parent's token, and
+    # the logits logit[v] = hres[pi_i(v)]. E rows hold a permutation of 1..V
+    # scaled by 1/V (exact in bf16, all positive, distinct), and SiLU
+    # increases on the positives, so head i's list for a parent with token t
+    # is exactly the library's stable argsort of -E[t][sigma_i][pi_i].
+    d = V
+    rng = np.random.default_rng(seed)
+    bf = lambda x: (np.asarray(x, np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    E = np.stack([rng.permutation(V) + 1 for _ in range(V)]).astype(np.float32) / V
+    sig = [rng.permutation(d) for _ in range(K)]
+    pis = [rng.permutation(V) for _ in range(K)]
+    c = [0.25 * (i + 1) for i in range(K)]
+    W = np.zeros((K, d, 2 * d), np.float32)
+    U = np.zeros((K, V, d), np.float32)
+    b = np.zeros((K, d), np.float32)
+    for i in range(K):
+        W[i, np.arange(d), d + sig[i]] = 1.0
+        U[i, np.arange(V), pis[i]] = 1.0
+        b[i] = c[i]
+    perm = [sig[i][pis[i]] for i in range(K)]  # logit[v] = SiLU(E[t][perm_i[v]] + c_i)
+    return bf(W), bf(b), bf(U), bf(E), E, sig, perm, c
+
+
+def test_hydra_rows_parent_sets():
+    # a hand-built topology: root; two depth-1 nodes, the first with two
+    # children and the second with one; one depth-3 node under node 3
+    parent = [-1, 0, 0, 1, 1, 2, 3]
+    assert oracle.hydra_rows(parent, 1) == [0]
+    assert oracle.hydra_rows(parent, 2) == [1, 2]
+    assert oracle.hydra_rows(parent, 3) == [3]
+    assert oracle.hydra_rows(parent, 4) == []
+    # the 64-node product-order tree over (10, 4, 2, 1): parents with children
+    # per level, hence rows per request for Hydra's four levels
+    topo = product_order_tree((10, 4, 2, 1), 64)
+    assert [len(oracle.hydra_rows(topo.parent, i)) for i in (1, 2, 3, 4)] == [1, 8, 14, 18]
+
+
+@pytest.mark.parametrize("topk,n_nodes", [((4, 2, 2, 1), 16), ((10, 4, 2, 1), 64), ((3, 3, 3), 20)])
+def test_hydra_levels_follow_each_nodes_own_parent_token(topk, n_nodes):
+    # Hydra's heads are sequentially dependent (Hydra abstract): a node at depth
+    # i takes its entry from the list head i computes for the node's own parent
+    # token. With the planted weights above the expected tree is a recursion of
+    # library sorts from the root token, independent of the oracle's arithmetic.
+    V, K = 64, len(topk)
+    W, b, U, E_bf, E, sig, perm, c = _hydra_planted(V, K, 7 + n_nodes)
+    topo = product_order_tree(topk, n_nodes)
+    h = np.zeros((3, V), np.uint16)
+    root = np.array([5, 40, 63], np.int32)
+    lens = np.array([0, 17, 1000], np.int32)
+    hy = oracle.hydra_expand(W, b, U, E_bf, h, topo.parent, topo.rank, topk, root, lens)
+    for r in range(3):
+        want = [int(root[r])]
+        for n in range(1, topo.n):
+            i = len(topo.paths[n])
+            parent_tok = want[topo.parent[n]]
+            order = np.argsort(-E[parent_tok][perm[i - 1]], kind="stable")
+            want.append(int(order[topo.rank[n]]))
+        assert hy["tree_tok"][r].tolist() == want
+        assert hy["tree_pos"][r].tolist() == [int(lens[r]) + len(p) for p in topo.paths]
+    # every level's rows are (request, parent with children at that depth), and
+    # each row's whole list is that parent's sort
+    for i, lvl in enumerate(hy["levels"], start=1):
+        parents = oracle.hydra_rows(topo.parent, i)
+        assert lvl["rows"] == [(r, p) for r in range(3) for p in parents]
+        for j, (r, p) in enumerate(lvl["rows"]):
+            t = int(hy["tree_tok"][r, p])
+            order = np.argsort(-E[t][perm[i - 1]], kind="stable")[: topk[i - 1]]
+            assert lvl["idx"][j].tolist() == order.tolist()
+            # the row itself: torch's SiLU of the gathered, shifted E row
+            z = torch.from_numpy(E[t][sig[i - 1]].astype(np.float64) + c[i - 1])
+            assert np.allclose(lvl["hres"][j], torch.nn.functional.silu(z).numpy(), rtol=0, atol=1e-14)
+
+
+def test_hydra_parent_token_outside_vocabulary_embeds_as_zero():
+    # a parent token outside [0, V) names no row of E: with h = 0 the row's
+    # pre-activation is then the constant bias c_1, every logit is SiLU(c_1)
+    # and the list is 0, 1, 2, ... (equal values, lower index first)
+    V, K = 64, 2
+    W, b, U, E_bf, _, _, _, c = _hydra_planted(V, K, 3)
+    topo = product_order_tree((4, 2), 7)
+    h = np.zeros((2, V), np.uint16)
+    hy = oracle.hydra_expand(W, b, U, E_bf, h, topo.parent, topo.rank, (4, 2),
+                             np.array([-1, V + 5], np.int32), np.array([0, 0], np.int32))
+    lvl1 = hy["levels"][0]
+    assert lvl1["idx"].tolist() == [[0, 1, 2, 3], [0, 1, 2, 3]]
+    want = torch.nn.functional.silu(torch.tensor(c[0], dtype=torch.float64)).item()
+    assert np.allclose(lvl1["hres"], want, rtol=0, atol=1e-15)
+
+
 # ------------------------------------------------------------------ the tree
 
 def test_tree_tokens_by_brute_force():
