@@ -117,7 +117,7 @@ def main() -> int:
     # own tree tokens; the oracle's step on the first --cpu-steps sets is the
     # CPU baseline. With heads over many rows the oracle runs the rows that
     # build the trees and its per-row time is scaled to all rows.
-    sets, cpu_times, acc_oracle = [], [], []
+    sets, cpu_times, acc_oracle, oracle_margin = [], [], [], []
     threads = oracle.threads()
     sample_note = ""
     if args.sets <= 0:  # rotate past the 256 MB Infinity Cache: non-weight bytes >= 2 x 256 MB
@@ -133,11 +133,14 @@ def main() -> int:
         if hydra:
             hy = oracle.hydra_expand(w["W"], w["b"], w["U"], w["E"], x["h"], topo.parent, topo.rank, wl.topk,
                                      x["root_tok"], x["lens"])
-            return hy["tree_tok"], None, time.perf_counter() - ta
+            margin = min(float(np.min(lvl["margin"])) for lvl in hy["levels"])
+            return hy["tree_tok"], {"margin": margin}, time.perf_counter() - ta
         if wl.verify == "sampled":  # one row per request: the heads' logits, then the drafts drawn from them
             heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], [1] * wl.K, want_logits=True)
-            full = oracle.draft_sample(heads["logits"], x["draft_words"], wl.topk, wl.temperature)["tok"]
-            tok, _ = oracle.tree_tokens_medusa(topo.parent, topo.rank, full, x["src_row"], x["root_tok"], x["lens"])
+            dr = oracle.draft_sample(heads["logits"], x["draft_words"], wl.topk, wl.temperature)
+            tok, _ = oracle.tree_tokens_medusa(topo.parent, topo.rank, dr["tok"], x["src_row"], x["root_tok"],
+                                               x["lens"])
+            heads["margin"] = dr["margin"]
             return tok, heads, time.perf_counter() - ta
         rows = sorted(set(int(r) for r in x["src_row"]))
         heads = oracle.heads_medusa(w["W"], w["b"], w["U"], x["h"], wl.topk, rows=rows)
@@ -154,18 +157,22 @@ def main() -> int:
         """The rest of the oracle's step (attention, verification, acceptance, compaction), and its time."""
         tc = time.perf_counter()
         oracle.tree_attention(topo.parent, x["q"], x["Kc"], x["Vc"], x["lens"])
+        vmargin = np.inf
         if wl.target_head:
-            tstar = oracle.target_argmax(x["Ht"].reshape(wl.B * topo.n, wl.d), w["Wt"])[0].reshape(wl.B, topo.n)
+            tstar, _, tm = oracle.target_argmax(x["Ht"].reshape(wl.B * topo.n, wl.d), w["Wt"])
+            tstar, vmargin = tstar.reshape(wl.B, topo.n), float(np.min(tm))
         elif wl.verify == "sampled":  # the token after every node the walk passes through
-            tstar = oracle.verify_sampled(topo.parent, tok, logits, heads["logits"], wl.temperature, x["u_words"],
-                                          x["g_words"])["chosen"]
+            vs = oracle.verify_sampled(topo.parent, tok, logits, heads["logits"], wl.temperature, x["u_words"],
+                                       x["g_words"])
+            tstar, vmargin = vs["chosen"], float(np.min(vs["margin"]))
         elif wl.verify == "typical":
-            tstar = oracle.typical_accept(topo.parent, tok, logits, wl.temperature, wl.eps, wl.delta,
-                                          x["g_words"])["chosen"]
+            ty = oracle.typical_accept(topo.parent, tok, logits, wl.temperature, wl.eps, wl.delta, x["g_words"])
+            tstar, vmargin = ty["chosen"], float(np.min(ty["margin"]))
         else:
             tstar = oracle.argmax(logits)
         r = oracle.accept(topo.parent, wl.K, tok, tstar, x["lens"])
         oracle.compact(x["Kc"], x["Vc"], x["lens"], r["accept_len"], r["path"], wl.K)
+        r["margin"] = min(vmargin, float(np.min(heads["margin"])) if heads is not None else np.inf)
         return r, time.perf_counter() - tc
 
     first = None
@@ -183,6 +190,7 @@ def main() -> int:
             r, rest_time = oracle_rest(x, tok, heads, logits)
             cpu_times.append(heads_time + rest_time)
             acc_oracle.append([int(v) for v in r["accept_len"]])
+            oracle_margin.append(r["margin"])
             log("oracle step %d: %.2f s (accept_len %s)" % (s, cpu_times[-1], acc_oracle[-1]))
             if first is None:
                 first = x
@@ -233,9 +241,9 @@ def main() -> int:
     lens_bank = [sets[i % len(sets)]["lens0"].clone() for i in range(args.warmup + 2 * args.steps)]
     torch.cuda.synchronize()
 
-    def one_step(i: int, pairs=None, lm=None):
+    def one_step(i: int, pairs=None, lm=None, lens=None):
         xd = dict(sets[i % len(sets)])
-        xd["lens"] = lens_bank[i]
+        xd["lens"] = lens_bank[i] if lens is None else lens
         for lvl in range(calls):
             if pairs is not None:
                 md.md_set_vocab_timing_events(pairs[lvl][0].cuda_event, pairs[lvl][1].cuda_event)
@@ -270,6 +278,22 @@ def main() -> int:
         if lm is not None and not wl.target_head:
             lm[1].record(stream)
 
+    # outside every timed region: one step on every input set the oracle ran,
+    # its accepted lengths against the oracle's (bit for bit; a difference is
+    # allowed only where the oracle saw a decision within tau of a tie)
+    acc_gpu, acc_check = [], []
+    for i in range(len(acc_oracle)):
+        one_step(i, lens=sets[i]["lens0"].clone())
+        acc_gpu.append([int(v) for v in step.accept_len.cpu().numpy()])
+        if acc_gpu[-1] == acc_oracle[i]:
+            acc_check.append("equal")
+        elif oracle_margin[i] <= 1e-4:
+            acc_check.append("near tie (oracle margin %.2g)" % oracle_margin[i])
+        else:
+            acc_check.append("DIFFERENT")
+    mismatch = [i for i, c in enumerate(acc_check) if c == "DIFFERENT"]
+    log("accepted lengths, GPU vs oracle, %d input sets: %s" % (len(acc_gpu), "all equal" if all(
+        c == "equal" for c in acc_check) else acc_check))
     for i in range(args.warmup):
         one_step(i)
     torch.cuda.synchronize()
@@ -423,7 +447,10 @@ def main() -> int:
         "step_hbm": {"bytes_per_step": step_bytes, "GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},
         "stream_read_GBps": round(stream_gbs, 1),
-        "acceptance": {"last_step_accept_len": acc_len, "oracle_accept_len": acc_oracle, "E_closed_form": round(E, 4)},
+        "acceptance": {"last_step_accept_len": acc_len, "gpu_accept_len": acc_gpu, "oracle_accept_len": acc_oracle,
+                       "gpu_vs_oracle": "equal on all %d input sets" % len(acc_gpu)
+                       if all(c == "equal" for c in acc_check) else acc_check,
+                       "E_closed_form": round(E, 4)},
         "cpu_baseline": cpu,
     }
     if lm_head:
@@ -432,6 +459,9 @@ def main() -> int:
         out["verification"] = verification
         out["acceptance"].pop("E_closed_form")
     print(json.dumps(out), flush=True)
+    if mismatch:
+        log("GPU accepted lengths differ from the oracle's on input sets %s" % mismatch)
+        return 3
     return 0
 
 

@@ -97,6 +97,19 @@ int64_t md_heads_weight_bytes(int kind, int dt, int d, int V, int K);
  * most 64 * B), with or without an operand-order copy of U. */
 size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, int kmax);
 
+/* Many bf16 rows (more than 128 through the projection) take a certified
+ * single-product pass: the matrix cores form U.hi only, every logit is
+ * known to within E = N ((1 + 2^-7) |h' - hi| + c(d) |h'|) of it (N the
+ * largest row norm of U in a 256-row tile, Cauchy-Schwarz), entries that
+ * cannot reach the top k are dropped and the rest re-scored from hi + lo, so
+ * the lists are those of the float32 re-scored logits over the whole
+ * vocabulary. This returns c(d): the float32 rounding allowance of both
+ * sums per unit |U_v| |h'| at contraction length d, from the recursive
+ * summation bound gamma_n = n u / (1 - n u), u = 2^-24, over d / 32 + 32
+ * roundings of the matrix-core sum and d / 64 + 6 of the re-scoring. Host
+ * only; -1 for d < 1. */
+float md_certified_rounding_allowance(int d);
+
 /* Operand order: a copy of nmat row-major bf16 matrices [rows][cols] laid
  * out for the matrix cores, written once when the weights load. Every MFMA
  * operand fragment (16 rows x 32 contraction elements, 1 KB) is contiguous

@@ -26,7 +26,7 @@ EXPORTS = (
     "md_target_argmax_workspace_bytes", "md_target_argmax", "md_tree_accept_tokens",
     "md_heads_logits_workspace_bytes", "md_medusa_heads_logits", "md_draft_sample_workspace_bytes", "md_draft_sample",
     "md_verify_sampled_workspace_bytes", "md_tree_verify_sampled", "md_accept_typical_workspace_bytes",
-    "md_tree_accept_typical", "md_operand_order_bytes", "md_operand_order",
+    "md_tree_accept_typical", "md_operand_order_bytes", "md_operand_order", "md_certified_rounding_allowance",
 )
 
 
@@ -63,6 +63,7 @@ def lib() -> ctypes.CDLL:
         sig = {
             "md_tree_validate": ([tp, i, vp], i),
             "md_heads_weight_bytes": ([i, i, i, i, i], i64),
+            "md_certified_rounding_allowance": ([i], f),
             "md_heads_workspace_bytes": ([i, i, i, i, i, i, i], sz),
             "md_medusa_heads": ([i, i, i, i, i, i, vp, i, tp] + [vp] * 12 + [sz, vp], i),
             "md_tree_build": ([tp, i, i, i, i, i, i] + [vp] * 6 + [vp], i),
@@ -138,6 +139,10 @@ def md_last_error() -> str:
 
 def md_heads_weight_bytes(kind: int, dt: int, d: int, V: int, K: int) -> int:
     return int(lib().md_heads_weight_bytes(kind, dt, d, V, K))
+
+
+def md_certified_rounding_allowance(d: int) -> float:
+    return float(lib().md_certified_rounding_allowance(d))
 
 
 def md_heads_workspace_bytes(kind: int, dt: int, M: int, d: int, V: int, K: int, kmax: int) -> int:

@@ -114,6 +114,8 @@ int64_t md_heads_weight_bytes(int kind, int dt, int d, int V, int K) {
     return params * (dt == MD_F32 ? 4 : 2);
 }
 
+float md_certified_rounding_allowance(int d) { return d > 0 ? cert_rounding_allowance(d) : -1.f; }
+
 size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, int kmax) {
     if (M <= 0 || d <= 0 || V <= 0 || K <= 0 || kmax <= 0) return 0;
     if (kind == MD_HEADS_HYDRA) {

@@ -12,9 +12,10 @@
 // a kv head are its Hq/Hkv query heads times the N nodes, so K and V tiles
 // staged in LDS serve every query head of the group. Each block keeps an
 // online softmax (running max, running sum, unnormalised output) and writes
-// them (the bf16 path writes its output rows divided by the running sum, as
-// 16-bit floats: half the bytes, rounding 2^-11 against the 2^-9 of the bf16
-// result); a combine kernel merges the key ranges by log-sum-exp.
+// them (the bf16 path writes its output rows divided by the running sum and
+// scaled by a power of two, as 16-bit floats: half the bytes, rounding 2^-11
+// against the 2^-9 of the bf16 result); a combine kernel merges the key
+// ranges by log-sum-exp.
 //
 // bf16 storage runs on the matrix cores (v_mfma_f32_16x16x32_bf16): a wave
 // owns 16 query rows and computes S^T = K Q^T per 16-key block, then
@@ -26,8 +27,9 @@
 // stages with two in flight; the V^T operand comes from gfx950's
 // transposing LDS read (ds_read_b64_tr_b16), so V is never transposed by
 // hand. float32 storage (small workloads) uses an LDS-tiled FMA kernel.
-#include <type_traits>
 #include <math.h>
+
+#include <type_traits>
 
 #include "md_internal.h"
 
@@ -295,7 +297,7 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
                                                      const uint16_t* __restrict__ Vc, const int32_t* __restrict__ lens,
                                                      float scale, int splits, int chunk, int qtiles, int ngroups,
                                                      uint16_t* __restrict__ po, float* __restrict__ pm,
-                                                     float* __restrict__ pl) {
+                                                     float* __restrict__ pl, float* __restrict__ pe) {
     constexpr int CPR = HD / 8;          // 16-byte chunks per key row
     constexpr int ROWB = HD * 2;         // bytes per key row
     constexpr int TILEB = DKT * ROWB;    // bytes of one K (or V) tile
@@ -480,14 +482,29 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
 
     l_i += xor16(l_i);  // the row's sum over its four lanes
     l_i += xor32(l_i);
+    // the key range's output row normalised (o / l, bounded by max |V|) and
+    // scaled by a power of two 2^-ex that puts its largest entry in
+    // [2^14, 2^15), stored as 16-bit floats: half the bytes of the split's
+    // partial rows, no overflow past the 16-bit range whatever the size of
+    // V, and the full 11-bit precision for every entry within 2^-28 of the
+    // row's largest. 2^ex travels beside the row.
+    const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < HD / 16; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(o[j][e] * inv));
+    amax = fmaxf(amax, xor16(amax));
+    amax = fmaxf(amax, xor32(amax));
+    // floor(log2 amax) from the exponent field (0 for zero and subnormal rows)
+    const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+    const int ex = ebits == 0 ? 0 : min(max(ebits - 127 - 14, -126), 127);
+    const float sc = inv * __uint_as_float((uint32_t)(127 - ex) << 23 & 0x7f800000u);
     if (rvalid) {
         const int64_t row = ((int64_t)b * N + node) * Hq + h;
-        // the key range's output row normalised (o / l, bounded by max |V|) as
-        // 16-bit floats: half the bytes of the split's partial rows
-        const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
 #pragma unroll
         for (int j = 0; j < HD / 16; ++j) {
-            const f32x4 v = o[j] * inv;
+            const f32x4 v = o[j] * sc;
             const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
                                 ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
             const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
@@ -497,20 +514,22 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
         if (g4 == 0) {
             pm[row * splits + s] = m_i;
             pl[row * splits + s] = l_i;
+            pe[row * splits + s] = ldexpf(1.f, ex);
         }
     }
 }
 
 // out = sum_s 2^{m_s - M} o_s / sum_s 2^{m_s - M} l_s  (M = max_s m_s; the row
 // statistics are kept in the log2 domain). P = float: o_s as accumulated;
-// P = uint16_t: o_s / l_s as 16-bit floats (the matrix-core kernel's rows).
-__device__ __forceinline__ float partial_o(const float* po, int64_t i, float l) { return po[i]; }
-__device__ __forceinline__ float partial_o(const uint16_t* po, int64_t i, float l) {
-    return l * (float)__builtin_bit_cast(_Float16, po[i]);
+// P = uint16_t: o_s / (l_s 2^{e_s}) as 16-bit floats with 2^{e_s} in pe (the
+// matrix-core kernel's rows).
+__device__ __forceinline__ float partial_o(const float* po, int64_t i, float l, float) { return po[i]; }
+__device__ __forceinline__ float partial_o(const uint16_t* po, int64_t i, float l, float sc) {
+    return (l * sc) * (float)__builtin_bit_cast(_Float16, po[i]);
 }
 template <typename T, typename P>
 __global__ void k_attn_combine(int hd, int splits, const P* __restrict__ po, const float* __restrict__ pm,
-                               const float* __restrict__ pl, T* __restrict__ out) {
+                               const float* __restrict__ pl, const float* __restrict__ pe, T* __restrict__ out) {
     const int64_t row = blockIdx.x;
     const int c = threadIdx.x;
     float M = -INFINITY;
@@ -522,7 +541,8 @@ __global__ void k_attn_combine(int hd, int splits, const P* __restrict__ po, con
         const float ms = pm[row * splits + s];
         const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
         const float ls = pl[row * splits + s];
-        num = fmaf(wgt, partial_o(po, (row * splits + s) * hd + c, ls), num);
+        const float sc = pe ? pe[row * splits + s] : 1.f;
+        num = fmaf(wgt, partial_o(po, (row * splits + s) * hd + c, ls, sc), num);
         den = fmaf(wgt, ls, den);
     }
     st(out, row * hd + c, num / den);
@@ -546,6 +566,8 @@ hipError_t launch_typed(const DevTree& t, int B, int Hq, int Hkv, int hd, int Lc
     float* pm = reinterpret_cast<float*>(w);
     w += align256((size_t)R * p.splits * 4);
     float* pl = reinterpret_cast<float*>(w);
+    w += align256((size_t)R * p.splits * 4);
+    float* pe = kHalfRows ? reinterpret_cast<float*>(w) : nullptr;  // the 16-bit rows' power-of-two scales
     const dim3 grid((unsigned)(B * Hkv * p.qtiles * p.splits));
     const T* qq = reinterpret_cast<const T*>(q);
     const T* kk = reinterpret_cast<const T*>(Kc);
@@ -555,10 +577,10 @@ hipError_t launch_typed(const DevTree& t, int B, int Hq, int Hkv, int hd, int Lc
         const dim3 mgrid((unsigned)(8 * p.qtiles * ((ngroups + 7) / 8)));
         if (hd == 64)
             hipLaunchKernelGGL(k_attn_mfma<64>, mgrid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv,
-                               lens, scale, p.splits, p.chunk, p.qtiles, ngroups, po, pm, pl);
+                               lens, scale, p.splits, p.chunk, p.qtiles, ngroups, po, pm, pl, pe);
         else
             hipLaunchKernelGGL(k_attn_mfma<128>, mgrid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv,
-                               lens, scale, p.splits, p.chunk, p.qtiles, ngroups, po, pm, pl);
+                               lens, scale, p.splits, p.chunk, p.qtiles, ngroups, po, pm, pl, pe);
     } else {
         if (hd == 64)
             hipLaunchKernelGGL((k_attn_fma<T, 64>), grid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv,
@@ -569,7 +591,7 @@ hipError_t launch_typed(const DevTree& t, int B, int Hq, int Hkv, int hd, int Lc
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_attn_combine<T, P>), dim3((unsigned)R), dim3(hd), 0, st_, hd, p.splits, po, pm, pl,
+    hipLaunchKernelGGL((k_attn_combine<T, P>), dim3((unsigned)R), dim3(hd), 0, st_, hd, p.splits, po, pm, pl, pe,
                        reinterpret_cast<T*>(out));
     return hipGetLastError();
 }
@@ -617,7 +639,7 @@ AttnPlan attention_plan(int dt, int B, int N, int Hq, int Hkv, int hd, int max_l
 size_t attention_ws_bytes(int dt, int B, int N, int Hq, int Hkv, int hd, int max_len) {
     const AttnPlan p = attention_plan(dt, B, N, Hq, Hkv, hd, max_len);
     const size_t R = (size_t)B * N * Hq;
-    return align256(R * p.splits * hd * (dt == 0 ? 4 : 2)) + 2 * align256(R * p.splits * 4);
+    return align256(R * p.splits * hd * (dt == 0 ? 4 : 2)) + (dt == 0 ? 2 : 3) * align256(R * p.splits * 4);
 }
 
 hipError_t attention_launch(const DevTree& t, int dt, int B, int Hq, int Hkv, int hd, int Lcap, int max_len,
@@ -626,3 +648,4 @@ hipError_t attention_launch(const DevTree& t, int dt, int B, int Hq, int Hkv, in
     if (dt == 0) return launch_typed<float>(t, B, Hq, Hkv, hd, Lcap, max_len, q, Kc, Vc, lens, scale, out, ws, s);
     return launch_typed<uint16_t>(t, B, Hq, Hkv, hd, Lcap, max_len, q, Kc, Vc, lens, scale, out, ws, s);
 }
+

@@ -1034,11 +1034,16 @@ hipError_t launch_direct(int cb, dim3 grid, hipStream_t s, const uint16_t* U, co
 // With h' = hi + lo' (hi = bf16(h'), lo' the exact rest), the logit is
 // l = U.hi + U.lo'. The matrix cores compute only l~ = U.hi; by
 // Cauchy-Schwarz |U_v.lo'| <= |U_v| |lo'|, so with N the largest row norm of
-// U in a vocabulary tile every logit of that tile satisfies
-//     |l~_v - l_v| <= E = N (|lo'| + 2^-14 |h'|)
-// where the second term covers float32 rounding of both the product sums
-// and the exact re-scoring below (<= 2^-15 |U_v| |h'| each for sums of
-// 8,192 terms in blocks of 32). A tile's k-th best l~ minus E is then a
+// U in a vocabulary tile every re-scored logit r_v of that tile satisfies
+//     |l~_v - r_v| <= E = N ((1 + 2^-7) |lo'| + c(d) |h'|)
+// where c(d) (cert_rounding_allowance) covers float32 rounding of both the
+// matrix-core sums and the re-scoring below by the standard bound for
+// recursive summation, |fl(sum) - sum| <= gamma_n sum |x_i y_i| <=
+// gamma_n |U_v| |x| with gamma_n = n u / (1 - n u), u = 2^-24, n the longest
+// chain of roundings a product goes through: d / 32 accumulator steps plus
+// up to 32 inside one MFMA for U.hi, d / 64 lane steps plus 6 butterfly
+// levels for the re-scoring. The 1 + 2^-7 covers lo = bf16(lo') in the
+// re-scoring and the float32 norms. A tile's k-th best l~ minus E is then a
 // lower bound T of the row's k-th best logit; only entries with
 // l~ + E >= T can belong to the top k. Those candidates are re-scored in
 // float32 from U and h' and the top k taken over the re-scored values.
@@ -1319,7 +1324,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
                                                               const uint16_t* __restrict__ hhi, int M, int d, int V,
                                                               int nh, int head0, int vtiles, int mtiles, KW kk, int Mh,
                                                               const float* __restrict__ lo_norm,
-                                                              const float* __restrict__ h_norm,
+                                                              const float* __restrict__ h_norm, float cert_c,
                                                               int* __restrict__ bound, int* __restrict__ slots,
                                                               int* __restrict__ count,
                                                               float* __restrict__ cand_ub, float* __restrict__ cand_lb,
@@ -1438,7 +1443,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
         if (m < M) {
             const float N = sqrtf(fmaxf(fmaxf(s_nrm[0], s_nrm[1]), fmaxf(s_nrm[2], s_nrm[3]))) * (1.f + 0x1p-10f);
             const int row = hh * M + m;
-            s_E[tid] = N * (lo_norm[row] + 0x1p-14f * h_norm[row]);
+            s_E[tid] = N * ((1.f + 0x1p-7f) * lo_norm[row] + cert_c * h_norm[row]);
             s_bound[tid] = o2f(__hip_atomic_load(bound + row, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
         } else {
             s_E[tid] = 0.f;
@@ -1797,6 +1802,18 @@ __global__ __launch_bounds__(BLOCK) void k_operand_order(const uint16_t* __restr
 }
 }  // namespace
 
+// c(d) of the certified pass's bound E (see the comment above kCertCap),
+// rounded up to float.
+float cert_rounding_allowance(int d) {
+    if (d <= 0) return 0.f;
+    const double u = 0x1p-24;
+    auto gamma = [u](double n) { return n * u / (1.0 - n * u); };
+    const double n_mfma = d / 32.0 + 32.0, n_rescore = d / 64.0 + 6.0;
+    const double c = (gamma(n_mfma) * (1.0 + 0x1p-8) + gamma(n_rescore) * (1.0 + 0x1p-16)) * (1.0 + 0x1p-10);
+    const float f = (float)c;
+    return (double)f >= c ? f : nextafterf(f, INFINITY);
+}
+
 size_t operand_order_bytes(int nmat, int rows, int cols) {
     return (size_t)nmat * ((rows + OP_TILE - 1) / OP_TILE) * OP_TILE * cols * 2;
 }
@@ -2005,7 +2022,8 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     } else {  // many rows: one product and the certificate
         const int vmtiles = (rows_v + VM - 1) / VM;
         hipLaunchKernelGGL(k_vocab_mfma_cert, dim3(8 * vmtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s, U, L.hhi,
-                           rows_v, a.d, a.V, nh_u, head0, vtiles, vmtiles, kk, Mh, L.lo_norm, L.h_norm, L.bound,
+                           rows_v, a.d, a.V, nh_u, head0, vtiles, vmtiles, kk, Mh, L.lo_norm, L.h_norm,
+                           cert_rounding_allowance(a.d), L.bound,
                            L.slots, L.count, L.cand_ub, L.cand_lb, L.cand_idx);
         *nlists = 0;
     }

@@ -70,6 +70,8 @@ bool residual_on_gemv(int dt, int kind, int M, int d, int din, bool op);
 hipError_t residual_gemv_split(const HeadsArgs& a, const DevTree* tree, float* hres, uint16_t* hhi, uint16_t* hlo,
                                int* bound, int bound_init, hipStream_t s);
 size_t heads_mfma_ws_bytes(int M, int d, int din, int V, int nh, int kmax, int shared_u);
+// float32 rounding allowance of the certified pass per unit |U_v| |h'| at contraction length d
+float cert_rounding_allowance(int d);
 hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1,
                              float** part_val, int** part_idx, int* nlists);
 hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1);

@@ -203,25 +203,26 @@ def hydra_rows(parent: Sequence[int], level: int):
     return [p for p in range(len(parent)) if dep[p] == level - 1 and any(parent[c] == p for c in range(len(parent)))]
 
 
-def hydra_expand(W, b, U, E, h, topo_parent, topo_rank, topk: Sequence[int], root_tok, lens,
-                 requests: Optional[Sequence[int]] = None, want_logits: bool = False) -> Dict[str, object]:
-    """Hydra heads, level by level (the Hydra summary and abstract).
+def hydra_level(W, b, U, E, h, topo_parent, topo_rank, topk: Sequence[int], level: int, tree_tok,
+                requests: Optional[Sequence[int]] = None, want_logits: bool = False) -> Dict[str, object]:
+    """Hydra's level `level` (the Hydra summary and abstract), given the tree's
+    tokens at depths below it (tree_tok [B, N]; the root at node 0).
 
-    Level i runs head i on one row per (request, parent at depth i - 1 with
-    children): x = [h_b ; E[token of the parent]], hres = h_b + SiLU(W_i x +
-    b_i), then head i's projection and top-k_i. A node at depth i takes entry
-    rank(n) of its own parent's list. Returns the tree tokens, positions and
-    every level's (rows, hres, idx, val, margin).
+    One row per (request, parent at depth level - 1 with children), in node
+    order: x = [h_b ; E[token of the parent]] (a token outside [0, V) embeds as
+    zeros), hres = h_b + SiLU(W_i x + b_i), then head i's projection and
+    top-k_i. Returns the rows, hres, idx, val, margin (and the logits), and the
+    tokens of the depth-`level` nodes: entry rank(n) of the node's own
+    parent's list.
     """
-    K = W.shape[0]
+    i = level
     N = len(topo_parent)
     dep = _depths(topo_parent)
     B = h.shape[0]
     reqs = list(range(B)) if requests is None else list(requests)
     hd = to_double(h)
-    Ed_cache: Dict[int, np.ndarray] = {}
-
     V = E.shape[0]
+    Ed_cache: Dict[int, np.ndarray] = {}
 
     def emb(tok: int) -> np.ndarray:
         # a token outside [0, V) names no row of E: it embeds as zeros
@@ -232,6 +233,33 @@ def hydra_expand(W, b, U, E, h, topo_parent, topo_rank, topk: Sequence[int], roo
                 Ed_cache[tok] = np.zeros(E.shape[1], dtype=np.float64)
         return Ed_cache[tok]
 
+    parents = hydra_rows(topo_parent, i)
+    rows = [(b_, p) for b_ in reqs for p in parents]
+    if not rows:
+        return {"rows": [], "tok": {}}
+    x = np.stack([np.concatenate([hd[b_], emb(int(tree_tok[b_, p]))]) for (b_, p) in rows])
+    base = np.stack([hd[b_] for (b_, _) in rows])
+    hres = residual(W[i - 1], b[i - 1], x, base)
+    idx, val, margin, lg = vocab_topk(U[i - 1], hres, topk[i - 1], want_logits=want_logits)
+    row_of = {rp: r for r, rp in enumerate(rows)}
+    tok = {(b_, n): int(idx[row_of[(b_, topo_parent[n])], topo_rank[n]])
+           for b_ in reqs for n in range(N) if dep[n] == i}
+    return {"rows": rows, "hres": hres, "idx": idx, "val": val, "margin": margin, "logits": lg, "tok": tok}
+
+
+def hydra_expand(W, b, U, E, h, topo_parent, topo_rank, topk: Sequence[int], root_tok, lens,
+                 requests: Optional[Sequence[int]] = None, want_logits: bool = False) -> Dict[str, object]:
+    """Hydra heads, level by level (the Hydra summary and abstract): level i
+    runs head i on one row per (request, parent at depth i - 1 with children)
+    and each depth-i node takes entry rank(n) of its own parent's list
+    (hydra_level). Returns the tree tokens, positions and every level's
+    (rows, hres, idx, val, margin).
+    """
+    K = W.shape[0]
+    N = len(topo_parent)
+    dep = _depths(topo_parent)
+    B = h.shape[0]
+    reqs = list(range(B)) if requests is None else list(requests)
     tok = np.full((B, N), -1, dtype=np.int32)
     pos = np.zeros((B, N), dtype=np.int32)
     for b_ in reqs:
@@ -240,20 +268,13 @@ def hydra_expand(W, b, U, E, h, topo_parent, topo_rank, topk: Sequence[int], roo
             pos[b_, n] = lens[b_] + dep[n]
     levels = []
     for i in range(1, K + 1):
-        parents = hydra_rows(topo_parent, i)
-        if not parents:
+        lvl = hydra_level(W, b, U, E, h, topo_parent, topo_rank, topk, i, tok, requests=reqs,
+                          want_logits=want_logits)
+        if not lvl["rows"]:
             break
-        rows = [(b_, p) for b_ in reqs for p in parents]
-        x = np.stack([np.concatenate([hd[b_], emb(int(tok[b_, p]))]) for (b_, p) in rows])
-        base = np.stack([hd[b_] for (b_, _) in rows])
-        hres = residual(W[i - 1], b[i - 1], x, base)
-        idx, val, margin, lg = vocab_topk(U[i - 1], hres, topk[i - 1], want_logits=want_logits)
-        row_of = {rp: r for r, rp in enumerate(rows)}
-        for b_ in reqs:
-            for n in range(N):
-                if dep[n] == i:
-                    tok[b_, n] = idx[row_of[(b_, topo_parent[n])], topo_rank[n]]
-        levels.append({"rows": rows, "hres": hres, "idx": idx, "val": val, "margin": margin, "logits": lg})
+        for (b_, n), t in lvl.pop("tok").items():
+            tok[b_, n] = t
+        levels.append(lvl)
     return {"tree_tok": tok, "tree_pos": pos, "levels": levels}
 
 

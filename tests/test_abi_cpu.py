@@ -23,7 +23,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 26
+    assert len(names) == 27
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -41,6 +41,44 @@ def test_weight_bytes_match_page():
     assert shared == 2 * (4 * (8192 * 8192 + 8192) + 128256 * 8192)
     assert round((8_942_321_664 - shared) / 2 / 1e9, 2) == 3.15
     assert md.md_heads_weight_bytes(3, 1, 8192, 128256, 4) == -1
+
+
+def _gamma(n):
+    u = 2.0 ** -24
+    return n * u / (1 - n * u)
+
+
+@pytest.mark.parametrize("d", [256, 1024, 8192, 16384, 40960])
+def test_certified_rounding_allowance_covers_float32_sums(d):
+    """The certified pass's float32 allowance per unit |U_v| |h'| grows with the contraction
+    length: at least the recursive-summation bound over the matrix-core chain (d / 32 accumulator
+    steps + 32 inside one instruction) plus the re-scoring chain (d / 64 lane steps + 6 butterfly
+    levels); and, as a check of the bound itself, at least the error of a float32 emulation of
+    the blocked sum on inputs whose products are all positive and of equal size."""
+    import numpy as np
+
+    c = md.md_certified_rounding_allowance(d)
+    assert c >= _gamma(d / 32 + 32) + _gamma(d / 64 + 6)
+    assert c <= 1.2 * (_gamma(d / 32 + 32) + _gamma(d / 64 + 6))
+    rng = np.random.default_rng(d)
+    x = np.abs(rng.standard_normal(d)).astype(np.float32)  # |U_v| |h'| = sum x_i^2 with U_v = h'
+    prod = x.astype(np.float64) ** 2
+    exact = prod.sum()
+    acc = np.float32(0)
+    for blk in prod.reshape(-1, 32):  # each 32-term block rounded once, then a float32 chain
+        acc = np.float32(acc + np.float32(blk.sum()))
+    lanes = prod.reshape(-1, 64).sum(axis=0).astype(np.float32)  # the re-scoring's per-lane sums, then a tree
+    while lanes.size > 1:
+        lanes = (lanes[: lanes.size // 2] + lanes[lanes.size // 2:]).astype(np.float32)
+    err = abs(float(acc) - exact) + abs(float(lanes[0]) - exact)
+    assert err <= c * exact
+    # 70B-shaped heads (d = 8,192): tighter than the 2^-14 the pass used when it was argued for
+    # that width only; from d = 40,960 on that constant would no longer cover the sums
+    if d == 8192:
+        assert c < 2.0 ** -14
+    if d == 40960:
+        assert c > 2.0 ** -14
+    assert md.md_certified_rounding_allowance(0) == -1.0
 
 
 def _tree(parent, rank, n=None):

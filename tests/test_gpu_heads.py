@@ -248,9 +248,12 @@ def test_heads_medusa_mfma_rows(wl, M):
     assert np.array_equal(gi, gi2) and np.array_equal(gv.view(np.uint32), gv2.view(np.uint32))
 
 
-@pytest.mark.parametrize("wl_name,M,rows", [("8b", 64, [0, 31, 63]), ("70b", 512, [0, 300, 511])])
+@pytest.mark.parametrize("wl_name,M,rows", [("8b", 64, [0, 31, 63]),
+                                             ("70b", 512, list(range(192, 256)) + [0, 130, 300, 511])])
 def test_heads_medusa_mfma_full_size_sampled(wl_name, M, rows):
-    """The 70B-shaped heads over all 512 tree nodes of a batch of 8 (the oracle checks sampled rows)."""
+    """The 70B-shaped heads over all 512 tree nodes of a batch of 8 on the certified pass: every row
+    of one request (the 64 nodes of request 3) and one row in each 128-row tile checked against the
+    oracle (lists, values and h')."""
     wl = LLAMA8B if wl_name == "8b" else LLAMA70B
     w = weights(wl, 8 if wl_name == "8b" else 70)
     h = synth.normal(91, 79, (M, wl.d), 1.0, wl.dtype)
@@ -259,6 +262,27 @@ def test_heads_medusa_mfma_full_size_sampled(wl_name, M, rows):
     ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, rows=rows, want_logits=True)
     ref["hres"] = ref["hres"]
     compare_medusa(wl, gi[rows], gv[rows], gh[:, rows], ref, label="%s M=%d rows %s" % (wl.name, M, rows))
+    del wd
+
+
+def test_heads_certified_pass_wide_contraction():
+    """512 rows x 2 heads at d = 16,384, twice the 70B width, on the certified single-product pass:
+    its rounding allowance grows with the contraction length, so the lists stay those of the
+    float32 re-scored logits (rows of every 128-row tile checked against the oracle)."""
+    md = _md()
+    wl = Workload("certified d=16384 V=3001 K=2", "medusa", B=1, d=16384, V=3001, K=2, dtype="bf16",
+                  topk=(10, 4), N=10, Hq=4, Hkv=1, hd=64, L=10)
+    M = 512
+    rows = [0, 1, 64, 127, 128, 200, 255, 256, 300, 383, 384, 450, 511]
+    assert md.md_certified_rounding_allowance(wl.d) > md.md_certified_rounding_allowance(8192)
+    w = weights(wl, 4400)
+    h = synth.normal(4400, 86, (M, wl.d), 1.0, wl.dtype)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), M)
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, rows=rows, want_logits=True)
+    compare_medusa(wl, gi[rows], gv[rows], gh[:, rows], ref, label="certified d=16384 M=%d" % M)
+    gi2, gv2, _ = gpu_heads_medusa(wl, wd, to_dev(h), M)
+    assert np.array_equal(gi, gi2) and np.array_equal(gv.view(np.uint32), gv2.view(np.uint32))
     del wd
 
 
