@@ -206,6 +206,22 @@ int md_tree_attention(const md_tree* tree, int dt, int B, int Hq, int Hkv, int h
                       const void* q, const void* Kc, const void* Vc, const int32_t* lens, float scale, void* out,
                       void* ws, size_t ws_bytes, void* stream);
 
+/* md_tree_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same inputs, outputs, checks and errors, no workspace
+ * argument. The key ranges' partial rows live in one static scratch array
+ * per GPU inside the library (md_tree_attention_noalloc_max_bytes() bytes,
+ * 32 MiB, held from the library's first use on that GPU until the process
+ * ends); the call allocates and frees nothing. Sizes whose workspace
+ * (md_attention_workspace_bytes) exceeds it return MD_EWORKSPACE. Every
+ * call on one GPU uses the same array: calls that overlap on one GPU (other
+ * streams, other threads) race, so serialise them. The first call on a GPU
+ * looks up the array's device address there (MD_EHIP if that fails). */
+int md_tree_attention_noalloc(const md_tree* tree, int dt, int B, int Hq, int Hkv, int hd, int Lcap, int max_len,
+                              const void* q, const void* Kc, const void* Vc, const int32_t* lens, float scale,
+                              void* out, void* stream);
+size_t md_tree_attention_noalloc_max_bytes(void);
+
 /* Workspace for md_tree_accept. */
 size_t md_accept_workspace_bytes(int B, int N, int V);
 

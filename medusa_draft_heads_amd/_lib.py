@@ -27,6 +27,7 @@ EXPORTS = (
     "md_heads_logits_workspace_bytes", "md_medusa_heads_logits", "md_draft_sample_workspace_bytes", "md_draft_sample",
     "md_verify_sampled_workspace_bytes", "md_tree_verify_sampled", "md_accept_typical_workspace_bytes",
     "md_tree_accept_typical", "md_operand_order_bytes", "md_operand_order", "md_certified_rounding_allowance",
+    "md_tree_attention_noalloc", "md_tree_attention_noalloc_max_bytes",
 )
 
 
@@ -69,6 +70,8 @@ def lib() -> ctypes.CDLL:
             "md_tree_build": ([tp, i, i, i, i, i, i] + [vp] * 6 + [vp], i),
             "md_attention_workspace_bytes": ([i, i, i, i, i, i, i], sz),
             "md_tree_attention": ([tp, i, i, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, sz, vp], i),
+            "md_tree_attention_noalloc": ([tp, i, i, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp], i),
+            "md_tree_attention_noalloc_max_bytes": ([], sz),
             "md_accept_workspace_bytes": ([i, i, i], sz),
             "md_tree_accept": ([tp, i, i, i, i, i, i, i] + [vp] * 10 + [sz, vp], i),
             "md_set_vocab_timing_events": ([vp, vp], i),
@@ -184,6 +187,17 @@ def md_tree_attention(tree, dt, B, Hq, Hkv, hd, Lcap, max_len, q, Kc, Vc, lens, 
     rc = lib().md_tree_attention(ctypes.byref(tree), dt, B, Hq, Hkv, hd, Lcap, max_len, _p(q), _p(Kc), _p(Vc),
                                  _p(lens), float(scale), _p(out), _p(ws), ws_bytes, _stream(stream))
     _check(rc)
+
+
+def md_tree_attention_noalloc(tree, dt, B, Hq, Hkv, hd, Lcap, max_len, q, Kc, Vc, lens, scale, out,
+                              stream=None) -> None:
+    rc = lib().md_tree_attention_noalloc(ctypes.byref(tree), dt, B, Hq, Hkv, hd, Lcap, max_len, _p(q), _p(Kc), _p(Vc),
+                                         _p(lens), float(scale), _p(out), _stream(stream))
+    _check(rc)
+
+
+def md_tree_attention_noalloc_max_bytes() -> int:
+    return int(lib().md_tree_attention_noalloc_max_bytes())
 
 
 def md_tree_accept(tree, dt, B, K, V, Hkv, hd, Lcap, logits, tree_tok, Kc, Vc, lens, accept_len, path, next_tok,

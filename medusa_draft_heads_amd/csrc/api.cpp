@@ -1,8 +1,10 @@
 // libmedusa C-ABI: argument checks, tree expansion and kernel dispatch.
 //
 // Every check below runs on the host before any HIP call, so a rejected call
-// enqueues nothing. The library holds no device memory and no state besides a
-// thread-local error string and the optional thread-local timing events.
+// enqueues nothing. The library holds no device memory besides one static
+// scratch array per GPU (md_tree_attention_noalloc), and no state besides
+// that array's per-device address, a thread-local error string and the
+// optional thread-local timing events.
 #include <hip/hip_runtime.h>
 
 #include <cstdarg>
@@ -256,6 +258,34 @@ int md_tree_attention(const md_tree* tree, int dt, int B, int Hq, int Hkv, int h
                                        (hipStream_t)stream),
                       "md_tree_attention");
 }
+
+int md_tree_attention_noalloc(const md_tree* tree, int dt, int B, int Hq, int Hkv, int hd, int Lcap, int max_len,
+                              const void* q, const void* Kc, const void* Vc, const int32_t* lens, float scale,
+                              void* out, void* stream) {
+    DevTree t;
+    int rc = expand_tree(tree, MD_MAX_HEADS, nullptr, &t);
+    if (rc) return rc;
+    if (check_dt(dt)) return MD_EINVAL;
+    if (B < 0 || Hq < 1 || Hkv < 1) return fail(MD_EINVAL, "B = %d, Hq = %d, Hkv = %d", B, Hq, Hkv);
+    if (Hq % Hkv) return fail(MD_EINVAL, "Hq = %d is not a multiple of Hkv = %d", Hq, Hkv);
+    if (hd != 64 && hd != 128) return fail(MD_EUNSUPPORTED, "head_dim %d (64 or 128 supported)", hd);
+    if (max_len < 0) return fail(MD_EINVAL, "max_len = %d", max_len);
+    if ((int64_t)max_len + t.n > Lcap) return fail(MD_ERANGE, "max_len %d + %d nodes exceeds Lcap %d", max_len, t.n, Lcap);
+    if (B == 0) return MD_OK;
+    if (!q || !Kc || !Vc || !lens || !out) return fail(MD_EINVAL, "a required pointer is NULL");
+    const size_t need = attention_ws_bytes(dt, B, t.n, Hq, Hkv, hd, max_len);
+    if (need > kAttnScratchBytes)
+        return fail(MD_EWORKSPACE, "these sizes need %zu bytes of scratch; the library's static scratch holds %zu",
+                    need, kAttnScratchBytes);
+    void* ws = nullptr;
+    rc = hip_status(attention_scratch(&ws), "md_tree_attention_noalloc (scratch address)");
+    if (rc) return rc;
+    return hip_status(attention_launch(t, dt, B, Hq, Hkv, hd, Lcap, max_len, q, Kc, Vc, lens, scale, out, ws,
+                                       (hipStream_t)stream),
+                      "md_tree_attention_noalloc");
+}
+
+size_t md_tree_attention_noalloc_max_bytes(void) { return kAttnScratchBytes; }
 
 size_t md_accept_workspace_bytes(int B, int N, int V) {
     if (B <= 0 || N <= 0 || V <= 0) return 0;

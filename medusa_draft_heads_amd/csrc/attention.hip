@@ -29,6 +29,7 @@
 // hand. float32 storage (small workloads) uses an LDS-tiled FMA kernel.
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "md_internal.h"
@@ -649,3 +650,37 @@ hipError_t attention_launch(const DevTree& t, int dt, int B, int Hq, int Hkv, in
     return launch_typed<uint16_t>(t, B, Hq, Hkv, hd, Lcap, max_len, q, Kc, Vc, lens, scale, out, ws, s);
 }
 
+// ---- the library's own attention scratch (for callers that cannot allocate)
+//
+// One fixed array per GPU, in the code object's device memory: the partial
+// rows and statistics of md_tree_attention_noalloc. In host code the name
+// `scratch` is only a host-side stand-in for the symbol; kernels get the
+// device address that hipGetSymbolAddress gives for the current device, kept
+// per device after the first call there. Nothing in it needs clearing: every
+// launch writes each partial row and statistic it later reads. Calls that
+// overlap on one GPU share the array and race.
+namespace {
+static __device__ __align__(256) unsigned char scratch[kAttnScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t attention_scratch(void** ptr) {
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
+}

@@ -110,6 +110,9 @@ size_t attention_ws_bytes(int dt, int B, int N, int Hq, int Hkv, int hd, int max
 hipError_t attention_launch(const DevTree& t, int dt, int B, int Hq, int Hkv, int hd, int Lcap, int max_len,
                             const void* q, const void* Kc, const void* Vc, const int32_t* lens, float scale,
                             void* out, void* ws, hipStream_t s);
+// the library's static attention scratch of the current device (md_tree_attention_noalloc)
+constexpr size_t kAttnScratchBytes = (size_t)32 << 20;
+hipError_t attention_scratch(void** ptr);
 
 // ---- accept (accept.hip) ----
 size_t accept_ws_bytes(int B, int N, int V);

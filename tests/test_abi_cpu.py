@@ -23,7 +23,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 27
+    assert len(names) == 29
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -164,6 +164,24 @@ def test_attention_and_accept_argument_errors():
     assert att(ws_bytes=need - 1) == L.MD_EWORKSPACE
     assert att(q=None) == L.MD_EINVAL
     assert att(B=0) == L.MD_OK
+
+    # the no-allocation variant: the same checks, and sizes whose workspace exceeds the library's
+    # static scratch are refused before any HIP call
+    cap = md.md_tree_attention_noalloc_max_bytes()
+    assert cap == 32 << 20
+
+    def att_na(dt=1, B=1, Hq=4, Hkv=2, hd=128, Lcap=200, max_len=100, q=P):
+        return lib.md_tree_attention_noalloc(t, dt, B, Hq, Hkv, hd, Lcap, max_len, q, P, P, P, 0.1, P, None)
+
+    assert att_na(hd=96) == L.MD_EUNSUPPORTED
+    assert att_na(Hq=5) == L.MD_EINVAL
+    assert att_na(Lcap=110) == L.MD_ERANGE
+    assert att_na(max_len=-1) == L.MD_EINVAL
+    assert att_na(q=None) == L.MD_EINVAL
+    assert att_na(B=0) == L.MD_OK
+    assert md.md_attention_workspace_bytes(1, 200, 16, 64, 2, 128, 100) > cap
+    assert att_na(B=200, Hq=64) == L.MD_EWORKSPACE
+    assert b"static scratch" in lib.md_last_error()
 
     wsa = md.md_accept_workspace_bytes(1, 16, 4096)
 
