@@ -38,7 +38,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 PEAK_BF16_TFLOPS = 2500.0
-PMC_FILE = os.path.join(ROOT, "profiles", "vocab_topk_70b_pmc.json")
+PMC_FILE = os.path.join(ROOT, "profiles", "heads_fused_70b_pmc.json")
 
 
 def log(msg: str) -> None:
@@ -355,6 +355,12 @@ def main() -> int:
         vocab_bytes += sum(head_rows) * wl.V * 4
     vocab_flops = 2.0 * wl.V * wl.d * sum(head_rows)  # algorithmic multiply-adds of the projections
     kernel = "vocabulary projection + per-head top-k"
+    # one bf16 row through per-head projections: residual blocks, projections, top-k and merge in
+    # one launch, which then reads W and b as well (and h, not h')
+    fused = (not hydra and wl.verify != "sampled"
+             and md.md_heads_fused(kind, 1 if wl.dtype == "bf16" else 0, wl.M, wl.d, wl.K))
+    if fused:
+        vocab_bytes = md.md_heads_weight_bytes(kind, 1, wl.d, wl.V, wl.K) + wl.M * wl.d * 2
     mfma_rows = min(head_rows) >= 8 and wl.dtype == "bf16"
     if mfma_rows:
         achieved = vocab_flops / (vocab_ms * 1e-3) / 1e12
@@ -376,6 +382,8 @@ def main() -> int:
         roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": traffic,
                     "kernel": ("vocabulary kernels of the 4 levels" if hydra else
+                               "k_heads_fused (residual blocks + vocabulary projections + per-head top-k + their "
+                               "merge, one launch)" if fused else
                                "k_vocab_topk<..., LOGITS> (vocabulary projection writing every logit)"
                                if wl.verify == "sampled" else
                                "k_vocab_topk (%s%s)" % (kernel, "; one U for the %d heads" % wl.K if wl.shared_u

@@ -97,6 +97,13 @@ int64_t md_heads_weight_bytes(int kind, int dt, int d, int V, int K);
  * most 64 * B), with or without an operand-order copy of U. */
 size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, int kmax);
 
+/* 1 when md_medusa_heads runs these sizes as a single launch (one bf16 row
+ * through per-head projections, kind MD_HEADS_MEDUSA): the residual blocks,
+ * the vocabulary projections, the per-head top-k and their merge in one
+ * kernel, so W streams in the same kernel as U and no merge kernel follows;
+ * else 0. Host only. */
+int md_heads_fused(int kind, int dt, int M, int d, int K);
+
 /* Many bf16 rows (more than 128 through the projection) take a certified
  * single-product pass: the matrix cores form U.hi only, every logit is
  * known to within E = N ((1 + 2^-7) |h' - hi| + c(d) |h'|) of it (N the

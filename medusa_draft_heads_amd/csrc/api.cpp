@@ -116,6 +116,11 @@ int64_t md_heads_weight_bytes(int kind, int dt, int d, int V, int K) {
     return params * (dt == MD_F32 ? 4 : 2);
 }
 
+int md_heads_fused(int kind, int dt, int M, int d, int K) {
+    if (!known_kind(kind) || K < 1 || K > MD_MAX_HEADS) return 0;
+    return kind == MD_HEADS_MEDUSA && heads_fused_applicable(dt, M, d, d, 0, K) ? 1 : 0;
+}
+
 float md_certified_rounding_allowance(int d) { return d > 0 ? cert_rounding_allowance(d) : -1.f; }
 
 size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, int kmax) {

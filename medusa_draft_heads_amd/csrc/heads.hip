@@ -24,6 +24,10 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
+#include <chrono>
+#include <mutex>
+#include <random>
 
 #include "md_internal.h"
 #include "md_wave.h"
@@ -396,27 +400,36 @@ __global__ __launch_bounds__(NW * MD_WAVE) void k_vocab_topk(const T* __restrict
     }
 }
 
-// One block per (row m, head slot hh). Every block of the vocabulary kernel
-// left one sorted list of its k best; the k best of the head are a k-way
-// merge of those lists: each wave takes k rounds of a wave-wide argmax over
-// its lanes' list heads, each round popping the winning list, and one wave
-// merges the waves' sorted lists the same way (no block barrier per round).
-// Vocabulary indices are unique, so the order (value desc, index asc) is
-// strict and the winner is unique.
-// LPT lists per thread; LPT = 0 takes any number of lists: each thread first
-// folds lists tid, tid + BLOCK, ... into one sorted list of its k best.
-template <int LPT>
-__global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ part_val,
-                                                      const int* __restrict__ part_idx, int M, int nh, int nlists,
-                                                      KK kk, int kmax, int32_t* __restrict__ topk_idx,
-                                                      float* __restrict__ topk_val) {
+// The k-way merge of nlists sorted lists of k (value, index) pairs at
+// pv/pi + base + list * kmax into out_idx/out_val (kmax entries, -1 / -inf
+// padded past k), by one block of BLOCK threads. Every list is sorted by
+// (value desc, index asc); each wave takes k rounds of a wave-wide argmax
+// over its lanes' list heads, each round popping the winning list, and one
+// wave merges the waves' sorted lists the same way (no block barrier per
+// round). Vocabulary indices are unique, so the order is strict and the
+// winner unique. LPT lists per thread; LPT = 0 takes any number of lists:
+// each thread first folds lists tid, tid + BLOCK, ... into one sorted list of
+// its k best. COH: the lists are read with agent-coherent loads (written by
+// other blocks of the same launch).
+template <bool COH>
+__device__ __forceinline__ float lval(const float* p, int64_t i) {
+    if constexpr (COH) return __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return p[i];
+}
+template <bool COH>
+__device__ __forceinline__ int lidx(const int* p, int64_t i) {
+    if constexpr (COH) return __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return p[i];
+}
+
+template <int LPT, bool COH>
+__device__ __forceinline__ void merge_lists(const float* __restrict__ part_val, const int* __restrict__ part_idx,
+                                            int64_t base, int nlists, int k, int kmax, int32_t* __restrict__ out_idx,
+                                            float* __restrict__ out_val) {
     constexpr int KM = MD_MAX_TOPK_DEV;
     __shared__ float wl_v[NWAVE][KM];
     __shared__ int wl_i[NWAVE][KM];
-    const int m = blockIdx.x / nh, hh = blockIdx.x - (blockIdx.x / nh) * nh;
-    const int k = kk.v[hh];
     const int tid = threadIdx.x, lane = tid & (MD_WAVE - 1), w = tid >> 6;
-    const int64_t base = ((int64_t)hh * M + m) * nlists * kmax;
     constexpr int NL = LPT > 0 ? LPT : 1;
     float v[NL][KM];
     int ix[NL][KM];
@@ -427,8 +440,8 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
 #pragma unroll
             for (int j = 0; j < KM; ++j) {
                 const bool ok = list < nlists && j < k;
-                v[l][j] = ok ? part_val[base + (int64_t)list * kmax + j] : -INFINITY;
-                ix[l][j] = ok ? part_idx[base + (int64_t)list * kmax + j] : INT_MAX;
+                v[l][j] = ok ? lval<COH>(part_val, base + (int64_t)list * kmax + j) : -INFINITY;
+                ix[l][j] = ok ? lidx<COH>(part_idx, base + (int64_t)list * kmax + j) : INT_MAX;
             }
         }
     } else {
@@ -439,8 +452,8 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
         }
         for (int list = tid; list < nlists; list += BLOCK) {
             for (int j = 0; j < k; ++j) {
-                const float cv = part_val[base + (int64_t)list * kmax + j];
-                const int ci = part_idx[base + (int64_t)list * kmax + j];
+                const float cv = lval<COH>(part_val, base + (int64_t)list * kmax + j);
+                const int ci = lidx<COH>(part_idx, base + (int64_t)list * kmax + j);
                 // a sorted list: once an entry misses this thread's KM best, so do the rest
                 if (!ranks_above(cv, ci, v[0][KM - 1], ix[0][KM - 1])) break;
 #pragma unroll
@@ -512,10 +525,227 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
     }
     if (lane < kmax) {
         const bool ok = lane < k && oi != INT_MAX;
-        const int64_t o = ((int64_t)m * nh + hh) * kmax + lane;
-        topk_idx[o] = ok ? oi : -1;
-        topk_val[o] = ok ? ov : -INFINITY;
+        out_idx[lane] = ok ? oi : -1;
+        out_val[lane] = ok ? ov : -INFINITY;
     }
+}
+
+// One block per (row m, head slot hh): the k best of the head are the k-way
+// merge of the sorted lists every block of the vocabulary kernel left.
+template <int LPT>
+__global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ part_val,
+                                                      const int* __restrict__ part_idx, int M, int nh, int nlists,
+                                                      KK kk, int kmax, int32_t* __restrict__ topk_idx,
+                                                      float* __restrict__ topk_val) {
+    const int m = blockIdx.x / nh, hh = blockIdx.x - (blockIdx.x / nh) * nh;
+    const int64_t base = ((int64_t)hh * M + m) * nlists * kmax;
+    const int64_t o = ((int64_t)m * nh + hh) * kmax;
+    merge_lists<LPT, false>(part_val, part_idx, base, nlists, kk.v[hh], kmax, topk_idx + o, topk_val + o);
+}
+
+// ---- one launch for the heads of one row (Medusa, bf16) ----
+//
+// The residual blocks, the vocabulary projections, the per-head top-k and
+// their k-way merge in a single launch, so the 537 MB of W (70B shape) stream
+// in the same kernel as the 8.4 GB of U instead of a short kernel of their
+// own, and the merge needs no launch. Block group j (wg blocks) first
+// computes h'_j: its waves split the d rows of W[j] as the residual kernel's
+// waves split them (same sums, bit for bit). Once every block of the group
+// has stored its share, each block loads h'_j and streams its share of U[j]
+// exactly as k_vocab_topk does, and the group's first block merges the
+// group's lists.
+//
+// Blocks of a group meet through per-block flag words that receive a token
+// unique to the launch. A block writes its share of h' (or its list) with
+// agent-coherent stores (sc1), waits for them to complete (s_waitcnt
+// vmcnt(0)), and only then stores its flag; a reader that has seen every flag
+// of its group equal to the token loads the data with agent-coherent loads.
+// So no cache write-back or invalidate is needed (a release or acquire at
+// agent scope would write back or invalidate the L2 of every XCD that
+// executes it). Flags are never cleared: a stale or uninitialised word cannot
+// hold this launch's token. Every wait is bounded: a block that gives up on
+// its group's h' computes all of h'_j itself (reading W[j] alone: slow, the
+// same result); a group leader that gives up on the lists writes -1 indices.
+constexpr int kSpinRes = 1 << 16;    // ~30 ms of polling before computing h' alone
+constexpr int kSpinLists = 1 << 19;  // ~250 ms of polling before giving up the merge
+
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Every flag of a group holds the token (block-wide; bounded polling).
+__device__ __forceinline__ bool group_flags(const uint64_t* __restrict__ flags, int n, uint64_t token, int limit) {
+    for (int it = 0; it < limit; ++it) {
+        int mine = 1;
+        for (int b = threadIdx.x; b < n; b += BLOCK)
+            mine &= __hip_atomic_load(flags + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == token;
+        if (__syncthreads_and(mine)) return true;
+        __builtin_amdgcn_s_sleep(8);
+    }
+    return false;
+}
+
+__global__ __launch_bounds__(BLOCK) void k_heads_fused(const uint16_t* __restrict__ W,
+                                                       const uint16_t* __restrict__ bias,
+                                                       const uint16_t* __restrict__ h, const uint16_t* __restrict__ U,
+                                                       int d, int V, int nh, int wg, KK kk, int kmax, uint64_t token,
+                                                       float* __restrict__ hres, float* __restrict__ hres_out,
+                                                       float* __restrict__ part_val, int* __restrict__ part_idx,
+                                                       uint64_t* __restrict__ flags_res,
+                                                       uint64_t* __restrict__ flags_list,
+                                                       int32_t* __restrict__ topk_idx, float* __restrict__ topk_val) {
+    extern __shared__ __align__(16) float xs[];  // [d]: h, then h'_j, then the wave lists
+    const int hh = blockIdx.x / wg, wgi = blockIdx.x - (blockIdx.x / wg) * wg;
+    if (hh >= nh) return;
+    const int tid = threadIdx.x, lane = tid & (MD_WAVE - 1), wv = tid >> 6;
+    for (int i = tid; i < d / 8; i += BLOCK) {
+        float v[8];
+        load8(h + 8 * i, v);
+        *reinterpret_cast<f32x4*>(xs + 8 * i) = f32x4{v[0], v[1], v[2], v[3]};
+        *reinterpret_cast<f32x4*>(xs + 8 * i + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    }
+    __syncthreads();
+
+    // this block's share of h'_hh
+    float* hres_h = hres + (int64_t)hh * d;
+    {
+        const int gw = wgi * NWAVE + wv, tw = wg * NWAVE;
+        const int r0 = (int)((int64_t)d * gw / tw), r1 = (int)((int64_t)d * (gw + 1) / tw);
+        const uint16_t* Wh = W + (int64_t)hh * d * d;
+        // lane j keeps the sum of row r0 + j; the epilogue and its stores come
+        // after the last row, so no store's completion holds up the next
+        // rows' loads (loads and stores share one counter)
+        float mine = 0.f;
+        for (int r = r0; r < r1; r += RPW) {
+            const int nv = min(RPW, r1 - r);
+            float acc[RPW][1];
+            rows_dot<uint16_t, 1>(Wh, d, r, nv, xs, d, lane, acc);
+#pragma unroll
+            for (int rr = 0; rr < RPW; ++rr) {
+                const float sum = wave_sum(acc[rr][0]);
+                if (rr < nv && lane == ((r - r0 + rr) & (MD_WAVE - 1))) mine = sum;
+            }
+        }
+        // a wave's share is at most 64 rows (the host takes this path only then)
+        if (r0 + lane < r1) {
+            const int ri = r0 + lane;
+            const float z = mine + (bias ? ldf(bias, (int64_t)hh * d + ri) : 0.f);
+            const float hv = xs[ri] + z / (1.f + expf(-z));
+            __hip_atomic_store(hres_h + ri, hv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (hres_out) hres_out[(int64_t)hh * d + ri] = hv;
+        }
+    }
+    wait_vm();
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(flags_res + blockIdx.x, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+    // h'_hh once the whole group has stored it (h in LDS is no longer read)
+    if (group_flags(flags_res + (int64_t)hh * wg, wg, token, kSpinRes)) {
+        for (int i = tid; i < d / 2; i += BLOCK) {
+            const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(hres_h) + i, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+            xs[2 * i] = __uint_as_float((uint32_t)v);
+            xs[2 * i + 1] = __uint_as_float((uint32_t)(v >> 32));
+        }
+    } else {
+        // the group did not finish in time: every row of h'_hh from W and h in
+        // memory, in the same order of sums
+        const uint16_t* Wh = W + (int64_t)hh * d * d;
+        for (int ri = wv; ri < d; ri += NWAVE) {
+            const uint16_t* wr = Wh + (int64_t)ri * d;
+            float acc = 0.f;
+            for (int c = lane * 8; c < d; c += MD_WAVE * 8) {
+                float wv8[8], hv8[8];
+                load8(wr + c, wv8);
+                load8(h + c, hv8);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc = fmaf(wv8[e], hv8[e], acc);
+            }
+            const float sum = wave_sum(acc);
+            if (lane == 0) {
+                const float z = sum + (bias ? ldf(bias, (int64_t)hh * d + ri) : 0.f);
+                xs[ri] = ldf(h, ri) + z / (1.f + expf(-z));
+            }
+        }
+    }
+    __syncthreads();
+
+    // this block's share of the vocabulary rows, as k_vocab_topk<bf16, 1, 4>
+    const int k = kk.v[hh];
+    float lv = -INFINITY, tv = -INFINITY;
+    int li = INT_MAX, ti = INT_MAX;
+    auto take = [&](int r, int nv, const float (&acc)[RPW][1]) {
+#pragma unroll
+        for (int rr = 0; rr < RPW; ++rr) {
+            const float sum = wave_sum(acc[rr][0]);
+            if (rr < nv && ranks_above(sum, r + rr, tv, ti)) {
+                list_insert(lv, li, sum, r + rr, k, lane);
+                tv = __shfl(lv, k - 1, MD_WAVE);
+                ti = __shfl(li, k - 1, MD_WAVE);
+            }
+        }
+    };
+    const int wih = wgi * NWAVE + wv, wph = wg * NWAVE;
+    const int v0 = (int)((int64_t)V * wih / wph), v1 = (int)((int64_t)V * (wih + 1) / wph);
+    const uint16_t* Uh = U + (int64_t)hh * V * d;
+    for (int r = v0; r < v1; r += RPW) {
+        const int nv = min(RPW, v1 - r);
+        float acc[RPW][1];
+        rows_dot<uint16_t, 1>(Uh, d, r, nv, xs, d, lane, acc);
+        take(r, nv, acc);
+    }
+    // the block's list: wave 0 merges the wave lists in LDS (over h', now dead)
+    __syncthreads();
+    float* sv = xs;                                           // [NWAVE][64]
+    int* si = reinterpret_cast<int*>(xs + NWAVE * MD_WAVE);  // [NWAVE][64]
+    sv[wv * MD_WAVE + lane] = lane < k ? lv : -INFINITY;
+    si[wv * MD_WAVE + lane] = lane < k ? li : INT_MAX;
+    __syncthreads();
+    if (wv == 0) {
+        float bv = -INFINITY, btv = -INFINITY;
+        int bi = INT_MAX, bti = INT_MAX;
+        for (int w2 = 0; w2 < NWAVE; ++w2) {
+            const float cv = sv[w2 * MD_WAVE + lane];
+            const int ci = si[w2 * MD_WAVE + lane];
+            uint64_t bm = __ballot(lane < k && ranks_above(cv, ci, btv, bti));
+            while (bm) {
+                const int src = __ffsll((long long)bm) - 1;
+                bm &= bm - 1;
+                const float x = __shfl(cv, src, MD_WAVE);
+                const int xi = __shfl(ci, src, MD_WAVE);
+                if (ranks_above(x, xi, btv, bti)) {
+                    list_insert(bv, bi, x, xi, k, lane);
+                    btv = __shfl(bv, k - 1, MD_WAVE);
+                    bti = __shfl(bi, k - 1, MD_WAVE);
+                }
+            }
+        }
+        if (lane < kmax) {
+            const int64_t o = ((int64_t)hh * wg + wgi) * kmax + lane;
+            __hip_atomic_store(part_val + o, bv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(part_idx + o, bi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        wait_vm();
+    }
+    __syncthreads();
+    if (tid == 0) __hip_atomic_store(flags_list + blockIdx.x, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (wgi != 0) return;
+
+    // the group's first block merges the group's wg lists into head hh's top-k
+    int32_t* oi = topk_idx + (int64_t)hh * kmax;
+    float* ov = topk_val + (int64_t)hh * kmax;
+    if (!group_flags(flags_list + (int64_t)hh * wg, wg, token, kSpinLists)) {
+        if (tid < kmax) {
+            oi[tid] = -1;
+            ov[tid] = -INFINITY;
+        }
+        return;
+    }
+    const int64_t base = (int64_t)hh * wg * kmax;
+    if (wg <= BLOCK)
+        merge_lists<1, true>(part_val, part_idx, base, wg, k, kmax, oi, ov);
+    else if (wg <= 2 * BLOCK)
+        merge_lists<2, true>(part_val, part_idx, base, wg, k, kmax, oi, ov);
+    else
+        merge_lists<0, true>(part_val, part_idx, base, wg, k, kmax, oi, ov);
 }
 
 struct Plan {
@@ -752,7 +982,10 @@ hipError_t residual_gemv_split(const HeadsArgs& a, const DevTree* tree, float* h
     return hipGetLastError();
 }
 
+size_t heads_fused_ws_bytes(int d, int nh, int kmax);
+
 size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u, bool op) {
+    if (heads_fused_applicable(dt, M, d, din, shared_u, nh)) return heads_fused_ws_bytes(d, nh, kmax);
     if (heads_mfma_applicable(dt, M, d, din, op, shared_u ? nh * M : M))
         return heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u);
     const Plan p = make_plan(dt, M, d, din, nh, shared_u);
@@ -774,7 +1007,9 @@ size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax, in
         heads_mfma_applicable(dt, M, d, din, true, shared_u ? nh * M : M) ? heads_mfma_ws_bytes(M, d, din, V, nh, kmax, shared_u)
                                                                           : 0;
     const size_t lists_max = (size_t)device_cus() * 4;  // blocks per head at most
-    const size_t gemv = align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * lists_max * kmax * 4);
+    size_t gemv = align256((size_t)nh * M * d * 4) + 2 * align256((size_t)nh * M * lists_max * kmax * 4);
+    // the fused one-row launch adds two flag words per block
+    if (heads_fused_applicable(dt, M, d, din, shared_u, nh)) gemv += 2 * align256((size_t)nh * lists_max * 8);
     return gemv > mfma ? gemv : mfma;
 }
 
@@ -858,7 +1093,98 @@ hipError_t target_argmax_launch(int dt, int R, int d, int V, const void* H, cons
     return target_argmax_gemv<uint16_t>(dt, R, d, V, H, Wt, tok, val, ws, s);
 }
 
+namespace {
+
+// A token per fused launch: never 0 (fresh memory), distinct across launches
+// of the process, and random-started so that a workspace last used by
+// another process cannot hold the same value.
+std::atomic<uint64_t> g_fused_token{0};
+std::once_flag g_fused_token_once;
+
+uint64_t next_fused_token() {
+    std::call_once(g_fused_token_once, [] {
+        std::random_device rd;
+        const uint64_t seed = ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        g_fused_token.store(seed | 1ull);
+    });
+    uint64_t t;
+    do t = g_fused_token.fetch_add(1); while (t == 0);
+    return t;
+}
+
+struct FusedPlan {
+    int wg;     // blocks per head
+    size_t lds;
+};
+
+FusedPlan fused_plan(int d, int nh) {
+    FusedPlan p;
+    p.lds = std::max((size_t)d * 4, (size_t)NWAVE * MD_WAVE * 8);
+    const int occ = resident_blocks(k_heads_fused, p.lds);
+    p.wg = std::max(1, device_cus() * occ / nh);
+    return p;
+}
+
+struct FusedWs {
+    float* hres;
+    float* pv;
+    int* pi;
+    uint64_t *flags_res, *flags_list;
+    size_t bytes;
+};
+
+FusedWs fused_ws(char* base, int d, int nh, int wg, int kmax) {
+    FusedWs L = {};
+    size_t off = 0;
+    auto take = [&](size_t n) {
+        char* q = base ? base + off : nullptr;
+        off += align256(n);
+        return q;
+    };
+    const size_t lists = (size_t)nh * wg * kmax * 4, flags = (size_t)nh * wg * 8;
+    L.hres = reinterpret_cast<float*>(take((size_t)nh * d * 4));
+    L.pv = reinterpret_cast<float*>(take(lists));
+    L.pi = reinterpret_cast<int*>(take(lists));
+    L.flags_res = reinterpret_cast<uint64_t*>(take(flags));
+    L.flags_list = reinterpret_cast<uint64_t*>(take(flags));
+    L.bytes = off;
+    return L;
+}
+
+hipError_t heads_fused_launch(const HeadsArgs& a, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    const FusedPlan p = fused_plan(a.d, a.nh);
+    const FusedWs L = fused_ws(reinterpret_cast<char*>(a.ws), a.d, a.nh, p.wg, a.kmax);
+    KK kk;
+    for (int i = 0; i < 8; ++i) kk.v[i] = i < a.nh ? a.kk[i] : 1;
+    hipError_t e;
+    if (ev0 && (e = hipEventRecord(ev0, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL(k_heads_fused, dim3((unsigned)(a.nh * p.wg)), dim3(BLOCK), p.lds, s,
+                       reinterpret_cast<const uint16_t*>(a.W), reinterpret_cast<const uint16_t*>(a.b),
+                       reinterpret_cast<const uint16_t*>(a.h), reinterpret_cast<const uint16_t*>(a.U), a.d, a.V, a.nh,
+                       p.wg, kk, a.kmax, next_fused_token(), L.hres, a.h_res, L.pv, L.pi, L.flags_res, L.flags_list,
+                       a.topk_idx, a.topk_val);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;
+    return hipSuccess;
+}
+
+}  // namespace
+
+// One Medusa row in bf16 through per-head projections: the single fused launch
+// (while a wave's share of a head's residual rows is at most 64, one per lane).
+bool heads_fused_applicable(int dt, int M, int d, int din, int shared_u, int nh) {
+    if (!(dt == 1 && M == 1 && din == d && !shared_u && nh >= 1)) return false;
+    const FusedPlan p = fused_plan(d, nh);
+    return (d + p.wg * NWAVE - 1) / (p.wg * NWAVE) <= MD_WAVE;
+}
+
+size_t heads_fused_ws_bytes(int d, int nh, int kmax) {
+    return fused_ws(nullptr, d, nh, fused_plan(d, nh).wg, kmax).bytes;
+}
+
 hipError_t heads_launch(const HeadsArgs& a, const DevTree* tree, hipStream_t s, hipEvent_t ev0, hipEvent_t ev1) {
+    if (!a.logits && a.kind == 0 && heads_fused_applicable(a.dt, a.M, a.d, a.din, a.shared_u, a.nh))
+        return heads_fused_launch(a, s, ev0, ev1);
     if (!a.logits &&
         heads_mfma_applicable(a.dt, a.M, a.d, a.din, a.U_op != nullptr, a.shared_u ? a.nh * a.M : a.M)) {
         // many rows: the two contractions on the matrix cores, then the same k-way merge

@@ -63,6 +63,8 @@ struct HeadsArgs {
 
 size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u, bool op);  // this plan
 size_t heads_ws_bound(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u);  // any plan of these sizes
+// one Medusa row in bf16 through per-head projections: one fused launch (residual, projection, top-k, merge)
+bool heads_fused_applicable(int dt, int M, int d, int din, int shared_u, int nh);
 // matrix-core path for many rows (heads_mfma.hip)
 bool heads_mfma_applicable(int dt, int M, int d, int din, bool op, int rows_v);  // rows_v: projection columns
 // one Medusa row with an operand-order copy (shared projection): the GEMV residual feeds the matrix cores

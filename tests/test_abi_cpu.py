@@ -23,7 +23,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 29
+    assert len(names) == 30
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -41,6 +41,19 @@ def test_weight_bytes_match_page():
     assert shared == 2 * (4 * (8192 * 8192 + 8192) + 128256 * 8192)
     assert round((8_942_321_664 - shared) / 2 / 1e9, 2) == 3.15
     assert md.md_heads_weight_bytes(3, 1, 8192, 128256, 4) == -1
+
+
+def test_heads_fused_rule():
+    """One bf16 row through per-head projections runs as a single launch; every other shape keeps
+    its separate kernels."""
+    assert md.md_heads_fused(md.MD_HEADS_MEDUSA, md.MD_BF16, 1, 8192, 4)
+    assert md.md_heads_fused(md.MD_HEADS_MEDUSA, md.MD_BF16, 1, 64, 8)
+    assert not md.md_heads_fused(md.MD_HEADS_MEDUSA, md.MD_F32, 1, 8192, 4)
+    assert not md.md_heads_fused(md.MD_HEADS_MEDUSA, md.MD_BF16, 2, 8192, 4)
+    assert not md.md_heads_fused(md.MD_HEADS_HYDRA, md.MD_BF16, 1, 4096, 4)
+    assert not md.md_heads_fused(md.MD_HEADS_MEDUSA_SHARED, md.MD_BF16, 1, 8192, 4)
+    assert not md.md_heads_fused(7, md.MD_BF16, 1, 8192, 4)
+    assert md.md_heads_workspace_bytes(md.MD_HEADS_MEDUSA, md.MD_BF16, 1, 8192, 128256, 4, 10) > 4 * 8192 * 4
 
 
 def _gamma(n):

@@ -64,8 +64,13 @@ SMALL_BF16 = Workload("small bf16: d=512 V=5003 K=3", "medusa", B=1, d=512, V=50
 
 @pytest.mark.parametrize("wl,M", [(TINY_F32, 1), (replace(TINY_F32, V=1111, bias_zero=False), 4),
                                   (SMALL_BF16, 1), (SMALL_BF16, 2), (SMALL_BF16, 3), (SMALL_BF16, 5),
-                                  (replace(SMALL_BF16, topk=(16, 1, 16)), 2)])
+                                  (replace(SMALL_BF16, topk=(16, 1, 16)), 2),
+                                  (replace(SMALL_BF16, d=256, V=777), 1), (replace(SMALL_BF16, d=64, V=300), 1),
+                                  (replace(SMALL_BF16, topk=(16, 1, 16)), 1)])
 def test_heads_medusa_small(wl, M):
+    """One bf16 row runs the single fused launch (residual blocks, projections, top-k and merge;
+    d = 64 and 256 leave h' smaller than the block's list area in LDS), more rows and float32 the
+    separate kernels."""
     seed = 1000 + M
     w = weights(wl, seed)
     h = synth.normal(seed, 77, (M, wl.d), 1.0, wl.dtype)
@@ -425,9 +430,10 @@ EIGHT = Workload("eight heads: d=256 V=3001 K=8", "medusa", B=1, d=256, V=3001, 
                  topk=(16, 9, 5, 4, 3, 2, 1, 1), N=10, Hq=4, Hkv=1, hd=64, L=10)
 
 
-@pytest.mark.parametrize("M", [2, 16])
+@pytest.mark.parametrize("M", [1, 2, 16])
 def test_heads_eight_heads(M):
-    """The largest head count the boundary takes (K = 8), on the GEMV (2 rows) and MFMA (16 rows) paths."""
+    """The largest head count the boundary takes (K = 8), on the fused one-row launch (8 block groups),
+    the GEMV (2 rows) and MFMA (16 rows) paths."""
     wl = EIGHT
     w = weights(wl, 4000 + M)
     h = synth.normal(4000 + M, 81, (M, wl.d), 1.0, wl.dtype)
