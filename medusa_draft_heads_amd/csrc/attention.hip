@@ -33,6 +33,7 @@
 #include <type_traits>
 
 #include "md_internal.h"
+#include "md_wave.h"
 
 namespace {
 
@@ -457,11 +458,7 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
     const int ntile = k1 > k0 ? (k1 - k0 + DKT - 1) / DKT : 0;
     auto tile_at = [&](int i) { return k0 + min(i, max(ntile - 1, 0)) * DKT; };
     auto step = [&](int i, const unsigned char* cur, unsigned char* nxt) {
-        static_assert(PPW == 4 || PPW == 2, "the waits below assume 2 or 4 pieces a wave");
-        if constexpr (PPW == 4)
-            asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(2)" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(md_wave::waitcnt_vm(PPW));  // PPW: the loads issue() makes per wave
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         issue(tile_at(i + 2), nxt);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this tile's work

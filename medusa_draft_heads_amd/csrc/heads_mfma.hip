@@ -650,17 +650,15 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* 
     // s land before it arrives; lgkmcnt(0) retires its reads of the buffer the
     // next loads overwrite; the clobber keeps the compiler's memory operations
     // on their side of it.
+    static_assert(NS == 1 || NS == 2, "one or two activation pieces per wave and stage");
+    constexpr int kStageLoads = NPA + NS;  // buffer->LDS loads issue() makes per wave
     auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
-        if constexpr (NS == 2)
-            asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
-        else
-            asm volatile("s_waitcnt vmcnt(5)" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(md_wave::waitcnt_vm(kStageLoads));
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         issue(min(s + 2, nk - 1) * VK, nxt);
         __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of this stage's work
         compute(cur);
     };
-    static_assert(NPA + 2 == 6, "the wait counts above assume 4 A pieces per wave");
     issue(0, nbuf0);
     issue(min(1, nk - 1) * VK, nbuf1);
     // three whole steps per iteration (no branch inside, so the compiler's
@@ -921,7 +919,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* 
         issue_a(j, ra[j]);
     }
     auto step = [&](int s, int j) {
-        __builtin_amdgcn_s_waitcnt((C::WAIT & 15) | ((C::WAIT >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+        __builtin_amdgcn_s_waitcnt(md_wave::waitcnt_vm(C::WAIT));
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         issue_b(s + P - 1, buf((j + P - 1) % P));
         __builtin_amdgcn_sched_barrier(0);
@@ -1399,14 +1397,14 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
     // the wait leaves the newer stage's loads (NPA + NPB per wave) open; the
     // barrier is LDS-only, so it does not wait for them either.
     const int nk = d / VK;
+    constexpr int kStageLoads = NPA + NPB;  // buffer->LDS loads issue() makes per wave
     auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
-        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(md_wave::waitcnt_vm(kStageLoads));
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         issue(min(s + 2, nk - 1) * VK, nxt);
         __builtin_amdgcn_sched_barrier(0);
         compute(cur);
     };
-    static_assert(NPA + NPB == 6, "the wait count above assumes 6 pieces per wave and stage");
     issue(0, sbuf0);
     issue(min(1, nk - 1) * VK, sbuf1);
     int ks = 0;
@@ -1670,14 +1668,14 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_wide(const uint16_t* __re
     // loads per wave open; an LDS-only barrier; past the last stage the loads
     // repeat it
     const int nk = d / VK;
+    constexpr int kStageLoads = NPA + NPB;  // buffer->LDS loads issue() makes per wave
     auto step = [&](int s, const unsigned char* cur, unsigned char* nxt) {
-        asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+        __builtin_amdgcn_s_waitcnt(md_wave::waitcnt_vm(kStageLoads));
         asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         issue(min(s + 2, nk - 1) * VK, nxt);
         __builtin_amdgcn_sched_barrier(0);
         compute(cur);
     };
-    static_assert(NPA + NPB == 6, "the wait count above assumes 6 pieces per wave and stage");
     issue(0, wbuf0);
     issue(min(1, nk - 1) * VK, wbuf1);
     int ks = 0;

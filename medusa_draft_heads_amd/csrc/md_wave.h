@@ -14,6 +14,19 @@
 
 namespace md_wave {
 
+// Immediate of s_waitcnt that waits until at most n vector-memory operations
+// of this wave are outstanding and leaves the other counters alone (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 (7: no wait), lgkmcnt
+// 11:8 (15: no wait)). The staged pipelines compute n from the same constants
+// their issue loops use, so a change to the number of loads a stage issues
+// changes the wait with it; the build rejects scratch use (spills are vector
+// memory operations too) in the kernels that rely on it.
+constexpr unsigned waitcnt_vm(int n) {
+    return (unsigned)(n & 15) | ((unsigned)(n >> 4) << 14) | (0x7u << 4) | (0xFu << 8);
+}
+static_assert(waitcnt_vm(0) == 0x0F70u && waitcnt_vm(6) == 0x0F76u && waitcnt_vm(63) == 0xCF7Fu,
+              "s_waitcnt vmcnt encoding");
+
 constexpr int kXor1 = 0xB1;        // quad_perm [1,0,3,2]: lane ^ 1
 constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]: lane ^ 2
 constexpr int kHalfMirror = 0x141;  // lane i <-> 7 - i within each 8
