@@ -7,9 +7,13 @@
 // optional thread-local timing events.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
+#include <random>
 #include <string>
 
 #include "../../include/medusa.h"
@@ -98,11 +102,27 @@ int check_dt(int dt) { return (dt == MD_F32 || dt == MD_BF16) ? MD_OK : fail(MD_
 
 }  // namespace
 
+uint64_t launch_token() {
+    static std::atomic<uint64_t> next{0};
+    static std::once_flag once;
+    std::call_once(once, [] {
+        std::random_device rd;
+        const uint64_t seed = ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^
+                              (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
+        next.store(seed | 1ull);
+    });
+    uint64_t t;
+    do t = next.fetch_add(1); while (t == 0);
+    return t;
+}
+
 extern "C" {
 
 const char* md_last_error(void) { return g_err.c_str(); }
 
 int md_tree_validate(const md_tree* t, int K, const int32_t* k_per_head) { return expand_tree(t, K, k_per_head, nullptr); }
+
+
 
 static bool known_kind(int kind) {
     return kind == MD_HEADS_MEDUSA || kind == MD_HEADS_HYDRA || kind == MD_HEADS_MEDUSA_SHARED;

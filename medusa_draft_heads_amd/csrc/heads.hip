@@ -24,12 +24,9 @@
 #include <math.h>
 
 #include <algorithm>
-#include <atomic>
-#include <chrono>
-#include <mutex>
-#include <random>
 
 #include "md_internal.h"
+#include "md_sync.h"
 #include "md_wave.h"
 
 namespace {
@@ -413,12 +410,12 @@ __global__ __launch_bounds__(NW * MD_WAVE) void k_vocab_topk(const T* __restrict
 // other blocks of the same launch).
 template <bool COH>
 __device__ __forceinline__ float lval(const float* p, int64_t i) {
-    if constexpr (COH) return __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (COH) return md_sync::get(p + i);
     return p[i];
 }
 template <bool COH>
 __device__ __forceinline__ int lidx(const int* p, int64_t i) {
-    if constexpr (COH) return __hip_atomic_load(p + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if constexpr (COH) return md_sync::get(p + i);
     return p[i];
 }
 
@@ -555,33 +552,16 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
 // exactly as k_vocab_topk does, and the group's first block merges the
 // group's lists.
 //
-// Blocks of a group meet through per-block flag words that receive a token
-// unique to the launch. A block writes its share of h' (or its list) with
-// agent-coherent stores (sc1), waits for them to complete (s_waitcnt
-// vmcnt(0)), and only then stores its flag; a reader that has seen every flag
-// of its group equal to the token loads the data with agent-coherent loads.
-// So no cache write-back or invalidate is needed (a release or acquire at
-// agent scope would write back or invalidate the L2 of every XCD that
-// executes it). Flags are never cleared: a stale or uninitialised word cannot
-// hold this launch's token. Every wait is bounded: a block that gives up on
-// its group's h' computes all of h'_j itself (reading W[j] alone: slow, the
-// same result); a group leader that gives up on the lists writes -1 indices.
+// Blocks of a group meet through per-block flag words holding a token
+// unique to the launch (md_sync.h): a block writes its share of h' (or its
+// list) with agent-coherent stores and raises its flag once they have
+// completed; a reader that sees every flag of its group loads the data with
+// agent-coherent loads, so no cache write-back or invalidate is needed.
+// Every wait is bounded: a block that gives up on its group's h' computes
+// all of h'_j itself (reading W[j] alone: slow, the same result); a group
+// leader that gives up on the lists writes -1 indices.
 constexpr int kSpinRes = 1 << 16;    // ~30 ms of polling before computing h' alone
 constexpr int kSpinLists = 1 << 19;  // ~250 ms of polling before giving up the merge
-
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// Every flag of a group holds the token (block-wide; bounded polling).
-__device__ __forceinline__ bool group_flags(const uint64_t* __restrict__ flags, int n, uint64_t token, int limit) {
-    for (int it = 0; it < limit; ++it) {
-        int mine = 1;
-        for (int b = threadIdx.x; b < n; b += BLOCK)
-            mine &= __hip_atomic_load(flags + b, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == token;
-        if (__syncthreads_and(mine)) return true;
-        __builtin_amdgcn_s_sleep(8);
-    }
-    return false;
-}
 
 __global__ __launch_bounds__(BLOCK) void k_heads_fused(const uint16_t* __restrict__ W,
                                                        const uint16_t* __restrict__ bias,
@@ -629,19 +609,16 @@ __global__ __launch_bounds__(BLOCK) void k_heads_fused(const uint16_t* __restric
             const int ri = r0 + lane;
             const float z = mine + (bias ? ldf(bias, (int64_t)hh * d + ri) : 0.f);
             const float hv = xs[ri] + z / (1.f + expf(-z));
-            __hip_atomic_store(hres_h + ri, hv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            md_sync::put(hres_h + ri, hv);
             if (hres_out) hres_out[(int64_t)hh * d + ri] = hv;
         }
     }
-    wait_vm();
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(flags_res + blockIdx.x, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    md_sync::raise_flag(flags_res + blockIdx.x, token);
 
     // h'_hh once the whole group has stored it (h in LDS is no longer read)
-    if (group_flags(flags_res + (int64_t)hh * wg, wg, token, kSpinRes)) {
+    if (md_sync::all_flags<BLOCK>(flags_res + (int64_t)hh * wg, wg, token, kSpinRes)) {
         for (int i = tid; i < d / 2; i += BLOCK) {
-            const uint64_t v = __hip_atomic_load(reinterpret_cast<const uint64_t*>(hres_h) + i, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t v = md_sync::get(reinterpret_cast<const uint64_t*>(hres_h) + i);
             xs[2 * i] = __uint_as_float((uint32_t)v);
             xs[2 * i + 1] = __uint_as_float((uint32_t)(v >> 32));
         }
@@ -720,19 +697,17 @@ __global__ __launch_bounds__(BLOCK) void k_heads_fused(const uint16_t* __restric
         }
         if (lane < kmax) {
             const int64_t o = ((int64_t)hh * wg + wgi) * kmax + lane;
-            __hip_atomic_store(part_val + o, bv, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(part_idx + o, bi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            md_sync::put(part_val + o, bv);
+            md_sync::put(part_idx + o, bi);
         }
-        wait_vm();
     }
-    __syncthreads();
-    if (tid == 0) __hip_atomic_store(flags_list + blockIdx.x, token, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    md_sync::raise_flag(flags_list + blockIdx.x, token);
     if (wgi != 0) return;
 
     // the group's first block merges the group's wg lists into head hh's top-k
     int32_t* oi = topk_idx + (int64_t)hh * kmax;
     float* ov = topk_val + (int64_t)hh * kmax;
-    if (!group_flags(flags_list + (int64_t)hh * wg, wg, token, kSpinLists)) {
+    if (!md_sync::all_flags<BLOCK>(flags_list + (int64_t)hh * wg, wg, token, kSpinLists)) {
         if (tid < kmax) {
             oi[tid] = -1;
             ov[tid] = -INFINITY;
@@ -1095,23 +1070,6 @@ hipError_t target_argmax_launch(int dt, int R, int d, int V, const void* H, cons
 
 namespace {
 
-// A token per fused launch: never 0 (fresh memory), distinct across launches
-// of the process, and random-started so that a workspace last used by
-// another process cannot hold the same value.
-std::atomic<uint64_t> g_fused_token{0};
-std::once_flag g_fused_token_once;
-
-uint64_t next_fused_token() {
-    std::call_once(g_fused_token_once, [] {
-        std::random_device rd;
-        const uint64_t seed = ((uint64_t)rd() << 32) ^ (uint64_t)rd() ^ (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count();
-        g_fused_token.store(seed | 1ull);
-    });
-    uint64_t t;
-    do t = g_fused_token.fetch_add(1); while (t == 0);
-    return t;
-}
-
 struct FusedPlan {
     int wg;     // blocks per head
     size_t lds;
@@ -1161,7 +1119,7 @@ hipError_t heads_fused_launch(const HeadsArgs& a, hipStream_t s, hipEvent_t ev0,
     hipLaunchKernelGGL(k_heads_fused, dim3((unsigned)(a.nh * p.wg)), dim3(BLOCK), p.lds, s,
                        reinterpret_cast<const uint16_t*>(a.W), reinterpret_cast<const uint16_t*>(a.b),
                        reinterpret_cast<const uint16_t*>(a.h), reinterpret_cast<const uint16_t*>(a.U), a.d, a.V, a.nh,
-                       p.wg, kk, a.kmax, next_fused_token(), L.hres, a.h_res, L.pv, L.pi, L.flags_res, L.flags_list,
+                       p.wg, kk, a.kmax, launch_token(), L.hres, a.h_res, L.pv, L.pi, L.flags_res, L.flags_list,
                        a.topk_idx, a.topk_val);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;

@@ -23,6 +23,12 @@ struct DevTree {
     uint64_t anc[64];       // bit j set: node j is this node or one of its ancestors
 };
 
+// A token for one launch of a kernel whose blocks meet through flag words
+// (md_sync.h): never 0, distinct across the process's launches, and started
+// at a random value so that a workspace last used by another process cannot
+// hold it (api.cpp).
+uint64_t launch_token();
+
 // Compute units of the current device (256 if the query fails).
 inline int device_cus() {
     int dev = 0, n = 0;
