@@ -362,6 +362,16 @@ int md_tree_accept_typical(const md_tree* tree, int dt, int B, int K, int V, int
                            int32_t* accept_len, int32_t* path, int32_t* next_tok, int32_t* compact_src, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* Testing hook for the single-launch heads kernel (md_heads_fused): the
+ * number of polls each of its two bounded waits makes on this thread's later
+ * md_medusa_heads calls before giving up (-1: the built-in limits, tens to
+ * hundreds of milliseconds). With residual_polls = 0 every block computes
+ * its head's h' alone instead of waiting for its group's (slow; the same
+ * results); with list_polls = 0 each head's merging block gives up at once
+ * and writes -1 indices and -inf values for its head (a failure the caller
+ * can see). Errors: MD_EINVAL for values below -1. */
+int md_set_wait_limits(int residual_polls, int list_polls);
+
 /* Timing hook for profiling: when both are non-NULL hipEvent_t handles, every
  * later md_medusa_heads or md_medusa_heads_logits call on this thread records
  * `start` on its stream right before its vocabulary-projection kernel and

@@ -27,7 +27,7 @@ EXPORTS = (
     "md_heads_logits_workspace_bytes", "md_medusa_heads_logits", "md_draft_sample_workspace_bytes", "md_draft_sample",
     "md_verify_sampled_workspace_bytes", "md_tree_verify_sampled", "md_accept_typical_workspace_bytes",
     "md_tree_accept_typical", "md_operand_order_bytes", "md_operand_order", "md_certified_rounding_allowance",
-    "md_tree_attention_noalloc", "md_tree_attention_noalloc_max_bytes", "md_heads_fused",
+    "md_tree_attention_noalloc", "md_tree_attention_noalloc_max_bytes", "md_heads_fused", "md_set_wait_limits",
 )
 
 
@@ -66,6 +66,7 @@ def lib() -> ctypes.CDLL:
             "md_heads_weight_bytes": ([i, i, i, i, i], i64),
             "md_certified_rounding_allowance": ([i], f),
             "md_heads_fused": ([i, i, i, i, i], i),
+            "md_set_wait_limits": ([i, i], i),
             "md_heads_workspace_bytes": ([i, i, i, i, i, i, i], sz),
             "md_medusa_heads": ([i, i, i, i, i, i, vp, i, tp] + [vp] * 12 + [sz, vp], i),
             "md_tree_build": ([tp, i, i, i, i, i, i] + [vp] * 6 + [vp], i),
@@ -147,6 +148,10 @@ def md_heads_weight_bytes(kind: int, dt: int, d: int, V: int, K: int) -> int:
 
 def md_heads_fused(kind: int, dt: int, M: int, d: int, K: int) -> bool:
     return bool(lib().md_heads_fused(kind, dt, M, d, K))
+
+
+def md_set_wait_limits(residual_polls: int, list_polls: int) -> None:
+    _check(lib().md_set_wait_limits(residual_polls, list_polls))
 
 
 def md_certified_rounding_allowance(d: int) -> float:

@@ -23,6 +23,7 @@ namespace {
 
 thread_local std::string g_err;
 thread_local hipEvent_t g_ev0 = nullptr, g_ev1 = nullptr;
+thread_local int g_spin_res = -1, g_spin_lists = -1;
 
 int fail(int code, const char* fmt, ...) {
     char buf[512];
@@ -230,6 +231,8 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
         need = heads_ws_bytes(dt, a.M, d, din, V, 1, kmax, 0, U_op != nullptr);
     }
     if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
+    a.spin_res = g_spin_res;
+    a.spin_lists = g_spin_lists;
     return hip_status(heads_launch(a, tp, (hipStream_t)stream, g_ev0, g_ev1), "md_medusa_heads");
 }
 
@@ -409,6 +412,7 @@ int md_medusa_heads_logits(int kind, int dt, int M, int d, int V, int K, const v
     if (ws_bytes < need) return fail(MD_EWORKSPACE, "workspace %zu bytes < %zu needed", ws_bytes, need);
     HeadsArgs a;
     memset(&a, 0, sizeof(a));
+    a.spin_res = a.spin_lists = -1;  // the single-launch kernel does not run here
     a.kind = 0;
     a.shared_u = kind == MD_HEADS_MEDUSA_SHARED;
     a.dt = dt;
@@ -533,6 +537,14 @@ int md_hbm_read_probe(const void* buf, size_t bytes, uint32_t* sink, void* strea
     if (!buf || !sink) return fail(MD_EINVAL, "a required pointer is NULL");
     if (bytes == 0 || bytes % 16) return fail(MD_EINVAL, "bytes = %zu (a positive multiple of 16)", bytes);
     return hip_status(probe_launch(buf, bytes, sink, (hipStream_t)stream), "md_hbm_read_probe");
+}
+
+int md_set_wait_limits(int residual_polls, int list_polls) {
+    if (residual_polls < -1 || list_polls < -1)
+        return fail(MD_EINVAL, "poll limits %d, %d (-1 or more)", residual_polls, list_polls);
+    g_spin_res = residual_polls;
+    g_spin_lists = list_polls;
+    return MD_OK;
 }
 
 int md_set_vocab_timing_events(void* start, void* stop) {

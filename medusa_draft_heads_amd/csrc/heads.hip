@@ -562,11 +562,15 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
 // leader that gives up on the lists writes -1 indices.
 constexpr int kSpinRes = 1 << 16;    // ~30 ms of polling before computing h' alone
 constexpr int kSpinLists = 1 << 19;  // ~250 ms of polling before giving up the merge
+struct SpinLimits {
+    int res, lists;  // polls of the two bounded waits
+};
 
 __global__ __launch_bounds__(BLOCK) void k_heads_fused(const uint16_t* __restrict__ W,
                                                        const uint16_t* __restrict__ bias,
                                                        const uint16_t* __restrict__ h, const uint16_t* __restrict__ U,
                                                        int d, int V, int nh, int wg, KK kk, int kmax, uint64_t token,
+                                                       SpinLimits spin,
                                                        float* __restrict__ hres, float* __restrict__ hres_out,
                                                        float* __restrict__ part_val, int* __restrict__ part_idx,
                                                        uint64_t* __restrict__ flags_res,
@@ -616,7 +620,7 @@ __global__ __launch_bounds__(BLOCK) void k_heads_fused(const uint16_t* __restric
     md_sync::raise_flag(flags_res + blockIdx.x, token);
 
     // h'_hh once the whole group has stored it (h in LDS is no longer read)
-    if (md_sync::all_flags<BLOCK>(flags_res + (int64_t)hh * wg, wg, token, kSpinRes)) {
+    if (md_sync::all_flags<BLOCK>(flags_res + (int64_t)hh * wg, wg, token, spin.res)) {
         for (int i = tid; i < d / 2; i += BLOCK) {
             const uint64_t v = md_sync::get(reinterpret_cast<const uint64_t*>(hres_h) + i);
             xs[2 * i] = __uint_as_float((uint32_t)v);
@@ -707,7 +711,7 @@ __global__ __launch_bounds__(BLOCK) void k_heads_fused(const uint16_t* __restric
     // the group's first block merges the group's wg lists into head hh's top-k
     int32_t* oi = topk_idx + (int64_t)hh * kmax;
     float* ov = topk_val + (int64_t)hh * kmax;
-    if (!md_sync::all_flags<BLOCK>(flags_list + (int64_t)hh * wg, wg, token, kSpinLists)) {
+    if (!md_sync::all_flags<BLOCK>(flags_list + (int64_t)hh * wg, wg, token, spin.lists)) {
         if (tid < kmax) {
             oi[tid] = -1;
             ov[tid] = -INFINITY;
@@ -1119,7 +1123,9 @@ hipError_t heads_fused_launch(const HeadsArgs& a, hipStream_t s, hipEvent_t ev0,
     hipLaunchKernelGGL(k_heads_fused, dim3((unsigned)(a.nh * p.wg)), dim3(BLOCK), p.lds, s,
                        reinterpret_cast<const uint16_t*>(a.W), reinterpret_cast<const uint16_t*>(a.b),
                        reinterpret_cast<const uint16_t*>(a.h), reinterpret_cast<const uint16_t*>(a.U), a.d, a.V, a.nh,
-                       p.wg, kk, a.kmax, launch_token(), L.hres, a.h_res, L.pv, L.pi, L.flags_res, L.flags_list,
+                       p.wg, kk, a.kmax, launch_token(),
+                       SpinLimits{a.spin_res >= 0 ? a.spin_res : kSpinRes, a.spin_lists >= 0 ? a.spin_lists : kSpinLists},
+                       L.hres, a.h_res, L.pv, L.pi, L.flags_res, L.flags_list,
                        a.topk_idx, a.topk_val);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (ev1 && (e = hipEventRecord(ev1, s)) != hipSuccess) return e;

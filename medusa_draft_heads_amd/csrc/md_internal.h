@@ -65,6 +65,7 @@ struct HeadsArgs {
     void* ws;
     float* logits;  // non-null: write every logit [M][logits_k][V] instead of the top-k (GEMV path)
     int logits_k;
+    int spin_res, spin_lists;  // polls of the single-launch kernel's bounded waits (-1: the built-in limits)
 };
 
 size_t heads_ws_bytes(int dt, int M, int d, int din, int V, int nh, int kmax, int shared_u, bool op);  // this plan

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 30
+    assert len(names) == 31
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -54,6 +54,9 @@ def test_heads_fused_rule():
     assert not md.md_heads_fused(md.MD_HEADS_MEDUSA_SHARED, md.MD_BF16, 1, 8192, 4)
     assert not md.md_heads_fused(7, md.MD_BF16, 1, 8192, 4)
     assert md.md_heads_workspace_bytes(md.MD_HEADS_MEDUSA, md.MD_BF16, 1, 8192, 128256, 4, 10) > 4 * 8192 * 4
+    lib = L.lib()
+    assert lib.md_set_wait_limits(-2, 0) == L.MD_EINVAL
+    assert lib.md_set_wait_limits(0, 0) == L.MD_OK and lib.md_set_wait_limits(-1, -1) == L.MD_OK
 
 
 def _gamma(n):

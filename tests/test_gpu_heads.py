@@ -83,6 +83,37 @@ def test_heads_medusa_small(wl, M):
     assert np.array_equal(gi, gi2) and np.array_equal(gv.view(np.uint32), gv2.view(np.uint32))
 
 
+@pytest.mark.parametrize("wl", [SMALL_BF16, replace(SMALL_BF16, d=256, V=777, topk=(16, 1, 4))],
+                         ids=["d=512", "d=256"])
+def test_heads_fused_give_up_paths(wl):
+    """The single-launch kernel's bounded waits, forced to give up from the host (md_set_wait_limits):
+    with no polls for its group's h', every block computes its head's h' alone from W and h, and the
+    lists, values and h' equal the normal launch's bit for bit (and the oracle's); with no polls for
+    the lists, each head's merging block gives up and writes -1 indices and -inf values."""
+    md = _md()
+    seed = 4500 + wl.d
+    w = weights(wl, seed)
+    h = synth.normal(seed, 87, (1, wl.d), 1.0, wl.dtype)
+    wd = {k: to_dev(v) for k, v in w.items()}
+    assert md.md_heads_fused(md.MD_HEADS_MEDUSA, md.MD_BF16, 1, wl.d, wl.K)
+    gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), 1)
+    try:
+        md.md_set_wait_limits(0, -1)
+        gi2, gv2, gh2 = gpu_heads_medusa(wl, wd, to_dev(h), 1)
+        md.md_set_wait_limits(-1, 0)
+        gi3, gv3, _ = gpu_heads_medusa(wl, wd, to_dev(h), 1)
+    finally:
+        md.md_set_wait_limits(-1, -1)
+    assert np.array_equal(gi, gi2) and np.array_equal(gv.view(np.uint32), gv2.view(np.uint32))
+    assert np.array_equal(gh.view(np.uint32), gh2.view(np.uint32))
+    ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, want_logits=True)
+    compare_medusa(wl, gi2, gv2, gh2, ref, label="%s, every block computing h' alone" % wl.name)
+    assert np.all(gi3 == -1) and np.all(np.isneginf(gv3))
+    # and the normal limits again: the normal result
+    gi4, gv4, _ = gpu_heads_medusa(wl, wd, to_dev(h), 1)
+    assert np.array_equal(gi, gi4) and np.array_equal(gv.view(np.uint32), gv4.view(np.uint32))
+
+
 def test_heads_structured_cases():
     """W = 0, b = 0 gives h' = h; U = I (V = d) gives the sorted h itself."""
     import torch
