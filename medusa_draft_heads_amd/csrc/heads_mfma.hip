@@ -542,8 +542,12 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restr
                 part_val[o] = lane < rounds ? ov : -INFINITY;
                 part_idx[o] = lane < rounds ? oi : INT_MAX;
             }
-            // with k candidates taken, the k-th is a lower bound for every later list
-            if (rounds == k && lane == k - 1) atomicMax(bound + (int64_t)hh * M + m, f2o(ov));
+            // with k candidates taken, the k-th is a lower bound for every later
+            // list; one no higher than the bound read above cannot raise it, and
+            // leaving its atomic out keeps tied logits (e.g. a zero row: every
+            // block's k-th equals the bound) from sending all blocks' atomics to
+            // one word, which took twice the kernel's streaming time
+            if (rounds == k && lane == k - 1 && ov > T) atomicMax(bound + (int64_t)hh * M + m, f2o(ov));
         }
     }
 }
@@ -736,7 +740,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* 
             part_val[o] = lane < rounds ? ov : -INFINITY;
             part_idx[o] = lane < rounds ? oi : INT_MAX;
         }
-        if (rounds == k && lane == k - 1) atomicMax(bound + (int64_t)hh * M + m, f2o(ov));
+        if (rounds == k && lane == k - 1 && ov > T) atomicMax(bound + (int64_t)hh * M + m, f2o(ov));
     }
 }
 
@@ -1002,7 +1006,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* 
                 part_val[o] = lane < rounds ? ov : -INFINITY;
                 part_idx[o] = lane < rounds ? oi : INT_MAX;
             }
-            if (rounds == k && lane == k - 1) atomicMax(bound + (int64_t)hh * M + m, f2o(ov));
+            if (rounds == k && lane == k - 1 && ov > T) atomicMax(bound + (int64_t)hh * M + m, f2o(ov));
         }
     }
 }

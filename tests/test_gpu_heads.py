@@ -263,6 +263,9 @@ MFMA_BF16 = Workload("mfma bf16: d=256 V=1000 K=3", "medusa", B=1, d=256, V=1000
                                   (replace(MFMA_BF16, V=20011, K=1, topk=(10,)), 250),
                                   (replace(MFMA_BF16, d=512, V=5003, topk=(16, 2, 9)), 65),
                                   (replace(MFMA_BF16, V=4099, topk=(10, 4, 1)), 72),
+                                  (replace(MFMA_BF16, d=512, V=3001, topk=(12, 5, 2)), 80),
+                                  (replace(MFMA_BF16, V=4099, topk=(10, 4, 1)), 81),
+                                  (replace(MFMA_BF16, d=256, V=3001, topk=(5, 2, 1)), 88),
                                   (replace(MFMA_BF16, d=128, V=3001, topk=(5, 2, 1)), 100),
                                   (replace(MFMA_BF16, V=2053, K=1, topk=(7,)), 128)])
 def test_heads_medusa_mfma_rows(wl, M):
@@ -270,9 +273,10 @@ def test_heads_medusa_mfma_rows(wl, M):
     leaves more than 1,024 partial lists per row for the merge). 250 rows of one head over 79
     vocabulary tiles would run every tile of a row before any bound exists, so they take the
     two-product narrow kernel (four row tiles) instead of the certified pass. 65 to 128 rows run
-    the register-streamed kernel with all rows in one tile (5 to 8 column blocks; 65 leaves one
-    valid column in the last block; at d = 128, 100 rows fill exactly one prefetch ring of 4 K
-    steps; at d = 256, 72 rows end their ring of 6 steps with a tail of 2)."""
+    the register-streamed kernel with all rows in one tile (5 to 8 column blocks; 65 and 81 leave
+    one valid column in the last block, 80 fills five; at d = 128, 100 rows fill exactly one
+    prefetch ring of 4 K steps; at d = 256, 72, 81 and 88 rows end their ring of 6 steps with a
+    tail of 2)."""
     seed = 2000 + M
     w = weights(wl, seed)
     h = synth.normal(seed, 78, (M, wl.d), 1.0, wl.dtype)

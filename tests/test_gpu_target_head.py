@@ -30,6 +30,7 @@ CASES = [
     ("bf16 mfma R=100 one tile", "bf16", 100, 256, 4099),
     ("bf16 mfma R=128 one tile", "bf16", 128, 128, 2053),
     ("bf16 mfma R=72 fewer K steps than the ring", "bf16", 72, 128, 3001),
+    ("bf16 mfma R=88 six column blocks, fewer K steps than the ring", "bf16", 88, 128, 3001),
     ("bf16 mfma R=130 ragged", "bf16", 130, 256, 3001),
     ("bf16 mfma many lists R=9", "bf16", 9, 128, 140001),
     ("70B-shaped LM head, 64 nodes", "bf16", 64, 8192, 128256),
@@ -57,6 +58,8 @@ OP_CASES = [
     ("bf16 operand order R=2", "bf16", 2, 512, 5003, True),
     ("bf16 operand order R=7", "bf16", 7, 256, 4099, True),
     ("bf16 operand order R=64", "bf16", 64, 512, 5003, True),
+    ("bf16 operand order R=80 five full column blocks", "bf16", 80, 256, 4099, True),
+    ("bf16 operand order R=81 one column of a sixth block", "bf16", 81, 512, 5003, True),
     ("bf16 operand order R=100 one tile", "bf16", 100, 256, 4099, True),
     ("bf16 operand order R=128 one tile", "bf16", 128, 128, 2053, True),
     ("bf16 operand order R=130 row-major kernel", "bf16", 130, 256, 3001, True),
