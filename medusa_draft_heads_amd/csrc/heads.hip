@@ -203,6 +203,22 @@ struct RowSrc {
 
 struct KK {
     int v[8];
+    // v[i] with no memory access: a kernel argument indexed by a runtime
+    // value is read with a vector load, and waiting for that load also waits
+    // for every store the wave still has in flight (stores share the counter).
+    // Each v[j] is read with a constant index (a scalar load) and made opaque
+    // to the compiler, which would otherwise turn the selects back into an
+    // indexed load.
+    __device__ __forceinline__ int at(int i) const {
+        int r = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int x = v[j];
+            asm volatile("" : "+s"(x));
+            r = i == j ? x : r;
+        }
+        return r;
+    }
 };
 
 // hres[hh][m][r] = x_m[r] + SiLU(sum_c W[head0+hh][r][c] x_m[c] + b[head0+hh][r])
@@ -318,7 +334,7 @@ __global__ __launch_bounds__(NW * MD_WAVE) void k_vocab_topk(const T* __restrict
     const int r0 = (int)((int64_t)V * wih / wph), r1 = (int)((int64_t)V * (wih + 1) / wph);
     int km[MR];  // top-k width of each row
 #pragma unroll
-    for (int m = 0; m < MR; ++m) km[m] = kk.v[Mh > 0 ? min((m0 + m) / Mh, 7) : hh];
+    for (int m = 0; m < MR; ++m) km[m] = kk.at(Mh > 0 ? min((m0 + m) / Mh, 7) : hh);
     const T* Uh = U + (int64_t)(head0 + hh) * V * d;
 
     float lv[MR], tv[MR];
@@ -371,7 +387,7 @@ __global__ __launch_bounds__(NW * MD_WAVE) void k_vocab_topk(const T* __restrict
     static_assert(NW >= MR, "one wave per activation row");
     const int m = wv;
     if (m >= mr) return;
-    const int k = kk.v[Mh > 0 ? min((m0 + m) / Mh, 7) : hh];
+    const int k = kk.at(Mh > 0 ? min((m0 + m) / Mh, 7) : hh);
     float bv = -INFINITY, btv = -INFINITY;
     int bi = INT_MAX, bti = INT_MAX;
     for (int w2 = 0; w2 < NW; ++w2) {
@@ -537,7 +553,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
     const int m = blockIdx.x / nh, hh = blockIdx.x - (blockIdx.x / nh) * nh;
     const int64_t base = ((int64_t)hh * M + m) * nlists * kmax;
     const int64_t o = ((int64_t)m * nh + hh) * kmax;
-    merge_lists<LPT, false>(part_val, part_idx, base, nlists, kk.v[hh], kmax, topk_idx + o, topk_val + o);
+    merge_lists<LPT, false>(part_val, part_idx, base, nlists, kk.at(hh), kmax, topk_idx + o, topk_val + o);
 }
 
 // ---- one launch for the heads of one row (Medusa, bf16) ----
@@ -650,7 +666,7 @@ __global__ __launch_bounds__(BLOCK) void k_heads_fused(const uint16_t* __restric
     __syncthreads();
 
     // this block's share of the vocabulary rows, as k_vocab_topk<bf16, 1, 4>
-    const int k = kk.v[hh];
+    const int k = kk.at(hh);
     float lv = -INFINITY, tv = -INFINITY;
     int li = INT_MAX, ti = INT_MAX;
     auto take = [&](int r, int nv, const float (&acc)[RPW][1]) {

@@ -85,6 +85,22 @@ __device__ __forceinline__ float o2f(int k) { return __int_as_float(k >= 0 ? k :
 
 struct KW {
     int v[8];
+    // v[i] with no memory access: a kernel argument indexed by a runtime
+    // value is read with a vector load, and waiting for that load also waits
+    // for every store the wave still has in flight (stores share the counter).
+    // Each v[j] is read with a constant index (a scalar load) and made opaque
+    // to the compiler, which would otherwise turn the selects back into an
+    // indexed load.
+    __device__ __forceinline__ int at(int i) const {
+        int r = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int x = v[j];
+            asm volatile("" : "+s"(x));
+            r = i == j ? x : r;
+        }
+        return r;
+    }
 };
 
 // Hydra rows: (request, parent) -> the parent's token.
@@ -506,7 +522,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma(const uint16_t* __restr
         for (int col = w; col < VM; col += 4) {
             const int m = m0 + col;
             if (m >= M) break;  // uniform: columns past M are padding
-            const int k = kk.v[Mh > 0 ? min(m / Mh, 7) : hh];
+            const int k = (Mh > 0 ? kk.at(__builtin_amdgcn_readfirstlane(min(m / Mh, 7))) : kk.at(hh));
             const float T = s_bound[col];
             const unsigned char* Sc = (col < 64 ? sbuf0 : sbuf1) + (col & 63) * 512;
             float x[2];
@@ -701,7 +717,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* 
     for (int col = w; col < NM; col += 4) {
         const int m = m0 + col;
         if (m >= M) break;  // uniform: columns past M are padding
-        const int k = kk.v[Mh > 0 ? min(m / Mh, 7) : hh];
+        const int k = (Mh > 0 ? kk.at(__builtin_amdgcn_readfirstlane(min(m / Mh, 7))) : kk.at(hh));
         const float T = s_bound[col];
         const unsigned char* Sc = colp(col);
         float x[4];
@@ -967,7 +983,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* 
         for (int col = w; col < ncol; col += 4) {
             const int m = 16 * cb0 + col;
             if (m >= M) break;  // uniform: columns past M are padding
-            const int k = kk.v[Mh > 0 ? min(m / Mh, 7) : hh];
+            const int k = (Mh > 0 ? kk.at(__builtin_amdgcn_readfirstlane(min(m / Mh, 7))) : kk.at(hh));
             const float T = s_bound[m];
             const unsigned char* Sc = colp(col);
             float x[4];
@@ -1145,7 +1161,7 @@ __global__ __launch_bounds__(BLOCK) void k_rescore(const uint16_t* __restrict__ 
     __shared__ int wi_s[BLOCK / 64];
     const int hh = blockIdx.x / M, m = blockIdx.x - hh * M;
     const int row = hh * M + m;  // row of h' and of the candidate arrays
-    const int k = kk.v[hh];
+    const int k = kk.at(hh);
     const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
     const uint16_t* Uh = U + (shared_u ? 0 : (int64_t)(head0 + hh) * V * d);
     const uint16_t* xh = hhi + (int64_t)row * d;
@@ -1536,7 +1552,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
                 if (ids[q] < 0) break;  // uniform
                 const int i = ids[q];
                 const int m = m0 + w + 4 * i, row = hh * M + m;
-                const int k = kk.v[Mh > 0 ? min(m / Mh, 7) : hh];
+                const int k = (Mh > 0 ? kk.at(__builtin_amdgcn_readfirstlane(min(m / Mh, 7))) : kk.at(hh));
                 float sv = svs[q];
                 float kth = -INFINITY;
                 if (k > 2) kth = o2f(wave_kth_largest_ordered(f2o(sv), k));

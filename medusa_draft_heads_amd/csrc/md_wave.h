@@ -32,9 +32,12 @@ constexpr int kXor2 = 0x4E;        // quad_perm [2,3,0,1]: lane ^ 2
 constexpr int kHalfMirror = 0x141;  // lane i <-> 7 - i within each 8
 constexpr int kMirror = 0x140;      // lane i <-> 15 - i within each 16
 
+// Every control used here reads a lane inside the same row, so no lane is
+// out of range; bound_ctrl lets the compiler fold the move into the
+// instruction that consumes it (one DPP-modified max per level).
 template <int CTRL>
 __device__ __forceinline__ int dpp(int v) {
-    return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false);
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xF, 0xF, true);
 }
 // The value of the lane 16 (32) apart: swapping a register with itself
 // leaves rows (r & ~1, r | 1) -- halves (0, 1) -- in the two results.

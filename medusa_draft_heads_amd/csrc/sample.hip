@@ -122,6 +122,22 @@ __device__ void block_argmax(float& v, int& i, float* shv, int* shi) {
 
 struct KS {
     int v[8];
+    // v[i] with no memory access: a kernel argument indexed by a runtime
+    // value is read with a vector load, and waiting for that load also waits
+    // for every store the wave still has in flight (stores share the counter).
+    // Each v[j] is read with a constant index (a scalar load) and made opaque
+    // to the compiler, which would otherwise turn the selects back into an
+    // indexed load.
+    __device__ __forceinline__ int at(int i) const {
+        int r = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            int x = v[j];
+            asm volatile("" : "+s"(x));
+            r = i == j ? x : r;
+        }
+        return r;
+    }
 };
 
 // Block (row-head rh = m K + h, vocabulary chunk ch): the chunk's k best
@@ -139,7 +155,7 @@ __global__ __launch_bounds__(BLOCK) void k_draft_part(const float* __restrict__ 
     __shared__ int out_i[KM];
     const int rh = blockIdx.x / chunks, ch = blockIdx.x - rh * chunks;
     const int m = rh / K, h = rh - m * K;
-    const int k = ks.v[h];
+    const int k = ks.at(h);
     const int tid = threadIdx.x;
     const int a = (int)((int64_t)V * ch / chunks), e = (int)((int64_t)V * (ch + 1) / chunks);
     const float* lg = logits + (int64_t)rh * V;
