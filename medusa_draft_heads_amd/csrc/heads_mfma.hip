@@ -150,9 +150,34 @@ __device__ __forceinline__ void tile_mma(const uint16_t (*As)[LP], const uint16_
 // h' = base + SiLU(z + b) for 4 consecutive rows r.. of head hh, activation
 // row m, stored as float32 and as its hi/lo bf16 split.
 // bw, hw: the 4 bias and base values (bf16 pairs; bw zero without a bias).
+// Where the residual epilogue also writes hi and lo in the activation
+// operand order of the narrow vocabulary kernel (hi == nullptr: not written).
+// Per matrix of R rows (one head's M rows, or with one shared projection the
+// heads' nh * M rows as one matrix): [tile of 64 rows][K step of 32][64
+// rows][64 bytes], the 16-byte chunk c of row rr in slot c ^ ((rr / 2) % 4),
+// i.e. exactly the LDS image of the kernel's activation stage, so each 1 KB
+// piece (16 rows) of a stage is one contiguous load. Rows past R are never
+// written; their products only reach padding columns.
+struct BoOut {
+    uint16_t* hi;
+    uint16_t* lo;
+    int shared;  // 1: the heads' rows form one [nh * M][d] matrix
+    int nh;
+};
+constexpr int kBoTile = 64;  // rows per tile of the ordered copy (the narrow kernel's activation tile)
+constexpr int kBoStep = 32;  // contraction elements per K step (its stage)
+__device__ __forceinline__ int64_t bo_offset(const BoOut& bo, int M, int d, int hh, int m, int r) {
+    const int hq = bo.shared ? 0 : hh, g = bo.shared ? hh * M + m : m;
+    const int R = bo.shared ? bo.nh * M : M;
+    const int ntile = (R + kBoTile - 1) / kBoTile, nk = d / kBoStep;
+    const int mt = g / kBoTile, rr = g % kBoTile, ks = r / kBoStep, c = (r / 8) % 4;
+    return ((((int64_t)hq * ntile + mt) * nk + ks) * kBoTile + rr) * kBoStep + (c ^ ((rr >> 1) & 3)) * 8 + (r % 8);
+}
+
 __device__ __forceinline__ void residual_out_w(const f32x4& z, u32x2 bw, u32x2 hw, int M, int d, int hh, int m, int r,
                                                float* __restrict__ hres, float* __restrict__ hres_out,
-                                               uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo) {
+                                               uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo,
+                                               const BoOut& bo) {
     const float bb[4] = {bf_lo(bw.x), bf_hi(bw.x), bf_lo(bw.y), bf_hi(bw.y)};
     const float base[4] = {bf_lo(hw.x), bf_hi(hw.x), bf_lo(hw.y), bf_hi(hw.y)};
     f32x4 hv;
@@ -174,6 +199,11 @@ __device__ __forceinline__ void residual_out_w(const f32x4& z, u32x2 bw, u32x2 h
     if (hres_out) *reinterpret_cast<f32x4*>(hres_out + o) = hv;
     *reinterpret_cast<u32x2*>(hhi + o) = u32x2{hi2[0], hi2[1]};
     *reinterpret_cast<u32x2*>(hlo + o) = u32x2{lo2[0], lo2[1]};
+    if (bo.hi) {  // 4 outputs r..r+3 (r % 4 == 0) lie in one 16-byte chunk
+        const int64_t ob = bo_offset(bo, M, d, hh, m, r);
+        *reinterpret_cast<u32x2*>(bo.hi + ob) = u32x2{hi2[0], hi2[1]};
+        *reinterpret_cast<u32x2*>(bo.lo + ob) = u32x2{lo2[0], lo2[1]};
+    }
 }
 __device__ __forceinline__ u32x2 bias_words(const uint16_t* __restrict__ bias, int head0, int hh, int d, int r) {
     return bias ? *reinterpret_cast<const u32x2*>(bias + (int64_t)(head0 + hh) * d + r) : u32x2{0u, 0u};
@@ -181,10 +211,11 @@ __device__ __forceinline__ u32x2 bias_words(const uint16_t* __restrict__ bias, i
 __device__ __forceinline__ void residual_out(const f32x4& z, const uint16_t* __restrict__ bias, const GemmRows& rows,
                                              int brow, int M, int d, int head0, int hh, int m, int r,
                                              float* __restrict__ hres, float* __restrict__ hres_out,
-                                             uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo) {
+                                             uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo,
+                                             const BoOut& bo) {
     const u32x2 bw = bias_words(bias, head0, hh, d, r);
     const u32x2 hw = *reinterpret_cast<const u32x2*>(rows.h + (int64_t)brow * d + r);
-    residual_out_w(z, bw, hw, M, d, hh, m, r, hres, hres_out, hhi, hlo);
+    residual_out_w(z, bw, hw, M, d, hh, m, r, hres, hres_out, hhi, hlo, bo);
 }
 
 // Phase 1: z = W x for rows [0, nh*d) of the heads' residual matrices and
@@ -199,7 +230,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __re
                                                             float* __restrict__ zpart,
                                                             float* __restrict__ hres, float* __restrict__ hres_out,
                                                             uint16_t* __restrict__ hhi, uint16_t* __restrict__ hlo,
-                                                            int* __restrict__ bound) {
+                                                            int* __restrict__ bound, BoOut bo) {
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
     __shared__ int s_tok[TM];
     __shared__ int s_b[TM];
@@ -300,7 +331,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_mfma(const uint16_t* __re
             const int m = m0 + mm;
             if (m >= M) continue;
             residual_out(acc[rb_][cb], bias, rows, rows.kind == 0 ? m : s_b[mm], M, d, head0, hh, m, r, hres, hres_out,
-                         hhi, hlo);
+                         hhi, hlo, bo);
         }
     }
 }
@@ -311,7 +342,7 @@ __global__ __launch_bounds__(BLOCK) void k_residual_finish(const float* __restri
                                                            const uint16_t* __restrict__ bias, GemmRows rows, int M,
                                                            int d, int nh, int head0, float* __restrict__ hres,
                                                            float* __restrict__ hres_out, uint16_t* __restrict__ hhi,
-                                                           uint16_t* __restrict__ hlo) {
+                                                           uint16_t* __restrict__ hlo, BoOut bo) {
     const int64_t q = (int64_t)blockIdx.x * BLOCK + threadIdx.x;  // index of 4 outputs over [nh][M][d]
     const int64_t total = (int64_t)nh * M * d / 4;
     if (q >= total) return;
@@ -344,7 +375,7 @@ __global__ __launch_bounds__(BLOCK) void k_residual_finish(const float* __restri
         for (int j = 0; j < 16; ++j)
             if (c + j < ksplit) z += p[j];
     }
-    residual_out_w(z, bw, hw, M, d, hh, m, r, hres, hres_out, hhi, hlo);
+    residual_out_w(z, bw, hw, M, d, hh, m, r, hres, hres_out, hhi, hlo, bo);
 }
 
 // Phase 2: logits = U (hi + lo) for one head's VR vocabulary rows x VM
@@ -585,13 +616,18 @@ static_assert(NM * VR * 4 <= 3 * NSTAGE, "the logit tile fits the three stage bu
 constexpr int NCOLS_PER_BUF = NSTAGE / (VR * 4);  // 24 columns of 256 logits per stage buffer
 constexpr int kNarrowRows = 128;  // up to this many activation rows the two-product kernels run (narrow to 64, then direct)
 
-template <int NS, bool OP>
+// BO: the activations come from the residual epilogue's ordered copy (bo_hi,
+// bo_lo; see BoOut), one contiguous 1 KB load a piece, instead of 16 rows of
+// 64 bytes from hhi / hlo (half cache lines, each fetched twice).
+template <int NS, bool OP, bool BO>
 __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* __restrict__ U,
                                                                 const uint16_t* __restrict__ hhi,
                                                                 const uint16_t* __restrict__ hlo, int M, int d, int V,
                                                                 int nh, int head0, int vtiles, int mtiles, int kmax,
                                                                 KW kk, int Mh, float* __restrict__ part_val,
-                                                                int* __restrict__ part_idx, int* __restrict__ bound) {
+                                                                int* __restrict__ part_idx, int* __restrict__ bound,
+                                                                const uint16_t* __restrict__ bo_hi,
+                                                                const uint16_t* __restrict__ bo_lo) {
     __shared__ __align__(1024) unsigned char nbuf0[NSTAGE];
     __shared__ __align__(1024) unsigned char nbuf1[NSTAGE];
     __shared__ __align__(1024) unsigned char nbuf2[NSTAGE];
@@ -620,6 +656,15 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* 
         __builtin_amdgcn_make_buffer_rsrc((void*)(hhi + hbase + (int64_t)m0 * d), 0, min(M - m0, NM) * d * 2, RSRC3);
     const __amdgpu_buffer_rsrc_t rL =
         __builtin_amdgcn_make_buffer_rsrc((void*)(hlo + hbase + (int64_t)m0 * d), 0, min(M - m0, NM) * d * 2, RSRC3);
+    // ordered copy: this (head, row tile)'s K steps of 4 KB; a piece whose 16
+    // rows all lie past M gets an offset past the resource (zeros, no traffic)
+    static_assert(kBoTile == NM && kBoStep == VK, "the ordered copy is the narrow kernel's activation stage image");
+    const int64_t bo_tile = ((int64_t)hh * mtiles + mt) * (d / VK) * NM * VK;
+    const __amdgpu_buffer_rsrc_t rHo =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(BO ? bo_hi + bo_tile : hhi), 0, (d / VK) * NB_BYTES, RSRC3);
+    const __amdgpu_buffer_rsrc_t rLo =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(BO ? bo_lo + bo_tile : hlo), 0, (d / VK) * NB_BYTES, RSRC3);
+    const uint32_t bo_off0 = 16 * w < M - m0 ? (uint32_t)w * 1024u + lane * 16 : 0xFFFFFF00u;
     auto issue = [&](int k0, unsigned char* base) {
         if constexpr (OP) {
 #pragma unroll
@@ -629,8 +674,14 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_narrow(const uint16_t* 
 #pragma unroll
             for (int j = 0; j < NPA; ++j) dmab(rA, base + (w + 4 * j) * 1024, voff0 + (uint32_t)(64 * j * d + k0) * 2);
         }
-        dmab(rH, base + A_BYTES + w * 1024, voff0 + (uint32_t)k0 * 2);
-        if constexpr (NS == 2) dmab(rL, base + A_BYTES + NB_BYTES + w * 1024, voff0 + (uint32_t)k0 * 2);
+        if constexpr (BO) {
+            const uint32_t o = bo_off0 == 0xFFFFFF00u ? bo_off0 : bo_off0 + (uint32_t)(k0 / VK) * NB_BYTES;
+            dmab(rHo, base + A_BYTES + w * 1024, o);
+            if constexpr (NS == 2) dmab(rLo, base + A_BYTES + NB_BYTES + w * 1024, o);
+        } else {
+            dmab(rH, base + A_BYTES + w * 1024, voff0 + (uint32_t)k0 * 2);
+            if constexpr (NS == 2) dmab(rL, base + A_BYTES + NB_BYTES + w * 1024, voff0 + (uint32_t)k0 * 2);
+        }
     };
 
     f32x4 acc[4][4];
@@ -819,13 +870,15 @@ struct DirectCfg {
     static_assert(2 * P * SB + 2 * 4 * 128 <= 160 * 1024, "two blocks fit the LDS of one CU");
 };
 
-template <int NS, int CB, bool OP>
+template <int NS, int CB, bool OP, bool BO>
 __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* __restrict__ U,
                                                                 const uint16_t* __restrict__ hhi,
                                                                 const uint16_t* __restrict__ hlo, int M, int d, int V,
                                                                 int nh, int head0, int vtiles, int kmax, KW kk, int Mh,
                                                                 float* __restrict__ part_val,
-                                                                int* __restrict__ part_idx, int* __restrict__ bound) {
+                                                                int* __restrict__ part_idx, int* __restrict__ bound,
+                                                                const uint16_t* __restrict__ bo_hi,
+                                                                const uint16_t* __restrict__ bo_lo) {
     typedef DirectCfg<NS, CB> C;
     constexpr int P = C::P;
     __shared__ __align__(1024) unsigned char db0[C::SB];
@@ -874,6 +927,16 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* 
         __builtin_amdgcn_make_buffer_rsrc((void*)(hlo + hbase), 0, M * d * 2, RSRC3);
     const int bc = lane >> 2;
     const uint32_t boff = (uint32_t)bc * d * 2 + 16 * ((lane & 3) ^ ((bc >> 1) & 3));
+    // BO: the residual epilogue's ordered copy (see BoOut): column block cb
+    // is row block cb % 4 of 64-row tile cb / 4, each K step of a tile 4 KB
+    // in place; blocks whose 16 rows all lie past M load nothing
+    static_assert(kBoTile == 64 && kBoStep == VK, "ordered copy tiles of four 16-row blocks");
+    const int64_t bo_head = (int64_t)hh * ((M + kBoTile - 1) / kBoTile) * nk * NB_BYTES / 2;
+    const uint32_t bo_size = (uint32_t)((M + kBoTile - 1) / kBoTile) * nk * NB_BYTES;
+    const __amdgpu_buffer_rsrc_t rHo =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(BO ? bo_hi + bo_head : hhi), 0, bo_size, RSRC3);
+    const __amdgpu_buffer_rsrc_t rLo =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(BO ? bo_lo + bo_head : hlo), 0, bo_size, RSRC3);
 
     u32x4 ra[P][4];
     auto issue_a = [&](int s, u32x4 (&r)[4]) {
@@ -894,8 +957,15 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* 
         for (int j = 0; j < C::NB; ++j) {
             const int p = min(w + 4 * j, C::NPC - 1);
             const int op = p / CB, cb = p - (p / CB) * CB;
-            const uint32_t o = boff + (uint32_t)(16 * cb) * d * 2 + ko;
-            dmab((NS == 2 && op) ? rL : rH, dst + p * 1024, o);
+            if constexpr (BO) {
+                const uint32_t o = 16 * cb < M ? ((uint32_t)(cb / 4) * nk + (uint32_t)min(s, nk - 1)) * NB_BYTES +
+                                                     (uint32_t)(cb % 4) * 1024u + lane * 16
+                                               : 0xFFFFFF00u;
+                dmab((NS == 2 && op) ? rLo : rHo, dst + p * 1024, o);
+            } else {
+                const uint32_t o = boff + (uint32_t)(16 * cb) * d * 2 + ko;
+                dmab((NS == 2 && op) ? rL : rH, dst + p * 1024, o);
+            }
         }
     };
 
@@ -1027,14 +1097,14 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* 
     }
 }
 
-template <int NS, bool OP>
+template <int NS, bool OP, bool BO>
 hipError_t launch_direct(int cb, dim3 grid, hipStream_t s, const uint16_t* U, const uint16_t* hhi, const uint16_t* hlo,
                          int M, int d, int V, int nh, int head0, int vtiles, int kmax, KW kk, int Mh, float* pv,
-                         int* pi, int* bound) {
+                         int* pi, int* bound, const uint16_t* bo_hi = nullptr, const uint16_t* bo_lo = nullptr) {
 #define MD_DIRECT(CBV)                                                                                               \
     case CBV:                                                                                                        \
-        hipLaunchKernelGGL((k_vocab_mfma_direct<NS, CBV, OP>), grid, dim3(BLOCK), 0, s, U, hhi, hlo, M, d, V, nh, head0, \
-                           vtiles, kmax, kk, Mh, pv, pi, bound);                                                     \
+        hipLaunchKernelGGL((k_vocab_mfma_direct<NS, CBV, OP, BO>), grid, dim3(BLOCK), 0, s, U, hhi, hlo, M, d, V, nh,    \
+                           head0, vtiles, kmax, kk, Mh, pv, pi, bound, bo_hi, bo_lo);                                 \
         break;
     switch (cb) {
         MD_DIRECT(5)
@@ -1726,7 +1796,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_residual_wide(const uint16_t* __re
 #pragma unroll
         for (int rb = 0; rb < 8; ++rb)
             residual_out_w(acc[rb][cb], bw[rb], hw[rb], M, d, hh, m, rt0 + 128 * wr + 16 * rb + 4 * g4, hres,
-                           hres_out, hhi, hlo);
+                           hres_out, hhi, hlo, BoOut{nullptr, nullptr, 0, 0});
     }
 }
 
@@ -1771,17 +1841,19 @@ hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt
     if (R <= kNarrowRows) {
         if (R > NM) {
             const int cb = (R + 15) / 16;
-            err = op ? launch_direct<1, true>(cb, dim3(vtiles), s, wt, h, h, R, d, V, 1, 0, vtiles, 1, kk, 0, pv, pi, bound)
-                     : launch_direct<1, false>(cb, dim3(vtiles), s, wt, h, h, R, d, V, 1, 0, vtiles, 1, kk, 0, pv, pi, bound);
+            err = op ? launch_direct<1, true, false>(cb, dim3(vtiles), s, wt, h, h, R, d, V, 1, 0, vtiles, 1, kk, 0, pv,
+                                                     pi, bound)
+                     : launch_direct<1, false, false>(cb, dim3(vtiles), s, wt, h, h, R, d, V, 1, 0, vtiles, 1, kk, 0, pv,
+                                                      pi, bound);
             if (err != hipSuccess) return err;
         } else {
             const dim3 grid(8 * ((vtiles + 7) / 8));
             if (op)
-                hipLaunchKernelGGL((k_vocab_mfma_narrow<1, true>), grid, dim3(BLOCK), 0, s, wt, h, h, R, d, V, 1, 0, vtiles,
-                                   1, 1, kk, 0, pv, pi, bound);
+                hipLaunchKernelGGL((k_vocab_mfma_narrow<1, true, false>), grid, dim3(BLOCK), 0, s, wt, h, h, R, d, V, 1, 0,
+                                   vtiles, 1, 1, kk, 0, pv, pi, bound, nullptr, nullptr);
             else
-                hipLaunchKernelGGL((k_vocab_mfma_narrow<1, false>), grid, dim3(BLOCK), 0, s, wt, h, h, R, d, V, 1, 0,
-                                   vtiles, 1, 1, kk, 0, pv, pi, bound);
+                hipLaunchKernelGGL((k_vocab_mfma_narrow<1, false, false>), grid, dim3(BLOCK), 0, s, wt, h, h, R, d, V, 1,
+                                   0, vtiles, 1, 1, kk, 0, pv, pi, bound, nullptr, nullptr);
         }
         *nlists = vtiles;
     } else {  // row-major LM head: the many-row kernel stages its tiles through LDS
@@ -1871,8 +1943,8 @@ bool residual_wide(int kind, int M, int d, int din, int nh) {
 }
 
 // Workspace: h' (float32, hi, lo), the per-row bounds, the split-contraction
-// partials, then either the narrow kernel's partial lists or the certified
-// pass's norms, slots and candidate buffers.
+// partials, then either the narrow kernel's partial lists and hi / lo in its
+// operand order or the certified pass's norms, slots and candidate buffers.
 struct MfmaWs {
     float* hres;
     uint16_t *hhi, *hlo;
@@ -1880,6 +1952,7 @@ struct MfmaWs {
     float* zpart;
     float *pv;  // narrow: partial lists [rows][vtiles][kmax]
     int* pi;
+    uint16_t *bo_hi, *bo_lo;  // narrow: hi / lo in its activation operand order (BoOut)
     float *lo_norm, *h_norm;  // certified: per row
     int *count, *slots;
     float *cand_ub, *cand_lb;
@@ -1906,6 +1979,10 @@ MfmaWs mfma_ws_layout(char* base, int M, int d, int din, int V, int nh, int kmax
         const size_t lists = rows * (size_t)((V + VR - 1) / VR) * kmax * 4;
         L.pv = reinterpret_cast<float*>(take(lists));
         L.pi = reinterpret_cast<int*>(take(lists));
+        // per head whole 64-row tiles (also covers the heads' rows as one matrix)
+        const size_t bo = (size_t)nh * ((M + kBoTile - 1) / kBoTile) * kBoTile * d * 2;
+        L.bo_hi = reinterpret_cast<uint16_t*>(take(bo));
+        L.bo_lo = reinterpret_cast<uint16_t*>(take(bo));
     } else {
         L.lo_norm = reinterpret_cast<float*>(take(rows * 4));
         L.h_norm = reinterpret_cast<float*>(take(rows * 4));
@@ -1979,6 +2056,11 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     // (one pass over W, HBM-bound) writes h' and its hi/lo split for the
     // matrix-core vocabulary kernel; otherwise a matrix-core residual
     const bool on_gemv = residual_on_gemv(a.dt, a.kind, a.M, a.d, a.din, a.U_op != nullptr);
+    // the few-row vocabulary kernels read hi / lo in their operand order when
+    // the matrix-core residual (k_residual_mfma, k_residual_finish) writes them
+    const int rows_v = a.shared_u ? a.nh * a.M : a.M, nh_u = a.shared_u ? 1 : a.nh;
+    const bool use_bo = !cert && !on_gemv && !residual_wide(a.kind, a.M, a.d, a.din, a.nh);
+    const BoOut bo = use_bo ? BoOut{L.bo_hi, L.bo_lo, a.shared_u, a.nh} : BoOut{nullptr, nullptr, 0, 0};
     if (on_gemv) {
         float ninf = -INFINITY;
         int nb;
@@ -1993,13 +2075,13 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     } else {
         hipLaunchKernelGGL(k_residual_mfma, dim3(ksplit * 8 * mtiles * ((units1 + 7) / 8)), dim3(BLOCK), 0, s,
                            reinterpret_cast<const uint16_t*>(a.W), bias, rows, a.M, a.d, a.din, a.nh, a.head0, mtiles,
-                           ksplit, L.zpart, L.hres, a.h_res, L.hhi, L.hlo, L.bound);
+                           ksplit, L.zpart, L.hres, a.h_res, L.hhi, L.hlo, L.bound, bo);
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (!on_gemv && ksplit > 1 && !residual_wide(a.kind, a.M, a.d, a.din, a.nh)) {
         const int64_t quads = e / 4;
         hipLaunchKernelGGL(k_residual_finish, dim3((unsigned)((quads + BLOCK - 1) / BLOCK)), dim3(BLOCK), 0, s, L.zpart,
-                           ksplit, bias, rows, a.M, a.d, a.nh, a.head0, L.hres, a.h_res, L.hhi, L.hlo);
+                           ksplit, bias, rows, a.M, a.d, a.nh, a.head0, L.hres, a.h_res, L.hhi, L.hlo, bo);
         if ((err = hipGetLastError()) != hipSuccess) return err;
     }
     if (cert) {
@@ -2009,7 +2091,6 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     }
     if (ev0 && (err = hipEventRecord(ev0, s)) != hipSuccess) return err;
     // a shared projection is one matrix over the heads' nh * M rows
-    const int rows_v = a.shared_u ? a.nh * a.M : a.M, nh_u = a.shared_u ? 1 : a.nh;
     const int units2 = nh_u * vtiles;
     const uint16_t* U = reinterpret_cast<const uint16_t*>(a.U);
     const int head0 = a.shared_u ? 0 : a.head0, Mh = a.shared_u ? a.M : 0;
@@ -2021,20 +2102,28 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
         const uint16_t* UA = op ? reinterpret_cast<const uint16_t*>(a.U_op) : U;
         if (rows_v > NM && rows_v <= kNarrowRows) {
             const int cb = (rows_v + 15) / 16;
-            err = op ? launch_direct<2, true>(cb, dim3(units2), s, UA, L.hhi, L.hlo, rows_v, a.d, a.V, nh_u, head0, vtiles,
-                                              a.kmax, kk, Mh, L.pv, L.pi, L.bound)
-                     : launch_direct<2, false>(cb, dim3(units2), s, UA, L.hhi, L.hlo, rows_v, a.d, a.V, nh_u, head0,
-                                               vtiles, a.kmax, kk, Mh, L.pv, L.pi, L.bound);
+#define MD_DIRECT_L(OPV, BOV)                                                                                    \
+    launch_direct<2, OPV, BOV>(cb, dim3(units2), s, UA, L.hhi, L.hlo, rows_v, a.d, a.V, nh_u, head0, vtiles, a.kmax, kk, \
+                               Mh, L.pv, L.pi, L.bound, bo.hi, bo.lo)
+            err = op ? (use_bo ? MD_DIRECT_L(true, true) : MD_DIRECT_L(true, false))
+                     : (use_bo ? MD_DIRECT_L(false, true) : MD_DIRECT_L(false, false));
+#undef MD_DIRECT_L
             if (err != hipSuccess) return err;
         } else {
             const int nmt = (rows_v + NM - 1) / NM;
             const dim3 grid(8 * nmt * ((units2 + 7) / 8));
-            if (op)
-                hipLaunchKernelGGL((k_vocab_mfma_narrow<2, true>), grid, dim3(BLOCK), 0, s, UA, L.hhi, L.hlo, rows_v, a.d,
-                                   a.V, nh_u, head0, vtiles, nmt, a.kmax, kk, Mh, L.pv, L.pi, L.bound);
+#define MD_NARROW(OPV, BOV)                                                                                          \
+    hipLaunchKernelGGL((k_vocab_mfma_narrow<2, OPV, BOV>), grid, dim3(BLOCK), 0, s, UA, L.hhi, L.hlo, rows_v, a.d, a.V, \
+                       nh_u, head0, vtiles, nmt, a.kmax, kk, Mh, L.pv, L.pi, L.bound, bo.hi, bo.lo)
+            if (op && use_bo)
+                MD_NARROW(true, true);
+            else if (op)
+                MD_NARROW(true, false);
+            else if (use_bo)
+                MD_NARROW(false, true);
             else
-                hipLaunchKernelGGL((k_vocab_mfma_narrow<2, false>), grid, dim3(BLOCK), 0, s, UA, L.hhi, L.hlo, rows_v,
-                                   a.d, a.V, nh_u, head0, vtiles, nmt, a.kmax, kk, Mh, L.pv, L.pi, L.bound);
+                MD_NARROW(false, false);
+#undef MD_NARROW
         }
         *nlists = vtiles;
     } else {  // many rows: one product and the certificate
