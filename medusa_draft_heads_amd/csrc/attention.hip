@@ -18,7 +18,8 @@
 // ranges by log-sum-exp.
 //
 // bf16 storage runs on the matrix cores (v_mfma_f32_16x16x32_bf16): a wave
-// owns 16 query rows and computes S^T = K Q^T per 16-key block, then
+// owns one or two groups of 16 query rows and computes, per group,
+// S^T = K Q^T per 16-key block, then
 // O^T += V^T P^T. In this orientation a lane keeps one query row (lane % 16)
 // in both the score and the output accumulators, so the running max, the
 // rescale and the bf16 P operand never leave the lane. K and V tiles of 32
@@ -43,7 +44,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 
 constexpr int QT = 16;  // query rows per block (FMA kernel)
-constexpr int MQT = 64; // query rows per block (MFMA kernel: 4 waves x 16)
+constexpr int MQT1 = 64;  // query rows per block of the MFMA kernel per 16-row group a wave holds (4 waves)
 constexpr int DKT = 32; // keys per tile (MFMA kernel)
 constexpr int KT = 64;  // keys per tile
 constexpr int BLOCK = 256;
@@ -287,14 +288,15 @@ __device__ __forceinline__ u32x2 lds_tr4(const unsigned char* p) {
     return __builtin_bit_cast(u32x2, v);
 }
 
-// One block: 64 query rows (4 waves x 16) of one (request, kv head) against
-// the keys [k0, k1) of its split, DKT keys a tile. K and V tiles go from
+// One block: 64 RG query rows (4 waves x RG groups of 16) of one (request,
+// kv head) against the keys [k0, k1) of its split, DKT keys a tile; with RG
+// = 2 every K and V fragment a wave reads from LDS serves both its groups. K and V tiles go from
 // memory straight into LDS (buffer->LDS loads, 16 bytes a lane, one
 // instruction per 1 KB piece) in three separately named stage buffers with
 // two tiles in flight, so no register staging, no transposing writes and one
 // barrier per tile.
-template <int HD>
-__global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int Hkv, int Lcap, int max_len,
+template <int HD, int RG>
+__global__ __launch_bounds__(BLOCK, RG == 1 ? 3 : 2) void k_attn_mfma(DevTree t, int Hq, int Hkv, int Lcap, int max_len,
                                                      const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
                                                      const uint16_t* __restrict__ Vc, const int32_t* __restrict__ lens,
                                                      float scale, int splits, int chunk, int qtiles, int ngroups,
@@ -327,24 +329,39 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
     const int g4 = lane >> 4, c16 = lane & 15;
     const int64_t kvbase = ((int64_t)b * Hkv + g) * Lcap;
 
-    // this lane's query row (the N index of both products)
-    const int r = qt * MQT + w * 16 + c16;
-    const bool rvalid = r < rows;
-    const int node = rvalid ? r / group : 0;
-    const int h = g * group + (rvalid ? r - (r / group) * group : 0);
-    const uint64_t anc = rvalid ? t.anc[node] : 0ull;
-    const int64_t qrow = (((int64_t)b * N + node) * Hq + h) * HD;
-    bf16x8 qf[HD / 32];
+    // this lane's query rows (the N index of both products): one in each of
+    // the wave's RG groups of 16 rows, which share every K and V fragment
+    static_assert(RG == 1 || RG == 2, "one or two 16-row groups a wave");
+    constexpr int MQT = MQT1 * RG;  // query rows per block
+    bool rvalid[RG];
+    int node[RG], hq[RG];
+    uint64_t anc[RG];
+    bf16x8 qf[RG][HD / 32];
 #pragma unroll
-    for (int c = 0; c < HD / 32; ++c) {
-        const u32x4 v = rvalid ? *reinterpret_cast<const u32x4*>(q + qrow + 8 * g4 + 32 * c) : u32x4{0u, 0u, 0u, 0u};
-        qf[c] = __builtin_bit_cast(bf16x8, v);
+    for (int gi = 0; gi < RG; ++gi) {
+        const int r = qt * MQT + (w * RG + gi) * 16 + c16;
+        rvalid[gi] = r < rows;
+        node[gi] = rvalid[gi] ? r / group : 0;
+        hq[gi] = g * group + (rvalid[gi] ? r - (r / group) * group : 0);
+        anc[gi] = rvalid[gi] ? t.anc[node[gi]] : 0ull;
+        const int64_t qrow = (((int64_t)b * N + node[gi]) * Hq + hq[gi]) * HD;
+#pragma unroll
+        for (int c = 0; c < HD / 32; ++c) {
+            const u32x4 v =
+                rvalid[gi] ? *reinterpret_cast<const u32x4*>(q + qrow + 8 * g4 + 32 * c) : u32x4{0u, 0u, 0u, 0u};
+            qf[gi][c] = __builtin_bit_cast(bf16x8, v);
+        }
     }
     const float scale_log2 = scale * 1.44269504088896340736f;
-    float m_i = -INFINITY, l_i = 0.f;
-    f32x4 o[HD / 16];
+    float m_i[RG], l_i[RG];
+    f32x4 o[RG][HD / 16];
 #pragma unroll
-    for (int j = 0; j < HD / 16; ++j) o[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int gi = 0; gi < RG; ++gi) {
+        m_i[gi] = -INFINITY;
+        l_i[gi] = 0.f;
+#pragma unroll
+        for (int j = 0; j < HD / 16; ++j) o[gi][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
 
     // keys past nkeys read as zero (and are masked); the cache rows of this
     // (request, kv head) bound every load
@@ -371,73 +388,81 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
 
     auto compute = [&](int kt0, const unsigned char* sK) {
         const unsigned char* sV = sK + TILEB;
-        // S^T for two 16-key blocks: st[kb][i] = S[row][kt0 + 16 kb + 4 g4 + i]
-        f32x4 st[2];
+        // S^T for two 16-key blocks: st[gi][kb][i] = S[row of group gi][kt0 + 16 kb + 4 g4 + i]
+        f32x4 st[RG][2];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            st[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int gi = 0; gi < RG; ++gi) st[gi][kb] = f32x4{0.f, 0.f, 0.f, 0.f};
             const int key = 16 * kb + c16;
 #pragma unroll
             for (int c = 0; c < HD / 32; ++c) {
                 const bf16x8 a = __builtin_bit_cast(
                     bf16x8, *reinterpret_cast<const u32x4*>(sK + key * ROWB + 16 * ((g4 + 4 * c) ^ swzK<CPR>(key))));
-                st[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[c], st[kb], 0, 0, 0);
+#pragma unroll
+                for (int gi = 0; gi < RG; ++gi)
+                    st[gi][kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[gi][c], st[gi][kb], 0, 0, 0);
             }
         }
         // scores in the log2 domain: s = scale * log2(e) * q.k, so that
         // e^{scale q.k - m} = 2^{s - m'} with the native exp2
-        float p[2][4];
-        float tmax = -INFINITY;
-        if (kt0 + DKT <= k1 && kt0 + DKT <= L) {
-            // the whole tile lies in the cached prefix: every key is visible
+        const bool in_prefix = kt0 + DKT <= k1 && kt0 + DKT <= L;  // every key of the tile is visible
+        bf16x8 pb[RG];
+#pragma unroll
+        for (int gi = 0; gi < RG; ++gi) {
+            float p[2][4];
+            float tmax = -INFINITY;
+            if (in_prefix) {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        p[kb][i] = st[gi][kb][i] * scale_log2;
+                        tmax = fmaxf(tmax, p[kb][i]);
+                    }
+            } else {
+#pragma unroll
+                for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int kidx = kt0 + kb * 16 + 4 * g4 + i;
+                        bool vis = kidx < k1;
+                        if (vis && kidx >= L) vis = (anc[gi] >> (kidx - L)) & 1ull;
+                        p[kb][i] = vis ? st[gi][kb][i] * scale_log2 : -INFINITY;
+                        tmax = fmaxf(tmax, p[kb][i]);
+                    }
+                }
+            }
+            // Lazy reference: P = 2^(s - m_i) with m_i the row's reference,
+            // moved only when a score passes it by more than 8 (P stays below
+            // 2^8); the four lanes of a row always share m_i. l_i sums this
+            // lane's keys only (one reduction at the end).
+            if (__ballot(tmax > m_i[gi] + 8.f)) {
+                tmax = fmaxf(tmax, xor16(tmax));
+                tmax = fmaxf(tmax, xor32(tmax));
+                if (tmax > m_i[gi]) {  // the same for the row's four lanes
+                    const float alpha = __builtin_amdgcn_exp2f(m_i[gi] - tmax);  // 0 while m_i is -inf
+                    l_i[gi] *= alpha;
+#pragma unroll
+                    for (int j = 0; j < HD / 16; ++j) o[gi][j] *= alpha;
+                    m_i[gi] = tmax;
+                }
+            }
+            const float mref = m_i[gi] == -INFINITY ? 0.f : m_i[gi];  // rows with no visible key yet
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    p[kb][i] = st[kb][i] * scale_log2;
-                    tmax = fmaxf(tmax, p[kb][i]);
+                    p[kb][i] = __builtin_amdgcn_exp2f(p[kb][i] - mref);
+                    l_i[gi] += p[kb][i];
                 }
-        } else {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int kidx = kt0 + kb * 16 + 4 * g4 + i;
-                    bool vis = kidx < k1;
-                    if (vis && kidx >= L) vis = (anc >> (kidx - L)) & 1ull;
-                    p[kb][i] = vis ? st[kb][i] * scale_log2 : -INFINITY;
-                    tmax = fmaxf(tmax, p[kb][i]);
-                }
-            }
+            // P^T operand: k index 8 g4 + e is key 4 g4 + e (e < 4) or 16 +
+            // 4 g4 + e - 4 (e >= 4), as in the V^T operand below
+            pb[gi] = bf16x8{(__bf16)p[0][0], (__bf16)p[0][1], (__bf16)p[0][2], (__bf16)p[0][3],
+                            (__bf16)p[1][0], (__bf16)p[1][1], (__bf16)p[1][2], (__bf16)p[1][3]};
         }
-        // Lazy reference: P = 2^(s - m_i) with m_i the row's reference, moved
-        // only when a score passes it by more than 8 (P stays below 2^8); the
-        // four lanes of a row always share m_i. l_i sums this lane's keys
-        // only (one reduction at the end).
-        if (__ballot(tmax > m_i + 8.f)) {
-            tmax = fmaxf(tmax, xor16(tmax));
-            tmax = fmaxf(tmax, xor32(tmax));
-            if (tmax > m_i) {  // the same for the row's four lanes
-                const float alpha = __builtin_amdgcn_exp2f(m_i - tmax);  // 0 while m_i is -inf
-                l_i *= alpha;
-#pragma unroll
-                for (int j = 0; j < HD / 16; ++j) o[j] *= alpha;
-                m_i = tmax;
-            }
-        }
-        const float mref = m_i == -INFINITY ? 0.f : m_i;  // rows with no visible key yet
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                p[kb][i] = __builtin_amdgcn_exp2f(p[kb][i] - mref);
-                l_i += p[kb][i];
-            }
 
-        // O^T += V^T P^T over the tile's 32 keys: operand k index 8 g4 + e is
-        // key 4 g4 + e (e < 4) or 16 + 4 g4 + e - 4 (e >= 4), in both operands
-        const bf16x8 pb = {(__bf16)p[0][0], (__bf16)p[0][1], (__bf16)p[0][2], (__bf16)p[0][3],
-                           (__bf16)p[1][0], (__bf16)p[1][1], (__bf16)p[1][2], (__bf16)p[1][3]};
+        // O^T += V^T P^T over the tile's 32 keys, each V^T fragment shared by the groups
         const int vk = 4 * g4 + (c16 >> 2);  // the key this lane addresses (first 16-key block)
         const int vq = c16 & 3;
 #pragma unroll
@@ -446,7 +471,9 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
             const u32x2 lo = lds_tr4(sV + vk * ROWB + 16 * (ch ^ swzV<CPR>(vk)) + bo);
             const u32x2 hi = lds_tr4(sV + (vk + 16) * ROWB + 16 * (ch ^ swzV<CPR>(vk + 16)) + bo);
             const bf16x8 a = __builtin_bit_cast(bf16x8, u32x4{lo.x, lo.y, hi.x, hi.y});
-            o[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb, o[j], 0, 0, 0);
+#pragma unroll
+            for (int gi = 0; gi < RG; ++gi)
+                o[gi][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[gi], o[gi][j], 0, 0, 0);
         }
     };
 
@@ -478,41 +505,45 @@ __global__ __launch_bounds__(BLOCK, 3) void k_attn_mfma(DevTree t, int Hq, int H
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads land before the block ends
     }
 
-    l_i += xor16(l_i);  // the row's sum over its four lanes
-    l_i += xor32(l_i);
-    // the key range's output row normalised (o / l, bounded by max |V|) and
-    // scaled by a power of two 2^-ex that puts its largest entry in
-    // [2^14, 2^15), stored as 16-bit floats: half the bytes of the split's
-    // partial rows, no overflow past the 16-bit range whatever the size of
-    // V, and the full 11-bit precision for every entry within 2^-28 of the
-    // row's largest. 2^ex travels beside the row.
-    const float inv = l_i > 0.f ? 1.f / l_i : 0.f;
-    float amax = 0.f;
 #pragma unroll
-    for (int j = 0; j < HD / 16; ++j)
+    for (int gi = 0; gi < RG; ++gi) {
+        float li = l_i[gi];
+        li += xor16(li);  // the row's sum over its four lanes
+        li += xor32(li);
+        // the key range's output row normalised (o / l, bounded by max |V|) and
+        // scaled by a power of two 2^-ex that puts its largest entry in
+        // [2^14, 2^15), stored as 16-bit floats: half the bytes of the split's
+        // partial rows, no overflow past the 16-bit range whatever the size of
+        // V, and the full 11-bit precision for every entry within 2^-28 of the
+        // row's largest. 2^ex travels beside the row.
+        const float inv = li > 0.f ? 1.f / li : 0.f;
+        float amax = 0.f;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(o[j][e] * inv));
-    amax = fmaxf(amax, xor16(amax));
-    amax = fmaxf(amax, xor32(amax));
-    // floor(log2 amax) from the exponent field (0 for zero and subnormal rows)
-    const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xffu);
-    const int ex = ebits == 0 ? 0 : min(max(ebits - 127 - 14, -126), 127);
-    const float sc = inv * __uint_as_float((uint32_t)(127 - ex) << 23 & 0x7f800000u);
-    if (rvalid) {
-        const int64_t row = ((int64_t)b * N + node) * Hq + h;
+        for (int j = 0; j < HD / 16; ++j)
 #pragma unroll
-        for (int j = 0; j < HD / 16; ++j) {
-            const f32x4 v = o[j] * sc;
-            const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
-            const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
-            *reinterpret_cast<u32x2*>(po + (row * splits + s) * HD + 16 * j + 4 * g4) = u32x2{w0, w1};
-        }
-        if (g4 == 0) {
-            pm[row * splits + s] = m_i;
-            pl[row * splits + s] = l_i;
-            pe[row * splits + s] = ldexpf(1.f, ex);
+            for (int e = 0; e < 4; ++e) amax = fmaxf(amax, fabsf(o[gi][j][e] * inv));
+        amax = fmaxf(amax, xor16(amax));
+        amax = fmaxf(amax, xor32(amax));
+        // floor(log2 amax) from the exponent field (0 for zero and subnormal rows)
+        const int ebits = (int)((__float_as_uint(amax) >> 23) & 0xffu);
+        const int ex = ebits == 0 ? 0 : min(max(ebits - 127 - 14, -126), 127);
+        const float sc = inv * __uint_as_float((uint32_t)(127 - ex) << 23 & 0x7f800000u);
+        if (rvalid[gi]) {
+            const int64_t row = ((int64_t)b * N + node[gi]) * Hq + hq[gi];
+#pragma unroll
+            for (int j = 0; j < HD / 16; ++j) {
+                const f32x4 v = o[gi][j] * sc;
+                const uint32_t w0 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[0]) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[1]) << 16);
+                const uint32_t w1 = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[2]) |
+                                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v[3]) << 16);
+                *reinterpret_cast<u32x2*>(po + (row * splits + s) * HD + 16 * j + 4 * g4) = u32x2{w0, w1};
+            }
+            if (g4 == 0) {
+                pm[row * splits + s] = m_i[gi];
+                pl[row * splits + s] = li;
+                pe[row * splits + s] = ldexpf(1.f, ex);
+            }
         }
     }
 }
@@ -573,12 +604,18 @@ hipError_t launch_typed(const DevTree& t, int B, int Hq, int Hkv, int hd, int Lc
     if constexpr (sizeof(T) == 2) {
         const int ngroups = B * Hkv * p.splits;
         const dim3 mgrid((unsigned)(8 * p.qtiles * ((ngroups + 7) / 8)));
-        if (hd == 64)
-            hipLaunchKernelGGL(k_attn_mfma<64>, mgrid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv,
-                               lens, scale, p.splits, p.chunk, p.qtiles, ngroups, po, pm, pl, pe);
+#define MD_ATTN(HDV, RGV)                                                                                  \
+    hipLaunchKernelGGL((k_attn_mfma<HDV, RGV>), mgrid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv, lens, \
+                       scale, p.splits, p.chunk, p.qtiles, ngroups, po, pm, pl, pe)
+        if (hd == 64 && p.rg == 2)
+            MD_ATTN(64, 2);
+        else if (hd == 64)
+            MD_ATTN(64, 1);
+        else if (p.rg == 2)
+            MD_ATTN(128, 2);
         else
-            hipLaunchKernelGGL(k_attn_mfma<128>, mgrid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv,
-                               lens, scale, p.splits, p.chunk, p.qtiles, ngroups, po, pm, pl, pe);
+            MD_ATTN(128, 1);
+#undef MD_ATTN
     } else {
         if (hd == 64)
             hipLaunchKernelGGL((k_attn_fma<T, 64>), grid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv,
@@ -595,15 +632,18 @@ hipError_t launch_typed(const DevTree& t, int B, int Hq, int Hkv, int hd, int Lc
 }
 
 // resident blocks per CU of the kernel that will run (one round of blocks)
-int attention_occupancy(int dt, int hd) {
+int attention_occupancy(int dt, int hd, int rg) {
     int n = 0;
     hipError_t e;
     if (dt == 0)
         e = hd == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_fma<float, 64>, BLOCK, 0)
                      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_fma<float, 128>, BLOCK, 0);
+    else if (rg == 2)
+        e = hd == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_mfma<64, 2>, BLOCK, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_mfma<128, 2>, BLOCK, 0);
     else
-        e = hd == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_mfma<64>, BLOCK, 0)
-                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_mfma<128>, BLOCK, 0);
+        e = hd == 64 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_mfma<64, 1>, BLOCK, 0)
+                     : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k_attn_mfma<128, 1>, BLOCK, 0);
     if (e != hipSuccess || n < 1) n = 2;
     return n;
 }
@@ -612,14 +652,21 @@ int attention_occupancy(int dt, int hd) {
 
 AttnPlan attention_plan(int dt, int B, int N, int Hq, int Hkv, int hd, int max_len) {
     AttnPlan p;
-    const int qt = dt == 0 ? QT : MQT;
-    const int kt = dt == 0 ? KT : DKT;
     p.rows = N * (Hq / Hkv);
+    // Two 16-row query groups a wave (each K and V fragment read from LDS
+    // serves both) once there are at least 128 query tiles of 64 rows: at
+    // batch 4 (Hydra, L = 8,192) attention + combine 59.5 -> 53.0 us, at
+    // batch 8 98.7 -> 89.8 us; at batch 1 (70B shape, 64 tiles) the fewer,
+    // longer blocks gain nothing and the extra key ranges cost the combine
+    // (28.0 -> 30.3 us), so one group there.
+    p.rg = dt == 0 ? 1 : (B * Hkv * ((p.rows + MQT1 - 1) / MQT1) >= 128 ? 2 : 1);
+    const int qt = dt == 0 ? QT : MQT1 * p.rg;
+    const int kt = dt == 0 ? KT : DKT;
     p.qtiles = (p.rows + qt - 1) / qt;
     const int base = B * Hkv * p.qtiles;
     const int tiles = (max_len + N + kt - 1) / kt;
     // split the keys so that one round of resident blocks covers the grid
-    const int target = device_cus() * attention_occupancy(dt, hd);
+    const int target = device_cus() * attention_occupancy(dt, hd, p.rg);
     int splits = target / base;
     // short ranges cost more in the split (partial rows written and combined)
     // than they gain in parallelism: under 8 tiles a range on average, half as

@@ -113,6 +113,7 @@ struct AttnPlan {
     int chunk;      // keys per split (multiple of the key tile)
     int qtiles;     // query tiles per (request, kv head)
     int rows;       // query rows per (request, kv head) = N * Hq / Hkv
+    int rg;         // 16-row query groups per wave of the matrix-core kernel (1 or 2)
 };
 AttnPlan attention_plan(int dt, int B, int N, int Hq, int Hkv, int hd, int max_len);
 size_t attention_ws_bytes(int dt, int B, int N, int Hq, int Hkv, int hd, int max_len);
