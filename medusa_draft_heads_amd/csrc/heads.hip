@@ -435,11 +435,13 @@ __device__ __forceinline__ int lidx(const int* p, int64_t i) {
     return p[i];
 }
 
-template <int LPT, bool COH>
+// KM: the register lists' length, at least k (4, 8 or 16: a shorter list
+// makes each pop of a winner's head cheaper).
+template <int LPT, bool COH, int KM = MD_MAX_TOPK_DEV>
 __device__ __forceinline__ void merge_lists(const float* __restrict__ part_val, const int* __restrict__ part_idx,
                                             int64_t base, int nlists, int k, int kmax, int32_t* __restrict__ out_idx,
                                             float* __restrict__ out_val) {
-    constexpr int KM = MD_MAX_TOPK_DEV;
+    static_assert(KM <= MD_MAX_TOPK_DEV, "no longer than a head's list");
     __shared__ float wl_v[NWAVE][KM];
     __shared__ int wl_i[NWAVE][KM];
     const int tid = threadIdx.x, lane = tid & (MD_WAVE - 1), w = tid >> 6;
@@ -545,7 +547,7 @@ __device__ __forceinline__ void merge_lists(const float* __restrict__ part_val, 
 
 // One block per (row m, head slot hh): the k best of the head are the k-way
 // merge of the sorted lists every block of the vocabulary kernel left.
-template <int LPT>
+template <int LPT, int KM>
 __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ part_val,
                                                       const int* __restrict__ part_idx, int M, int nh, int nlists,
                                                       KK kk, int kmax, int32_t* __restrict__ topk_idx,
@@ -553,7 +555,7 @@ __global__ __launch_bounds__(BLOCK) void k_topk_merge(const float* __restrict__ 
     const int m = blockIdx.x / nh, hh = blockIdx.x - (blockIdx.x / nh) * nh;
     const int64_t base = ((int64_t)hh * M + m) * nlists * kmax;
     const int64_t o = ((int64_t)m * nh + hh) * kmax;
-    merge_lists<LPT, false>(part_val, part_idx, base, nlists, kk.at(hh), kmax, topk_idx + o, topk_val + o);
+    merge_lists<LPT, false, KM>(part_val, part_idx, base, nlists, kk.at(hh), kmax, topk_idx + o, topk_val + o);
 }
 
 // ---- one launch for the heads of one row (Medusa, bf16) ----
@@ -816,21 +818,33 @@ Plan make_plan(int dt, int M, int d, int din, int nh, int shared_u) {
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // The k-way merge of nlists sorted lists per (row, head).
+template <int KM>
+void launch_merge_km(int lpt, const float* pv, const int* pi, int M, int nh, int nlists, KK kk, int kmax,
+                     int32_t* topk_idx, float* topk_val, hipStream_t s) {
+    if (lpt <= 1)
+        hipLaunchKernelGGL((k_topk_merge<1, KM>), dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax,
+                           topk_idx, topk_val);
+    else if (lpt == 2)
+        hipLaunchKernelGGL((k_topk_merge<2, KM>), dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax,
+                           topk_idx, topk_val);
+    else if (lpt <= 4)
+        hipLaunchKernelGGL((k_topk_merge<4, KM>), dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax,
+                           topk_idx, topk_val);
+    else
+        hipLaunchKernelGGL((k_topk_merge<0, KM>), dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax,
+                           topk_idx, topk_val);
+}
 hipError_t launch_merge(const float* pv, const int* pi, int M, int nh, int nlists, KK kk, int kmax, int32_t* topk_idx,
                         float* topk_val, hipStream_t s) {
     const int lpt = (nlists + BLOCK - 1) / BLOCK;
-    if (lpt <= 1)
-        hipLaunchKernelGGL(k_topk_merge<1>, dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax, topk_idx,
-                           topk_val);
-    else if (lpt == 2)
-        hipLaunchKernelGGL(k_topk_merge<2>, dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax, topk_idx,
-                           topk_val);
-    else if (lpt <= 4)
-        hipLaunchKernelGGL(k_topk_merge<4>, dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax, topk_idx,
-                           topk_val);
+    int kbig = 1;  // the largest k of the call's heads
+    for (int i = 0; i < nh && i < 8; ++i) kbig = std::max(kbig, kk.v[i]);
+    if (kbig <= 4)
+        launch_merge_km<4>(lpt, pv, pi, M, nh, nlists, kk, kmax, topk_idx, topk_val, s);
+    else if (kbig <= 8)
+        launch_merge_km<8>(lpt, pv, pi, M, nh, nlists, kk, kmax, topk_idx, topk_val, s);
     else
-        hipLaunchKernelGGL(k_topk_merge<0>, dim3(M * nh), dim3(BLOCK), 0, s, pv, pi, M, nh, nlists, kk, kmax, topk_idx,
-                           topk_val);
+        launch_merge_km<16>(lpt, pv, pi, M, nh, nlists, kk, kmax, topk_idx, topk_val, s);
     return hipGetLastError();
 }
 
