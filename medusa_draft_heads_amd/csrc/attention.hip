@@ -549,16 +549,10 @@ __global__ __launch_bounds__(BLOCK, RG == 1 ? 3 : 2) void k_attn_mfma(DevTree t,
 }
 
 // out = sum_s 2^{m_s - M} o_s / sum_s 2^{m_s - M} l_s  (M = max_s m_s; the row
-// statistics are kept in the log2 domain). P = float: o_s as accumulated;
-// P = uint16_t: o_s / (l_s 2^{e_s}) as 16-bit floats with 2^{e_s} in pe (the
-// matrix-core kernel's rows).
-__device__ __forceinline__ float partial_o(const float* po, int64_t i, float l, float) { return po[i]; }
-__device__ __forceinline__ float partial_o(const uint16_t* po, int64_t i, float l, float sc) {
-    return (l * sc) * (float)__builtin_bit_cast(_Float16, po[i]);
-}
-template <typename T, typename P>
-__global__ void k_attn_combine(int hd, int splits, const P* __restrict__ po, const float* __restrict__ pm,
-                               const float* __restrict__ pl, const float* __restrict__ pe, T* __restrict__ out) {
+// statistics are kept in the log2 domain). float32 rows (the FMA kernel's): o_s
+// as accumulated, one block per query row.
+__global__ void k_attn_combine(int hd, int splits, const float* __restrict__ po, const float* __restrict__ pm,
+                               const float* __restrict__ pl, float* __restrict__ out) {
     const int64_t row = blockIdx.x;
     const int c = threadIdx.x;
     float M = -INFINITY;
@@ -569,12 +563,74 @@ __global__ void k_attn_combine(int hd, int splits, const P* __restrict__ po, con
     for (int s = 0; s < splits; ++s) {
         const float ms = pm[row * splits + s];
         const float wgt = ms == -INFINITY ? 0.f : exp2f(ms - M);
-        const float ls = pl[row * splits + s];
-        const float sc = pe ? pe[row * splits + s] : 1.f;
-        num = fmaf(wgt, partial_o(po, (row * splits + s) * hd + c, ls, sc), num);
-        den = fmaf(wgt, ls, den);
+        num = fmaf(wgt, po[(row * splits + s) * hd + c], num);
+        den = fmaf(wgt, pl[row * splits + s], den);
     }
-    st(out, row * hd + c, num / den);
+    out[row * hd + c] = num / den;
+}
+
+// The matrix-core kernel's rows: o_s / (l_s 2^{e_s}) as 16-bit floats, 2^{e_s}
+// in pe. A thread owns 8 consecutive dimensions (one 16-byte load per range)
+// of one row, HD / 8 threads a row, 256 / (HD / 8) rows a block; the ranges'
+// rows and statistics are loaded 8 ranges at a time before they are merged
+// with a running maximum (out = num / den as above, reached by rescaling
+// num and den whenever the maximum rises).
+template <int HD>
+__global__ __launch_bounds__(256) void k_attn_combine16(int64_t R, int splits, const uint16_t* __restrict__ po,
+                                                        const float* __restrict__ pm, const float* __restrict__ pl,
+                                                        const float* __restrict__ pe, uint16_t* __restrict__ out) {
+    constexpr int CPR = HD / 8, RPB = 256 / CPR;
+    const int64_t row = (int64_t)blockIdx.x * RPB + threadIdx.x / CPR;
+    const int c = threadIdx.x % CPR;
+    if (row >= R) return;
+    const int64_t sb = row * splits;
+    float M = -INFINITY, den = 0.f;
+    float num[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) num[e] = 0.f;
+    for (int s0 = 0; s0 < splits; s0 += 8) {
+        float ms[8], ls[8], es[8];
+        u32x4 ov[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const bool ok = s0 + j < splits;
+            const int64_t i = sb + (ok ? s0 + j : 0);
+            ms[j] = ok ? pm[i] : -INFINITY;
+            ls[j] = ok ? pl[i] : 0.f;
+            es[j] = ok ? pe[i] : 0.f;
+            ov[j] = ok ? *reinterpret_cast<const u32x4*>(po + i * HD + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (ms[j] == -INFINITY) continue;  // a range with no visible key adds nothing
+            if (ms[j] > M) {
+                const float a = M == -INFINITY ? 0.f : exp2f(M - ms[j]);
+                den *= a;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) num[e] *= a;
+                M = ms[j];
+            }
+            const float wl = exp2f(ms[j] - M) * ls[j];
+            den += wl;
+            const float f = wl * es[j];
+            const uint32_t wd[4] = {ov[j].x, ov[j].y, ov[j].z, ov[j].w};
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint16_t hbits = (uint16_t)(wd[e >> 1] >> (16 * (e & 1)));
+                num[e] = fmaf(f, (float)__builtin_bit_cast(_Float16, hbits), num[e]);
+            }
+        }
+    }
+    const float inv = den > 0.f ? 1.f / den : 0.f;
+    uint32_t wo[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+        uint32_t u0 = __float_as_uint(num[2 * h] * inv), u1 = __float_as_uint(num[2 * h + 1] * inv);
+        u0 += 0x7FFFu + ((u0 >> 16) & 1u);  // round to nearest even bf16
+        u1 += 0x7FFFu + ((u1 >> 16) & 1u);
+        wo[h] = (u0 >> 16) | (u1 & 0xffff0000u);
+    }
+    *reinterpret_cast<u32x4*>(out + row * HD + 8 * c) = u32x4{wo[0], wo[1], wo[2], wo[3]};
 }
 
 inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -626,8 +682,19 @@ hipError_t launch_typed(const DevTree& t, int B, int Hq, int Hkv, int hd, int Lc
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_attn_combine<T, P>), dim3((unsigned)R), dim3(hd), 0, st_, hd, p.splits, po, pm, pl, pe,
-                       reinterpret_cast<T*>(out));
+    if constexpr (kHalfRows) {
+        const int64_t rpb = 256 / (hd / 8);
+        const dim3 cgrid((unsigned)((R + rpb - 1) / rpb));
+        if (hd == 64)
+            hipLaunchKernelGGL(k_attn_combine16<64>, cgrid, dim3(256), 0, st_, R, p.splits, po, pm, pl, pe,
+                               reinterpret_cast<uint16_t*>(out));
+        else
+            hipLaunchKernelGGL(k_attn_combine16<128>, cgrid, dim3(256), 0, st_, R, p.splits, po, pm, pl, pe,
+                               reinterpret_cast<uint16_t*>(out));
+    } else {
+        hipLaunchKernelGGL(k_attn_combine, dim3((unsigned)R), dim3(hd), 0, st_, hd, p.splits, po, pm, pl,
+                           reinterpret_cast<float*>(out));
+    }
     return hipGetLastError();
 }
 
