@@ -30,6 +30,7 @@
 // hand. float32 storage (small workloads) uses an LDS-tiled FMA kernel.
 #include <math.h>
 
+#include <algorithm>
 #include <mutex>
 #include <type_traits>
 
@@ -732,8 +733,15 @@ AttnPlan attention_plan(int dt, int B, int N, int Hq, int Hkv, int hd, int max_l
     p.qtiles = (p.rows + qt - 1) / qt;
     const int base = B * Hkv * p.qtiles;
     const int tiles = (max_len + N + kt - 1) / kt;
-    // split the keys so that one round of resident blocks covers the grid
-    const int target = device_cus() * attention_occupancy(dt, hd, p.rg);
+    // split the keys so that one round of resident blocks covers the grid;
+    // one-group waves at two blocks a CU, though three fit: with every CU
+    // holding the same number of blocks, fewer and longer ranges cost less
+    // than the third block gains (70B shape, B = 1, L = 4,096, attention +
+    // combine: 12 ranges 28.9 us, 8 ranges 25.7; 8B shape 17.5 -> 14.9 by
+    // the halving below; 70B at L = 2,048 20.8 -> 19.9; 10 ranges, which
+    // leave half the CUs a third block, 29.9)
+    const int occ = attention_occupancy(dt, hd, p.rg);
+    const int target = device_cus() * (dt != 0 && p.rg == 1 ? std::min(occ, 2) : occ);
     int splits = target / base;
     // short ranges cost more in the split (partial rows written and combined)
     // than they gain in parallelism: under 8 tiles a range on average, half as
