@@ -77,6 +77,11 @@ ATTN_CASES = [
     ("8B-shaped bf16", "bf16", 1, ((10, 4, 2, 1), 64), 32, 8, 128, [2048]),
     ("70B-shaped bf16", "bf16", 1, ((10, 4, 2, 1), 64), 64, 8, 128, [4096]),
     ("Hydra-shaped bf16 batch 4", "bf16", 4, ((10, 4, 2, 1), 64), 32, 8, 128, [8192] * 4),
+    # one query head per kv head: few query tiles, so the keys split into
+    # 26 ranges (the combine merges them 8 at a time, then a partial 2)
+    ("many key ranges bf16", "bf16", 1, ((10, 4, 2, 1), 64), 8, 8, 128, [4096]),
+    # 32 ranges; the second request's 21 keys leave all ranges past the first empty
+    ("many ranges ragged bf16 hd64", "bf16", 2, ((4, 2, 2, 1), 16), 4, 4, 64, [3000, 5]),
 ]
 
 
