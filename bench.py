@@ -65,7 +65,9 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=-1,
+                    help="untimed steps before timing (default: as many as take 0.5 s; the clocks take a few "
+                         "hundred milliseconds of load to settle)")
     ap.add_argument("--workload", default="70b",
                     choices=["70b", "70b_chain", "8b", "tiny", "70b_b8", "hydra_b4", "70b_shared", "70b_lmhead",
                              "70b_sampled", "70b_typical"])
@@ -236,14 +238,12 @@ def main() -> int:
             b.record(stream)
     torch.cuda.synchronize()
 
-    # every step starts from the same cached lengths: each step index gets its
-    # own copy of its set's lengths, made before any timing (the step grows them)
-    lens_bank = [sets[i % len(sets)]["lens0"].clone() for i in range(args.warmup + 2 * args.steps)]
-    torch.cuda.synchronize()
+    # every step starts from its set's cached lengths: each step gets its own
+    # copy of them (the step grows them)
 
     def one_step(i: int, pairs=None, lm=None, lens=None):
         xd = dict(sets[i % len(sets)])
-        xd["lens"] = lens_bank[i] if lens is None else lens
+        xd["lens"] = lens
         for lvl in range(calls):
             if pairs is not None:
                 md.md_set_vocab_timing_events(pairs[lvl][0].cuda_event, pairs[lvl][1].cuda_event)
@@ -294,15 +294,28 @@ def main() -> int:
     mismatch = [i for i, c in enumerate(acc_check) if c == "DIFFERENT"]
     log("accepted lengths, GPU vs oracle, %d input sets: %s" % (len(acc_gpu), "all equal" if all(
         c == "equal" for c in acc_check) else acc_check))
-    for i in range(args.warmup):
-        one_step(i)
+    # warm-up: a fixed count, or by default steps until 0.5 s have passed (with
+    # 10 warm-up steps the first ~100 timed steps of the Hydra workload ran
+    # 1.03 ms against 0.91 ms once the clocks had settled); each step gets a
+    # fresh copy of its set's lengths
+    n_warm = 0
+    t_warm = time.perf_counter()
+    while (n_warm < args.warmup) if args.warmup >= 0 else (time.perf_counter() - t_warm < 0.5):
+        for _ in range(1 if args.warmup >= 0 else 10):
+            one_step(n_warm, lens=sets[n_warm % len(sets)]["lens0"].clone())
+            n_warm += 1
+        if args.warmup < 0:
+            torch.cuda.synchronize()
+    args.warmup = n_warm
+    # every timed step's own copy of its set's lengths, made before timing
+    lens_bank = [sets[(n_warm + i) % len(sets)]["lens0"].clone() for i in range(2 * args.steps)]
     torch.cuda.synchronize()
     # the timed steps: nothing but the steps between the two events (a HIP
     # event recorded between two kernels costs ~6 us of GPU time here)
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(args.steps):
-        one_step(args.warmup + i)
+        one_step(args.warmup + i, lens=lens_bank[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
@@ -312,7 +325,7 @@ def main() -> int:
     bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     bounds[0].record(stream)
     for i in range(args.steps):
-        one_step(args.warmup + args.steps + i, ev[i], lm_ev[i] if lm_ev else None)
+        one_step(args.warmup + args.steps + i, ev[i], lm_ev[i] if lm_ev else None, lens=lens_bank[args.steps + i])
         bounds[i + 1].record(stream)
     torch.cuda.synchronize()
     per_step = np.array([bounds[i].elapsed_time(bounds[i + 1]) for i in range(args.steps)])
