@@ -422,6 +422,120 @@ __device__ __forceinline__ void dmab_nt(__amdgpu_buffer_rsrc_t r, unsigned char*
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)dst, 16, off, 0, 0, 2);
 }
 
+// The residual over at most 16 activation rows (Hydra's first level, a few
+// Medusa rows): a block owns 16 rows of the heads' W (one MFMA row block)
+// over the whole contraction, its 8 waves splitting the contraction into 8
+// runs. Each wave streams its run of W and of the activation rows ([h ;
+// E[parent token]] for Hydra, gathered by row) straight into a ring of RP
+// register stages (16 bytes a lane per fragment: W from HBM, the activation
+// rows, shared by every block, from L2), then the 8 partial sums meet in LDS
+// and are added in wave order (the result does not depend on timing). No
+// partial sums go through memory and no second launch finishes them
+// (Hydra's 4-row level: 18.7 us against 17.6 + 4.7 for the split
+// contraction and its finish). Each block reads all its activation rows
+// from L2, 16 KB of them per 1 KB of W at d = 4,096, so the kernel stops
+// paying beyond one column block (32 and 72 rows: 26.8 and 34.2 us against
+// 23.9 and 29.2), where the split-contraction kernel runs instead. RC: 16-row
+// column blocks (1).
+constexpr int kRowsWaves = 8;  // waves of k_residual_rows
+constexpr int kRowsRing = 8;   // K steps in flight per wave
+template <int RC>
+__global__ __launch_bounds__(kRowsWaves * MD_WAVE) void k_residual_rows(
+    const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias, GemmRows rows, int M, int d, int din, int nh,
+    int head0, float* __restrict__ hres, float* __restrict__ hres_out, uint16_t* __restrict__ hhi,
+    uint16_t* __restrict__ hlo, int* __restrict__ bound, BoOut bo) {
+    constexpr int RP = kRowsRing;
+    __shared__ f32x4 red[kRowsWaves][RC][MD_WAVE];
+    __shared__ int s_tok[16 * RC];
+    __shared__ int s_b[16 * RC];
+    const int row0 = blockIdx.x * 16;  // over nh * d rows (d % 16 == 0: never straddles heads)
+    const int hh = row0 / d, r0 = row0 - hh * d;
+    const int tid = threadIdx.x, lane = tid & (MD_WAVE - 1);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int g4 = lane >> 4, c16 = lane & 15;
+    // the vocabulary kernel that follows keeps a lower bound of each (head,
+    // row)'s k-th best logit here; start from -inf
+    if (blockIdx.x == 0)
+        for (int j = tid; j < nh * M; j += kRowsWaves * MD_WAVE) bound[j] = f2o(-INFINITY);
+    if (tid < 16 * RC) {
+        const int m = tid;
+        int b = m, tok = -1;
+        if (rows.kind == 1 && m < M) {
+            b = m / rows.P;
+            const int p = rows.parents[m - b * rows.P];
+            tok = p == 0 ? rows.root_tok[b] : rows.tree_tok[(int64_t)b * rows.N + p];
+            if (tok < 0 || tok >= rows.V) tok = -1;  // out-of-vocabulary token: zero embedding
+        }
+        s_b[tid] = b;
+        s_tok[tid] = tok;
+    }
+    __syncthreads();
+
+    // This wave's run [kb, kb + kw) of the contraction lies wholly in h or
+    // in E's half (kw divides d). A: W rows row0 + c16, chunk g4 of each K
+    // step; B: activation row 16 cb + c16, chunk g4. Rows past M, and E rows
+    // of out-of-vocabulary tokens, get an offset past their buffer (2^31, far
+    // enough that adding a K offset cannot wrap it back): they load zeros.
+    const int kw = din / kRowsWaves, kb = w * kw;
+    const bool in_e = rows.kind == 1 && kb >= d;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(W + ((int64_t)head0 * d + row0) * din), 0, 16 * din * 2, RSRC3);
+    const __amdgpu_buffer_rsrc_t rB = in_e ? __builtin_amdgcn_make_buffer_rsrc((void*)rows.E, 0, 0x7FFFFFF0, RSRC3)
+                                           : __builtin_amdgcn_make_buffer_rsrc((void*)rows.h, 0, 0x7FFFFFF0, RSRC3);
+    static_assert(kRowsWaves * 32 * kRowsRing == 2048, "the applicability rule's din % 2048");
+    const uint32_t aoff = (uint32_t)c16 * din * 2 + (uint32_t)(kb + 8 * g4) * 2;
+    uint32_t boff[RC];
+#pragma unroll
+    for (int cb = 0; cb < RC; ++cb) {
+        const int m = 16 * cb + c16;
+        const int src = m >= M ? -1 : (in_e ? s_tok[m] : (rows.kind == 1 ? s_b[m] : m));
+        const int kk0 = in_e ? kb - d : kb;
+        boff[cb] = src < 0 ? 0x80000000u : (uint32_t)src * d * 2 + (uint32_t)(kk0 + 8 * g4) * 2;
+    }
+    u32x4 ra[RP], rb[RP][RC];
+    const int nst = kw / 32;  // K steps of the run (a multiple of RP)
+    auto issue = [&](int s, int j) {
+        const uint32_t ko = (uint32_t)min(s, nst - 1) * 64;
+        ra[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, aoff + ko, 0, 0);
+#pragma unroll
+        for (int cb = 0; cb < RC; ++cb)
+            rb[j][cb] = __builtin_amdgcn_raw_buffer_load_b128(rB, boff[cb] + ko, 0, 0);
+    };
+    f32x4 acc[RC];
+#pragma unroll
+    for (int cb = 0; cb < RC; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < RP; ++j) issue(j, j);
+    for (int s0 = 0; s0 < nst; s0 += RP) {
+#pragma unroll
+        for (int j = 0; j < RP; ++j) {
+#pragma unroll
+            for (int cb = 0; cb < RC; ++cb)
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[j]),
+                                                                  __builtin_bit_cast(bf16x8, rb[j][cb]), acc[cb], 0, 0,
+                                                                  0);
+            issue(s0 + j + RP, j);  // past the run: repeats its last step, never used
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads land before the wave goes on
+    // lane (g4, c16) holds z rows r0 + 4 g4 + i of activation row 16 cb + c16
+#pragma unroll
+    for (int cb = 0; cb < RC; ++cb) red[w][cb][lane] = acc[cb];
+    __syncthreads();
+    // thread t: 4 consecutive outputs (row quad g, activation row m)
+    if (tid < 4 * 16 * RC) {
+        const int g = tid / (16 * RC), m = tid - g * (16 * RC);
+        if (m < M) {
+            const int cb = m / 16, l = 16 * g + (m & 15);
+            f32x4 z = red[0][cb][l];
+#pragma unroll
+            for (int ww = 1; ww < kRowsWaves; ++ww) z += red[ww][cb][l];
+            residual_out(z, bias, rows, rows.kind == 0 ? m : s_b[m], M, d, head0, hh, m, r0 + 4 * g, hres, hres_out,
+                         hhi, hlo, bo);
+        }
+    }
+}
+
 // Operand order: a copy of a row-major [rows][d] bf16 matrix in which every
 // MFMA A fragment (16 rows x 32 contraction elements, 1 KB) is contiguous in
 // lane order (lane l: row l % 16, elements 8 (l / 16) .. + 7), laid out
@@ -1935,6 +2049,13 @@ int residual_ksplit(int M, int d, int din, int nh) {
     return ks;
 }
 
+// Up to 16 activation rows: k_residual_rows (16 rows of W a block, the whole
+// contraction, no split partials), where every gathered row offset fits the
+// 31-bit range its buffer loads address (E: V x d bf16).
+bool residual_rows(int M, int d, int din, int V) {
+    return M >= 1 && M <= 16 && din % 2048 == 0 && d % 16 == 0 && (din == d || (int64_t)V * d * 2 <= 0x7FF00000LL);
+}
+
 // Many Medusa rows with whole 256-row tiles of W and enough of them to fill
 // the GPU without a split contraction: the certified pass's pipeline
 // (k_residual_wide); otherwise the 128 x 128 register-staged tiles.
@@ -1969,7 +2090,7 @@ MfmaWs mfma_ws_layout(char* base, int M, int d, int din, int V, int nh, int kmax
         return p;
     };
     const size_t e = (size_t)nh * M * d, rows = (size_t)nh * M;
-    const int ks = residual_ksplit(M, d, din, nh);
+    const int ks = residual_rows(M, d, din, V) ? 1 : residual_ksplit(M, d, din, nh);
     L.hres = reinterpret_cast<float*>(take(e * 4));
     L.hhi = reinterpret_cast<uint16_t*>(take(e * 2));
     L.hlo = reinterpret_cast<uint16_t*>(take(e * 2));
@@ -2050,7 +2171,8 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     rows.tree_tok = a.tree_tok;
 
     const int units1 = a.nh * a.d / TR;
-    const int ksplit = residual_ksplit(a.M, a.d, a.din, a.nh);
+    const bool rows16 = residual_rows(a.M, a.d, a.din, a.V);
+    const int ksplit = rows16 ? 1 : residual_ksplit(a.M, a.d, a.din, a.nh);
     const uint16_t* bias = reinterpret_cast<const uint16_t*>(a.b);
     // one Medusa row (a shared projection) with an operand-order copy: the GEMV residual
     // (one pass over W, HBM-bound) writes h' and its hi/lo split for the
@@ -2072,6 +2194,11 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
         hipLaunchKernelGGL(k_residual_wide, dim3(8 * wm * ((wu + 7) / 8)), dim3(BLOCK), 0, s,
                            reinterpret_cast<const uint16_t*>(a.W), bias, rows, a.M, a.d, a.nh, a.head0, wm, L.hres,
                            a.h_res, L.hhi, L.hlo, L.bound);
+    } else if (rows16) {
+        const dim3 g((unsigned)(a.nh * a.d / 16)), blk(kRowsWaves * MD_WAVE);
+        const uint16_t* Wp = reinterpret_cast<const uint16_t*>(a.W);
+        hipLaunchKernelGGL(k_residual_rows<1>, g, blk, 0, s, Wp, bias, rows, a.M, a.d, a.din, a.nh, a.head0, L.hres,
+                           a.h_res, L.hhi, L.hlo, L.bound, bo);
     } else {
         hipLaunchKernelGGL(k_residual_mfma, dim3(ksplit * 8 * mtiles * ((units1 + 7) / 8)), dim3(BLOCK), 0, s,
                            reinterpret_cast<const uint16_t*>(a.W), bias, rows, a.M, a.d, a.din, a.nh, a.head0, mtiles,
