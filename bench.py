@@ -83,6 +83,9 @@ def main() -> int:
                     help="also keep operand-order copies of the vocabulary matrices for the few-row matrix-core "
                          "kernels (auto: bf16 Hydra levels, LM-head verification and the shared projection, where "
                          "2 to 128 projection columns meet them)")
+    ap.add_argument("--tile-norms", default="auto", choices=["auto", "on", "off"],
+                    help="also keep the vocabulary matrices' tile norms (md_vocab_tile_norms), which the many-row "
+                         "certified pass then reads instead of computing (auto: bf16 heads over more than 128 rows)")
     ap.add_argument("--seed", type=int, default=70)
     ap.add_argument("--cpu-1thread", type=int, default=1, help="also time one oracle step on one thread (0: skip)")
     args = ap.parse_args()
@@ -226,6 +229,12 @@ def main() -> int:
         wd.update(step.operand_order_weights(wd))
         torch.cuda.synchronize()
         log("operand-order copies: %s" % ", ".join(k for k in ("U_op", "Wt_op") if k in wd))
+    use_tn = args.tile_norms == "on" or (args.tile_norms == "auto" and wl.dtype == "bf16" and not hydra
+                                          and wl.M * (wl.K if wl.shared_u else 1) > 128)
+    if use_tn:  # made once with the weights, outside every timed region
+        wd.update(step.tile_norm_weights(wd))
+        torch.cuda.synchronize()
+        log("tile norms of U: %d floats" % wd["U_norms"].numel())
     stream = torch.cuda.current_stream()
     calls = depth if hydra else 1  # heads calls per step, each with its own event pair
     ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
@@ -254,7 +263,7 @@ def main() -> int:
             elif wl.verify == "sampled":
                 step.heads_logits(xd["h"], wd["W"], wd["b"], wd["U"])
             else:
-                step.heads(xd["h"], wd["W"], wd["b"], wd["U"], U_op=wd.get("U_op"))
+                step.heads(xd["h"], wd["W"], wd["b"], wd["U"], U_op=wd.get("U_op"), U_norms=wd.get("U_norms"))
             if pairs is not None:
                 md.md_set_vocab_timing_events(None, None)
         if wl.verify == "sampled":
@@ -463,7 +472,8 @@ def main() -> int:
         "config": {"workload": wl.name, "batch": wl.B, "d": wl.d, "V": wl.V, "heads": wl.K, "topk": list(wl.topk),
                    "tree_nodes": wl.N, "heads_rows_per_step": sum(head_rows), "Hq": wl.Hq, "Hkv": wl.Hkv,
                    "head_dim": wl.hd, "L": wl.L_max, "input_sets": len(sets),
-                   "weights_layout": "row-major + operand-order copy" if use_op else "row-major"},
+                   "weights_layout": "row-major + operand-order copy" if use_op else "row-major",
+                   "tile_norms": bool(use_tn)},
         "roofline": roofline,
         "step_hbm": {"bytes_per_step": step_bytes, "GBps": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 1),
                      "frac": round(step_bytes / (ms_per_step * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)},

@@ -138,6 +138,26 @@ size_t md_operand_order_bytes(int nmat, int rows, int cols);
  * (cols not a positive multiple of 32), MD_EHIP. */
 int md_operand_order(int nmat, int rows, int cols, const void* src, void* dst, void* stream);
 
+/* Tile norms of a vocabulary matrix, made once when the weights load.
+ *
+ * The many-row heads (more than 128 bf16 rows, e.g. 64 tree nodes x batch 8)
+ * run one bf16 product per logit and certify the top-k against a rounding
+ * allowance that scales with the largest row norm of U in each 256-row
+ * vocabulary tile ("What each one is", "Trees": the k best of each head's
+ * logits). Those norms depend on U alone; given this table the pass reads
+ * them instead of computing them on the matrix cores at every call.
+ * norms[mat][t] = max over rows v in [256 t, 256 t + 256) of the sum over
+ * j of U[mat][v][j]^2 (rows past V count 0), float32, computed from the bf16
+ * values (their squares are exact in float32; the sum's relative rounding
+ * error stays below 2^-16 for d <= 2^14, well inside the pass's margin). */
+/* Bytes of the table: nmat * ceil(V / 256) * 4; 0 when nmat or V < 1. */
+size_t md_vocab_tile_norms_bytes(int nmat, int V);
+/* Writes the table of U (device, bf16, [nmat][V][d]) to norms (device,
+ * md_vocab_tile_norms_bytes(...) bytes, caller-owned).
+ * Errors: MD_EINVAL (nmat or V < 1, NULL pointers), MD_EUNSUPPORTED (d not
+ * a positive multiple of 8), MD_EHIP. */
+int md_vocab_tile_norms(int nmat, int V, int d, const void* U, float* norms, void* stream);
+
 /* The draft heads and their top-k lists.
  *
  * Medusa (kind = MD_HEADS_MEDUSA, level = 0): for every row m < M of
@@ -173,11 +193,18 @@ int md_operand_order(int nmat, int rows, int cols, const void* src, void* dst, v
  * md_operand_order over the K matrices [V][d], or the one shared matrix).
  * With it the matrix-core path runs from 2 bf16 rows (else from 8) and its
  * few-row kernels (up to 128 rows) read U_op instead of U; the results are
- * the same bit for bit. MD_EINVAL if given with dt = MD_F32. */
+ * the same bit for bit. MD_EINVAL if given with dt = MD_F32.
+ *
+ * U_norms (optional, NULL for none): md_vocab_tile_norms of U (the K
+ * matrices, or the one shared matrix; bf16 only). The many-row certified pass
+ * then takes each tile's row norm from it instead of computing it; the lists
+ * are the same (they come from the exact re-scoring either way). MD_EINVAL
+ * if given with dt = MD_F32. A table that does not belong to U, or is too
+ * small, voids the certificate (undefined results, no fault). */
 int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t* k_per_head, int level,
                     const md_tree* tree, const void* h, const void* W, const void* b, const void* U, const void* U_op,
-                    const void* E, const int32_t* root_tok, const int32_t* tree_tok, int32_t* topk_idx,
-                    float* topk_val, float* h_res, void* ws, size_t ws_bytes, void* stream);
+                    const float* U_norms, const void* E, const int32_t* root_tok, const int32_t* tree_tok,
+                    int32_t* topk_idx, float* topk_val, float* h_res, void* ws, size_t ws_bytes, void* stream);
 
 /* The candidate tree's tokens and positions ("Trees").
  *

@@ -13,7 +13,8 @@ from ._lib import (MD_BF16, MD_F32, MD_HEADS_HYDRA, MD_HEADS_MEDUSA, MD_HEADS_ME
                    md_draft_sample, md_verify_sampled_workspace_bytes, md_tree_verify_sampled,
                    md_accept_typical_workspace_bytes, md_tree_accept_typical, md_operand_order_bytes,
                    md_operand_order, operand_order, md_certified_rounding_allowance, md_tree_attention_noalloc,
-                   md_tree_attention_noalloc_max_bytes, md_heads_fused, md_set_wait_limits)
+                   md_tree_attention_noalloc_max_bytes, md_heads_fused, md_set_wait_limits, md_vocab_tile_norms_bytes,
+                   md_vocab_tile_norms, vocab_tile_norms)
 from .step import MedusaStep, StepConfig
 
 __all__ = [
@@ -26,6 +27,6 @@ __all__ = [
     "md_verify_sampled_workspace_bytes", "md_tree_verify_sampled", "md_accept_typical_workspace_bytes",
     "md_tree_accept_typical", "md_operand_order_bytes", "md_operand_order", "operand_order",
     "md_certified_rounding_allowance", "md_tree_attention_noalloc", "md_tree_attention_noalloc_max_bytes",
-    "md_heads_fused", "md_set_wait_limits",
+    "md_heads_fused", "md_set_wait_limits", "md_vocab_tile_norms_bytes", "md_vocab_tile_norms", "vocab_tile_norms",
     "MedusaStep", "StepConfig",
 ]

@@ -27,6 +27,7 @@ EXPORTS = (
     "md_heads_logits_workspace_bytes", "md_medusa_heads_logits", "md_draft_sample_workspace_bytes", "md_draft_sample",
     "md_verify_sampled_workspace_bytes", "md_tree_verify_sampled", "md_accept_typical_workspace_bytes",
     "md_tree_accept_typical", "md_operand_order_bytes", "md_operand_order", "md_certified_rounding_allowance",
+    "md_vocab_tile_norms_bytes", "md_vocab_tile_norms",
     "md_tree_attention_noalloc", "md_tree_attention_noalloc_max_bytes", "md_heads_fused", "md_set_wait_limits",
 )
 
@@ -68,7 +69,9 @@ def lib() -> ctypes.CDLL:
             "md_heads_fused": ([i, i, i, i, i], i),
             "md_set_wait_limits": ([i, i], i),
             "md_heads_workspace_bytes": ([i, i, i, i, i, i, i], sz),
-            "md_medusa_heads": ([i, i, i, i, i, i, vp, i, tp] + [vp] * 12 + [sz, vp], i),
+            "md_medusa_heads": ([i, i, i, i, i, i, vp, i, tp] + [vp] * 13 + [sz, vp], i),
+            "md_vocab_tile_norms_bytes": ([i, i], sz),
+            "md_vocab_tile_norms": ([i, i, i, vp, vp, vp], i),
             "md_tree_build": ([tp, i, i, i, i, i, i] + [vp] * 6 + [vp], i),
             "md_attention_workspace_bytes": ([i, i, i, i, i, i, i], sz),
             "md_tree_attention": ([tp, i, i, i, i, i, i, i, vp, vp, vp, vp, f, vp, vp, sz, vp], i),
@@ -171,15 +174,16 @@ def md_accept_workspace_bytes(B: int, N: int, V: int) -> int:
 
 
 def md_medusa_heads(kind, dt, M, d, V, K, k_per_head, level, tree, h, W, b, U, E, root_tok, tree_tok, topk_idx,
-                    topk_val, h_res, ws, ws_bytes=None, stream=None, U_op=None) -> None:
-    """U_op: optional operand-order copy of U (see md_operand_order)."""
+                    topk_val, h_res, ws, ws_bytes=None, stream=None, U_op=None, U_norms=None) -> None:
+    """U_op: optional operand-order copy of U (see md_operand_order); U_norms: optional tile norms of U
+    (see md_vocab_tile_norms)."""
     kp = (ctypes.c_int32 * K)(*k_per_head)
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
     rc = lib().md_medusa_heads(kind, dt, M, d, V, K, ctypes.cast(kp, ctypes.c_void_p), level,
                                ctypes.byref(tree) if tree is not None else None, _p(h), _p(W), _p(b), _p(U), _p(U_op),
-                               _p(E), _p(root_tok), _p(tree_tok), _p(topk_idx), _p(topk_val), _p(h_res), _p(ws),
-                               ws_bytes, _stream(stream))
+                               _p(U_norms), _p(E), _p(root_tok), _p(tree_tok), _p(topk_idx), _p(topk_val), _p(h_res),
+                               _p(ws), ws_bytes, _stream(stream))
     _check(rc)
 
 
@@ -238,6 +242,28 @@ def md_operand_order_bytes(nmat, rows, cols) -> int:
 
 def md_operand_order(nmat, rows, cols, src, dst, stream=None) -> None:
     _check(lib().md_operand_order(nmat, rows, cols, _p(src), _p(dst), _stream(stream)))
+
+
+def md_vocab_tile_norms_bytes(nmat, V) -> int:
+    return int(lib().md_vocab_tile_norms_bytes(nmat, V))
+
+
+def md_vocab_tile_norms(nmat, V, d, U, norms, stream=None) -> None:
+    _check(lib().md_vocab_tile_norms(nmat, V, d, _p(U), _p(norms), _stream(stream)))
+
+
+def vocab_tile_norms(mat):
+    """A new float32 device tensor [nmat, ceil(V / 256)] holding md_vocab_tile_norms of a bf16 tensor
+    [V, d] or [nmat, V, d] (computed once, when weights load)."""
+    import torch
+
+    if mat.dtype != torch.bfloat16 or mat.dim() not in (2, 3):
+        raise MedusaError(MD_EINVAL, "tile norms take a bf16 [V, d] or [nmat, V, d] tensor")
+    m3 = mat if mat.dim() == 3 else mat.unsqueeze(0)
+    nmat, V, d = m3.shape
+    out = torch.empty(md_vocab_tile_norms_bytes(nmat, V) // 4, dtype=torch.float32, device=mat.device)
+    md_vocab_tile_norms(nmat, V, d, m3.contiguous(), out)
+    return out.view(nmat, -1)
 
 
 def operand_order(mat):

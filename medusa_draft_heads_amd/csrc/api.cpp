@@ -160,11 +160,12 @@ size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, in
 
 int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t* k_per_head, int level,
                     const md_tree* tree, const void* h, const void* W, const void* b, const void* U, const void* U_op,
-                    const void* E, const int32_t* root_tok, const int32_t* tree_tok, int32_t* topk_idx,
-                    float* topk_val, float* h_res, void* ws, size_t ws_bytes, void* stream) {
+                    const float* U_norms, const void* E, const int32_t* root_tok, const int32_t* tree_tok,
+                    int32_t* topk_idx, float* topk_val, float* h_res, void* ws, size_t ws_bytes, void* stream) {
     if (!known_kind(kind)) return fail(MD_EINVAL, "kind = %d", kind);
     if (check_dt(dt)) return MD_EINVAL;
     if (U_op && dt != MD_BF16) return fail(MD_EINVAL, "an operand-order copy of U exists for bf16 only");
+    if (U_norms && dt != MD_BF16) return fail(MD_EINVAL, "tile norms of U exist for bf16 only");
     if (M < 0) return fail(MD_EINVAL, "M = %d", M);
     if (K < 1 || K > MD_MAX_HEADS) return fail(MD_EINVAL, "K = %d heads (1..8 supported)", K);
     if (!k_per_head) return fail(MD_EINVAL, "k_per_head is NULL");
@@ -198,6 +199,7 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
     a.b = b;
     a.U = U;
     a.U_op = U_op;
+    a.U_norms = U_norms;
     a.E = E;
     a.root_tok = root_tok;
     a.tree_tok = tree_tok;
@@ -370,6 +372,18 @@ int md_operand_order(int nmat, int rows, int cols, const void* src, void* dst, v
     if (cols < 32 || cols % 32) return fail(MD_EUNSUPPORTED, "cols = %d (a positive multiple of 32 is required)", cols);
     if (!src || !dst) return fail(MD_EINVAL, "a required pointer is NULL");
     return hip_status(operand_order_launch(nmat, rows, cols, src, dst, (hipStream_t)stream), "md_operand_order");
+}
+
+size_t md_vocab_tile_norms_bytes(int nmat, int V) {
+    if (nmat < 1 || V < 1) return 0;
+    return (size_t)nmat * vocab_tiles(V) * sizeof(float);
+}
+
+int md_vocab_tile_norms(int nmat, int V, int d, const void* U, float* norms, void* stream) {
+    if (nmat < 1 || V < 1) return fail(MD_EINVAL, "nmat = %d, V = %d", nmat, V);
+    if (d < 8 || d % 8) return fail(MD_EUNSUPPORTED, "d = %d (a positive multiple of 8 is required)", d);
+    if (!U || !norms) return fail(MD_EINVAL, "a required pointer is NULL");
+    return hip_status(vocab_tile_norms_launch(U, nmat, V, d, norms, (hipStream_t)stream), "md_vocab_tile_norms");
 }
 
 int md_tree_accept_tokens(const md_tree* tree, int dt, int B, int K, int Hkv, int hd, int Lcap,

@@ -1231,6 +1231,47 @@ hipError_t launch_direct(int cb, dim3 grid, hipStream_t s, const uint16_t* U, co
     return hipGetLastError();
 }
 
+// ---- the largest row norm of each vocabulary tile (once per weight set) ----
+//
+// out[mat][vt] = max over the tile's rows v of sum_j U[mat][v][j]^2 (rows past
+// V count 0). The squares of bf16 values are exact in float32 and a row's sum
+// carries a relative rounding error below (d / 512 + 6) 2^-24, far inside the
+// 2^-10 the certified pass adds to the norm's square root. A wave per row at
+// a time, 16 bytes a lane per load; the lanes' sums are added in a fixed order.
+__global__ __launch_bounds__(BLOCK) void k_tile_norms(const uint16_t* __restrict__ U, int V, int d, int vtiles,
+                                                      float* __restrict__ out) {
+    __shared__ float s_mx[BLOCK / MD_WAVE];
+    const int mat = blockIdx.x / vtiles, vt = blockIdx.x - mat * vtiles;
+    const int lane = threadIdx.x & (MD_WAVE - 1), w = threadIdx.x >> 6;
+    float mx = 0.f;
+    for (int r = w; r < VR; r += BLOCK / MD_WAVE) {
+        const int v = vt * VR + r;
+        if (v >= V) break;  // uniform: rows past V
+        const uint16_t* row = U + ((int64_t)mat * V + v) * d;
+        float acc = 0.f;
+        for (int c = 8 * lane; c < d; c += 8 * MD_WAVE) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>(row + c);
+            const uint32_t wd[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float lo = __uint_as_float(wd[e] << 16), hi = __uint_as_float(wd[e] & 0xffff0000u);
+                acc = fmaf(lo, lo, acc);
+                acc = fmaf(hi, hi, acc);
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, MD_WAVE);
+        mx = fmaxf(mx, acc);
+    }
+    if (lane == 0) s_mx[w] = mx;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float m = s_mx[0];
+        for (int i = 1; i < BLOCK / MD_WAVE; ++i) m = fmaxf(m, s_mx[i]);
+        out[blockIdx.x] = m;
+    }
+}
+
 // ---- certified single-product vocabulary pass (many rows) ----
 //
 // With h' = hi + lo' (hi = bf16(h'), lo' the exact rest), the logit is
@@ -1522,9 +1563,13 @@ __device__ __forceinline__ int wave_kth_largest_ordered(int v, int k) {
 // every entry that can still reach the top k appended to the row's candidate
 // buffer. The epilogue's global atomics go out for all of a wave's columns at
 // once rather than one column after another.
+// PRE: the tiles' row norms come from a table made once per weight set
+// (k_tile_norms) instead of the Gram products, 4 of every 36 MFMAs.
+template <bool PRE>
 __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __restrict__ U,
                                                               const uint16_t* __restrict__ hhi, int M, int d, int V,
                                                               int nh, int head0, int vtiles, int mtiles, KW kk, int Mh,
+                                                              const float* __restrict__ tile_n2,
                                                               const float* __restrict__ lo_norm,
                                                               const float* __restrict__ h_norm, float cert_c,
                                                               int* __restrict__ bound, int* __restrict__ slots,
@@ -1587,13 +1632,16 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
                 acc[rb][cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rb], b, acc[rb][cb], 0, 0, 0);
         }
         // the two waves of a row band split its Gram blocks: wc takes row blocks 4 wc .. 4 wc + 3
-        if (wc == 0) {
+        if constexpr (!PRE) {
+            if (wc == 0) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) gram[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], a[j], gram[j], 0, 0, 0);
-        } else {
+                for (int j = 0; j < 4; ++j)
+                    gram[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[j], a[j], gram[j], 0, 0, 0);
+            } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                gram[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[4 + j], a[4 + j], gram[j], 0, 0, 0);
+                for (int j = 0; j < 4; ++j)
+                    gram[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[4 + j], a[4 + j], gram[j], 0, 0, 0);
+            }
         }
     };
 
@@ -1637,6 +1685,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
             mx = fmaxf(mx, dv);
         }
         mx = md_wave::wave_max(mx);
+        if constexpr (PRE) mx = tile_n2[(int64_t)(head0 + hh) * vtiles + vt];
         if (lane == 0) s_nrm[w] = mx;
     }
     __syncthreads();
@@ -2255,10 +2304,16 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
         *nlists = vtiles;
     } else {  // many rows: one product and the certificate
         const int vmtiles = (rows_v + VM - 1) / VM;
-        hipLaunchKernelGGL(k_vocab_mfma_cert, dim3(8 * vmtiles * ((units2 + 7) / 8)), dim3(BLOCK), 0, s, U, L.hhi,
-                           rows_v, a.d, a.V, nh_u, head0, vtiles, vmtiles, kk, Mh, L.lo_norm, L.h_norm,
-                           cert_rounding_allowance(a.d), L.bound,
-                           L.slots, L.count, L.cand_ub, L.cand_lb, L.cand_idx);
+        const dim3 cgrid(8 * vmtiles * ((units2 + 7) / 8));
+        if (a.U_norms)
+            hipLaunchKernelGGL(k_vocab_mfma_cert<true>, cgrid, dim3(BLOCK), 0, s, U, L.hhi, rows_v, a.d, a.V, nh_u, head0,
+                               vtiles, vmtiles, kk, Mh, a.U_norms, L.lo_norm, L.h_norm, cert_rounding_allowance(a.d),
+                               L.bound, L.slots, L.count, L.cand_ub, L.cand_lb, L.cand_idx);
+        else
+            hipLaunchKernelGGL(k_vocab_mfma_cert<false>, cgrid, dim3(BLOCK), 0, s, U, L.hhi, rows_v, a.d, a.V, nh_u,
+                               head0, vtiles, vmtiles, kk, Mh, nullptr, L.lo_norm, L.h_norm,
+                               cert_rounding_allowance(a.d), L.bound, L.slots, L.count, L.cand_ub, L.cand_lb,
+                               L.cand_idx);
         *nlists = 0;
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
@@ -2272,4 +2327,13 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
     *part_val = L.pv;
     *part_idx = L.pi;
     return hipSuccess;
+}
+
+int vocab_tiles(int V) { return (V + VR - 1) / VR; }
+
+hipError_t vocab_tile_norms_launch(const void* U, int nmat, int V, int d, float* out, hipStream_t s) {
+    const int vt = vocab_tiles(V);
+    hipLaunchKernelGGL(k_tile_norms, dim3((unsigned)(nmat * vt)), dim3(BLOCK), 0, s,
+                       reinterpret_cast<const uint16_t*>(U), V, d, vt, out);
+    return hipGetLastError();
 }

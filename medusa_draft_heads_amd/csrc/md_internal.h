@@ -56,6 +56,7 @@ struct HeadsArgs {
     const void* b;
     const void* U;
     const void* U_op;  // optional operand-order copy of U (bf16), read by the few-row matrix-core kernels
+    const float* U_norms;  // optional largest squared row norm of U per 256-row tile (bf16), read by the certified pass
     const void* E;
     const int32_t* root_tok;
     const int32_t* tree_tok;
@@ -92,6 +93,9 @@ bool argmax_mfma_applicable(int dt, int R, int d, bool op);
 size_t argmax_mfma_ws_bytes(int R, int V);
 hipError_t argmax_mfma_launch(int R, int d, int V, const void* H, const void* Wt, const void* Wt_op, void* ws,
                               hipStream_t s, float** part_val, int** part_idx, int* nlists);
+// the largest squared row norm of each 256-row tile of nmat [V][d] bf16 matrices -> out [nmat][ceil(V / 256)]
+hipError_t vocab_tile_norms_launch(const void* U, int nmat, int V, int d, float* out, hipStream_t s);
+int vocab_tiles(int V);
 // the operand-order copy of nmat row-major [rows][cols] bf16 matrices (heads_mfma.hip)
 size_t operand_order_bytes(int nmat, int rows, int cols);
 hipError_t operand_order_launch(int nmat, int rows, int cols, const void* src, void* dst, hipStream_t s);

@@ -100,10 +100,11 @@ class MedusaStep:
         self.h_res = None
 
     # -- the four calls -------------------------------------------------------
-    def heads(self, h, W, b, U, E=None, root_tok=None, level: int = 0, h_res=None, U_op=None) -> None:
+    def heads(self, h, W, b, U, E=None, root_tok=None, level: int = 0, h_res=None, U_op=None, U_norms=None) -> None:
         c = self.cfg
         L.md_medusa_heads(c.kind, self.dt, c.M, c.d, c.V, c.K, c.k_per_head, level, self.tree, h, W, b, U, E,
-                          root_tok, self.tree_tok, self.topk_idx, self.topk_val, h_res, self.ws_heads, U_op=U_op)
+                          root_tok, self.tree_tok, self.topk_idx, self.topk_val, h_res, self.ws_heads, U_op=U_op,
+                          U_norms=U_norms)
 
     def build(self, src_row, root_tok, lens, level: int = 0) -> None:
         c = self.cfg
@@ -125,6 +126,13 @@ class MedusaStep:
         c = self.cfg
         L.md_target_argmax(self.dt, c.B * self.N, c.d, c.V, Ht, Wt, self.target_tok, self.target_val, self.ws_target,
                            Wt_op=Wt_op)
+
+    def tile_norm_weights(self, w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
+        """The tile norms of the vocabulary matrices (U_norms), made once when the weights load; bf16 only.
+        run() passes them on when w holds them (the many-row certified pass reads them)."""
+        if self.dt != L.MD_BF16:
+            raise ValueError("tile norms exist for bf16 weights only")
+        return {"U_norms": L.vocab_tile_norms(w["U"])}
 
     def operand_order_weights(self, w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
         """Operand-order copies of the vocabulary matrices (U_op, and Wt_op with target_head), made once
@@ -178,13 +186,13 @@ class MedusaStep:
             self.verify_sampled(x["logits"], x["u_words"], x["g_words"], x["Kc"], x["Vc"], x["lens"])
             return
         if c.kind != L.MD_HEADS_HYDRA:
-            self.heads(x["h"], w["W"], w["b"], w["U"], U_op=w.get("U_op"))
+            self.heads(x["h"], w["W"], w["b"], w["U"], U_op=w.get("U_op"), U_norms=w.get("U_norms"))
             self.build(x["src_row"], x["root_tok"], x["lens"])
         else:
             depth = max(self._depths())
             for level in range(1, depth + 1):
                 self.heads(x["h"], w["W"], w["b"], w["U"], E=w["E"], root_tok=x["root_tok"], level=level,
-                           U_op=w.get("U_op"))
+                           U_op=w.get("U_op"), U_norms=w.get("U_norms"))
                 self.build(None, x["root_tok"], x["lens"], level=level)
         self.attention(x["q"], x["Kc"], x["Vc"], x["lens"])
         if c.target_head:

@@ -23,7 +23,7 @@ def header_functions():
 
 def test_exports_every_declared_function():
     names = header_functions()
-    assert len(names) == 31
+    assert len(names) == 33
     lib = L.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -138,9 +138,9 @@ def test_heads_argument_errors():
                                                       product_order_tree((4, 2, 2, 1), 16).rank)]))
 
     def call(kind=0, dt=1, M=1, d=256, V=4096, K=4, kph=kpv, level=0, tree=None, h=P, W=P, U=P, ws=P, ws_bytes=1 << 30,
-             E=None, root=None, tok=None, U_op=None):
-        return lib.md_medusa_heads(kind, dt, M, d, V, K, kph, level, tree, h, W, None, U, U_op, E, root, tok, P, P, None,
-                                   ws, ws_bytes, None)
+             E=None, root=None, tok=None, U_op=None, U_norms=None):
+        return lib.md_medusa_heads(kind, dt, M, d, V, K, kph, level, tree, h, W, None, U, U_op, U_norms, E, root, tok, P,
+                                   P, None, ws, ws_bytes, None)
 
     assert call(kind=3) == L.MD_EINVAL
     assert call(kind=2, level=1) == L.MD_EINVAL  # a shared projection is Medusa: level 0
@@ -159,6 +159,7 @@ def test_heads_argument_errors():
     assert call(kind=1, level=1, tree=None, E=P, root=P) == L.MD_EINVAL
     assert call(M=-1) == L.MD_EINVAL
     assert call(dt=0, U_op=P) == L.MD_EINVAL  # the operand-order copy is bf16 only
+    assert call(dt=0, U_norms=P) == L.MD_EINVAL  # so are the tile norms
     assert call(M=0) == L.MD_OK  # an empty batch enqueues nothing
 
 
@@ -342,3 +343,16 @@ def test_sampled_decoding_argument_errors():
 def test_timing_hook_pairs():
     assert L.lib().md_set_vocab_timing_events(0x10, None) == L.MD_EINVAL
     assert L.lib().md_set_vocab_timing_events(None, None) == L.MD_OK
+
+
+def test_vocab_tile_norms_argument_errors():
+    lib = L.lib()
+    P = 0x1000  # never dereferenced: every call below is rejected on the host
+    assert lib.md_vocab_tile_norms_bytes(4, 128256) == 4 * 501 * 4
+    assert lib.md_vocab_tile_norms_bytes(1, 256) == 4 and lib.md_vocab_tile_norms_bytes(1, 257) == 8
+    assert lib.md_vocab_tile_norms_bytes(0, 256) == 0 and lib.md_vocab_tile_norms_bytes(1, 0) == 0
+    assert lib.md_vocab_tile_norms(0, 256, 64, P, P, None) == L.MD_EINVAL
+    assert lib.md_vocab_tile_norms(1, 0, 64, P, P, None) == L.MD_EINVAL
+    assert lib.md_vocab_tile_norms(1, 256, 60, P, P, None) == L.MD_EUNSUPPORTED
+    assert lib.md_vocab_tile_norms(1, 256, 64, None, P, None) == L.MD_EINVAL
+    assert lib.md_vocab_tile_norms(1, 256, 64, P, None, None) == L.MD_EINVAL

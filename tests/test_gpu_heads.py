@@ -27,7 +27,7 @@ def _md():
     return md
 
 
-def gpu_heads_medusa(wl: Workload, wd, h_dev, M, U_op=None):
+def gpu_heads_medusa(wl: Workload, wd, h_dev, M, U_op=None, U_norms=None):
     import torch
 
     md = _md()
@@ -39,7 +39,7 @@ def gpu_heads_medusa(wl: Workload, wd, h_dev, M, U_op=None):
     hres = torch.empty(K, M, wl.d, dtype=torch.float32, device="cuda")
     ws = torch.empty(md.md_heads_workspace_bytes(kind, dt, M, wl.d, wl.V, K, kmax), dtype=torch.uint8, device="cuda")
     md.md_medusa_heads(kind, dt, M, wl.d, wl.V, K, wl.topk, 0, None, h_dev, wd["W"], wd["b"], wd["U"], None, None,
-                       None, idx, val, hres, ws, U_op=U_op)
+                       None, idx, val, hres, ws, U_op=U_op, U_norms=U_norms)
     torch.cuda.synchronize()
     return from_dev(idx), from_dev(val), from_dev(hres)
 
@@ -286,6 +286,10 @@ def test_heads_medusa_mfma_rows(wl, M):
     compare_medusa(wl, gi, gv, gh, ref, label="%s M=%d" % (wl.name, M))
     gi2, gv2, gh2 = gpu_heads_medusa(wl, wd, to_dev(h), M)
     assert np.array_equal(gi, gi2) and np.array_equal(gv.view(np.uint32), gv2.view(np.uint32))
+    # with the tile norms of U the certified pass (130 rows) skips its own norms; the lists come
+    # from the same exact re-scoring, so they are the same bit for bit (other paths ignore them)
+    gi3, gv3, _ = gpu_heads_medusa(wl, wd, to_dev(h), M, U_norms=_md().vocab_tile_norms(wd["U"]))
+    assert np.array_equal(gi, gi3) and np.array_equal(gv.view(np.uint32), gv3.view(np.uint32))
 
 
 @pytest.mark.parametrize("wl_name,M,rows", [("8b", 64, [0, 31, 63]),
@@ -302,6 +306,9 @@ def test_heads_medusa_mfma_full_size_sampled(wl_name, M, rows):
     ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, rows=rows, want_logits=True)
     ref["hres"] = ref["hres"]
     compare_medusa(wl, gi[rows], gv[rows], gh[:, rows], ref, label="%s M=%d rows %s" % (wl.name, M, rows))
+    # the certified pass reading the tile norms: every list and value of all M rows the same
+    gi2, gv2, _ = gpu_heads_medusa(wl, wd, to_dev(h), M, U_norms=_md().vocab_tile_norms(wd["U"]))
+    assert np.array_equal(gi, gi2) and np.array_equal(gv.view(np.uint32), gv2.view(np.uint32))
     del wd
 
 
@@ -323,7 +330,24 @@ def test_heads_certified_pass_wide_contraction():
     compare_medusa(wl, gi[rows], gv[rows], gh[:, rows], ref, label="certified d=16384 M=%d" % M)
     gi2, gv2, _ = gpu_heads_medusa(wl, wd, to_dev(h), M)
     assert np.array_equal(gi, gi2) and np.array_equal(gv.view(np.uint32), gv2.view(np.uint32))
+    gi3, gv3, _ = gpu_heads_medusa(wl, wd, to_dev(h), M, U_norms=md.vocab_tile_norms(wd["U"]))
+    assert np.array_equal(gi, gi3) and np.array_equal(gv.view(np.uint32), gv3.view(np.uint32))
     del wd
+
+
+@pytest.mark.parametrize("nmat,V,d", [(2, 1000, 512), (1, 256, 64), (3, 513, 8192)])
+def test_vocab_tile_norms(nmat, V, d):
+    """md_vocab_tile_norms against float64 on the host: each 256-row tile's largest sum of squares
+    (the last tile ragged at V = 1,000 and 513)."""
+    md = _md()
+    U = synth.normal(4500 + V, 87, (nmat, V, d), 1.0, "bf16")
+    Uf = synth.bf16_to_f32(U).astype(np.float64)
+    n2 = (Uf * Uf).sum(axis=2)  # [nmat, V]
+    tiles = (V + 255) // 256
+    ref = np.stack([[n2[m, 256 * t:256 * t + 256].max() for t in range(tiles)] for m in range(nmat)])
+    got = from_dev(md.vocab_tile_norms(to_dev(U)))
+    assert got.shape == (nmat, tiles)
+    assert np.max(np.abs(got - ref) / ref) <= 1e-5
 
 
 # ------------------------------------- operand-order copy of the projection
@@ -456,6 +480,8 @@ def test_heads_shared_projection_many_rows_sampled():
     gi, gv, gh = gpu_heads_medusa(wl, wd, to_dev(h), M)
     ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, rows=rows, want_logits=True)
     compare_medusa(wl, gi[rows], gv[rows], gh[:, rows], ref, label="%s M=%d rows %s" % (wl.name, M, rows))
+    gi2, gv2, _ = gpu_heads_medusa(wl, wd, to_dev(h), M, U_norms=_md().vocab_tile_norms(wd["U"]))
+    assert np.array_equal(gi, gi2) and np.array_equal(gv.view(np.uint32), gv2.view(np.uint32))
     del wd
 
 
