@@ -536,6 +536,122 @@ __global__ __launch_bounds__(kRowsWaves * MD_WAVE) void k_residual_rows(
     }
 }
 
+// The residual over 17 to 77 activation rows at din = 8,192 (Hydra's levels
+// past the first at d = 4,096): a block owns one 128-row tile of W and one
+// eighth of the contraction (1,024 elements). It first stages its eighth of
+// every activation row in LDS (gathered from h and E, 2 KB a row, one zero
+// row for the padding columns), then its 8 waves each stream 16 rows of W
+// through a register ring and take the activation fragments from LDS, so the
+// block reads its activation chunk once (where k_residual_rows read 16 KB of
+// them per 1 KB of W from L2). Blocks of one chunk run on one XCD (ids x +
+// 8 u: chunk x) and share its L2. The 8 partial sums per output go to zpart
+// [8][nh][M][d], added by k_residual_finish in chunk order.
+constexpr int kStageKC = 1024;                 // contraction elements per chunk
+constexpr int kStagePitch = kStageKC + 8;      // LDS row pitch (bf16): rows 16 bytes apart mod 256
+constexpr int kStageRows = 78;                 // activation rows + the zero row
+static_assert(kStageRows * kStagePitch * 2 + 2 * kStageRows * 4 <= 160 * 1024, "the chunk fits the LDS");
+template <int RC>
+__global__ __launch_bounds__(kRowsWaves * MD_WAVE) void k_residual_staged(
+    const uint16_t* __restrict__ W, GemmRows rows, int M, int d, int din, int nh, int head0,
+    float* __restrict__ zpart, int* __restrict__ bound) {
+    constexpr int RP = kRowsRing;
+    __shared__ __align__(16) uint16_t xs[kStageRows * kStagePitch];
+    __shared__ int s_tok[kStageRows];
+    __shared__ int s_b[kStageRows];
+    const int kc = blockIdx.x & 7, tile = blockIdx.x >> 3;  // contraction chunk (= XCD), 128-row tile of W
+    const int row0 = tile * 128;                              // over nh * d rows (d % 128 == 0)
+    const int hh = row0 / d, r0 = row0 - hh * d;
+    const int tid = threadIdx.x, lane = tid & (MD_WAVE - 1);
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int g4 = lane >> 4, c16 = lane & 15;
+    if (blockIdx.x == 0)
+        for (int j = tid; j < nh * M; j += kRowsWaves * MD_WAVE) bound[j] = f2o(-INFINITY);
+    if (tid < M) {
+        const int m = tid;
+        int b = m, tok = -1;
+        if (rows.kind == 1) {
+            b = m / rows.P;
+            const int p = rows.parents[m - b * rows.P];
+            tok = p == 0 ? rows.root_tok[b] : rows.tree_tok[(int64_t)b * rows.N + p];
+            if (tok < 0 || tok >= rows.V) tok = -1;  // out-of-vocabulary token: zero embedding
+        }
+        s_b[m] = b;
+        s_tok[m] = tok;
+    }
+    __syncthreads();
+    // A: W rows row0 + 16 w + c16, chunk g4 of each K step of the block's
+    // chunk; the ring's first loads go out before the activation rows are
+    // staged (W does not wait for them)
+    const int kb = kc * kStageKC;
+    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(W + ((int64_t)head0 * d + row0 + 16 * w) * din), 0, 16 * din * 2, RSRC3);
+    const uint32_t aoff = (uint32_t)c16 * din * 2 + (uint32_t)(kb + 8 * g4) * 2;
+    u32x4 ra[RP];
+    constexpr int nst = kStageKC / 32;
+    static_assert(nst % RP == 0, "whole rounds of the ring");
+    auto issue = [&](int s, int j) {
+        ra[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, aoff + (uint32_t)min(s, nst - 1) * 64, 0, 0);
+    };
+#pragma unroll
+    for (int j = 0; j < RP; ++j) issue(j, j);
+
+    // the chunk [kb, kb + 1024) of every activation row (wholly in h or in
+    // E's half): a thread's pieces (at most SPT) are all loaded before any is
+    // stored, one memory round trip instead of one each
+    const bool in_e = rows.kind == 1 && kb >= d;
+    constexpr int CPRW = kStageKC / 8;  // 16-byte pieces a row
+    constexpr int SPT = (kStageRows * CPRW + kRowsWaves * MD_WAVE - 1) / (kRowsWaves * MD_WAVE);
+    const int npieces = (M + 1) * CPRW;
+    u32x4 xv[SPT];
+#pragma unroll
+    for (int q = 0; q < SPT; ++q) {
+        const int i = tid + q * kRowsWaves * MD_WAVE;
+        const int m = i / CPRW, c = i - m * CPRW;
+        xv[q] = u32x4{0u, 0u, 0u, 0u};
+        if (i < npieces && m < M) {
+            const int src = in_e ? s_tok[m] : (rows.kind == 1 ? s_b[m] : m);
+            if (src >= 0)
+                xv[q] = *reinterpret_cast<const u32x4*>((in_e ? rows.E : rows.h) + (int64_t)src * d +
+                                                        (in_e ? kb - d : kb) + 8 * c);
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < SPT; ++q) {
+        const int i = tid + q * kRowsWaves * MD_WAVE;
+        const int m = i / CPRW, c = i - m * CPRW;
+        if (i < npieces) *reinterpret_cast<u32x4*>(xs + m * kStagePitch + 8 * c) = xv[q];
+    }
+    __syncthreads();
+
+    uint32_t bl[RC];  // LDS element offsets of the lane's B rows (rows past M read the zero row)
+#pragma unroll
+    for (int cb = 0; cb < RC; ++cb) bl[cb] = (uint32_t)min(16 * cb + c16, M) * kStagePitch + 8 * g4;
+    f32x4 acc[RC];
+#pragma unroll
+    for (int cb = 0; cb < RC; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s0 = 0; s0 < nst; s0 += RP) {
+#pragma unroll
+        for (int j = 0; j < RP; ++j) {
+            const int s = s0 + j;
+#pragma unroll
+            for (int cb = 0; cb < RC; ++cb) {
+                const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(xs + bl[cb] + 32 * s));
+                acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, ra[j]), bv, acc[cb], 0, 0,
+                                                                  0);
+            }
+            issue(s + RP, j);  // past the chunk: repeats its last step, never used
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads land before the wave ends
+    // lane (g4, c16) holds z rows r0 + 16 w + 4 g4 + i of activation row 16 cb + c16
+#pragma unroll
+    for (int cb = 0; cb < RC; ++cb) {
+        const int m = 16 * cb + c16;
+        if (m < M)
+            *reinterpret_cast<f32x4*>(zpart + (((int64_t)kc * nh + hh) * M + m) * d + r0 + 16 * w + 4 * g4) = acc[cb];
+    }
+}
+
 // Operand order: a copy of a row-major [rows][d] bf16 matrix in which every
 // MFMA A fragment (16 rows x 32 contraction elements, 1 KB) is contiguous in
 // lane order (lane l: row l % 16, elements 8 (l / 16) .. + 7), laid out
@@ -2105,6 +2221,12 @@ bool residual_rows(int M, int d, int din, int V) {
     return M >= 1 && M <= 16 && din % 2048 == 0 && d % 16 == 0 && (din == d || (int64_t)V * d * 2 <= 0x7FF00000LL);
 }
 
+// 17 to 77 activation rows at din = 8,192: k_residual_staged (the activation
+// chunk staged in LDS, 8 contraction chunks, k_residual_finish after it).
+bool residual_staged(int M, int d, int din, int nh) {
+    return M > 16 && M < kStageRows && din == 8 * kStageKC && d % 128 == 0 && (nh * d / 128) * 8 >= 256;
+}
+
 // Many Medusa rows with whole 256-row tiles of W and enough of them to fill
 // the GPU without a split contraction: the certified pass's pipeline
 // (k_residual_wide); otherwise the 128 x 128 register-staged tiles.
@@ -2139,7 +2261,7 @@ MfmaWs mfma_ws_layout(char* base, int M, int d, int din, int V, int nh, int kmax
         return p;
     };
     const size_t e = (size_t)nh * M * d, rows = (size_t)nh * M;
-    const int ks = residual_rows(M, d, din, V) ? 1 : residual_ksplit(M, d, din, nh);
+    const int ks = residual_rows(M, d, din, V) ? 1 : (residual_staged(M, d, din, nh) ? 8 : residual_ksplit(M, d, din, nh));
     L.hres = reinterpret_cast<float*>(take(e * 4));
     L.hhi = reinterpret_cast<uint16_t*>(take(e * 2));
     L.hlo = reinterpret_cast<uint16_t*>(take(e * 2));
@@ -2221,7 +2343,8 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
 
     const int units1 = a.nh * a.d / TR;
     const bool rows16 = residual_rows(a.M, a.d, a.din, a.V);
-    const int ksplit = rows16 ? 1 : residual_ksplit(a.M, a.d, a.din, a.nh);
+    const bool staged = !rows16 && residual_staged(a.M, a.d, a.din, a.nh);
+    const int ksplit = rows16 ? 1 : (staged ? 8 : residual_ksplit(a.M, a.d, a.din, a.nh));
     const uint16_t* bias = reinterpret_cast<const uint16_t*>(a.b);
     // one Medusa row (a shared projection) with an operand-order copy: the GEMV residual
     // (one pass over W, HBM-bound) writes h' and its hi/lo split for the
@@ -2248,6 +2371,18 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
         const uint16_t* Wp = reinterpret_cast<const uint16_t*>(a.W);
         hipLaunchKernelGGL(k_residual_rows<1>, g, blk, 0, s, Wp, bias, rows, a.M, a.d, a.din, a.nh, a.head0, L.hres,
                            a.h_res, L.hhi, L.hlo, L.bound, bo);
+    } else if (staged) {
+        const dim3 g((unsigned)(8 * (a.nh * a.d / 128))), blk(kRowsWaves * MD_WAVE);
+        const uint16_t* Wp = reinterpret_cast<const uint16_t*>(a.W);
+#define MD_STAGED(RCV)                                                                                               \
+    hipLaunchKernelGGL(k_residual_staged<RCV>, g, blk, 0, s, Wp, rows, a.M, a.d, a.din, a.nh, a.head0, L.zpart, L.bound)
+        switch ((a.M + 15) / 16) {
+            case 2: MD_STAGED(2); break;
+            case 3: MD_STAGED(3); break;
+            case 4: MD_STAGED(4); break;
+            default: MD_STAGED(5); break;
+        }
+#undef MD_STAGED
     } else {
         hipLaunchKernelGGL(k_residual_mfma, dim3(ksplit * 8 * mtiles * ((units1 + 7) / 8)), dim3(BLOCK), 0, s,
                            reinterpret_cast<const uint16_t*>(a.W), bias, rows, a.M, a.d, a.din, a.nh, a.head0, mtiles,

@@ -293,6 +293,8 @@ def test_heads_medusa_mfma_rows(wl, M):
 
 
 @pytest.mark.parametrize("wl_name,M,rows", [("8b", 64, [0, 31, 63]),
+                                             # 40 rows of d = 8,192: the residual staged in LDS (8 chunks)
+                                             ("70b", 40, [0, 17, 39]),
                                              ("70b", 512, list(range(192, 256)) + [0, 130, 300, 511])])
 def test_heads_medusa_mfma_full_size_sampled(wl_name, M, rows):
     """The 70B-shaped heads over all 512 tree nodes of a batch of 8 on the certified pass: every row
