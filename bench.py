@@ -228,7 +228,7 @@ def main() -> int:
     if use_op:  # made once with the weights, outside every timed region
         wd.update(step.operand_order_weights(wd))
         torch.cuda.synchronize()
-        log("operand-order copies: %s" % ", ".join(k for k in ("U_op", "Wt_op") if k in wd))
+        log("operand-order copies: %s" % ", ".join(k for k in ("U_op", "W_op", "Wt_op") if k in wd))
     use_tn = args.tile_norms == "on" or (args.tile_norms == "auto" and wl.dtype == "bf16" and not hydra
                                           and wl.M * (wl.K if wl.shared_u else 1) > 128)
     if use_tn:  # made once with the weights, outside every timed region
@@ -258,12 +258,13 @@ def main() -> int:
                 md.md_set_vocab_timing_events(pairs[lvl][0].cuda_event, pairs[lvl][1].cuda_event)
             if hydra:
                 step.heads(xd["h"], wd["W"], wd["b"], wd["U"], E=wd["E"], root_tok=xd["root_tok"], level=lvl + 1,
-                           U_op=wd.get("U_op"))
+                           U_op=wd.get("U_op"), W_op=wd.get("W_op"))
                 step.build(None, xd["root_tok"], xd["lens"], level=lvl + 1)
             elif wl.verify == "sampled":
                 step.heads_logits(xd["h"], wd["W"], wd["b"], wd["U"])
             else:
-                step.heads(xd["h"], wd["W"], wd["b"], wd["U"], U_op=wd.get("U_op"), U_norms=wd.get("U_norms"))
+                step.heads(xd["h"], wd["W"], wd["b"], wd["U"], U_op=wd.get("U_op"), U_norms=wd.get("U_norms"),
+                           W_op=wd.get("W_op"))
             if pairs is not None:
                 md.md_set_vocab_timing_events(None, None)
         if wl.verify == "sampled":

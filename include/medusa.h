@@ -200,11 +200,19 @@ int md_vocab_tile_norms(int nmat, int V, int d, const void* U, float* norms, voi
  * then takes each tile's row norm from it instead of computing it; the lists
  * are the same (they come from the exact re-scoring either way). MD_EINVAL
  * if given with dt = MD_F32. A table that does not belong to U, or is too
- * small, voids the certificate (undefined results, no fault). */
+ * small, voids the certificate (undefined results, no fault).
+ *
+ * W_op (optional, NULL for none): the operand-order copy of W (bf16 only;
+ * md_operand_order over the K matrices [d][din], din = d, or 2d for Hydra).
+ * The few-row matrix-core residual kernels (up to 16 rows, and 17 to 77 rows
+ * at din = 8,192) then read each weight fragment as one consecutive 1 KB;
+ * the products and their order are the same, so are the results, bit for
+ * bit. MD_EINVAL if given with dt = MD_F32. */
 int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t* k_per_head, int level,
                     const md_tree* tree, const void* h, const void* W, const void* b, const void* U, const void* U_op,
-                    const float* U_norms, const void* E, const int32_t* root_tok, const int32_t* tree_tok,
-                    int32_t* topk_idx, float* topk_val, float* h_res, void* ws, size_t ws_bytes, void* stream);
+                    const float* U_norms, const void* W_op, const void* E, const int32_t* root_tok,
+                    const int32_t* tree_tok, int32_t* topk_idx, float* topk_val, float* h_res, void* ws,
+                    size_t ws_bytes, void* stream);
 
 /* The candidate tree's tokens and positions ("Trees").
  *

@@ -69,7 +69,7 @@ def lib() -> ctypes.CDLL:
             "md_heads_fused": ([i, i, i, i, i], i),
             "md_set_wait_limits": ([i, i], i),
             "md_heads_workspace_bytes": ([i, i, i, i, i, i, i], sz),
-            "md_medusa_heads": ([i, i, i, i, i, i, vp, i, tp] + [vp] * 13 + [sz, vp], i),
+            "md_medusa_heads": ([i, i, i, i, i, i, vp, i, tp] + [vp] * 14 + [sz, vp], i),
             "md_vocab_tile_norms_bytes": ([i, i], sz),
             "md_vocab_tile_norms": ([i, i, i, vp, vp, vp], i),
             "md_tree_build": ([tp, i, i, i, i, i, i] + [vp] * 6 + [vp], i),
@@ -174,16 +174,16 @@ def md_accept_workspace_bytes(B: int, N: int, V: int) -> int:
 
 
 def md_medusa_heads(kind, dt, M, d, V, K, k_per_head, level, tree, h, W, b, U, E, root_tok, tree_tok, topk_idx,
-                    topk_val, h_res, ws, ws_bytes=None, stream=None, U_op=None, U_norms=None) -> None:
-    """U_op: optional operand-order copy of U (see md_operand_order); U_norms: optional tile norms of U
-    (see md_vocab_tile_norms)."""
+                    topk_val, h_res, ws, ws_bytes=None, stream=None, U_op=None, U_norms=None, W_op=None) -> None:
+    """U_op / W_op: optional operand-order copies of U / W (see md_operand_order); U_norms: optional
+    tile norms of U (see md_vocab_tile_norms)."""
     kp = (ctypes.c_int32 * K)(*k_per_head)
     if ws_bytes is None:
         ws_bytes = ws.numel() * ws.element_size()
     rc = lib().md_medusa_heads(kind, dt, M, d, V, K, ctypes.cast(kp, ctypes.c_void_p), level,
                                ctypes.byref(tree) if tree is not None else None, _p(h), _p(W), _p(b), _p(U), _p(U_op),
-                               _p(U_norms), _p(E), _p(root_tok), _p(tree_tok), _p(topk_idx), _p(topk_val), _p(h_res),
-                               _p(ws), ws_bytes, _stream(stream))
+                               _p(U_norms), _p(W_op), _p(E), _p(root_tok), _p(tree_tok), _p(topk_idx), _p(topk_val),
+                               _p(h_res), _p(ws), ws_bytes, _stream(stream))
     _check(rc)
 
 

@@ -160,12 +160,14 @@ size_t md_heads_workspace_bytes(int kind, int dt, int M, int d, int V, int K, in
 
 int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t* k_per_head, int level,
                     const md_tree* tree, const void* h, const void* W, const void* b, const void* U, const void* U_op,
-                    const float* U_norms, const void* E, const int32_t* root_tok, const int32_t* tree_tok,
-                    int32_t* topk_idx, float* topk_val, float* h_res, void* ws, size_t ws_bytes, void* stream) {
+                    const float* U_norms, const void* W_op, const void* E, const int32_t* root_tok,
+                    const int32_t* tree_tok, int32_t* topk_idx, float* topk_val, float* h_res, void* ws,
+                    size_t ws_bytes, void* stream) {
     if (!known_kind(kind)) return fail(MD_EINVAL, "kind = %d", kind);
     if (check_dt(dt)) return MD_EINVAL;
     if (U_op && dt != MD_BF16) return fail(MD_EINVAL, "an operand-order copy of U exists for bf16 only");
     if (U_norms && dt != MD_BF16) return fail(MD_EINVAL, "tile norms of U exist for bf16 only");
+    if (W_op && dt != MD_BF16) return fail(MD_EINVAL, "an operand-order copy of W exists for bf16 only");
     if (M < 0) return fail(MD_EINVAL, "M = %d", M);
     if (K < 1 || K > MD_MAX_HEADS) return fail(MD_EINVAL, "K = %d heads (1..8 supported)", K);
     if (!k_per_head) return fail(MD_EINVAL, "k_per_head is NULL");
@@ -200,6 +202,7 @@ int md_medusa_heads(int kind, int dt, int M, int d, int V, int K, const int32_t*
     a.U = U;
     a.U_op = U_op;
     a.U_norms = U_norms;
+    a.W_op = W_op;
     a.E = E;
     a.root_tok = root_tok;
     a.tree_tok = tree_tok;

@@ -436,10 +436,16 @@ __device__ __forceinline__ void dmab_nt(__amdgpu_buffer_rsrc_t r, unsigned char*
 // from L2, 16 KB of them per 1 KB of W at d = 4,096, so the kernel stops
 // paying beyond one column block (32 and 72 rows: 26.8 and 34.2 us against
 // 23.9 and 29.2), where the split-contraction kernel runs instead. RC: 16-row
-// column blocks (1).
+// column blocks (1). OP: W is the operand-order copy (md_operand_order of
+// [heads][d][din]): each fragment one consecutive 1 KB, non-temporal loads.
 constexpr int kRowsWaves = 8;  // waves of k_residual_rows
 constexpr int kRowsRing = 8;   // K steps in flight per wave
-template <int RC>
+// byte offset of the A fragment of rows r .. r + 15 (r % 16 == 0) of one head
+// at K step ks in the operand-order copy of W [heads][d][din]
+__device__ __forceinline__ uint32_t w_op_frag(int r, int ks, int din) {
+    return (uint32_t)(((r / 256) * (din / 32) + ks) * 16 + (r % 256) / 16) * 1024;
+}
+template <int RC, bool OP>
 __global__ __launch_bounds__(kRowsWaves * MD_WAVE) void k_residual_rows(
     const uint16_t* __restrict__ W, const uint16_t* __restrict__ bias, GemmRows rows, int M, int d, int din, int nh,
     int head0, float* __restrict__ hres, float* __restrict__ hres_out, uint16_t* __restrict__ hhi,
@@ -478,12 +484,15 @@ __global__ __launch_bounds__(kRowsWaves * MD_WAVE) void k_residual_rows(
     // enough that adding a K offset cannot wrap it back): they load zeros.
     const int kw = din / kRowsWaves, kb = w * kw;
     const bool in_e = rows.kind == 1 && kb >= d;
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(W + ((int64_t)head0 * d + row0) * din), 0, 16 * din * 2, RSRC3);
+    const int dpad = (d + 255) / 256 * 256;  // rows of a head in the operand-order copy
+    const __amdgpu_buffer_rsrc_t rA =
+        OP ? __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)(head0 + hh) * dpad * din), 0, dpad * din * 2, RSRC3)
+           : __builtin_amdgcn_make_buffer_rsrc((void*)(W + ((int64_t)head0 * d + row0) * din), 0, 16 * din * 2, RSRC3);
     const __amdgpu_buffer_rsrc_t rB = in_e ? __builtin_amdgcn_make_buffer_rsrc((void*)rows.E, 0, 0x7FFFFFF0, RSRC3)
                                            : __builtin_amdgcn_make_buffer_rsrc((void*)rows.h, 0, 0x7FFFFFF0, RSRC3);
     static_assert(kRowsWaves * 32 * kRowsRing == 2048, "the applicability rule's din % 2048");
-    const uint32_t aoff = (uint32_t)c16 * din * 2 + (uint32_t)(kb + 8 * g4) * 2;
+    const uint32_t aoff = OP ? w_op_frag(r0, kb / 32, din) + lane * 16 : (uint32_t)c16 * din * 2 + (uint32_t)(kb + 8 * g4) * 2;
+    constexpr uint32_t kStepA = OP ? 16 * 1024 : 64;  // bytes between a lane's A pieces of consecutive K steps
     uint32_t boff[RC];
 #pragma unroll
     for (int cb = 0; cb < RC; ++cb) {
@@ -496,7 +505,7 @@ __global__ __launch_bounds__(kRowsWaves * MD_WAVE) void k_residual_rows(
     const int nst = kw / 32;  // K steps of the run (a multiple of RP)
     auto issue = [&](int s, int j) {
         const uint32_t ko = (uint32_t)min(s, nst - 1) * 64;
-        ra[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, aoff + ko, 0, 0);
+        ra[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, aoff + (uint32_t)min(s, nst - 1) * kStepA, 0, OP ? 2 : 0);
 #pragma unroll
         for (int cb = 0; cb < RC; ++cb)
             rb[j][cb] = __builtin_amdgcn_raw_buffer_load_b128(rB, boff[cb] + ko, 0, 0);
@@ -550,7 +559,7 @@ constexpr int kStageKC = 1024;                 // contraction elements per chunk
 constexpr int kStagePitch = kStageKC + 8;      // LDS row pitch (bf16): rows 16 bytes apart mod 256
 constexpr int kStageRows = 78;                 // activation rows + the zero row
 static_assert(kStageRows * kStagePitch * 2 + 2 * kStageRows * 4 <= 160 * 1024, "the chunk fits the LDS");
-template <int RC>
+template <int RC, bool OP>
 __global__ __launch_bounds__(kRowsWaves * MD_WAVE) void k_residual_staged(
     const uint16_t* __restrict__ W, GemmRows rows, int M, int d, int din, int nh, int head0,
     float* __restrict__ zpart, int* __restrict__ bound) {
@@ -583,14 +592,19 @@ __global__ __launch_bounds__(kRowsWaves * MD_WAVE) void k_residual_staged(
     // chunk; the ring's first loads go out before the activation rows are
     // staged (W does not wait for them)
     const int kb = kc * kStageKC;
-    const __amdgpu_buffer_rsrc_t rA = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(W + ((int64_t)head0 * d + row0 + 16 * w) * din), 0, 16 * din * 2, RSRC3);
-    const uint32_t aoff = (uint32_t)c16 * din * 2 + (uint32_t)(kb + 8 * g4) * 2;
+    const int dpad = (d + 255) / 256 * 256;  // rows of a head in the operand-order copy
+    const __amdgpu_buffer_rsrc_t rA =
+        OP ? __builtin_amdgcn_make_buffer_rsrc((void*)(W + (int64_t)(head0 + hh) * dpad * din), 0, dpad * din * 2, RSRC3)
+           : __builtin_amdgcn_make_buffer_rsrc((void*)(W + ((int64_t)head0 * d + row0 + 16 * w) * din), 0,
+                                               16 * din * 2, RSRC3);
+    const uint32_t aoff = OP ? w_op_frag(r0 + 16 * w, kb / 32, din) + lane * 16
+                             : (uint32_t)c16 * din * 2 + (uint32_t)(kb + 8 * g4) * 2;
+    constexpr uint32_t kStepA = OP ? 16 * 1024 : 64;  // bytes between a lane's A pieces of consecutive K steps
     u32x4 ra[RP];
     constexpr int nst = kStageKC / 32;
     static_assert(nst % RP == 0, "whole rounds of the ring");
     auto issue = [&](int s, int j) {
-        ra[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, aoff + (uint32_t)min(s, nst - 1) * 64, 0, 0);
+        ra[j] = __builtin_amdgcn_raw_buffer_load_b128(rA, aoff + (uint32_t)min(s, nst - 1) * kStepA, 0, OP ? 2 : 0);
     };
 #pragma unroll
     for (int j = 0; j < RP; ++j) issue(j, j);
@@ -2368,14 +2382,23 @@ hipError_t heads_mfma_launch(const HeadsArgs& a, const DevTree* tree, hipStream_
                            a.h_res, L.hhi, L.hlo, L.bound);
     } else if (rows16) {
         const dim3 g((unsigned)(a.nh * a.d / 16)), blk(kRowsWaves * MD_WAVE);
-        const uint16_t* Wp = reinterpret_cast<const uint16_t*>(a.W);
-        hipLaunchKernelGGL(k_residual_rows<1>, g, blk, 0, s, Wp, bias, rows, a.M, a.d, a.din, a.nh, a.head0, L.hres,
-                           a.h_res, L.hhi, L.hlo, L.bound, bo);
+        if (a.W_op)
+            hipLaunchKernelGGL((k_residual_rows<1, true>), g, blk, 0, s, reinterpret_cast<const uint16_t*>(a.W_op), bias,
+                               rows, a.M, a.d, a.din, a.nh, a.head0, L.hres, a.h_res, L.hhi, L.hlo, L.bound, bo);
+        else
+            hipLaunchKernelGGL((k_residual_rows<1, false>), g, blk, 0, s, reinterpret_cast<const uint16_t*>(a.W), bias,
+                               rows, a.M, a.d, a.din, a.nh, a.head0, L.hres, a.h_res, L.hhi, L.hlo, L.bound, bo);
     } else if (staged) {
         const dim3 g((unsigned)(8 * (a.nh * a.d / 128))), blk(kRowsWaves * MD_WAVE);
-        const uint16_t* Wp = reinterpret_cast<const uint16_t*>(a.W);
-#define MD_STAGED(RCV)                                                                                               \
-    hipLaunchKernelGGL(k_residual_staged<RCV>, g, blk, 0, s, Wp, rows, a.M, a.d, a.din, a.nh, a.head0, L.zpart, L.bound)
+        const bool wop = a.W_op != nullptr;
+        const uint16_t* Wp = reinterpret_cast<const uint16_t*>(wop ? a.W_op : a.W);
+#define MD_STAGED(RCV)                                                                                                 \
+    if (wop)                                                                                                           \
+        hipLaunchKernelGGL((k_residual_staged<RCV, true>), g, blk, 0, s, Wp, rows, a.M, a.d, a.din, a.nh, a.head0,      \
+                           L.zpart, L.bound);                                                                          \
+    else                                                                                                               \
+        hipLaunchKernelGGL((k_residual_staged<RCV, false>), g, blk, 0, s, Wp, rows, a.M, a.d, a.din, a.nh, a.head0,     \
+                           L.zpart, L.bound)
         switch ((a.M + 15) / 16) {
             case 2: MD_STAGED(2); break;
             case 3: MD_STAGED(3); break;

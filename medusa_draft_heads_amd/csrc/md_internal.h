@@ -57,6 +57,7 @@ struct HeadsArgs {
     const void* U;
     const void* U_op;  // optional operand-order copy of U (bf16), read by the few-row matrix-core kernels
     const float* U_norms;  // optional largest squared row norm of U per 256-row tile (bf16), read by the certified pass
+    const void* W_op;      // optional operand-order copy of W (bf16), read by the few-row residual kernels
     const void* E;
     const int32_t* root_tok;
     const int32_t* tree_tok;

@@ -100,11 +100,12 @@ class MedusaStep:
         self.h_res = None
 
     # -- the four calls -------------------------------------------------------
-    def heads(self, h, W, b, U, E=None, root_tok=None, level: int = 0, h_res=None, U_op=None, U_norms=None) -> None:
+    def heads(self, h, W, b, U, E=None, root_tok=None, level: int = 0, h_res=None, U_op=None, U_norms=None,
+              W_op=None) -> None:
         c = self.cfg
         L.md_medusa_heads(c.kind, self.dt, c.M, c.d, c.V, c.K, c.k_per_head, level, self.tree, h, W, b, U, E,
                           root_tok, self.tree_tok, self.topk_idx, self.topk_val, h_res, self.ws_heads, U_op=U_op,
-                          U_norms=U_norms)
+                          U_norms=U_norms, W_op=W_op)
 
     def build(self, src_row, root_tok, lens, level: int = 0) -> None:
         c = self.cfg
@@ -135,11 +136,12 @@ class MedusaStep:
         return {"U_norms": L.vocab_tile_norms(w["U"])}
 
     def operand_order_weights(self, w: Dict[str, torch.Tensor]) -> Dict[str, torch.Tensor]:
-        """Operand-order copies of the vocabulary matrices (U_op, and Wt_op with target_head), made once
+        """Operand-order copies of the vocabulary matrices (U_op, and Wt_op with target_head) and of the
+        residual matrices (W_op), made once
         when the weights load; bf16 only. run() passes them on when w holds them."""
         if self.dt != L.MD_BF16:
             raise ValueError("operand-order copies exist for bf16 weights only")
-        out = {"U_op": L.operand_order(w["U"])}
+        out = {"U_op": L.operand_order(w["U"]), "W_op": L.operand_order(w["W"])}
         if self.cfg.target_head:
             out["Wt_op"] = L.operand_order(w["Wt"])
         return out
@@ -186,13 +188,13 @@ class MedusaStep:
             self.verify_sampled(x["logits"], x["u_words"], x["g_words"], x["Kc"], x["Vc"], x["lens"])
             return
         if c.kind != L.MD_HEADS_HYDRA:
-            self.heads(x["h"], w["W"], w["b"], w["U"], U_op=w.get("U_op"), U_norms=w.get("U_norms"))
+            self.heads(x["h"], w["W"], w["b"], w["U"], U_op=w.get("U_op"), U_norms=w.get("U_norms"), W_op=w.get("W_op"))
             self.build(x["src_row"], x["root_tok"], x["lens"])
         else:
             depth = max(self._depths())
             for level in range(1, depth + 1):
                 self.heads(x["h"], w["W"], w["b"], w["U"], E=w["E"], root_tok=x["root_tok"], level=level,
-                           U_op=w.get("U_op"), U_norms=w.get("U_norms"))
+                           U_op=w.get("U_op"), U_norms=w.get("U_norms"), W_op=w.get("W_op"))
                 self.build(None, x["root_tok"], x["lens"], level=level)
         self.attention(x["q"], x["Kc"], x["Vc"], x["lens"])
         if c.target_head:

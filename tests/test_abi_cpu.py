@@ -138,9 +138,9 @@ def test_heads_argument_errors():
                                                       product_order_tree((4, 2, 2, 1), 16).rank)]))
 
     def call(kind=0, dt=1, M=1, d=256, V=4096, K=4, kph=kpv, level=0, tree=None, h=P, W=P, U=P, ws=P, ws_bytes=1 << 30,
-             E=None, root=None, tok=None, U_op=None, U_norms=None):
-        return lib.md_medusa_heads(kind, dt, M, d, V, K, kph, level, tree, h, W, None, U, U_op, U_norms, E, root, tok, P,
-                                   P, None, ws, ws_bytes, None)
+             E=None, root=None, tok=None, U_op=None, U_norms=None, W_op=None):
+        return lib.md_medusa_heads(kind, dt, M, d, V, K, kph, level, tree, h, W, None, U, U_op, U_norms, W_op, E, root,
+                                   tok, P, P, None, ws, ws_bytes, None)
 
     assert call(kind=3) == L.MD_EINVAL
     assert call(kind=2, level=1) == L.MD_EINVAL  # a shared projection is Medusa: level 0
@@ -160,6 +160,7 @@ def test_heads_argument_errors():
     assert call(M=-1) == L.MD_EINVAL
     assert call(dt=0, U_op=P) == L.MD_EINVAL  # the operand-order copy is bf16 only
     assert call(dt=0, U_norms=P) == L.MD_EINVAL  # so are the tile norms
+    assert call(dt=0, W_op=P) == L.MD_EINVAL  # and the operand-order copy of W
     assert call(M=0) == L.MD_OK  # an empty batch enqueues nothing
 
 

@@ -27,7 +27,7 @@ def _md():
     return md
 
 
-def gpu_heads_medusa(wl: Workload, wd, h_dev, M, U_op=None, U_norms=None):
+def gpu_heads_medusa(wl: Workload, wd, h_dev, M, U_op=None, U_norms=None, W_op=None):
     import torch
 
     md = _md()
@@ -39,7 +39,7 @@ def gpu_heads_medusa(wl: Workload, wd, h_dev, M, U_op=None, U_norms=None):
     hres = torch.empty(K, M, wl.d, dtype=torch.float32, device="cuda")
     ws = torch.empty(md.md_heads_workspace_bytes(kind, dt, M, wl.d, wl.V, K, kmax), dtype=torch.uint8, device="cuda")
     md.md_medusa_heads(kind, dt, M, wl.d, wl.V, K, wl.topk, 0, None, h_dev, wd["W"], wd["b"], wd["U"], None, None,
-                       None, idx, val, hres, ws, U_op=U_op, U_norms=U_norms)
+                       None, idx, val, hres, ws, U_op=U_op, U_norms=U_norms, W_op=W_op)
     torch.cuda.synchronize()
     return from_dev(idx), from_dev(val), from_dev(hres)
 
@@ -145,7 +145,7 @@ def test_heads_medusa_full_size(wl_name):
 
 # ---------------------------------------------------------------- Hydra
 
-def gpu_hydra_level(wl, wd, h_dev, root_dev, tok_dev, tree, level, rows, U_op=None):
+def gpu_hydra_level(wl, wd, h_dev, root_dev, tok_dev, tree, level, rows, U_op=None, W_op=None):
     import torch
 
     md = _md()
@@ -156,7 +156,7 @@ def gpu_hydra_level(wl, wd, h_dev, root_dev, tok_dev, tree, level, rows, U_op=No
     ws = torch.empty(md.md_heads_workspace_bytes(1, dt, wl.B, wl.d, wl.V, wl.K, wl.kmax), dtype=torch.uint8,
                      device="cuda")
     md.md_medusa_heads(1, dt, wl.B, wl.d, wl.V, wl.K, wl.topk, level, tree, h_dev, wd["W"], wd["b"], wd["U"], wd["E"],
-                       root_dev, tok_dev, idx, val, hres, ws, U_op=U_op)
+                       root_dev, tok_dev, idx, val, hres, ws, U_op=U_op, W_op=W_op)
     torch.cuda.synchronize()
     return from_dev(idx), from_dev(val), from_dev(hres)
 
@@ -170,6 +170,7 @@ def check_hydra(wl, seed, requests=None, op=False):
                               x["root_tok"], x["lens"], requests=requests, want_logits=True)
     wd = {k: to_dev(v) for k, v in w.items()}
     U_op = md.operand_order(wd["U"]) if op else None
+    W_op = md.operand_order(wd["W"]) if op else None
     tree = md.make_tree(topo.parent, topo.rank)
     tok_dev = to_dev(np.where(ref["tree_tok"] < 0, 0, ref["tree_tok"]).astype(np.int32))  # oracle's upstream tokens
     h_dev, root_dev = to_dev(x["h"]), to_dev(x["root_tok"])
@@ -178,7 +179,11 @@ def check_hydra(wl, seed, requests=None, op=False):
     for li, lvl in enumerate(ref["levels"]):
         level = li + 1
         P = len(oracle.hydra_rows(topo.parent, level))
-        gi, gv, gh = gpu_hydra_level(wl, wd, h_dev, root_dev, tok_dev, tree, level, wl.B * P, U_op=U_op)
+        gi, gv, gh = gpu_hydra_level(wl, wd, h_dev, root_dev, tok_dev, tree, level, wl.B * P, U_op=U_op, W_op=W_op)
+        if op:  # the residual reads W's operand-order copy in the same order as W itself: the same bits
+            gi0, gv0, gh0 = gpu_hydra_level(wl, wd, h_dev, root_dev, tok_dev, tree, level, wl.B * P, U_op=U_op)
+            assert np.array_equal(gi, gi0) and np.array_equal(gv.view(np.uint32), gv0.view(np.uint32))
+            assert np.array_equal(gh.view(np.uint32), gh0.view(np.uint32))
         # GPU rows are (b, parent) over all requests; pick the oracle's rows
         sel = [b * P + j for b in reqs for j in range(P)]
         assert len(sel) == len(lvl["rows"])
@@ -308,9 +313,13 @@ def test_heads_medusa_mfma_full_size_sampled(wl_name, M, rows):
     ref = oracle.heads_medusa(w["W"], w["b"], w["U"], h, wl.topk, rows=rows, want_logits=True)
     ref["hres"] = ref["hres"]
     compare_medusa(wl, gi[rows], gv[rows], gh[:, rows], ref, label="%s M=%d rows %s" % (wl.name, M, rows))
-    # the certified pass reading the tile norms: every list and value of all M rows the same
-    gi2, gv2, _ = gpu_heads_medusa(wl, wd, to_dev(h), M, U_norms=_md().vocab_tile_norms(wd["U"]))
+    # the certified pass reading the tile norms: every list and value of all M rows the same; the
+    # residual reading the operand-order copy of W: the same bits (h' too)
+    md = _md()
+    gi2, gv2, gh2 = gpu_heads_medusa(wl, wd, to_dev(h), M, U_norms=md.vocab_tile_norms(wd["U"]),
+                                     W_op=md.operand_order(wd["W"]))
     assert np.array_equal(gi, gi2) and np.array_equal(gv.view(np.uint32), gv2.view(np.uint32))
+    assert np.array_equal(gh.view(np.uint32), gh2.view(np.uint32))
     del wd
 
 

@@ -79,7 +79,7 @@ def hydra_levels_checked(wl, w, wd, x, xd, step, topo):
     ties = 0
     for level in range(1, depth + 1):
         step.heads(xd["h"], wd["W"], wd["b"], wd["U"], E=wd["E"], root_tok=xd["root_tok"], level=level,
-                   U_op=wd.get("U_op"))
+                   U_op=wd.get("U_op"), W_op=wd.get("W_op"))
         step.build(None, xd["root_tok"], xd["lens"], level=level)
         torch.cuda.synchronize()
         lvl = oracle.hydra_level(w["W"], w["b"], w["U"], w["E"], x["h"], topo.parent, topo.rank, wl.topk, level, tok,
@@ -267,6 +267,7 @@ def test_step_hydra_batch4():
     w = weights(wl, seed)
     wd = {k: to_dev(v) for k, v in w.items()}
     wd["U_op"] = md.operand_order(wd["U"])
+    wd["W_op"] = md.operand_order(wd["W"])
     step, topo = make_step(wl)
     acc = run_and_compare(wl, w, wd, step, topo, seed, 0)
     print("Hydra batch-4 step accepted", acc.tolist())
