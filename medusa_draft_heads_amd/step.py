@@ -141,7 +141,11 @@ class MedusaStep:
         when the weights load; bf16 only. run() passes them on when w holds them."""
         if self.dt != L.MD_BF16:
             raise ValueError("operand-order copies exist for bf16 weights only")
-        out = {"U_op": L.operand_order(w["U"]), "W_op": L.operand_order(w["W"])}
+        out = {"U_op": L.operand_order(w["U"])}
+        # W's copy only where a few-row matrix-core residual reads it (Hydra's levels, 2 to 77 Medusa
+        # rows); one row runs the fused or GEMV residual on W itself
+        if self.cfg.kind == L.MD_HEADS_HYDRA or 1 < self.cfg.M < 78:
+            out["W_op"] = L.operand_order(w["W"])
         if self.cfg.target_head:
             out["Wt_op"] = L.operand_order(w["Wt"])
         return out
