@@ -254,6 +254,15 @@ __device__ __forceinline__ bool xcd_group_decode(int id, int qtiles, int ngroups
     group = (u / qtiles) * 8 + x;
     return group < ngroups;
 }
+// With (request, kv head) pairs a multiple of 8: every block of one pair on
+// one XCD (pair p on XCD p % 8), so its K and V and its query rows are each
+// fetched once into that XCD's L2, whatever the query tile and key range.
+__device__ __forceinline__ void xcd_head_decode(int id, int qtiles, int splits, int& group, int& qt) {
+    const int x = id & 7, u = id >> 3, per = qtiles * splits;
+    const int j = u / per, rem = u - j * per;
+    qt = rem / splits;
+    group = (j * 8 + x) * splits + (rem - qt * splits);
+}
 
 // word 3 of a raw buffer resource on this chip family (32-bit data format, no swizzle)
 constexpr int RSRC3 = 0x00020000;
@@ -301,7 +310,7 @@ __global__ __launch_bounds__(BLOCK, RG == 1 ? 3 : 2) void k_attn_mfma(DevTree t,
                                                      const uint16_t* __restrict__ q, const uint16_t* __restrict__ Kc,
                                                      const uint16_t* __restrict__ Vc, const int32_t* __restrict__ lens,
                                                      float scale, int splits, int chunk, int qtiles, int ngroups,
-                                                     uint16_t* __restrict__ po, float* __restrict__ pm,
+                                                     int head_map, uint16_t* __restrict__ po, float* __restrict__ pm,
                                                      float* __restrict__ pl, float* __restrict__ pe) {
     constexpr int CPR = HD / 8;          // 16-byte chunks per key row
     constexpr int ROWB = HD * 2;         // bytes per key row
@@ -315,7 +324,10 @@ __global__ __launch_bounds__(BLOCK, RG == 1 ? 3 : 2) void k_attn_mfma(DevTree t,
     __shared__ __align__(1024) unsigned char sb2[2 * TILEB];
 
     int grp, qt;
-    if (!xcd_group_decode(blockIdx.x, qtiles, ngroups, grp, qt)) return;
+    if (head_map)
+        xcd_head_decode(blockIdx.x, qtiles, splits, grp, qt);
+    else if (!xcd_group_decode(blockIdx.x, qtiles, ngroups, grp, qt))
+        return;
     const int s = grp % splits;
     const int g = (grp / splits) % Hkv;
     const int b = grp / (splits * Hkv);
@@ -660,10 +672,11 @@ hipError_t launch_typed(const DevTree& t, int B, int Hq, int Hkv, int hd, int Lc
     const T* vv = reinterpret_cast<const T*>(Vc);
     if constexpr (sizeof(T) == 2) {
         const int ngroups = B * Hkv * p.splits;
-        const dim3 mgrid((unsigned)(8 * p.qtiles * ((ngroups + 7) / 8)));
+        const int head_map = (B * Hkv) % 8 == 0;  // every (request, kv head) pair's blocks on one XCD
+        const dim3 mgrid((unsigned)(head_map ? B * Hkv * p.qtiles * p.splits : 8 * p.qtiles * ((ngroups + 7) / 8)));
 #define MD_ATTN(HDV, RGV)                                                                                  \
     hipLaunchKernelGGL((k_attn_mfma<HDV, RGV>), mgrid, dim3(BLOCK), 0, st_, t, Hq, Hkv, Lcap, max_len, qq, kk, vv, lens, \
-                       scale, p.splits, p.chunk, p.qtiles, ngroups, po, pm, pl, pe)
+                       scale, p.splits, p.chunk, p.qtiles, ngroups, head_map, po, pm, pl, pe)
         if (hd == 64 && p.rg == 2)
             MD_ATTN(64, 2);
         else if (hd == 64)
