@@ -1272,6 +1272,13 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_direct(const uint16_t* 
     for (int j = 0; j < P; ++j)
         if (s0 + j < nk) step(s0 + j, j);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // the repeated loads land before the buffers are reused
+    // The ring is read here: the U loads of the last steps go into slots no
+    // later step reads, and dropped as unused they would leave fewer loads
+    // behind each stage than the counted wait assumes.
+#pragma unroll
+    for (int j = 0; j < P; ++j)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) asm volatile("" ::"v"(ra[j][rb]));
     if (tid < CB * 16)
         s_bound[tid] = tid < M ? o2f(__hip_atomic_load(bound + (int64_t)hh * M + tid, __ATOMIC_RELAXED,
                                                         __HIP_MEMORY_SCOPE_AGENT))
