@@ -121,17 +121,16 @@ __global__ __launch_bounds__(BLOCK) void k_accept(DevTree t, int K, int Hkv, int
             if (lane < N) bi = target_tok[(int64_t)b * N + lane];
         } else if (lane < N) {
             const int64_t r = ((int64_t)b * N + lane) * chunks;
-            // 16 parts per round: one memory round trip for up to 16 chunks a row
-            for (int c0 = 0; c0 < chunks; c0 += 16) {
-                float v[16];
-                int ix[16];
+            for (int c0 = 0; c0 < chunks; c0 += 8) {
+                float v[8];
+                int ix[8];
 #pragma unroll
-                for (int u = 0; u < 16; ++u) {
+                for (int u = 0; u < 8; ++u) {
                     v[u] = c0 + u < chunks ? part_v[r + c0 + u] : -INFINITY;
                     ix[u] = c0 + u < chunks ? part_i[r + c0 + u] : INT_MAX;
                 }
 #pragma unroll
-                for (int u = 0; u < 16; ++u)
+                for (int u = 0; u < 8; ++u)
                     if (beats(v[u], ix[u], bv, bi)) {
                         bv = v[u];
                         bi = ix[u];
