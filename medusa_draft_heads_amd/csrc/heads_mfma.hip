@@ -1756,6 +1756,9 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
     const int slot = (g4 ^ ((c16 >> 1) & 3)) * 16;
     auto compute = [&](const unsigned char* sA) {
         const unsigned char* sB = sA + A_BYTES;
+        // raised issue priority over the products: a wave whose stage has
+        // landed keeps the matrix units fed while the SIMD's other wave waits
+        __builtin_amdgcn_s_setprio(1);
         bf16x8 a[8];
 #pragma unroll
         for (int rb = 0; rb < 8; ++rb)
@@ -1780,6 +1783,7 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
                     gram[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[4 + j], a[4 + j], gram[j], 0, 0, 0);
             }
         }
+        __builtin_amdgcn_s_setprio(0);
     };
 
     // Three stage buffers with two stages in flight, as in the narrow kernel:
