@@ -1756,9 +1756,11 @@ __global__ __launch_bounds__(BLOCK, 2) void k_vocab_mfma_cert(const uint16_t* __
     const int slot = (g4 ^ ((c16 >> 1) & 3)) * 16;
     auto compute = [&](const unsigned char* sA) {
         const unsigned char* sB = sA + A_BYTES;
-        // raised issue priority over the products: a wave whose stage has
-        // landed keeps the matrix units fed while the SIMD's other wave waits
-        __builtin_amdgcn_s_setprio(1);
+        // the highest issue priority over the stage's fragment reads and
+        // products: a wave whose stage has landed keeps the matrix units fed
+        // while the SIMD's other wave waits (raised only after the reads,
+        // the pass was slower)
+        __builtin_amdgcn_s_setprio(3);
         bf16x8 a[8];
 #pragma unroll
         for (int rb = 0; rb < 8; ++rb)
