@@ -238,3 +238,35 @@ def test_accept_argmax_ties_take_lowest_index():
     tok = np.array([[5, 0, 7]], np.int32)  # node 1 matches t*(root) = 0; node 2 would need t*(1) = 7
     got, ref = run_accept("f32", topo, 2, 1, V, 1, 64, [2], 8, seed=1, tok=tok, logits=logits)
     assert got["accept_len"][0] == 2 and got["next_tok"][0] == 0
+
+
+def test_accept_argmax_512_rows_ties_across_halves():
+    """Batch 8 x 64 nodes = 512 rows of the full 128,256-entry vocabulary (the batch-8 verification
+    shape, where the argmax splits each row into chunks). Every row's two largest logits lie one in
+    each half of the row: equal (the lower index must win) or the upper one larger by 0.5 (the
+    larger must win). A node's first child carries its parent's target choice and its second child
+    the parent's other planted index, so the accepted branch is the first-child chain to depth 4,
+    and a wrong choice at any row on it changes the path, the length or the next token."""
+    topo = product_order_tree((10, 4, 2, 1), 64)
+    B, V, N = 8, 128256, topo.n
+    rng = np.random.default_rng(11)
+    half = V // 2
+    i0 = rng.integers(0, half, size=(B, N))
+    i1 = rng.integers(half, V, size=(B, N))
+    bigger = rng.random((B, N)) < 0.5
+    logits = np.zeros((B, N, V), np.float32)
+    bi, ni = np.meshgrid(np.arange(B), np.arange(N), indexing="ij")
+    logits[bi, ni, i0] = 10.0
+    logits[bi, ni, i1] = np.where(bigger, 10.5, 10.0).astype(np.float32)
+    tstar = np.where(bigger, i1, i0)
+    other = np.where(bigger, i0, i1)
+    tok = np.zeros((B, N), np.int32)
+    for b in range(B):
+        tok[b, 0] = 7
+        for n in range(1, N):
+            p, r = topo.parent[n], topo.rank[n]
+            tok[b, n] = tstar[b, p] if r == 0 else (other[b, p] if r == 1 else (tstar[b, p] + r) % V)
+    got, ref = run_accept("bf16", topo, 4, B, V, 8, 128, [100] * B, 200, seed=12, tok=tok, logits=logits)
+    assert np.all(ref["accept_len"] == 5) and np.all(got["accept_len"] == 5)
+    deepest = got["path"][:, 4]
+    assert np.array_equal(got["next_tok"], tstar[np.arange(B), deepest])
